@@ -1,0 +1,234 @@
+// api.cpp -- the extern "C" entry points declared in include/gdn.h.
+//
+// Host side only: argument validation (before anything is enqueued), choice of
+// kernel, and the launches.  Nothing here allocates device memory, keeps
+// global mutable state, or synchronises the host with the stream.
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int kMaxGrid = 65535;
+
+gdn_status hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+bool valid_dtype(int dt) { return dt == GDN_F32 || dt == GDN_BF16; }
+
+// Host mirror of packed offsets: cu[0] == first, non-decreasing, cu[n] == last.
+bool offsets_ok(const int32_t* cu, int32_t n, int64_t first_max, int64_t last, bool exact_ends) {
+  if (!cu || n < 1) return false;
+  if (cu[0] < 0 || cu[0] > first_max) return false;
+  if (exact_ends && cu[0] != 0) return false;
+  for (int32_t i = 0; i < n; ++i)
+    if (cu[i + 1] < cu[i]) return false;
+  if (cu[n] > last) return false;
+  if (exact_ends && cu[n] != last) return false;
+  return true;
+}
+
+// Token stride: 0 selects the dense value; otherwise a multiple of 8, >= dense.
+bool stride_ok(int64_t* stride, int64_t dense) {
+  if (*stride == 0) *stride = dense;
+  return *stride >= dense && *stride % 8 == 0;
+}
+
+// Which chunk kernel serves (in_dt, K, V); GDN_OK when one does.
+gdn_status chunk_supported(int in_dt, int32_t K, int32_t V) {
+  if (in_dt == GDN_BF16) return (K == 128 && V > 0 && V % 128 == 0) ? GDN_OK : GDN_ERR_UNSUPPORTED;
+  if (K == 32 || K == 64) return (V > 0 && V % 32 == 0) ? GDN_OK : GDN_ERR_UNSUPPORTED;
+  return GDN_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(int status) {
+  switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case GDN_ERR_BAD_SHAPE: return "negative or inconsistent sizes";
+    case GDN_ERR_BAD_DTYPE: return "dtype not accepted by this entry point";
+    case GDN_ERR_UNSUPPORTED: return "no kernel for this combination of sizes and dtype";
+    case GDN_ERR_BAD_SEQLENS: return "malformed cu_seqlens / segment offsets, or offsets with B > 1";
+    case GDN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int gdn_abi_version(void) { return kAbiVersion; }
+
+gdn_status gdn_gate_fwd(const float* a, const float* b, const float* A_log, const float* dt_bias,
+                        int64_t n_tokens, int32_t H, float* g, float* beta, hipStream_t stream) {
+  if (n_tokens < 0 || H <= 0) return GDN_ERR_BAD_SHAPE;
+  if (n_tokens == 0) return GDN_OK;
+  if (!a || !b || !A_log || !dt_bias || !g || !beta) return GDN_ERR_NULL_POINTER;
+  return hip_status(gdn::launch_gate(a, b, A_log, dt_bias, n_tokens, H, g, beta, stream));
+}
+
+gdn_status gdn_conv1d_fwd(const void* x, const void* w, const void* bias, gdn_dtype dt,
+                          const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                          int32_t n_seqs, int32_t B, int64_t T, int32_t channels,
+                          int32_t width, int32_t apply_silu, int32_t l2norm_channels,
+                          int32_t head_dim, float l2_eps, void* y, hipStream_t stream) {
+  if (!valid_dtype(dt)) return GDN_ERR_BAD_DTYPE;
+  if (B < 1 || T < 0 || channels <= 0 || channels % 8 != 0) return GDN_ERR_BAD_SHAPE;
+  if (width < 1 || width > 4) return GDN_ERR_UNSUPPORTED;
+  if (l2norm_channels < 0 || l2norm_channels > channels) return GDN_ERR_BAD_SHAPE;
+  if (l2norm_channels > 0) {
+    if (head_dim < 8 || head_dim > 512 || (head_dim & (head_dim - 1)) != 0) return GDN_ERR_UNSUPPORTED;
+    if (l2norm_channels % head_dim != 0) return GDN_ERR_BAD_SHAPE;
+  }
+  if (cu_seqlens) {
+    if (B != 1 || n_seqs < 1) return GDN_ERR_BAD_SEQLENS;
+    if (cu_seqlens_host && !offsets_ok(cu_seqlens_host, n_seqs, 0, T, true)) return GDN_ERR_BAD_SEQLENS;
+  }
+  const int64_t total = (int64_t)B * T;
+  if (total == 0) return GDN_OK;
+  if (!x || !w || !y) return GDN_ERR_NULL_POINTER;
+  if ((total + 31) / 32 > kMaxGrid) return GDN_ERR_UNSUPPORTED;
+  return hip_status(gdn::launch_conv1d(x, w, bias, dt, cu_seqlens, n_seqs, B, T, channels, width,
+                                       apply_silu, l2norm_channels, head_dim, l2_eps, y, stream));
+}
+
+gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, gdn_dtype in_dt,
+                         int64_t q_token_stride, int64_t k_token_stride, int64_t v_token_stride,
+                         const float* g, const float* beta, float scale,
+                         const float* initial_state, const int32_t* cu_seqlens,
+                         const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t B, int64_t T,
+                         int32_t H_qk, int32_t H_v, int32_t K, int32_t V, void* o,
+                         gdn_dtype o_dt, float* final_state, hipStream_t stream) {
+  if (!valid_dtype(in_dt) || !valid_dtype(o_dt)) return GDN_ERR_BAD_DTYPE;
+  if (B < 1 || T < 0 || H_qk < 1 || H_v < 1 || K < 1 || V < 1) return GDN_ERR_BAD_SHAPE;
+  if (H_v % H_qk != 0) return GDN_ERR_BAD_SHAPE;
+  if (!stride_ok(&q_token_stride, (int64_t)H_qk * K) || !stride_ok(&k_token_stride, (int64_t)H_qk * K) ||
+      !stride_ok(&v_token_stride, (int64_t)H_v * V))
+    return GDN_ERR_BAD_SHAPE;
+  if (cu_seqlens) {
+    if (B != 1 || n_seqs < 1) return GDN_ERR_BAD_SEQLENS;
+    if (cu_seqlens_host && !offsets_ok(cu_seqlens_host, n_seqs, 0, T, true)) return GDN_ERR_BAD_SEQLENS;
+  }
+  const gdn_status sup = chunk_supported(in_dt, K, V);
+  if (sup != GDN_OK) return sup;
+  const int32_t N = cu_seqlens ? n_seqs : B;
+  if (N > kMaxGrid || H_v > kMaxGrid) return GDN_ERR_UNSUPPORTED;
+  const int64_t total = cu_seqlens ? T : (int64_t)B * T;
+  if (total == 0 && !final_state) return GDN_OK;
+  if (total > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL_POINTER;
+  gdn::ChunkArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.cu = cu_seqlens;
+  a.n_seqs = N;
+  a.row_len = T;
+  a.Ttot = total;
+  a.Hqk = H_qk;
+  a.Hv = H_v;
+  a.K = K;
+  a.V = V;
+  a.q_stride = q_token_stride;
+  a.k_stride = k_token_stride;
+  a.v_stride = v_token_stride;
+  a.scale = scale;
+  a.in_dt = in_dt;
+  a.s0_mode = initial_state ? 1 : 0;
+  a.s0 = initial_state;
+  a.o = o;
+  a.o_dt = o_dt;
+  a.sf = final_state;
+  a.sf_seq_stride = (int64_t)H_v * K * V;
+  a.sf_head_stride = (int64_t)K * V;
+  a.sf_row_stride = V;
+  const hipError_t e = in_dt == GDN_BF16 ? gdn::launch_chunk_bf16(a, stream)
+                                         : gdn::launch_chunk_f32(a, stream);
+  return hip_status(e);
+}
+
+gdn_status gdn_segment_state_scan(const void* k, const void* v, gdn_dtype in_dt,
+                                  int64_t k_token_stride, int64_t v_token_stride,
+                                  const float* g, const float* beta,
+                                  const int32_t* seg_offsets, const int32_t* seg_offsets_host,
+                                  int32_t P, const float* initial_state, int64_t T,
+                                  int32_t H_qk, int32_t H_v, int32_t K, int32_t V, float* M,
+                                  float* b, float* seg_initial_states, float* final_state,
+                                  hipStream_t stream) {
+  if (!valid_dtype(in_dt)) return GDN_ERR_BAD_DTYPE;
+  if (in_dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+  if (P < 1 || T < 0 || H_qk < 1 || H_v < 1 || H_v % H_qk != 0) return GDN_ERR_BAD_SHAPE;
+  if (K != 128 || V < 1 || V % 128 != 0) return GDN_ERR_UNSUPPORTED;
+  if (P > kMaxGrid || H_v > kMaxGrid) return GDN_ERR_UNSUPPORTED;
+  if (!stride_ok(&k_token_stride, (int64_t)H_qk * K) || !stride_ok(&v_token_stride, (int64_t)H_v * V))
+    return GDN_ERR_BAD_SHAPE;
+  if (!seg_offsets) return GDN_ERR_NULL_POINTER;
+  if (seg_offsets_host && !offsets_ok(seg_offsets_host, P, T, T, false)) return GDN_ERR_BAD_SEQLENS;
+  if (!k || !v || !g || !beta || !M || !b || !seg_initial_states) return GDN_ERR_NULL_POINTER;
+  gdn::ChunkArgs a{};
+  a.q = nullptr;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.cu = seg_offsets;
+  a.n_seqs = P;
+  a.row_len = T;
+  a.Ttot = T;
+  a.Hqk = H_qk;
+  a.Hv = H_v;
+  a.K = K;
+  a.V = V;
+  a.q_stride = k_token_stride;
+  a.k_stride = k_token_stride;
+  a.v_stride = v_token_stride;
+  a.scale = 1.f;
+  a.in_dt = in_dt;
+  a.s0_mode = 0;
+  a.o_dt = GDN_F32;
+  hipError_t e = gdn::launch_segment_pass1(a, M, b, stream);
+  if (e != hipSuccess) return GDN_ERR_HIP;
+  e = gdn::launch_compose(M, b, initial_state, P, H_v, K, V, seg_initial_states, final_state, stream);
+  return hip_status(e);
+}
+
+size_t gdn_segmented_workspace_bytes(int32_t P, int32_t H_v, int32_t K, int32_t V) {
+  if (P < 1 || H_v < 1 || K < 1 || V < 1) return 0;
+  const size_t per = (size_t)H_v * K;
+  return sizeof(float) * (size_t)P * per * ((size_t)K + 2 * (size_t)V);
+}
+
+gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
+                                   gdn_dtype in_dt, int64_t q_token_stride,
+                                   int64_t k_token_stride, int64_t v_token_stride,
+                                   const float* g, const float* beta,
+                                   float scale, const float* initial_state,
+                                   const int32_t* seg_offsets, const int32_t* seg_offsets_host,
+                                   int32_t P, int64_t T, int32_t H_qk, int32_t H_v, int32_t K,
+                                   int32_t V, void* o, gdn_dtype o_dt, float* final_state,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!valid_dtype(in_dt) || !valid_dtype(o_dt)) return GDN_ERR_BAD_DTYPE;
+  if (in_dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+  if (P < 1 || T < 0 || H_qk < 1 || H_v < 1 || H_v % H_qk != 0) return GDN_ERR_BAD_SHAPE;
+  if (K != 128 || V < 1 || V % 128 != 0) return GDN_ERR_UNSUPPORTED;
+  if (seg_offsets_host && !offsets_ok(seg_offsets_host, P, 0, T, true)) return GDN_ERR_BAD_SEQLENS;
+  if (!q || !k || !v || !g || !beta || !o || !seg_offsets || !workspace) return GDN_ERR_NULL_POINTER;
+  if (workspace_bytes < gdn_segmented_workspace_bytes(P, H_v, K, V)) return GDN_ERR_BAD_SHAPE;
+  float* M = static_cast<float*>(workspace);
+  float* b = M + (size_t)P * H_v * K * K;
+  float* starts = b + (size_t)P * H_v * K * V;
+  gdn_status s = gdn_segment_state_scan(k, v, in_dt, k_token_stride, v_token_stride, g, beta,
+                                        seg_offsets, nullptr, P,
+                                        initial_state, T, H_qk, H_v, K, V, M, b, starts,
+                                        final_state, stream);
+  if (s != GDN_OK) return s;
+  return gdn_chunk_fwd(q, k, v, in_dt, q_token_stride, k_token_stride, v_token_stride, g, beta,
+                       scale, starts, seg_offsets, nullptr, P, 1, T, H_qk,
+                       H_v, K, V, o, o_dt, nullptr, stream);
+}
+
+}  // extern "C"

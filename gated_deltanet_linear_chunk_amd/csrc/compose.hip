@@ -1,0 +1,84 @@
+// compose.hip -- fp32 chain of segment affine maps.
+//
+// Given per-segment maps S_end = M_i S_start + b_i, the true start state of
+// every segment follows from S_start,0 = S0 and S_start,i+1 = M_i S_start,i + b_i,
+// composed in fp32 (the sglang fork PR "Qwen3.5 cp - #1" chain-reduces its
+// (b, M) pairs in fp32).  Each column of the K x V state is its own affine
+// chain, so the work is split over (v-head, 16-column slice): 256 threads per
+// workgroup, each producing 8 entries of M_i S + b_i per step, with the
+// current start state of the slice held in LDS.  Segments follow one another
+// inside the workgroup, which needs only the M S products (a tree over
+// segments would also need M M products, K / 16 times more work per level).
+#include "device_common.h"
+#include "kernels.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int CK = 128;  // key dim
+constexpr int CT = 16;   // state columns per workgroup
+constexpr int CTHREADS = 256;
+
+__global__ void __launch_bounds__(CTHREADS) compose_kernel(const float* __restrict__ M,
+                                                           const float* __restrict__ b,
+                                                           const float* __restrict__ s0, int P,
+                                                           int Hv, int V,
+                                                           float* __restrict__ starts,
+                                                           float* __restrict__ final_state) {
+  __shared__ float sS[2][CK][CT];
+  const int tid = threadIdx.x;
+  const int c0 = blockIdx.x * CT;
+  const int h = blockIdx.y;
+  const int d = tid >> 1;          // output row
+  const int cc = (tid & 1) * 8;    // 8 output columns
+
+  const int64_t state_head = (int64_t)h * CK * V;
+  for (int i = tid; i < CK * CT; i += CTHREADS) {
+    const int r = i / CT, c = i % CT;
+    sS[0][r][c] = s0 ? s0[state_head + (int64_t)r * V + c0 + c] : 0.f;
+  }
+  __syncthreads();
+  int cur = 0;
+  for (int seg = 0; seg < P; ++seg) {
+    const int64_t seg_state = (int64_t)seg * Hv * CK * V + state_head;
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      starts[seg_state + (int64_t)d * V + c0 + cc + j] = sS[cur][d][cc + j];
+      acc[j] = b[seg_state + (int64_t)d * V + c0 + cc + j];
+    }
+    const float* Mrow = M + ((int64_t)seg * Hv + h) * CK * CK + (int64_t)d * CK;
+    for (int l = 0; l < CK; l += 4) {
+      const float4 m4 = *reinterpret_cast<const float4*>(Mrow + l);
+      const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(mv[u], sS[cur][l + u][cc + j], acc[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sS[cur ^ 1][d][cc + j] = acc[j];
+    cur ^= 1;
+    __syncthreads();
+  }
+  if (final_state) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      final_state[state_head + (int64_t)d * V + c0 + cc + j] = sS[cur][d][cc + j];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_compose(const float* M, const float* b, const float* s0, int P, int Hv, int K,
+                          int V, float* starts, float* final_state, hipStream_t stream) {
+  if (P == 0 || Hv == 0) return hipSuccess;
+  if (K != CK || V % CT != 0) return hipErrorInvalidValue;
+  dim3 grid(V / CT, Hv);
+  hipLaunchKernelGGL(compose_kernel, grid, dim3(CTHREADS), 0, stream, M, b, s0, P, Hv, V, starts,
+                     final_state);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,90 @@
+// device_common.h -- small device helpers shared by the gfx950 kernels.
+//
+// bf16 <-> fp32 conversion (round to nearest even), split of an fp32 value into
+// a bf16 pair (hi + lo), and the MFMA fragment conventions used by the chunk
+// kernels.
+//
+// MFMA v_mfma_f32_16x16x32_bf16 (wave64): lane l, c16 = l % 16, g4 = l / 16.
+//   A (16 x 32, M x K): lane holds 8 values of row c16,
+//   B (32 x 16, K x N): lane holds 8 values of column c16,
+//   C/D (16 x 16):      lane holds rows 4*g4 + e (e = 0..3) of column c16.
+// The K index carried by (g4, j) only has to agree between A and B.  These
+// kernels use the "accumulator-compatible" assignment
+//   j = 0..3 -> k = 4*g4 + j,   j = 4..7 -> k = 16 + 4*g4 + (j - 4),
+// so that the accumulator tiles of one product (rows 4*g4+e of two vertically
+// adjacent 16 x 16 tiles) are, register for register, the B operand of the
+// next product along that row index -- no trip through LDS.  An operand read
+// from a row-major LDS matrix under this assignment is two 8-byte reads.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// x ~= hi + lo with both in bf16; |x - hi - lo| <= 2^-16 |x| (about).
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16_bits(x);
+  lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u16x8 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// A/B fragment from a row-major bf16 LDS matrix (pitch in elements):
+// row `row`, K columns k0 + {4*g4..4*g4+3} and k0 + 16 + {4*g4..4*g4+3}.
+__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* base, int pitch, int row, int k0,
+                                           int g4) {
+  const uint16_t* p = base + row * pitch + k0 + 4 * g4;
+  u16x4 a = *reinterpret_cast<const u16x4*>(p);
+  u16x4 b = *reinterpret_cast<const u16x4*>(p + 16);
+  u16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return as_bf16x8(r);
+}
+
+// Pack two accumulator tiles (4 floats each, rows 4*g4+e of tiles t0 and t1)
+// into hi and lo B fragments.
+__device__ __forceinline__ void split_frag(const f32x4& t0, const f32x4& t1, bf16x8& hi,
+                                           bf16x8& lo) {
+  u16x8 h, l;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint16_t a, b;
+    split_bf16(t0[e], a, b);
+    h[e] = a;
+    l[e] = b;
+    split_bf16(t1[e], a, b);
+    h[4 + e] = a;
+    l[4 + e] = b;
+  }
+  hi = as_bf16x8(h);
+  lo = as_bf16x8(l);
+}
+
+__device__ __forceinline__ int clampi(int64_t x, int64_t lo, int64_t hi) {
+  return (int)(x < lo ? lo : (x > hi ? hi : x));
+}
+
+}  // namespace gdn

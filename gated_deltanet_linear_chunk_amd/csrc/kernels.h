@@ -1,0 +1,51 @@
+// kernels.h -- launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+hipError_t launch_gate(const float* a, const float* b, const float* A_log, const float* dt_bias,
+                       int64_t n_tokens, int H, float* g, float* beta, hipStream_t stream);
+
+hipError_t launch_conv1d(const void* x, const void* w, const void* bias, int dt,
+                         const int32_t* cu, int n_seqs, int B, int64_t T, int C, int width,
+                         int apply_silu, int l2_channels, int head_dim, float l2_eps, void* y,
+                         hipStream_t stream);
+
+// Where the sequences of a chunk-rule launch come from and what they produce.
+struct ChunkArgs {
+  const void* q;  // [Ttot, Hqk, K] (may be null when no output is produced)
+  const void* k;  // [Ttot, Hqk, K]
+  const void* v;  // [Ttot, Hv, V]
+  const float* g;     // [Ttot, Hv]
+  const float* beta;  // [Ttot, Hv]
+  const int32_t* cu;  // device offsets [n_seqs + 1] or null (then rows of row_len)
+  int n_seqs;
+  int64_t row_len;
+  int64_t Ttot;
+  int Hqk, Hv, K, V;
+  // elements between consecutive tokens of q, k and v (dense: Hqk*K, Hqk*K, Hv*V)
+  int64_t q_stride, k_stride, v_stride;
+  float scale;
+  int in_dt;  // 0 f32, 1 bf16
+  // initial state: 0 zero, 1 load from s0 [n_seqs, Hv, K, V], 2 identity (augmented M columns)
+  int s0_mode;
+  const float* s0;
+  void* o;  // [Ttot, Hv, V] or null
+  int o_dt;
+  // final state destination: element (seq, h, row i, col j) at
+  // sf + seq * sf_seq_stride + h * sf_head_stride + i * sf_row_stride + j
+  float* sf;
+  int64_t sf_seq_stride, sf_head_stride, sf_row_stride;
+};
+
+hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t stream);
+// Pass 1 of the segment scan: M columns (v = 0, S0 = I) and b columns (S0 = 0).
+hipError_t launch_segment_pass1(const ChunkArgs& a, float* M, float* b, hipStream_t stream);
+hipError_t launch_compose(const float* M, const float* b, const float* s0, int P, int Hv, int K,
+                          int V, float* starts, float* final_state, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,189 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated delta rule forward library.
+ *
+ * The library computes the forward pass of a GatedDeltaNet linear-attention
+ * layer's core: the gated delta rule recurrence (per head, a K x V state)
+ *     S_t = exp(g_t) (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = scale * S_t^T q_t,
+ * evaluated chunk-parallel (64 tokens per chunk) on MFMA tiles, plus the steps
+ * around it that the pages describe: the gates beta = sigmoid(b),
+ * g = -exp(A_log) softplus(a + dt_bias); the causal depthwise conv1d + SiLU
+ * over the concatenated q|k|v channels with packed samples that never see each
+ * other (LlamaFactory PR "[v1] support GDN Ulysses cp", Design, decisions 5-7);
+ * and the segment-wise affine state passing S_end = M S_start + b with a chain
+ * of (M, b) reduced in fp32 (sglang fork PR "Qwen3.5 cp - #1", PR body and
+ * Patches; prime-rl PR "feat: hybrid CP for Qwen3.5 MoE", Approach and
+ * Communication-cost table), run here as a single-GPU segment-parallel scan.
+ * The state is stored K x V (prime-rl PR, Summary); the pages' V x K form
+ * S (I - beta k k^T) is its transpose.
+ *
+ * Conventions for every entry point:
+ *  - Tensor arguments are DEVICE pointers to caller-owned, contiguous,
+ *    row-major memory, 16-byte aligned.  The library allocates nothing, keeps
+ *    no global mutable state, and never frees or retains caller memory.
+ *  - Host pointers are named *_host and are read before the call returns.
+ *  - Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *    without waiting for it.  Results are valid once the stream reaches them.
+ *  - Every call returns a gdn_status.  Argument errors are detected on the
+ *    host before anything is enqueued, and then nothing is written.  A launch
+ *    failure returns GDN_ERR_HIP.  No C++ exception crosses this boundary.
+ *  - Packed samples: cu_seqlens (int32 [n_seqs + 1], device) holds sample
+ *    offsets, cu[0] = 0, cu[n_seqs] = total tokens, non-decreasing.  It is
+ *    only accepted with B == 1 (LlamaFactory PR, Design, decision 6).  Kernels
+ *    clamp every offset into [0, T] so a malformed array cannot make them
+ *    access memory out of bounds; pass the same array as cu_seqlens_host to
+ *    have it validated (GDN_ERR_BAD_SEQLENS) before launch.
+ *  - GQA: v-head h reads q/k head h / (H_v / H_qk) (contiguous groups).
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+  GDN_ERR_BAD_SHAPE = 2,    /* negative / inconsistent sizes */
+  GDN_ERR_BAD_DTYPE = 3,    /* dtype code not accepted by this entry point */
+  GDN_ERR_UNSUPPORTED = 4,  /* valid request this build has no kernel for */
+  GDN_ERR_BAD_SEQLENS = 5,  /* cu_seqlens / offsets malformed or with B > 1 */
+  GDN_ERR_HIP = 6           /* a HIP runtime call or kernel launch failed */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Static text for a status code; never NULL. */
+const char* gdn_status_string(int status);
+
+/* ABI version of this header (incremented on any signature change). */
+int gdn_abi_version(void);
+
+/*
+ * Gates (the pages' beta and g): for every token t and v-head h,
+ *     beta[t, h] = 1 / (1 + exp(-b[t, h])),
+ *     g[t, h]    = -exp(A_log[h]) * softplus(a[t, h] + dt_bias[h]),
+ * softplus(x) = log(1 + exp(x)).  a, b, g, beta: fp32 [n_tokens, H];
+ * A_log, dt_bias: fp32 [H].  g and beta are the gate inputs of
+ * gdn_chunk_fwd.  n_tokens == 0 is a no-op.
+ */
+gdn_status gdn_gate_fwd(const float* a, const float* b, const float* A_log,
+                        const float* dt_bias, int64_t n_tokens, int32_t H, float* g,
+                        float* beta, hipStream_t stream);
+
+/*
+ * Causal depthwise conv1d over token-major channels, with optional SiLU and
+ * optional per-head L2 normalisation (LlamaFactory PR, Design, decision 5:
+ * the conv takes cu_seqlens so no sample sees another sample's tokens):
+ *     z[t, c] = bias[c] + sum_{j=0}^{width-1} w[c, j] * x[t - width + 1 + j, c]
+ * with x counted as 0 before the start of t's sample (or batch row);
+ *     y = silu(z) = z / (1 + exp(-z)) when apply_silu, else z;
+ * then, when l2norm_channels > 0, every group of head_dim consecutive
+ * channels in [0, l2norm_channels) (the q and k heads) is divided by
+ * sqrt(sum y^2 + l2_eps).  Accumulation is fp32; y is stored in `dt`.
+ *  x, y      [B, T, channels] in dt (f32 or bf16)
+ *  w         [channels, width] in dt;  bias [channels] in dt or NULL
+ *  cu_seqlens device int32 [n_seqs + 1] or NULL (then B rows of T tokens)
+ *  width in [1, 4]; channels % 8 == 0; l2norm_channels % head_dim == 0;
+ *  head_dim in {16, 32, 64, 128, 256} when l2norm_channels > 0.
+ */
+gdn_status gdn_conv1d_fwd(const void* x, const void* w, const void* bias, gdn_dtype dt,
+                          const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                          int32_t n_seqs, int32_t B, int64_t T, int32_t channels,
+                          int32_t width, int32_t apply_silu, int32_t l2norm_channels,
+                          int32_t head_dim, float l2_eps, void* y, hipStream_t stream);
+
+/*
+ * Chunked gated delta rule forward (chunk size 64).  For every sequence n
+ * (a cu_seqlens sample, or a batch row) and v-head h, starting from
+ * initial_state[n, h] (zero when NULL), the recurrence above runs over the
+ * sequence's tokens; o[t, h] = scale * S_t^T q_t, and final_state[n, h]
+ * receives the state after the last token (the sglang PR hands this state to
+ * the decode path).  The chunk grid is anchored at each sequence start; a
+ * zero-length sequence copies initial_state to final_state.
+ *  q, k   [B, T, H_qk, K] in in_dt        v   [B, T, H_v, V] in in_dt
+ *  g,beta fp32 [B, T, H_v]                o   [B, T, H_v, V] in o_dt
+ *  initial_state, final_state fp32 [N, H_v, K, V], N = n_seqs (packed) or B;
+ *  either may be NULL.
+ *  *_token_stride: elements between consecutive tokens of q, k, v (0 = dense:
+ *  H_qk*K, H_qk*K, H_v*V).  A larger stride reads q, k, v straight out of a
+ *  wider token-major buffer, e.g. the conv1d output [T, q|k|v channels];
+ *  strides must be multiples of 8 and at least the dense size.  The B
+ *  batch rows are then B*T tokens at that stride.
+ * Kernels: in_dt = BF16 runs bf16 MFMA tiles with fp32 accumulation, an fp32
+ * state, and split-bf16 operands where fp32 intermediates meet the matrix
+ * cores (needs K = 128, V % 128 == 0); in_dt = F32 runs an fp32 vector-ALU
+ * kernel (K in {32, 64}, V % 32 == 0).
+ * o_dt is F32 or BF16 (round to nearest even).
+ */
+gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, gdn_dtype in_dt,
+                         int64_t q_token_stride, int64_t k_token_stride, int64_t v_token_stride,
+                         const float* g, const float* beta, float scale,
+                         const float* initial_state, const int32_t* cu_seqlens,
+                         const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t B, int64_t T,
+                         int32_t H_qk, int32_t H_v, int32_t K, int32_t V, void* o,
+                         gdn_dtype o_dt, float* final_state, hipStream_t stream);
+
+/*
+ * Segment state scan: one long sequence cut into P contiguous segments
+ * [seg_offsets[i], seg_offsets[i+1]) of the token arrays (the sglang PR's
+ * per-rank segments, here on one GPU).  Pass 1 computes, for every segment
+ * and v-head, the affine map of the segment, S_end = M S_start + b
+ * (M: K x K, the product of the segment's per-token transitions; b: the state
+ * reached from a zero start), by running the chunked rule on the augmented
+ * state [M | b] started at [I | 0].  The maps are then composed in fp32,
+ * S_start,0 = initial_state (zero when NULL), S_start,i+1 = M_i S_start,i + b_i.
+ *  k [T, H_qk, K], v [T, H_v, V] in in_dt (BF16, K = 128, V % 128 == 0),
+ *  token strides as in gdn_chunk_fwd (0 = dense);
+ *  g, beta fp32 [T, H_v]; seg_offsets device int32 [P + 1] (host mirror
+ *  seg_offsets_host optional, validated when given);
+ *  initial_state fp32 [H_v, K, V] or NULL;
+ *  M fp32 [P, H_v, K, K] and b fp32 [P, H_v, K, V] (outputs, required);
+ *  seg_initial_states fp32 [P, H_v, K, V] (output, required);
+ *  final_state fp32 [H_v, K, V] or NULL (the state after the last segment).
+ * Running gdn_chunk_fwd with cu_seqlens = seg_offsets (seg_offsets[0] = 0,
+ * seg_offsets[P] = T) and initial_state = seg_initial_states is pass 2: it
+ * yields every output of the unsegmented run.
+ */
+gdn_status gdn_segment_state_scan(const void* k, const void* v, gdn_dtype in_dt,
+                                  int64_t k_token_stride, int64_t v_token_stride,
+                                  const float* g, const float* beta,
+                                  const int32_t* seg_offsets, const int32_t* seg_offsets_host,
+                                  int32_t P, const float* initial_state, int64_t T,
+                                  int32_t H_qk, int32_t H_v, int32_t K, int32_t V, float* M,
+                                  float* b, float* seg_initial_states, float* final_state,
+                                  hipStream_t stream);
+
+/*
+ * Segment-parallel forward of one long sequence: gdn_segment_state_scan
+ * (pass 1 + fp32 composition) followed by gdn_chunk_fwd over the segments
+ * started from the composed states (pass 2).  Same q/k/v/g/beta/o layouts as
+ * gdn_chunk_fwd with B = 1; seg_offsets as above with seg_offsets[0] = 0 and
+ * seg_offsets[P] = T.  final_state fp32 [H_v, K, V] or NULL.
+ * workspace: device memory of at least gdn_segmented_workspace_bytes(...)
+ * bytes, used for M, b, the composed starts and the per-segment final states;
+ * its contents on entry do not matter.
+ */
+size_t gdn_segmented_workspace_bytes(int32_t P, int32_t H_v, int32_t K, int32_t V);
+
+gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
+                                   gdn_dtype in_dt, int64_t q_token_stride,
+                                   int64_t k_token_stride, int64_t v_token_stride,
+                                   const float* g, const float* beta,
+                                   float scale, const float* initial_state,
+                                   const int32_t* seg_offsets, const int32_t* seg_offsets_host,
+                                   int32_t P, int64_t T, int32_t H_qk, int32_t H_v, int32_t K,
+                                   int32_t V, void* o, gdn_dtype o_dt, float* final_state,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

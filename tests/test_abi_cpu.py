@@ -1,0 +1,143 @@
+"""The C ABI library: loads, exports every symbol include/gdn.h declares, and
+rejects bad arguments on the host before touching a GPU (so these run without
+one: validation happens before any HIP call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_linear_chunk_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+OK, NULLP, SHAPE, DTYPE, UNSUP, SEQ = 0, 1, 2, 3, 4, 5
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.library_path()):
+        from gated_deltanet_linear_chunk_amd import build
+
+        build.build()
+    return gdn.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert set(declared) == set(gdn.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    for s in range(7):
+        assert lib.gdn_status_string(s)
+    assert b"unknown" in lib.gdn_status_string(99)
+    assert lib.gdn_abi_version() == 1
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation first
+
+
+def _chunk(lib, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, in_dt=1, qs=0, ks=0, vs=0, g=FAKE, beta=FAKE, scale=1.0, s0=None, cu=None,
+                cu_host=None,
+                n_seqs=0, B=1, T=64, Hqk=16, Hv=32, K=128, V=128, o=FAKE, o_dt=0, fin=None, stream=None)
+    args.update(kw)
+    return lib.gdn_chunk_fwd(*args.values())
+
+
+def test_chunk_validation(lib):
+    assert _chunk(lib, q=None) == NULLP
+    assert _chunk(lib, o=None) == NULLP
+    assert _chunk(lib, in_dt=7) == DTYPE
+    assert _chunk(lib, o_dt=5) == DTYPE
+    assert _chunk(lib, B=0) == SHAPE
+    assert _chunk(lib, T=-1) == SHAPE
+    assert _chunk(lib, qs=100) == SHAPE  # below the dense 16 * 128
+    assert _chunk(lib, vs=32 * 128 + 4) == SHAPE  # not a multiple of 8
+    assert _chunk(lib, ks=8192, qs=8192, vs=8192, q=None) == NULLP  # a wide stride itself is fine
+    assert _chunk(lib, Hqk=3) == SHAPE  # 32 % 3 != 0
+    assert _chunk(lib, K=64) == UNSUP  # bf16 kernel needs K = 128
+    assert _chunk(lib, V=96) == UNSUP
+    assert _chunk(lib, in_dt=0, K=128) == UNSUP  # fp32 kernel: K in {32, 64}
+    assert _chunk(lib, in_dt=0, K=32, V=48) == UNSUP
+    assert _chunk(lib, cu=FAKE, n_seqs=2, B=2) == SEQ  # cu_seqlens needs B == 1
+    assert _chunk(lib, cu=FAKE, n_seqs=0) == SEQ
+    bad = (ctypes.c_int32 * 3)(0, 40, 30)  # decreasing
+    assert _chunk(lib, cu=FAKE, cu_host=bad, n_seqs=2) == SEQ
+    short = (ctypes.c_int32 * 3)(0, 30, 60)  # does not end at T
+    assert _chunk(lib, cu=FAKE, cu_host=short, n_seqs=2) == SEQ
+    start = (ctypes.c_int32 * 3)(4, 30, 64)
+    assert _chunk(lib, cu=FAKE, cu_host=start, n_seqs=2) == SEQ
+    # nothing to do: no tokens and no state requested
+    assert _chunk(lib, T=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
+
+
+def test_conv_validation(lib):
+    def conv(**kw):
+        a = dict(x=FAKE, w=FAKE, bias=None, dt=1, cu=None, cu_host=None, n=0, B=1, T=32, C=8192, W=4, silu=1,
+                 l2=4096, hd=128, eps=1e-6, y=FAKE, stream=None)
+        a.update(kw)
+        return lib.gdn_conv1d_fwd(*a.values())
+
+    assert conv(x=None) == NULLP
+    assert conv(dt=3) == DTYPE
+    assert conv(C=100) == SHAPE  # channels % 8
+    assert conv(W=5) == UNSUP
+    assert conv(W=0) == UNSUP
+    assert conv(l2=100) == SHAPE
+    assert conv(hd=96) == UNSUP
+    assert conv(cu=FAKE, n=2, B=2) == SEQ
+    assert conv(cu=FAKE, n=2, cu_host=(ctypes.c_int32 * 3)(0, 10, 31)) == SEQ
+    assert conv(T=0, x=None, w=None, y=None) == OK
+
+
+def test_gate_and_segment_validation(lib):
+    assert lib.gdn_gate_fwd(FAKE, FAKE, FAKE, FAKE, 10, 0, FAKE, FAKE, None) == SHAPE
+    assert lib.gdn_gate_fwd(None, FAKE, FAKE, FAKE, 10, 4, FAKE, FAKE, None) == NULLP
+    assert lib.gdn_gate_fwd(None, None, None, None, 0, 4, None, None, None) == OK
+
+    def scan(**kw):
+        a = dict(k=FAKE, v=FAKE, dt=1, ks=0, vs=0, g=FAKE, beta=FAKE, off=FAKE, off_host=None, P=8, s0=None, T=4096,
+                 Hqk=16,
+                 Hv=32, K=128, V=128, M=FAKE, b=FAKE, starts=FAKE, fin=None, stream=None)
+        a.update(kw)
+        return lib.gdn_segment_state_scan(*a.values())
+
+    assert scan(off=None) == NULLP
+    assert scan(ks=12) == SHAPE
+    assert scan(M=None) == NULLP
+    assert scan(dt=0) == UNSUP
+    assert scan(P=0) == SHAPE
+    assert scan(V=200) == UNSUP
+    off = (ctypes.c_int32 * 3)(0, 5000, 4096)
+    assert scan(P=2, off_host=off) == SEQ
+    assert lib.gdn_segmented_workspace_bytes(8, 32, 128, 128) == 4 * 8 * 32 * 128 * (128 + 256)
+    assert lib.gdn_segmented_workspace_bytes(0, 32, 128, 128) == 0
+    seg = lib.gdn_chunk_fwd_segmented
+    ws = lib.gdn_segmented_workspace_bytes(2, 32, 128, 128)
+    good = (ctypes.c_int32 * 3)(0, 2048, 4096)
+    assert seg(FAKE, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE, 1.0, None, FAKE, good, 2, 4096, 16, 32, 128, 128, FAKE, 0, None,
+               FAKE, ws - 1, None) == SHAPE
+    assert seg(FAKE, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE, 1.0, None, FAKE, good, 2, 4096, 16, 32, 128, 128, FAKE, 0, None,
+               None, ws, None) == NULLP
+    notfull = (ctypes.c_int32 * 3)(0, 2048, 4000)
+    assert seg(FAKE, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE, 1.0, None, FAKE, notfull, 2, 4096, 16, 32, 128, 128, FAKE, 0, None,
+               FAKE, ws, None) == SEQ
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(4, 8)
+    with pytest.raises(ValueError):
+        gdn.gdn_conv1d_fwd(x, torch.zeros(8, 4))

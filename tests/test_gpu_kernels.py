@@ -1,0 +1,264 @@
+"""GPU parity at small sizes: every kernel against the fp64 oracle on the same
+seeded inputs (sizes span several 64-token chunks and ragged tails), plus the
+bit-exact properties (packed == per-sample, determinism, untouched memory).
+
+The GPU side derives g and beta with its own gate kernel; the oracle derives
+them in fp64 from the same raw draws.
+"""
+
+import numpy as np
+import pytest
+
+import gdn_inputs
+import oracle
+from parity_util import assert_bf16, assert_f32, dev, host, stats
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU-only machines skip via -m "not gpu"
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import gated_deltanet_linear_chunk_amd as gdn  # noqa: E402
+
+
+def _gpu_gates(d):
+    g, beta = gdn.gdn_gate_fwd(dev(d["a"]), dev(d["b"]), dev(d["A_log"]), dev(d["dt_bias"]))
+    return g, beta
+
+
+def _oracle_gates(d):
+    return oracle.gates(d["a"], d["b"], d["A_log"], d["dt_bias"])
+
+
+def _run_chunk(d, dtype, s0=None, o_dtype=None, use_cu=True):
+    q = dev(d["q"], dtype)[None]
+    k = dev(d["k"], dtype)[None]
+    v = dev(d["v"], dtype)[None]
+    g, beta = _gpu_gates(d)
+    cu = dev(d["cu_seqlens"], "i32") if use_cu else None
+    o, fin = gdn.gdn_chunk_fwd(
+        q, k, v, g[None], beta[None], initial_state=None if s0 is None else dev(s0),
+        cu_seqlens=cu, cu_seqlens_host=d["cu_seqlens"] if use_cu else None, o_dtype=o_dtype,
+    )
+    torch.cuda.synchronize()
+    return o[0], fin
+
+
+def _oracle_chunk(d, s0=None):
+    g, beta = _oracle_gates(d)
+    return oracle.recurrence(d["q"], d["k"], d["v"], g, beta, s0, d["cu_seqlens"])
+
+
+# --------------------------------------------------------------------------- #
+def test_gate_kernel():
+    rng = np.random.default_rng(7)
+    a = (rng.standard_normal((300, 8)) * 4).astype(np.float32)
+    b = (rng.standard_normal((300, 8)) * 4).astype(np.float32)
+    A_log = rng.uniform(-3, 3, 8).astype(np.float32)
+    dt = rng.uniform(-1, 1, 8).astype(np.float32)
+    g, beta = gdn.gdn_gate_fwd(dev(a), dev(b), dev(A_log), dev(dt))
+    go, bo = oracle.gates(a, b, A_log, dt)
+    np.testing.assert_allclose(host(g), go, rtol=2e-6, atol=1e-30)
+    np.testing.assert_allclose(host(beta), bo, rtol=2e-6, atol=1e-30)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("l2", [False, True])
+def test_conv1d_packed(dtype, l2):
+    w = gdn_inputs.Workload("conv", 11, 300, 5, 2, 4, 128, 64, dtype, conv_width=4, lengths=[1, 63, 64, 2, 170])
+    d = gdn_inputs.draw(w)
+    C = d["x"].shape[1]
+    l2ch = 2 * 2 * 128 if l2 else 0
+    y = gdn.gdn_conv1d_fwd(dev(d["x"], dtype), dev(d["conv_w"], dtype), dev(d["conv_bias"], dtype),
+                           cu_seqlens=dev(d["cu_seqlens"], "i32"), cu_seqlens_host=d["cu_seqlens"],
+                           l2norm_channels=l2ch, head_dim=128)
+    ref = oracle.conv1d(d["x"], d["conv_w"], d["conv_bias"], d["cu_seqlens"])
+    if l2:
+        q, k, _ = oracle.split_channels(ref, 2, 4, 128, 64)
+        ref = ref.copy()
+        ref[:, :l2ch] = np.concatenate([oracle.l2norm(q).reshape(300, -1), oracle.l2norm(k).reshape(300, -1)], 1)
+    got = host(y)
+    assert got.shape == (300, C)
+    if dtype == "f32":
+        np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-5)
+    else:
+        err = np.abs(got - ref)
+        assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-5), float((err - 2.0 ** -8 * np.abs(ref)).max())
+
+
+def test_conv1d_batched_rows_and_width():
+    rng = np.random.default_rng(12)
+    B, T, C = 3, 70, 256
+    x = gdn_inputs.bf16_round(rng.standard_normal((B, T, C)).astype(np.float32))
+    for W in (1, 2, 3, 4):
+        wt = gdn_inputs.bf16_round(rng.standard_normal((C, W)).astype(np.float32))
+        y = gdn.gdn_conv1d_fwd(dev(x, "bf16"), dev(wt, "bf16"), None, apply_silu=False)
+        cu = np.arange(B + 1) * T
+        ref = oracle.conv1d(x.reshape(B * T, C), wt, None, cu, silu=False).reshape(B, T, C)
+        err = np.abs(host(y) - ref)
+        assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-5)
+
+
+# --------------------------------------------------------------------------- #
+def test_chunk_fp32_tiny_workload():
+    d = gdn_inputs.draw(gdn_inputs.WORKLOADS["tiny_fp32_T256_H2_K32"])
+    o, fin = _run_chunk(d, "f32")
+    oref, fref = _oracle_chunk(d)
+    assert_f32(host(o), oref, "o")
+    assert_f32(host(fin), fref, "final")
+
+
+@pytest.mark.parametrize("K,V", [(32, 32), (64, 64), (32, 96)])
+def test_chunk_fp32_packed_with_state(K, V):
+    d = gdn_inputs.small(21, [1, 64, 65, 130, 7], 2, 4, K, V, "f32")
+    N = 5
+    s0 = (np.random.default_rng(3).standard_normal((N, 4, K, V)) * 0.5).astype(np.float32)
+    o, fin = _run_chunk(d, "f32", s0)
+    oref, fref = _oracle_chunk(d, s0)
+    assert_f32(host(o), oref, "o")
+    assert_f32(host(fin), fref, "final")
+
+
+GATES = {
+    "fast": dict(A_log_range=(0.0, float(np.log(16.0)))),
+    "slow": dict(A_log_range=(-2.0, 0.0)),
+    "very_slow": dict(A_log_range=(-8.0, -4.0)),
+    "zero_decay": dict(gate_kind="zero_decay"),
+}
+
+
+@pytest.mark.parametrize("gates", list(GATES))
+@pytest.mark.parametrize("V", [128, 256])
+def test_chunk_bf16_packed(gates, V):
+    lengths = [1, 63, 64, 65, 127, 300]
+    d = gdn_inputs.small(31, lengths, 2, 4, 128, V, "bf16", **GATES[gates])
+    s0 = (np.random.default_rng(4).standard_normal((len(lengths), 4, 128, V)) * 0.05).astype(np.float32)
+    o, fin = _run_chunk(d, "bf16", s0, o_dtype=torch.float32)
+    oref, fref = _oracle_chunk(d, s0)
+    so = assert_bf16(host(o), oref, "o")
+    sf = assert_bf16(host(fin), fref, "final")
+    print("\nbf16 %s V=%d o %s final %s" % (gates, V, so, sf))
+
+
+def test_chunk_bf16_store_o_bf16():
+    d = gdn_inputs.small(32, [200, 57], 1, 2, 128, 128, "bf16")
+    o, _ = _run_chunk(d, "bf16", o_dtype=torch.bfloat16)
+    oref, _ = _oracle_chunk(d)
+    assert_bf16(host(o), oref, "o bf16", bf16_store=True)
+
+
+def test_chunk_bf16_batched_rows_equal_packed():
+    """B rows without cu_seqlens give the same bits as the packed form."""
+    lengths = [128, 128, 128]
+    d = gdn_inputs.small(33, lengths, 2, 4, 128, 128, "bf16")
+    s0 = (np.random.default_rng(5).standard_normal((3, 4, 128, 128)) * 0.02).astype(np.float32)
+    o_p, f_p = _run_chunk(d, "bf16", s0, o_dtype=torch.float32)
+    g, beta = _gpu_gates(d)
+    q = dev(d["q"], "bf16").reshape(3, 128, 2, 128)
+    k = dev(d["k"], "bf16").reshape(3, 128, 2, 128)
+    v = dev(d["v"], "bf16").reshape(3, 128, 4, 128)
+    o_b, f_b = gdn.gdn_chunk_fwd(q, k, v, g.reshape(3, 128, 4), beta.reshape(3, 128, 4),
+                                 initial_state=dev(s0), o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o_b.reshape(o_p.shape), o_p)
+    assert torch.equal(f_b, f_p)
+
+
+def test_chunk_bf16_packed_equals_per_sample_bitwise():
+    lengths = [65, 1, 130, 64]
+    d = gdn_inputs.small(34, lengths, 2, 4, 128, 128, "bf16", A_log_range=(-2.0, 0.0))
+    o, fin = _run_chunk(d, "bf16", o_dtype=torch.float32)
+    cu = d["cu_seqlens"]
+    g, beta = _gpu_gates(d)
+    for n in range(len(lengths)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        on, fn = gdn.gdn_chunk_fwd(dev(d["q"][a:b], "bf16")[None], dev(d["k"][a:b], "bf16")[None],
+                                   dev(d["v"][a:b], "bf16")[None], g[a:b][None].contiguous(),
+                                   beta[a:b][None].contiguous(), o_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(on[0], o[a:b]), n
+        assert torch.equal(fn[0], fin[n]), n
+
+
+def test_chunk_bf16_deterministic_and_leak_free():
+    lengths = [100, 150]
+    d = gdn_inputs.small(35, lengths, 2, 4, 128, 128, "bf16", A_log_range=(-2.0, 0.0))
+    o1, f1 = _run_chunk(d, "bf16", o_dtype=torch.float32)
+    o2, f2 = _run_chunk(d, "bf16", o_dtype=torch.float32)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+    d2 = dict(d)
+    d2["v"] = d["v"].copy()
+    d2["v"][100:] = gdn_inputs.bf16_round(d2["v"][100:] + 1.0)
+    o3, f3 = _run_chunk(d2, "bf16", o_dtype=torch.float32)
+    assert torch.equal(o3[:100], o1[:100]) and torch.equal(f3[0], f1[0])
+    assert not torch.equal(o3[100:], o1[100:])
+
+
+def test_chunk_zero_length_samples_keep_state():
+    lengths = [0, 70, 0]
+    d = gdn_inputs.small(36, lengths, 1, 2, 128, 128, "bf16")
+    s0 = (np.random.default_rng(6).standard_normal((3, 2, 128, 128))).astype(np.float32)
+    o, fin = _run_chunk(d, "bf16", s0, o_dtype=torch.float32)
+    f = host(fin)
+    np.testing.assert_array_equal(f[0], s0[0])
+    np.testing.assert_array_equal(f[2], s0[2])
+    oref, fref = _oracle_chunk(d, s0)
+    assert_bf16(host(o), oref, "o")
+
+
+def test_chunk_scale_argument():
+    d = gdn_inputs.small(37, [90], 1, 2, 128, 128, "bf16")
+    g, beta = _gpu_gates(d)
+    args = (dev(d["q"], "bf16")[None], dev(d["k"], "bf16")[None], dev(d["v"], "bf16")[None], g[None], beta[None])
+    o1, _ = gdn.gdn_chunk_fwd(*args, o_dtype=torch.float32)
+    o2, _ = gdn.gdn_chunk_fwd(*args, scale=0.25, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o1 * 0.25)
+
+
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("gates", ["zero_decay", "very_slow", "fast"])
+def test_segment_state_scan(gates):
+    T = 512
+    d = gdn_inputs.small(41, [T], 2, 4, 128, 128, "bf16", **GATES[gates])
+    off = np.array([0, 64, 100, 256, 257, 512], dtype=np.int32)
+    s0 = (np.random.default_rng(8).standard_normal((4, 128, 128)) * 0.1).astype(np.float32)
+    g, beta = _gpu_gates(d)
+    M, b, starts, fin = gdn.gdn_segment_state_scan(dev(d["k"], "bf16"), dev(d["v"], "bf16"), g, beta,
+                                                   dev(off, "i32"), off, initial_state=dev(s0))
+    torch.cuda.synchronize()
+    go, bo = _oracle_gates(d)
+    Mref, bref = oracle.segment_affine(d["k"], d["v"], go, bo, off, Hqk=2)
+    sref, fref = oracle.chain(Mref, bref, s0)
+    for i in range(len(off) - 1):
+        if gates != "fast":  # fast gates drive M below the fp32 range; nothing to compare
+            assert_bf16(host(M[i]), Mref[i], "M[%d]" % i)
+        assert_bf16(host(b[i]), bref[i], "b[%d]" % i)
+        assert_bf16(host(starts[i]), sref[i], "start[%d]" % i)
+    assert_bf16(host(fin), fref, "final")
+
+
+@pytest.mark.parametrize("gates", ["zero_decay", "slow"])
+def test_segmented_forward_matches_oracle(gates):
+    T = 640
+    d = gdn_inputs.small(42, [T], 2, 4, 128, 128, "bf16", **GATES[gates])
+    off = np.array([0, 128, 320, 321, 640], dtype=np.int32)
+    s0 = (np.random.default_rng(9).standard_normal((1, 4, 128, 128)) * 0.05).astype(np.float32)
+    g, beta = _gpu_gates(d)
+    o, fin = gdn.gdn_chunk_fwd_segmented(dev(d["q"], "bf16")[None], dev(d["k"], "bf16")[None],
+                                         dev(d["v"], "bf16")[None], g[None], beta[None], dev(off, "i32"), off,
+                                         initial_state=dev(s0[0]), o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    oref, fref = _oracle_chunk(d, s0)
+    assert_bf16(host(o[0]), oref, "o")
+    assert_bf16(host(fin), fref[0], "final")
+    # one segment is exactly the plain path
+    one = np.array([0, T], dtype=np.int32)
+    o1, _ = gdn.gdn_chunk_fwd_segmented(dev(d["q"], "bf16")[None], dev(d["k"], "bf16")[None],
+                                        dev(d["v"], "bf16")[None], g[None], beta[None], dev(one, "i32"), one,
+                                        initial_state=dev(s0[0]), o_dtype=torch.float32)
+    o2, _ = gdn.gdn_chunk_fwd(dev(d["q"], "bf16")[None], dev(d["k"], "bf16")[None], dev(d["v"], "bf16")[None],
+                              g[None], beta[None], initial_state=dev(s0), o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)

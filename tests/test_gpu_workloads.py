@@ -1,0 +1,160 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the
+benchmark times.  The oracle recomputes a sample of (sequence, head) units one
+by one (each unit is independent), so these finish in seconds; every other
+unit is checked for finiteness.  Tolerances as in parity_util.
+"""
+
+import numpy as np
+import pytest
+
+import gdn_inputs
+import oracle
+from parity_util import assert_bf16, assert_f32, dev, host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import gated_deltanet_linear_chunk_amd as gdn  # noqa: E402
+
+
+def _units(N, Hv, n, seed):
+    rng = np.random.default_rng(seed)
+    idx = rng.choice(N * Hv, size=min(n, N * Hv), replace=False)
+    return sorted((int(i // Hv), int(i % Hv)) for i in idx)
+
+
+def _oracle_unit(q, k, v, g, beta, cu, n, h, Hqk, Hv, s0=None):
+    a, b = int(cu[n]), int(cu[n + 1])
+    hq = h // (Hv // Hqk)
+    s = None if s0 is None else s0[n : n + 1, h : h + 1]
+    return oracle.recurrence(q[a:b, hq : hq + 1], k[a:b, hq : hq + 1], v[a:b, h : h + 1], g[a:b, h : h + 1],
+                             beta[a:b, h : h + 1], s, threads=0)
+
+
+def _pipeline(d, w):
+    """conv1d (+ q/k L2 norm) -> strided q, k, v views -> gates -> chunk rule."""
+    T = w.total_tokens
+    Hqk, Hv, K, V = w.Hqk, w.Hv, w.K, w.V
+    C = d["x"].shape[1]
+    if w.batch_rows > 1:
+        x = dev(d["x"], "bf16").reshape(w.batch_rows, T // w.batch_rows, C)
+        y = gdn.gdn_conv1d_fwd(x, dev(d["conv_w"], "bf16"), dev(d["conv_bias"], "bf16"),
+                               l2norm_channels=2 * Hqk * K, head_dim=K)
+        B, L = w.batch_rows, T // w.batch_rows
+        cu = None
+    else:
+        cu = dev(d["cu_seqlens"], "i32")
+        y = gdn.gdn_conv1d_fwd(dev(d["x"], "bf16"), dev(d["conv_w"], "bf16"), dev(d["conv_bias"], "bf16"),
+                               cu_seqlens=cu, cu_seqlens_host=d["cu_seqlens"], l2norm_channels=2 * Hqk * K,
+                               head_dim=K)
+        B, L = 1, T
+    y = y.reshape(B, L, C)
+    q = y[..., : Hqk * K].unflatten(-1, (Hqk, K))
+    k = y[..., Hqk * K : 2 * Hqk * K].unflatten(-1, (Hqk, K))
+    v = y[..., 2 * Hqk * K :].unflatten(-1, (Hv, V))
+    g, beta = gdn.gdn_gate_fwd(dev(d["a"]).reshape(B, L, Hv), dev(d["b"]).reshape(B, L, Hv), dev(d["A_log"]),
+                               dev(d["dt_bias"]))
+    s0 = dev(d["s0"]) if "s0" in d else None
+    o, fin = gdn.gdn_chunk_fwd(q, k, v, g, beta, initial_state=s0, cu_seqlens=cu,
+                               cu_seqlens_host=None if cu is None else d["cu_seqlens"], o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    return o.reshape(T, Hv, V), fin
+
+
+@pytest.mark.parametrize("name", ["packed_varlen_bf16_T8192_N8_Hv32_K128", "batched_prefill_bf16_B8_T4096_Hv32_K128"])
+def test_pipeline_workload(name):
+    """conv1d + SiLU + L2 norm + gates + chunk rule, end to end."""
+    w = gdn_inputs.WORKLOADS[name]
+    d = gdn_inputs.draw(w, with_qkv=False)
+    o, fin = _pipeline(d, w)
+    assert torch.isfinite(o).all() and torch.isfinite(fin).all()
+    qr, kr, vr = oracle.pipeline_activations(d["x"], d["conv_w"], d["conv_bias"], d["cu_seqlens"], w.Hqk, w.Hv,
+                                             w.K, w.V)
+    g, beta = oracle.gates(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    s0 = d.get("s0")
+    cu = d["cu_seqlens"]
+    N = len(cu) - 1
+    oh, fh = host(o), host(fin)
+    for n, h in _units(N, w.Hv, 6, 1):
+        oref, fref = _oracle_unit(qr, kr, vr, g, beta, cu, n, h, w.Hqk, w.Hv, s0)
+        a, b = int(cu[n]), int(cu[n + 1])
+        assert_bf16(oh[a:b, h], oref[:, 0], "o unit %d,%d" % (n, h))
+        assert_bf16(fh[n, h], fref[0, 0], "final unit %d,%d" % (n, h))
+
+
+def test_chunk_only_packed_workload():
+    """The packed workload with q/k/v drawn directly (the chunk rule alone)."""
+    w = gdn_inputs.WORKLOADS["packed_varlen_bf16_T8192_N8_Hv32_K128"]
+    d = gdn_inputs.draw(w)
+    g, beta = gdn.gdn_gate_fwd(dev(d["a"]), dev(d["b"]), dev(d["A_log"]), dev(d["dt_bias"]))
+    o, fin = gdn.gdn_chunk_fwd(dev(d["q"], "bf16")[None], dev(d["k"], "bf16")[None], dev(d["v"], "bf16")[None],
+                               g[None], beta[None], cu_seqlens=dev(d["cu_seqlens"], "i32"),
+                               cu_seqlens_host=d["cu_seqlens"], o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    go, bo = oracle.gates(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    cu = d["cu_seqlens"]
+    oh, fh = host(o[0]), host(fin)
+    for n, h in _units(len(cu) - 1, w.Hv, 6, 2):
+        oref, fref = _oracle_unit(d["q"], d["k"], d["v"], go, bo, cu, n, h, w.Hqk, w.Hv)
+        a, b = int(cu[n]), int(cu[n + 1])
+        assert_bf16(oh[a:b, h], oref[:, 0], "o unit %d,%d" % (n, h))
+        assert_bf16(fh[n, h], fref[0, 0], "final unit %d,%d" % (n, h))
+
+
+def test_long_segmented_workload():
+    """32768 tokens in 8 segments: pass 1, fp32 chain, pass 2 == unsegmented, == oracle."""
+    w = gdn_inputs.WORKLOADS["long_segmented_bf16_T32768_P8_Hv32_K128"]
+    d = gdn_inputs.draw(w)
+    q, k, v = dev(d["q"], "bf16")[None], dev(d["k"], "bf16")[None], dev(d["v"], "bf16")[None]
+    g, beta = gdn.gdn_gate_fwd(dev(d["a"]), dev(d["b"]), dev(d["A_log"]), dev(d["dt_bias"]))
+    off = d["seg_offsets"]
+    o_s, f_s = gdn.gdn_chunk_fwd_segmented(q, k, v, g[None], beta[None], dev(off, "i32"), off,
+                                           o_dtype=torch.float32)
+    o_u, f_u = gdn.gdn_chunk_fwd(q, k, v, g[None], beta[None], o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    go, bo = oracle.gates(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    heads = [0, 7, 18, 31]
+    T = w.total_tokens
+    for h in heads:
+        hq = h // 2
+        oref, fref = oracle.recurrence(d["q"][:, hq : hq + 1], d["k"][:, hq : hq + 1], d["v"][:, h : h + 1],
+                                       go[:, h : h + 1], bo[:, h : h + 1])
+        assert_bf16(host(o_s[0, :, h]), oref[:, 0], "segmented o head %d" % h)
+        assert_bf16(host(o_u[0, :, h]), oref[:, 0], "unsegmented o head %d" % h)
+        assert_bf16(host(f_s[h]), fref[0, 0], "segmented final head %d" % h)
+        assert_bf16(host(f_u[0, h]), fref[0, 0], "unsegmented final head %d" % h)
+    assert_bf16(host(o_s), host(o_u), "segmented vs unsegmented, all heads")
+
+
+def test_wide_state_workload():
+    """H = 64, K = 128, V = 256 (two 128-column slices per head), 4 packed samples, slow gates."""
+    w = gdn_inputs.WORKLOADS["wide_state_bf16_T32768_N4_H64_K128_V256"]
+    d = gdn_inputs.draw(w)
+    g, beta = gdn.gdn_gate_fwd(dev(d["a"]), dev(d["b"]), dev(d["A_log"]), dev(d["dt_bias"]))
+    cu = d["cu_seqlens"]
+    o, fin = gdn.gdn_chunk_fwd(dev(d["q"], "bf16")[None], dev(d["k"], "bf16")[None], dev(d["v"], "bf16")[None],
+                               g[None], beta[None], cu_seqlens=dev(cu, "i32"), cu_seqlens_host=cu,
+                               o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(fin).all()
+    go, bo = oracle.gates(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    for n, h in _units(len(cu) - 1, w.Hv, 4, 3):
+        oref, fref = _oracle_unit(d["q"], d["k"], d["v"], go, bo, cu, n, h, w.Hqk, w.Hv)
+        a, b = int(cu[n]), int(cu[n + 1])
+        assert_bf16(host(o[0, a:b, h]), oref[:, 0], "o unit %d,%d" % (n, h))
+        assert_bf16(host(fin[n, h]), fref[0, 0], "final unit %d,%d" % (n, h))
+
+
+def test_tiny_fp32_workload_full():
+    w = gdn_inputs.WORKLOADS["tiny_fp32_T256_H2_K32"]
+    d = gdn_inputs.draw(w)
+    g, beta = gdn.gdn_gate_fwd(dev(d["a"]), dev(d["b"]), dev(d["A_log"]), dev(d["dt_bias"]))
+    o, fin = gdn.gdn_chunk_fwd(dev(d["q"])[None], dev(d["k"])[None], dev(d["v"])[None], g[None], beta[None])
+    torch.cuda.synchronize()
+    go, bo = oracle.gates(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    oref, fref = oracle.recurrence(d["q"], d["k"], d["v"], go, bo)
+    assert_f32(host(o[0]), oref, "o")
+    assert_f32(host(fin), fref, "final")
