@@ -24,6 +24,8 @@ __all__ = [
     "gdn_segment_state_scan",
     "gdn_chunk_fwd_segmented",
     "gdn_segmented_workspace_bytes",
+    "gdn_chunk_fwd_workspace_bytes",
+    "gdn_segment_state_scan_workspace_bytes",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -38,7 +40,9 @@ EXPORTED_SYMBOLS = (
     "gdn_abi_version",
     "gdn_gate_fwd",
     "gdn_conv1d_fwd",
+    "gdn_chunk_fwd_workspace_bytes",
     "gdn_chunk_fwd",
+    "gdn_segment_state_scan_workspace_bytes",
     "gdn_segment_state_scan",
     "gdn_segmented_workspace_bytes",
     "gdn_chunk_fwd_segmented",
@@ -75,11 +79,15 @@ def load_library():
     lib.gdn_abi_version.restype = ctypes.c_int
     lib.gdn_gate_fwd.argtypes = [P, P, P, P, i64, i32, P, P, P]
     lib.gdn_conv1d_fwd.argtypes = [P, P, P, ctypes.c_int, P, P, i32, i32, i64, i32, i32, i32, i32, i32, f32, P, P]
+    lib.gdn_chunk_fwd_workspace_bytes.argtypes = [ctypes.c_int, i64, i32, i32, i32, i32]
+    lib.gdn_chunk_fwd_workspace_bytes.restype = sz
     lib.gdn_chunk_fwd.argtypes = [P, P, P, ctypes.c_int, i64, i64, i64, P, P, f32, P, P, P, i32, i32, i64, i32, i32,
-                                  i32, i32, P, ctypes.c_int, P, P]
+                                  i32, i32, P, ctypes.c_int, P, P, sz, P]
+    lib.gdn_segment_state_scan_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
+    lib.gdn_segment_state_scan_workspace_bytes.restype = sz
     lib.gdn_segment_state_scan.argtypes = [P, P, ctypes.c_int, i64, i64, P, P, P, P, i32, P, i64, i32, i32, i32, i32,
-                                           P, P, P, P, P]
-    lib.gdn_segmented_workspace_bytes.argtypes = [i32, i32, i32, i32]
+                                           P, P, P, P, P, sz, P]
+    lib.gdn_segmented_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
     lib.gdn_segmented_workspace_bytes.restype = sz
     lib.gdn_chunk_fwd_segmented.argtypes = [P, P, P, ctypes.c_int, i64, i64, i64, P, P, f32, P, P, P, i32, i64, i32,
                                             i32, i32, i32, P, ctypes.c_int, P, P, sz, P]
@@ -210,8 +218,25 @@ def gdn_conv1d_fwd(x, w, bias=None, cu_seqlens=None, cu_seqlens_host=None, apply
     return y
 
 
+def gdn_chunk_fwd_workspace_bytes(in_dtype, total_tokens: int, n_seqs: int, Hv: int, K: int, V: int) -> int:
+    torch = _torch()
+    code = BF16 if in_dtype == torch.bfloat16 else F32
+    return int(load_library().gdn_chunk_fwd_workspace_bytes(code, total_tokens, n_seqs, Hv, K, V))
+
+
+def _workspace(nbytes: int, device, given=None):
+    torch = _torch()
+    if given is not None:
+        if given.numel() * given.element_size() < nbytes:
+            raise ValueError("workspace too small: %d bytes needed" % nbytes)
+        return given
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
 def gdn_chunk_fwd(q, k, v, g, beta, scale: float = 1.0, initial_state=None, cu_seqlens=None,
-                  cu_seqlens_host=None, o_dtype=None, output_final_state: bool = True):
+                  cu_seqlens_host=None, o_dtype=None, output_final_state: bool = True, workspace=None):
     """Chunked gated delta rule forward.
 
     q, k [B, T, Hqk, K]; v [B, T, Hv, V]; g, beta fp32 [B, T, Hv];
@@ -240,16 +265,18 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale: float = 1.0, initial_state=None, cu_s
     o_dtype = v.dtype if o_dtype is None else o_dtype
     o = torch.empty((B, T, Hv, V), dtype=o_dtype, device=dev)
     fin = torch.empty((N, Hv, K, V), dtype=torch.float32, device=dev) if output_final_state else None
+    total = T if cu_seqlens is not None else B * T
+    ws = _workspace(gdn_chunk_fwd_workspace_bytes(q.dtype, total, N, Hv, K, V), dev, workspace)
     st = load_library().gdn_chunk_fwd(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), qs, ks, vs, _ptr(g), _ptr(beta), float(scale), _ptr(initial_state),
         _ptr(cu_seqlens), _host_offsets(cu_seqlens_host), 0 if cu_seqlens is None else N, B, T, Hqk, Hv, K, V,
-        _ptr(o), _dtype_code(o), _ptr(fin), _stream(dev),
+        _ptr(o), _dtype_code(o), _ptr(fin), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev),
     )
     _check("gdn_chunk_fwd", st)
     return o, fin
 
 
-def gdn_segment_state_scan(k, v, g, beta, seg_offsets, seg_offsets_host=None, initial_state=None):
+def gdn_segment_state_scan(k, v, g, beta, seg_offsets, seg_offsets_host=None, initial_state=None, workspace=None):
     """Pass 1 + fp32 composition over P contiguous segments of one sequence.
 
     k [T, Hqk, K] (or [1, T, Hqk, K]); v [T, Hv, V]; g, beta fp32 [T, Hv];
@@ -275,17 +302,23 @@ def gdn_segment_state_scan(k, v, g, beta, seg_offsets, seg_offsets_host=None, in
     b = torch.empty((P, Hv, K, V), dtype=torch.float32, device=dev)
     starts = torch.empty((P, Hv, K, V), dtype=torch.float32, device=dev)
     fin = torch.empty((Hv, K, V), dtype=torch.float32, device=dev)
+    ws = _workspace(int(load_library().gdn_segment_state_scan_workspace_bytes(T, P, Hv, K, V)), dev, workspace)
     st = load_library().gdn_segment_state_scan(
         _ptr(k3), _ptr(v3), _dtype_code(k3), ks, vs, _ptr(g), _ptr(beta), _ptr(seg_offsets),
         _host_offsets(seg_offsets_host),
-        P, _ptr(initial_state), T, Hqk, Hv, K, V, _ptr(M), _ptr(b), _ptr(starts), _ptr(fin), _stream(dev),
+        P, _ptr(initial_state), T, Hqk, Hv, K, V, _ptr(M), _ptr(b), _ptr(starts), _ptr(fin), _ptr(ws), ws.numel(),
+        _stream(dev),
     )
     _check("gdn_segment_state_scan", st)
     return M, b, starts, fin
 
 
-def gdn_segmented_workspace_bytes(P: int, Hv: int, K: int, V: int) -> int:
-    return int(load_library().gdn_segmented_workspace_bytes(P, Hv, K, V))
+def gdn_segment_state_scan_workspace_bytes(T: int, P: int, Hv: int, K: int, V: int) -> int:
+    return int(load_library().gdn_segment_state_scan_workspace_bytes(T, P, Hv, K, V))
+
+
+def gdn_segmented_workspace_bytes(T: int, P: int, Hv: int, K: int, V: int) -> int:
+    return int(load_library().gdn_segmented_workspace_bytes(T, P, Hv, K, V))
 
 
 def gdn_chunk_fwd_segmented(q, k, v, g, beta, seg_offsets, seg_offsets_host=None, scale: float = 1.0,
@@ -308,7 +341,7 @@ def gdn_chunk_fwd_segmented(q, k, v, g, beta, seg_offsets, seg_offsets_host=None
     if B != 1:
         raise ValueError("segmented forward takes one sequence (B == 1)")
     P = seg_offsets.numel() - 1
-    need = gdn_segmented_workspace_bytes(P, Hv, K, V)
+    need = gdn_segmented_workspace_bytes(T, P, Hv, K, V)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _require(workspace, "workspace", dev)

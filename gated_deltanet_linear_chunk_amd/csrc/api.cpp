@@ -43,6 +43,10 @@ gdn_status chunk_supported(int in_dt, int32_t K, int32_t V) {
   return GDN_ERR_UNSUPPORTED;
 }
 
+size_t tbuf_bytes(int64_t Ttot, int32_t n_seqs, int32_t H_v) {
+  return sizeof(float) * 2560 * (size_t)gdn::chunk_slots(Ttot, n_seqs) * (size_t)H_v;
+}
+
 }  // namespace
 
 extern "C" {
@@ -95,13 +99,22 @@ gdn_status gdn_conv1d_fwd(const void* x, const void* w, const void* bias, gdn_dt
                                        apply_silu, l2norm_channels, head_dim, l2_eps, y, stream));
 }
 
+size_t gdn_chunk_fwd_workspace_bytes(gdn_dtype in_dt, int64_t total_tokens, int32_t n_seqs,
+                                     int32_t H_v, int32_t K, int32_t V) {
+  (void)K;
+  (void)V;
+  if (in_dt != GDN_BF16 || total_tokens < 0 || n_seqs < 0 || H_v < 1) return 0;
+  return tbuf_bytes(total_tokens, n_seqs, H_v);
+}
+
 gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, gdn_dtype in_dt,
                          int64_t q_token_stride, int64_t k_token_stride, int64_t v_token_stride,
                          const float* g, const float* beta, float scale,
                          const float* initial_state, const int32_t* cu_seqlens,
                          const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t B, int64_t T,
                          int32_t H_qk, int32_t H_v, int32_t K, int32_t V, void* o,
-                         gdn_dtype o_dt, float* final_state, hipStream_t stream) {
+                         gdn_dtype o_dt, float* final_state, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
   if (!valid_dtype(in_dt) || !valid_dtype(o_dt)) return GDN_ERR_BAD_DTYPE;
   if (B < 1 || T < 0 || H_qk < 1 || H_v < 1 || K < 1 || V < 1) return GDN_ERR_BAD_SHAPE;
   if (H_v % H_qk != 0) return GDN_ERR_BAD_SHAPE;
@@ -119,7 +132,12 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, gdn_dtype 
   const int64_t total = cu_seqlens ? T : (int64_t)B * T;
   if (total == 0 && !final_state) return GDN_OK;
   if (total > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL_POINTER;
+  if (in_dt == GDN_BF16) {
+    if (!workspace) return GDN_ERR_NULL_POINTER;
+    if (workspace_bytes < tbuf_bytes(total, N, H_v)) return GDN_ERR_BAD_SHAPE;
+  }
   gdn::ChunkArgs a{};
+  a.tbuf = static_cast<float*>(workspace);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -151,6 +169,14 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, gdn_dtype 
   return hip_status(e);
 }
 
+size_t gdn_segment_state_scan_workspace_bytes(int64_t T, int32_t P, int32_t H_v, int32_t K,
+                                              int32_t V) {
+  (void)K;
+  (void)V;
+  if (T < 0 || P < 1 || H_v < 1) return 0;
+  return tbuf_bytes(T, P, H_v);
+}
+
 gdn_status gdn_segment_state_scan(const void* k, const void* v, gdn_dtype in_dt,
                                   int64_t k_token_stride, int64_t v_token_stride,
                                   const float* g, const float* beta,
@@ -158,7 +184,7 @@ gdn_status gdn_segment_state_scan(const void* k, const void* v, gdn_dtype in_dt,
                                   int32_t P, const float* initial_state, int64_t T,
                                   int32_t H_qk, int32_t H_v, int32_t K, int32_t V, float* M,
                                   float* b, float* seg_initial_states, float* final_state,
-                                  hipStream_t stream) {
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!valid_dtype(in_dt)) return GDN_ERR_BAD_DTYPE;
   if (in_dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
   if (P < 1 || T < 0 || H_qk < 1 || H_v < 1 || H_v % H_qk != 0) return GDN_ERR_BAD_SHAPE;
@@ -168,8 +194,10 @@ gdn_status gdn_segment_state_scan(const void* k, const void* v, gdn_dtype in_dt,
     return GDN_ERR_BAD_SHAPE;
   if (!seg_offsets) return GDN_ERR_NULL_POINTER;
   if (seg_offsets_host && !offsets_ok(seg_offsets_host, P, T, T, false)) return GDN_ERR_BAD_SEQLENS;
-  if (!k || !v || !g || !beta || !M || !b || !seg_initial_states) return GDN_ERR_NULL_POINTER;
+  if (!k || !v || !g || !beta || !M || !b || !seg_initial_states || !workspace) return GDN_ERR_NULL_POINTER;
+  if (workspace_bytes < tbuf_bytes(T, P, H_v)) return GDN_ERR_BAD_SHAPE;
   gdn::ChunkArgs a{};
+  a.tbuf = static_cast<float*>(workspace);
   a.q = nullptr;
   a.k = k;
   a.v = v;
@@ -196,10 +224,10 @@ gdn_status gdn_segment_state_scan(const void* k, const void* v, gdn_dtype in_dt,
   return hip_status(e);
 }
 
-size_t gdn_segmented_workspace_bytes(int32_t P, int32_t H_v, int32_t K, int32_t V) {
-  if (P < 1 || H_v < 1 || K < 1 || V < 1) return 0;
+size_t gdn_segmented_workspace_bytes(int64_t T, int32_t P, int32_t H_v, int32_t K, int32_t V) {
+  if (T < 0 || P < 1 || H_v < 1 || K < 1 || V < 1) return 0;
   const size_t per = (size_t)H_v * K;
-  return sizeof(float) * (size_t)P * per * ((size_t)K + 2 * (size_t)V);
+  return sizeof(float) * (size_t)P * per * ((size_t)K + 2 * (size_t)V) + tbuf_bytes(T, P, H_v);
 }
 
 gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
@@ -217,18 +245,21 @@ gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
   if (K != 128 || V < 1 || V % 128 != 0) return GDN_ERR_UNSUPPORTED;
   if (seg_offsets_host && !offsets_ok(seg_offsets_host, P, 0, T, true)) return GDN_ERR_BAD_SEQLENS;
   if (!q || !k || !v || !g || !beta || !o || !seg_offsets || !workspace) return GDN_ERR_NULL_POINTER;
-  if (workspace_bytes < gdn_segmented_workspace_bytes(P, H_v, K, V)) return GDN_ERR_BAD_SHAPE;
+  const size_t need = gdn_segmented_workspace_bytes(T, P, H_v, K, V);
+  if (workspace_bytes < need) return GDN_ERR_BAD_SHAPE;
   float* M = static_cast<float*>(workspace);
   float* b = M + (size_t)P * H_v * K * K;
   float* starts = b + (size_t)P * H_v * K * V;
+  float* tb = starts + (size_t)P * H_v * K * V;
+  const size_t tb_bytes = tbuf_bytes(T, P, H_v);
   gdn_status s = gdn_segment_state_scan(k, v, in_dt, k_token_stride, v_token_stride, g, beta,
                                         seg_offsets, nullptr, P,
                                         initial_state, T, H_qk, H_v, K, V, M, b, starts,
-                                        final_state, stream);
+                                        final_state, tb, tb_bytes, stream);
   if (s != GDN_OK) return s;
   return gdn_chunk_fwd(q, k, v, in_dt, q_token_stride, k_token_stride, v_token_stride, g, beta,
                        scale, starts, seg_offsets, nullptr, P, 1, T, H_qk,
-                       H_v, K, V, o, o_dt, nullptr, stream);
+                       H_v, K, V, o, o_dt, nullptr, tb, tb_bytes, stream);
 }
 
 }  // extern "C"

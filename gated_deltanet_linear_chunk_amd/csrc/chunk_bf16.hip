@@ -1,38 +1,31 @@
-// chunk_bf16.hip -- chunked gated delta rule on gfx950 bf16 MFMA tiles.
+// chunk_bf16.hip -- serial chunk scan of the gated delta rule on gfx950 MFMA.
 //
-// One workgroup of 8 waves owns one (sequence or segment, v-head, 128-column
-// slice of V) and walks its 64-token chunks in order; the K x 128 fp32 state
-// never leaves the registers: wave w holds columns 16w..16w+15 of it as eight
-// 16 x 16 accumulator tiles (32 floats per lane).
+// One workgroup owns one (sequence or segment, v-head, 128-column slice of V)
+// and walks its 64-token chunks in order.  The K x 128 fp32 state never leaves
+// the registers: with NW waves, wave w holds state columns (128/NW) w .. as
+// 16 x 16 accumulator tiles.  T = (I + A)^{-1} of every chunk comes from the
+// prep kernel (chunk_prep.hip); everything else is done here, per chunk (local
+// tokens r, s; G = in-chunk cumulative gate in fp64):
+//   P  = lower(Q K^T * e^{G_r - G_s})          (Gram on MFMA, mask on VALU)
+//   W  = T diag(beta e^G) K,  U0 = T diag(beta) V      (MFMA)
+//   U  = U0 - W S,  O = diag(e^G) Q S + P U,
+//   S <- e^{G_last} S + K^T diag(e^{G_last - G}) U       (MFMA, S in fp32)
+// which is the token recurrence regrouped by chunk.  The next chunk's q, k, v,
+// T, g and beta are fetched into registers while the current chunk computes;
+// O goes through LDS so that its global stores are whole 16-byte vectors.
 //
-// Per chunk (local tokens r, s; G = in-chunk cumulative gate, in fp64):
-//  prep, independent of the state --
-//    Gram products K K^T and Q K^T (bf16 inputs, exact products, fp32 sums),
-//    A = strictly-lower(diag(beta) K K^T * e^{G_r - G_s}),
-//    P = lower(Q K^T * e^{G_r - G_s}),
-//    T = (I + A)^{-1} in fp32 (16 x 16 diagonal blocks by forward
-//        substitution, then block rows),
-//    W = T diag(beta e^G) K, U0 = T diag(beta) V on MFMA;
-//  state step --
-//    U = U0 - W S, O = diag(e^G) Q S + P U, S <- e^{G_last} S + K^T diag(e^{G_last - G}) U.
-// That is the token recurrence regrouped by chunk (WY / UT form).
+// Precision: each fp32 quantity that meets the matrix cores is split into a
+// bf16 pair hi + lo (~16 significant bits) and multiplied against exact bf16
+// data (q, k, v) or against another pair (hi*hi + hi*lo + lo*hi): the T
+// products against K and V, S against W and Q, P against U, the decayed U
+// against K.  W alone is a single bf16 operand: W S sums 128 terms whose
+// rounding errors average out.
 //
-// Precision: every fp32 quantity that meets the matrix cores is split into a
-// bf16 pair hi + lo (about 16 significant bits) and multiplied against exact
-// bf16 data (q, k, v) or against another pair (hi*hi + hi*lo + lo*hi):
-// T diag(beta e^G) and T diag(beta) against K and V, S against W and Q,
-// P against U, diag(e^{G_last - G}) U against K.  W alone is a single bf16
-// operand: W S is a 128-term sum whose rounding errors average out.  With
-// these choices the kernel's error is set by fp32 accumulation, not by bf16.
-//
-// LDS (bytes, bf16 unless noted; pitches padded by 16 B):
-//   sQ [64][136]            sK [64][136] (dead after the Gram products ->
-//                                          reused for the fp32 T [64][68])
-//   sKt [128][72] (K^T)     sVt [128][72] (V^T, this workgroup's 128 columns)
-//   sP [2][64][72] (P hi, lo)
-//   sT2 [4][64][72] (T diag(beta e^G) hi/lo, T diag(beta) hi/lo; also the
-//                    scratch of the block-row inversion before that)
-//   sA fp32 [64][68] (A; then reused for -W as bf16 [64][136])
+// LDS (bf16 unless noted; row pitches padded by 16 B):
+//   sQ [64][136], sK [64][136] (then -W), sKt [128][72] (K^T),
+//   sVt [128][72] (V^T of this slice), sP [2][64][72] (hi, lo),
+//   sT2 [4][64][72] (T diag(beta e^G) hi/lo, T diag(beta) hi/lo; during the
+//   state step it holds the fp32 O tile [64][132]), gates.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -41,52 +34,69 @@ namespace gdn {
 namespace {
 
 constexpr int CH = 64;
-constexpr int KD = 128;  // key dim
-constexpr int BV = 128;  // value columns per workgroup
-constexpr int NWAVE = 8;
-constexpr int NTHREADS = NWAVE * 64;
+constexpr int KD = 128;
+constexpr int BV = 128;
 
-constexpr int QP = KD + 8;  // pitch of row-major [64][K] bf16 tiles
-constexpr int TP = CH + 8;  // pitch of [*][64] bf16 tiles
-constexpr int FP = CH + 4;  // pitch of fp32 [64][64] tiles
+constexpr int QP = KD + 8;
+constexpr int TP = CH + 8;
+constexpr int OP = BV + 4;  // fp32 O tile pitch
 
 constexpr int OFF_Q = 0;
-constexpr int OFF_K = OFF_Q + CH * QP * 2;      // also fp32 T
+constexpr int OFF_K = OFF_Q + CH * QP * 2;  // K rows, then -W rows
 constexpr int OFF_KT = OFF_K + CH * QP * 2;
 constexpr int OFF_VT = OFF_KT + KD * TP * 2;
 constexpr int OFF_P = OFF_VT + BV * TP * 2;
-constexpr int OFF_T2 = OFF_P + 2 * CH * TP * 2;
-constexpr int OFF_A = OFF_T2 + 4 * CH * TP * 2;  // also -W
-constexpr int OFF_G = OFF_A + CH * QP * 2;        // double[64]
+constexpr int OFF_T2 = OFF_P + 2 * CH * TP * 2;  // also the fp32 O tile
+constexpr int OFF_G = OFF_T2 + 4 * CH * TP * 2;  // double[64]
 constexpr int OFF_BETA = OFF_G + CH * 8;
 constexpr int OFF_GAM = OFF_BETA + CH * 4;
 constexpr int OFF_DEC = OFF_GAM + CH * 4;
 constexpr int LDS_BYTES = OFF_DEC + CH * 4;
-static_assert(CH * FP * 4 <= CH * QP * 2, "fp32 T must fit in the K tile");
-static_assert(CH * FP * 4 <= CH * QP * 2, "fp32 A must fit in the -W tile");
-static_assert(3 * 256 * 4 <= 4 * CH * TP * 2, "inversion scratch must fit in sT2");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+static_assert(CH * OP * 4 <= 4 * CH * TP * 2, "O tile must fit over sT2");
+
+// Kernel modes: forward with fp32 o, forward with bf16 o, segment pass 1.
+enum { kOutF32 = 0, kOutBF16 = 1, kPass1 = 2 };
 
 struct Pass1 {
-  int m_tiles;  // leading blockIdx.x values that evolve M columns (v = 0, S0 = I)
+  int m_tiles;   // leading blockIdx.x values that evolve M columns (v = 0, S0 = I)
   float* m_out;  // [n_seqs, Hv, K, K]
 };
 
 __device__ __forceinline__ void zero4(f32x4& x) { x[0] = x[1] = x[2] = x[3] = 0.f; }
 
-template <bool kHasPass1>
-__global__ void __launch_bounds__(NTHREADS) chunk_bf16_kernel(ChunkArgs a, Pass1 p1) {
+// Keeps the instruction scheduler from moving work across this point: bounds
+// how far LDS fragment loads are hoisted ahead of their MFMAs (and with them
+// the registers in flight) to one short group of products.
+#define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// tile index (0..9) -> (block row i, block column j) of the lower 4 x 4 tiles
+__device__ __forceinline__ void tile_ij(int t, int& i, int& j) {
+  i = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
+  j = t - (i * (i + 1)) / 2;
+}
+
+
+template <int kMode, int NW>
+__global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 p1) {
+  constexpr int NT = NW * 64;
+  constexpr int CPW = BV / NW;     // state columns per wave
+  constexpr int NCT = CPW / 16;    // 16-column tiles per wave
+  constexpr int NPAIR = 512 / NT;  // (row pair, 8 columns) units per thread per matrix
+  constexpr int NTF = (640 + NT - 1) / NT;  // float4 of T per thread
+  constexpr int DTW = 8 / NW > 0 ? 8 / NW : 1;  // 16-row key tiles of W per wave
+  constexpr bool kOut = kMode != kPass1;
+  static_assert(CPW % 16 == 0 && NW * CPW == BV, "wave layout");
+
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + OFF_Q);
   uint16_t* sK = reinterpret_cast<uint16_t*>(smem + OFF_K);
-  float* sTf = reinterpret_cast<float*>(smem + OFF_K);
+  uint16_t* sWn = sK;
   uint16_t* sKt = reinterpret_cast<uint16_t*>(smem + OFF_KT);
   uint16_t* sVt = reinterpret_cast<uint16_t*>(smem + OFF_VT);
   uint16_t* sP = reinterpret_cast<uint16_t*>(smem + OFF_P);
   uint16_t* sT2 = reinterpret_cast<uint16_t*>(smem + OFF_T2);
-  float* sY = reinterpret_cast<float*>(smem + OFF_T2);
-  float* sA = reinterpret_cast<float*>(smem + OFF_A);
-  uint16_t* sWn = reinterpret_cast<uint16_t*>(smem + OFF_A);
+  float* sO = reinterpret_cast<float*>(smem + OFF_T2);
   double* sG = reinterpret_cast<double*>(smem + OFF_G);
   float* sBeta = reinterpret_cast<float*>(smem + OFF_BETA);
   float* sGam = reinterpret_cast<float*>(smem + OFF_GAM);
@@ -98,12 +108,13 @@ __global__ void __launch_bounds__(NTHREADS) chunk_bf16_kernel(ChunkArgs a, Pass1
   const int g4 = lane >> 4;
   const int c16 = lane & 15;
 
-  // ---- which unit this workgroup runs -------------------------------------
   bool m_mode = false;
   int tile = blockIdx.x;
-  if (kHasPass1 && tile < p1.m_tiles) m_mode = true;
-  if (kHasPass1 && !m_mode) tile -= p1.m_tiles;
-  const int v0 = tile * BV;  // first column (of V, or of M in m_mode)
+  if (kMode == kPass1) {
+    m_mode = tile < p1.m_tiles;
+    if (!m_mode) tile -= p1.m_tiles;
+  }
+  const int v0 = tile * BV;
   const int h = blockIdx.y;
   const int seq = blockIdx.z;
   const int hq = h / (a.Hv / a.Hqk);
@@ -115,81 +126,152 @@ __global__ void __launch_bounds__(NTHREADS) chunk_bf16_kernel(ChunkArgs a, Pass1
     bos = (int64_t)seq * a.row_len;
     eos = bos + a.row_len;
   }
-  const uint16_t* qg = (const uint16_t*)a.q;
-  const uint16_t* kg = (const uint16_t*)a.k;
-  const uint16_t* vg = m_mode ? nullptr : (const uint16_t*)a.v;
-  const bool want_o = !m_mode && a.o != nullptr && qg != nullptr;
+  const bool load_v = !m_mode;
   const int s0_mode = m_mode ? 2 : a.s0_mode;
-  const int col_base = v0 + wave * 16;  // this wave's first state column
+  const int col_base = v0 + wave * CPW;
 
-  // ---- initial state: S[d][col_base + c16], d = 16*dt + 4*g4 + e ----------
-  f32x4 S[8];
+  // Per-thread base pointers of the prefetch: unit u covers token rows
+  // 2 * (pid & 31) + {0, 1} and columns 8 * (pid >> 5) .. + 7.  Lanes run along
+  // the tokens so that the transposed LDS stores (K^T, V^T) of a wave hit
+  // consecutive banks; the 16-byte global loads of the four column groups of a
+  // row come from neighbouring lanes and waves and meet in the caches.
+  const uint16_t* kbase[NPAIR];
+  const uint16_t* qbase[NPAIR];
+  const uint16_t* vbase[NPAIR];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int d = 16 * dt + 4 * g4 + e;
-      float s = 0.f;
-      if (s0_mode == 1)
-        s = a.s0[((int64_t)seq * a.Hv + h) * (int64_t)KD * a.V + (int64_t)d * a.V + col_base + c16];
-      else if (s0_mode == 2)
-        s = (d == col_base + c16) ? 1.f : 0.f;
-      S[dt][e] = s;
-    }
+  for (int u = 0; u < NPAIR; ++u) {
+    const int pid = tid + u * NT;
+    const int r0 = 2 * (pid & 31), d8 = (pid >> 5) * 8;
+    kbase[u] = (const uint16_t*)a.k + (bos + r0) * a.k_stride + hq * KD + d8;
+    qbase[u] = kOut ? (const uint16_t*)a.q + (bos + r0) * a.q_stride + hq * KD + d8 : nullptr;
+    vbase[u] = load_v ? (const uint16_t*)a.v + (bos + r0) * a.v_stride + (int64_t)h * a.V + v0 + d8 : nullptr;
   }
+  const float* tbase = a.tbuf + (int64_t)h * 2560 + 4 * tid;
+  const int64_t tslot_stride = (int64_t)a.Hv * 2560;
+  const float* gbase = a.g + (bos + tid) * a.Hv + h;
+  const float* bbase = a.beta + (bos + tid) * a.Hv + h;
 
-  // sP's upper tiles (0,1) and (2,3) are read as zeros by the P U product and
-  // are never written afterwards.
-  for (int i = tid; i < 2 * CH * TP; i += NTHREADS) sP[i] = 0;
+  // ---- initial state: S[ct][dt][e] = S[16 dt + 4 g4 + e][col_base + 16 ct + c16]
+  f32x4 S[NCT][8];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 16 * dt + 4 * g4 + e;
+        const int col = col_base + 16 * ct + c16;
+        float s = 0.f;
+        if (s0_mode == 1)
+          s = a.s0[((int64_t)seq * a.Hv + h) * (int64_t)KD * a.V + (int64_t)d * a.V + col];
+        else if (s0_mode == 2)
+          s = (d == col) ? 1.f : 0.f;
+        S[ct][dt][e] = s;
+      }
 
+  // Upper tiles of sP and sT2 that the triangular products read must be zero;
+  // sP is never written there, sT2 is rewritten (O tile) and re-zeroed below.
+  for (int i = tid; i < (2 + 4) * CH * TP; i += NT) sP[i] = 0;
+
+  // ---- prefetch registers --------------------------------------------------
+  uint4 pk[2 * NPAIR], pq[2 * NPAIR], pv[2 * NPAIR];
+  float4 pt[NTF];
+  float pg = 0.f, pb = 0.f;
+  auto prefetch = [&](int64_t t0) {
+    const int64_t rel = t0 - bos;
+    const int L = (int)((eos - t0) < CH ? (eos - t0) : CH);
+#pragma unroll
+    for (int u = 0; u < NPAIR; ++u) {
+      const int pid = tid + u * NT;
+      const int r0 = 2 * (pid & 31);
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        uint4 kz = make_uint4(0, 0, 0, 0), qz = kz, vz = kz;
+        if (r0 + x < L) {
+          kz = *reinterpret_cast<const uint4*>(kbase[u] + (rel + x) * a.k_stride);
+          if (kOut) qz = *reinterpret_cast<const uint4*>(qbase[u] + (rel + x) * a.q_stride);
+          if (load_v) vz = *reinterpret_cast<const uint4*>(vbase[u] + (rel + x) * a.v_stride);
+        }
+        pk[2 * u + x] = kz;
+        pq[2 * u + x] = qz;
+        pv[2 * u + x] = vz;
+      }
+    }
+    const float* ts = tbase + ((t0 >> 6) + seq) * tslot_stride;
+#pragma unroll
+    for (int u = 0; u < NTF; ++u)
+      if (tid + u * NT < 640) pt[u] = *reinterpret_cast<const float4*>(ts + 4 * u * NT);
+    if (tid < 64) {
+      const bool ok = tid < L;
+      pg = ok ? gbase[rel * a.Hv] : 0.f;
+      pb = ok ? bbase[rel * a.Hv] : 0.f;
+    }
+  };
+  if (bos < eos) prefetch(bos);
+
+  // Flush of the fp32 O tile staged in LDS (rows < L of the chunk at t0).
+  auto flush_o = [&](int64_t t0, int L) {
+    if (!kOut) return;
+    // 64 rows x 128 columns; 8 columns (32 B of fp32, 16 B of bf16) per unit
+    for (int u = tid; u < CH * (BV / 8); u += NT) {
+      const int r = u >> 4, c8 = (u & 15) * 8;
+      if (r >= L) continue;
+      const float* src = sO + r * OP + c8;
+      const float4 x0 = *reinterpret_cast<const float4*>(src);
+      const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+      const int64_t off = ((t0 + r) * a.Hv + h) * (int64_t)a.V + v0 + c8;
+      if (kMode == kOutBF16) {
+        uint4 w;
+        w.x = pack_bf16x2(a.scale * x0.x, a.scale * x0.y);
+        w.y = pack_bf16x2(a.scale * x0.z, a.scale * x0.w);
+        w.z = pack_bf16x2(a.scale * x1.x, a.scale * x1.y);
+        w.w = pack_bf16x2(a.scale * x1.z, a.scale * x1.w);
+        *reinterpret_cast<uint4*>((uint16_t*)a.o + off) = w;
+      } else {
+        float* dst = (float*)a.o + off;
+        *reinterpret_cast<float4*>(dst) =
+            make_float4(a.scale * x0.x, a.scale * x0.y, a.scale * x0.z, a.scale * x0.w);
+        *reinterpret_cast<float4*>(dst + 4) =
+            make_float4(a.scale * x1.x, a.scale * x1.y, a.scale * x1.z, a.scale * x1.w);
+      }
+    }
+  };
+
+  int64_t prev_t0 = -1;
+  int prev_L = 0;
   for (int64_t t0 = bos; t0 < eos; t0 += CH) {
     const int L = (int)((eos - t0) < CH ? (eos - t0) : CH);
     __syncthreads();  // the previous chunk is fully consumed
 
-    // ---- load q, k (row-major + transposed), v (transposed), g, beta -------
-    {
-      const int rp = tid >> 4;          // row pair 0..31
-      const int d8 = (tid & 15) * 8;    // 8-element column group
-      const int r0 = 2 * rp, r1 = r0 + 1;
-      uint4 kz0 = make_uint4(0, 0, 0, 0), kz1 = kz0, qz0 = kz0, qz1 = kz0, vz0 = kz0, vz1 = kz0;
-      const int64_t head_off = (int64_t)hq * KD + d8;
-      const int64_t v_off = (int64_t)h * a.V + v0 + d8;
-      if (r0 < L) {
-        kz0 = *reinterpret_cast<const uint4*>(kg + (t0 + r0) * a.k_stride + head_off);
-        if (want_o) qz0 = *reinterpret_cast<const uint4*>(qg + (t0 + r0) * a.q_stride + head_off);
-        if (vg) vz0 = *reinterpret_cast<const uint4*>(vg + (t0 + r0) * a.v_stride + v_off);
-      }
-      if (r1 < L) {
-        kz1 = *reinterpret_cast<const uint4*>(kg + (t0 + r1) * a.k_stride + head_off);
-        if (want_o) qz1 = *reinterpret_cast<const uint4*>(qg + (t0 + r1) * a.q_stride + head_off);
-        if (vg) vz1 = *reinterpret_cast<const uint4*>(vg + (t0 + r1) * a.v_stride + v_off);
-      }
-      *reinterpret_cast<uint4*>(sK + r0 * QP + d8) = kz0;
-      *reinterpret_cast<uint4*>(sK + r1 * QP + d8) = kz1;
-      *reinterpret_cast<uint4*>(sQ + r0 * QP + d8) = qz0;
-      *reinterpret_cast<uint4*>(sQ + r1 * QP + d8) = qz1;
-      const uint32_t k0w[4] = {kz0.x, kz0.y, kz0.z, kz0.w};
-      const uint32_t k1w[4] = {kz1.x, kz1.y, kz1.z, kz1.w};
-      const uint32_t v0w[4] = {vz0.x, vz0.y, vz0.z, vz0.w};
-      const uint32_t v1w[4] = {vz1.x, vz1.y, vz1.z, vz1.w};
+    if (kOut && prev_t0 >= 0) flush_o(prev_t0, prev_L);
+
+    // ---- stash the prefetched chunk in LDS --------------------------------
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // element 2j (low half) and 2j+1 (high half) of each row
-        const uint32_t klo = (k0w[j] & 0xFFFFu) | (k1w[j] << 16);
-        const uint32_t khi = (k0w[j] >> 16) | (k1w[j] & 0xFFFF0000u);
-        *reinterpret_cast<uint32_t*>(sKt + (d8 + 2 * j) * TP + r0) = klo;
-        *reinterpret_cast<uint32_t*>(sKt + (d8 + 2 * j + 1) * TP + r0) = khi;
-        const uint32_t vlo = (v0w[j] & 0xFFFFu) | (v1w[j] << 16);
-        const uint32_t vhi = (v0w[j] >> 16) | (v1w[j] & 0xFFFF0000u);
-        *reinterpret_cast<uint32_t*>(sVt + (d8 + 2 * j) * TP + r0) = vlo;
-        *reinterpret_cast<uint32_t*>(sVt + (d8 + 2 * j + 1) * TP + r0) = vhi;
+    for (int u = 0; u < NPAIR; ++u) {
+      const int pid = tid + u * NT;
+      const int r0 = 2 * (pid & 31), d8 = (pid >> 5) * 8;
+      const uint4 k0 = pk[2 * u], k1 = pk[2 * u + 1], v0v = pv[2 * u], v1v = pv[2 * u + 1];
+      *reinterpret_cast<uint4*>(sK + r0 * QP + d8) = k0;
+      *reinterpret_cast<uint4*>(sK + (r0 + 1) * QP + d8) = k1;
+      if (kOut) {
+        *reinterpret_cast<uint4*>(sQ + r0 * QP + d8) = pq[2 * u];
+        *reinterpret_cast<uint4*>(sQ + (r0 + 1) * QP + d8) = pq[2 * u + 1];
+      }
+      const uint32_t kw0[4] = {k0.x, k0.y, k0.z, k0.w};
+      const uint32_t kw1[4] = {k1.x, k1.y, k1.z, k1.w};
+      const uint32_t vw0[4] = {v0v.x, v0v.y, v0v.z, v0v.w};
+      const uint32_t vw1[4] = {v1v.x, v1v.y, v1v.z, v1v.w};
+#pragma unroll
+      for (int jx = 0; jx < 4; ++jx) {
+        const int d0 = d8 + 2 * jx, d1 = d0 + 1;
+        *reinterpret_cast<uint32_t*>(sKt + d0 * TP + r0) = (kw0[jx] & 0xFFFFu) | (kw1[jx] << 16);
+        *reinterpret_cast<uint32_t*>(sKt + d1 * TP + r0) = (kw0[jx] >> 16) | (kw1[jx] & 0xFFFF0000u);
+        *reinterpret_cast<uint32_t*>(sVt + d0 * TP + r0) = (vw0[jx] & 0xFFFFu) | (vw1[jx] << 16);
+        *reinterpret_cast<uint32_t*>(sVt + d1 * TP + r0) = (vw0[jx] >> 16) | (vw1[jx] & 0xFFFF0000u);
       }
     }
     if (wave == 0) {
-      // in-chunk inclusive cumulative gate in fp64 (padding rows add 0)
-      const bool ok = lane < L;
-      double G = ok ? (double)a.g[(t0 + lane) * a.Hv + h] : 0.0;
-      sBeta[lane] = ok ? a.beta[(t0 + lane) * a.Hv + h] : 0.f;
+      double G = (double)pg;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const double o = __shfl_up(G, off, 64);
@@ -197,240 +279,277 @@ __global__ void __launch_bounds__(NTHREADS) chunk_bf16_kernel(ChunkArgs a, Pass1
       }
       const double Glast = __shfl(G, 63, 64);
       sG[lane] = G;
+      sBeta[lane] = pb;
       sGam[lane] = expf((float)G);
       sDec[lane] = expf((float)(Glast - G));
     }
-    __syncthreads();
+    __syncthreads();  // A: chunk data and gates in LDS; O tile flushed
 
-    // ---- Gram products: 10 lower 16x16 tiles of K K^T and of Q K^T --------
-    // job 0..9: K K^T tile (i, j); job 10..19: Q K^T tile (i, j), i >= j.
-    f32x4 gacc[3];
-    int gjob[3];
+    // ---- T diag(beta e^G), T diag(beta) as bf16 pairs, from the T registers
+    // (upper tiles (0,1), (2,3) re-zeroed: the O tile overwrote them)
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      const int job = wave + NWAVE * u;
-      gjob[u] = job;
-      zero4(gacc[u]);
-      if (job < 20 && (job < 10 || want_o)) {
-        const int jj = job % 10;
-        // tile (i, j) for jj in order (0,0),(1,0),(1,1),(2,0),(2,1),(2,2),(3,0),...
-        const int i = jj >= 6 ? 3 : (jj >= 3 ? 2 : (jj >= 1 ? 1 : 0));
-        const int j = jj - (i * (i + 1)) / 2;
-        const uint16_t* Am = job < 10 ? sK : sQ;
+    for (int u = 0; u < NTF; ++u) {
+      const int f = tid + u * NT;
+      if (f < 640) {
+        int bi, bj;
+        tile_ij(f >> 6, bi, bj);
+        const int e4 = (f & 63) * 4;
+        const int r = 16 * bi + (e4 >> 4), s0 = 16 * bj + (e4 & 15);
+        const float4 b4 = *reinterpret_cast<const float4*>(sBeta + s0);
+        const float4 y4 = *reinterpret_cast<const float4*>(sGam + s0);
+        const float u0 = pt[u].x * b4.x, u1 = pt[u].y * b4.y, u2 = pt[u].z * b4.z, u3 = pt[u].w * b4.w;
+        uint32_t a0, a1, b0, b1, c0, c1, e0, e1;
+        split2(u0 * y4.x, u1 * y4.y, a0, b0);
+        split2(u2 * y4.z, u3 * y4.w, a1, b1);
+        split2(u0, u1, c0, e0);
+        split2(u2, u3, c1, e1);
+        const u32x2 wh = {a0, a1}, wl = {b0, b1}, uh = {c0, c1}, ul = {e0, e1};
+        *reinterpret_cast<u32x2*>(sT2 + 0 * CH * TP + r * TP + s0) = wh;
+        *reinterpret_cast<u32x2*>(sT2 + 1 * CH * TP + r * TP + s0) = wl;
+        *reinterpret_cast<u32x2*>(sT2 + 2 * CH * TP + r * TP + s0) = uh;
+        *reinterpret_cast<u32x2*>(sT2 + 3 * CH * TP + r * TP + s0) = ul;
+      }
+    }
+    if (kOut) {
+      // zero tiles (0,1) and (2,3) of the four T matrices: 4 x 2 x 16 rows x 16 cols
+      for (int i = tid; i < 4 * 2 * 16 * 4; i += NT) {
+        const int mat = i >> 7, which = (i >> 6) & 1, rr = (i >> 2) & 15, c4 = (i & 3) * 4;
+        const int r = which ? 32 + rr : rr, c = which ? 48 + c4 : 16 + c4;
+        *reinterpret_cast<u32x2*>(sT2 + mat * CH * TP + r * TP + c) = u32x2{0u, 0u};
+      }
+    }
+    // ---- P = lower(Q K^T * decay) as bf16 pairs -----------------------------
+    if (kOut) {
+      constexpr int NPT = (10 + NW - 1) / NW;  // Gram tiles per wave
+      f32x4 acc[NPT];
 #pragma unroll
-        for (int m = 0; m < KD / 32; ++m) {
-          const bf16x8 fa = lds_frag(Am, QP, 16 * i + c16, 32 * m, g4);
-          const bf16x8 fb = lds_frag(sK, QP, 16 * j + c16, 32 * m, g4);
-          gacc[u] = mfma16(fa, fb, gacc[u]);
+      for (int u = 0; u < NPT; ++u) zero4(acc[u]);
+#pragma unroll
+      for (int m = 0; m < KD / 32; ++m) {
+#pragma unroll
+        for (int u = 0; u < NPT; ++u) {
+          const int t = wave + NW * u;
+          if (t < 10) {
+            int i, j;
+            tile_ij(t, i, j);
+            const bf16x8 fa = lds_frag(sQ, QP, 16 * i + c16, 32 * m, g4);
+            const bf16x8 fb = lds_frag(sK, QP, 16 * j + c16, 32 * m, g4);
+            acc[u] = mfma16(fa, fb, acc[u]);
+          }
         }
       }
-    }
-    __syncthreads();  // sK is about to be reused for T
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      const int job = gjob[u];
-      if (job >= 20 || (job >= 10 && !want_o)) continue;
-      const int jj = job % 10;
-      const int i = jj >= 6 ? 3 : (jj >= 3 ? 2 : (jj >= 1 ? 1 : 0));
-      const int j = jj - (i * (i + 1)) / 2;
-      const int s = 16 * j + c16;
-      const double Gs = sG[s];
+      for (int u = 0; u < NPT; ++u) {
+        const int t = wave + NW * u;
+        if (t < 10) {
+          int i, j;
+          tile_ij(t, i, j);
+          const int s = 16 * j + c16;
+          const double Gs = sG[s];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * i + 4 * g4 + e;
-        if (job < 10) {
-          float val = 0.f;
-          if (r > s) val = sBeta[r] * gacc[u][e] * expf((float)(sG[r] - Gs));
-          sA[r * FP + s] = val;
-        } else {
-          float val = 0.f;
-          if (r >= s) val = gacc[u][e] * expf((float)(sG[r] - Gs));
-          uint16_t hi, lo;
-          split_bf16(val, hi, lo);
-          sP[r * TP + s] = hi;
-          sP[CH * TP + r * TP + s] = lo;
-        }
-      }
-    }
-    __syncthreads();
-
-    // ---- T = (I + A)^{-1}: diagonal 16x16 blocks ----------------------------
-    if (wave == 0) {
-      const int b = lane >> 4;  // block
-      const int j = lane & 15;  // column within the block
-      const float* Ab = sA + (16 * b) * FP + 16 * b;
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float val = (r == j) ? 1.f : 0.f;
-#pragma unroll
-        for (int s = 0; s < r; ++s) val = fmaf(-Ab[r * FP + s], x[s], val);
-        x[r] = val;  // zero above the diagonal (r < j) by construction
-      }
-      float* Tb = sTf + (16 * b) * FP + 16 * b;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Tb[r * FP + j] = x[r];
-    }
-    __syncthreads();
-    // ---- off-diagonal block rows: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj ----
-#pragma unroll
-    for (int i = 1; i < 4; ++i) {
-      for (int idx = tid; idx < 256 * i; idx += NTHREADS) {
-        const int j = idx >> 8, r = (idx >> 4) & 15, c = idx & 15;
-        float acc = 0.f;
-        for (int kb = j; kb < i; ++kb) {
-          const float* Ar = sA + (16 * i + r) * FP + 16 * kb;
-          const float* Tc = sTf + (16 * kb) * FP + 16 * j + c;
-#pragma unroll
-          for (int s = 0; s < 16; ++s) acc = fmaf(Ar[s], Tc[s * FP], acc);
-        }
-        sY[(j * 16 + r) * 16 + c] = acc;
-      }
-      __syncthreads();
-      for (int idx = tid; idx < 256 * i; idx += NTHREADS) {
-        const int j = idx >> 8, r = (idx >> 4) & 15, c = idx & 15;
-        const float* Tr = sTf + (16 * i + r) * FP + 16 * i;
-        float acc = 0.f;
-        for (int m = 0; m <= r; ++m) acc = fmaf(Tr[m], sY[(j * 16 + m) * 16 + c], acc);
-        sTf[(16 * i + r) * FP + 16 * j + c] = -acc;
-      }
-      __syncthreads();
-    }
-
-    // ---- T diag(beta e^G), T diag(beta) as bf16 pairs (full 64 x 64) -------
-    for (int idx = tid; idx < CH * CH / 4; idx += NTHREADS) {
-      const int r = idx >> 4, s0 = (idx & 15) * 4;
-      u16x4 w_hi, w_lo, u_hi, u_lo;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int s = s0 + e;
-        const float t = (s <= r) ? sTf[r * FP + s] : 0.f;
-        uint16_t hi, lo;
-        split_bf16(t * sBeta[s] * sGam[s], hi, lo);
-        w_hi[e] = hi;
-        w_lo[e] = lo;
-        split_bf16(t * sBeta[s], hi, lo);
-        u_hi[e] = hi;
-        u_lo[e] = lo;
-      }
-      *reinterpret_cast<u16x4*>(sT2 + 0 * CH * TP + r * TP + s0) = w_hi;
-      *reinterpret_cast<u16x4*>(sT2 + 1 * CH * TP + r * TP + s0) = w_lo;
-      *reinterpret_cast<u16x4*>(sT2 + 2 * CH * TP + r * TP + s0) = u_hi;
-      *reinterpret_cast<u16x4*>(sT2 + 3 * CH * TP + r * TP + s0) = u_lo;
-    }
-    __syncthreads();
-
-    // ---- W^T = K^T (T diag(beta e^G))^T: wave owns key rows 16*wave.. -----
-    // Stored negated as bf16 -W[r][d] (row-major), the A operand of W S.
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      f32x4 acc;
-      zero4(acc);
-#pragma unroll
-      for (int m = 0; m <= rt / 2; ++m) {
-        const bf16x8 fa = lds_frag(sKt, TP, 16 * wave + c16, 32 * m, g4);
-        const bf16x8 fh = lds_frag(sT2 + 0 * CH * TP, TP, 16 * rt + c16, 32 * m, g4);
-        const bf16x8 fl = lds_frag(sT2 + 1 * CH * TP, TP, 16 * rt + c16, 32 * m, g4);
-        acc = mfma16(fa, fh, acc);
-        acc = mfma16(fa, fl, acc);
-      }
-      // acc[e] = W[r = 16 rt + c16][d = 16 wave + 4 g4 + e]
-      u16x4 wv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) wv[e] = f32_to_bf16_bits(-acc[e]);
-      *reinterpret_cast<u16x4*>(sWn + (16 * rt + c16) * QP + 16 * wave + 4 * g4) = wv;
-    }
-    // ---- U0 = T diag(beta) V for this wave's 16 columns --------------------
-    f32x4 U[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      zero4(U[rt]);
-      if (vg) {
-#pragma unroll
-        for (int m = 0; m <= rt / 2; ++m) {
-          const bf16x8 fb = lds_frag(sVt, TP, 16 * wave + c16, 32 * m, g4);
-          const bf16x8 fh = lds_frag(sT2 + 2 * CH * TP, TP, 16 * rt + c16, 32 * m, g4);
-          const bf16x8 fl = lds_frag(sT2 + 3 * CH * TP, TP, 16 * rt + c16, 32 * m, g4);
-          U[rt] = mfma16(fh, fb, U[rt]);
-          U[rt] = mfma16(fl, fb, U[rt]);
-        }
-      }
-    }
-    __syncthreads();  // -W complete
-
-    // ---- state step ---------------------------------------------------------
-    bf16x8 Shi[4], Slo[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) split_frag(S[2 * m], S[2 * m + 1], Shi[m], Slo[m]);
-    // U = U0 - W S
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const bf16x8 fw = lds_frag(sWn, QP, 16 * rt + c16, 32 * m, g4);
-        U[rt] = mfma16(fw, Shi[m], U[rt]);
-        U[rt] = mfma16(fw, Slo[m], U[rt]);
-      }
-    }
-    bf16x8 Uhi[2], Ulo[2];
-    if (want_o) {
-#pragma unroll
-      for (int m = 0; m < 2; ++m) split_frag(U[2 * m], U[2 * m + 1], Uhi[m], Ulo[m]);
-      // O = diag(gamma) Q S + P U
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        f32x4 qs;
-        zero4(qs);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const bf16x8 fq = lds_frag(sQ, QP, 16 * rt + c16, 32 * m, g4);
-          qs = mfma16(fq, Shi[m], qs);
-          qs = mfma16(fq, Slo[m], qs);
-        }
-        f32x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = qs[e] * sGam[16 * rt + 4 * g4 + e];
-#pragma unroll
-        for (int m = 0; m <= rt / 2; ++m) {
-          const bf16x8 ph = lds_frag(sP, TP, 16 * rt + c16, 32 * m, g4);
-          const bf16x8 pl = lds_frag(sP + CH * TP, TP, 16 * rt + c16, 32 * m, g4);
-          o = mfma16(ph, Uhi[m], o);
-          o = mfma16(ph, Ulo[m], o);
-          o = mfma16(pl, Uhi[m], o);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * rt + 4 * g4 + e;
-          if (r < L) {
-            const int64_t off = ((t0 + r) * a.Hv + h) * (int64_t)a.V + col_base + c16;
-            const float val = a.scale * o[e];
-            if (a.o_dt == 1)
-              ((uint16_t*)a.o)[off] = f32_to_bf16_bits(val);
-            else
-              ((float*)a.o)[off] = val;
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * i + 4 * g4 + e;
+            const float val = (r >= s) ? acc[u][e] * expf((float)(sG[r] - Gs)) : 0.f;
+            uint32_t hi, lo;
+            split2(val, 0.f, hi, lo);
+            sP[r * TP + s] = (uint16_t)hi;
+            sP[CH * TP + r * TP + s] = (uint16_t)lo;
           }
         }
       }
     }
-    // S <- e^{G_last} S + K^T (diag(dec) U)
+    // ---- fetch the next chunk while this one computes -----------------------
+    if (t0 + CH < eos) prefetch(t0 + CH);
+    __syncthreads();  // B: sT2, sP ready; sK no longer read
+
+    // ---- -W = -(T diag(beta e^G) K) rows -> sWn (over sK) -------------------
+    // All hi products first, then all lo products: consecutive MFMAs never
+    // share an accumulator.
+    {
+      f32x4 acc[DTW][4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+      for (int dd = 0; dd < DTW; ++dd)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) U[rt][e] *= sDec[16 * rt + 4 * g4 + e];
+        for (int rt = 0; rt < 4; ++rt) zero4(acc[dd][rt]);
 #pragma unroll
-    for (int m = 0; m < 2; ++m) split_frag(U[2 * m], U[2 * m + 1], Uhi[m], Ulo[m]);
-    const float glast = sGam[CH - 1];
+      for (int part = 0; part < 2; ++part) {
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
+        for (int m = 0; m < 2; ++m) {
+          bf16x8 fa[DTW];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[dt][e] *= glast;
+          for (int dd = 0; dd < DTW; ++dd) fa[dd] = lds_frag(sKt, TP, 16 * (wave * DTW + dd) + c16, 32 * m, g4);
+#pragma unroll
+          for (int rt = 2 * m; rt < 4; ++rt) {
+            const bf16x8 ft = lds_frag(sT2 + part * CH * TP, TP, 16 * rt + c16, 32 * m, g4);
+#pragma unroll
+            for (int dd = 0; dd < DTW; ++dd) acc[dd][rt] = mfma16(fa[dd], ft, acc[dd][rt]);
+          }
+          SCHED_FENCE();
+        }
+      }
+#pragma unroll
+      for (int dd = 0; dd < DTW; ++dd)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          // acc[e] = W[r = 16 rt + c16][d = 16 dt + 4 g4 + e]
+          u32x2 wv;
+          wv[0] = pack_bf16x2(-acc[dd][rt][0], -acc[dd][rt][1]);
+          wv[1] = pack_bf16x2(-acc[dd][rt][2], -acc[dd][rt][3]);
+          *reinterpret_cast<u32x2*>(sWn + (16 * rt + c16) * QP + 16 * (wave * DTW + dd) + 4 * g4) = wv;
+        }
+    }
+    // ---- U0 = T diag(beta) V for this wave's columns ------------------------
+    f32x4 U[NCT][4];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) zero4(U[ct][rt]);
+    if (load_v) {
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const bf16x8 fk = lds_frag(sKt, TP, 16 * dt + c16, 32 * m, g4);
-        S[dt] = mfma16(fk, Uhi[m], S[dt]);
-        S[dt] = mfma16(fk, Ulo[m], S[dt]);
+        bf16x8 fb[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) fb[ct] = lds_frag(sVt, TP, wave * CPW + 16 * ct + c16, 32 * m, g4);
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+#pragma unroll
+          for (int rt = 2 * m; rt < 4; ++rt) {
+            const bf16x8 ft = lds_frag(sT2 + (2 + part) * CH * TP, TP, 16 * rt + c16, 32 * m, g4);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) U[ct][rt] = mfma16(ft, fb[ct], U[ct][rt]);
+          }
+        }
+        SCHED_FENCE();
       }
     }
+    __syncthreads();  // C: -W complete, sT2 free for the O tile
+
+    // ---- state step -------------------------------------------------------
+    // U = U0 - W S and Q S share each 32-row k-step of the split state; within
+    // a k-step the hi products of all tiles precede the lo products.
+    f32x4 O[NCT][4];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) zero4(O[ct][rt]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      bf16x8 sp[2][NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) split_frag(S[ct][2 * m], S[ct][2 * m + 1], sp[0][ct], sp[1][ct]);
+      bf16x8 fw[4], fq[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        fw[rt] = lds_frag(sWn, QP, 16 * rt + c16, 32 * m, g4);
+        if (kOut) fq[rt] = lds_frag(sQ, QP, 16 * rt + c16, 32 * m, g4);
+      }
+#pragma unroll
+      for (int part = 0; part < 2; ++part)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) {
+            U[ct][rt] = mfma16(fw[rt], sp[part][ct], U[ct][rt]);
+            if (kOut) O[ct][rt] = mfma16(fq[rt], sp[part][ct], O[ct][rt]);
+          }
+      SCHED_FENCE();
+    }
+    if (kOut) {
+      // O = diag(gamma) Q S + P U  -> fp32 O tile in LDS
+      bf16x8 Uhi[NCT][2], Ulo[NCT][2];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) split_frag(U[ct][2 * m], U[ct][2 * m + 1], Uhi[ct][m], Ulo[ct][m]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const float4 gam = *reinterpret_cast<const float4*>(sGam + 16 * rt + 4 * g4);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          O[ct][rt][0] *= gam.x;
+          O[ct][rt][1] *= gam.y;
+          O[ct][rt][2] *= gam.z;
+          O[ct][rt][3] *= gam.w;
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        bf16x8 ph[4], pl[4];
+#pragma unroll
+        for (int rt = 2 * m; rt < 4; ++rt) {
+          ph[rt] = lds_frag(sP, TP, 16 * rt + c16, 32 * m, g4);
+          pl[rt] = lds_frag(sP + CH * TP, TP, 16 * rt + c16, 32 * m, g4);
+        }
+#pragma unroll
+        for (int part = 0; part < 3; ++part)
+#pragma unroll
+          for (int rt = 2 * m; rt < 4; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+              const bf16x8 pa = part == 2 ? pl[rt] : ph[rt];
+              const bf16x8 ub = part == 1 ? Ulo[ct][m] : Uhi[ct][m];
+              O[ct][rt] = mfma16(pa, ub, O[ct][rt]);
+            }
+        SCHED_FENCE();
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sO[(16 * rt + 4 * g4 + e) * OP + wave * CPW + 16 * ct + c16] = O[ct][rt][e];
+    }
+    // S <- e^{G_last} S + K^T (diag(dec) U)
+    {
+      bf16x8 Uhi[NCT][2], Ulo[NCT][2];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const float4 dec = *reinterpret_cast<const float4*>(sDec + 16 * rt + 4 * g4);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          U[ct][rt][0] *= dec.x;
+          U[ct][rt][1] *= dec.y;
+          U[ct][rt][2] *= dec.z;
+          U[ct][rt][3] *= dec.w;
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) split_frag(U[ct][2 * m], U[ct][2 * m + 1], Uhi[ct][m], Ulo[ct][m]);
+      const float glast = sGam[CH - 1];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) S[ct][dt][e] *= glast;
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          bf16x8 fk[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) fk[x] = lds_frag(sKt, TP, 16 * (4 * half + x) + c16, 32 * m, g4);
+#pragma unroll
+          for (int part = 0; part < 2; ++part)
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+              for (int ct = 0; ct < NCT; ++ct) {
+                const int dt = 4 * half + x;
+                S[ct][dt] = mfma16(fk[x], part ? Ulo[ct][m] : Uhi[ct][m], S[ct][dt]);
+              }
+          SCHED_FENCE();
+        }
+    }
+    prev_t0 = t0;
+    prev_L = L;
+  }
+  if (kOut && prev_t0 >= 0) {
+    __syncthreads();
+    flush_o(prev_t0, prev_L);
   }
 
   // ---- final state ----------------------------------------------------------
@@ -445,32 +564,47 @@ __global__ void __launch_bounds__(NTHREADS) chunk_bf16_kernel(ChunkArgs a, Pass1
   }
   if (dst) {
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        dst[(int64_t)(16 * dt + 4 * g4 + e) * row_stride + col_base + c16] = S[dt][e];
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          dst[(int64_t)(16 * dt + 4 * g4 + e) * row_stride + col_base + 16 * ct + c16] = S[ct][dt][e];
   }
+}
+
+constexpr int kScanWaves = 4;
+
+template <int kMode>
+hipError_t launch_scan(const ChunkArgs& a, Pass1 p1, dim3 grid, hipStream_t stream) {
+  const void* fn = (const void*)chunk_scan_kernel<kMode, kScanWaves>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((chunk_scan_kernel<kMode, kScanWaves>), grid, dim3(kScanWaves * 64), LDS_BYTES, stream,
+                     a, p1);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t stream) {
   if (a.n_seqs == 0 || a.Hv == 0) return hipSuccess;
-  if (a.K != KD || a.V % BV != 0) return hipErrorInvalidValue;
-  hipError_t e = hipFuncSetAttribute((const void*)chunk_bf16_kernel<false>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  if (a.K != KD || a.V % BV != 0 || a.tbuf == nullptr) return hipErrorInvalidValue;
+  hipError_t e = launch_chunk_prep(a, stream);
   if (e != hipSuccess) return e;
-  dim3 grid(a.V / BV, a.Hv, a.n_seqs);
-  Pass1 p1{0, nullptr};
-  hipLaunchKernelGGL(chunk_bf16_kernel<false>, grid, dim3(NTHREADS), LDS_BYTES, stream, a, p1);
-  return hipGetLastError();
+  const dim3 grid(a.V / BV, a.Hv, a.n_seqs);
+  if (a.o == nullptr || a.q == nullptr) {
+    // state only: run the scan without outputs
+    return launch_scan<kPass1>(a, Pass1{0, nullptr}, grid, stream);
+  }
+  return a.o_dt == 1 ? launch_scan<kOutBF16>(a, Pass1{0, nullptr}, grid, stream)
+                     : launch_scan<kOutF32>(a, Pass1{0, nullptr}, grid, stream);
 }
 
 hipError_t launch_segment_pass1(const ChunkArgs& a, float* M, float* b, hipStream_t stream) {
   if (a.n_seqs == 0 || a.Hv == 0) return hipSuccess;
-  if (a.K != KD || a.V % BV != 0) return hipErrorInvalidValue;
-  hipError_t e = hipFuncSetAttribute((const void*)chunk_bf16_kernel<true>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  if (a.K != KD || a.V % BV != 0 || a.tbuf == nullptr) return hipErrorInvalidValue;
+  hipError_t e = launch_chunk_prep(a, stream);
   if (e != hipSuccess) return e;
   ChunkArgs c = a;
   c.q = nullptr;
@@ -480,10 +614,7 @@ hipError_t launch_segment_pass1(const ChunkArgs& a, float* M, float* b, hipStrea
   c.sf_head_stride = (int64_t)KD * a.V;
   c.sf_row_stride = a.V;
   c.s0_mode = 0;
-  Pass1 p1{KD / BV, M};
-  dim3 grid(KD / BV + a.V / BV, a.Hv, a.n_seqs);
-  hipLaunchKernelGGL(chunk_bf16_kernel<true>, grid, dim3(NTHREADS), LDS_BYTES, stream, c, p1);
-  return hipGetLastError();
+  return launch_scan<kPass1>(c, Pass1{KD / BV, M}, dim3(KD / BV + a.V / BV, a.Hv, a.n_seqs), stream);
 }
 
 }  // namespace gdn

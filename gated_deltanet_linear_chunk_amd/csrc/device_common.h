@@ -45,6 +45,27 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
   lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (element 0 in the low half), round to nearest even
+// (one v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float x0, float x1) {
+  const f32x2 v = {x0, x1};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Split two fp32 values into packed bf16 hi and lo words: x ~= hi + lo.
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(x0, x1);
+  const float r0 = x0 - __uint_as_float(hi << 16);
+  const float r1 = x1 - __uint_as_float(hi & 0xFFFF0000u);
+  lo = pack_bf16x2(r0, r1);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u16x8 v) {
   return __builtin_bit_cast(bf16x8, v);
 }
@@ -68,19 +89,15 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* base, int pitch, int 
 // into hi and lo B fragments.
 __device__ __forceinline__ void split_frag(const f32x4& t0, const f32x4& t1, bf16x8& hi,
                                            bf16x8& lo) {
-  u16x8 h, l;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    uint16_t a, b;
-    split_bf16(t0[e], a, b);
-    h[e] = a;
-    l[e] = b;
-    split_bf16(t1[e], a, b);
-    h[4 + e] = a;
-    l[4 + e] = b;
-  }
-  hi = as_bf16x8(h);
-  lo = as_bf16x8(l);
+  uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+  split2(t0[0], t0[1], h0, l0);
+  split2(t0[2], t0[3], h1, l1);
+  split2(t1[0], t1[1], h2, l2);
+  split2(t1[2], t1[3], h3, l3);
+  const u32x4 h = {h0, h1, h2, h3};
+  const u32x4 l = {l0, l1, l2, l3};
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
 }
 
 __device__ __forceinline__ int clampi(int64_t x, int64_t lo, int64_t hi) {

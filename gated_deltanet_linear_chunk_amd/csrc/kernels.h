@@ -39,7 +39,13 @@ struct ChunkArgs {
   // sf + seq * sf_seq_stride + h * sf_head_stride + i * sf_row_stride + j
   float* sf;
   int64_t sf_seq_stride, sf_head_stride, sf_row_stride;
+  // bf16 path: per-chunk T = (I + A)^{-1} blocks, chunk_slots(Ttot, n_seqs) * Hv * 2560 floats
+  float* tbuf;
 };
+
+// Number of chunk slots a launch over Ttot tokens in n_seqs sequences uses.
+int64_t chunk_slots(int64_t Ttot, int n_seqs);
+hipError_t launch_chunk_prep(const ChunkArgs& a, hipStream_t stream);
 
 hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t stream);
 hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t stream);

@@ -121,14 +121,23 @@ gdn_status gdn_conv1d_fwd(const void* x, const void* w, const void* bias, gdn_dt
  * cores (needs K = 128, V % 128 == 0); in_dt = F32 runs an fp32 vector-ALU
  * kernel (K in {32, 64}, V % 32 == 0).
  * o_dt is F32 or BF16 (round to nearest even).
+ * workspace: device memory of at least gdn_chunk_fwd_workspace_bytes(...)
+ * bytes (0 for F32 inputs; NULL allowed then).  The BF16 path stores there
+ * the per-chunk matrices T = (I + A)^{-1} of the UT transform, which a
+ * parallel pass computes before the serial chunk scan; contents on entry do
+ * not matter.  Concurrent calls need separate workspaces.
  */
+size_t gdn_chunk_fwd_workspace_bytes(gdn_dtype in_dt, int64_t total_tokens, int32_t n_seqs,
+                                     int32_t H_v, int32_t K, int32_t V);
+
 gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, gdn_dtype in_dt,
                          int64_t q_token_stride, int64_t k_token_stride, int64_t v_token_stride,
                          const float* g, const float* beta, float scale,
                          const float* initial_state, const int32_t* cu_seqlens,
                          const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t B, int64_t T,
                          int32_t H_qk, int32_t H_v, int32_t K, int32_t V, void* o,
-                         gdn_dtype o_dt, float* final_state, hipStream_t stream);
+                         gdn_dtype o_dt, float* final_state, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Segment state scan: one long sequence cut into P contiguous segments
@@ -150,7 +159,12 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, gdn_dtype 
  * Running gdn_chunk_fwd with cu_seqlens = seg_offsets (seg_offsets[0] = 0,
  * seg_offsets[P] = T) and initial_state = seg_initial_states is pass 2: it
  * yields every output of the unsegmented run.
+ * workspace: at least gdn_segment_state_scan_workspace_bytes(...) bytes
+ * (the per-chunk T matrices of pass 1).
  */
+size_t gdn_segment_state_scan_workspace_bytes(int64_t T, int32_t P, int32_t H_v, int32_t K,
+                                              int32_t V);
+
 gdn_status gdn_segment_state_scan(const void* k, const void* v, gdn_dtype in_dt,
                                   int64_t k_token_stride, int64_t v_token_stride,
                                   const float* g, const float* beta,
@@ -158,7 +172,7 @@ gdn_status gdn_segment_state_scan(const void* k, const void* v, gdn_dtype in_dt,
                                   int32_t P, const float* initial_state, int64_t T,
                                   int32_t H_qk, int32_t H_v, int32_t K, int32_t V, float* M,
                                   float* b, float* seg_initial_states, float* final_state,
-                                  hipStream_t stream);
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Segment-parallel forward of one long sequence: gdn_segment_state_scan
@@ -167,10 +181,10 @@ gdn_status gdn_segment_state_scan(const void* k, const void* v, gdn_dtype in_dt,
  * gdn_chunk_fwd with B = 1; seg_offsets as above with seg_offsets[0] = 0 and
  * seg_offsets[P] = T.  final_state fp32 [H_v, K, V] or NULL.
  * workspace: device memory of at least gdn_segmented_workspace_bytes(...)
- * bytes, used for M, b, the composed starts and the per-segment final states;
+ * bytes, used for M, b, the composed starts and the per-chunk T matrices;
  * its contents on entry do not matter.
  */
-size_t gdn_segmented_workspace_bytes(int32_t P, int32_t H_v, int32_t K, int32_t V);
+size_t gdn_segmented_workspace_bytes(int64_t T, int32_t P, int32_t H_v, int32_t K, int32_t V);
 
 gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
                                    gdn_dtype in_dt, int64_t q_token_stride,

@@ -51,7 +51,8 @@ FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails va
 def _chunk(lib, **kw):
     args = dict(q=FAKE, k=FAKE, v=FAKE, in_dt=1, qs=0, ks=0, vs=0, g=FAKE, beta=FAKE, scale=1.0, s0=None, cu=None,
                 cu_host=None,
-                n_seqs=0, B=1, T=64, Hqk=16, Hv=32, K=128, V=128, o=FAKE, o_dt=0, fin=None, stream=None)
+                n_seqs=0, B=1, T=64, Hqk=16, Hv=32, K=128, V=128, o=FAKE, o_dt=0, fin=None, ws=FAKE,
+                ws_bytes=1 << 40, stream=None)
     args.update(kw)
     return lib.gdn_chunk_fwd(*args.values())
 
@@ -79,6 +80,11 @@ def test_chunk_validation(lib):
     assert _chunk(lib, cu=FAKE, cu_host=short, n_seqs=2) == SEQ
     start = (ctypes.c_int32 * 3)(4, 30, 64)
     assert _chunk(lib, cu=FAKE, cu_host=start, n_seqs=2) == SEQ
+    assert _chunk(lib, ws=None) == NULLP  # the bf16 path needs its T workspace
+    need = lib.gdn_chunk_fwd_workspace_bytes(1, 64, 1, 32, 128, 128)
+    assert need == 4 * 2560 * (1 + 1) * 32
+    assert _chunk(lib, ws_bytes=need - 1) == SHAPE
+    assert lib.gdn_chunk_fwd_workspace_bytes(0, 64, 1, 2, 32, 32) == 0  # fp32 path needs none
     # nothing to do: no tokens and no state requested
     assert _chunk(lib, T=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
 
@@ -110,22 +116,26 @@ def test_gate_and_segment_validation(lib):
     def scan(**kw):
         a = dict(k=FAKE, v=FAKE, dt=1, ks=0, vs=0, g=FAKE, beta=FAKE, off=FAKE, off_host=None, P=8, s0=None, T=4096,
                  Hqk=16,
-                 Hv=32, K=128, V=128, M=FAKE, b=FAKE, starts=FAKE, fin=None, stream=None)
+                 Hv=32, K=128, V=128, M=FAKE, b=FAKE, starts=FAKE, fin=None, ws=FAKE, ws_bytes=1 << 40,
+                 stream=None)
         a.update(kw)
         return lib.gdn_segment_state_scan(*a.values())
 
     assert scan(off=None) == NULLP
     assert scan(ks=12) == SHAPE
     assert scan(M=None) == NULLP
+    assert scan(ws=None) == NULLP
+    assert scan(ws_bytes=lib.gdn_segment_state_scan_workspace_bytes(4096, 8, 32, 128, 128) - 4) == SHAPE
     assert scan(dt=0) == UNSUP
     assert scan(P=0) == SHAPE
     assert scan(V=200) == UNSUP
     off = (ctypes.c_int32 * 3)(0, 5000, 4096)
     assert scan(P=2, off_host=off) == SEQ
-    assert lib.gdn_segmented_workspace_bytes(8, 32, 128, 128) == 4 * 8 * 32 * 128 * (128 + 256)
-    assert lib.gdn_segmented_workspace_bytes(0, 32, 128, 128) == 0
+    assert lib.gdn_segmented_workspace_bytes(4096, 8, 32, 128, 128) == 4 * 8 * 32 * 128 * (128 + 256) + \
+        lib.gdn_segment_state_scan_workspace_bytes(4096, 8, 32, 128, 128)
+    assert lib.gdn_segmented_workspace_bytes(4096, 0, 32, 128, 128) == 0
     seg = lib.gdn_chunk_fwd_segmented
-    ws = lib.gdn_segmented_workspace_bytes(2, 32, 128, 128)
+    ws = lib.gdn_segmented_workspace_bytes(4096, 2, 32, 128, 128)
     good = (ctypes.c_int32 * 3)(0, 2048, 4096)
     assert seg(FAKE, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE, 1.0, None, FAKE, good, 2, 4096, 16, 32, 128, 128, FAKE, 0, None,
                FAKE, ws - 1, None) == SHAPE
