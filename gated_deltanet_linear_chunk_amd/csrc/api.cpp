@@ -44,7 +44,7 @@ gdn_status chunk_supported(int in_dt, int32_t K, int32_t V) {
 }
 
 size_t tbuf_bytes(int64_t Ttot, int32_t n_seqs, int32_t H_v) {
-  return sizeof(float) * 2560 * (size_t)gdn::chunk_slots(Ttot, n_seqs) * (size_t)H_v;
+  return (size_t)gdn::PREP_RECORD_BYTES * (size_t)gdn::chunk_slots(Ttot, n_seqs) * (size_t)H_v;
 }
 
 }  // namespace

@@ -3,29 +3,29 @@
 // One workgroup owns one (sequence or segment, v-head, 128-column slice of V)
 // and walks its 64-token chunks in order.  The K x 128 fp32 state never leaves
 // the registers: with NW waves, wave w holds state columns (128/NW) w .. as
-// 16 x 16 accumulator tiles.  T = (I + A)^{-1} of every chunk comes from the
-// prep kernel (chunk_prep.hip); everything else is done here, per chunk (local
-// tokens r, s; G = in-chunk cumulative gate in fp64):
-//   P  = lower(Q K^T * e^{G_r - G_s})          (Gram on MFMA, mask on VALU)
-//   W  = T diag(beta e^G) K,  U0 = T diag(beta) V      (MFMA)
+// 16 x 16 accumulator tiles.  Everything about a chunk that does not depend on
+// the state (the UT-transform products T diag(beta e^G) and T diag(beta), the
+// masked Q K^T, e^G and the decays) comes precomputed from the prep kernel
+// (chunk_prep.hip); per chunk (local tokens r, s) the scan then does
+//   W  = T diag(beta e^G) K,  U0 = T diag(beta) V                 (MFMA)
 //   U  = U0 - W S,  O = diag(e^G) Q S + P U,
 //   S <- e^{G_last} S + K^T diag(e^{G_last - G}) U       (MFMA, S in fp32)
-// which is the token recurrence regrouped by chunk.  The next chunk's q, k, v,
-// T, g and beta are fetched into registers while the current chunk computes;
-// O goes through LDS so that its global stores are whole 16-byte vectors.
+// which is the token recurrence regrouped by chunk.  The next chunk's q, k, v
+// and prep record are fetched into registers while the current chunk
+// computes; O goes through LDS so that its global stores are 16-byte vectors.
 //
-// Precision: each fp32 quantity that meets the matrix cores is split into a
-// bf16 pair hi + lo (~16 significant bits) and multiplied against exact bf16
-// data (q, k, v) or against another pair (hi*hi + hi*lo + lo*hi): the T
-// products against K and V, S against W and Q, P against U, the decayed U
-// against K.  W alone is a single bf16 operand: W S sums 128 terms whose
-// rounding errors average out.
+// Precision: each fp32 quantity that meets the matrix cores is a bf16 pair
+// hi + lo (~16 significant bits) multiplied against exact bf16 data (q, k, v)
+// or against another pair (hi*hi + hi*lo + lo*hi): the T products against K
+// and V, S against W and Q, P against U, the decayed U against K.  W alone is
+// a single bf16 operand: W S sums 128 terms whose rounding errors average out.
 //
-// LDS (bf16 unless noted; row pitches padded by 16 B):
-//   sQ [64][136], sK [64][136] (then -W), sKt [128][72] (K^T),
+// LDS (bf16 unless noted; row pitches padded by 16 B, which makes the
+// fragment reads conflict-free):
+//   sQ [64][136], sW [64][136] (-W), sKt [128][72] (K^T),
 //   sVt [128][72] (V^T of this slice), sP [2][64][72] (hi, lo),
 //   sT2 [4][64][72] (T diag(beta e^G) hi/lo, T diag(beta) hi/lo; during the
-//   state step it holds the fp32 O tile [64][132]), gates.
+//   state step it holds the fp32 O tile [64][132]), gamma[64], dec[64] fp32.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -42,20 +42,23 @@ constexpr int TP = CH + 8;
 constexpr int OP = BV + 4;  // fp32 O tile pitch
 
 constexpr int OFF_Q = 0;
-constexpr int OFF_K = OFF_Q + CH * QP * 2;  // K rows, then -W rows
-constexpr int OFF_KT = OFF_K + CH * QP * 2;
+constexpr int OFF_W = OFF_Q + CH * QP * 2;
+constexpr int OFF_KT = OFF_W + CH * QP * 2;
 constexpr int OFF_VT = OFF_KT + KD * TP * 2;
 constexpr int OFF_P = OFF_VT + BV * TP * 2;
 constexpr int OFF_T2 = OFF_P + 2 * CH * TP * 2;  // also the fp32 O tile
-constexpr int OFF_G = OFF_T2 + 4 * CH * TP * 2;  // double[64]
-constexpr int OFF_BETA = OFF_G + CH * 8;
-constexpr int OFF_GAM = OFF_BETA + CH * 4;
+constexpr int OFF_GAM = OFF_T2 + 4 * CH * TP * 2;
 constexpr int OFF_DEC = OFF_GAM + CH * 4;
 constexpr int LDS_BYTES = OFF_DEC + CH * 4;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 static_assert(CH * OP * 4 <= 4 * CH * TP * 2, "O tile must fit over sT2");
 
-// Kernel modes: forward with fp32 o, forward with bf16 o, segment pass 1.
+// 16-byte units of a prep record: 6 x 10 tiles x 32, then gamma and dec
+constexpr int REC_MAT_UNITS = 6 * 10 * 32;
+constexpr int REC_UNITS = REC_MAT_UNITS + 2 * 16;
+static_assert(REC_UNITS * 16 == PREP_RECORD_BYTES, "record layout");
+
+// Kernel modes: forward with fp32 o, forward with bf16 o, state only / pass 1.
 enum { kOutF32 = 0, kOutBF16 = 1, kPass1 = 2 };
 
 struct Pass1 {
@@ -76,29 +79,25 @@ __device__ __forceinline__ void tile_ij(int t, int& i, int& j) {
   j = t - (i * (i + 1)) / 2;
 }
 
-
 template <int kMode, int NW>
 __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 p1) {
   constexpr int NT = NW * 64;
   constexpr int CPW = BV / NW;     // state columns per wave
   constexpr int NCT = CPW / 16;    // 16-column tiles per wave
   constexpr int NPAIR = 512 / NT;  // (row pair, 8 columns) units per thread per matrix
-  constexpr int NTF = (640 + NT - 1) / NT;  // float4 of T per thread
-  constexpr int DTW = 8 / NW > 0 ? 8 / NW : 1;  // 16-row key tiles of W per wave
+  constexpr int NREC = (REC_UNITS + NT - 1) / NT;  // record units per thread
+  constexpr int DTW = 8 / NW > 0 ? 8 / NW : 1;     // 16-row key tiles of W per wave
   constexpr bool kOut = kMode != kPass1;
   static_assert(CPW % 16 == 0 && NW * CPW == BV, "wave layout");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + OFF_Q);
-  uint16_t* sK = reinterpret_cast<uint16_t*>(smem + OFF_K);
-  uint16_t* sWn = sK;
+  uint16_t* sWn = reinterpret_cast<uint16_t*>(smem + OFF_W);
   uint16_t* sKt = reinterpret_cast<uint16_t*>(smem + OFF_KT);
   uint16_t* sVt = reinterpret_cast<uint16_t*>(smem + OFF_VT);
   uint16_t* sP = reinterpret_cast<uint16_t*>(smem + OFF_P);
   uint16_t* sT2 = reinterpret_cast<uint16_t*>(smem + OFF_T2);
   float* sO = reinterpret_cast<float*>(smem + OFF_T2);
-  double* sG = reinterpret_cast<double*>(smem + OFF_G);
-  float* sBeta = reinterpret_cast<float*>(smem + OFF_BETA);
   float* sGam = reinterpret_cast<float*>(smem + OFF_GAM);
   float* sDec = reinterpret_cast<float*>(smem + OFF_DEC);
 
@@ -133,23 +132,21 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   // Per-thread base pointers of the prefetch: unit u covers token rows
   // 2 * (pid & 31) + {0, 1} and columns 8 * (pid >> 5) .. + 7.  Lanes run along
   // the tokens so that the transposed LDS stores (K^T, V^T) of a wave hit
-  // consecutive banks; the 16-byte global loads of the four column groups of a
-  // row come from neighbouring lanes and waves and meet in the caches.
-  const uint16_t* kbase[NPAIR];
-  const uint16_t* qbase[NPAIR];
-  const uint16_t* vbase[NPAIR];
-#pragma unroll
-  for (int u = 0; u < NPAIR; ++u) {
-    const int pid = tid + u * NT;
-    const int r0 = 2 * (pid & 31), d8 = (pid >> 5) * 8;
-    kbase[u] = (const uint16_t*)a.k + (bos + r0) * a.k_stride + hq * KD + d8;
-    qbase[u] = kOut ? (const uint16_t*)a.q + (bos + r0) * a.q_stride + hq * KD + d8 : nullptr;
-    vbase[u] = load_v ? (const uint16_t*)a.v + (bos + r0) * a.v_stride + (int64_t)h * a.V + v0 + d8 : nullptr;
-  }
-  const float* tbase = a.tbuf + (int64_t)h * 2560 + 4 * tid;
-  const int64_t tslot_stride = (int64_t)a.Hv * 2560;
-  const float* gbase = a.g + (bos + tid) * a.Hv + h;
-  const float* bbase = a.beta + (bos + tid) * a.Hv + h;
+  // consecutive banks; the 16-byte global loads of the column groups of a row
+  // come from neighbouring waves and meet in the caches.
+  static_assert(NPAIR == 1, "the prefetch below is written for 512 threads");
+  const int r0_pf = 2 * (tid & 31), d8_pf = (tid >> 5) * 8;
+  // base pointers at the sequence start; the prefetch adds the token offset
+  // t0 - bos + row, with row clamped to the chunk's last valid token
+  const uint16_t* kbase = (const uint16_t*)a.k + bos * a.k_stride + hq * KD + d8_pf;
+  const uint16_t* qbase = kOut ? (const uint16_t*)a.q + bos * a.q_stride + hq * KD + d8_pf : kbase;
+  const int64_t q_stride = kOut ? a.q_stride : a.k_stride;
+  // without values (M columns) the v loads re-read k and are discarded
+  const uint16_t* vbase =
+      load_v ? (const uint16_t*)a.v + bos * a.v_stride + (int64_t)h * a.V + v0 + d8_pf : kbase;
+  const int64_t v_stride = load_v ? a.v_stride : a.k_stride;
+  const unsigned char* rbase = (const unsigned char*)a.tbuf + (int64_t)h * PREP_RECORD_BYTES + 16 * tid;
+  const int64_t rslot_stride = (int64_t)a.Hv * PREP_RECORD_BYTES;
 
   // ---- initial state: S[ct][dt][e] = S[16 dt + 4 g4 + e][col_base + 16 ct + c16]
   f32x4 S[NCT][8];
@@ -174,40 +171,31 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   for (int i = tid; i < (2 + 4) * CH * TP; i += NT) sP[i] = 0;
 
   // ---- prefetch registers --------------------------------------------------
-  uint4 pk[2 * NPAIR], pq[2 * NPAIR], pv[2 * NPAIR];
-  float4 pt[NTF];
-  float pg = 0.f, pb = 0.f;
-  auto prefetch = [&](int64_t t0) {
-    const int64_t rel = t0 - bos;
-    const int L = (int)((eos - t0) < CH ? (eos - t0) : CH);
-#pragma unroll
-    for (int u = 0; u < NPAIR; ++u) {
-      const int pid = tid + u * NT;
-      const int r0 = 2 * (pid & 31);
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        uint4 kz = make_uint4(0, 0, 0, 0), qz = kz, vz = kz;
-        if (r0 + x < L) {
-          kz = *reinterpret_cast<const uint4*>(kbase[u] + (rel + x) * a.k_stride);
-          if (kOut) qz = *reinterpret_cast<const uint4*>(qbase[u] + (rel + x) * a.q_stride);
-          if (load_v) vz = *reinterpret_cast<const uint4*>(vbase[u] + (rel + x) * a.v_stride);
-        }
-        pk[2 * u + x] = kz;
-        pq[2 * u + x] = qz;
-        pv[2 * u + x] = vz;
-      }
-    }
-    const float* ts = tbase + ((t0 >> 6) + seq) * tslot_stride;
-#pragma unroll
-    for (int u = 0; u < NTF; ++u)
-      if (tid + u * NT < 640) pt[u] = *reinterpret_cast<const float4*>(ts + 4 * u * NT);
-    if (tid < 64) {
-      const bool ok = tid < L;
-      pg = ok ? gbase[rel * a.Hv] : 0.f;
-      pb = ok ? bbase[rel * a.Hv] : 0.f;
-    }
-  };
-  if (bos < eos) prefetch(bos);
+  // Every prefetch load is unconditional (rows past the end of the sequence
+  // re-read its last row and are zeroed when stashed; record units past the
+  // end re-read the last unit), so the loads form one branch-free batch that
+  // stays in flight while the current chunk computes.
+  static_assert(NREC == 4, "record prefetch is written for 4 units per thread");
+  u32x4 pk0, pk1, pq0, pq1, pv0, pv1, pr0, pr1, pr2, pr3;
+#define GDN_PREFETCH(T0)                                                                      \
+  do {                                                                                        \
+    const int64_t rel_ = (T0) - bos;                                                          \
+    const int L_ = (int)((eos - (T0)) < CH ? (eos - (T0)) : CH);                              \
+    const int64_t row0_ = rel_ + (r0_pf < L_ ? r0_pf : L_ - 1);                               \
+    const int64_t row1_ = rel_ + (r0_pf + 1 < L_ ? r0_pf + 1 : L_ - 1);                       \
+    pk0 = *reinterpret_cast<const u32x4*>(kbase + row0_ * a.k_stride);                        \
+    pk1 = *reinterpret_cast<const u32x4*>(kbase + row1_ * a.k_stride);                        \
+    pq0 = *reinterpret_cast<const u32x4*>(qbase + row0_ * q_stride);                          \
+    pq1 = *reinterpret_cast<const u32x4*>(qbase + row1_ * q_stride);                          \
+    pv0 = *reinterpret_cast<const u32x4*>(vbase + row0_ * v_stride);                          \
+    pv1 = *reinterpret_cast<const u32x4*>(vbase + row1_ * v_stride);                          \
+    const unsigned char* rs_ = rbase + (((T0) >> 6) + seq) * rslot_stride;                    \
+    pr0 = *reinterpret_cast<const u32x4*>(rs_);                                               \
+    pr1 = *reinterpret_cast<const u32x4*>(rs_ + 16 * NT);                                     \
+    pr2 = *reinterpret_cast<const u32x4*>(rs_ + 32 * NT);                                     \
+    pr3 = *reinterpret_cast<const u32x4*>(rs_ + (tid + 3 * NT < REC_UNITS ? 48 * NT : 16 * (REC_UNITS - 1 - tid))); \
+  } while (0)
+  if (bos < eos) GDN_PREFETCH(bos);
 
   // Flush of the fp32 O tile staged in LDS (rows < L of the chunk at t0).
   auto flush_o = [&](int64_t t0, int L) {
@@ -243,126 +231,66 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
     const int L = (int)((eos - t0) < CH ? (eos - t0) : CH);
     __syncthreads();  // the previous chunk is fully consumed
 
+    // ---- flush the previous O tile; stash q, k, v (not over sT2) ------------
     if (kOut && prev_t0 >= 0) flush_o(prev_t0, prev_L);
-
-    // ---- stash the prefetched chunk in LDS --------------------------------
-#pragma unroll
-    for (int u = 0; u < NPAIR; ++u) {
-      const int pid = tid + u * NT;
-      const int r0 = 2 * (pid & 31), d8 = (pid >> 5) * 8;
-      const uint4 k0 = pk[2 * u], k1 = pk[2 * u + 1], v0v = pv[2 * u], v1v = pv[2 * u + 1];
-      *reinterpret_cast<uint4*>(sK + r0 * QP + d8) = k0;
-      *reinterpret_cast<uint4*>(sK + (r0 + 1) * QP + d8) = k1;
+    {
+      const int r0 = r0_pf, d8 = d8_pf;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const bool ok0 = r0 < L, ok1 = r0 + 1 < L;
+      const u32x4 k0 = ok0 ? pk0 : z, k1 = ok1 ? pk1 : z;
+      const u32x4 v0v = (load_v && ok0) ? pv0 : z, v1v = (load_v && ok1) ? pv1 : z;
       if (kOut) {
-        *reinterpret_cast<uint4*>(sQ + r0 * QP + d8) = pq[2 * u];
-        *reinterpret_cast<uint4*>(sQ + (r0 + 1) * QP + d8) = pq[2 * u + 1];
+        *reinterpret_cast<u32x4*>(sQ + r0 * QP + d8) = ok0 ? pq0 : z;
+        *reinterpret_cast<u32x4*>(sQ + (r0 + 1) * QP + d8) = ok1 ? pq1 : z;
       }
-      const uint32_t kw0[4] = {k0.x, k0.y, k0.z, k0.w};
-      const uint32_t kw1[4] = {k1.x, k1.y, k1.z, k1.w};
-      const uint32_t vw0[4] = {v0v.x, v0v.y, v0v.z, v0v.w};
-      const uint32_t vw1[4] = {v1v.x, v1v.y, v1v.z, v1v.w};
 #pragma unroll
       for (int jx = 0; jx < 4; ++jx) {
         const int d0 = d8 + 2 * jx, d1 = d0 + 1;
-        *reinterpret_cast<uint32_t*>(sKt + d0 * TP + r0) = (kw0[jx] & 0xFFFFu) | (kw1[jx] << 16);
-        *reinterpret_cast<uint32_t*>(sKt + d1 * TP + r0) = (kw0[jx] >> 16) | (kw1[jx] & 0xFFFF0000u);
-        *reinterpret_cast<uint32_t*>(sVt + d0 * TP + r0) = (vw0[jx] & 0xFFFFu) | (vw1[jx] << 16);
-        *reinterpret_cast<uint32_t*>(sVt + d1 * TP + r0) = (vw0[jx] >> 16) | (vw1[jx] & 0xFFFF0000u);
+        *reinterpret_cast<uint32_t*>(sKt + d0 * TP + r0) = (k0[jx] & 0xFFFFu) | (k1[jx] << 16);
+        *reinterpret_cast<uint32_t*>(sKt + d1 * TP + r0) = (k0[jx] >> 16) | (k1[jx] & 0xFFFF0000u);
+        if (load_v) {
+          *reinterpret_cast<uint32_t*>(sVt + d0 * TP + r0) = (v0v[jx] & 0xFFFFu) | (v1v[jx] << 16);
+          *reinterpret_cast<uint32_t*>(sVt + d1 * TP + r0) = (v0v[jx] >> 16) | (v1v[jx] & 0xFFFF0000u);
+        }
       }
     }
-    if (wave == 0) {
-      double G = (double)pg;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const double o = __shfl_up(G, off, 64);
-        if (lane >= off) G += o;
-      }
-      const double Glast = __shfl(G, 63, 64);
-      sG[lane] = G;
-      sBeta[lane] = pb;
-      sGam[lane] = expf((float)G);
-      sDec[lane] = expf((float)(Glast - G));
-    }
-    __syncthreads();  // A: chunk data and gates in LDS; O tile flushed
+    if (kOut) __syncthreads();  // the O tile is flushed before sT2 is rewritten
 
-    // ---- T diag(beta e^G), T diag(beta) as bf16 pairs, from the T registers
-    // (upper tiles (0,1), (2,3) re-zeroed: the O tile overwrote them)
+    // ---- stash the prep record: T products (sT2), P (sP), gamma, dec -------
+    {
+      const u32x4 prv[4] = {pr0, pr1, pr2, pr3};
 #pragma unroll
-    for (int u = 0; u < NTF; ++u) {
-      const int f = tid + u * NT;
-      if (f < 640) {
-        int bi, bj;
-        tile_ij(f >> 6, bi, bj);
-        const int e4 = (f & 63) * 4;
-        const int r = 16 * bi + (e4 >> 4), s0 = 16 * bj + (e4 & 15);
-        const float4 b4 = *reinterpret_cast<const float4*>(sBeta + s0);
-        const float4 y4 = *reinterpret_cast<const float4*>(sGam + s0);
-        const float u0 = pt[u].x * b4.x, u1 = pt[u].y * b4.y, u2 = pt[u].z * b4.z, u3 = pt[u].w * b4.w;
-        uint32_t a0, a1, b0, b1, c0, c1, e0, e1;
-        split2(u0 * y4.x, u1 * y4.y, a0, b0);
-        split2(u2 * y4.z, u3 * y4.w, a1, b1);
-        split2(u0, u1, c0, e0);
-        split2(u2, u3, c1, e1);
-        const u32x2 wh = {a0, a1}, wl = {b0, b1}, uh = {c0, c1}, ul = {e0, e1};
-        *reinterpret_cast<u32x2*>(sT2 + 0 * CH * TP + r * TP + s0) = wh;
-        *reinterpret_cast<u32x2*>(sT2 + 1 * CH * TP + r * TP + s0) = wl;
-        *reinterpret_cast<u32x2*>(sT2 + 2 * CH * TP + r * TP + s0) = uh;
-        *reinterpret_cast<u32x2*>(sT2 + 3 * CH * TP + r * TP + s0) = ul;
+      for (int u = 0; u < 4; ++u) {
+        const int f = tid + u * NT;
+        if (f < REC_MAT_UNITS) {
+          const int mat = f / 320, rem = f - 320 * mat;
+          if (mat < 4 || kOut) {
+            int bi, bj;
+            tile_ij(rem >> 5, bi, bj);
+            const int r = 16 * bi + ((rem >> 1) & 15), c = 16 * bj + 8 * (rem & 1);
+            uint16_t* dst = mat < 4 ? sT2 + mat * CH * TP : sP + (mat - 4) * CH * TP;
+            *reinterpret_cast<u32x4*>(dst + r * TP + c) = prv[u];
+          }
+        } else if (f < REC_UNITS) {
+          const int g = f - REC_MAT_UNITS;  // 0..15 gamma, 16..31 dec
+          float* dst = g < 16 ? sGam + 4 * g : sDec + 4 * (g - 16);
+          *reinterpret_cast<u32x4*>(dst) = prv[u];
+        }
       }
     }
     if (kOut) {
-      // zero tiles (0,1) and (2,3) of the four T matrices: 4 x 2 x 16 rows x 16 cols
+      // zero tiles (0,1) and (2,3) of the four T matrices (the O tile overwrote them)
       for (int i = tid; i < 4 * 2 * 16 * 4; i += NT) {
         const int mat = i >> 7, which = (i >> 6) & 1, rr = (i >> 2) & 15, c4 = (i & 3) * 4;
         const int r = which ? 32 + rr : rr, c = which ? 48 + c4 : 16 + c4;
         *reinterpret_cast<u32x2*>(sT2 + mat * CH * TP + r * TP + c) = u32x2{0u, 0u};
       }
     }
-    // ---- P = lower(Q K^T * decay) as bf16 pairs -----------------------------
-    if (kOut) {
-      constexpr int NPT = (10 + NW - 1) / NW;  // Gram tiles per wave
-      f32x4 acc[NPT];
-#pragma unroll
-      for (int u = 0; u < NPT; ++u) zero4(acc[u]);
-#pragma unroll
-      for (int m = 0; m < KD / 32; ++m) {
-#pragma unroll
-        for (int u = 0; u < NPT; ++u) {
-          const int t = wave + NW * u;
-          if (t < 10) {
-            int i, j;
-            tile_ij(t, i, j);
-            const bf16x8 fa = lds_frag(sQ, QP, 16 * i + c16, 32 * m, g4);
-            const bf16x8 fb = lds_frag(sK, QP, 16 * j + c16, 32 * m, g4);
-            acc[u] = mfma16(fa, fb, acc[u]);
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < NPT; ++u) {
-        const int t = wave + NW * u;
-        if (t < 10) {
-          int i, j;
-          tile_ij(t, i, j);
-          const int s = 16 * j + c16;
-          const double Gs = sG[s];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * i + 4 * g4 + e;
-            const float val = (r >= s) ? acc[u][e] * expf((float)(sG[r] - Gs)) : 0.f;
-            uint32_t hi, lo;
-            split2(val, 0.f, hi, lo);
-            sP[r * TP + s] = (uint16_t)hi;
-            sP[CH * TP + r * TP + s] = (uint16_t)lo;
-          }
-        }
-      }
-    }
     // ---- fetch the next chunk while this one computes -----------------------
-    if (t0 + CH < eos) prefetch(t0 + CH);
-    __syncthreads();  // B: sT2, sP ready; sK no longer read
+    if (t0 + CH < eos) GDN_PREFETCH(t0 + CH);
+    __syncthreads();  // A: chunk data in LDS
 
-    // ---- -W = -(T diag(beta e^G) K) rows -> sWn (over sK) -------------------
+    // ---- -W = -(T diag(beta e^G) K) rows -> sWn ------------------------------
     // All hi products first, then all lo products: consecutive MFMAs never
     // share an accumulator.
     {
@@ -422,7 +350,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
         SCHED_FENCE();
       }
     }
-    __syncthreads();  // C: -W complete, sT2 free for the O tile
+    __syncthreads();  // B: -W complete, sT2 free for the O tile
 
     // ---- state step -------------------------------------------------------
     // U = U0 - W S and Q S share each 32-row k-step of the split state; within
@@ -552,6 +480,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
     flush_o(prev_t0, prev_L);
   }
 
+#undef GDN_PREFETCH
   // ---- final state ----------------------------------------------------------
   float* dst = nullptr;
   int64_t row_stride = 0;
@@ -573,7 +502,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   }
 }
 
-constexpr int kScanWaves = 4;
+constexpr int kScanWaves = 8;  // the prefetch code assumes 512 threads
 
 template <int kMode>
 hipError_t launch_scan(const ChunkArgs& a, Pass1 p1, dim3 grid, hipStream_t stream) {
@@ -590,10 +519,11 @@ hipError_t launch_scan(const ChunkArgs& a, Pass1 p1, dim3 grid, hipStream_t stre
 hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t stream) {
   if (a.n_seqs == 0 || a.Hv == 0) return hipSuccess;
   if (a.K != KD || a.V % BV != 0 || a.tbuf == nullptr) return hipErrorInvalidValue;
-  hipError_t e = launch_chunk_prep(a, stream);
+  const bool with_o = a.o != nullptr && a.q != nullptr;
+  hipError_t e = launch_chunk_prep(a, with_o ? 1 : 0, stream);
   if (e != hipSuccess) return e;
   const dim3 grid(a.V / BV, a.Hv, a.n_seqs);
-  if (a.o == nullptr || a.q == nullptr) {
+  if (!with_o) {
     // state only: run the scan without outputs
     return launch_scan<kPass1>(a, Pass1{0, nullptr}, grid, stream);
   }
@@ -604,7 +534,7 @@ hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t stream) {
 hipError_t launch_segment_pass1(const ChunkArgs& a, float* M, float* b, hipStream_t stream) {
   if (a.n_seqs == 0 || a.Hv == 0) return hipSuccess;
   if (a.K != KD || a.V % BV != 0 || a.tbuf == nullptr) return hipErrorInvalidValue;
-  hipError_t e = launch_chunk_prep(a, stream);
+  hipError_t e = launch_chunk_prep(a, 0, stream);
   if (e != hipSuccess) return e;
   ChunkArgs c = a;
   c.q = nullptr;

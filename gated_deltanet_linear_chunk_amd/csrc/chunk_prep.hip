@@ -1,22 +1,26 @@
-// chunk_prep.hip -- per-chunk UT transform matrix T = (I + A)^{-1}, in parallel.
+// chunk_prep.hip -- everything of a chunk that does not depend on the state.
 //
 // For a 64-token chunk with local tokens r, s and in-chunk cumulative gate
-// G (fp64), A = strictly-lower(diag(beta) K K^T * e^{G_r - G_s}) and
-// T = (I + A)^{-1} is unit lower triangular.  T depends only on k, g and beta
-// of its own chunk, never on the recurrent state, so it is computed here for
-// every (chunk, v-head) at once, off the serial chunk scan, and stored in fp32.
+// G (fp64):
+//   A = strictly-lower(diag(beta) K K^T * e^{G_r - G_s}),  T = (I + A)^{-1},
+//   P = lower(Q K^T * e^{G_r - G_s}),
+//   gamma_r = e^{G_r},  dec_r = e^{G_last - G_r}.
+// None of these depends on the recurrent state, so they are computed here for
+// every (chunk, v-head) at once, off the serial chunk scan, which then only
+// multiplies them against its state.
 //
-// One wave owns one (chunk slot, v-head), so there is no cross-wave
-// synchronisation and many waves share a compute unit: the K fragments come
-// straight from global memory into the 16 x 16 x 32 bf16 MFMA for K K^T (exact
-// products, fp32 sums); the mask is applied in registers; the four 16 x 16
-// diagonal blocks are inverted by forward substitution (lane = block, column);
-// the block rows follow from T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj with each
-// lane producing four entries of a block row.
+// One wave owns one (chunk slot, v-head): K and Q fragments come straight from
+// global memory into the 16 x 16 x 32 bf16 MFMA (exact products, fp32 sums);
+// masks are applied in registers; the four 16 x 16 diagonal blocks of T are
+// inverted by forward substitution (lane = block, column) and the block rows
+// follow from T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj.
 //
-// Storage: the 10 lower 16 x 16 blocks (i >= j, index i(i+1)/2 + j), row-major
-// inside a block, zeros above the diagonal of diagonal blocks:
-//   tbuf[((slot * Hv + h) * 10 + blk) * 256 + 16 * r + c].
+// Record per (chunk slot, v-head), PREP_RECORD_BYTES long:
+//   6 bf16 matrices x 10 lower 16 x 16 tiles (i >= j, index i(i+1)/2 + j,
+//   row-major inside a tile), in the order
+//     T diag(beta e^G) hi, lo;  T diag(beta) hi, lo;  P hi, lo
+//   (hi = bf16(x), lo = bf16(x - hi)), then gamma[64] and dec[64] in fp32.
+// Without outputs (state-only runs) the P tiles are not written.
 // Chunk slots: chunk j of sequence n (first token cu[n] + 64 j) has slot
 // floor((cu[n] + 64 j) / 64) + n, which is unique and below
 // ceil(T / 64) + n_seqs; unused slots are skipped.
@@ -29,7 +33,7 @@ namespace {
 
 constexpr int CH = 64;
 constexpr int KD = 128;
-constexpr int BP = 17;  // fp32 pitch of a 16 x 16 block in LDS
+constexpr int BP = 17;  // fp32 pitch of a 16 x 16 tile in LDS
 
 __device__ __forceinline__ int64_t seq_begin(const ChunkArgs& a, int n) {
   return a.cu ? (int64_t)clampi(a.cu[n], 0, a.Ttot) : (int64_t)n * a.row_len;
@@ -37,12 +41,17 @@ __device__ __forceinline__ int64_t seq_begin(const ChunkArgs& a, int n) {
 
 __device__ __forceinline__ int blk(int i, int j) { return (i * (i + 1)) / 2 + j; }
 
-__global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a) {
+__device__ __forceinline__ void tile_rc(int b, int& i, int& j) {
+  i = b >= 6 ? 3 : (b >= 3 ? 2 : (b >= 1 ? 1 : 0));
+  j = b - (i * (i + 1)) / 2;
+}
+
+__global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p) {
   __shared__ float sA[10][16][BP];
-  __shared__ float sT[10][16][BP];
+  __shared__ float sT[10][16][BP];  // P staging, then T
   __shared__ float sY[16][BP];
   __shared__ double sG[CH];
-  __shared__ float sBeta[CH];
+  __shared__ float sBeta[CH], sGam[CH];
 
   const int lane = threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
@@ -68,22 +77,33 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a) {
   if (t0 >= eos) return;  // unused slot
   const int L = (int)((eos - t0) < CH ? (eos - t0) : CH);
 
-  // ---- gates ----------------------------------------------------------------
+  unsigned char* rec = (unsigned char*)a.tbuf + ((int64_t)slot * a.Hv + h) * PREP_RECORD_BYTES;
+  uint16_t* rmat = (uint16_t*)rec;  // [6][10][256]
+  float* rgam = (float*)(rec + 6 * 10 * 256 * 2);
+  float* rdec = rgam + CH;
+
+  // ---- gates: G (fp64 prefix sum), gamma, dec ---------------------------------
   {
     const bool ok = lane < L;
     double G = ok ? (double)a.g[(t0 + lane) * a.Hv + h] : 0.0;
-    sBeta[lane] = ok ? a.beta[(t0 + lane) * a.Hv + h] : 0.f;
+    const float b = ok ? a.beta[(t0 + lane) * a.Hv + h] : 0.f;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const double o = __shfl_up(G, off, 64);
       if (lane >= off) G += o;
     }
+    const double Glast = __shfl(G, 63, 64);
+    const float gam = expf((float)G);
     sG[lane] = G;
+    sBeta[lane] = b;
+    sGam[lane] = gam;
+    rgam[lane] = gam;
+    rdec[lane] = expf((float)(Glast - G));
   }
 
-  // ---- K fragments straight from global memory: row tile i, k-step m -------
-  // (contiguous k = 32 m + 8 g4 .. +7 in both operands; rows past L are zero)
-  const uint16_t* kg = (const uint16_t*)a.k + (int64_t)hq * KD + 8 * g4;
+  // ---- K (and Q) fragments straight from global memory ----------------------
+  // row tile i, k-step m: contiguous k = 32 m + 8 g4 .. +7; rows past L are 0
+  const int64_t head_off = (int64_t)hq * KD + 8 * g4;
   bf16x8 kf[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -91,13 +111,56 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (r < L) v = *reinterpret_cast<const u32x4*>(kg + (t0 + r) * a.k_stride + 32 * m);
+      if (r < L) v = *reinterpret_cast<const u32x4*>((const uint16_t*)a.k + (t0 + r) * a.k_stride + head_off + 32 * m);
       kf[i][m] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  __syncthreads();  // sG, sBeta visible to all lanes
+  __syncthreads();  // gates visible to all lanes
 
-  // ---- A = strictly-lower(diag(beta) K K^T * decay), 10 tiles ---------------
+  // ---- P = lower(Q K^T * decay) -> record (hi, lo) ----------------------------
+  if (with_p) {
+    bf16x8 qf[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * i + c16;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (r < L) v = *reinterpret_cast<const u32x4*>((const uint16_t*)a.q + (t0 + r) * a.q_stride + head_off + 32 * m);
+        qf[i][m] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j <= i; ++j) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc = mfma16(qf[i][m], kf[j][m], acc);
+        const int s = 16 * j + c16;
+        const double Gs = sG[s];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = 4 * g4 + e, r = 16 * i + rr;
+          sT[blk(i, j)][rr][c16] = (r >= s) ? acc[e] * expf((float)(sG[r] - Gs)) : 0.f;
+        }
+      }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 10; ++u) {
+      const int f = lane + 64 * u;  // 4-element group: tile f/64, element 4 (f % 64)
+      const int b = f >> 6, e4 = (f & 63) * 4, rr = e4 >> 4, cc = e4 & 15;
+      const float* src = &sT[b][rr][cc];
+      uint32_t h0, l0, h1, l1;
+      split2(src[0], src[1], h0, l0);
+      split2(src[2], src[3], h1, l1);
+      *reinterpret_cast<u32x2*>(rmat + (4 * 10 + b) * 256 + e4) = u32x2{h0, h1};
+      *reinterpret_cast<u32x2*>(rmat + (5 * 10 + b) * 256 + e4) = u32x2{l0, l1};
+    }
+    __syncthreads();  // sT is reused for T
+  }
+
+  // ---- A = strictly-lower(diag(beta) K K^T * decay) ---------------------------
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -115,7 +178,7 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a) {
     }
   __syncthreads();
 
-  // ---- diagonal blocks: lane = (block b, column c) ---------------------------
+  // ---- T: diagonal blocks, lane = (block b, column c) -------------------------
   {
     const int b = g4, c = c16;
     const float(*Ab)[BP] = sA[blk(b, b)];
@@ -132,7 +195,7 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a) {
   }
   __syncthreads();
 
-  // ---- block rows: lane = (row rr, columns 4 c4 .. 4 c4 + 3) ----------------
+  // ---- T: block rows, lane = (row rr, columns 4 c4 .. 4 c4 + 3) ---------------
   {
     const int rr = lane >> 2, c4 = (lane & 3) * 4;
     for (int i = 1; i < 4; ++i) {
@@ -175,14 +238,30 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a) {
     }
   }
 
-  // ---- write the 10 blocks: 640 float4, 10 per lane --------------------------
-  float* out = a.tbuf + ((int64_t)slot * a.Hv + h) * 2560;
+  // ---- T diag(beta e^G), T diag(beta) as bf16 pairs -> record -----------------
 #pragma unroll
   for (int u = 0; u < 10; ++u) {
     const int f = lane + 64 * u;
     const int b = f >> 6, e4 = (f & 63) * 4, rr = e4 >> 4, cc = e4 & 15;
+    int bi, bj;
+    tile_rc(b, bi, bj);
+    const int s = 16 * bj + cc;
     const float* src = &sT[b][rr][cc];
-    *reinterpret_cast<float4*>(out + 4 * f) = make_float4(src[0], src[1], src[2], src[3]);
+    float tb[4], tw[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      tb[x] = src[x] * sBeta[s + x];
+      tw[x] = tb[x] * sGam[s + x];
+    }
+    uint32_t wh0, wl0, wh1, wl1, uh0, ul0, uh1, ul1;
+    split2(tw[0], tw[1], wh0, wl0);
+    split2(tw[2], tw[3], wh1, wl1);
+    split2(tb[0], tb[1], uh0, ul0);
+    split2(tb[2], tb[3], uh1, ul1);
+    *reinterpret_cast<u32x2*>(rmat + (0 * 10 + b) * 256 + e4) = u32x2{wh0, wh1};
+    *reinterpret_cast<u32x2*>(rmat + (1 * 10 + b) * 256 + e4) = u32x2{wl0, wl1};
+    *reinterpret_cast<u32x2*>(rmat + (2 * 10 + b) * 256 + e4) = u32x2{uh0, uh1};
+    *reinterpret_cast<u32x2*>(rmat + (3 * 10 + b) * 256 + e4) = u32x2{ul0, ul1};
   }
 }
 
@@ -190,10 +269,10 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a) {
 
 int64_t chunk_slots(int64_t Ttot, int n_seqs) { return (Ttot + 63) / 64 + n_seqs; }
 
-hipError_t launch_chunk_prep(const ChunkArgs& a, hipStream_t stream) {
+hipError_t launch_chunk_prep(const ChunkArgs& a, int with_p, hipStream_t stream) {
   const int64_t slots = chunk_slots(a.Ttot, a.n_seqs);
   if (slots == 0 || a.Hv == 0) return hipSuccess;
-  hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)slots, a.Hv), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)slots, a.Hv), dim3(64), 0, stream, a, with_p);
   return hipGetLastError();
 }
 

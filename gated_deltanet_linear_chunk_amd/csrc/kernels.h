@@ -39,13 +39,18 @@ struct ChunkArgs {
   // sf + seq * sf_seq_stride + h * sf_head_stride + i * sf_row_stride + j
   float* sf;
   int64_t sf_seq_stride, sf_head_stride, sf_row_stride;
-  // bf16 path: per-chunk T = (I + A)^{-1} blocks, chunk_slots(Ttot, n_seqs) * Hv * 2560 floats
+  // bf16 path: per-(chunk slot, v-head) records of the state-independent chunk
+  // quantities, chunk_slots(Ttot, n_seqs) * Hv * PREP_RECORD_BYTES bytes
   float* tbuf;
 };
 
+// One record: 6 bf16 matrices x 10 tiles x 256, then gamma[64], dec[64] fp32.
+constexpr int PREP_RECORD_BYTES = 6 * 10 * 256 * 2 + 2 * 64 * 4;
+
 // Number of chunk slots a launch over Ttot tokens in n_seqs sequences uses.
 int64_t chunk_slots(int64_t Ttot, int n_seqs);
-hipError_t launch_chunk_prep(const ChunkArgs& a, hipStream_t stream);
+// with_p: also form the output matrix P (needs q).
+hipError_t launch_chunk_prep(const ChunkArgs& a, int with_p, hipStream_t stream);
 
 hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t stream);
 hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t stream);
