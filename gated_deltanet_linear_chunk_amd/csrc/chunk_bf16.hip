@@ -1,31 +1,33 @@
 // chunk_bf16.hip -- serial chunk scan of the gated delta rule on gfx950 MFMA.
 //
-// One workgroup owns one (sequence or segment, v-head, 128-column slice of V)
-// and walks its 64-token chunks in order.  The K x 128 fp32 state never leaves
-// the registers: with NW waves, wave w holds state columns (128/NW) w .. as
-// 16 x 16 accumulator tiles.  Everything about a chunk that does not depend on
-// the state (the UT-transform products T diag(beta e^G) and T diag(beta), the
-// masked Q K^T, e^G and the decays) comes precomputed from the prep kernel
-// (chunk_prep.hip); per chunk (local tokens r, s) the scan then does
-//   W  = T diag(beta e^G) K,  U0 = T diag(beta) V                 (MFMA)
-//   U  = U0 - W S,  O = diag(e^G) Q S + P U,
-//   S <- e^{G_last} S + K^T diag(e^{G_last - G}) U       (MFMA, S in fp32)
-// which is the token recurrence regrouped by chunk.  The next chunk's q, k, v
-// and prep record are fetched into registers while the current chunk
-// computes; O goes through LDS so that its global stores are 16-byte vectors.
+// One workgroup (8 waves) owns one (sequence or segment, v-head, 128-column
+// slice of V) and walks its 64-token chunks in order.  The K x 128 fp32 state
+// never leaves the registers: wave w holds state columns 16 w .. 16 w + 15 as
+// eight 16 x 16 accumulator tiles.  Everything about a chunk that does not
+// depend on the state -- the UT-transform products -T diag(beta e^G) and
+// T diag(beta) (T = (I + A)^{-1}), the masked Q K^T, e^G and the decays --
+// comes precomputed from the prep kernel (chunk_prep.hip).  Per chunk (local
+// tokens r, s), each wave then does, for its own columns and without any
+// further synchronisation:
+//   U  = T diag(beta) V - T diag(beta e^G) (K S)    (= U0 - W S)
+//   O  = diag(e^G) Q S + P U
+//   S <- e^{G_last} S + K^T diag(e^{G_last - G}) U
+// which is the token recurrence regrouped by chunk.  Two barriers per chunk:
+// one before the shared tiles are overwritten, one after they are filled.
+// The next chunk's q, k, v and prep record are fetched into registers while
+// the current chunk computes; O goes through its own LDS tile so that its
+// global stores are 16-byte vectors.
 //
-// Precision: each fp32 quantity that meets the matrix cores is a bf16 pair
-// hi + lo (~16 significant bits) multiplied against exact bf16 data (q, k, v)
-// or against another pair (hi*hi + hi*lo + lo*hi): the T products against K
-// and V, S against W and Q, P against U, the decayed U against K.  W alone is
-// a single bf16 operand: W S sums 128 terms whose rounding errors average out.
+// Precision: every fp32 quantity that meets the matrix cores is a bf16 pair
+// hi + lo (~16 significant bits), multiplied against exact bf16 data (q, k,
+// v) or against another pair (hi*hi + hi*lo + lo*hi): S against K and Q, the
+// T products against V and against K S, P against U, the decayed U against K.
 //
-// LDS (bf16 unless noted; row pitches padded by 16 B, which makes the
-// fragment reads conflict-free):
-//   sQ [64][136], sW [64][136] (-W), sKt [128][72] (K^T),
-//   sVt [128][72] (V^T of this slice), sP [2][64][72] (hi, lo),
-//   sT2 [4][64][72] (T diag(beta e^G) hi/lo, T diag(beta) hi/lo; during the
-//   state step it holds the fp32 O tile [64][132]), gamma[64], dec[64] fp32.
+// LDS (bf16 unless noted; row pitches padded by 16 B, which keeps the MFMA
+// fragment reads free of bank conflicts):
+//   sQ [64][136], sK [64][136], sKt [128][72] (K^T), sVt [128][72] (V^T of
+//   this slice), sP [2][64][72] (hi, lo), sT2 [4][64][72] (-T diag(beta e^G)
+//   hi/lo, T diag(beta) hi/lo), sO fp32 [64][132], gamma[64], dec[64] fp32.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -42,16 +44,16 @@ constexpr int TP = CH + 8;
 constexpr int OP = BV + 4;  // fp32 O tile pitch
 
 constexpr int OFF_Q = 0;
-constexpr int OFF_W = OFF_Q + CH * QP * 2;
-constexpr int OFF_KT = OFF_W + CH * QP * 2;
+constexpr int OFF_K = OFF_Q + CH * QP * 2;
+constexpr int OFF_KT = OFF_K + CH * QP * 2;
 constexpr int OFF_VT = OFF_KT + KD * TP * 2;
 constexpr int OFF_P = OFF_VT + BV * TP * 2;
-constexpr int OFF_T2 = OFF_P + 2 * CH * TP * 2;  // also the fp32 O tile
-constexpr int OFF_GAM = OFF_T2 + 4 * CH * TP * 2;
+constexpr int OFF_T2 = OFF_P + 2 * CH * TP * 2;
+constexpr int OFF_O = OFF_T2 + 4 * CH * TP * 2;
+constexpr int OFF_GAM = OFF_O + CH * OP * 4;
 constexpr int OFF_DEC = OFF_GAM + CH * 4;
 constexpr int LDS_BYTES = OFF_DEC + CH * 4;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-static_assert(CH * OP * 4 <= 4 * CH * TP * 2, "O tile must fit over sT2");
 
 // 16-byte units of a prep record: 6 x 10 tiles x 32, then gamma and dec
 constexpr int REC_MAT_UNITS = 6 * 10 * 32;
@@ -86,18 +88,17 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   constexpr int NCT = CPW / 16;    // 16-column tiles per wave
   constexpr int NPAIR = 512 / NT;  // (row pair, 8 columns) units per thread per matrix
   constexpr int NREC = (REC_UNITS + NT - 1) / NT;  // record units per thread
-  constexpr int DTW = 8 / NW > 0 ? 8 / NW : 1;     // 16-row key tiles of W per wave
   constexpr bool kOut = kMode != kPass1;
   static_assert(CPW % 16 == 0 && NW * CPW == BV, "wave layout");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + OFF_Q);
-  uint16_t* sWn = reinterpret_cast<uint16_t*>(smem + OFF_W);
+  uint16_t* sK = reinterpret_cast<uint16_t*>(smem + OFF_K);
   uint16_t* sKt = reinterpret_cast<uint16_t*>(smem + OFF_KT);
   uint16_t* sVt = reinterpret_cast<uint16_t*>(smem + OFF_VT);
   uint16_t* sP = reinterpret_cast<uint16_t*>(smem + OFF_P);
   uint16_t* sT2 = reinterpret_cast<uint16_t*>(smem + OFF_T2);
-  float* sO = reinterpret_cast<float*>(smem + OFF_T2);
+  float* sO = reinterpret_cast<float*>(smem + OFF_O);
   float* sGam = reinterpret_cast<float*>(smem + OFF_GAM);
   float* sDec = reinterpret_cast<float*>(smem + OFF_DEC);
 
@@ -167,7 +168,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
       }
 
   // Upper tiles of sP and sT2 that the triangular products read must be zero;
-  // sP is never written there, sT2 is rewritten (O tile) and re-zeroed below.
+  // the record stash only ever writes the lower tiles.
   for (int i = tid; i < (2 + 4) * CH * TP; i += NT) sP[i] = 0;
 
   // ---- prefetch registers --------------------------------------------------
@@ -197,48 +198,19 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   } while (0)
   if (bos < eos) GDN_PREFETCH(bos);
 
-  // Flush of the fp32 O tile staged in LDS (rows < L of the chunk at t0).
-  auto flush_o = [&](int64_t t0, int L) {
-    if (!kOut) return;
-    // 64 rows x 128 columns; 8 columns (32 B of fp32, 16 B of bf16) per unit
-    for (int u = tid; u < CH * (BV / 8); u += NT) {
-      const int r = u >> 4, c8 = (u & 15) * 8;
-      if (r >= L) continue;
-      const float* src = sO + r * OP + c8;
-      const float4 x0 = *reinterpret_cast<const float4*>(src);
-      const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
-      const int64_t off = ((t0 + r) * a.Hv + h) * (int64_t)a.V + v0 + c8;
-      if (kMode == kOutBF16) {
-        uint4 w;
-        w.x = pack_bf16x2(a.scale * x0.x, a.scale * x0.y);
-        w.y = pack_bf16x2(a.scale * x0.z, a.scale * x0.w);
-        w.z = pack_bf16x2(a.scale * x1.x, a.scale * x1.y);
-        w.w = pack_bf16x2(a.scale * x1.z, a.scale * x1.w);
-        *reinterpret_cast<uint4*>((uint16_t*)a.o + off) = w;
-      } else {
-        float* dst = (float*)a.o + off;
-        *reinterpret_cast<float4*>(dst) =
-            make_float4(a.scale * x0.x, a.scale * x0.y, a.scale * x0.z, a.scale * x0.w);
-        *reinterpret_cast<float4*>(dst + 4) =
-            make_float4(a.scale * x1.x, a.scale * x1.y, a.scale * x1.z, a.scale * x1.w);
-      }
-    }
-  };
-
-  int64_t prev_t0 = -1;
-  int prev_L = 0;
   for (int64_t t0 = bos; t0 < eos; t0 += CH) {
     const int L = (int)((eos - t0) < CH ? (eos - t0) : CH);
-    __syncthreads();  // the previous chunk is fully consumed
+    __syncthreads();  // every wave is done with the previous chunk's tiles
 
-    // ---- flush the previous O tile; stash q, k, v (not over sT2) ------------
-    if (kOut && prev_t0 >= 0) flush_o(prev_t0, prev_L);
+    // ---- stash q, k, v and the prep record ---------------------------------
     {
       const int r0 = r0_pf, d8 = d8_pf;
       const u32x4 z = {0u, 0u, 0u, 0u};
       const bool ok0 = r0 < L, ok1 = r0 + 1 < L;
       const u32x4 k0 = ok0 ? pk0 : z, k1 = ok1 ? pk1 : z;
       const u32x4 v0v = (load_v && ok0) ? pv0 : z, v1v = (load_v && ok1) ? pv1 : z;
+      *reinterpret_cast<u32x4*>(sK + r0 * QP + d8) = k0;
+      *reinterpret_cast<u32x4*>(sK + (r0 + 1) * QP + d8) = k1;
       if (kOut) {
         *reinterpret_cast<u32x4*>(sQ + r0 * QP + d8) = ok0 ? pq0 : z;
         *reinterpret_cast<u32x4*>(sQ + (r0 + 1) * QP + d8) = ok1 ? pq1 : z;
@@ -254,121 +226,52 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
         }
       }
     }
-    if (kOut) __syncthreads();  // the O tile is flushed before sT2 is rewritten
-
-    // ---- stash the prep record: T products (sT2), P (sP), gamma, dec -------
     {
+      // Every unit is stored (no branch around a store): a unit past the end
+      // of the record holds a copy of the last unit and rewrites it in place,
+      // and in state-only runs the P units land unused in sP.
       const u32x4 prv[4] = {pr0, pr1, pr2, pr3};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int f = tid + u * NT;
+        const int f = min(tid + u * NT, REC_UNITS - 1);
+        unsigned char* dst;
         if (f < REC_MAT_UNITS) {
           const int mat = f / 320, rem = f - 320 * mat;
-          if (mat < 4 || kOut) {
-            int bi, bj;
-            tile_ij(rem >> 5, bi, bj);
-            const int r = 16 * bi + ((rem >> 1) & 15), c = 16 * bj + 8 * (rem & 1);
-            uint16_t* dst = mat < 4 ? sT2 + mat * CH * TP : sP + (mat - 4) * CH * TP;
-            *reinterpret_cast<u32x4*>(dst + r * TP + c) = prv[u];
-          }
-        } else if (f < REC_UNITS) {
+          int bi, bj;
+          tile_ij(rem >> 5, bi, bj);
+          const int r = 16 * bi + ((rem >> 1) & 15), c = 16 * bj + 8 * (rem & 1);
+          // sP (two matrices) sits right before the four matrices of sT2
+          dst = smem + OFF_T2 + 2 * ((mat < 4 ? mat : mat - 6) * CH * TP + r * TP + c);
+        } else {
           const int g = f - REC_MAT_UNITS;  // 0..15 gamma, 16..31 dec
-          float* dst = g < 16 ? sGam + 4 * g : sDec + 4 * (g - 16);
-          *reinterpret_cast<u32x4*>(dst) = prv[u];
+          dst = smem + OFF_GAM + 16 * g;
         }
-      }
-    }
-    if (kOut) {
-      // zero tiles (0,1) and (2,3) of the four T matrices (the O tile overwrote them)
-      for (int i = tid; i < 4 * 2 * 16 * 4; i += NT) {
-        const int mat = i >> 7, which = (i >> 6) & 1, rr = (i >> 2) & 15, c4 = (i & 3) * 4;
-        const int r = which ? 32 + rr : rr, c = which ? 48 + c4 : 16 + c4;
-        *reinterpret_cast<u32x2*>(sT2 + mat * CH * TP + r * TP + c) = u32x2{0u, 0u};
+        *reinterpret_cast<u32x4*>(dst) = prv[u];
       }
     }
     // ---- fetch the next chunk while this one computes -----------------------
     if (t0 + CH < eos) GDN_PREFETCH(t0 + CH);
     __syncthreads();  // A: chunk data in LDS
 
-    // ---- -W = -(T diag(beta e^G) K) rows -> sWn ------------------------------
-    // All hi products first, then all lo products: consecutive MFMAs never
-    // share an accumulator.
-    {
-      f32x4 acc[DTW][4];
-#pragma unroll
-      for (int dd = 0; dd < DTW; ++dd)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) zero4(acc[dd][rt]);
-#pragma unroll
-      for (int part = 0; part < 2; ++part) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          bf16x8 fa[DTW];
-#pragma unroll
-          for (int dd = 0; dd < DTW; ++dd) fa[dd] = lds_frag(sKt, TP, 16 * (wave * DTW + dd) + c16, 32 * m, g4);
-#pragma unroll
-          for (int rt = 2 * m; rt < 4; ++rt) {
-            const bf16x8 ft = lds_frag(sT2 + part * CH * TP, TP, 16 * rt + c16, 32 * m, g4);
-#pragma unroll
-            for (int dd = 0; dd < DTW; ++dd) acc[dd][rt] = mfma16(fa[dd], ft, acc[dd][rt]);
-          }
-          SCHED_FENCE();
-        }
-      }
-#pragma unroll
-      for (int dd = 0; dd < DTW; ++dd)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          // acc[e] = W[r = 16 rt + c16][d = 16 dt + 4 g4 + e]
-          u32x2 wv;
-          wv[0] = pack_bf16x2(-acc[dd][rt][0], -acc[dd][rt][1]);
-          wv[1] = pack_bf16x2(-acc[dd][rt][2], -acc[dd][rt][3]);
-          *reinterpret_cast<u32x2*>(sWn + (16 * rt + c16) * QP + 16 * (wave * DTW + dd) + 4 * g4) = wv;
-        }
-    }
-    // ---- U0 = T diag(beta) V for this wave's columns ------------------------
-    f32x4 U[NCT][4];
+    // From here on each wave touches only its own state columns.
+    // ---- K S and Q S over the split state (hi pass, then lo pass per k-step)
+    f32x4 KS[NCT][4], O[NCT][4];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) zero4(U[ct][rt]);
-    if (load_v) {
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        bf16x8 fb[NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) fb[ct] = lds_frag(sVt, TP, wave * CPW + 16 * ct + c16, 32 * m, g4);
-#pragma unroll
-        for (int part = 0; part < 2; ++part) {
-#pragma unroll
-          for (int rt = 2 * m; rt < 4; ++rt) {
-            const bf16x8 ft = lds_frag(sT2 + (2 + part) * CH * TP, TP, 16 * rt + c16, 32 * m, g4);
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) U[ct][rt] = mfma16(ft, fb[ct], U[ct][rt]);
-          }
-        }
-        SCHED_FENCE();
+      for (int rt = 0; rt < 4; ++rt) {
+        zero4(KS[ct][rt]);
+        zero4(O[ct][rt]);
       }
-    }
-    __syncthreads();  // B: -W complete, sT2 free for the O tile
-
-    // ---- state step -------------------------------------------------------
-    // U = U0 - W S and Q S share each 32-row k-step of the split state; within
-    // a k-step the hi products of all tiles precede the lo products.
-    f32x4 O[NCT][4];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) zero4(O[ct][rt]);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       bf16x8 sp[2][NCT];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) split_frag(S[ct][2 * m], S[ct][2 * m + 1], sp[0][ct], sp[1][ct]);
-      bf16x8 fw[4], fq[4];
+      bf16x8 fk[4], fq[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        fw[rt] = lds_frag(sWn, QP, 16 * rt + c16, 32 * m, g4);
+        fk[rt] = lds_frag(sK, QP, 16 * rt + c16, 32 * m, g4);
         if (kOut) fq[rt] = lds_frag(sQ, QP, 16 * rt + c16, 32 * m, g4);
       }
 #pragma unroll
@@ -377,13 +280,65 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) {
-            U[ct][rt] = mfma16(fw[rt], sp[part][ct], U[ct][rt]);
+            KS[ct][rt] = mfma16(fk[rt], sp[part][ct], KS[ct][rt]);
             if (kOut) O[ct][rt] = mfma16(fq[rt], sp[part][ct], O[ct][rt]);
           }
       SCHED_FENCE();
     }
+
+    // ---- U = T diag(beta) V - T diag(beta e^G) (K S) --------------------------
+    // The two sums go to separate accumulators (U, X) so that consecutive
+    // products alternate between independent tiles.
+    f32x4 U[NCT][4], X[NCT][4];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        zero4(U[ct][rt]);
+        zero4(X[ct][rt]);
+      }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      bf16x8 kh[NCT], kl[NCT], fv[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        split_frag(KS[ct][2 * m], KS[ct][2 * m + 1], kh[ct], kl[ct]);
+        if (load_v) fv[ct] = lds_frag(sVt, TP, wave * CPW + 16 * ct + c16, 32 * m, g4);
+      }
+      bf16x8 wh[4], wl[4], th[4], tl[4];
+#pragma unroll
+      for (int rt = 2 * m; rt < 4; ++rt) {
+        wh[rt] = lds_frag(sT2, TP, 16 * rt + c16, 32 * m, g4);
+        wl[rt] = lds_frag(sT2 + CH * TP, TP, 16 * rt + c16, 32 * m, g4);
+        if (load_v) {
+          th[rt] = lds_frag(sT2 + 2 * CH * TP, TP, 16 * rt + c16, 32 * m, g4);
+          tl[rt] = lds_frag(sT2 + 3 * CH * TP, TP, 16 * rt + c16, 32 * m, g4);
+        }
+      }
+#pragma unroll
+      for (int part = 0; part < 5; ++part) {
+        const bool to_u = part == 1 || part == 3;
+        if (to_u && !load_v) continue;
+#pragma unroll
+        for (int rt = 2 * m; rt < 4; ++rt)
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) {
+            if (part == 0) X[ct][rt] = mfma16(wh[rt], kh[ct], X[ct][rt]);
+            if (part == 1) U[ct][rt] = mfma16(th[rt], fv[ct], U[ct][rt]);
+            if (part == 2) X[ct][rt] = mfma16(wh[rt], kl[ct], X[ct][rt]);
+            if (part == 3) U[ct][rt] = mfma16(tl[rt], fv[ct], U[ct][rt]);
+            if (part == 4) X[ct][rt] = mfma16(wl[rt], kh[ct], X[ct][rt]);
+          }
+      }
+      SCHED_FENCE();
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) U[ct][rt] += X[ct][rt];
+
     if (kOut) {
-      // O = diag(gamma) Q S + P U  -> fp32 O tile in LDS
+      // ---- O = diag(gamma) Q S + P U  -> fp32 O tile in LDS -------------------
       bf16x8 Uhi[NCT][2], Ulo[NCT][2];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
@@ -420,6 +375,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
             }
         SCHED_FENCE();
       }
+      // Through this wave's own columns of the O tile (no other wave touches
+      // them, and a wave's LDS accesses complete in order) to 16-byte stores.
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -427,8 +384,37 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             sO[(16 * rt + 4 * g4 + e) * OP + wave * CPW + 16 * ct + c16] = O[ct][rt][e];
+      // Rows past the end of the chunk store a second copy of its last row
+      // instead, so that every store is unconditional and the memory counter
+      // waits further on stay exact.
+      constexpr int RUNS = CPW / 8;  // 8-column runs per row
+#pragma unroll
+      for (int i = 0; i < CH * RUNS / 64; ++i) {
+        const int u = lane + 64 * i;
+        const int r = min(u / RUNS, L - 1), c = wave * CPW + 8 * (u % RUNS);
+        const float* src = sO + r * OP + c;
+        const float4 x0 = *reinterpret_cast<const float4*>(src);
+        const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+        {
+          const int64_t off = ((t0 + r) * a.Hv + h) * (int64_t)a.V + v0 + c;
+          if (kMode == kOutBF16) {
+            uint4 w;
+            w.x = pack_bf16x2(a.scale * x0.x, a.scale * x0.y);
+            w.y = pack_bf16x2(a.scale * x0.z, a.scale * x0.w);
+            w.z = pack_bf16x2(a.scale * x1.x, a.scale * x1.y);
+            w.w = pack_bf16x2(a.scale * x1.z, a.scale * x1.w);
+            *reinterpret_cast<uint4*>((uint16_t*)a.o + off) = w;
+          } else {
+            float* dst = (float*)a.o + off;
+            *reinterpret_cast<float4*>(dst) =
+                make_float4(a.scale * x0.x, a.scale * x0.y, a.scale * x0.z, a.scale * x0.w);
+            *reinterpret_cast<float4*>(dst + 4) =
+                make_float4(a.scale * x1.x, a.scale * x1.y, a.scale * x1.z, a.scale * x1.w);
+          }
+        }
+      }
     }
-    // S <- e^{G_last} S + K^T (diag(dec) U)
+    // ---- S <- e^{G_last} S + K^T (diag(dec) U) -------------------------------
     {
       bf16x8 Uhi[NCT][2], Ulo[NCT][2];
 #pragma unroll
@@ -472,12 +458,6 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
           SCHED_FENCE();
         }
     }
-    prev_t0 = t0;
-    prev_L = L;
-  }
-  if (kOut && prev_t0 >= 0) {
-    __syncthreads();
-    flush_o(prev_t0, prev_L);
   }
 
 #undef GDN_PREFETCH

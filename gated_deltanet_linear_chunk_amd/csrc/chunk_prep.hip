@@ -18,7 +18,7 @@
 // Record per (chunk slot, v-head), PREP_RECORD_BYTES long:
 //   6 bf16 matrices x 10 lower 16 x 16 tiles (i >= j, index i(i+1)/2 + j,
 //   row-major inside a tile), in the order
-//     T diag(beta e^G) hi, lo;  T diag(beta) hi, lo;  P hi, lo
+//     -T diag(beta e^G) hi, lo;  T diag(beta) hi, lo;  P hi, lo
 //   (hi = bf16(x), lo = bf16(x - hi)), then gamma[64] and dec[64] in fp32.
 // Without outputs (state-only runs) the P tiles are not written.
 // Chunk slots: chunk j of sequence n (first token cu[n] + 64 j) has slot
@@ -238,7 +238,7 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p)
     }
   }
 
-  // ---- T diag(beta e^G), T diag(beta) as bf16 pairs -> record -----------------
+  // ---- -T diag(beta e^G), T diag(beta) as bf16 pairs -> record ----------------
 #pragma unroll
   for (int u = 0; u < 10; ++u) {
     const int f = lane + 64 * u;
@@ -251,7 +251,7 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p)
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       tb[x] = src[x] * sBeta[s + x];
-      tw[x] = tb[x] * sGam[s + x];
+      tw[x] = -tb[x] * sGam[s + x];  // stored negated: the scan subtracts it
     }
     uint32_t wh0, wl0, wh1, wl1, uh0, ul0, uh1, ul1;
     split2(tw[0], tw[1], wh0, wl0);
