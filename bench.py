@@ -19,6 +19,7 @@ prefill, wide state) with the same method.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -53,6 +54,38 @@ def chunk_alg_bytes(T, N, Hqk, Hv, K, V, o_bytes, in_bytes=2, s0=False):
 
 def conv_alg_bytes(T, C, in_bytes=2):
     return 2 * in_bytes * T * C
+
+
+CHUNK_SOURCES = ("chunk_prep.hip", "chunk_bf16.hip", "device_common.h", "kernels.h")
+
+
+def sources_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gated_deltanet_linear_chunk_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(workload):
+    """HBM bytes per gdn_chunk_fwd launch (FETCH_SIZE + WRITE_SIZE of its two kernels, scaled by a copy
+    calibration) from the committed rocprofv3 summary; None when the kernel sources have changed since
+    the counters were taken, or when there is no summary."""
+    path = os.path.join(ROOT, "profiles", "chunk_fwd_%s.md" % workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(("#", "|", "`")):
+                key, _, val = line.partition(":")
+                fields[key.strip()] = val.strip()
+    if fields.get("chunk_sources_sha256_16") != sources_digest(CHUNK_SOURCES):
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def _torch():
@@ -264,7 +297,8 @@ def main():
                    "o_dtype": args.o_dtype, "step": "gates + conv1d/SiLU/L2 + chunked rule"},
         "mfma_frac_chunk": flops_chunk / (chunk_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": "chunk_bf16_kernel",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": profiled_traffic(MAIN),
+                     "kernel": "gdn_chunk_fwd = chunk_prep_kernel + chunk_scan_kernel<0,8>",
                      "alg_bytes_per_launch": bytes_chunk, "alg_flops_per_launch": flops_chunk,
                      "avg_launch_ms": chunk_ms},
         "kernels_ms": {"chunk": chunk_ms, "conv1d": conv_ms},

@@ -122,10 +122,11 @@ gdn_status gdn_conv1d_fwd(const void* x, const void* w, const void* bias, gdn_dt
  * kernel (K in {32, 64}, V % 32 == 0).
  * o_dt is F32 or BF16 (round to nearest even).
  * workspace: device memory of at least gdn_chunk_fwd_workspace_bytes(...)
- * bytes (0 for F32 inputs; NULL allowed then).  The BF16 path stores there
- * the per-chunk matrices T = (I + A)^{-1} of the UT transform, which a
- * parallel pass computes before the serial chunk scan; contents on entry do
- * not matter.  Concurrent calls need separate workspaces.
+ * bytes (0 for F32 inputs; NULL allowed then).  The BF16 path stores there,
+ * per 64-token chunk and v-head, the state-independent matrices of the UT
+ * transform (products of T = (I + A)^{-1}, the masked Q K^T, the decays),
+ * which a parallel pass computes before the serial chunk scan; contents on
+ * entry do not matter.  Concurrent calls need separate workspaces.
  */
 size_t gdn_chunk_fwd_workspace_bytes(gdn_dtype in_dt, int64_t total_tokens, int32_t n_seqs,
                                      int32_t H_v, int32_t K, int32_t V);
@@ -160,7 +161,7 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, gdn_dtype 
  * seg_offsets[P] = T) and initial_state = seg_initial_states is pass 2: it
  * yields every output of the unsegmented run.
  * workspace: at least gdn_segment_state_scan_workspace_bytes(...) bytes
- * (the per-chunk T matrices of pass 1).
+ * (the per-chunk UT-transform matrices of pass 1).
  */
 size_t gdn_segment_state_scan_workspace_bytes(int64_t T, int32_t P, int32_t H_v, int32_t K,
                                               int32_t V);
@@ -181,7 +182,7 @@ gdn_status gdn_segment_state_scan(const void* k, const void* v, gdn_dtype in_dt,
  * gdn_chunk_fwd with B = 1; seg_offsets as above with seg_offsets[0] = 0 and
  * seg_offsets[P] = T.  final_state fp32 [H_v, K, V] or NULL.
  * workspace: device memory of at least gdn_segmented_workspace_bytes(...)
- * bytes, used for M, b, the composed starts and the per-chunk T matrices;
+ * bytes, used for M, b, the composed starts and the per-chunk matrices;
  * its contents on entry do not matter.
  */
 size_t gdn_segmented_workspace_bytes(int64_t T, int32_t P, int32_t H_v, int32_t K, int32_t V);
