@@ -223,17 +223,24 @@ def l2norm(x, eps: float = 1e-6) -> np.ndarray:
 
 
 def round_bf16(x) -> np.ndarray:
-    """Round fp64 values to the nearest bfloat16 value (ties to even), via exact fp32.
+    """Round values to the nearest bfloat16 value (ties to even), one rounding.
 
-    Two-step rounding (fp64 -> fp32 -> bf16) can differ from direct rounding only
-    when the fp64 value lies within one fp32 ulp of a bf16 midpoint; the result
-    is returned in fp64.
+    fp64 input is first rounded to fp32, which keeps every bit that decides the
+    bf16 result except when it lands exactly on a bf16 midpoint (the halfway
+    point between two neighbouring bf16 values); there the fp64 value itself
+    says on which side of the midpoint it lies.  The result is returned in fp64.
     """
+    x = np.asarray(x)
+    xd = x.astype(np.float64)
     f = np.ascontiguousarray(x, dtype=np.float32)
     u = f.view(np.uint32).astype(np.uint64)
     lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) & 0xFFFF0000).astype(np.uint32)
-    return r.view(np.float32).astype(np.float64).reshape(f.shape)
+    r = (u + 0x7FFF + lsb) & 0xFFFF0000
+    on_mid = (u & 0xFFFF) == 0x8000
+    ax, af = np.abs(xd), np.abs(f.astype(np.float64))
+    r = np.where(on_mid & (ax > af), (u & 0xFFFF0000) + 0x10000, r)
+    r = np.where(on_mid & (ax < af), u & 0xFFFF0000, r)
+    return r.astype(np.uint32).view(np.float32).astype(np.float64).reshape(f.shape)
 
 
 def split_channels(y, Hqk: int, Hv: int, K: int, V: int):

@@ -403,6 +403,54 @@ def test_round_bf16_matches_torch():
     assert oracle.round_bf16(np.array([1.0 + 3 * 2 ** -8]))[0] == 1.0 + 2 ** -6
 
 
+def test_round_bf16_fp64_single_rounding():
+    """fp64 values just off a bf16 midpoint round to the nearer side (not to even), checked
+    against exact rational arithmetic on random and constructed near-midpoint values."""
+    from fractions import Fraction
+
+    def nearest_bf16(v):
+        # exact: enumerate the two bf16 neighbours of v from its binade
+        fv = Fraction(v)
+        if fv == 0:
+            return 0.0
+        s = -1 if fv < 0 else 1
+        a = abs(fv)
+        e = 0
+        while a >= 2:
+            a /= 2
+            e += 1
+        while a < 1:
+            a *= 2
+            e -= 1
+        ulp = Fraction(2) ** (e - 7)
+        lo = (abs(fv) // ulp) * ulp
+        hi = lo + ulp
+        d_lo, d_hi = abs(fv) - lo, hi - abs(fv)
+        if d_lo < d_hi:
+            r = lo
+        elif d_hi < d_lo:
+            r = hi
+        else:
+            r = lo if (lo / ulp) % 2 == 0 else hi
+        return s * float(r)
+
+    assert oracle.round_bf16(np.array([1.0 + 2 ** -8 + 2 ** -40]))[0] == 1.0 + 2 ** -7
+    assert oracle.round_bf16(np.array([1.0 + 2 ** -8 - 2 ** -40]))[0] == 1.0
+    assert oracle.round_bf16(np.array([-(1.0 + 2 ** -8 + 2 ** -40)]))[0] == -(1.0 + 2 ** -7)
+    rng = np.random.default_rng(57)
+    base = oracle.round_bf16(rng.standard_normal(300) * 10 ** rng.uniform(-3, 3, 300))
+    base = base[base != 0]
+    half_ulp = 2.0 ** (np.floor(np.log2(np.abs(base))) - 8)
+    mids = base + np.sign(base) * half_ulp  # exact midpoints between bf16 neighbours
+    vals = np.concatenate([
+        rng.standard_normal(300) * 10 ** rng.uniform(-5, 5, 300),
+        mids, mids * (1 + 2.0 ** -45), mids * (1 - 2.0 ** -45), mids * (1 + 2.0 ** -30),
+    ])
+    got = oracle.round_bf16(vals)
+    want = np.array([nearest_bf16(float(v)) for v in vals])
+    np.testing.assert_array_equal(got, want)
+
+
 def test_pipeline_activations_split_and_norm():
     w = gdn_inputs.Workload("t", 5, 40, 2, 1, 2, 8, 4, "bf16", conv_width=4, lengths=[25, 15])
     d = gdn_inputs.draw(w)
