@@ -174,28 +174,40 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   // ---- prefetch registers --------------------------------------------------
   // Every prefetch load is unconditional (rows past the end of the sequence
   // re-read its last row and are zeroed when stashed; record units past the
-  // end re-read the last unit), so the loads form one branch-free batch that
-  // stays in flight while the current chunk computes.
+  // end re-read the last unit).  The next chunk's loads are issued in three
+  // groups between the compute phases of the current one, so that the
+  // vector memory pipeline works through them while the matrix cores run
+  // instead of holding up a barrier.
   static_assert(NREC == 4, "record prefetch is written for 4 units per thread");
   u32x4 pk0, pk1, pq0, pq1, pv0, pv1, pr0, pr1, pr2, pr3;
-#define GDN_PREFETCH(T0)                                                                      \
+#define GDN_PF_ROWS(T0)                                                                        \
+  const int64_t rel_ = (T0) - bos;                                                            \
+  const int L_ = (int)((eos - (T0)) < CH ? (eos - (T0)) : CH);                                \
+  const int64_t row0_ = rel_ + (r0_pf < L_ ? r0_pf : L_ - 1);                                 \
+  const int64_t row1_ = rel_ + (r0_pf + 1 < L_ ? r0_pf + 1 : L_ - 1);
+#define GDN_PF_REC(T0)                                                                         \
   do {                                                                                        \
-    const int64_t rel_ = (T0) - bos;                                                          \
-    const int L_ = (int)((eos - (T0)) < CH ? (eos - (T0)) : CH);                              \
-    const int64_t row0_ = rel_ + (r0_pf < L_ ? r0_pf : L_ - 1);                               \
-    const int64_t row1_ = rel_ + (r0_pf + 1 < L_ ? r0_pf + 1 : L_ - 1);                       \
-    pk0 = *reinterpret_cast<const u32x4*>(kbase + row0_ * a.k_stride);                        \
-    pk1 = *reinterpret_cast<const u32x4*>(kbase + row1_ * a.k_stride);                        \
-    pq0 = *reinterpret_cast<const u32x4*>(qbase + row0_ * q_stride);                          \
-    pq1 = *reinterpret_cast<const u32x4*>(qbase + row1_ * q_stride);                          \
-    pv0 = *reinterpret_cast<const u32x4*>(vbase + row0_ * v_stride);                          \
-    pv1 = *reinterpret_cast<const u32x4*>(vbase + row1_ * v_stride);                          \
     const unsigned char* rs_ = rbase + (((T0) >> 6) + seq) * rslot_stride;                    \
     pr0 = *reinterpret_cast<const u32x4*>(rs_);                                               \
     pr1 = *reinterpret_cast<const u32x4*>(rs_ + 16 * NT);                                     \
     pr2 = *reinterpret_cast<const u32x4*>(rs_ + 32 * NT);                                     \
     pr3 = *reinterpret_cast<const u32x4*>(rs_ + (tid + 3 * NT < REC_UNITS ? 48 * NT : 16 * (REC_UNITS - 1 - tid))); \
   } while (0)
+#define GDN_PF_KQ(T0)                                                                          \
+  do {                                                                                        \
+    GDN_PF_ROWS(T0)                                                                           \
+    pk0 = *reinterpret_cast<const u32x4*>(kbase + row0_ * a.k_stride);                        \
+    pk1 = *reinterpret_cast<const u32x4*>(kbase + row1_ * a.k_stride);                        \
+    pq0 = *reinterpret_cast<const u32x4*>(qbase + row0_ * q_stride);                          \
+    pq1 = *reinterpret_cast<const u32x4*>(qbase + row1_ * q_stride);                          \
+  } while (0)
+#define GDN_PF_V(T0)                                                                           \
+  do {                                                                                        \
+    GDN_PF_ROWS(T0)                                                                           \
+    pv0 = *reinterpret_cast<const u32x4*>(vbase + row0_ * v_stride);                          \
+    pv1 = *reinterpret_cast<const u32x4*>(vbase + row1_ * v_stride);                          \
+  } while (0)
+#define GDN_PREFETCH(T0) do { GDN_PF_REC(T0); GDN_PF_KQ(T0); GDN_PF_V(T0); } while (0)
   if (bos < eos) GDN_PREFETCH(bos);
 
   for (int64_t t0 = bos; t0 < eos; t0 += CH) {
@@ -250,8 +262,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
       }
     }
     // ---- fetch the next chunk while this one computes -----------------------
-    if (t0 + CH < eos) GDN_PREFETCH(t0 + CH);
     __syncthreads();  // A: chunk data in LDS
+    const bool more_ = t0 + CH < eos;
+    if (more_) GDN_PF_REC(t0 + CH);
 
     // From here on each wave touches only its own state columns.
     // ---- K S and Q S over the split state (hi pass, then lo pass per k-step)
@@ -286,6 +299,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
       SCHED_FENCE();
     }
 
+    if (more_) GDN_PF_KQ(t0 + CH);
     // ---- U = T diag(beta) V - T diag(beta e^G) (K S) --------------------------
     // The two sums go to separate accumulators (U, X) so that consecutive
     // products alternate between independent tiles.
@@ -337,6 +351,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) U[ct][rt] += X[ct][rt];
 
+    if (more_) GDN_PF_V(t0 + CH);
     if (kOut) {
       // ---- O = diag(gamma) Q S + P U  -> fp32 O tile in LDS -------------------
       bf16x8 Uhi[NCT][2], Ulo[NCT][2];
@@ -461,6 +476,10 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   }
 
 #undef GDN_PREFETCH
+#undef GDN_PF_ROWS
+#undef GDN_PF_REC
+#undef GDN_PF_KQ
+#undef GDN_PF_V
   // ---- final state ----------------------------------------------------------
   float* dst = nullptr;
   int64_t row_stride = 0;
