@@ -40,59 +40,78 @@ hipError_t launch_gate(const float* a, const float* b, const float* A_log, const
 // ----------------------------------------------------------------------------
 // Causal depthwise conv1d.
 //
-// One thread owns 8 consecutive channels (one 16-byte bf16 vector) and walks a
-// tile of TOK consecutive tokens, keeping the last 3 inputs of its channels in
-// registers.  A block of 256 threads covers 2048 channels; a wave (512
-// channels) is one contiguous 1 KiB row segment per token, so every load and
-// store is fully coalesced.  The history is zeroed at each sample start; the
-// sample of the tile's first token comes from a binary search of cu_seqlens
-// (or from the batch row), later boundaries from walking the offsets.
-// The per-head L2 norm reduces over head_dim / 8 adjacent lanes with xor
-// shuffles, which stay inside one head because heads are 8-channel aligned.
+// One thread owns 8 consecutive channels (one 16-byte bf16 vector); a block of
+// 256 threads covers 2048 channels and walks a run of tokens in sub-tiles of
+// SUB tokens.  A wave (512 channels) reads one contiguous 1 KiB row segment
+// per token, so every load and store is fully coalesced.  The rows of the
+// next sub-tile are loaded while the current one is computed (two register
+// buffers), and the last three inputs of the thread's channels stay in
+// registers as the history.  Rows before the start of the current token's
+// sample count as zero: the sample of the run's first token comes from a
+// binary search of cu_seqlens (or from the batch row), later boundaries from
+// walking the offsets, all of it uniform across the block; sub-tiles with no
+// sample start among their first three tokens skip the masking.
+// A block covers either normalised (q/k) channels or the others, so every
+// wave runs one kind of work.  The per-head L2 norm sums over
+// head_dim / 8 adjacent lanes with DPP exchanges (xor 1, xor 2, then the
+// half-row and row mirrors), which stay inside one head because heads are
+// 8-channel aligned.
+// Unnormalised bf16 outputs are the bf16 nearest to the exact result: each
+// value carries an error bound, and the few whose bound straddles a bf16
+// rounding midpoint are queued and recomputed in fp64 at the end of the run.
 // ----------------------------------------------------------------------------
 constexpr int CONV_THREADS = 256;
 constexpr int CONV_CH_PER_THREAD = 8;
-constexpr int CONV_TOK = 32;
+constexpr int CONV_QCAP = 256;  // queued doubtful roundings per wave
+#ifndef GDN_CONV_BLOCKS
+#define GDN_CONV_BLOCKS 1024  // blocks per launch the token runs are sized for
+#endif
 
 template <typename T>
-struct Vec8;
+struct ConvRow;
 
 template <>
-struct Vec8<uint16_t> {  // bf16
-  static __device__ __forceinline__ void load(const uint16_t* p, float* out) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+struct ConvRow<uint16_t> {  // bf16: one 16-byte vector per row
+  static constexpr int SUB = 8;
+  typedef u32x4 raw_t;
+  static __device__ __forceinline__ raw_t load(const uint16_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+  }
+  static __device__ __forceinline__ void unpack(const raw_t& r, float* out) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      out[2 * i] = __uint_as_float(w[i] << 16);
-      out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      out[2 * i] = __uint_as_float(r[i] << 16);
+      out[2 * i + 1] = __uint_as_float(r[i] & 0xFFFF0000u);
     }
   }
   static __device__ __forceinline__ void store(uint16_t* p, const float* in) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = (uint32_t)f32_to_bf16_bits(in[2 * i]) | ((uint32_t)f32_to_bf16_bits(in[2 * i + 1]) << 16);
-    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    const u32x4 w = {pack_bf16x2(in[0], in[1]), pack_bf16x2(in[2], in[3]), pack_bf16x2(in[4], in[5]),
+                     pack_bf16x2(in[6], in[7])};
+    *reinterpret_cast<u32x4*>(p) = w;
   }
-  static __device__ __forceinline__ float scalar(const uint16_t* p, int i) {
+  static __device__ __forceinline__ float scalar(const uint16_t* p, int64_t i) {
     return bf16_bits_to_f32(p[i]);
   }
 };
 
 template <>
-struct Vec8<float> {
-  static __device__ __forceinline__ void load(const float* p, float* out) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+struct ConvRow<float> {
+  static constexpr int SUB = 4;
+  struct raw_t {
+    float4 a, b;
+  };
+  static __device__ __forceinline__ raw_t load(const float* p) {
+    return raw_t{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
+  }
+  static __device__ __forceinline__ void unpack(const raw_t& r, float* out) {
+    out[0] = r.a.x; out[1] = r.a.y; out[2] = r.a.z; out[3] = r.a.w;
+    out[4] = r.b.x; out[5] = r.b.y; out[6] = r.b.z; out[7] = r.b.w;
   }
   static __device__ __forceinline__ void store(float* p, const float* in) {
     *reinterpret_cast<float4*>(p) = make_float4(in[0], in[1], in[2], in[3]);
     *reinterpret_cast<float4*>(p + 4) = make_float4(in[4], in[5], in[6], in[7]);
   }
-  static __device__ __forceinline__ float scalar(const float* p, int i) { return p[i]; }
+  static __device__ __forceinline__ float scalar(const float* p, int64_t i) { return p[i]; }
 };
 
 // Sample index of token t (largest n with cu[n] <= t), offsets clamped to [0, T].
@@ -109,113 +128,358 @@ __device__ __forceinline__ int find_sample(const int32_t* cu, int n_seqs, int64_
   return lo;
 }
 
-template <typename T>
-__global__ void __launch_bounds__(CONV_THREADS) conv1d_kernel(
-    const T* __restrict__ x, const T* __restrict__ w, const T* __restrict__ bias,
-    const int32_t* __restrict__ cu, int n_seqs, int64_t row_len, int64_t Ttot, int C, int width,
-    int apply_silu, int l2_channels, int l2_lanes_log2, float l2_eps, T* __restrict__ y) {
-  const int c0 = (blockIdx.x * CONV_THREADS + threadIdx.x) * CONV_CH_PER_THREAD;
-  const bool active = c0 < C;
-  const int64_t t_begin = (int64_t)blockIdx.y * CONV_TOK;
-  const int64_t t_end = t_begin + CONV_TOK < Ttot ? t_begin + CONV_TOK : Ttot;
+// First token of the region (sample, trailing tokens past the last offset, or
+// batch row) that holds token t.
+__device__ __forceinline__ int64_t region_start(const int32_t* cu, int n_seqs, int64_t row_len,
+                                                int64_t Ttot, int64_t t) {
+  if (!cu) return (t / row_len) * row_len;
+  const int64_t last = clampi(cu[n_seqs], 0, Ttot);
+  if (t >= last) return last;
+  return clampi(cu[find_sample(cu, n_seqs, t, Ttot)], 0, Ttot);
+}
 
-  // taps aligned so that tap 3 multiplies the current token (zero-filled when width < 4)
-  float wt[4][CONV_CH_PER_THREAD];
-  float bs[CONV_CH_PER_THREAD];
-#pragma unroll
-  for (int i = 0; i < CONV_CH_PER_THREAD; ++i) {
-    const int c = active ? c0 + i : 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int src = j - (4 - width);
-      wt[j][i] = (active && src >= 0) ? Vec8<T>::scalar(w, c * width + src) : 0.f;
-    }
-    bs[i] = (active && bias) ? Vec8<T>::scalar(bias, c) : 0.f;
+// bf16 nearest to d (ties to even), as a float.  Rounding d to fp32 first
+// can only mislead when the fp32 result lands exactly on a bf16 midpoint;
+// that case is decided by comparing d with the midpoint.
+__device__ __forceinline__ float bf16_nearest_f64(double d) {
+  const float f = (float)d;
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0xFFFFu) == 0x8000u) {
+    const double ad = fabs(d), am = fabs((double)f);
+    if (ad > am) return __uint_as_float((b & 0xFFFF0000u) + 0x10000u);
+    if (ad < am) return __uint_as_float(b & 0xFFFF0000u);
   }
+  b = (b + 0x7FFFu + ((b >> 16) & 1u)) & 0xFFFF0000u;
+  return __uint_as_float(b);
+}
 
-  // sample bounds of the first token
-  int64_t s_start, s_end;
-  int n = 0;
-  if (cu) {
-    n = find_sample(cu, n_seqs, t_begin, Ttot);
-    s_start = clampi(cu[n], 0, Ttot);
-    s_end = clampi(cu[n + 1], s_start, Ttot);
-  } else {
-    s_start = (t_begin / row_len) * row_len;
-    s_end = s_start + row_len;
+template <int kCtrl>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false);
+  return v + __int_as_float(o);
+}
+
+// Sum over aligned groups of 2^lanes_log2 lanes (uniform lanes_log2 <= 6).
+__device__ __forceinline__ float group_sum(float v, int lanes_log2) {
+  if (lanes_log2 >= 1) v = dpp_add<0xB1>(v);   // quad_perm [1, 0, 3, 2]: xor 1
+  if (lanes_log2 >= 2) v = dpp_add<0x4E>(v);   // quad_perm [2, 3, 0, 1]: xor 2
+  if (lanes_log2 >= 3) v = dpp_add<0x141>(v);  // half-row mirror: the other quad of 8
+  if (lanes_log2 >= 4) v = dpp_add<0x140>(v);  // row mirror: the other half of 16
+  if (lanes_log2 >= 5) v += __shfl_xor(v, 16, 64);
+  if (lanes_log2 >= 6) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// Whether y (fp32, from bf16 inputs) might round to another bf16 value than
+// the exact conv (+ SiLU) result.  The tap products are exact and each of the
+// four fused sums rounds once, by at most 2^-24 of its magnitude, which is
+// below A = |bias| + sum |w| * xmax (xmax: the largest |x| of the channel over
+// the sub-tile and its history); the SiLU evaluation adds a few ulp of y.
+// E = 2^-20 |y| + 9 * 2^-24 A covers both about twice over.  The nearest
+// rounding midpoint to y is the one above its bf16 truncation.
+// Ab = 9 * 2^-24 * A, prepared once per sub-tile and channel.
+__device__ __forceinline__ bool rounding_in_doubt(float y, float Ab) {
+  const float E = fmaf(0x1p-20f, fabsf(y), Ab);
+  const float mid = __uint_as_float((__float_as_uint(y) & 0xFFFF0000u) | 0x8000u);
+  return fabsf(y - mid) <= E;
+}
+
+// One conv (+ SiLU) output in fp64 (the products of bf16 values and their sum
+// are exact there), stored as its nearest bf16.
+__device__ __noinline__ void settle_value(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                                          const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
+                                          const int32_t* __restrict__ cu, int n_seqs, int64_t row_len,
+                                          int64_t Ttot, int64_t C, int width, int apply_silu, int64_t t,
+                                          int64_t c) {
+  const int64_t back_max = t - region_start(cu, n_seqs, row_len, Ttot, t);
+  double z = bias ? (double)bf16_bits_to_f32(bias[c]) : 0.0;
+  for (int j = 0; j < width; ++j) {
+    const int back = width - 1 - j;  // tap j multiplies x[t - back]
+    if (back <= back_max)
+      z += (double)bf16_bits_to_f32(w[c * width + j]) * (double)bf16_bits_to_f32(x[(t - back) * C + c]);
   }
+  const double v = apply_silu ? z / (1.0 + exp(-z)) : z;
+  y[t * C + c] = f32_to_bf16_bits(bf16_nearest_f64(v));
+}
 
-  float h1[CONV_CH_PER_THREAD], h2[CONV_CH_PER_THREAD], h3[CONV_CH_PER_THREAD];  // x[t-3..t-1]
+struct ConvParams {
+  const int32_t* cu;
+  int n_seqs;
+  int64_t row_len, Ttot;
+  int C;            // channels of the whole row (the row pitch)
+  int c_begin, c_end;  // channel range of this launch
+  int l2_end;          // channels below are L2-normalised per head
+  int width, apply_silu;
+  int l2_lanes_log2;
+  float l2_eps;
+  int tile_tokens;  // tokens per block (a multiple of SUB)
+};
+
+// One sub-tile of SUB tokens for this thread's 8 channels.  kMode: 0 plain,
+// 1 plain with the rounding check (bf16 output), 2 L2-normalised.  kMasked:
+// the sub-tile reaches past the run or starts a sample within its first
+// three tokens, so history rows are masked per token (hist_code: 2 bits per
+// token, the count of its history rows inside its sample).
+template <typename T, int kMode, bool kMasked>
+__device__ __forceinline__ void conv_sub(const typename ConvRow<T>::raw_t (&buf)[ConvRow<T>::SUB],
+                                         float (&h1)[CONV_CH_PER_THREAD], float (&h2)[CONV_CH_PER_THREAD],
+                                         float (&h3)[CONV_CH_PER_THREAD],
+                                         const float (&wt)[4][CONV_CH_PER_THREAD],
+                                         const float (&bs)[CONV_CH_PER_THREAD],
+                                         const float (&wabs)[CONV_CH_PER_THREAD], int n_valid,
+                                         uint32_t hist_code, const ConvParams& p, bool active,
+                                         T* __restrict__ yrow, uint32_t* queue, uint32_t* qcount,
+                                         int64_t ts, int64_t tw0, int c0, bool& overflow) {
+  using Row = ConvRow<T>;
+  constexpr int SUB = Row::SUB;
+  constexpr int NCH = CONV_CH_PER_THREAD;
+  constexpr bool kCheck = kMode == 1 && sizeof(T) == 2;
+  float Ab[NCH];
+  if (kCheck) {
+    float xm[NCH];
 #pragma unroll
-  for (int i = 0; i < CONV_CH_PER_THREAD; ++i) h1[i] = h2[i] = h3[i] = 0.f;
-  if (active) {
-    float tmp[CONV_CH_PER_THREAD];
-    if (t_begin - 3 >= s_start) {
-      Vec8<T>::load(x + (t_begin - 3) * C + c0, tmp);
+    for (int i = 0; i < NCH; ++i) xm[i] = fmaxf(fmaxf(fabsf(h1[i]), fabsf(h2[i])), fabsf(h3[i]));
 #pragma unroll
-      for (int i = 0; i < CONV_CH_PER_THREAD; ++i) h1[i] = tmp[i];
+    for (int tt = 0; tt < SUB; ++tt) {
+      float r[NCH];
+      Row::unpack(buf[tt], r);
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) xm[i] = fmaxf(xm[i], fabsf(r[i]));
     }
-    if (t_begin - 2 >= s_start) {
-      Vec8<T>::load(x + (t_begin - 2) * C + c0, tmp);
 #pragma unroll
-      for (int i = 0; i < CONV_CH_PER_THREAD; ++i) h2[i] = tmp[i];
-    }
-    if (t_begin - 1 >= s_start) {
-      Vec8<T>::load(x + (t_begin - 1) * C + c0, tmp);
-#pragma unroll
-      for (int i = 0; i < CONV_CH_PER_THREAD; ++i) h3[i] = tmp[i];
-    }
+    for (int i = 0; i < NCH; ++i) Ab[i] = fmaf(wabs[i], xm[i], fabsf(bs[i])) * (9.f * 0x1p-24f);
   }
-  const bool do_l2 = l2_channels > 0 && c0 < l2_channels;
-
-  for (int64_t t = t_begin; t < t_end; ++t) {
-    while (t >= s_end) {  // crossed into the next sample: reset the history
-      if (cu && n + 1 < n_seqs) {
-        ++n;
-        s_start = s_end;
-        s_end = clampi(cu[n + 1], s_start, Ttot);
-      } else if (cu) {  // tokens past the last offset form one trailing region
-        s_start = s_end;
-        s_end = Ttot;
-      } else {
-        s_start = s_end;
-        s_end = s_start + row_len;
-      }
 #pragma unroll
-      for (int i = 0; i < CONV_CH_PER_THREAD; ++i) h1[i] = h2[i] = h3[i] = 0.f;
-    }
-    float cur[CONV_CH_PER_THREAD], out[CONV_CH_PER_THREAD];
-    if (active) {
-      Vec8<T>::load(x + t * C + c0, cur);
-    } else {
-#pragma unroll
-      for (int i = 0; i < CONV_CH_PER_THREAD; ++i) cur[i] = 0.f;
-    }
+  for (int tt = 0; tt < SUB; ++tt) {
+    if (kMasked && tt >= n_valid) break;
+    const int hist = kMasked ? (int)((hist_code >> (2 * tt)) & 3u) : 3;
+    float cur[NCH], out[NCH];
+    Row::unpack(buf[tt], cur);
     float ss = 0.f;
+    uint32_t dbits = 0;
 #pragma unroll
-    for (int i = 0; i < CONV_CH_PER_THREAD; ++i) {
+    for (int i = 0; i < NCH; ++i) {
+      const float x1 = (!kMasked || hist >= 3) ? h1[i] : 0.f;
+      const float x2 = (!kMasked || hist >= 2) ? h2[i] : 0.f;
+      const float x3 = (!kMasked || hist >= 1) ? h3[i] : 0.f;
       float z = bs[i];
-      z = fmaf(wt[0][i], h1[i], z);
-      z = fmaf(wt[1][i], h2[i], z);
-      z = fmaf(wt[2][i], h3[i], z);
+      z = fmaf(wt[0][i], x1, z);
+      z = fmaf(wt[1][i], x2, z);
+      z = fmaf(wt[2][i], x3, z);
       z = fmaf(wt[3][i], cur[i], z);
-      if (apply_silu) z = z / (1.f + expf(-z));
-      out[i] = z;
-      ss = fmaf(z, z, ss);
+      const float v = p.apply_silu ? z * __builtin_amdgcn_rcpf(1.f + __expf(-z)) : z;
+      out[i] = v;
+      if (kMode == 2) ss = fmaf(v, v, ss);
+      if (kCheck) dbits |= (rounding_in_doubt(v, Ab[i]) ? 1u : 0u) << i;
       h1[i] = h2[i];
       h2[i] = h3[i];
       h3[i] = cur[i];
     }
-    if (l2_channels > 0) {  // uniform across the block: every lane joins the shuffles
-      for (int m = 1; m < (1 << l2_lanes_log2); m <<= 1) ss += __shfl_xor(ss, m, 64);
-      if (do_l2) {
-        const float inv = 1.f / sqrtf(ss + l2_eps);
+    if (kMode == 2) {  // every lane of the wave joins the exchanges
+      ss = group_sum(ss, p.l2_lanes_log2);
+      const float inv = __builtin_amdgcn_rsqf(ss + p.l2_eps);
 #pragma unroll
-        for (int i = 0; i < CONV_CH_PER_THREAD; ++i) out[i] *= inv;
+      for (int i = 0; i < NCH; ++i) out[i] *= inv;
+    }
+    if (active) Row::store(yrow + (int64_t)tt * p.C, out);
+    if constexpr (kCheck) {
+      if (active && dbits) {  // rare: queue (token, channel) for the fp64 pass
+        const uint32_t nq = (uint32_t)__popc(dbits);
+        uint32_t pos = atomicAdd(qcount, nq);
+        while (dbits) {
+          const int i = __builtin_ctz(dbits);
+          dbits &= dbits - 1;
+          const int64_t t = ts + tt;
+          if (pos < CONV_QCAP)  // (channel within the launch) << 8 | token within the run
+            queue[pos] = ((uint32_t)(c0 + i - p.c_begin) << 8) | (uint32_t)(t - tw0);
+          else  // queue full: this lane settles its whole run at the end
+            overflow = true;
+          ++pos;
+        }
       }
     }
-    if (active) Vec8<T>::store(y + t * C + c0, out);
+    // one token at a time: keeps the scheduler from interleaving tokens,
+    // which would unpack every row at once and run out of registers
+    __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+template <typename T, int kMode>
+__device__ __forceinline__ void conv1d_run(const T* __restrict__ x, const T* __restrict__ w,
+                                           const T* __restrict__ bias, T* __restrict__ y, const ConvParams& p) {
+  using Row = ConvRow<T>;
+  constexpr int SUB = Row::SUB;
+  constexpr int NCH = CONV_CH_PER_THREAD;
+  __shared__ uint32_t s_queue[CONV_THREADS / 64][CONV_QCAP];
+  __shared__ uint32_t s_qcount[CONV_THREADS / 64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c0 = p.c_begin + (blockIdx.x * CONV_THREADS + threadIdx.x) * NCH;
+  const bool active = c0 < p.c_end;
+  const int cl = active ? c0 : p.c_begin;  // an inactive lane reads a valid segment
+  const int64_t tw0 = (int64_t)blockIdx.y * p.tile_tokens;
+  const int64_t tw1 = tw0 + p.tile_tokens < p.Ttot ? tw0 + p.tile_tokens : p.Ttot;
+  const int64_t C = p.C;
+  if (lane == 0) s_qcount[wave] = 0;
+
+  // ---- history rows and the first sub-tile, in flight before anything else --------
+  typename Row::raw_t hraw[3], bufA[SUB], bufB[SUB];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int64_t r = tw0 - 3 + i;
+    hraw[i] = Row::load(x + (r < 0 ? 0 : r) * C + cl);
+  }
+  auto load_sub = [&](typename Row::raw_t(&buf)[SUB], int64_t ts) {
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+      const int64_t r = ts + i < p.Ttot ? ts + i : p.Ttot - 1;
+      buf[i] = Row::load(x + r * C + cl);
+    }
+  };
+  load_sub(bufA, tw0);
+
+  // ---- taps aligned so that tap 3 multiplies the current token --------------------
+  float wt[4][NCH], bs[NCH], wabs[NCH];
+  if (sizeof(T) == 2 && p.width == 4) {  // 8 channels x 4 taps = 64 contiguous bytes
+    const uint16_t* wp = reinterpret_cast<const uint16_t*>(w) + (int64_t)cl * 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(wp + 8 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {  // word e of vector q: channel 2q + e/2, taps 2(e%2), 2(e%2)+1
+        const int ch = 2 * q + (e >> 1), tap = 2 * (e & 1);
+        wt[tap][ch] = __uint_as_float(v[e] << 16);
+        wt[tap + 1][ch] = __uint_as_float(v[e] & 0xFFFF0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int src = j - (4 - p.width);
+        wt[j][i] = src >= 0 ? Row::scalar(w, (int64_t)(cl + i) * p.width + src) : 0.f;
+      }
+  }
+  if (sizeof(T) == 2 && bias) {
+    float tmp[NCH];
+    ConvRow<uint16_t>::unpack(*reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(bias) + cl), tmp);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) bs[i] = tmp[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) bs[i] = bias ? Row::scalar(bias, cl + i) : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+    wabs[i] = fabsf(wt[0][i]) + fabsf(wt[1][i]) + fabsf(wt[2][i]) + fabsf(wt[3][i]);
+
+  // ---- region (sample / batch row) of the first token ----------------------------
+  int n = 0;
+  int64_t s_start, s_end;
+  if (p.cu) {
+    n = find_sample(p.cu, p.n_seqs, tw0, p.Ttot);
+    s_start = clampi(p.cu[n], 0, p.Ttot);
+    s_end = clampi(p.cu[n + 1], s_start, p.Ttot);
+  } else {
+    s_start = (tw0 / p.row_len) * p.row_len;
+    s_end = s_start + p.row_len;
+  }
+  float h1[NCH], h2[NCH], h3[NCH];  // x[t-3], x[t-2], x[t-1]
+  Row::unpack(hraw[0], h1);
+  Row::unpack(hraw[1], h2);
+  Row::unpack(hraw[2], h3);
+
+  // Uniform walk over the sub-tile at ts: 2-bit history counts per token, and
+  // whether anything needs masking.
+  auto walk = [&](int64_t ts, uint32_t& code) -> bool {
+    const int64_t te = ts + SUB < tw1 ? ts + SUB : tw1;
+    if (te == ts + SUB && te <= s_end && ts - s_start >= 3) {
+      code = 0xFFFFFFFFu;
+      return false;
+    }
+    code = 0;
+    for (int64_t t = ts; t < te; ++t) {
+      while (t >= s_end) {  // the next region starts at or before t
+        if (p.cu && n + 1 < p.n_seqs) {
+          ++n;
+          s_start = s_end;
+          s_end = clampi(p.cu[n + 1], s_start, p.Ttot);
+        } else if (p.cu) {  // tokens past the last offset form one trailing region
+          s_start = s_end;
+          s_end = p.Ttot;
+        } else {
+          s_start = s_end;
+          s_end = s_start + p.row_len;
+        }
+      }
+      const int64_t back = t - s_start;
+      code |= (uint32_t)(back < 3 ? back : 3) << (2 * (t - ts));
+    }
+    return true;
+  };
+
+  uint32_t* queue = s_queue[wave];
+  uint32_t* qcount = &s_qcount[wave];
+  bool overflow = false;
+#define GDN_CONV_SUB(BUF, TS)                                                                          \
+  do {                                                                                                 \
+    uint32_t code_;                                                                                    \
+    const bool masked_ = walk((TS), code_);                                                            \
+    const int nv_ = (int)((TS) + SUB < tw1 ? SUB : tw1 - (TS));                                        \
+    T* yrow_ = y + (TS) * C + c0;                                                                      \
+    if (masked_)                                                                                       \
+      conv_sub<T, kMode, true>(BUF, h1, h2, h3, wt, bs, wabs, nv_, code_, p, active, yrow_, queue,     \
+                               qcount, (TS), tw0, c0, overflow);                                       \
+    else                                                                                               \
+      conv_sub<T, kMode, false>(BUF, h1, h2, h3, wt, bs, wabs, nv_, code_, p, active, yrow_, queue,    \
+                                qcount, (TS), tw0, c0, overflow);                                      \
+  } while (0)
+  for (int64_t ts = tw0; ts < tw1; ts += 2 * SUB) {
+    load_sub(bufB, ts + SUB);
+    GDN_CONV_SUB(bufA, ts);
+    if (ts + SUB >= tw1) break;
+    load_sub(bufA, ts + 2 * SUB);
+    GDN_CONV_SUB(bufB, ts + SUB);
+  }
+#undef GDN_CONV_SUB
+
+  // ---- settle the queued roundings in fp64 -----------------------------------------
+  if constexpr (kMode == 1 && sizeof(T) == 2) {
+    // the queue and this wave's stores above are complete before any lane
+    // reads the queue or overwrites a value another lane stored
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    const uint32_t nq = min(*qcount, (uint32_t)CONV_QCAP);
+    for (uint32_t e = lane; e < nq; e += 64) {
+      const uint32_t v = queue[e];
+      const int64_t t = tw0 + (int64_t)(v & 0xFFu);
+      const int64_t c = p.c_begin + (int64_t)(v >> 8);
+      if (t >= tw1 || c >= p.c_end) continue;  // entries come from active lanes only
+      settle_value(reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w),
+                   reinterpret_cast<const uint16_t*>(bias), reinterpret_cast<uint16_t*>(y), p.cu, p.n_seqs,
+                   p.row_len, p.Ttot, C, p.width, p.apply_silu, t, c);
+    }
+    if (overflow && active) {  // more doubtful values than the queue holds: redo the run in fp64
+      for (int64_t t = tw0; t < tw1; ++t)
+        for (int i = 0; i < NCH; ++i)
+          settle_value(reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w),
+                       reinterpret_cast<const uint16_t*>(bias), reinterpret_cast<uint16_t*>(y), p.cu,
+                       p.n_seqs, p.row_len, p.Ttot, C, p.width, p.apply_silu, t, c0 + i);
+    }
+  }
+}
+
+// Blocks below l2_end run the normalised channels, the others the plain ones
+// (with the rounding check for bf16); every block lies on one side.
+template <typename T>
+__global__ void __launch_bounds__(CONV_THREADS) conv1d_kernel(const T* __restrict__ x, const T* __restrict__ w,
+                                                              const T* __restrict__ bias, T* __restrict__ y,
+                                                              ConvParams p) {
+  if (p.c_begin + (int)blockIdx.x * CONV_THREADS * CONV_CH_PER_THREAD < p.l2_end)
+    conv1d_run<T, 2>(x, w, bias, y, p);
+  else
+    conv1d_run<T, sizeof(T) == 2 ? 1 : 0>(x, w, bias, y, p);
 }
 
 hipError_t launch_conv1d(const void* x, const void* w, const void* bias, int dt,
@@ -225,22 +489,49 @@ hipError_t launch_conv1d(const void* x, const void* w, const void* bias, int dt,
   const int64_t Ttot = cu ? T : (int64_t)B * T;
   if (Ttot == 0 || C == 0) return hipSuccess;
   const int per_block = CONV_THREADS * CONV_CH_PER_THREAD;
-  dim3 grid((unsigned)((C + per_block - 1) / per_block), (unsigned)((Ttot + CONV_TOK - 1) / CONV_TOK));
   int lanes_log2 = 0;
   if (l2_channels > 0)
     while ((CONV_CH_PER_THREAD << lanes_log2) < head_dim) ++lanes_log2;
-  const int64_t row_len = cu ? Ttot : T;
-  if (dt == 1) {
-    hipLaunchKernelGGL(conv1d_kernel<uint16_t>, grid, dim3(CONV_THREADS), 0, stream,
-                       (const uint16_t*)x, (const uint16_t*)w, (const uint16_t*)bias, cu, n_seqs,
-                       row_len, Ttot, C, width, apply_silu, l2_channels, lanes_log2, l2_eps,
-                       (uint16_t*)y);
-  } else {
-    hipLaunchKernelGGL(conv1d_kernel<float>, grid, dim3(CONV_THREADS), 0, stream,
-                       (const float*)x, (const float*)w, (const float*)bias, cu, n_seqs, row_len,
-                       Ttot, C, width, apply_silu, l2_channels, lanes_log2, l2_eps, (float*)y);
+  ConvParams p;
+  p.cu = cu;
+  p.n_seqs = n_seqs;
+  p.row_len = cu ? Ttot : T;
+  p.Ttot = Ttot;
+  p.C = C;
+  p.width = width;
+  p.apply_silu = apply_silu;
+  p.l2_lanes_log2 = lanes_log2;
+  p.l2_eps = l2_eps;
+  const int sub = dt == 1 ? ConvRow<uint16_t>::SUB : ConvRow<float>::SUB;
+  p.l2_end = l2_channels;
+  // One launch when the normalised channels end on a block boundary,
+  // otherwise one launch on each side of that boundary.
+  const bool split = l2_channels % per_block != 0;
+  for (int part = 0; part < (split ? 2 : 1); ++part) {
+    p.c_begin = split && part == 1 ? l2_channels : 0;
+    p.c_end = split && part == 0 ? l2_channels : C;
+    if (p.c_end <= p.c_begin) continue;
+    const int cblocks = (p.c_end - p.c_begin + per_block - 1) / per_block;
+    // runs of 2-4 sub-tiles per block, aiming at about GDN_CONV_BLOCKS blocks;
+    // a run of 4 bf16 sub-tiles gives a wave 16K values, about 140 of which
+    // (well below CONV_QCAP) are queued for fp64 on data like the layer's
+    const int64_t subs = (Ttot + sub - 1) / sub;
+    int64_t per = (subs * cblocks + GDN_CONV_BLOCKS - 1) / GDN_CONV_BLOCKS;
+    per = per < 2 ? 2 : (per > 4 ? 4 : per);
+    const int64_t per_min = (subs + 65534) / 65535;  // grid y stays within 65535
+    if (per < per_min) per = per_min;
+    p.tile_tokens = (int)(per * sub);
+    const dim3 grid((unsigned)cblocks, (unsigned)((Ttot + p.tile_tokens - 1) / p.tile_tokens));
+    if (dt == 1)
+      hipLaunchKernelGGL(conv1d_kernel<uint16_t>, grid, dim3(CONV_THREADS), 0, stream, (const uint16_t*)x,
+                         (const uint16_t*)w, (const uint16_t*)bias, (uint16_t*)y, p);
+    else
+      hipLaunchKernelGGL(conv1d_kernel<float>, grid, dim3(CONV_THREADS), 0, stream, (const float*)x,
+                         (const float*)w, (const float*)bias, (float*)y, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace gdn

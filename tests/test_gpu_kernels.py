@@ -85,6 +85,20 @@ def test_conv1d_packed(dtype, l2):
     else:
         err = np.abs(got - ref)
         assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-5), float((err - 2.0 ** -8 * np.abs(ref)).max())
+        # channels stored without normalisation are the bf16 nearest to the exact value
+        plain = slice(l2ch, None)
+        np.testing.assert_array_equal(got[:, plain], oracle.round_bf16(ref[:, plain]))
+
+
+def test_conv1d_bf16_rounding_is_exact_at_scale():
+    """Every unnormalised bf16 output equals the oracle's fp64 value rounded once to bf16, over
+    enough values (about 2M) that the fp64 settling of doubtful roundings runs many times."""
+    w = gdn_inputs.Workload("conv_big", 13, 2048, 3, 1, 8, 64, 128, "bf16", conv_width=4, lengths=[700, 1000, 348])
+    d = gdn_inputs.draw(w)
+    y = gdn.gdn_conv1d_fwd(dev(d["x"], "bf16"), dev(d["conv_w"], "bf16"), dev(d["conv_bias"], "bf16"),
+                           cu_seqlens=dev(d["cu_seqlens"], "i32"), cu_seqlens_host=d["cu_seqlens"])
+    ref = oracle.conv1d(d["x"], d["conv_w"], d["conv_bias"], d["cu_seqlens"])
+    np.testing.assert_array_equal(host(y), oracle.round_bf16(ref))
 
 
 def test_conv1d_batched_rows_and_width():
@@ -96,8 +110,7 @@ def test_conv1d_batched_rows_and_width():
         y = gdn.gdn_conv1d_fwd(dev(x, "bf16"), dev(wt, "bf16"), None, apply_silu=False)
         cu = np.arange(B + 1) * T
         ref = oracle.conv1d(x.reshape(B * T, C), wt, None, cu, silu=False).reshape(B, T, C)
-        err = np.abs(host(y) - ref)
-        assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-5)
+        np.testing.assert_array_equal(host(y), oracle.round_bf16(ref))
 
 
 # --------------------------------------------------------------------------- #
