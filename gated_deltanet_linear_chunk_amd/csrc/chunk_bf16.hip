@@ -130,13 +130,14 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   const int s0_mode = m_mode ? 2 : a.s0_mode;
   const int col_base = v0 + wave * CPW;
 
-  // Per-thread base pointers of the prefetch: unit u covers token rows
-  // 2 * (pid & 31) + {0, 1} and columns 8 * (pid >> 5) .. + 7.  Lanes run along
-  // the tokens so that the transposed LDS stores (K^T, V^T) of a wave hit
-  // consecutive banks; the 16-byte global loads of the column groups of a row
-  // come from neighbouring waves and meet in the caches.
-  static_assert(NPAIR == 1, "the prefetch below is written for 512 threads");
+  // Prefetch units: unit u = tid + NT j (j < NPAIR) covers token rows
+  // 2 (u & 31) + {0, 1} and columns 8 (u >> 5) .. + 7, so all units of a
+  // thread share its two rows.  Lanes run along the tokens so that the
+  // transposed LDS stores (K^T, V^T) of a wave hit consecutive banks; the
+  // 16-byte global loads of the column groups of a row come from neighbouring
+  // waves and meet in the caches.
   const int r0_pf = 2 * (tid & 31), d8_pf = (tid >> 5) * 8;
+  constexpr int kDJ = (NT / 32) * 8;  // column step between a thread's units
   // base pointers at the sequence start; the prefetch adds the token offset
   // t0 - bos + row, with row clamped to the chunk's last valid token
   const uint16_t* kbase = (const uint16_t*)a.k + bos * a.k_stride + hq * KD + d8_pf;
@@ -146,7 +147,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   const uint16_t* vbase =
       load_v ? (const uint16_t*)a.v + bos * a.v_stride + (int64_t)h * a.V + v0 + d8_pf : kbase;
   const int64_t v_stride = load_v ? a.v_stride : a.k_stride;
-  const unsigned char* rbase = (const unsigned char*)a.tbuf + (int64_t)h * PREP_RECORD_BYTES + 16 * tid;
+  const unsigned char* rbase = (const unsigned char*)a.tbuf + (int64_t)h * PREP_RECORD_BYTES;
   const int64_t rslot_stride = (int64_t)a.Hv * PREP_RECORD_BYTES;
 
   // ---- initial state: S[ct][dt][e] = S[16 dt + 4 g4 + e][col_base + 16 ct + c16]
@@ -178,8 +179,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   // groups between the compute phases of the current one, so that the
   // vector memory pipeline works through them while the matrix cores run
   // instead of holding up a barrier.
-  static_assert(NREC == 4, "record prefetch is written for 4 units per thread");
-  u32x4 pk0, pk1, pq0, pq1, pv0, pv1, pr0, pr1, pr2, pr3;
+  u32x4 pk[NPAIR][2], pq[NPAIR][2], pv[NPAIR][2], pr[NREC];
 #define GDN_PF_ROWS(T0)                                                                        \
   const int64_t rel_ = (T0) - bos;                                                            \
   const int L_ = (int)((eos - (T0)) < CH ? (eos - (T0)) : CH);                                \
@@ -188,24 +188,26 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
 #define GDN_PF_REC(T0)                                                                         \
   do {                                                                                        \
     const unsigned char* rs_ = rbase + (((T0) >> 6) + seq) * rslot_stride;                    \
-    pr0 = *reinterpret_cast<const u32x4*>(rs_);                                               \
-    pr1 = *reinterpret_cast<const u32x4*>(rs_ + 16 * NT);                                     \
-    pr2 = *reinterpret_cast<const u32x4*>(rs_ + 32 * NT);                                     \
-    pr3 = *reinterpret_cast<const u32x4*>(rs_ + (tid + 3 * NT < REC_UNITS ? 48 * NT : 16 * (REC_UNITS - 1 - tid))); \
+    _Pragma("unroll") for (int u_ = 0; u_ < NREC; ++u_)                                        \
+      pr[u_] = *reinterpret_cast<const u32x4*>(rs_ + 16 * min(tid + u_ * NT, REC_UNITS - 1));   \
   } while (0)
 #define GDN_PF_KQ(T0)                                                                          \
   do {                                                                                        \
     GDN_PF_ROWS(T0)                                                                           \
-    pk0 = *reinterpret_cast<const u32x4*>(kbase + row0_ * a.k_stride);                        \
-    pk1 = *reinterpret_cast<const u32x4*>(kbase + row1_ * a.k_stride);                        \
-    pq0 = *reinterpret_cast<const u32x4*>(qbase + row0_ * q_stride);                          \
-    pq1 = *reinterpret_cast<const u32x4*>(qbase + row1_ * q_stride);                          \
+    _Pragma("unroll") for (int j_ = 0; j_ < NPAIR; ++j_) {                                     \
+      pk[j_][0] = *reinterpret_cast<const u32x4*>(kbase + row0_ * a.k_stride + kDJ * j_);     \
+      pk[j_][1] = *reinterpret_cast<const u32x4*>(kbase + row1_ * a.k_stride + kDJ * j_);     \
+      pq[j_][0] = *reinterpret_cast<const u32x4*>(qbase + row0_ * q_stride + kDJ * j_);       \
+      pq[j_][1] = *reinterpret_cast<const u32x4*>(qbase + row1_ * q_stride + kDJ * j_);       \
+    }                                                                                         \
   } while (0)
 #define GDN_PF_V(T0)                                                                           \
   do {                                                                                        \
     GDN_PF_ROWS(T0)                                                                           \
-    pv0 = *reinterpret_cast<const u32x4*>(vbase + row0_ * v_stride);                          \
-    pv1 = *reinterpret_cast<const u32x4*>(vbase + row1_ * v_stride);                          \
+    _Pragma("unroll") for (int j_ = 0; j_ < NPAIR; ++j_) {                                     \
+      pv[j_][0] = *reinterpret_cast<const u32x4*>(vbase + row0_ * v_stride + kDJ * j_);       \
+      pv[j_][1] = *reinterpret_cast<const u32x4*>(vbase + row1_ * v_stride + kDJ * j_);       \
+    }                                                                                         \
   } while (0)
 #define GDN_PREFETCH(T0) do { GDN_PF_REC(T0); GDN_PF_KQ(T0); GDN_PF_V(T0); } while (0)
   if (bos < eos) GDN_PREFETCH(bos);
@@ -215,17 +217,18 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
     __syncthreads();  // every wave is done with the previous chunk's tiles
 
     // ---- stash q, k, v and the prep record ---------------------------------
-    {
-      const int r0 = r0_pf, d8 = d8_pf;
+#pragma unroll
+    for (int j = 0; j < NPAIR; ++j) {
+      const int r0 = r0_pf, d8 = d8_pf + kDJ * j;
       const u32x4 z = {0u, 0u, 0u, 0u};
       const bool ok0 = r0 < L, ok1 = r0 + 1 < L;
-      const u32x4 k0 = ok0 ? pk0 : z, k1 = ok1 ? pk1 : z;
-      const u32x4 v0v = (load_v && ok0) ? pv0 : z, v1v = (load_v && ok1) ? pv1 : z;
+      const u32x4 k0 = ok0 ? pk[j][0] : z, k1 = ok1 ? pk[j][1] : z;
+      const u32x4 v0v = (load_v && ok0) ? pv[j][0] : z, v1v = (load_v && ok1) ? pv[j][1] : z;
       *reinterpret_cast<u32x4*>(sK + r0 * QP + d8) = k0;
       *reinterpret_cast<u32x4*>(sK + (r0 + 1) * QP + d8) = k1;
       if (kOut) {
-        *reinterpret_cast<u32x4*>(sQ + r0 * QP + d8) = ok0 ? pq0 : z;
-        *reinterpret_cast<u32x4*>(sQ + (r0 + 1) * QP + d8) = ok1 ? pq1 : z;
+        *reinterpret_cast<u32x4*>(sQ + r0 * QP + d8) = ok0 ? pq[j][0] : z;
+        *reinterpret_cast<u32x4*>(sQ + (r0 + 1) * QP + d8) = ok1 ? pq[j][1] : z;
       }
 #pragma unroll
       for (int jx = 0; jx < 4; ++jx) {
@@ -242,9 +245,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
       // Every unit is stored (no branch around a store): a unit past the end
       // of the record holds a copy of the last unit and rewrites it in place,
       // and in state-only runs the P units land unused in sP.
-      const u32x4 prv[4] = {pr0, pr1, pr2, pr3};
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < NREC; ++u) {
         const int f = min(tid + u * NT, REC_UNITS - 1);
         unsigned char* dst;
         if (f < REC_MAT_UNITS) {
@@ -258,7 +260,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
           const int g = f - REC_MAT_UNITS;  // 0..15 gamma, 16..31 dec
           dst = smem + OFF_GAM + 16 * g;
         }
-        *reinterpret_cast<u32x4*>(dst) = prv[u];
+        *reinterpret_cast<u32x4*>(dst) = pr[u];
       }
     }
     // ---- fetch the next chunk while this one computes -----------------------
