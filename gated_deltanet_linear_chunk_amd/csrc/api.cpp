@@ -7,7 +7,11 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "kernels.h"
+#include "split_plan.h"
 
 namespace {
 
@@ -45,6 +49,24 @@ gdn_status chunk_supported(int in_dt, int32_t K, int32_t V) {
 
 size_t tbuf_bytes(int64_t Ttot, int32_t n_seqs, int32_t H_v) {
   return (size_t)gdn::PREP_RECORD_BYTES * (size_t)gdn::chunk_slots(Ttot, n_seqs) * (size_t)H_v;
+}
+
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 256;
+  return n;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of a split run: records of n_seg segments, M and b of the pass-1
+// segments, start states of the later segments, the plan's index arrays.
+size_t split_workspace_bytes(int64_t total, int n_seg, int n_prefix, int32_t H_v, int32_t K, int32_t V) {
+  const size_t st = (size_t)H_v * K * V * sizeof(float);
+  return align256(tbuf_bytes(total, n_seg, H_v)) + align256((size_t)n_prefix * H_v * K * K * sizeof(float)) +
+         2 * align256((size_t)n_prefix * st) +
+         align256(sizeof(int32_t) * (size_t)gdn::split_plan_ints_max(n_seg, n_prefix));
 }
 
 }  // namespace
@@ -101,10 +123,11 @@ gdn_status gdn_conv1d_fwd(const void* x, const void* w, const void* bias, gdn_dt
 
 size_t gdn_chunk_fwd_workspace_bytes(gdn_dtype in_dt, int64_t total_tokens, int32_t n_seqs,
                                      int32_t H_v, int32_t K, int32_t V) {
-  (void)K;
-  (void)V;
-  if (in_dt != GDN_BF16 || total_tokens < 0 || n_seqs < 0 || H_v < 1) return 0;
-  return tbuf_bytes(total_tokens, n_seqs, H_v);
+  if (in_dt != GDN_BF16 || total_tokens < 0 || n_seqs < 0 || H_v < 1 || K < 1 || V < 1) return 0;
+  const size_t plain = tbuf_bytes(total_tokens, n_seqs, H_v);
+  const int pmax = gdn::max_prefix_segments(H_v, V, device_cus());
+  if (pmax == 0 || n_seqs < 1) return plain;
+  return std::max(plain, split_workspace_bytes(total_tokens, n_seqs + pmax, pmax, H_v, K, V));
 }
 
 gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, gdn_dtype in_dt,
@@ -164,6 +187,47 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, gdn_dtype 
   a.sf_seq_stride = (int64_t)H_v * K * V;
   a.sf_head_stride = (int64_t)K * V;
   a.sf_row_stride = V;
+  if (in_dt == GDN_BF16 && cu_seqlens && cu_seqlens_host && total > 0) {
+    gdn::SplitPlan plan;
+    if (gdn::plan_split(cu_seqlens_host, N, H_v, V, initial_state != nullptr, device_cus(), plan) &&
+        workspace_bytes >= split_workspace_bytes(total, plan.n_seg, plan.n_prefix, H_v, K, V)) {
+      // ---- segment-split run (see plan_split) ----------------------------------
+      unsigned char* w = static_cast<unsigned char*>(workspace);
+      const size_t st = (size_t)H_v * K * V;
+      float* rec = reinterpret_cast<float*>(w);
+      w += align256(tbuf_bytes(total, plan.n_seg, H_v));
+      float* M = reinterpret_cast<float*>(w);
+      w += align256((size_t)plan.n_prefix * H_v * K * K * sizeof(float));
+      float* bmap = reinterpret_cast<float*>(w);
+      w += align256((size_t)plan.n_prefix * st * sizeof(float));
+      float* starts = reinterpret_cast<float*>(w);
+      w += align256((size_t)plan.n_prefix * st * sizeof(float));
+      int32_t* ints = reinterpret_cast<int32_t*>(w);
+      hipError_t e = hipMemcpyAsync(ints, plan.ints.data(), plan.ints.size() * sizeof(int32_t),
+                                    hipMemcpyHostToDevice, stream);
+      if (e != hipSuccess) return GDN_ERR_HIP;
+      a.tbuf = rec;
+      a.cu = ints;
+      a.n_seqs = plan.n_seg;
+      e = gdn::launch_chunk_prep(a, 1, stream);  // one set of records serves both passes
+      if (e != hipSuccess) return GDN_ERR_HIP;
+      gdn::ChunkArgs p1 = a;
+      p1.seq_order = ints + plan.off_pre();
+      p1.n_blocks_z = plan.n_prefix;
+      e = gdn::launch_segment_pass1(p1, M, bmap, stream, false);
+      if (e != hipSuccess) return GDN_ERR_HIP;
+      e = gdn::launch_compose_chains(M, bmap, initial_state, ints + plan.off_chains(), plan.n_chain, H_v, K, V,
+                                     starts, 0, nullptr, stream);
+      if (e != hipSuccess) return GDN_ERR_HIP;
+      gdn::ChunkArgs p2 = a;
+      p2.seq_order = ints + plan.off_order();
+      p2.n_blocks_z = plan.n_seg;
+      p2.s0_ref = ints + plan.off_s0ref();
+      p2.s0_seg = starts;
+      p2.sf_map = ints + plan.off_sfmap();
+      return hip_status(gdn::launch_chunk_bf16(p2, stream, false));
+    }
+  }
   const hipError_t e = in_dt == GDN_BF16 ? gdn::launch_chunk_bf16(a, stream)
                                          : gdn::launch_chunk_f32(a, stream);
   return hip_status(e);

@@ -116,7 +116,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   }
   const int v0 = tile * BV;
   const int h = blockIdx.y;
-  const int seq = blockIdx.z;
+  const int zb = blockIdx.z;
+  const int seq = a.seq_order ? a.seq_order[zb] : zb;
   const int hq = h / (a.Hv / a.Hqk);
   int64_t bos, eos;
   if (a.cu) {
@@ -127,7 +128,19 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
     eos = bos + a.row_len;
   }
   const bool load_v = !m_mode;
-  const int s0_mode = m_mode ? 2 : a.s0_mode;
+  // start state of this head: identity (M columns), zero, or K x V rows of V
+  const float* s0p = nullptr;
+  if (!m_mode) {
+    if (a.s0_ref) {
+      const int r = a.s0_ref[seq];
+      if (r >= 0)
+        s0p = a.s0_seg + ((int64_t)r * a.Hv + h) * (int64_t)KD * a.V;
+      else if (r <= -2 && a.s0)
+        s0p = a.s0 + ((int64_t)(-2 - r) * a.Hv + h) * (int64_t)KD * a.V;
+    } else if (a.s0_mode == 1) {
+      s0p = a.s0 + ((int64_t)seq * a.Hv + h) * (int64_t)KD * a.V;
+    }
+  }
   const int col_base = v0 + wave * CPW;
 
   // Prefetch units: unit u = tid + NT j (j < NPAIR) covers token rows
@@ -161,10 +174,10 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
         const int d = 16 * dt + 4 * g4 + e;
         const int col = col_base + 16 * ct + c16;
         float s = 0.f;
-        if (s0_mode == 1)
-          s = a.s0[((int64_t)seq * a.Hv + h) * (int64_t)KD * a.V + (int64_t)d * a.V + col];
-        else if (s0_mode == 2)
+        if (m_mode)
           s = (d == col) ? 1.f : 0.f;
+        else if (s0p)
+          s = s0p[(int64_t)d * a.V + col];
         S[ct][dt][e] = s;
       }
 
@@ -485,11 +498,12 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   // ---- final state ----------------------------------------------------------
   float* dst = nullptr;
   int64_t row_stride = 0;
+  const int out_row = a.sf_map ? a.sf_map[seq] : zb;
   if (m_mode) {
-    dst = p1.m_out + ((int64_t)seq * a.Hv + h) * (int64_t)KD * KD;
+    dst = p1.m_out + ((int64_t)zb * a.Hv + h) * (int64_t)KD * KD;
     row_stride = KD;
-  } else if (a.sf) {
-    dst = a.sf + (int64_t)seq * a.sf_seq_stride + (int64_t)h * a.sf_head_stride;
+  } else if (a.sf && out_row >= 0) {
+    dst = a.sf + (int64_t)out_row * a.sf_seq_stride + (int64_t)h * a.sf_head_stride;
     row_stride = a.sf_row_stride;
   }
   if (dst) {
@@ -517,13 +531,17 @@ hipError_t launch_scan(const ChunkArgs& a, Pass1 p1, dim3 grid, hipStream_t stre
 
 }  // namespace
 
-hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t stream) {
+hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t stream, bool prep) {
   if (a.n_seqs == 0 || a.Hv == 0) return hipSuccess;
   if (a.K != KD || a.V % BV != 0 || a.tbuf == nullptr) return hipErrorInvalidValue;
   const bool with_o = a.o != nullptr && a.q != nullptr;
-  hipError_t e = launch_chunk_prep(a, with_o ? 1 : 0, stream);
-  if (e != hipSuccess) return e;
-  const dim3 grid(a.V / BV, a.Hv, a.n_seqs);
+  if (prep) {
+    hipError_t e = launch_chunk_prep(a, with_o ? 1 : 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  const int nz = a.seq_order ? a.n_blocks_z : a.n_seqs;
+  if (nz == 0) return hipSuccess;
+  const dim3 grid(a.V / BV, a.Hv, nz);
   if (!with_o) {
     // state only: run the scan without outputs
     return launch_scan<kPass1>(a, Pass1{0, nullptr}, grid, stream);
@@ -532,11 +550,13 @@ hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t stream) {
                      : launch_scan<kOutF32>(a, Pass1{0, nullptr}, grid, stream);
 }
 
-hipError_t launch_segment_pass1(const ChunkArgs& a, float* M, float* b, hipStream_t stream) {
+hipError_t launch_segment_pass1(const ChunkArgs& a, float* M, float* b, hipStream_t stream, bool prep) {
   if (a.n_seqs == 0 || a.Hv == 0) return hipSuccess;
   if (a.K != KD || a.V % BV != 0 || a.tbuf == nullptr) return hipErrorInvalidValue;
-  hipError_t e = launch_chunk_prep(a, 0, stream);
-  if (e != hipSuccess) return e;
+  if (prep) {
+    hipError_t e = launch_chunk_prep(a, 0, stream);
+    if (e != hipSuccess) return e;
+  }
   ChunkArgs c = a;
   c.q = nullptr;
   c.o = nullptr;
@@ -545,7 +565,11 @@ hipError_t launch_segment_pass1(const ChunkArgs& a, float* M, float* b, hipStrea
   c.sf_head_stride = (int64_t)KD * a.V;
   c.sf_row_stride = a.V;
   c.s0_mode = 0;
-  return launch_scan<kPass1>(c, Pass1{KD / BV, M}, dim3(KD / BV + a.V / BV, a.Hv, a.n_seqs), stream);
+  c.s0_ref = nullptr;
+  c.sf_map = nullptr;
+  const int nz = a.seq_order ? a.n_blocks_z : a.n_seqs;
+  if (nz == 0) return hipSuccess;
+  return launch_scan<kPass1>(c, Pass1{KD / BV, M}, dim3(KD / BV + a.V / BV, a.Hv, nz), stream);
 }
 
 }  // namespace gdn

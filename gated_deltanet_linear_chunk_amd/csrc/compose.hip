@@ -20,33 +20,44 @@ constexpr int CK = 128;  // key dim
 constexpr int CT = 16;   // state columns per workgroup
 constexpr int CTHREADS = 256;
 
+struct Chain {
+  int n, p0, count, out0;
+};
+
 __global__ void __launch_bounds__(CTHREADS) compose_kernel(const float* __restrict__ M,
                                                            const float* __restrict__ b,
-                                                           const float* __restrict__ s0, int P,
-                                                           int Hv, int V,
-                                                           float* __restrict__ starts,
+                                                           const float* __restrict__ s0,
+                                                           const int32_t* __restrict__ chains,
+                                                           Chain single, int Hv, int V,
+                                                           float* __restrict__ out, int write_before,
                                                            float* __restrict__ final_state) {
   __shared__ float sS[2][CK][CT];
   const int tid = threadIdx.x;
   const int c0 = blockIdx.x * CT;
   const int h = blockIdx.y;
+  const int ci = blockIdx.z;
+  const Chain ch = chains ? Chain{chains[4 * ci], chains[4 * ci + 1], chains[4 * ci + 2], chains[4 * ci + 3]}
+                          : single;
   const int d = tid >> 1;          // output row
   const int cc = (tid & 1) * 8;    // 8 output columns
 
-  const int64_t state_head = (int64_t)h * CK * V;
+  const int64_t head = (int64_t)h * CK * V;
+  const int64_t row = (int64_t)Hv * CK * V;  // one [Hv, K, V] state
   for (int i = tid; i < CK * CT; i += CTHREADS) {
     const int r = i / CT, c = i % CT;
-    sS[0][r][c] = s0 ? s0[state_head + (int64_t)r * V + c0 + c] : 0.f;
+    sS[0][r][c] = (s0 && ch.n >= 0) ? s0[ch.n * row + head + (int64_t)r * V + c0 + c] : 0.f;
   }
   __syncthreads();
   int cur = 0;
-  for (int seg = 0; seg < P; ++seg) {
-    const int64_t seg_state = (int64_t)seg * Hv * CK * V + state_head;
+  for (int j = 0; j < ch.count; ++j) {
+    const int seg = ch.p0 + j;
+    const int64_t seg_state = (int64_t)seg * row + head;
+    float* dst = out + (int64_t)(ch.out0 + j) * row + head + (int64_t)d * V + c0 + cc;
     float acc[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      starts[seg_state + (int64_t)d * V + c0 + cc + j] = sS[cur][d][cc + j];
-      acc[j] = b[seg_state + (int64_t)d * V + c0 + cc + j];
+    for (int k = 0; k < 8; ++k) {
+      if (write_before) dst[k] = sS[cur][d][cc + k];
+      acc[k] = b[seg_state + (int64_t)d * V + c0 + cc + k];
     }
     const float* Mrow = M + ((int64_t)seg * Hv + h) * CK * CK + (int64_t)d * CK;
     for (int l = 0; l < CK; l += 4) {
@@ -55,29 +66,46 @@ __global__ void __launch_bounds__(CTHREADS) compose_kernel(const float* __restri
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = fmaf(mv[u], sS[cur][l + u][cc + j], acc[j]);
+        for (int k = 0; k < 8; ++k) acc[k] = fmaf(mv[u], sS[cur][l + u][cc + k], acc[k]);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sS[cur ^ 1][d][cc + j] = acc[j];
+    for (int k = 0; k < 8; ++k) {
+      sS[cur ^ 1][d][cc + k] = acc[k];
+      if (!write_before) dst[k] = acc[k];
+    }
     cur ^= 1;
     __syncthreads();
   }
   if (final_state) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      final_state[state_head + (int64_t)d * V + c0 + cc + j] = sS[cur][d][cc + j];
+    for (int k = 0; k < 8; ++k)
+      final_state[ci * row + head + (int64_t)d * V + c0 + cc + k] = sS[cur][d][cc + k];
   }
 }
 
 }  // namespace
 
+hipError_t launch_compose_chains(const float* M, const float* b, const float* s0,
+                                 const int32_t* chains, int n_chains, int Hv, int K, int V,
+                                 float* out, int write_before, float* final_state,
+                                 hipStream_t stream) {
+  if (n_chains == 0 || Hv == 0) return hipSuccess;
+  if (K != CK || V % CT != 0) return hipErrorInvalidValue;
+  dim3 grid(V / CT, Hv, n_chains);
+  hipLaunchKernelGGL(compose_kernel, grid, dim3(CTHREADS), 0, stream, M, b, s0, chains, Chain{0, 0, 0, 0}, Hv, V,
+                     out, write_before, final_state);
+  return hipGetLastError();
+}
+
+// One chain over P segments of one sequence: starts of every segment, then
+// the final state.
 hipError_t launch_compose(const float* M, const float* b, const float* s0, int P, int Hv, int K,
                           int V, float* starts, float* final_state, hipStream_t stream) {
   if (P == 0 || Hv == 0) return hipSuccess;
   if (K != CK || V % CT != 0) return hipErrorInvalidValue;
-  dim3 grid(V / CT, Hv);
-  hipLaunchKernelGGL(compose_kernel, grid, dim3(CTHREADS), 0, stream, M, b, s0, P, Hv, V, starts,
-                     final_state);
+  dim3 grid(V / CT, Hv, 1);
+  hipLaunchKernelGGL(compose_kernel, grid, dim3(CTHREADS), 0, stream, M, b, s0, nullptr, Chain{0, 0, P, 0}, Hv, V,
+                     starts, 1, final_state);
   return hipGetLastError();
 }
 

@@ -42,6 +42,13 @@ struct ChunkArgs {
   // bf16 path: per-(chunk slot, v-head) records of the state-independent chunk
   // quantities, chunk_slots(Ttot, n_seqs) * Hv * PREP_RECORD_BYTES bytes
   float* tbuf;
+  // Optional maps of the bf16 scan (all null: block z runs sequence z, whose
+  // start state follows s0_mode and whose final state goes to row z of sf).
+  const int32_t* seq_order;  // [n_blocks_z]: sequence (of cu) that block z runs
+  int n_blocks_z;            // grid z when seq_order is set
+  const int32_t* s0_ref;     // [n_seqs]: >= 0 row of s0_seg, -1 zero, <= -2 row -2-r of s0
+  const float* s0_seg;       // start states [*, Hv, K, V] picked by s0_ref
+  const int32_t* sf_map;     // [n_seqs]: row of sf for the final state, -1 none
 };
 
 // One record: 6 bf16 matrices x 10 tiles x 256, then gamma[64], dec[64] fp32.
@@ -53,10 +60,23 @@ int64_t chunk_slots(int64_t Ttot, int n_seqs);
 hipError_t launch_chunk_prep(const ChunkArgs& a, int with_p, hipStream_t stream);
 
 hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t stream);
-hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t stream);
-// Pass 1 of the segment scan: M columns (v = 0, S0 = I) and b columns (S0 = 0).
-hipError_t launch_segment_pass1(const ChunkArgs& a, float* M, float* b, hipStream_t stream);
+// prep + scan; with prep = false the records in a.tbuf must already be there
+hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t stream, bool prep = true);
+// Pass 1 of the segment scan: M columns (v = 0, S0 = I) and b columns (S0 = 0),
+// row z of M and b for block z.
+hipError_t launch_segment_pass1(const ChunkArgs& a, float* M, float* b, hipStream_t stream,
+                                bool prep = true);
+// fp32 chains of affine maps.  chains[4 c .. 4 c + 3] = {n, p0, count, out0}:
+// chain c starts from row n of s0 (zero when s0 is null or n < 0) and applies
+// maps p0 .. p0 + count - 1 of (M, b) in order; with write_before, out row
+// out0 + j receives the state before map j, else the state after it; final
+// (when not null) row c receives the state after the last map.
+// One chain of P maps (s0 row 0): starts of all P segments and the final state.
 hipError_t launch_compose(const float* M, const float* b, const float* s0, int P, int Hv, int K,
                           int V, float* starts, float* final_state, hipStream_t stream);
+hipError_t launch_compose_chains(const float* M, const float* b, const float* s0,
+                                 const int32_t* chains, int n_chains, int Hv, int K, int V,
+                                 float* out, int write_before, float* final_state,
+                                 hipStream_t stream);
 
 }  // namespace gdn

@@ -1,0 +1,145 @@
+// split_plan.cpp -- host planning of segment splits for packed chunk-rule runs.
+//
+// The chunk scan is serial along a sequence, so a packed batch whose samples
+// differ a lot in length is bounded by its longest sample.  When the offsets
+// are known on the host, long samples are cut into chunk-aligned segments:
+// pass 1 runs the state-only scan of every segment but the last of each
+// sample on the augmented state [M | b] (the segment's affine map), an fp32
+// chain turns the maps into the true start state of every later segment, and
+// pass 2 runs all segments of all samples at once from those starts (the same
+// segment-wise state passing as the segmented entry point, applied per sample).
+// The cut length is chosen with a small list-scheduling model of the two
+// passes on the device's compute units; nothing is split unless the model
+// expects the run to be at least 15% shorter.
+#include "split_plan.h"
+
+#include <algorithm>
+#include <functional>
+#include <queue>
+
+namespace gdn {
+
+namespace {
+
+// Finish time of blocks of the given durations dispatched in order, each to
+// the first free compute unit (one block per unit at a time).
+double makespan(const std::vector<double>& blocks, int cus) {
+  std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+  for (int i = 0; i < cus; ++i) free_at.push(0.0);
+  double end = 0.0;
+  for (double d : blocks) {
+    const double t = free_at.top() + d;
+    free_at.pop();
+    free_at.push(t);
+    end = std::max(end, t);
+  }
+  return end;
+}
+
+}  // namespace
+
+// Upper bound on pass-1 segments: their blocks (K/128 + V/128 per head) fit
+// twice on the compute units.
+int max_prefix_segments(int32_t H_v, int32_t V, int cus) {
+  const int tiles1 = 1 + V / 128;
+  return std::max(0, 2 * cus / std::max(1, H_v * tiles1));
+}
+
+int64_t split_plan_ints_max(int n_seg, int n_prefix) {
+  return 4 * (int64_t)n_seg + 1 + 5 * (int64_t)n_prefix;
+}
+
+bool plan_split(const int32_t* cu, int32_t N, int32_t H_v, int32_t V, bool has_s0, int cus,
+                SplitPlan& out) {
+  const int tiles2 = V / 128, tiles1 = 1 + V / 128;
+  const int pmax = max_prefix_segments(H_v, V, cus);
+  if (pmax == 0) return false;
+  std::vector<int64_t> chunks(N);
+  int64_t cmax = 0;
+  for (int32_t n = 0; n < N; ++n) {
+    chunks[n] = ((int64_t)cu[n + 1] - cu[n] + 63) / 64;
+    cmax = std::max(cmax, chunks[n]);
+  }
+  // pass 2 (or the unsplit scan): longest first
+  auto pass2 = [&](std::vector<int64_t> lens) {
+    std::sort(lens.begin(), lens.end(), std::greater<int64_t>());
+    std::vector<double> blocks;
+    for (int64_t c : lens)
+      for (int i = 0; i < H_v * tiles2; ++i) blocks.push_back((double)c);
+    return makespan(blocks, cus);
+  };
+  const double base = pass2(chunks);
+  double best = base;
+  int64_t best_seg = 0;
+  for (int parts = 2; parts <= 16; ++parts) {
+    const int64_t seg = (cmax + parts - 1) / parts;  // chunks per segment
+    if (seg < 4) break;
+    std::vector<int64_t> lens;
+    int64_t n_prefix = 0, longest_chain = 0;
+    for (int32_t n = 0; n < N; ++n) {
+      const int64_t s = chunks[n] > seg ? (chunks[n] + seg - 1) / seg : 1;
+      n_prefix += s - 1;
+      longest_chain = std::max(longest_chain, s - 1);
+      for (int64_t j = 0; j < s; ++j) lens.push_back(std::min(seg, chunks[n] - j * seg));
+    }
+    if (n_prefix == 0 || n_prefix > pmax) continue;
+    // a pass-1 chunk skips q, the output and P: about 0.7 of a pass-2 chunk;
+    // a chain step costs about one chunk
+    std::vector<double> p1((size_t)n_prefix * H_v * tiles1, 0.7 * (double)seg);
+    const double t = makespan(p1, cus) + (double)longest_chain + pass2(lens);
+    if (t < best) {
+      best = t;
+      best_seg = seg;
+    }
+  }
+  if (best_seg == 0 || best > 0.85 * base) return false;
+
+  // ---- the plan for segments of best_seg chunks --------------------------------
+  struct Seg {
+    int32_t begin, end, n, j, s;
+  };
+  std::vector<Seg> segs;
+  for (int32_t n = 0; n < N; ++n) {
+    const int64_t s = chunks[n] > best_seg ? (chunks[n] + best_seg - 1) / best_seg : 1;
+    for (int64_t j = 0; j < s; ++j) {
+      const int32_t b = (int32_t)(cu[n] + 64 * best_seg * j);
+      const int32_t e = j + 1 < s ? (int32_t)(cu[n] + 64 * best_seg * (j + 1)) : cu[n + 1];
+      segs.push_back({b, e, n, (int32_t)j, (int32_t)s});
+    }
+  }
+  out.n_seg = (int)segs.size();
+  out.n_prefix = 0;
+  out.n_chain = 0;
+  for (const Seg& g : segs) {
+    if (g.j + 1 < g.s) ++out.n_prefix;
+    if (g.j == 0 && g.s > 1) ++out.n_chain;
+  }
+  out.ints.assign((size_t)out.off_chains() + 4 * out.n_chain, 0);
+  int32_t* I = out.ints.data();
+  for (int i = 0; i < out.n_seg; ++i) I[i] = segs[i].begin;
+  I[out.n_seg] = segs.back().end;
+  std::vector<int32_t> order(out.n_seg);
+  for (int i = 0; i < out.n_seg; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+    return segs[x].end - segs[x].begin > segs[y].end - segs[y].begin;
+  });
+  std::copy(order.begin(), order.end(), I + out.off_order());
+  int pre = 0, later = 0, chain = 0;
+  for (int i = 0; i < out.n_seg; ++i) {
+    const Seg& g = segs[i];
+    if (g.j == 0 && g.s > 1) {  // the chain of this sample: maps of its pass-1 segments
+      int32_t* c = I + out.off_chains() + 4 * chain++;
+      c[0] = has_s0 ? g.n : -1;
+      c[1] = pre;
+      c[2] = g.s - 1;
+      c[3] = later;
+    }
+    I[out.off_s0ref() + i] = g.j == 0 ? (has_s0 ? -2 - g.n : -1) : later++;
+    I[out.off_sfmap() + i] = g.j + 1 == g.s ? g.n : -1;
+    if (g.j + 1 < g.s) I[out.off_pre() + pre++] = i;
+  }
+  return true;
+}
+
+
+}  // namespace gdn

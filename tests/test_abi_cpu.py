@@ -83,8 +83,9 @@ def test_chunk_validation(lib):
     assert _chunk(lib, ws=None) == NULLP  # the bf16 path needs its T workspace
     need = lib.gdn_chunk_fwd_workspace_bytes(1, 64, 1, 32, 128, 128)
     record = 6 * 10 * 256 * 2 + 2 * 64 * 4  # per (chunk slot, v-head)
-    assert need == record * (1 + 1) * 32
-    assert _chunk(lib, ws_bytes=need - 1) == SHAPE
+    plain = record * (1 + 1) * 32  # records of every chunk slot; the query adds room for splitting
+    assert need >= plain
+    assert _chunk(lib, ws_bytes=plain - 1) == SHAPE
     assert lib.gdn_chunk_fwd_workspace_bytes(0, 64, 1, 2, 32, 32) == 0  # fp32 path needs none
     # nothing to do: no tokens and no state requested
     assert _chunk(lib, T=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK

@@ -154,6 +154,33 @@ def test_chunk_bf16_packed(gates, V):
     print("\nbf16 %s V=%d o %s final %s" % (gates, V, so, sf))
 
 
+@pytest.mark.parametrize("gates", ["slow", "zero_decay", "fast"])
+@pytest.mark.parametrize("V", [128, 256])
+def test_chunk_bf16_split_long_samples(gates, V):
+    """Packed samples of very different lengths with host offsets: the long ones are cut into
+    segments (pass 1 maps, fp32 chains, pass 2 from the composed starts); outputs and final
+    states match the oracle, and the unsplit run (no host offsets) within the same bound."""
+    lengths = [2500, 0, 700, 64, 1, 1350]
+    d = gdn_inputs.small(38, lengths, 2, 4, 128, V, "bf16", **GATES[gates])
+    s0 = (np.random.default_rng(8).standard_normal((len(lengths), 4, 128, V)) * 0.05).astype(np.float32)
+    o, fin = _run_chunk(d, "bf16", s0, o_dtype=torch.float32)
+    oref, fref = _oracle_chunk(d, s0)
+    so = assert_bf16(host(o), oref, "o")
+    sf = assert_bf16(host(fin), fref, "final")
+    np.testing.assert_array_equal(host(fin)[1], s0[1])  # zero-length sample keeps its state
+    print("\nsplit %s V=%d o %s final %s" % (gates, V, so, sf))
+    q = dev(d["q"], "bf16")[None]
+    k = dev(d["k"], "bf16")[None]
+    v = dev(d["v"], "bf16")[None]
+    g, beta = _gpu_gates(d)
+    o2, f2 = gdn.gdn_chunk_fwd(q, k, v, g[None], beta[None], initial_state=dev(s0),
+                               cu_seqlens=dev(d["cu_seqlens"], "i32"), o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_bf16(host(o2[0]), oref, "o unsplit")
+    if gates != "fast":  # fast decay forgets the start state: both paths can agree bit for bit
+        assert not torch.equal(o2[0], o)  # the split path really ran
+
+
 def test_chunk_bf16_store_o_bf16():
     d = gdn_inputs.small(32, [200, 57], 1, 2, 128, 128, "bf16")
     o, _ = _run_chunk(d, "bf16", o_dtype=torch.bfloat16)

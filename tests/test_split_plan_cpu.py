@@ -1,0 +1,118 @@
+"""Host logic of the segment split of packed runs (csrc/split_plan.cpp), on the CPU.
+
+The planner is compiled with g++ together with a small driver (split_plan_main.cpp) and run on
+sample lengths shaped like the workloads; every plan is checked for what pass 1, the fp32 chains
+and pass 2 rely on: the segments tile every sample in order and are chunk-aligned from its start,
+each later segment gets exactly one composed start state from the chain of its sample, every
+sample's final state comes from its last segment, and the pass-1 list is the non-last segments.
+"""
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "gated_deltanet_linear_chunk_amd", "csrc")
+
+
+@pytest.fixture(scope="module")
+def planner(tmp_path_factory):
+    if shutil.which("g++") is None:
+        pytest.skip("needs g++")
+    exe = str(tmp_path_factory.mktemp("plan") / "split_plan")
+    subprocess.run(["g++", "-O1", "-std=c++17", "-I", CSRC, os.path.join(ROOT, "tests", "split_plan_main.cpp"),
+                    os.path.join(CSRC, "split_plan.cpp"), "-o", exe], check=True)
+
+    def run(lengths, Hv, V, has_s0=True, cus=256):
+        inp = "%d %d %d %d %d %s" % (Hv, V, int(has_s0), cus, len(lengths), " ".join(map(str, lengths)))
+        out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True).stdout.split("\n")
+        split, n_seg, n_prefix, n_chain = map(int, out[0].split())
+        ints = np.array(out[1].split(), dtype=np.int64)
+        return dict(split=bool(split), n_seg=n_seg, n_prefix=n_prefix, n_chain=n_chain, ints=ints,
+                    pmax=int(out[2]))
+    return run
+
+
+def check_plan(p, lengths, has_s0):
+    n_seg, n_prefix, n_chain, I = p["n_seg"], p["n_prefix"], p["n_chain"], p["ints"]
+    assert len(I) == (n_seg + 1) + 3 * n_seg + n_prefix + 4 * n_chain
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    seg_cu = I[: n_seg + 1]
+    o = n_seg + 1
+    order, s0_ref, sf_map = I[o: o + n_seg], I[o + n_seg: o + 2 * n_seg], I[o + 2 * n_seg: o + 3 * n_seg]
+    pre = I[o + 3 * n_seg: o + 3 * n_seg + n_prefix]
+    chains = I[o + 3 * n_seg + n_prefix:].reshape(n_chain, 4)
+    assert seg_cu[0] == 0 and seg_cu[-1] == cu[-1] and np.all(np.diff(seg_cu) >= 0)
+    # segments tile the samples: every sample boundary is a segment boundary
+    assert set(cu.tolist()) <= set(seg_cu.tolist())
+    sample = np.searchsorted(cu, seg_cu[:-1], side="right") - 1
+    # zero-length samples own one empty segment each: attribute by final-state map instead
+    owners = {}
+    for i in range(n_seg):
+        a, b = seg_cu[i], seg_cu[i + 1]
+        if b > a:
+            n = int(sample[i])
+            assert cu[n] <= a and b <= cu[n + 1]
+            assert (a - cu[n]) % 64 == 0  # chunk-aligned from the sample start
+            owners.setdefault(n, []).append(i)
+    assert sorted(order.tolist()) == list(range(n_seg))
+    seg_len = np.diff(seg_cu)
+    assert np.all(np.diff(seg_len[order]) <= 0)  # longest first
+    # final states: one per sample, from its last segment
+    assert sorted(x for x in sf_map.tolist() if x >= 0) == list(range(len(lengths)))
+    later = []
+    for n, segs in owners.items():
+        assert segs == list(range(segs[0], segs[-1] + 1))
+        assert sf_map[segs[-1]] == n and all(sf_map[i] == -1 for i in segs[:-1])
+        assert s0_ref[segs[0]] == ((-2 - n) if has_s0 else -1)
+        later += [int(s0_ref[i]) for i in segs[1:]]
+        for i in segs[:-1]:
+            assert seg_len[i] % 64 == 0
+    assert sorted(later) == list(range(n_prefix))
+    assert sorted(pre.tolist()) == pre.tolist() and len(pre) == n_prefix
+    assert all(sf_map[i] == -1 for i in pre)
+    # chains: sample n's maps are consecutive pass-1 rows, outputs are its later segments' starts
+    assert len(chains) == sum(1 for segs in owners.values() if len(segs) > 1)
+    for n0, p0, count, out0 in chains:
+        n = int(sample[pre[p0]])
+        assert n0 == (n if has_s0 else -1)
+        segs = owners[n]
+        assert count == len(segs) - 1
+        assert pre[p0: p0 + count].tolist() == segs[:-1]
+        assert [int(s0_ref[i]) for i in segs[1:]] == list(range(out0, out0 + count))
+    assert n_prefix <= p["pmax"]
+
+
+def test_packed_workload_is_split(planner):
+    lengths = [1097, 99, 338, 1601, 835, 265, 3540, 417]
+    for has_s0 in (False, True):
+        p = planner(lengths, 32, 128, has_s0)
+        assert p["split"] and p["n_prefix"] >= 1
+        check_plan(p, lengths, has_s0)
+        seg_len = np.diff(p["ints"][: p["n_seg"] + 1])
+        assert seg_len.max() < 3540 * 0.6  # the longest sample no longer bounds the scan
+
+
+@pytest.mark.parametrize("lengths,Hv,V", [
+    ([2500, 0, 700, 64, 1, 1350], 4, 128),
+    ([2500, 0, 700, 64, 1, 1350], 4, 256),
+    ([32768], 16, 128),
+    ([0, 9000, 0], 8, 128),
+    ([64 * 40, 64 * 40 + 1], 2, 128),
+])
+def test_plans_are_consistent(planner, lengths, Hv, V):
+    for has_s0 in (False, True):
+        p = planner(lengths, Hv, V, has_s0)
+        if p["split"]:
+            check_plan(p, lengths, has_s0)
+
+
+@pytest.mark.parametrize("lengths,Hv,V", [
+    ([4096] * 8, 32, 128),           # batched rows: balanced already
+    ([100, 300, 64, 1], 32, 128),    # short samples
+    ([139, 2655, 12374, 17600], 64, 256),  # many heads: no room for pass-1 blocks
+])
+def test_balanced_or_crowded_runs_are_not_split(planner, lengths, Hv, V):
+    assert not planner(lengths, Hv, V)["split"]
