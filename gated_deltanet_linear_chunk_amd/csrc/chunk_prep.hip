@@ -12,8 +12,9 @@
 // One wave owns one (chunk slot, v-head): K and Q fragments come straight from
 // global memory into the 16 x 16 x 32 bf16 MFMA (exact products, fp32 sums);
 // masks are applied in registers; the four 16 x 16 diagonal blocks of T are
-// inverted by forward substitution (lane = block, column) and the block rows
-// follow from T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj.
+// inverted by forward substitution (lane = block, column) and the other
+// blocks follow, one block diagonal at a time, from
+// T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj on fp32 MFMAs.
 //
 // Record per (chunk slot, v-head), PREP_RECORD_BYTES long:
 //   6 bf16 matrices x 10 lower 16 x 16 tiles (i >= j, index i(i+1)/2 + j,
@@ -41,6 +42,21 @@ __device__ __forceinline__ int64_t seq_begin(const ChunkArgs& a, int n) {
 
 __device__ __forceinline__ int blk(int i, int j) { return (i * (i + 1)) / 2 + j; }
 
+// e^x for x = G_r - G_s <= 0 (an fp64 difference, so no cancellation), on the
+// hardware exp2: relative error a few 2^-24, far below the bf16 pairs the
+// results are stored as.
+__device__ __forceinline__ float decay(double x) {
+  return __builtin_amdgcn_exp2f((float)x * 1.4426950408889634f);
+}
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// fp32 16 x 16 x 4 MFMA: lane l holds A[l % 16][l / 16], B[l / 16][l % 16];
+// D rows 4 (l / 16) + e of column l % 16.
+__device__ __forceinline__ f32x4_t mfma_f32_4(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ void tile_rc(int b, int& i, int& j) {
   i = b >= 6 ? 3 : (b >= 3 ? 2 : (b >= 1 ? 1 : 0));
   j = b - (i * (i + 1)) / 2;
@@ -49,7 +65,7 @@ __device__ __forceinline__ void tile_rc(int b, int& i, int& j) {
 __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p) {
   __shared__ float sA[10][16][BP];
   __shared__ float sT[10][16][BP];  // P staging, then T
-  __shared__ float sY[16][BP];
+  __shared__ float sY[3][16][BP];
   __shared__ double sG[CH];
   __shared__ float sBeta[CH], sGam[CH];
 
@@ -142,7 +158,7 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int rr = 4 * g4 + e, r = 16 * i + rr;
-          sT[blk(i, j)][rr][c16] = (r >= s) ? acc[e] * expf((float)(sG[r] - Gs)) : 0.f;
+          sT[blk(i, j)][rr][c16] = (r >= s) ? acc[e] * decay(sG[r] - Gs) : 0.f;
         }
       }
     __syncthreads();
@@ -173,7 +189,7 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int rr = 4 * g4 + e, r = 16 * i + rr;
-        sA[blk(i, j)][rr][c16] = (r > s) ? sBeta[r] * acc[e] * expf((float)(sG[r] - Gs)) : 0.f;
+        sA[blk(i, j)][rr][c16] = (r > s) ? sBeta[r] * acc[e] * decay(sG[r] - Gs) : 0.f;
       }
     }
   __syncthreads();
@@ -195,46 +211,43 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p)
   }
   __syncthreads();
 
-  // ---- T: block rows, lane = (row rr, columns 4 c4 .. 4 c4 + 3) ---------------
+  // ---- T: off-diagonal blocks, T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj -------------
+  // Blocks one diagonal at a time (the blocks of a diagonal are independent);
+  // each 16 x 16 x 16 product is four fp32 MFMAs with operands read from LDS.
   {
-    const int rr = lane >> 2, c4 = (lane & 3) * 4;
-    for (int i = 1; i < 4; ++i) {
-      for (int jb = 0; jb < i; ++jb) {
-        float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
-        for (int kb = jb; kb < i; ++kb) {
-          const float* Ar = sA[blk(i, kb)][rr];
-          const float(*Tk)[BP] = sT[blk(kb, jb)];
+    const int ar = c16, ak = g4;  // A operand: row, k within a 4-step
 #pragma unroll
-          for (int s = 0; s < 16; ++s) {
-            const float av = Ar[s];
-            y0 = fmaf(av, Tk[s][c4], y0);
-            y1 = fmaf(av, Tk[s][c4 + 1], y1);
-            y2 = fmaf(av, Tk[s][c4 + 2], y2);
-            y3 = fmaf(av, Tk[s][c4 + 3], y3);
-          }
-        }
-        sY[rr][c4] = y0;
-        sY[rr][c4 + 1] = y1;
-        sY[rr][c4 + 2] = y2;
-        sY[rr][c4 + 3] = y3;
-        __syncthreads();
-        const float* Ti = sT[blk(i, i)][rr];
-        float t0v = 0.f, t1v = 0.f, t2v = 0.f, t3v = 0.f;
+    for (int dist = 1; dist < 4; ++dist) {
+      // Y_ij = sum_k A_ik T_kj for every block of this diagonal, kept in sY
+      f32x4_t y[3];
 #pragma unroll
-        for (int mm = 0; mm < 16; ++mm) {
-          const float tv = Ti[mm];  // zero above the diagonal
-          t0v = fmaf(tv, sY[mm][c4], t0v);
-          t1v = fmaf(tv, sY[mm][c4 + 1], t1v);
-          t2v = fmaf(tv, sY[mm][c4 + 2], t2v);
-          t3v = fmaf(tv, sY[mm][c4 + 3], t3v);
+      for (int bb = 0; bb < 4 - dist; ++bb) {
+        const int i = bb + dist, j = bb;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int kb = j; kb < i; ++kb) {
+          const float(*Aik)[BP] = sA[blk(i, kb)];
+          const float(*Tkj)[BP] = sT[blk(kb, j)];
+#pragma unroll
+          for (int st = 0; st < 4; ++st) acc = mfma_f32_4(Aik[ar][4 * st + ak], Tkj[4 * st + ak][c16], acc);
         }
-        float* dst = sT[blk(i, jb)][rr];
-        dst[c4] = -t0v;
-        dst[c4 + 1] = -t1v;
-        dst[c4 + 2] = -t2v;
-        dst[c4 + 3] = -t3v;
-        __syncthreads();
+        y[bb] = acc;
       }
+#pragma unroll
+      for (int bb = 0; bb < 4 - dist; ++bb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sY[bb][4 * g4 + e][c16] = y[bb][e];
+      __syncthreads();
+#pragma unroll
+      for (int bb = 0; bb < 4 - dist; ++bb) {
+        const int i = bb + dist, j = bb;
+        const float(*Tii)[BP] = sT[blk(i, i)];
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) acc = mfma_f32_4(Tii[ar][4 * st + ak], sY[bb][4 * st + ak][c16], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sT[blk(i, j)][4 * g4 + e][c16] = -acc[e];
+      }
+      __syncthreads();
     }
   }
 
