@@ -6,7 +6,8 @@
 // (b, M) pairs in fp32).  Each column of the K x V state is its own affine
 // chain, so the work is split over (v-head, 16-column slice): 256 threads per
 // workgroup, each producing 8 entries of M_i S + b_i per step, with the
-// current start state of the slice held in LDS.  Segments follow one another
+// current start state of the slice and the step's M (loaded with coalesced
+// 16-byte reads, all in flight at once) held in LDS.  Segments follow one another
 // inside the workgroup, which needs only the M S products (a tree over
 // segments would also need M M products, K / 16 times more work per level).
 #include "device_common.h"
@@ -32,6 +33,7 @@ __global__ void __launch_bounds__(CTHREADS) compose_kernel(const float* __restri
                                                            float* __restrict__ out, int write_before,
                                                            float* __restrict__ final_state) {
   __shared__ float sS[2][CK][CT];
+  __shared__ __attribute__((aligned(16))) float sM[CK][CK + 4];  // M of the current step
   const int tid = threadIdx.x;
   const int c0 = blockIdx.x * CT;
   const int h = blockIdx.y;
@@ -53,15 +55,28 @@ __global__ void __launch_bounds__(CTHREADS) compose_kernel(const float* __restri
     const int seg = ch.p0 + j;
     const int64_t seg_state = (int64_t)seg * row + head;
     float* dst = out + (int64_t)(ch.out0 + j) * row + head + (int64_t)d * V + c0 + cc;
-    float acc[8];
+    // M of this step into LDS with coalesced 16-byte loads (all in flight at once)
+    const float* Mseg = M + ((int64_t)seg * Hv + h) * CK * CK;
+    float4 mv4[CK * CK / 4 / CTHREADS];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (write_before) dst[k] = sS[cur][d][cc + k];
-      acc[k] = b[seg_state + (int64_t)d * V + c0 + cc + k];
+    for (int i = 0; i < CK * CK / 4 / CTHREADS; ++i)
+      mv4[i] = *reinterpret_cast<const float4*>(Mseg + 4 * (tid + CTHREADS * i));
+    const float4 b0 = *reinterpret_cast<const float4*>(b + seg_state + (int64_t)d * V + c0 + cc);
+    const float4 b1 = *reinterpret_cast<const float4*>(b + seg_state + (int64_t)d * V + c0 + cc + 4);
+#pragma unroll
+    for (int i = 0; i < CK * CK / 4 / CTHREADS; ++i) {
+      const int e = 4 * (tid + CTHREADS * i);
+      *reinterpret_cast<float4*>(&sM[e / CK][e % CK]) = mv4[i];
     }
-    const float* Mrow = M + ((int64_t)seg * Hv + h) * CK * CK + (int64_t)d * CK;
+    float acc[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    if (write_before) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) dst[k] = sS[cur][d][cc + k];
+    }
+    __syncthreads();
+#pragma unroll 4
     for (int l = 0; l < CK; l += 4) {
-      const float4 m4 = *reinterpret_cast<const float4*>(Mrow + l);
+      const float4 m4 = *reinterpret_cast<const float4*>(&sM[d][l]);
       const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
 #pragma unroll
       for (int u = 0; u < 4; ++u)
