@@ -4,12 +4,11 @@
 // slice of V) and walks its 64-token chunks in order.  The K x 128 fp32 state
 // never leaves the registers: wave w holds state columns 16 w .. 16 w + 15 as
 // eight 16 x 16 accumulator tiles.  Everything about a chunk that does not
-// depend on the state -- the UT-transform products -T diag(beta e^G) and
-// T diag(beta) (T = (I + A)^{-1}), the masked Q K^T, e^G and the decays --
-// comes precomputed from the prep kernel (chunk_prep.hip).  Per chunk (local
-// tokens r, s), each wave then does, for its own columns and without any
-// further synchronisation:
-//   U  = T diag(beta) V - T diag(beta e^G) (K S)    (= U0 - W S)
+// depend on the state -- T diag(beta) (T = (I + A)^{-1}, the UT transform),
+// the masked Q K^T, e^G and the decays -- comes precomputed from the prep
+// kernel (chunk_prep.hip).  Per chunk (local tokens r, s), each wave then
+// does, for its own columns and without any further synchronisation:
+//   U  = T diag(beta) (V - diag(e^G) K S)      (= U0 - W S)
 //   O  = diag(e^G) Q S + P U
 //   S <- e^{G_last} S + K^T diag(e^{G_last - G}) U
 // which is the token recurrence regrouped by chunk.  Two barriers per chunk:
@@ -19,15 +18,15 @@
 // global stores are 16-byte vectors.
 //
 // Precision: every fp32 quantity that meets the matrix cores is a bf16 pair
-// hi + lo (~16 significant bits), multiplied against exact bf16 data (q, k,
-// v) or against another pair (hi*hi + hi*lo + lo*hi): S against K and Q, the
-// T products against V and against K S, P against U, the decayed U against K.
+// hi + lo (~16 significant bits), multiplied against exact bf16 data (q, k)
+// or against another pair (hi*hi + hi*lo + lo*hi): S against K and Q, T diag(beta)
+// against V - e^G K S, P against U, the decayed U against K.
 //
 // LDS (bf16 unless noted; row pitches padded by 16 B, which keeps the MFMA
 // fragment reads free of bank conflicts):
 //   sQ [64][136], sK [64][136], sKt [128][72] (K^T), sVt [128][72] (V^T of
-//   this slice), sP [2][64][72] (hi, lo), sT2 [4][64][72] (-T diag(beta e^G)
-//   hi/lo, T diag(beta) hi/lo), sO fp32 [64][132], gamma[64], dec[64] fp32.
+//   this slice), sP [2][64][72] (hi, lo), sT2 [2][64][72] (T diag(beta)
+//   hi/lo), sO fp32 [64][132], gamma[64], dec[64] fp32.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -49,14 +48,14 @@ constexpr int OFF_KT = OFF_K + CH * QP * 2;
 constexpr int OFF_VT = OFF_KT + KD * TP * 2;
 constexpr int OFF_P = OFF_VT + BV * TP * 2;
 constexpr int OFF_T2 = OFF_P + 2 * CH * TP * 2;
-constexpr int OFF_O = OFF_T2 + 4 * CH * TP * 2;
+constexpr int OFF_O = OFF_T2 + 2 * CH * TP * 2;
 constexpr int OFF_GAM = OFF_O + CH * OP * 4;
 constexpr int OFF_DEC = OFF_GAM + CH * 4;
 constexpr int LDS_BYTES = OFF_DEC + CH * 4;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
-// 16-byte units of a prep record: 6 x 10 tiles x 32, then gamma and dec
-constexpr int REC_MAT_UNITS = 6 * 10 * 32;
+// 16-byte units of a prep record: 4 x 10 tiles x 32, then gamma and dec
+constexpr int REC_MAT_UNITS = 4 * 10 * 32;
 constexpr int REC_UNITS = REC_MAT_UNITS + 2 * 16;
 static_assert(REC_UNITS * 16 == PREP_RECORD_BYTES, "record layout");
 
@@ -183,7 +182,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
 
   // Upper tiles of sP and sT2 that the triangular products read must be zero;
   // the record stash only ever writes the lower tiles.
-  for (int i = tid; i < (2 + 4) * CH * TP; i += NT) sP[i] = 0;
+  for (int i = tid; i < (2 + 2) * CH * TP; i += NT) sP[i] = 0;
 
   // ---- prefetch registers --------------------------------------------------
   // Every prefetch load is unconditional (rows past the end of the sequence
@@ -267,8 +266,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
           int bi, bj;
           tile_ij(rem >> 5, bi, bj);
           const int r = 16 * bi + ((rem >> 1) & 15), c = 16 * bj + 8 * (rem & 1);
-          // sP (two matrices) sits right before the four matrices of sT2
-          dst = smem + OFF_T2 + 2 * ((mat < 4 ? mat : mat - 6) * CH * TP + r * TP + c);
+          // sP (two matrices) sits right before the two matrices of sT2
+          dst = smem + OFF_T2 + 2 * ((mat < 2 ? mat : mat - 4) * CH * TP + r * TP + c);
         } else {
           const int g = f - REC_MAT_UNITS;  // 0..15 gamma, 16..31 dec
           dst = smem + OFF_GAM + 16 * g;
@@ -315,57 +314,58 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
     }
 
     if (more_) GDN_PF_KQ(t0 + CH);
-    // ---- U = T diag(beta) V - T diag(beta e^G) (K S) --------------------------
-    // The two sums go to separate accumulators (U, X) so that consecutive
-    // products alternate between independent tiles.
-    f32x4 U[NCT][4], X[NCT][4];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        zero4(U[ct][rt]);
-        zero4(X[ct][rt]);
-      }
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      bf16x8 kh[NCT], kl[NCT], fv[NCT];
+    // ---- U = T diag(beta) (V - e^G K S) ------------------------------------------
+    // R = V - gamma * (K S) is formed in the accumulator layout (V read from its
+    // transposed tile, four consecutive tokens per lane), split into bf16
+    // pairs, and multiplied by T diag(beta) as hi*hi + hi*lo + lo*hi.
+    f32x4 U[NCT][4];
+    {
+      bf16x8 rh[NCT][2], rl[NCT][2];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        split_frag(KS[ct][2 * m], KS[ct][2 * m + 1], kh[ct], kl[ct]);
-        if (load_v) fv[ct] = lds_frag(sVt, TP, wave * CPW + 16 * ct + c16, 32 * m, g4);
-      }
-      bf16x8 wh[4], wl[4], th[4], tl[4];
+        f32x4 R[4];
 #pragma unroll
-      for (int rt = 2 * m; rt < 4; ++rt) {
-        wh[rt] = lds_frag(sT2, TP, 16 * rt + c16, 32 * m, g4);
-        wl[rt] = lds_frag(sT2 + CH * TP, TP, 16 * rt + c16, 32 * m, g4);
-        if (load_v) {
-          th[rt] = lds_frag(sT2 + 2 * CH * TP, TP, 16 * rt + c16, 32 * m, g4);
-          tl[rt] = lds_frag(sT2 + 3 * CH * TP, TP, 16 * rt + c16, 32 * m, g4);
-        }
-      }
-#pragma unroll
-      for (int part = 0; part < 5; ++part) {
-        const bool to_u = part == 1 || part == 3;
-        if (to_u && !load_v) continue;
-#pragma unroll
-        for (int rt = 2 * m; rt < 4; ++rt)
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) {
-            if (part == 0) X[ct][rt] = mfma16(wh[rt], kh[ct], X[ct][rt]);
-            if (part == 1) U[ct][rt] = mfma16(th[rt], fv[ct], U[ct][rt]);
-            if (part == 2) X[ct][rt] = mfma16(wh[rt], kl[ct], X[ct][rt]);
-            if (part == 3) U[ct][rt] = mfma16(tl[rt], fv[ct], U[ct][rt]);
-            if (part == 4) X[ct][rt] = mfma16(wl[rt], kh[ct], X[ct][rt]);
+        for (int rt = 0; rt < 4; ++rt) {
+          const float4 gam = *reinterpret_cast<const float4*>(sGam + 16 * rt + 4 * g4);
+          R[rt][0] = -gam.x * KS[ct][rt][0];
+          R[rt][1] = -gam.y * KS[ct][rt][1];
+          R[rt][2] = -gam.z * KS[ct][rt][2];
+          R[rt][3] = -gam.w * KS[ct][rt][3];
+          if (load_v) {
+            const u32x2 vv =
+                *reinterpret_cast<const u32x2*>(sVt + (wave * CPW + 16 * ct + c16) * TP + 16 * rt + 4 * g4);
+            R[rt][0] += __uint_as_float(vv[0] << 16);
+            R[rt][1] += __uint_as_float(vv[0] & 0xFFFF0000u);
+            R[rt][2] += __uint_as_float(vv[1] << 16);
+            R[rt][3] += __uint_as_float(vv[1] & 0xFFFF0000u);
           }
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) split_frag(R[2 * m], R[2 * m + 1], rh[ct][m], rl[ct][m]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) zero4(U[ct][rt]);
       }
-      SCHED_FENCE();
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        bf16x8 th[4], tl[4];
+#pragma unroll
+        for (int rt = 2 * m; rt < 4; ++rt) {
+          th[rt] = lds_frag(sT2, TP, 16 * rt + c16, 32 * m, g4);
+          tl[rt] = lds_frag(sT2 + CH * TP, TP, 16 * rt + c16, 32 * m, g4);
+        }
+#pragma unroll
+        for (int part = 0; part < 3; ++part)
+#pragma unroll
+          for (int rt = 2 * m; rt < 4; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+              const bf16x8 ta = part == 2 ? tl[rt] : th[rt];
+              const bf16x8 rb = part == 1 ? rl[ct][m] : rh[ct][m];
+              U[ct][rt] = mfma16(ta, rb, U[ct][rt]);
+            }
+        SCHED_FENCE();
+      }
     }
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) U[ct][rt] += X[ct][rt];
-
     if (more_) GDN_PF_V(t0 + CH);
     if (kOut) {
       // ---- O = diag(gamma) Q S + P U  -> fp32 O tile in LDS -------------------

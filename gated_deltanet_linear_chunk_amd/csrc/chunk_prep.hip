@@ -17,10 +17,12 @@
 // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj on fp32 MFMAs.
 //
 // Record per (chunk slot, v-head), PREP_RECORD_BYTES long:
-//   6 bf16 matrices x 10 lower 16 x 16 tiles (i >= j, index i(i+1)/2 + j,
+//   4 bf16 matrices x 10 lower 16 x 16 tiles (i >= j, index i(i+1)/2 + j,
 //   row-major inside a tile), in the order
-//     -T diag(beta e^G) hi, lo;  T diag(beta) hi, lo;  P hi, lo
+//     T diag(beta) hi, lo;  P hi, lo
 //   (hi = bf16(x), lo = bf16(x - hi)), then gamma[64] and dec[64] in fp32.
+// (The UT transform's other product, T diag(beta e^G) K S, is formed by the
+// scan as T diag(beta) (e^G * K S), so it needs no matrix of its own.)
 // Without outputs (state-only runs) the P tiles are not written.
 // Chunk slots: chunk j of sequence n (first token cu[n] + 64 j) has slot
 // floor((cu[n] + 64 j) / 64) + n, which is unique and below
@@ -67,7 +69,7 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p)
   __shared__ float sT[10][16][BP];  // P staging, then T
   __shared__ float sY[3][16][BP];
   __shared__ double sG[CH];
-  __shared__ float sBeta[CH], sGam[CH];
+  __shared__ float sBeta[CH];
 
   const int lane = threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
@@ -94,9 +96,40 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p)
   const int L = (int)((eos - t0) < CH ? (eos - t0) : CH);
 
   unsigned char* rec = (unsigned char*)a.tbuf + ((int64_t)slot * a.Hv + h) * PREP_RECORD_BYTES;
-  uint16_t* rmat = (uint16_t*)rec;  // [6][10][256]
-  float* rgam = (float*)(rec + 6 * 10 * 256 * 2);
+  uint16_t* rmat = (uint16_t*)rec;  // [4][10][256]
+  float* rgam = (float*)(rec + 4 * 10 * 256 * 2);
   float* rdec = rgam + CH;
+
+  // ---- K and Q fragments straight from global memory, in flight first ----------
+  // row tile i, k-step m: contiguous k = 32 m + 8 g4 .. +7; rows past L read
+  // the last row and are zeroed (every load unconditional)
+  const int64_t head_off = (int64_t)hq * KD + 8 * g4;
+  bf16x8 kf[4][4], qf[4][4];
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * i + c16;
+      const int64_t row = t0 + (r < L ? r : L - 1);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>((const uint16_t*)a.k + row * a.k_stride + head_off + 32 * m);
+        kf[i][m] = __builtin_bit_cast(bf16x8, r < L ? v : z);
+      }
+    }
+    if (with_p) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * i + c16;
+        const int64_t row = t0 + (r < L ? r : L - 1);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>((const uint16_t*)a.q + row * a.q_stride + head_off + 32 * m);
+          qf[i][m] = __builtin_bit_cast(bf16x8, r < L ? v : z);
+        }
+      }
+    }
+  }
 
   // ---- gates: G (fp64 prefix sum), gamma, dec ---------------------------------
   {
@@ -112,40 +145,14 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p)
     const float gam = expf((float)G);
     sG[lane] = G;
     sBeta[lane] = b;
-    sGam[lane] = gam;
     rgam[lane] = gam;
     rdec[lane] = expf((float)(Glast - G));
   }
 
-  // ---- K (and Q) fragments straight from global memory ----------------------
-  // row tile i, k-step m: contiguous k = 32 m + 8 g4 .. +7; rows past L are 0
-  const int64_t head_off = (int64_t)hq * KD + 8 * g4;
-  bf16x8 kf[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * i + c16;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (r < L) v = *reinterpret_cast<const u32x4*>((const uint16_t*)a.k + (t0 + r) * a.k_stride + head_off + 32 * m);
-      kf[i][m] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
   __syncthreads();  // gates visible to all lanes
 
   // ---- P = lower(Q K^T * decay) -> record (hi, lo) ----------------------------
   if (with_p) {
-    bf16x8 qf[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * i + c16;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (r < L) v = *reinterpret_cast<const u32x4*>((const uint16_t*)a.q + (t0 + r) * a.q_stride + head_off + 32 * m);
-        qf[i][m] = __builtin_bit_cast(bf16x8, v);
-      }
-    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -170,8 +177,8 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p)
       uint32_t h0, l0, h1, l1;
       split2(src[0], src[1], h0, l0);
       split2(src[2], src[3], h1, l1);
-      *reinterpret_cast<u32x2*>(rmat + (4 * 10 + b) * 256 + e4) = u32x2{h0, h1};
-      *reinterpret_cast<u32x2*>(rmat + (5 * 10 + b) * 256 + e4) = u32x2{l0, l1};
+      *reinterpret_cast<u32x2*>(rmat + (2 * 10 + b) * 256 + e4) = u32x2{h0, h1};
+      *reinterpret_cast<u32x2*>(rmat + (3 * 10 + b) * 256 + e4) = u32x2{l0, l1};
     }
     __syncthreads();  // sT is reused for T
   }
@@ -251,7 +258,7 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p)
     }
   }
 
-  // ---- -T diag(beta e^G), T diag(beta) as bf16 pairs -> record ----------------
+  // ---- T diag(beta) as bf16 pairs -> record -----------------------------------
 #pragma unroll
   for (int u = 0; u < 10; ++u) {
     const int f = lane + 64 * u;
@@ -260,21 +267,14 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p)
     tile_rc(b, bi, bj);
     const int s = 16 * bj + cc;
     const float* src = &sT[b][rr][cc];
-    float tb[4], tw[4];
+    float tb[4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      tb[x] = src[x] * sBeta[s + x];
-      tw[x] = -tb[x] * sGam[s + x];  // stored negated: the scan subtracts it
-    }
-    uint32_t wh0, wl0, wh1, wl1, uh0, ul0, uh1, ul1;
-    split2(tw[0], tw[1], wh0, wl0);
-    split2(tw[2], tw[3], wh1, wl1);
+    for (int x = 0; x < 4; ++x) tb[x] = src[x] * sBeta[s + x];
+    uint32_t uh0, ul0, uh1, ul1;
     split2(tb[0], tb[1], uh0, ul0);
     split2(tb[2], tb[3], uh1, ul1);
-    *reinterpret_cast<u32x2*>(rmat + (0 * 10 + b) * 256 + e4) = u32x2{wh0, wh1};
-    *reinterpret_cast<u32x2*>(rmat + (1 * 10 + b) * 256 + e4) = u32x2{wl0, wl1};
-    *reinterpret_cast<u32x2*>(rmat + (2 * 10 + b) * 256 + e4) = u32x2{uh0, uh1};
-    *reinterpret_cast<u32x2*>(rmat + (3 * 10 + b) * 256 + e4) = u32x2{ul0, ul1};
+    *reinterpret_cast<u32x2*>(rmat + (0 * 10 + b) * 256 + e4) = u32x2{uh0, uh1};
+    *reinterpret_cast<u32x2*>(rmat + (1 * 10 + b) * 256 + e4) = u32x2{ul0, ul1};
   }
 }
 

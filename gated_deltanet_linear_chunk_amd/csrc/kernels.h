@@ -51,8 +51,8 @@ struct ChunkArgs {
   const int32_t* sf_map;     // [n_seqs]: row of sf for the final state, -1 none
 };
 
-// One record: 6 bf16 matrices x 10 tiles x 256, then gamma[64], dec[64] fp32.
-constexpr int PREP_RECORD_BYTES = 6 * 10 * 256 * 2 + 2 * 64 * 4;
+// One record: 4 bf16 matrices x 10 tiles x 256, then gamma[64], dec[64] fp32.
+constexpr int PREP_RECORD_BYTES = 4 * 10 * 256 * 2 + 2 * 64 * 4;
 
 // Number of chunk slots a launch over Ttot tokens in n_seqs sequences uses.
 int64_t chunk_slots(int64_t Ttot, int n_seqs);

@@ -82,7 +82,7 @@ def test_chunk_validation(lib):
     assert _chunk(lib, cu=FAKE, cu_host=start, n_seqs=2) == SEQ
     assert _chunk(lib, ws=None) == NULLP  # the bf16 path needs its T workspace
     need = lib.gdn_chunk_fwd_workspace_bytes(1, 64, 1, 32, 128, 128)
-    record = 6 * 10 * 256 * 2 + 2 * 64 * 4  # per (chunk slot, v-head)
+    record = 4 * 10 * 256 * 2 + 2 * 64 * 4  # per (chunk slot, v-head)
     plain = record * (1 + 1) * 32  # records of every chunk slot; the query adds room for splitting
     assert need >= plain
     assert _chunk(lib, ws_bytes=plain - 1) == SHAPE
