@@ -8,8 +8,9 @@ H_v = 32, K = V = 128, bf16): gates, causal conv1d + SiLU + q/k L2 norm over
 the 8192 q|k|v channels, and the chunked delta rule reading q, k, v straight
 out of the conv output.  Inputs are resident in HBM before the timed region.
 The line printed is one JSON object (see the fields below); `value` is tokens
-per second of the whole step.  The chunk kernel's own duration is measured
-with HIP events recorded on the stream it runs on, and set against the HBM
+per second of the whole step.  The duration of the gdn_chunk_fwd call (its
+kernels: chunk prep, segment pass 1, map chains, scan) is measured with HIP
+events recorded on the stream it runs on, and set against the HBM
 roofline (its algorithmic bytes) and the bf16 MFMA peak (its algorithmic
 flops).  The fp64 CPU oracle is timed on the same workload on the host.
 Extras time the other workloads (segment-parallel long sequence, batched
@@ -56,7 +57,8 @@ def conv_alg_bytes(T, C, in_bytes=2):
     return 2 * in_bytes * T * C
 
 
-CHUNK_SOURCES = ("chunk_prep.hip", "chunk_bf16.hip", "device_common.h", "kernels.h")
+CHUNK_SOURCES = ("chunk_prep.hip", "chunk_bf16.hip", "compose.hip", "split_plan.cpp", "api.cpp", "device_common.h",
+                 "kernels.h")
 
 
 def sources_digest(names):
@@ -68,7 +70,7 @@ def sources_digest(names):
 
 
 def profiled_traffic(workload):
-    """HBM bytes per gdn_chunk_fwd launch (FETCH_SIZE + WRITE_SIZE of its two kernels, scaled by a copy
+    """HBM bytes per gdn_chunk_fwd call (FETCH_SIZE + WRITE_SIZE of its kernels, scaled by a copy
     calibration) from the committed rocprofv3 summary; None when the kernel sources have changed since
     the counters were taken, or when there is no summary."""
     path = os.path.join(ROOT, "profiles", "chunk_fwd_%s.md" % workload)
@@ -298,7 +300,8 @@ def main():
         "mfma_frac_chunk": flops_chunk / (chunk_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": profiled_traffic(MAIN),
-                     "kernel": "gdn_chunk_fwd = chunk_prep_kernel + chunk_scan_kernel<0,8>",
+                     "kernel": "gdn_chunk_fwd (segment-split path) = plan copy + chunk_prep_kernel + "
+                               "chunk_scan_kernel<2,8> + compose_kernel + chunk_scan_kernel<0,8>",
                      "alg_bytes_per_launch": bytes_chunk, "alg_flops_per_launch": flops_chunk,
                      "avg_launch_ms": chunk_ms},
         "kernels_ms": {"chunk": chunk_ms, "conv1d": conv_ms},
