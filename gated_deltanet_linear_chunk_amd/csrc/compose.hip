@@ -4,12 +4,16 @@
 // every segment follows from S_start,0 = S0 and S_start,i+1 = M_i S_start,i + b_i,
 // composed in fp32 (the sglang fork PR "Qwen3.5 cp - #1" chain-reduces its
 // (b, M) pairs in fp32).  Each column of the K x V state is its own affine
-// chain, so the work is split over (v-head, 16-column slice): 256 threads per
-// workgroup, each producing 8 entries of M_i S + b_i per step, with the
-// current start state of the slice and the step's M (loaded with coalesced
-// 16-byte reads, all in flight at once) held in LDS.  Segments follow one another
-// inside the workgroup, which needs only the M S products (a tree over
-// segments would also need M M products, K / 16 times more work per level).
+// chain, so the work is split over (v-head, 16-column slice).  A step is the
+// 128 x 128 by 128 x 16 product M_i S on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32, fp32 products and sums): wave w of the workgroup owns
+// row tiles 2w and 2w + 1, reads its rows of M_i straight from global memory
+// (16-byte loads, all in flight at once) and the state slice from LDS.  The k
+// order of the sums is free, so lane group g (lanes 16g .. 16g + 15) takes
+// k = 32 g + s at step s, which makes its M reads contiguous.  Segments follow
+// one another inside the workgroup, which needs only the M S products (a tree
+// over segments would also need M M products, K / 16 times more work per
+// level).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -20,6 +24,11 @@ namespace {
 constexpr int CK = 128;  // key dim
 constexpr int CT = 16;   // state columns per workgroup
 constexpr int CTHREADS = 256;
+// State slice in LDS: row k at k * CT + 16 * (k / 32), so that the four lane
+// groups of a fragment read (rows 32 apart) fall on different banks.
+constexpr int SROWS = CK * CT + 16 * (CK / 32);
+
+__device__ __forceinline__ int sidx(int k, int c) { return k * CT + c + 16 * (k >> 5); }
 
 struct Chain {
   int n, p0, count, out0;
@@ -32,69 +41,76 @@ __global__ void __launch_bounds__(CTHREADS) compose_kernel(const float* __restri
                                                            Chain single, int Hv, int V,
                                                            float* __restrict__ out, int write_before,
                                                            float* __restrict__ final_state) {
-  __shared__ float sS[2][CK][CT];
-  __shared__ __attribute__((aligned(16))) float sM[CK][CK + 4];  // M of the current step
+  __shared__ float sS[2][SROWS];
   const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, c = lane & 15;  // lane group, column within the slice
   const int c0 = blockIdx.x * CT;
   const int h = blockIdx.y;
   const int ci = blockIdx.z;
   const Chain ch = chains ? Chain{chains[4 * ci], chains[4 * ci + 1], chains[4 * ci + 2], chains[4 * ci + 3]}
                           : single;
-  const int d = tid >> 1;          // output row
-  const int cc = (tid & 1) * 8;    // 8 output columns
 
   const int64_t head = (int64_t)h * CK * V;
   const int64_t row = (int64_t)Hv * CK * V;  // one [Hv, K, V] state
   for (int i = tid; i < CK * CT; i += CTHREADS) {
-    const int r = i / CT, c = i % CT;
-    sS[0][r][c] = (s0 && ch.n >= 0) ? s0[ch.n * row + head + (int64_t)r * V + c0 + c] : 0.f;
+    const int r = i / CT, cc = i % CT;
+    sS[0][sidx(r, cc)] = (s0 && ch.n >= 0) ? s0[ch.n * row + head + (int64_t)r * V + c0 + cc] : 0.f;
   }
   __syncthreads();
+  // accumulator element e of row tile t: row 16 (2 wave + t) + 4 g + e, column c
+  int orow[2][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) orow[t][e] = 16 * (2 * wave + t) + 4 * g + e;
   int cur = 0;
   for (int j = 0; j < ch.count; ++j) {
     const int seg = ch.p0 + j;
-    const int64_t seg_state = (int64_t)seg * row + head;
-    float* dst = out + (int64_t)(ch.out0 + j) * row + head + (int64_t)d * V + c0 + cc;
-    // M of this step into LDS with coalesced 16-byte loads (all in flight at once)
+    const float* bseg = b + (int64_t)seg * row + head + c0 + c;
+    float* dst = out + (int64_t)(ch.out0 + j) * row + head + c0 + c;
+    // A operands: rows 16 (2 wave + t) + c of M, k = 32 g .. 32 g + 31
     const float* Mseg = M + ((int64_t)seg * Hv + h) * CK * CK;
-    float4 mv4[CK * CK / 4 / CTHREADS];
+    f32x4 ma[2][8];
 #pragma unroll
-    for (int i = 0; i < CK * CK / 4 / CTHREADS; ++i)
-      mv4[i] = *reinterpret_cast<const float4*>(Mseg + 4 * (tid + CTHREADS * i));
-    const float4 b0 = *reinterpret_cast<const float4*>(b + seg_state + (int64_t)d * V + c0 + cc);
-    const float4 b1 = *reinterpret_cast<const float4*>(b + seg_state + (int64_t)d * V + c0 + cc + 4);
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int i = 0; i < CK * CK / 4 / CTHREADS; ++i) {
-      const int e = 4 * (tid + CTHREADS * i);
-      *reinterpret_cast<float4*>(&sM[e / CK][e % CK]) = mv4[i];
-    }
-    float acc[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      for (int q = 0; q < 8; ++q)
+        ma[t][q] = *reinterpret_cast<const f32x4*>(Mseg + (int64_t)(16 * (2 * wave + t) + c) * CK + 32 * g + 4 * q);
+    f32x4 acc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[t][e] = bseg[(int64_t)orow[t][e] * V];
     if (write_before) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) dst[k] = sS[cur][d][cc + k];
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int l = 0; l < CK; l += 4) {
-      const float4 m4 = *reinterpret_cast<const float4*>(&sM[d][l]);
-      const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k] = fmaf(mv[u], sS[cur][l + u][cc + k], acc[k]);
+        for (int e = 0; e < 4; ++e) dst[(int64_t)orow[t][e] * V] = sS[cur][sidx(orow[t][e], c)];
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      sS[cur ^ 1][d][cc + k] = acc[k];
-      if (!write_before) dst[k] = acc[k];
+    for (int s = 0; s < 32; ++s) {
+      const float bv = sS[cur][sidx(32 * g + s, c)];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ma[t][s >> 2][s & 3], bv, acc[t], 0, 0, 0);
     }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sS[cur ^ 1][sidx(orow[t][e], c)] = acc[t][e];
+        if (!write_before) dst[(int64_t)orow[t][e] * V] = acc[t][e];
+      }
     cur ^= 1;
     __syncthreads();
   }
   if (final_state) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      final_state[ci * row + head + (int64_t)d * V + c0 + cc + k] = sS[cur][d][cc + k];
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        final_state[ci * row + head + (int64_t)orow[t][e] * V + c0 + c] = sS[cur][sidx(orow[t][e], c)];
   }
 }
 

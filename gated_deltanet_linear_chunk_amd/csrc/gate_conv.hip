@@ -331,7 +331,8 @@ __device__ __forceinline__ void conv1d_run(const T* __restrict__ x, const T* __r
   auto load_sub = [&](typename Row::raw_t(&buf)[SUB], int64_t ts) {
 #pragma unroll
     for (int i = 0; i < SUB; ++i) {
-      const int64_t r = ts + i < p.Ttot ? ts + i : p.Ttot - 1;
+      // rows past the run re-read its last row (a cache hit), not the next run's
+      const int64_t r = ts + i < tw1 ? ts + i : tw1 - 1;
       buf[i] = Row::load(x + r * C + cl);
     }
   };
