@@ -173,11 +173,11 @@ __device__ __forceinline__ float group_sum(float v, int lanes_log2) {
 // Whether y (fp32, from bf16 inputs) might round to another bf16 value than
 // the exact conv (+ SiLU) result.  The tap products are exact and each of the
 // four fused sums rounds once, by at most 2^-24 of its magnitude, which is
-// below A = |bias| + sum |w| * xmax (xmax: the largest |x| of the channel over
-// the sub-tile and its history); the SiLU evaluation adds a few ulp of y.
+// below A = |bias| + sum_j |w_j| |x_j| (the output's own taps, summed in fp32
+// alongside z); the SiLU evaluation adds a few ulp of y.
 // E = 2^-20 |y| + 9 * 2^-24 A covers both about twice over.  The nearest
 // rounding midpoint to y is the one above its bf16 truncation.
-// Ab = 9 * 2^-24 * A, prepared once per sub-tile and channel.
+// Ab = 9 * 2^-24 * A.
 __device__ __forceinline__ bool rounding_in_doubt(float y, float Ab) {
   const float E = fmaf(0x1p-20f, fabsf(y), Ab);
   const float mid = __uint_as_float((__float_as_uint(y) & 0xFFFF0000u) | 0x8000u);
@@ -185,17 +185,15 @@ __device__ __forceinline__ bool rounding_in_doubt(float y, float Ab) {
 }
 
 // One conv (+ SiLU) output in fp64 (the products of bf16 values and their sum
-// are exact there), stored as its nearest bf16.
+// are exact there), stored as its nearest bf16.  hist: how many rows before t
+// lie in t's sample (at most 3 matter).
 __device__ __noinline__ void settle_value(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                                           const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
-                                          const int32_t* __restrict__ cu, int n_seqs, int64_t row_len,
-                                          int64_t Ttot, int64_t C, int width, int apply_silu, int64_t t,
-                                          int64_t c) {
-  const int64_t back_max = t - region_start(cu, n_seqs, row_len, Ttot, t);
+                                          int64_t C, int width, int apply_silu, int64_t t, int64_t c, int hist) {
   double z = bias ? (double)bf16_bits_to_f32(bias[c]) : 0.0;
   for (int j = 0; j < width; ++j) {
     const int back = width - 1 - j;  // tap j multiplies x[t - back]
-    if (back <= back_max)
+    if (back <= hist)
       z += (double)bf16_bits_to_f32(w[c * width + j]) * (double)bf16_bits_to_f32(x[(t - back) * C + c]);
   }
   const double v = apply_silu ? z / (1.0 + exp(-z)) : z;
@@ -226,7 +224,7 @@ __device__ __forceinline__ void conv_sub(const typename ConvRow<T>::raw_t (&buf)
                                          float (&h3)[CONV_CH_PER_THREAD],
                                          const float (&wt)[4][CONV_CH_PER_THREAD],
                                          const float (&bs)[CONV_CH_PER_THREAD],
-                                         const float (&wabs)[CONV_CH_PER_THREAD], int n_valid,
+                                         int n_valid,
                                          uint32_t hist_code, const ConvParams& p, bool active,
                                          T* __restrict__ yrow, uint32_t* queue, uint32_t* qcount,
                                          int64_t ts, int64_t tw0, int c0, bool& overflow) {
@@ -234,21 +232,6 @@ __device__ __forceinline__ void conv_sub(const typename ConvRow<T>::raw_t (&buf)
   constexpr int SUB = Row::SUB;
   constexpr int NCH = CONV_CH_PER_THREAD;
   constexpr bool kCheck = kMode == 1 && sizeof(T) == 2;
-  float Ab[NCH];
-  if (kCheck) {
-    float xm[NCH];
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) xm[i] = fmaxf(fmaxf(fabsf(h1[i]), fabsf(h2[i])), fabsf(h3[i]));
-#pragma unroll
-    for (int tt = 0; tt < SUB; ++tt) {
-      float r[NCH];
-      Row::unpack(buf[tt], r);
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) xm[i] = fmaxf(xm[i], fabsf(r[i]));
-    }
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) Ab[i] = fmaf(wabs[i], xm[i], fabsf(bs[i])) * (9.f * 0x1p-24f);
-  }
 #pragma unroll
   for (int tt = 0; tt < SUB; ++tt) {
     if (kMasked && tt >= n_valid) break;
@@ -270,7 +253,14 @@ __device__ __forceinline__ void conv_sub(const typename ConvRow<T>::raw_t (&buf)
       const float v = p.apply_silu ? z * __builtin_amdgcn_rcpf(1.f + __expf(-z)) : z;
       out[i] = v;
       if (kMode == 2) ss = fmaf(v, v, ss);
-      if (kCheck) dbits |= (rounding_in_doubt(v, Ab[i]) ? 1u : 0u) << i;
+      if (kCheck) {
+        float A = fabsf(bs[i]);
+        A = fmaf(fabsf(wt[0][i]), fabsf(x1), A);
+        A = fmaf(fabsf(wt[1][i]), fabsf(x2), A);
+        A = fmaf(fabsf(wt[2][i]), fabsf(x3), A);
+        A = fmaf(fabsf(wt[3][i]), fabsf(cur[i]), A);
+        dbits |= (rounding_in_doubt(v, A * (9.f * 0x1p-24f)) ? 1u : 0u) << i;
+      }
       h1[i] = h2[i];
       h2[i] = h3[i];
       h3[i] = cur[i];
@@ -284,14 +274,15 @@ __device__ __forceinline__ void conv_sub(const typename ConvRow<T>::raw_t (&buf)
     if (active) Row::store(yrow + (int64_t)tt * p.C, out);
     if constexpr (kCheck) {
       if (active && dbits) {  // rare: queue (token, channel) for the fp64 pass
+        // entry = channel within the launch << 10 | history rows << 8 | token within the run
         const uint32_t nq = (uint32_t)__popc(dbits);
         uint32_t pos = atomicAdd(qcount, nq);
+        const uint32_t tag = ((uint32_t)hist << 8) | (uint32_t)(ts + tt - tw0);
         while (dbits) {
           const int i = __builtin_ctz(dbits);
           dbits &= dbits - 1;
-          const int64_t t = ts + tt;
-          if (pos < CONV_QCAP)  // (channel within the launch) << 8 | token within the run
-            queue[pos] = ((uint32_t)(c0 + i - p.c_begin) << 8) | (uint32_t)(t - tw0);
+          if (pos < CONV_QCAP)
+            queue[pos] = ((uint32_t)(c0 + i - p.c_begin) << 10) | tag;
           else  // queue full: this lane settles its whole run at the end
             overflow = true;
           ++pos;
@@ -339,7 +330,7 @@ __device__ __forceinline__ void conv1d_run(const T* __restrict__ x, const T* __r
   load_sub(bufA, tw0);
 
   // ---- taps aligned so that tap 3 multiplies the current token --------------------
-  float wt[4][NCH], bs[NCH], wabs[NCH];
+  float wt[4][NCH], bs[NCH];
   if (sizeof(T) == 2 && p.width == 4) {  // 8 channels x 4 taps = 64 contiguous bytes
     const uint16_t* wp = reinterpret_cast<const uint16_t*>(w) + (int64_t)cl * 4;
 #pragma unroll
@@ -370,14 +361,21 @@ __device__ __forceinline__ void conv1d_run(const T* __restrict__ x, const T* __r
 #pragma unroll
     for (int i = 0; i < NCH; ++i) bs[i] = bias ? Row::scalar(bias, cl + i) : 0.f;
   }
-#pragma unroll
-  for (int i = 0; i < NCH; ++i)
-    wabs[i] = fabsf(wt[0][i]) + fabsf(wt[1][i]) + fabsf(wt[2][i]) + fabsf(wt[3][i]);
 
   // ---- region (sample / batch row) of the first token ----------------------------
   int n = 0;
   int64_t s_start, s_end;
-  if (p.cu) {
+  if (p.cu && p.n_seqs < 64) {
+    // one load of every offset across the wave instead of a chain of
+    // dependent loads: the sample is the last n with cu[n] <= tw0
+    const int li = lane < p.n_seqs ? lane : p.n_seqs;
+    const int cl_ = (int)clampi(p.cu[li], 0, p.Ttot);
+    const uint64_t m = __ballot(lane < p.n_seqs && cl_ <= tw0);
+    n = m ? 63 - __builtin_clzll(m) : 0;
+    s_start = __builtin_amdgcn_readfirstlane(__shfl(cl_, n, 64));
+    const int64_t e_ = __builtin_amdgcn_readfirstlane(__shfl(cl_, n + 1, 64));
+    s_end = e_ > s_start ? e_ : s_start;
+  } else if (p.cu) {
     n = find_sample(p.cu, p.n_seqs, tw0, p.Ttot);
     s_start = clampi(p.cu[n], 0, p.Ttot);
     s_end = clampi(p.cu[n + 1], s_start, p.Ttot);
@@ -429,10 +427,10 @@ __device__ __forceinline__ void conv1d_run(const T* __restrict__ x, const T* __r
     const int nv_ = (int)((TS) + SUB < tw1 ? SUB : tw1 - (TS));                                        \
     T* yrow_ = y + (TS) * C + c0;                                                                      \
     if (masked_)                                                                                       \
-      conv_sub<T, kMode, true>(BUF, h1, h2, h3, wt, bs, wabs, nv_, code_, p, active, yrow_, queue,     \
+      conv_sub<T, kMode, true>(BUF, h1, h2, h3, wt, bs, nv_, code_, p, active, yrow_, queue,           \
                                qcount, (TS), tw0, c0, overflow);                                       \
     else                                                                                               \
-      conv_sub<T, kMode, false>(BUF, h1, h2, h3, wt, bs, wabs, nv_, code_, p, active, yrow_, queue,    \
+      conv_sub<T, kMode, false>(BUF, h1, h2, h3, wt, bs, nv_, code_, p, active, yrow_, queue,          \
                                 qcount, (TS), tw0, c0, overflow);                                      \
   } while (0)
   for (int64_t ts = tw0; ts < tw1; ts += 2 * SUB) {
@@ -451,22 +449,56 @@ __device__ __forceinline__ void conv1d_run(const T* __restrict__ x, const T* __r
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // A lane takes entries lane, lane + 64, ...: every load of all of them is
+    // issued first (one memory round trip; unused slots read a valid
+    // address), then each value is recomputed in fp64 and stored.
     const uint32_t nq = min(*qcount, (uint32_t)CONV_QCAP);
-    for (uint32_t e = lane; e < nq; e += 64) {
-      const uint32_t v = queue[e];
+    constexpr int SE = CONV_QCAP / 64;
+    const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+    const uint16_t* wb = reinterpret_cast<const uint16_t*>(w);
+    const uint16_t* bb = reinterpret_cast<const uint16_t*>(bias);
+    bool eok[SE];
+    int64_t et[SE], ec[SE];
+    int eh[SE];
+    uint16_t xv[SE][4], wv[SE][4], bv[SE];
+#pragma unroll
+    for (int k = 0; k < SE; ++k) {
+      const uint32_t e = lane + 64u * k;
+      const uint32_t v = queue[e < nq ? e : 0];
       const int64_t t = tw0 + (int64_t)(v & 0xFFu);
-      const int64_t c = p.c_begin + (int64_t)(v >> 8);
-      if (t >= tw1 || c >= p.c_end) continue;  // entries come from active lanes only
-      settle_value(reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w),
-                   reinterpret_cast<const uint16_t*>(bias), reinterpret_cast<uint16_t*>(y), p.cu, p.n_seqs,
-                   p.row_len, p.Ttot, C, p.width, p.apply_silu, t, c);
+      const int64_t c = p.c_begin + (int64_t)(v >> 10);
+      eok[k] = e < nq && t < tw1 && c < p.c_end;  // entries come from active lanes only
+      et[k] = eok[k] ? t : tw0;
+      ec[k] = eok[k] ? c : p.c_begin;
+      eh[k] = (int)((v >> 8) & 3u);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int jj = j < p.width ? j : p.width - 1;
+        const int64_t r = et[k] - (p.width - 1 - jj);  // tap jj multiplies x[t - (width - 1 - jj)]
+        xv[k][j] = xb[(r < 0 ? 0 : r) * C + ec[k]];
+        wv[k][j] = wb[ec[k] * p.width + jj];
+      }
+      bv[k] = bb ? bb[ec[k]] : (uint16_t)0;
+    }
+#pragma unroll
+    for (int k = 0; k < SE; ++k) {
+      if (!eok[k]) continue;
+      double z = (double)bf16_bits_to_f32(bv[k]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j < p.width && p.width - 1 - j <= eh[k])
+          z += (double)bf16_bits_to_f32(wv[k][j]) * (double)bf16_bits_to_f32(xv[k][j]);
+      const double val = p.apply_silu ? z / (1.0 + exp(-z)) : z;
+      reinterpret_cast<uint16_t*>(y)[et[k] * C + ec[k]] = f32_to_bf16_bits(bf16_nearest_f64(val));
     }
     if (overflow && active) {  // more doubtful values than the queue holds: redo the run in fp64
-      for (int64_t t = tw0; t < tw1; ++t)
+      for (int64_t t = tw0; t < tw1; ++t) {
+        const int64_t back = t - region_start(p.cu, p.n_seqs, p.row_len, p.Ttot, t);
         for (int i = 0; i < NCH; ++i)
           settle_value(reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w),
-                       reinterpret_cast<const uint16_t*>(bias), reinterpret_cast<uint16_t*>(y), p.cu,
-                       p.n_seqs, p.row_len, p.Ttot, C, p.width, p.apply_silu, t, c0 + i);
+                       reinterpret_cast<const uint16_t*>(bias), reinterpret_cast<uint16_t*>(y), C, p.width,
+                       p.apply_silu, t, c0 + i, back < 3 ? (int)back : 3);
+      }
     }
   }
 }
@@ -522,6 +554,9 @@ hipError_t launch_conv1d(const void* x, const void* w, const void* bias, int dt,
     const int64_t per_min = (subs + 65534) / 65535;  // grid y stays within 65535
     if (per < per_min) per = per_min;
     p.tile_tokens = (int)(per * sub);
+    // queued bf16 roundings name their token within the run in 8 bits and
+    // their channel within the launch in 22
+    if (dt == 1 && (p.tile_tokens > 256 || p.c_end - p.c_begin > (1 << 22))) return hipErrorInvalidValue;
     const dim3 grid((unsigned)cblocks, (unsigned)((Ttot + p.tile_tokens - 1) / p.tile_tokens));
     if (dt == 1)
       hipLaunchKernelGGL(conv1d_kernel<uint16_t>, grid, dim3(CONV_THREADS), 0, stream, (const uint16_t*)x,
