@@ -64,7 +64,7 @@ __device__ __forceinline__ void tile_rc(int b, int& i, int& j) {
   j = b - (i * (i + 1)) / 2;
 }
 
-__global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p) {
+__global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p, int heads_per_wave) {
   __shared__ float sA[10][16][BP];
   __shared__ float sT[10][16][BP];  // P staging, then T
   __shared__ float sY[3][16][BP];
@@ -74,8 +74,8 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p)
   const int lane = threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int slot = blockIdx.x;
-  const int h = blockIdx.y;
-  const int hq = h / (a.Hv / a.Hqk);
+  const int h0 = blockIdx.y * heads_per_wave;  // v-heads h0 .. h0 + heads_per_wave - 1 share q/k head hq
+  const int hq = h0 / (a.Hv / a.Hqk);
 
   // sequence n owning this slot: the largest n with floor(cu[n]/64) + n <= slot
   int lo = 0, hi = a.n_seqs - 1;
@@ -94,11 +94,6 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p)
   const int64_t t0 = bos + 64 * j0;
   if (t0 >= eos) return;  // unused slot
   const int L = (int)((eos - t0) < CH ? (eos - t0) : CH);
-
-  unsigned char* rec = (unsigned char*)a.tbuf + ((int64_t)slot * a.Hv + h) * PREP_RECORD_BYTES;
-  uint16_t* rmat = (uint16_t*)rec;  // [4][10][256]
-  float* rgam = (float*)(rec + 4 * 10 * 256 * 2);
-  float* rdec = rgam + CH;
 
   // ---- K and Q fragments straight from global memory, in flight first ----------
   // row tile i, k-step m: contiguous k = 32 m + 8 g4 .. +7; rows past L read
@@ -130,6 +125,14 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p)
       }
     }
   }
+
+  for (int hh = 0; hh < heads_per_wave; ++hh) {
+  const int h = h0 + hh;
+  unsigned char* rec = (unsigned char*)a.tbuf + ((int64_t)slot * a.Hv + h) * PREP_RECORD_BYTES;
+  uint16_t* rmat = (uint16_t*)rec;  // [4][10][256]
+  float* rgam = (float*)(rec + 4 * 10 * 256 * 2);
+  float* rdec = rgam + CH;
+  if (hh > 0) __syncthreads();  // the previous head is done with the LDS tiles
 
   // ---- gates: G (fp64 prefix sum), gamma, dec ---------------------------------
   {
@@ -276,6 +279,7 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p)
     *reinterpret_cast<u32x2*>(rmat + (0 * 10 + b) * 256 + e4) = u32x2{uh0, uh1};
     *reinterpret_cast<u32x2*>(rmat + (1 * 10 + b) * 256 + e4) = u32x2{ul0, ul1};
   }
+  }  // v-heads of this q/k head
 }
 
 }  // namespace
@@ -285,7 +289,10 @@ int64_t chunk_slots(int64_t Ttot, int n_seqs) { return (Ttot + 63) / 64 + n_seqs
 hipError_t launch_chunk_prep(const ChunkArgs& a, int with_p, hipStream_t stream) {
   const int64_t slots = chunk_slots(a.Ttot, a.n_seqs);
   if (slots == 0 || a.Hv == 0) return hipSuccess;
-  hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)slots, a.Hv), dim3(64), 0, stream, a, with_p);
+  // Two v-heads that read the same q/k head share one wave (one load of the
+  // q/k fragments and half the waves); otherwise one v-head per wave.
+  const int per = (a.Hv / a.Hqk) % 2 == 0 ? 2 : 1;
+  hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)slots, a.Hv / per), dim3(64), 0, stream, a, with_p, per);
   return hipGetLastError();
 }
 
