@@ -403,45 +403,6 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
               const bf16x8 ub = part == 1 ? Ulo[ct][m] : Uhi[ct][m];
               O[ct][rt] = mfma16(pa, ub, O[ct][rt]);
             }
-        SCHED_FENCE();
-      }
-      // Through this wave's own columns of the O tile (no other wave touches
-      // them, and a wave's LDS accesses complete in order) to 16-byte stores.
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sO[(16 * rt + 4 * g4 + e) * OP + wave * CPW + 16 * ct + c16] = O[ct][rt][e];
-      // Rows past the end of the chunk store a second copy of its last row
-      // instead, so that every store is unconditional and the memory counter
-      // waits further on stay exact.
-      constexpr int RUNS = CPW / 8;  // 8-column runs per row
-#pragma unroll
-      for (int i = 0; i < CH * RUNS / 64; ++i) {
-        const int u = lane + 64 * i;
-        const int r = min(u / RUNS, L - 1), c = wave * CPW + 8 * (u % RUNS);
-        const float* src = sO + r * OP + c;
-        const float4 x0 = *reinterpret_cast<const float4*>(src);
-        const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
-        {
-          const int64_t off = ((t0 + r) * a.Hv + h) * (int64_t)a.V + v0 + c;
-          if (kMode == kOutBF16) {
-            uint4 w;
-            w.x = pack_bf16x2(a.scale * x0.x, a.scale * x0.y);
-            w.y = pack_bf16x2(a.scale * x0.z, a.scale * x0.w);
-            w.z = pack_bf16x2(a.scale * x1.x, a.scale * x1.y);
-            w.w = pack_bf16x2(a.scale * x1.z, a.scale * x1.w);
-            *reinterpret_cast<uint4*>((uint16_t*)a.o + off) = w;
-          } else {
-            float* dst = (float*)a.o + off;
-            *reinterpret_cast<float4*>(dst) =
-                make_float4(a.scale * x0.x, a.scale * x0.y, a.scale * x0.z, a.scale * x0.w);
-            *reinterpret_cast<float4*>(dst + 4) =
-                make_float4(a.scale * x1.x, a.scale * x1.y, a.scale * x1.z, a.scale * x1.w);
-          }
-        }
       }
     }
     // ---- S <- e^{G_last} S + K^T (diag(dec) U) -------------------------------
@@ -487,6 +448,46 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
               }
           SCHED_FENCE();
         }
+    }
+    if (kOut) {
+      // Through this wave's own columns of the O tile (no other wave touches
+      // them, and a wave's LDS accesses complete in order) to 16-byte stores.
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sO[(16 * rt + 4 * g4 + e) * OP + wave * CPW + 16 * ct + c16] = O[ct][rt][e];
+      // Rows past the end of the chunk store a second copy of its last row
+      // instead, so that every store is unconditional and the memory counter
+      // waits further on stay exact.
+      constexpr int RUNS = CPW / 8;  // 8-column runs per row
+#pragma unroll
+      for (int i = 0; i < CH * RUNS / 64; ++i) {
+        const int u = lane + 64 * i;
+        const int r = min(u / RUNS, L - 1), c = wave * CPW + 8 * (u % RUNS);
+        const float* src = sO + r * OP + c;
+        const float4 x0 = *reinterpret_cast<const float4*>(src);
+        const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+        {
+          const int64_t off = ((t0 + r) * a.Hv + h) * (int64_t)a.V + v0 + c;
+          if (kMode == kOutBF16) {
+            uint4 w;
+            w.x = pack_bf16x2(a.scale * x0.x, a.scale * x0.y);
+            w.y = pack_bf16x2(a.scale * x0.z, a.scale * x0.w);
+            w.z = pack_bf16x2(a.scale * x1.x, a.scale * x1.y);
+            w.w = pack_bf16x2(a.scale * x1.z, a.scale * x1.w);
+            *reinterpret_cast<uint4*>((uint16_t*)a.o + off) = w;
+          } else {
+            float* dst = (float*)a.o + off;
+            *reinterpret_cast<float4*>(dst) =
+                make_float4(a.scale * x0.x, a.scale * x0.y, a.scale * x0.z, a.scale * x0.w);
+            *reinterpret_cast<float4*>(dst + 4) =
+                make_float4(a.scale * x1.x, a.scale * x1.y, a.scale * x1.z, a.scale * x1.w);
+          }
+        }
+      }
     }
   }
 
