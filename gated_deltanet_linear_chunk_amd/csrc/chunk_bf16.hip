@@ -54,10 +54,14 @@ constexpr int OFF_DEC = OFF_GAM + CH * 4;
 constexpr int LDS_BYTES = OFF_DEC + CH * 4;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
-// 16-byte units of a prep record: 4 x 10 tiles x 32, then gamma and dec
-constexpr int REC_MAT_UNITS = 4 * 10 * 32;
-constexpr int REC_UNITS = REC_MAT_UNITS + 2 * 16;
+// 16-byte units of a prep record: T diag(beta) hi, lo (2 x 10 tiles x 32),
+// gamma and dec (2 x 16), then P hi, lo (2 x 10 x 32).  Forward scans read all
+// of it, state-only scans the part before P.
+constexpr int REC_TB_UNITS = 2 * 10 * 32;
+constexpr int REC_STATE_UNITS = REC_TB_UNITS + 2 * 16;
+constexpr int REC_UNITS = REC_STATE_UNITS + 2 * 10 * 32;
 static_assert(REC_UNITS * 16 == PREP_RECORD_BYTES, "record layout");
+static_assert(REC_TB_UNITS * 16 == PREP_REC_GAM && REC_STATE_UNITS * 16 == PREP_REC_P, "record layout");
 
 // Kernel modes: forward with fp32 o, forward with bf16 o, state only / pass 1.
 enum { kOutF32 = 0, kOutBF16 = 1, kPass1 = 2 };
@@ -86,8 +90,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   constexpr int CPW = BV / NW;     // state columns per wave
   constexpr int NCT = CPW / 16;    // 16-column tiles per wave
   constexpr int NPAIR = 512 / NT;  // (row pair, 8 columns) units per thread per matrix
-  constexpr int NREC = (REC_UNITS + NT - 1) / NT;  // record units per thread
   constexpr bool kOut = kMode != kPass1;
+  constexpr int RUNITS = kOut ? REC_UNITS : REC_STATE_UNITS;  // record units this mode reads
+  constexpr int NREC = (RUNITS + NT - 1) / NT;                 // record units per thread
   static_assert(CPW % 16 == 0 && NW * CPW == BV, "wave layout");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -201,7 +206,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   do {                                                                                        \
     const unsigned char* rs_ = rbase + (((T0) >> 6) + seq) * rslot_stride;                    \
     _Pragma("unroll") for (int u_ = 0; u_ < NREC; ++u_)                                        \
-      pr[u_] = *reinterpret_cast<const u32x4*>(rs_ + 16 * min(tid + u_ * NT, REC_UNITS - 1));   \
+      pr[u_] = *reinterpret_cast<const u32x4*>(rs_ + 16 * min(tid + u_ * NT, RUNITS - 1));      \
   } while (0)
 #define GDN_PF_KQ(T0)                                                                          \
   do {                                                                                        \
@@ -255,21 +260,22 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
     }
     {
       // Every unit is stored (no branch around a store): a unit past the end
-      // of the record holds a copy of the last unit and rewrites it in place,
-      // and in state-only runs the P units land unused in sP.
+      // of what this mode reads holds a copy of its last unit and rewrites it
+      // in place.
 #pragma unroll
       for (int u = 0; u < NREC; ++u) {
-        const int f = min(tid + u * NT, REC_UNITS - 1);
+        const int f = min(tid + u * NT, RUNITS - 1);
         unsigned char* dst;
-        if (f < REC_MAT_UNITS) {
-          const int mat = f / 320, rem = f - 320 * mat;
+        if (f < REC_TB_UNITS || f >= REC_STATE_UNITS) {
+          // T diag(beta) hi, lo -> sT2; P hi, lo -> sP (two matrices each)
+          const int fm = f < REC_TB_UNITS ? f : f - REC_STATE_UNITS;
+          const int mat = fm / 320, rem = fm - 320 * mat;
           int bi, bj;
           tile_ij(rem >> 5, bi, bj);
           const int r = 16 * bi + ((rem >> 1) & 15), c = 16 * bj + 8 * (rem & 1);
-          // sP (two matrices) sits right before the two matrices of sT2
-          dst = smem + OFF_T2 + 2 * ((mat < 2 ? mat : mat - 4) * CH * TP + r * TP + c);
+          dst = smem + (f < REC_TB_UNITS ? OFF_T2 : OFF_P) + 2 * (mat * CH * TP + r * TP + c);
         } else {
-          const int g = f - REC_MAT_UNITS;  // 0..15 gamma, 16..31 dec
+          const int g = f - REC_TB_UNITS;  // 0..15 gamma, 16..31 dec
           dst = smem + OFF_GAM + 16 * g;
         }
         *reinterpret_cast<u32x4*>(dst) = pr[u];

@@ -17,10 +17,10 @@
 // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj on fp32 MFMAs.
 //
 // Record per (chunk slot, v-head), PREP_RECORD_BYTES long:
-//   4 bf16 matrices x 10 lower 16 x 16 tiles (i >= j, index i(i+1)/2 + j,
-//   row-major inside a tile), in the order
-//     T diag(beta) hi, lo;  P hi, lo
-//   (hi = bf16(x), lo = bf16(x - hi)), then gamma[64] and dec[64] in fp32.
+//   T diag(beta) hi, lo;  gamma[64], dec[64] (fp32);  P hi, lo
+//   (each matrix: 10 lower 16 x 16 bf16 tiles, i >= j, index i(i+1)/2 + j,
+//   row-major inside a tile; hi = bf16(x), lo = bf16(x - hi)), so that a
+//   state-only scan reads one contiguous prefix.
 // (The UT transform's other product, T diag(beta e^G) K S, is formed by the
 // scan as T diag(beta) (e^G * K S), so it needs no matrix of its own.)
 // Without outputs (state-only runs) the P tiles are not written.
@@ -129,9 +129,10 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p,
   for (int hh = 0; hh < heads_per_wave; ++hh) {
   const int h = h0 + hh;
   unsigned char* rec = (unsigned char*)a.tbuf + ((int64_t)slot * a.Hv + h) * PREP_RECORD_BYTES;
-  uint16_t* rmat = (uint16_t*)rec;  // [4][10][256]
-  float* rgam = (float*)(rec + 4 * 10 * 256 * 2);
-  float* rdec = rgam + CH;
+  uint16_t* rtb = (uint16_t*)(rec + PREP_REC_TB);  // [2][10][256]
+  uint16_t* rp = (uint16_t*)(rec + PREP_REC_P);    // [2][10][256]
+  float* rgam = (float*)(rec + PREP_REC_GAM);
+  float* rdec = (float*)(rec + PREP_REC_DEC);
   if (hh > 0) __syncthreads();  // the previous head is done with the LDS tiles
 
   // ---- gates: G (fp64 prefix sum), gamma, dec ---------------------------------
@@ -180,8 +181,8 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p,
       uint32_t h0, l0, h1, l1;
       split2(src[0], src[1], h0, l0);
       split2(src[2], src[3], h1, l1);
-      *reinterpret_cast<u32x2*>(rmat + (2 * 10 + b) * 256 + e4) = u32x2{h0, h1};
-      *reinterpret_cast<u32x2*>(rmat + (3 * 10 + b) * 256 + e4) = u32x2{l0, l1};
+      *reinterpret_cast<u32x2*>(rp + (0 * 10 + b) * 256 + e4) = u32x2{h0, h1};
+      *reinterpret_cast<u32x2*>(rp + (1 * 10 + b) * 256 + e4) = u32x2{l0, l1};
     }
     __syncthreads();  // sT is reused for T
   }
@@ -276,8 +277,8 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p,
     uint32_t uh0, ul0, uh1, ul1;
     split2(tb[0], tb[1], uh0, ul0);
     split2(tb[2], tb[3], uh1, ul1);
-    *reinterpret_cast<u32x2*>(rmat + (0 * 10 + b) * 256 + e4) = u32x2{uh0, uh1};
-    *reinterpret_cast<u32x2*>(rmat + (1 * 10 + b) * 256 + e4) = u32x2{ul0, ul1};
+    *reinterpret_cast<u32x2*>(rtb + (0 * 10 + b) * 256 + e4) = u32x2{uh0, uh1};
+    *reinterpret_cast<u32x2*>(rtb + (1 * 10 + b) * 256 + e4) = u32x2{ul0, ul1};
   }
   }  // v-heads of this q/k head
 }

@@ -51,8 +51,13 @@ struct ChunkArgs {
   const int32_t* sf_map;     // [n_seqs]: row of sf for the final state, -1 none
 };
 
-// One record: 4 bf16 matrices x 10 tiles x 256, then gamma[64], dec[64] fp32.
-constexpr int PREP_RECORD_BYTES = 4 * 10 * 256 * 2 + 2 * 64 * 4;
+// One record: T diag(beta) hi, lo (bf16, 10 tiles x 256 each), gamma[64] and
+// dec[64] (fp32), then P hi, lo; a state-only scan reads just the part before P.
+constexpr int PREP_REC_TB = 0;                        // 2 x 10 x 256 bf16
+constexpr int PREP_REC_GAM = PREP_REC_TB + 2 * 10 * 256 * 2;
+constexpr int PREP_REC_DEC = PREP_REC_GAM + 64 * 4;
+constexpr int PREP_REC_P = PREP_REC_DEC + 64 * 4;     // 2 x 10 x 256 bf16
+constexpr int PREP_RECORD_BYTES = PREP_REC_P + 2 * 10 * 256 * 2;
 
 // Number of chunk slots a launch over Ttot tokens in n_seqs sequences uses.
 int64_t chunk_slots(int64_t Ttot, int n_seqs);
