@@ -125,6 +125,38 @@ def recurrence(
     return o, fin
 
 
+def decode_step(q, k, v, g, beta, state, scale: float = 1.0, state_indices=None):
+    """One token of the gated delta rule for each of N sequences, in fp64.
+
+    The recurrent decode step that follows a prefill (the sglang fork PR
+    "Qwen3.5 cp - #1" hands the final state of the prefill to the standard
+    decode path): per sequence n and v-head h, with S = state[r, h] (K x V),
+    S <- e^g S; u <- beta (v - S^T k); S <- S + k u^T; o <- scale S^T q.
+    q, k [N, Hqk, K]; v [N, Hv, V]; g, beta [N, Hv]; state [R, Hv, K, V].
+    Row r = state_indices[n] (or n when None); a negative index skips the
+    sequence (o = 0, no state touched).  v-head h reads q/k head h // (Hv // Hqk).
+    Returns (o [N, Hv, V], the updated state as a new array).
+    """
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    S_all = _f64(state).copy()
+    N, Hqk, K = k.shape
+    Hv, V = v.shape[1], v.shape[2]
+    grp = Hv // Hqk
+    o = np.zeros((N, Hv, V))
+    for n in range(N):
+        r = n if state_indices is None else int(state_indices[n])
+        if r < 0:
+            continue
+        for h in range(Hv):
+            kk, qq = k[n, h // grp], q[n, h // grp]
+            S = np.exp(g[n, h]) * S_all[r, h]
+            u = beta[n, h] * (v[n, h] - S.T @ kk)
+            S = S + np.outer(kk, u)
+            o[n, h] = scale * (S.T @ qq)
+            S_all[r, h] = S
+    return o, S_all
+
+
 def transition(k, g, beta, t0: int, t1: int, Hqk: int, Hv: int, threads: int = 0) -> np.ndarray:
     """M [Hv, K, K] = A_{t1-1} ... A_{t0}, A_t = e^{g_t}(I - beta_t k_t k_t^T), by dense products."""
     lib = _load()

@@ -89,6 +89,47 @@ def test_handworked_recurrence():
     np.testing.assert_allclose(fin[0, 0], np.array(d["final_state"]), rtol=0, atol=1e-15)
 
 
+def test_decode_steps_reproduce_handworked_recurrence():
+    """Decode steps from the zero state, one token at a time, give the hand-worked o and state."""
+    d = json.load(open(os.path.join(GOLDEN, "handworked_recurrence_K2_V2.json")))
+    S = np.zeros((1, 1, 2, 2))
+    for t in range(3):
+        o, S = oracle.decode_step(np.array(d["q"][t])[None, None], np.array(d["k"][t])[None, None],
+                                  np.array(d["v"][t])[None, None], np.array([[d["g"][t]]]),
+                                  np.array([[d["beta"][t]]]), S)
+        np.testing.assert_allclose(o[0, 0], np.array(d["o"][t]), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(S[0, 0], np.array(d["final_state"]), rtol=0, atol=1e-15)
+
+
+def test_decode_step_is_one_token_samples_of_the_recurrence():
+    """N sequences of one token each through the C recurrence (with GQA, a scale, rows picked by
+    indices, a skipped slot) equal the decode step."""
+    rng = np.random.default_rng(31)
+    N, Hqk, Hv, K, V, R = 5, 2, 4, 6, 3, 7
+    q, k, v, g, beta, _ = _rand_case(32, N, Hqk, Hv, K, V, unit_keys=True)
+    state = rng.standard_normal((R, Hv, K, V))
+    idx = np.array([3, 0, -1, 6, 2])
+    o, S = oracle.decode_step(q, k, v, g, beta, state, scale=0.7, state_indices=idx)
+    live = idx >= 0
+    cu = np.arange(int(live.sum()) + 1)
+    orr, fin = oracle.recurrence(q[live], k[live], v[live], g[live], beta[live], state[idx[live]], cu, scale=0.7)
+    assert np.abs(o[live] - orr).max() <= 1e-12 * np.abs(orr).max()
+    assert np.abs(S[idx[live]] - fin).max() <= 1e-12 * np.abs(fin).max()
+    assert np.all(o[~live] == 0)
+    untouched = np.setdiff1d(np.arange(R), idx[live])
+    assert np.array_equal(S[untouched], state[untouched])
+
+
+def test_decode_after_prefill_continues_the_sequence():
+    """Recurrence over T tokens, then a decode step on token T, equals the recurrence over T + 1."""
+    q, k, v, g, beta, S0 = _rand_case(33, 21, 1, 2, 4, 3, unit_keys=True, s0=True)
+    o_all, fin_all = oracle.recurrence(q, k, v, g, beta, S0)
+    _, fin = oracle.recurrence(q[:-1], k[:-1], v[:-1], g[:-1], beta[:-1], S0)
+    o, S = oracle.decode_step(q[-1:], k[-1:], v[-1:], g[-1:], beta[-1:], fin)
+    assert np.abs(o[0] - o_all[-1]).max() <= 1e-12 * np.abs(o_all).max()
+    assert np.abs(S - fin_all).max() <= 1e-12 * np.abs(fin_all).max()
+
+
 @pytest.mark.parametrize("seed,T,Hqk,Hv,K,V", [(0, 17, 1, 1, 3, 2), (1, 40, 1, 2, 5, 4), (2, 64, 2, 4, 8, 8), (3, 9, 2, 2, 1, 1)])
 def test_bruteforce_tiny(seed, T, Hqk, Hv, K, V):
     q, k, v, g, beta, S0 = _rand_case(seed, T, Hqk, Hv, K, V, unit_keys=(K > 1), s0=True)
