@@ -14,7 +14,8 @@ events recorded on the stream it runs on, and set against the HBM
 roofline (its algorithmic bytes) and the bf16 MFMA peak (its algorithmic
 flops).  The fp64 CPU oracle is timed on the same workload on the host.
 Extras time the other workloads (segment-parallel long sequence, batched
-prefill, wide state) with the same method.
+prefill, wide state, and the recurrent decode step on 256 sequences) with the
+same method.
 """
 
 from __future__ import annotations
@@ -204,6 +205,38 @@ def build_chunk_only(w, d, o_dtype, segmented=False):
     return step, timer
 
 
+DECODE_N = 256  # sequences per decode step
+
+
+def decode_alg_bytes(N, Hqk, Hv, K, V, in_bytes=2, o_bytes=4):
+    """HBM bytes one decode step must move: every state read and written once, plus the token's inputs and o."""
+    return N * (Hv * K * V * 4 * 2 + in_bytes * (2 * Hqk * K + Hv * V) + 8 * Hv + o_bytes * Hv * V)
+
+
+def build_decode(N, Hqk, Hv, K, V):
+    """One decode token for each of N sequences (bf16 q/k/v, fp32 states of N(0, 0.02) updated in place)."""
+    torch = _torch()
+    import gated_deltanet_linear_chunk_amd as gdn
+
+    d = gdn_inputs.small(4242, [1] * N, Hqk, Hv, K, V, "bf16", s0_std=0.02, name="decode")
+    dev = torch.device("cuda:0")
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)  # noqa: E731
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)  # noqa: E731
+    q, k, v = bf(d["q"]), bf(d["k"]), bf(d["v"])
+    g, beta = gdn.gdn_gate_fwd(f32(d["a"]), f32(d["b"]), f32(d["A_log"]), f32(d["dt_bias"]))
+    state = f32(d["s0"])
+    timer = Timer()
+
+    def step(time_kernels=False):
+        e = timer.start() if time_kernels else None
+        o = gdn.gdn_decode_step(q, k, v, g, beta, state, o_dtype=torch.float32)
+        if time_kernels:
+            timer.stop(e)
+        return o
+
+    return step, timer
+
+
 def timed(step, steps, warmup):
     torch = _torch()
     for _ in range(warmup):
@@ -331,6 +364,16 @@ def main():
             }
             del st, dx
             torch.cuda.empty_cache()
+        st, tm = build_decode(DECODE_N, 16, 32, 128, 128)
+        s = timed(st, max(3, args.steps // 4), 2)
+        ms = tm.mean_ms()
+        nbytes = decode_alg_bytes(DECODE_N, 16, 32, 128, 128)
+        extras["decode_bf16_N%d_Hv32_K128[decode step]" % DECODE_N] = {
+            "tokens_per_s": DECODE_N / s, "ms_per_step": s * 1e3, "main_kernel_ms": ms,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "alg_bytes": nbytes,
+        }
+        del st
+        torch.cuda.empty_cache()
         result["extras"] = extras
 
     if not args.no_cpu:

@@ -26,6 +26,7 @@ __all__ = [
     "gdn_segmented_workspace_bytes",
     "gdn_chunk_fwd_workspace_bytes",
     "gdn_segment_state_scan_workspace_bytes",
+    "gdn_decode_step",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -46,6 +47,7 @@ EXPORTED_SYMBOLS = (
     "gdn_segment_state_scan",
     "gdn_segmented_workspace_bytes",
     "gdn_chunk_fwd_segmented",
+    "gdn_decode_step",
 )
 
 
@@ -91,8 +93,10 @@ def load_library():
     lib.gdn_segmented_workspace_bytes.restype = sz
     lib.gdn_chunk_fwd_segmented.argtypes = [P, P, P, ctypes.c_int, i64, i64, i64, P, P, f32, P, P, P, i32, i64, i32,
                                             i32, i32, i32, P, ctypes.c_int, P, P, sz, P]
+    lib.gdn_decode_step.argtypes = [P, P, P, ctypes.c_int, P, P, f32, P, P, i64, i32, i32, i32, i32, i32, P,
+                                    ctypes.c_int, P]
     for name in ("gdn_gate_fwd", "gdn_conv1d_fwd", "gdn_chunk_fwd", "gdn_segment_state_scan",
-                 "gdn_chunk_fwd_segmented"):
+                 "gdn_chunk_fwd_segmented", "gdn_decode_step"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -356,3 +360,37 @@ def gdn_chunk_fwd_segmented(q, k, v, g, beta, seg_offsets, seg_offsets_host=None
     )
     _check("gdn_chunk_fwd_segmented", st)
     return o, fin
+
+
+def gdn_decode_step(q, k, v, g, beta, state, scale: float = 1.0, state_indices=None, o_dtype=None):
+    """Recurrent decode step: one new token per sequence, state updated in place.
+
+    q, k [N, Hqk, K]; v [N, Hv, V] (float32 or bfloat16); g, beta fp32 [N, Hv];
+    state fp32 [R, Hv, K, V]; state_indices int32 [N] (row of state per sequence,
+    negative = skip) or None (row n).  Returns o [N, Hv, V] in o_dtype (default v's dtype).
+    """
+    torch = _torch()
+    dev = q.device
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, name, dev)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype")
+    _require(g, "g", dev, torch.float32)
+    _require(beta, "beta", dev, torch.float32)
+    _require(state, "state", dev, torch.float32)
+    _require(state_indices, "state_indices", dev, torch.int32)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or state.dim() != 4:
+        raise ValueError("q, k must be [N, Hqk, K], v [N, Hv, V], state [R, Hv, K, V]")
+    N, Hqk, K = q.shape
+    Hv, V = v.shape[1], v.shape[2]
+    if v.shape[0] != N or g.shape != (N, Hv) or beta.shape != (N, Hv) or state.shape[1:] != (Hv, K, V):
+        raise ValueError("v / g / beta / state shapes disagree with q")
+    if state_indices is not None and state_indices.shape != (N,):
+        raise ValueError("state_indices must be [N]")
+    o_dtype = v.dtype if o_dtype is None else o_dtype
+    o = torch.empty((N, Hv, V), dtype=o_dtype, device=dev)
+    st = load_library().gdn_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g), _ptr(beta), float(scale), _ptr(state),
+        _ptr(state_indices), state.shape[0], N, Hqk, Hv, K, V, _ptr(o), _dtype_code(o), _stream(dev))
+    _check("gdn_decode_step", st)
+    return o

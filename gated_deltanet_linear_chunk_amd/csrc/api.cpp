@@ -326,4 +326,38 @@ gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
                        H_v, K, V, o, o_dt, nullptr, tb, tb_bytes, stream);
 }
 
+
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v, gdn_dtype in_dt,
+                           const float* g, const float* beta, float scale, float* state,
+                           const int32_t* state_indices, int64_t n_state_rows, int32_t N,
+                           int32_t H_qk, int32_t H_v, int32_t K, int32_t V, void* o,
+                           gdn_dtype o_dt, hipStream_t stream) {
+  if (!valid_dtype(in_dt) || !valid_dtype(o_dt)) return GDN_ERR_BAD_DTYPE;
+  if (N < 0 || H_qk < 1 || H_v < 1 || K < 1 || V < 1 || n_state_rows < 0) return GDN_ERR_BAD_SHAPE;
+  if (H_v % H_qk != 0) return GDN_ERR_BAD_SHAPE;
+  if (!state_indices && n_state_rows < N) return GDN_ERR_BAD_SHAPE;
+  if ((K != 32 && K != 64 && K != 128) || V % 32 != 0 || N > 65535) return GDN_ERR_UNSUPPORTED;
+  if (N == 0) return GDN_OK;
+  if (!q || !k || !v || !g || !beta || !state || !o) return GDN_ERR_NULL_POINTER;
+  gdn::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.scale = scale;
+  a.state = state;
+  a.state_indices = state_indices;
+  a.n_state_rows = n_state_rows;
+  a.N = N;
+  a.Hqk = H_qk;
+  a.Hv = H_v;
+  a.K = K;
+  a.V = V;
+  a.in_dt = in_dt == GDN_BF16 ? 1 : 0;
+  a.o_dt = o_dt == GDN_BF16 ? 1 : 0;
+  a.o = o;
+  return hip_status(gdn::launch_decode(a, stream));
+}
+
 }  // extern "C"

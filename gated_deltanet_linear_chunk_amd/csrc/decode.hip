@@ -1,0 +1,149 @@
+// decode.hip -- the recurrent decode step: one new token per sequence.
+//
+// After a prefill hands over its final state (the sglang fork PR "Qwen3.5 cp -
+// #1" passes the final state to the standard decode path), each new token of
+// sequence n updates the K x V fp32 state of every v-head h in place:
+//   S <- e^g S;  u = beta (v - S^T k);  S <- S + k u^T;  o = scale S^T q,
+// the token recurrence itself.  Per (sequence, head) the step reads and
+// writes the whole state (K V fp32) against O(K + V) other numbers, so it is
+// bound by HBM: one pass over the state, which stays in registers between the
+// two column sums over K.
+//
+// One workgroup of 256 threads owns (sequence, v-head, 32 state columns).
+// Thread t holds columns 4 (t % 8) .. + 3 of the slice in K / 32 consecutive
+// rows (row group t / 8): one 16-byte load and one store per row, eight
+// threads covering a 128-byte row segment.  The column sums over the K rows
+// (S^T k, then S^T q of the updated state) reduce over the eight row groups
+// of a wave with lane exchanges and over the four waves through LDS.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int DT = 256;   // threads per workgroup
+constexpr int DCOLS = 32; // state columns per workgroup
+
+template <typename T>
+__device__ __forceinline__ float load_f(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_f<float>(const float* p, int64_t i) {
+  return p[i];
+}
+template <>
+__device__ __forceinline__ float load_f<uint16_t>(const uint16_t* p, int64_t i) {
+  return bf16_bits_to_f32(p[i]);
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, f32x4 x);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, f32x4 x) {
+  *reinterpret_cast<f32x4*>(p) = x;
+}
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, f32x4 x) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+}
+
+// Sum over the 32 row groups of the workgroup; every thread gets the totals of
+// its four columns.
+__device__ __forceinline__ f32x4 column_sum(f32x4 p, float (*red)[DCOLS], int wave, int lane, int c4) {
+#pragma unroll
+  for (int off = 8; off < 64; off <<= 1)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] += __shfl_xor(p[e], off, 64);
+  if (lane < 8) *reinterpret_cast<f32x4*>(&red[wave][4 * c4]) = p;
+  __syncthreads();
+  f32x4 t = *reinterpret_cast<const f32x4*>(&red[0][4 * c4]);
+#pragma unroll
+  for (int w = 1; w < DT / 64; ++w) t += *reinterpret_cast<const f32x4*>(&red[w][4 * c4]);
+  return t;
+}
+
+template <int K, typename Tin, typename Tout>
+__global__ void __launch_bounds__(DT) decode_kernel(DecodeArgs a) {
+  constexpr int RPG = K / 32;  // rows per row group
+  __shared__ __attribute__((aligned(16))) float red_k[DT / 64][DCOLS];
+  __shared__ __attribute__((aligned(16))) float red_q[DT / 64][DCOLS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c4 = tid & 7, rg = tid >> 3;
+  const int h = blockIdx.y, n = blockIdx.z;
+  const int hq = h / (a.Hv / a.Hqk);
+  const int j0 = blockIdx.x * DCOLS + 4 * c4;
+  const int64_t r = a.state_indices ? (int64_t)a.state_indices[n] : (int64_t)n;
+  Tout* o = reinterpret_cast<Tout*>(a.o) + ((int64_t)n * a.Hv + h) * a.V + j0;
+  if (r < 0 || r >= a.n_state_rows) {  // a skipped slot (uniform over the workgroup)
+    if (rg == 0) store4<Tout>(o, f32x4{0.f, 0.f, 0.f, 0.f});
+    return;
+  }
+  float* S = a.state + ((r * a.Hv + h) * K + rg * RPG) * (int64_t)a.V + j0;
+  f32x4 s[RPG];
+#pragma unroll
+  for (int i = 0; i < RPG; ++i) s[i] = *reinterpret_cast<const f32x4*>(S + (int64_t)i * a.V);
+  const Tin* kp = reinterpret_cast<const Tin*>(a.k) + ((int64_t)n * a.Hqk + hq) * K + rg * RPG;
+  const Tin* qp = reinterpret_cast<const Tin*>(a.q) + ((int64_t)n * a.Hqk + hq) * K + rg * RPG;
+  const Tin* vp = reinterpret_cast<const Tin*>(a.v) + ((int64_t)n * a.Hv + h) * a.V + j0;
+  float kv[RPG], qv[RPG];
+#pragma unroll
+  for (int i = 0; i < RPG; ++i) {
+    kv[i] = load_f<Tin>(kp, i);
+    qv[i] = load_f<Tin>(qp, i);
+  }
+  const f32x4 vv = {load_f<Tin>(vp, 0), load_f<Tin>(vp, 1), load_f<Tin>(vp, 2), load_f<Tin>(vp, 3)};
+  const float decay = expf(a.g[(int64_t)n * a.Hv + h]);
+  const float bt = a.beta[(int64_t)n * a.Hv + h];
+
+  // S <- e^g S, and this thread's rows of S^T k
+  f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < RPG; ++i) {
+    s[i] *= decay;
+    p += s[i] * kv[i];
+  }
+  const f32x4 sk = column_sum(p, red_k, wave, lane, c4);
+  const f32x4 u = bt * (vv - sk);
+  // S <- S + k u^T, written back, and this thread's rows of S^T q
+  f32x4 pq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < RPG; ++i) {
+    s[i] += kv[i] * u;
+    *reinterpret_cast<f32x4*>(S + (int64_t)i * a.V) = s[i];
+    pq += s[i] * qv[i];
+  }
+  const f32x4 sq = column_sum(pq, red_q, wave, lane, c4);
+  if (tid < 8) store4<Tout>(o, a.scale * sq);
+}
+
+template <int K>
+hipError_t launch_k(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.V / DCOLS), (unsigned)a.Hv, (unsigned)a.N);
+  if (a.in_dt == 1) {
+    if (a.o_dt == 1)
+      hipLaunchKernelGGL((decode_kernel<K, uint16_t, uint16_t>), grid, dim3(DT), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<K, uint16_t, float>), grid, dim3(DT), 0, stream, a);
+  } else {
+    if (a.o_dt == 1)
+      hipLaunchKernelGGL((decode_kernel<K, float, uint16_t>), grid, dim3(DT), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<K, float, float>), grid, dim3(DT), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  if (a.N == 0) return hipSuccess;
+  if (a.V % DCOLS != 0) return hipErrorInvalidValue;
+  switch (a.K) {
+    case 32: return launch_k<32>(a, stream);
+    case 64: return launch_k<64>(a, stream);
+    case 128: return launch_k<128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gdn

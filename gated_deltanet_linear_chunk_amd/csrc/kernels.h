@@ -84,4 +84,21 @@ hipError_t launch_compose_chains(const float* M, const float* b, const float* s0
                                  float* out, int write_before, float* final_state,
                                  hipStream_t stream);
 
+// One decode token per sequence on the fp32 state (see decode.hip).
+struct DecodeArgs {
+  const void* q;  // [N, Hqk, K] in in_dt
+  const void* k;  // [N, Hqk, K]
+  const void* v;  // [N, Hv, V]
+  const float* g;     // [N, Hv]
+  const float* beta;  // [N, Hv]
+  float scale;
+  float* state;                  // [n_state_rows, Hv, K, V], updated in place
+  const int32_t* state_indices;  // [N] row of state per sequence (< 0: skip), or null (row n)
+  int64_t n_state_rows;
+  int N, Hqk, Hv, K, V;
+  int in_dt, o_dt;  // 0 f32, 1 bf16
+  void* o;          // [N, Hv, V]
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
 }  // namespace gdn

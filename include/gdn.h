@@ -197,6 +197,27 @@ gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
                                    int32_t V, void* o, gdn_dtype o_dt, float* final_state,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Recurrent decode step: one new token for each of N sequences, on states
+ * kept by the caller (the sglang fork PR "Qwen3.5 cp - #1" hands the final
+ * state of the prefill to the standard decode path; PR body).  For sequence
+ * n and v-head h, with S = state[r, h] (K x V, fp32) and r = state_indices[n]
+ * (r = n when state_indices is NULL), the recurrence above advances one token
+ * in place:  S <- e^g S; u = beta (v - S^T k); S <- S + k u^T;
+ * o[n, h] = scale * S^T q.  A row r < 0 or >= n_state_rows skips sequence n:
+ * its o is zero and no state is touched (padding slots of a serving batch).
+ * Two sequences must not name the same row.
+ *  q, k  [N, H_qk, K] in in_dt     v [N, H_v, V] in in_dt
+ *  g,beta fp32 [N, H_v]            o [N, H_v, V] in o_dt
+ *  state fp32 [n_state_rows, H_v, K, V]; state_indices int32 [N] (device) or NULL.
+ * K in {32, 64, 128}, V % 32 == 0, N <= 65535; all arithmetic in fp32.
+ */
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v, gdn_dtype in_dt,
+                           const float* g, const float* beta, float scale, float* state,
+                           const int32_t* state_indices, int64_t n_state_rows, int32_t N,
+                           int32_t H_qk, int32_t H_v, int32_t K, int32_t V, void* o,
+                           gdn_dtype o_dt, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -148,6 +148,26 @@ def test_gate_and_segment_validation(lib):
                FAKE, ws, None) == SEQ
 
 
+def test_decode_validation(lib):
+    def dec(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, dt=1, g=FAKE, beta=FAKE, scale=1.0, state=FAKE, idx=None, rows=64, N=64,
+                 Hqk=16, Hv=32, K=128, V=128, o=FAKE, o_dt=1, stream=None)
+        a.update(kw)
+        return lib.gdn_decode_step(*a.values())
+
+    assert dec(dt=7) == DTYPE
+    assert dec(o_dt=7) == DTYPE
+    assert dec(N=-1) == SHAPE
+    assert dec(Hv=24) == SHAPE  # not a multiple of H_qk
+    assert dec(rows=63) == SHAPE  # fewer state rows than sequences, no indices
+    assert dec(K=96) == UNSUP
+    assert dec(V=100) == UNSUP
+    assert dec(N=70000, rows=70000) == UNSUP
+    assert dec(state=None) == NULLP
+    assert dec(o=None) == NULLP
+    assert dec(N=0, q=None, k=None, v=None, g=None, beta=None, state=None, o=None) == OK
+
+
 def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(4, 8)

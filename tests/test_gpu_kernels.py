@@ -302,3 +302,77 @@ def test_segmented_forward_matches_oracle(gates):
                               g[None], beta[None], initial_state=dev(s0), o_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+# --------------------------------------------------------------------------- #
+# Recurrent decode step (one new token per sequence, state updated in place)
+# --------------------------------------------------------------------------- #
+def _decode_inputs(seed, N, Hqk, Hv, K, V, dtype):
+    """N one-token samples of the usual recipe, plus N fp32 states."""
+    d = gdn_inputs.small(seed, [1] * N, Hqk, Hv, K, V, dtype, s0_std=0.5)
+    return d, d["s0"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 32), (32, 256)])
+def test_decode_step_matches_oracle(dtype, K, V):
+    N, Hqk, Hv = 40, 2, 4
+    d, s0 = _decode_inputs(41, N, Hqk, Hv, K, V, dtype)
+    g, beta = _gpu_gates(d)
+    state = dev(s0)
+    o = gdn.gdn_decode_step(dev(d["q"], dtype), dev(d["k"], dtype), dev(d["v"], dtype), g, beta, state,
+                            scale=0.75, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    og, bg = _oracle_gates(d)
+    oref, sref = oracle.decode_step(d["q"], d["k"], d["v"], og, bg, s0, scale=0.75)
+    check = assert_f32 if dtype == "f32" else assert_bf16
+    so = check(host(o), oref, "o")
+    ss = check(host(state), sref, "state")
+    print("\ndecode %s K=%d V=%d o %s state %s" % (dtype, K, V, so, ss))
+
+
+def test_decode_step_state_rows_skips_and_bf16_o():
+    """Rows picked by index; negative and out-of-range indices skip their sequence (o = 0, no
+    state row touched); bf16 o is the fp32 result rounded."""
+    N, Hqk, Hv, K, V, R = 6, 1, 2, 128, 128, 10
+    d, _ = _decode_inputs(42, N, Hqk, Hv, K, V, "bf16")
+    s0 = (np.random.default_rng(43).standard_normal((R, Hv, K, V)) * 0.5).astype(np.float32)
+    idx = np.array([7, 2, -1, 9, 0, 15], dtype=np.int32)
+    g, beta = _gpu_gates(d)
+    state = dev(s0)
+    o = gdn.gdn_decode_step(dev(d["q"], "bf16"), dev(d["k"], "bf16"), dev(d["v"], "bf16"), g, beta, state,
+                            state_indices=dev(idx, "i32"), o_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    og, bg = _oracle_gates(d)
+    ref_idx = np.where(idx < R, idx, -1)
+    oref, sref = oracle.decode_step(d["q"], d["k"], d["v"], og, bg, s0, state_indices=ref_idx)
+    got_o, got_s = host(o), host(state)
+    live = ref_idx >= 0
+    assert np.all(got_o[~live] == 0)
+    untouched = np.setdiff1d(np.arange(R), ref_idx[live])
+    np.testing.assert_array_equal(got_s[untouched], s0[untouched].astype(np.float64))
+    assert_bf16(got_s[ref_idx[live]], sref[ref_idx[live]], "state")
+    rms = np.sqrt(np.mean(oref[live] ** 2))
+    assert np.all(np.abs(got_o[live] - oref[live]) <= 2e-2 * rms + 2.0 ** -8 * np.abs(oref[live]))
+
+
+def test_decode_continues_a_chunk_prefill():
+    """gdn_chunk_fwd over packed samples hands its final states to the decode step; one more token
+    per sample then matches the oracle recurrence over the longer samples."""
+    lengths = [300, 1, 64, 129]
+    N, Hqk, Hv, K, V = len(lengths), 2, 4, 128, 128
+    full = gdn_inputs.small(44, [n + 1 for n in lengths], Hqk, Hv, K, V, "bf16")
+    cu = full["cu_seqlens"]
+    last = cu[1:] - 1
+    keep = np.setdiff1d(np.arange(cu[-1]), last)
+    pre = {key: full[key][keep] for key in ("q", "k", "v", "a", "b")}
+    pre.update(A_log=full["A_log"], dt_bias=full["dt_bias"], cu_seqlens=np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32))
+    _, fin = _run_chunk(pre, "bf16", o_dtype=torch.float32)
+    g, beta = gdn.gdn_gate_fwd(dev(full["a"][last]), dev(full["b"][last]), dev(full["A_log"]), dev(full["dt_bias"]))
+    o = gdn.gdn_decode_step(dev(full["q"][last], "bf16"), dev(full["k"][last], "bf16"), dev(full["v"][last], "bf16"),
+                            g, beta, fin, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    oref, fref = _oracle_chunk(full)
+    so = assert_bf16(host(o), oref[last], "o")
+    sf = assert_bf16(host(fin), fref, "state")
+    print("\ndecode after prefill o %s state %s" % (so, sf))
