@@ -157,6 +157,21 @@ def decode_step(q, k, v, g, beta, state, scale: float = 1.0, state_indices=None)
     return o, S_all
 
 
+def gated_rmsnorm(o, z, weight=None, eps: float = 1e-6) -> np.ndarray:
+    """The output norm gated by z that follows the chunk rule, in fp64.
+
+    The LlamaFactory PR "[v1] support GDN Ulysses cp" (Design) runs
+    "chunk_gated_delta_rule + norm" with the z component; the pages give no
+    formula, so this is the plain reading of a per-head RMS norm gated by SiLU(z):
+    over the last axis (V), y = o / sqrt(mean(o^2) + eps) * weight * z sigmoid(z).
+    o, z [..., V]; weight [V] or None (ones).
+    """
+    o, z = _f64(o), _f64(z)
+    w = np.ones(o.shape[-1]) if weight is None else _f64(weight)
+    inv = 1.0 / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    return o * inv * w * (z / (1.0 + np.exp(-z)))
+
+
 def transition(k, g, beta, t0: int, t1: int, Hqk: int, Hv: int, threads: int = 0) -> np.ndarray:
     """M [Hv, K, K] = A_{t1-1} ... A_{t0}, A_t = e^{g_t}(I - beta_t k_t k_t^T), by dense products."""
     lib = _load()

@@ -520,3 +520,42 @@ def test_generator_bf16_values_exact():
     for key in ("q", "k", "v", "x", "conv_w", "conv_bias"):
         t = torch.from_numpy(d[key])
         np.testing.assert_array_equal(t.to(torch.bfloat16).to(torch.float32).numpy(), d[key])
+
+
+# --------------------------------------------------------------------------- #
+# gated output norm
+# --------------------------------------------------------------------------- #
+def test_gated_rmsnorm_equals_torch_rms_norm_times_silu():
+    """A library routine: torch's rms_norm (float64, CPU) times its SiLU."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(51)
+    o = rng.standard_normal((7, 3, 128)) * 2.0
+    z = rng.standard_normal((7, 3, 128)) * 3.0
+    w = rng.uniform(0.5, 1.5, 128)
+    y = oracle.gated_rmsnorm(o, z, w, eps=1e-5)
+    ot, zt, wt = (torch.from_numpy(x) for x in (o, z, w))
+    ref = torch.nn.functional.rms_norm(ot, (128,), wt, 1e-5) * torch.nn.functional.silu(zt)
+    assert np.abs(y - ref.numpy()).max() <= 1e-13
+
+
+def test_gated_rmsnorm_closed_forms():
+    rng = np.random.default_rng(52)
+    o = rng.standard_normal((5, 64))
+    z = rng.standard_normal((5, 64)) * 2.0
+    # mean over V, eps inside the root: the RMS of the normalised part is sqrt(m / (m + eps))
+    eps = 0.3
+    y = oracle.gated_rmsnorm(o, np.full_like(o, 60.0), None, eps)  # silu(60) = 60 to 1e-24
+    m = np.mean(o * o, axis=-1)
+    assert np.allclose(np.sqrt(np.mean((y / 60.0) ** 2, axis=-1)), np.sqrt(m / (m + eps)), rtol=1e-12, atol=0)
+    # scale invariance without eps, odd in o
+    assert np.allclose(oracle.gated_rmsnorm(7.5 * o, z, None, 0.0), oracle.gated_rmsnorm(o, z, None, 0.0), rtol=1e-12)
+    assert np.array_equal(oracle.gated_rmsnorm(-o, z, None, 0.0), -oracle.gated_rmsnorm(o, z, None, 0.0))
+    # the gate is SiLU, not the sigmoid: silu(z) - silu(-z) = z
+    one = np.ones((1, 64)) * np.sqrt(1.0 - 1e-6)  # rms(one)^2 + eps = 1
+    gz = oracle.gated_rmsnorm(one, z[:1], None, 1e-6) / one
+    gmz = oracle.gated_rmsnorm(one, -z[:1], None, 1e-6) / one
+    assert np.allclose(gz - gmz, z[:1], rtol=0, atol=1e-12)
+    # weight scales channels one by one
+    w = np.arange(1, 65, dtype=np.float64)
+    assert np.allclose(oracle.gated_rmsnorm(o, z, w, 1e-6), oracle.gated_rmsnorm(o, z, None, 1e-6) * w, rtol=1e-14)
+
