@@ -14,8 +14,8 @@ events recorded on the stream it runs on, and set against the HBM
 roofline (its algorithmic bytes) and the bf16 MFMA peak (its algorithmic
 flops).  The fp64 CPU oracle is timed on the same workload on the host.
 Extras time the other workloads (segment-parallel long sequence, batched
-prefill, wide state, and the recurrent decode step on 256 sequences) with the
-same method.
+prefill, wide state, the recurrent decode step on 256 sequences, and the
+gated output norm on the packed workload's output) with the same method.
 """
 
 from __future__ import annotations
@@ -237,6 +237,29 @@ def build_decode(N, Hqk, Hv, K, V):
     return step, timer
 
 
+def build_gated_norm(rows, V):
+    """The gated output norm over rows of V values: fp32 o (as the chunk rule writes it), bf16 z, bf16 y."""
+    torch = _torch()
+    import gated_deltanet_linear_chunk_amd as gdn
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(77)
+    o = torch.randn((rows, V), generator=gen, device=dev, dtype=torch.float32)
+    z = torch.randn((rows, V), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    w = torch.rand((V,), generator=gen, device=dev, dtype=torch.float32) + 0.5
+    y = torch.empty((rows, V), dtype=torch.bfloat16, device=dev)
+    timer = Timer()
+
+    def step(time_kernels=False):
+        e = timer.start() if time_kernels else None
+        out = gdn.gdn_gated_rmsnorm_fwd(o, z, w, eps=1e-6, out=y)
+        if time_kernels:
+            timer.stop(e)
+        return out
+
+    return step, timer
+
+
 def timed(step, steps, warmup):
     torch = _torch()
     for _ in range(warmup):
@@ -370,6 +393,17 @@ def main():
         nbytes = decode_alg_bytes(DECODE_N, 16, 32, 128, 128)
         extras["decode_bf16_N%d_Hv32_K128[decode step]" % DECODE_N] = {
             "tokens_per_s": DECODE_N / s, "ms_per_step": s * 1e3, "main_kernel_ms": ms,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "alg_bytes": nbytes,
+        }
+        del st
+        torch.cuda.empty_cache()
+        rows = w.total_tokens * w.Hv
+        st, tm = build_gated_norm(rows, w.V)
+        s = timed(st, max(3, args.steps // 4), 2)
+        ms = tm.mean_ms()
+        nbytes = rows * w.V * (4 + 2 + 2)
+        extras["gated_norm_f32o_bf16z_T8192_Hv32_V128[norm]"] = {
+            "tokens_per_s": w.total_tokens / s, "ms_per_step": s * 1e3, "main_kernel_ms": ms,
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "alg_bytes": nbytes,
         }
         del st

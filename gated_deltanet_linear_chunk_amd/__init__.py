@@ -27,6 +27,7 @@ __all__ = [
     "gdn_chunk_fwd_workspace_bytes",
     "gdn_segment_state_scan_workspace_bytes",
     "gdn_decode_step",
+    "gdn_gated_rmsnorm_fwd",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -48,6 +49,7 @@ EXPORTED_SYMBOLS = (
     "gdn_segmented_workspace_bytes",
     "gdn_chunk_fwd_segmented",
     "gdn_decode_step",
+    "gdn_gated_rmsnorm_fwd",
 )
 
 
@@ -95,8 +97,9 @@ def load_library():
                                             i32, i32, i32, P, ctypes.c_int, P, P, sz, P]
     lib.gdn_decode_step.argtypes = [P, P, P, ctypes.c_int, P, P, f32, P, P, i64, i32, i32, i32, i32, i32, P,
                                     ctypes.c_int, P]
+    lib.gdn_gated_rmsnorm_fwd.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P, f32, i64, i32, P, ctypes.c_int, P]
     for name in ("gdn_gate_fwd", "gdn_conv1d_fwd", "gdn_chunk_fwd", "gdn_segment_state_scan",
-                 "gdn_chunk_fwd_segmented", "gdn_decode_step"):
+                 "gdn_chunk_fwd_segmented", "gdn_decode_step", "gdn_gated_rmsnorm_fwd"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -394,3 +397,32 @@ def gdn_decode_step(q, k, v, g, beta, state, scale: float = 1.0, state_indices=N
         _ptr(state_indices), state.shape[0], N, Hqk, Hv, K, V, _ptr(o), _dtype_code(o), _stream(dev))
     _check("gdn_decode_step", st)
     return o
+
+
+def gdn_gated_rmsnorm_fwd(o, z, weight=None, eps: float = 1e-6, y_dtype=None, out=None):
+    """Output norm gated by z: y = o / sqrt(mean(o^2) + eps) * weight * silu(z) over the last axis.
+
+    o, z [..., V] (float32 or bfloat16, same shape); weight fp32 [V] or None.
+    Returns y (a new tensor in y_dtype, default o's dtype, or `out`, which may be o).
+    """
+    torch = _torch()
+    dev = o.device
+    _require(o, "o", dev)
+    _require(z, "z", dev)
+    _require(weight, "weight", dev, torch.float32)
+    if z.shape != o.shape:
+        raise ValueError("z must have o's shape")
+    V = o.shape[-1]
+    if weight is not None and weight.shape != (V,):
+        raise ValueError("weight must be [V]")
+    if out is None:
+        out = torch.empty(o.shape, dtype=o.dtype if y_dtype is None else y_dtype, device=dev)
+    else:
+        _require(out, "out", dev)
+        if out.shape != o.shape:
+            raise ValueError("out must have o's shape")
+    st = load_library().gdn_gated_rmsnorm_fwd(_ptr(o), _dtype_code(o), _ptr(z), _dtype_code(z), _ptr(weight),
+                                              float(eps), o.numel() // V, V, _ptr(out), _dtype_code(out), _stream(dev))
+    _check("gdn_gated_rmsnorm_fwd", st)
+    return out
+

@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 
 SOURCES = ["api.cpp", "split_plan.cpp", "gate_conv.hip", "chunk_f32.hip", "chunk_prep.hip", "chunk_bf16.hip",
-           "compose.hip", "decode.hip"]
+           "compose.hip", "decode.hip", "gated_norm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

@@ -360,4 +360,28 @@ gdn_status gdn_decode_step(const void* q, const void* k, const void* v, gdn_dtyp
   return hip_status(gdn::launch_decode(a, stream));
 }
 
+gdn_status gdn_gated_rmsnorm_fwd(const void* o, gdn_dtype o_dt, const void* z, gdn_dtype z_dt,
+                                 const float* weight, float eps, int64_t rows, int32_t V, void* y,
+                                 gdn_dtype y_dt, hipStream_t stream) {
+  if (!valid_dtype(o_dt) || !valid_dtype(z_dt) || !valid_dtype(y_dt)) return GDN_ERR_BAD_DTYPE;
+  if (rows < 0 || V < 1 || !(eps >= 0.f)) return GDN_ERR_BAD_SHAPE;
+  if (V != 32 && V != 64 && V != 128 && V != 256 && V != 512) return GDN_ERR_UNSUPPORTED;
+  const int rpb = 256 / (V / 8);
+  if ((rows + rpb - 1) / rpb > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+  if (rows == 0) return GDN_OK;
+  if (!o || !z || !y) return GDN_ERR_NULL_POINTER;
+  gdn::GatedNormArgs a;
+  a.o = o;
+  a.z = z;
+  a.weight = weight;
+  a.eps = eps;
+  a.rows = rows;
+  a.V = V;
+  a.o_dt = o_dt == GDN_BF16 ? 1 : 0;
+  a.z_dt = z_dt == GDN_BF16 ? 1 : 0;
+  a.y_dt = y_dt == GDN_BF16 ? 1 : 0;
+  a.y = y;
+  return hip_status(gdn::launch_gated_norm(a, stream));
+}
+
 }  // extern "C"

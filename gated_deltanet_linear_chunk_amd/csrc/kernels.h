@@ -101,4 +101,17 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Output norm gated by z over rows of V values (see gated_norm.hip).
+struct GatedNormArgs {
+  const void* o;        // [rows, V] in o_dt
+  const void* z;        // [rows, V] in z_dt
+  const float* weight;  // [V] or null (ones)
+  float eps;
+  int64_t rows;
+  int V;
+  int o_dt, z_dt, y_dt;  // 0 f32, 1 bf16
+  void* y;               // [rows, V] in y_dt
+};
+hipError_t launch_gated_norm(const GatedNormArgs& a, hipStream_t stream);
+
 }  // namespace gdn

@@ -218,6 +218,21 @@ gdn_status gdn_decode_step(const void* q, const void* k, const void* v, gdn_dtyp
                            int32_t H_qk, int32_t H_v, int32_t K, int32_t V, void* o,
                            gdn_dtype o_dt, hipStream_t stream);
 
+/*
+ * Output norm gated by z, the step after the chunk rule ("chunk_gated_delta_rule
+ * + norm" with the z component: LlamaFactory PR "[v1] support GDN Ulysses cp",
+ * Design; the pages give no formula, this is a per-head RMS norm gated by
+ * SiLU(z)).  For every row r (one token of one v-head) of V values:
+ *   y[r] = o[r] / sqrt(mean(o[r]^2) + eps) * weight * z[r] sigmoid(z[r]).
+ *  o [rows, V] in o_dt, z [rows, V] in z_dt, weight fp32 [V] or NULL (ones),
+ *  y [rows, V] in y_dt (may be o when both dtypes and shapes agree: each row is
+ *  read before it is written by the same threads).
+ * V in {32, 64, 128, 256, 512}; eps >= 0; fp32 arithmetic.
+ */
+gdn_status gdn_gated_rmsnorm_fwd(const void* o, gdn_dtype o_dt, const void* z, gdn_dtype z_dt,
+                                 const float* weight, float eps, int64_t rows, int32_t V, void* y,
+                                 gdn_dtype y_dt, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -168,6 +168,22 @@ def test_decode_validation(lib):
     assert dec(N=0, q=None, k=None, v=None, g=None, beta=None, state=None, o=None) == OK
 
 
+def test_gated_norm_validation(lib):
+    def gn(**kw):
+        a = dict(o=FAKE, o_dt=0, z=FAKE, z_dt=1, w=None, eps=1e-6, rows=100, V=128, y=FAKE, y_dt=1, stream=None)
+        a.update(kw)
+        return lib.gdn_gated_rmsnorm_fwd(*a.values())
+
+    assert gn(o_dt=9) == DTYPE
+    assert gn(y_dt=9) == DTYPE
+    assert gn(rows=-1) == SHAPE
+    assert gn(eps=-1.0) == SHAPE
+    assert gn(eps=float("nan")) == SHAPE
+    assert gn(V=96) == UNSUP
+    assert gn(z=None) == NULLP
+    assert gn(rows=0, o=None, z=None, y=None) == OK
+
+
 def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(4, 8)

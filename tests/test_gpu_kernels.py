@@ -376,3 +376,55 @@ def test_decode_continues_a_chunk_prefill():
     so = assert_bf16(host(o), oref[last], "o")
     sf = assert_bf16(host(fin), fref, "state")
     print("\ndecode after prefill o %s state %s" % (so, sf))
+
+
+# --------------------------------------------------------------------------- #
+# Output norm gated by z
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("o_dt,z_dt", [("f32", "bf16"), ("bf16", "bf16"), ("f32", "f32")])
+@pytest.mark.parametrize("V", [32, 128, 256])
+def test_gated_norm_matches_oracle(o_dt, z_dt, V):
+    rng = np.random.default_rng(61)
+    rows = 1003  # not a multiple of any rows-per-workgroup count
+    o = (rng.standard_normal((rows, V)) * 0.3).astype(np.float32)
+    z = (rng.standard_normal((rows, V)) * 2.0).astype(np.float32)
+    w = rng.uniform(0.5, 1.5, V).astype(np.float32)
+    if o_dt == "bf16":
+        o = oracle.round_bf16(o).astype(np.float32)
+    if z_dt == "bf16":
+        z = oracle.round_bf16(z).astype(np.float32)
+    y = gdn.gdn_gated_rmsnorm_fwd(dev(o, o_dt), dev(z, z_dt), dev(w), eps=1e-5, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.gated_rmsnorm(o, z, w, 1e-5)
+    s = assert_f32(host(y), ref, "y")
+    print("\ngated norm o %s z %s V=%d %s" % (o_dt, z_dt, V, s))
+
+
+def test_gated_norm_bf16_in_place_and_without_weight():
+    """bf16 y written over o (each row is read before it is written), no weight: the fp32 result rounded."""
+    rng = np.random.default_rng(62)
+    rows, V = 4099, 128
+    o = oracle.round_bf16(rng.standard_normal((rows, V))).astype(np.float32)
+    z = oracle.round_bf16(rng.standard_normal((rows, V)) * 2.0).astype(np.float32)
+    ot = dev(o, "bf16")
+    y = gdn.gdn_gated_rmsnorm_fwd(ot, dev(z, "bf16"), None, eps=1e-6, out=ot)
+    torch.cuda.synchronize()
+    assert y.data_ptr() == ot.data_ptr()
+    ref = oracle.gated_rmsnorm(o, z, None, 1e-6)
+    got = host(y)
+    assert np.all(np.abs(got - ref) <= 1e-5 + 2.0 ** -8 * np.abs(ref))
+
+
+def test_gated_norm_after_the_chunk_rule():
+    """gdn_chunk_fwd's o (fp32, [T, H_v, V]) through the norm matches the oracle recurrence's o normed."""
+    d = gdn_inputs.small(63, [200, 57, 130], 2, 4, 128, 128, "bf16")
+    o, _ = _run_chunk(d, "bf16", o_dtype=torch.float32)
+    z = (np.random.default_rng(64).standard_normal(o.shape) * 2.0).astype(np.float32)
+    z = oracle.round_bf16(z).astype(np.float32)
+    w = np.random.default_rng(65).uniform(0.5, 1.5, 128).astype(np.float32)
+    y = gdn.gdn_gated_rmsnorm_fwd(o, dev(z, "bf16"), dev(w), eps=1e-6, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    oref, _ = _oracle_chunk(d)
+    ref = oracle.gated_rmsnorm(oref, z, w, 1e-6)
+    s = assert_bf16(host(y), ref, "y")
+    print("\nnorm after chunk %s" % (s,))
