@@ -62,9 +62,9 @@ hipError_t launch_gate(const float* a, const float* b, const float* A_log, const
 // ----------------------------------------------------------------------------
 constexpr int CONV_THREADS = 256;
 constexpr int CONV_CH_PER_THREAD = 8;
-constexpr int CONV_QCAP = 256;  // queued doubtful roundings per wave
+constexpr int CONV_QCAP = 512;  // queued doubtful roundings per wave
 #ifndef GDN_CONV_BLOCKS
-#define GDN_CONV_BLOCKS 1024  // blocks per launch the token runs are sized for
+#define GDN_CONV_BLOCKS 512  // blocks per launch the token runs are sized for (2 per CU)
 #endif
 
 template <typename T>
@@ -545,12 +545,12 @@ hipError_t launch_conv1d(const void* x, const void* w, const void* bias, int dt,
     p.c_end = split && part == 0 ? l2_channels : C;
     if (p.c_end <= p.c_begin) continue;
     const int cblocks = (p.c_end - p.c_begin + per_block - 1) / per_block;
-    // runs of 2-4 sub-tiles per block, aiming at about GDN_CONV_BLOCKS blocks;
-    // a run of 4 bf16 sub-tiles gives a wave 16K values, about 140 of which
+    // runs of 2-8 sub-tiles per block, aiming at about GDN_CONV_BLOCKS blocks;
+    // a run of 8 bf16 sub-tiles gives a wave 32K values, about 120 of which
     // (well below CONV_QCAP) are queued for fp64 on data like the layer's
     const int64_t subs = (Ttot + sub - 1) / sub;
     int64_t per = (subs * cblocks + GDN_CONV_BLOCKS - 1) / GDN_CONV_BLOCKS;
-    per = per < 2 ? 2 : (per > 4 ? 4 : per);
+    per = per < 2 ? 2 : (per > 8 ? 8 : per);
     const int64_t per_min = (subs + 65534) / 65535;  // grid y stays within 65535
     if (per < per_min) per = per_min;
     p.tile_tokens = (int)(per * sub);
