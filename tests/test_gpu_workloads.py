@@ -158,3 +158,26 @@ def test_tiny_fp32_workload_full():
     oref, fref = oracle.recurrence(d["q"], d["k"], d["v"], go, bo)
     assert_f32(host(o[0]), oref, "o")
     assert_f32(host(fin), fref, "final")
+
+
+def test_conv1d_packed_workload_rounding_is_exact():
+    """The conv of the packed workload (8192 tokens x 8192 channels, q/k L2-normalised) in the launch
+    configuration the benchmark times: every v channel equals the oracle's fp64 conv + SiLU rounded
+    once to bf16, over all 33.5 M values; sampled q/k tokens match the normalised oracle."""
+    w = gdn_inputs.WORKLOADS["packed_varlen_bf16_T8192_N8_Hv32_K128"]
+    d = gdn_inputs.draw(w, with_qkv=False)
+    l2ch = 2 * w.Hqk * w.K
+    y = gdn.gdn_conv1d_fwd(dev(d["x"], "bf16"), dev(d["conv_w"], "bf16"), dev(d["conv_bias"], "bf16"),
+                           cu_seqlens=dev(d["cu_seqlens"], "i32"), cu_seqlens_host=d["cu_seqlens"],
+                           l2norm_channels=l2ch, head_dim=w.K)
+    torch.cuda.synchronize()
+    got = host(y)
+    cu = d["cu_seqlens"]
+    ref_v = oracle.conv1d(d["x"][:, l2ch:], d["conv_w"][l2ch:], d["conv_bias"][l2ch:], cu)
+    mism = int(np.count_nonzero(got[:, l2ch:] != oracle.round_bf16(ref_v)))
+    assert mism == 0, "%d of %d v values differ from the correctly rounded result" % (mism, ref_v.size)
+    rows = np.random.default_rng(71).choice(w.total_tokens, 256, replace=False)
+    qk = oracle.conv1d(d["x"][:, :l2ch], d["conv_w"][:l2ch], d["conv_bias"][:l2ch], cu)[rows]
+    qk = oracle.l2norm(qk.reshape(len(rows), -1, w.K)).reshape(len(rows), -1)
+    err = np.abs(got[rows, :l2ch] - qk)
+    assert np.all(err <= 2.0 ** -8 * np.abs(qk) + 1e-5), float(err.max())
