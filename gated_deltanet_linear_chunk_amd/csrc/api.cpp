@@ -35,9 +35,11 @@ bool offsets_ok(const int32_t* cu, int32_t n, int64_t first_max, int64_t last, b
 }
 
 // Token stride: 0 selects the dense value; otherwise a multiple of 8, >= dense.
+// Below 2^24 elements, so that the kernels form a lane's offset inside a
+// 64-token chunk with one 24-bit multiply.
 bool stride_ok(int64_t* stride, int64_t dense) {
   if (*stride == 0) *stride = dense;
-  return *stride >= dense && *stride % 8 == 0;
+  return *stride >= dense && *stride % 8 == 0 && *stride < (int64_t(1) << 24);
 }
 
 // Which chunk kernel serves (in_dt, K, V); GDN_OK when one does.

@@ -23,7 +23,11 @@
 // against V - e^G K S, P against U, the decayed U against K.
 //
 // LDS (bf16 unless noted; row pitches padded by 16 B, which keeps the MFMA
-// fragment reads free of bank conflicts):
+// fragment reads free of bank conflicts).  The tiles read as MFMA operands
+// (Q, K, K^T, T diag(beta), P) store each 32-wide block of their K index in
+// fragment order: index 16 h + 4 g + j sits at 8 g + 4 h + j, so the eight
+// values a lane feeds one MFMA are contiguous and come in one 16-byte read
+// (two 8-byte reads 32 bytes apart run at about half the LDS rate):
 //   sQ [64][136], sK [64][136], sKt [128][72] (K^T), sVt [128][72] (V^T of
 //   this slice), sP [2][64][72] (hi, lo), sT2 [2][64][72] (T diag(beta)
 //   hi/lo), sO fp32 [64][132], gamma[64], dec[64] fp32.
@@ -82,6 +86,25 @@ __device__ __forceinline__ void zero4(f32x4& x) { x[0] = x[1] = x[2] = x[3] = 0.
 __device__ __forceinline__ void tile_ij(int t, int& i, int& j) {
   i = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
   j = t - (i * (i + 1)) / 2;
+}
+
+// Position of K index c inside its 32-wide block in the fragment order
+// (c = 16 h + 4 g + j -> 8 g + 4 h + j); groups of four stay together.
+__device__ __forceinline__ int frag_pos(int c) {
+  return (c & ~31) + 8 * ((c >> 2) & 3) + 4 * ((c >> 4) & 1) + (c & 3);
+}
+
+// A or B fragment of k-step k0 (a multiple of 32) for row `row` of a tile in
+// fragment order: one 16-byte read.
+__device__ __forceinline__ bf16x8 frag16(const uint16_t* base, int pitch, int row, int k0, int g4) {
+  return *reinterpret_cast<const bf16x8*>(base + row * pitch + k0 + 8 * g4);
+}
+
+// Eight consecutive K indices c .. c + 7 (c a multiple of 8) as two 8-byte
+// stores in fragment order.
+__device__ __forceinline__ void store8_frag(uint16_t* row_base, int c, const u32x4& v) {
+  *reinterpret_cast<u32x2*>(row_base + frag_pos(c)) = u32x2{v[0], v[1]};
+  *reinterpret_cast<u32x2*>(row_base + frag_pos(c + 4)) = u32x2{v[2], v[3]};
 }
 
 template <int kMode, int NW>
@@ -155,15 +178,18 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   // waves and meet in the caches.
   const int r0_pf = 2 * (tid & 31), d8_pf = (tid >> 5) * 8;
   constexpr int kDJ = (NT / 32) * 8;  // column step between a thread's units
-  // base pointers at the sequence start; the prefetch adds the token offset
-  // t0 - bos + row, with row clamped to the chunk's last valid token
-  const uint16_t* kbase = (const uint16_t*)a.k + bos * a.k_stride + hq * KD + d8_pf;
-  const uint16_t* qbase = kOut ? (const uint16_t*)a.q + bos * a.q_stride + hq * KD + d8_pf : kbase;
+  // Uniform base pointers at the sequence start.  Per chunk the prefetch moves
+  // them to the chunk's first token (scalar arithmetic) and adds a lane's
+  // 32-bit byte offset, row * stride + column, with row clamped to the chunk's
+  // last valid token; the host keeps strides below 2^24 elements, so the
+  // row * stride product is one 24-bit multiply.
+  const char* kbase = (const char*)((const uint16_t*)a.k + bos * a.k_stride + hq * KD);
+  const char* qbase = kOut ? (const char*)((const uint16_t*)a.q + bos * a.q_stride + hq * KD) : kbase;
   const int64_t q_stride = kOut ? a.q_stride : a.k_stride;
   // without values (M columns) the v loads re-read k and are discarded
-  const uint16_t* vbase =
-      load_v ? (const uint16_t*)a.v + bos * a.v_stride + (int64_t)h * a.V + v0 + d8_pf : kbase;
+  const char* vbase = load_v ? (const char*)((const uint16_t*)a.v + bos * a.v_stride + (int64_t)h * a.V + v0) : kbase;
   const int64_t v_stride = load_v ? a.v_stride : a.k_stride;
+  const uint32_t ks32 = (uint32_t)a.k_stride, qs32 = (uint32_t)q_stride, vs32 = (uint32_t)v_stride;
   const unsigned char* rbase = (const unsigned char*)a.tbuf + (int64_t)h * PREP_RECORD_BYTES;
   const int64_t rslot_stride = (int64_t)a.Hv * PREP_RECORD_BYTES;
 
@@ -200,8 +226,11 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
 #define GDN_PF_ROWS(T0)                                                                        \
   const int64_t rel_ = (T0) - bos;                                                            \
   const int L_ = (int)((eos - (T0)) < CH ? (eos - (T0)) : CH);                                \
-  const int64_t row0_ = rel_ + (r0_pf < L_ ? r0_pf : L_ - 1);                                 \
-  const int64_t row1_ = rel_ + (r0_pf + 1 < L_ ? r0_pf + 1 : L_ - 1);
+  const uint32_t row0_ = (uint32_t)(r0_pf < L_ ? r0_pf : L_ - 1);                             \
+  const uint32_t row1_ = (uint32_t)(r0_pf + 1 < L_ ? r0_pf + 1 : L_ - 1);
+// one 16-byte load at uniform base B (chunk start) + lane byte offset
+#define GDN_LD16(B, ROW, S32, COL) \
+  (*reinterpret_cast<const u32x4*>((B) + (uint32_t)(2u * (__umul24((ROW), (S32)) + (uint32_t)(COL)))))
 #define GDN_PF_REC(T0)                                                                         \
   do {                                                                                        \
     const unsigned char* rs_ = rbase + (((T0) >> 6) + seq) * rslot_stride;                    \
@@ -211,19 +240,22 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
 #define GDN_PF_KQ(T0)                                                                          \
   do {                                                                                        \
     GDN_PF_ROWS(T0)                                                                           \
+    const char* kc_ = kbase + 2 * rel_ * a.k_stride;                                          \
+    const char* qc_ = qbase + 2 * rel_ * q_stride;                                            \
     _Pragma("unroll") for (int j_ = 0; j_ < NPAIR; ++j_) {                                     \
-      pk[j_][0] = *reinterpret_cast<const u32x4*>(kbase + row0_ * a.k_stride + kDJ * j_);     \
-      pk[j_][1] = *reinterpret_cast<const u32x4*>(kbase + row1_ * a.k_stride + kDJ * j_);     \
-      pq[j_][0] = *reinterpret_cast<const u32x4*>(qbase + row0_ * q_stride + kDJ * j_);       \
-      pq[j_][1] = *reinterpret_cast<const u32x4*>(qbase + row1_ * q_stride + kDJ * j_);       \
+      pk[j_][0] = GDN_LD16(kc_, row0_, ks32, d8_pf + kDJ * j_);                                \
+      pk[j_][1] = GDN_LD16(kc_, row1_, ks32, d8_pf + kDJ * j_);                                \
+      pq[j_][0] = GDN_LD16(qc_, row0_, qs32, d8_pf + kDJ * j_);                                \
+      pq[j_][1] = GDN_LD16(qc_, row1_, qs32, d8_pf + kDJ * j_);                                \
     }                                                                                         \
   } while (0)
 #define GDN_PF_V(T0)                                                                           \
   do {                                                                                        \
     GDN_PF_ROWS(T0)                                                                           \
+    const char* vc_ = vbase + 2 * rel_ * v_stride;                                            \
     _Pragma("unroll") for (int j_ = 0; j_ < NPAIR; ++j_) {                                     \
-      pv[j_][0] = *reinterpret_cast<const u32x4*>(vbase + row0_ * v_stride + kDJ * j_);       \
-      pv[j_][1] = *reinterpret_cast<const u32x4*>(vbase + row1_ * v_stride + kDJ * j_);       \
+      pv[j_][0] = GDN_LD16(vc_, row0_, vs32, d8_pf + kDJ * j_);                                \
+      pv[j_][1] = GDN_LD16(vc_, row1_, vs32, d8_pf + kDJ * j_);                                \
     }                                                                                         \
   } while (0)
 #define GDN_PREFETCH(T0) do { GDN_PF_REC(T0); GDN_PF_KQ(T0); GDN_PF_V(T0); } while (0)
@@ -241,17 +273,17 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
       const bool ok0 = r0 < L, ok1 = r0 + 1 < L;
       const u32x4 k0 = ok0 ? pk[j][0] : z, k1 = ok1 ? pk[j][1] : z;
       const u32x4 v0v = (load_v && ok0) ? pv[j][0] : z, v1v = (load_v && ok1) ? pv[j][1] : z;
-      *reinterpret_cast<u32x4*>(sK + r0 * QP + d8) = k0;
-      *reinterpret_cast<u32x4*>(sK + (r0 + 1) * QP + d8) = k1;
+      store8_frag(sK + r0 * QP, d8, k0);
+      store8_frag(sK + (r0 + 1) * QP, d8, k1);
       if (kOut) {
-        *reinterpret_cast<u32x4*>(sQ + r0 * QP + d8) = ok0 ? pq[j][0] : z;
-        *reinterpret_cast<u32x4*>(sQ + (r0 + 1) * QP + d8) = ok1 ? pq[j][1] : z;
+        store8_frag(sQ + r0 * QP, d8, ok0 ? pq[j][0] : z);
+        store8_frag(sQ + (r0 + 1) * QP, d8, ok1 ? pq[j][1] : z);
       }
 #pragma unroll
       for (int jx = 0; jx < 4; ++jx) {
         const int d0 = d8 + 2 * jx, d1 = d0 + 1;
-        *reinterpret_cast<uint32_t*>(sKt + d0 * TP + r0) = (k0[jx] & 0xFFFFu) | (k1[jx] << 16);
-        *reinterpret_cast<uint32_t*>(sKt + d1 * TP + r0) = (k0[jx] >> 16) | (k1[jx] & 0xFFFF0000u);
+        *reinterpret_cast<uint32_t*>(sKt + d0 * TP + frag_pos(r0)) = (k0[jx] & 0xFFFFu) | (k1[jx] << 16);
+        *reinterpret_cast<uint32_t*>(sKt + d1 * TP + frag_pos(r0)) = (k0[jx] >> 16) | (k1[jx] & 0xFFFF0000u);
         if (load_v) {
           *reinterpret_cast<uint32_t*>(sVt + d0 * TP + r0) = (v0v[jx] & 0xFFFFu) | (v1v[jx] << 16);
           *reinterpret_cast<uint32_t*>(sVt + d1 * TP + r0) = (v0v[jx] >> 16) | (v1v[jx] & 0xFFFF0000u);
@@ -265,20 +297,25 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
 #pragma unroll
       for (int u = 0; u < NREC; ++u) {
         const int f = min(tid + u * NT, RUNITS - 1);
-        unsigned char* dst;
+        unsigned char *dst0, *dst1;  // the unit's two 8-byte halves
         if (f < REC_TB_UNITS || f >= REC_STATE_UNITS) {
-          // T diag(beta) hi, lo -> sT2; P hi, lo -> sP (two matrices each)
+          // T diag(beta) hi, lo -> sT2; P hi, lo -> sP (two matrices each),
+          // columns c .. c + 7 of row r, in fragment order
           const int fm = f < REC_TB_UNITS ? f : f - REC_STATE_UNITS;
           const int mat = fm / 320, rem = fm - 320 * mat;
           int bi, bj;
           tile_ij(rem >> 5, bi, bj);
           const int r = 16 * bi + ((rem >> 1) & 15), c = 16 * bj + 8 * (rem & 1);
-          dst = smem + (f < REC_TB_UNITS ? OFF_T2 : OFF_P) + 2 * (mat * CH * TP + r * TP + c);
+          unsigned char* row = smem + (f < REC_TB_UNITS ? OFF_T2 : OFF_P) + 2 * (mat * CH * TP + r * TP);
+          dst0 = row + 2 * frag_pos(c);
+          dst1 = row + 2 * frag_pos(c + 4);
         } else {
           const int g = f - REC_TB_UNITS;  // 0..15 gamma, 16..31 dec
-          dst = smem + OFF_GAM + 16 * g;
+          dst0 = smem + OFF_GAM + 16 * g;
+          dst1 = dst0 + 8;
         }
-        *reinterpret_cast<u32x4*>(dst) = pr[u];
+        *reinterpret_cast<u32x2*>(dst0) = u32x2{pr[u][0], pr[u][1]};
+        *reinterpret_cast<u32x2*>(dst1) = u32x2{pr[u][2], pr[u][3]};
       }
     }
     // ---- fetch the next chunk while this one computes -----------------------
@@ -304,8 +341,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
       bf16x8 fk[4], fq[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        fk[rt] = lds_frag(sK, QP, 16 * rt + c16, 32 * m, g4);
-        if (kOut) fq[rt] = lds_frag(sQ, QP, 16 * rt + c16, 32 * m, g4);
+        fk[rt] = frag16(sK, QP, 16 * rt + c16, 32 * m, g4);
+        if (kOut) fq[rt] = frag16(sQ, QP, 16 * rt + c16, 32 * m, g4);
       }
 #pragma unroll
       for (int part = 0; part < 2; ++part)
@@ -356,8 +393,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
         bf16x8 th[4], tl[4];
 #pragma unroll
         for (int rt = 2 * m; rt < 4; ++rt) {
-          th[rt] = lds_frag(sT2, TP, 16 * rt + c16, 32 * m, g4);
-          tl[rt] = lds_frag(sT2 + CH * TP, TP, 16 * rt + c16, 32 * m, g4);
+          th[rt] = frag16(sT2, TP, 16 * rt + c16, 32 * m, g4);
+          tl[rt] = frag16(sT2 + CH * TP, TP, 16 * rt + c16, 32 * m, g4);
         }
 #pragma unroll
         for (int part = 0; part < 3; ++part)
@@ -396,8 +433,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
         bf16x8 ph[4], pl[4];
 #pragma unroll
         for (int rt = 2 * m; rt < 4; ++rt) {
-          ph[rt] = lds_frag(sP, TP, 16 * rt + c16, 32 * m, g4);
-          pl[rt] = lds_frag(sP + CH * TP, TP, 16 * rt + c16, 32 * m, g4);
+          ph[rt] = frag16(sP, TP, 16 * rt + c16, 32 * m, g4);
+          pl[rt] = frag16(sP + CH * TP, TP, 16 * rt + c16, 32 * m, g4);
         }
 #pragma unroll
         for (int part = 0; part < 3; ++part)
@@ -442,7 +479,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
         for (int half = 0; half < 2; ++half) {
           bf16x8 fk[4];
 #pragma unroll
-          for (int x = 0; x < 4; ++x) fk[x] = lds_frag(sKt, TP, 16 * (4 * half + x) + c16, 32 * m, g4);
+          for (int x = 0; x < 4; ++x) fk[x] = frag16(sKt, TP, 16 * (4 * half + x) + c16, 32 * m, g4);
 #pragma unroll
           for (int part = 0; part < 2; ++part)
 #pragma unroll
@@ -469,6 +506,10 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
       // instead, so that every store is unconditional and the memory counter
       // waits further on stay exact.
       constexpr int RUNS = CPW / 8;  // 8-column runs per row
+      // uniform element offset of (chunk start, head, slice) plus a lane's
+      // 32-bit offset r * Hv * V + c (Hv * V is below 2^24: it bounds v's stride)
+      const int64_t obase = (t0 * a.Hv + h) * (int64_t)a.V + v0;
+      const uint32_t tok32 = (uint32_t)(a.Hv * a.V);
 #pragma unroll
       for (int i = 0; i < CH * RUNS / 64; ++i) {
         const int u = lane + 64 * i;
@@ -477,16 +518,16 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
         const float4 x0 = *reinterpret_cast<const float4*>(src);
         const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
         {
-          const int64_t off = ((t0 + r) * a.Hv + h) * (int64_t)a.V + v0 + c;
+          const uint32_t lo = __umul24((uint32_t)r, tok32) + (uint32_t)c;
           if (kMode == kOutBF16) {
             uint4 w;
             w.x = pack_bf16x2(a.scale * x0.x, a.scale * x0.y);
             w.y = pack_bf16x2(a.scale * x0.z, a.scale * x0.w);
             w.z = pack_bf16x2(a.scale * x1.x, a.scale * x1.y);
             w.w = pack_bf16x2(a.scale * x1.z, a.scale * x1.w);
-            *reinterpret_cast<uint4*>((uint16_t*)a.o + off) = w;
+            *reinterpret_cast<uint4*>((char*)((uint16_t*)a.o + obase) + 2u * lo) = w;
           } else {
-            float* dst = (float*)a.o + off;
+            float* dst = (float*)((char*)((float*)a.o + obase) + 4u * lo);
             *reinterpret_cast<float4*>(dst) =
                 make_float4(a.scale * x0.x, a.scale * x0.y, a.scale * x0.z, a.scale * x0.w);
             *reinterpret_cast<float4*>(dst + 4) =
@@ -502,6 +543,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
 #undef GDN_PF_REC
 #undef GDN_PF_KQ
 #undef GDN_PF_V
+#undef GDN_LD16
   // ---- final state ----------------------------------------------------------
   float* dst = nullptr;
   int64_t row_stride = 0;

@@ -114,7 +114,8 @@ gdn_status gdn_conv1d_fwd(const void* x, const void* w, const void* bias, gdn_dt
  *  *_token_stride: elements between consecutive tokens of q, k, v (0 = dense:
  *  H_qk*K, H_qk*K, H_v*V).  A larger stride reads q, k, v straight out of a
  *  wider token-major buffer, e.g. the conv1d output [T, q|k|v channels];
- *  strides must be multiples of 8 and at least the dense size.  The B
+ *  strides must be multiples of 8, at least the dense size and below 2^24
+ *  elements (GDN_ERR_BAD_SHAPE otherwise).  The B
  *  batch rows are then B*T tokens at that stride.
  * Kernels: in_dt = BF16 runs bf16 MFMA tiles with fp32 accumulation, an fp32
  * state, and split-bf16 operands where fp32 intermediates meet the matrix
