@@ -67,6 +67,11 @@ def test_chunk_validation(lib):
     assert _chunk(lib, qs=100) == SHAPE  # below the dense 16 * 128
     assert _chunk(lib, vs=32 * 128 + 4) == SHAPE  # not a multiple of 8
     assert _chunk(lib, ks=8192, qs=8192, vs=8192, q=None) == NULLP  # a wide stride itself is fine
+    big = (1 << 24) - 8  # largest stride accepted: the kernels form in-chunk offsets with 24-bit multiplies
+    assert _chunk(lib, ks=big, qs=big, vs=big, q=None) == NULLP
+    assert _chunk(lib, ks=1 << 24) == SHAPE
+    assert _chunk(lib, qs=1 << 24) == SHAPE
+    assert _chunk(lib, vs=1 << 24) == SHAPE
     assert _chunk(lib, Hqk=3) == SHAPE  # 32 % 3 != 0
     assert _chunk(lib, K=64) == UNSUP  # bf16 kernel needs K = 128
     assert _chunk(lib, V=96) == UNSUP
@@ -125,6 +130,7 @@ def test_gate_and_segment_validation(lib):
 
     assert scan(off=None) == NULLP
     assert scan(ks=12) == SHAPE
+    assert scan(vs=1 << 24) == SHAPE
     assert scan(M=None) == NULLP
     assert scan(ws=None) == NULLP
     assert scan(ws_bytes=lib.gdn_segment_state_scan_workspace_bytes(4096, 8, 32, 128, 128) - 4) == SHAPE
