@@ -71,9 +71,24 @@ static_assert(REC_TB_UNITS * 16 == PREP_REC_GAM && REC_STATE_UNITS * 16 == PREP_
 enum { kOutF32 = 0, kOutBF16 = 1, kPass1 = 2 };
 
 struct Pass1 {
-  int m_tiles;   // leading blockIdx.x values that evolve M columns (v = 0, S0 = I)
+  int m_tiles;   // leading tiles of a (segment, head) that evolve M columns (v = 0, S0 = I)
   float* m_out;  // [n_seqs, Hv, K, K]
 };
+
+// Workgroups go to the eight XCDs in turn by id, each XCD with its own L2.
+// The grid is 1-D over logical blocks (tile fastest, then v-head, then
+// sequence); a group of `group` consecutive logical blocks reads the same q/k
+// (the v-heads of one q/k head with all their tiles) and, within a head, the
+// same records.  When the groups split evenly over the XCDs, physical id L
+// runs member (L / 8) % group of group (L % 8) + 8 (L / 8 / group), so every
+// member of a group has the same L % 8 (one XCD, one L2 copy of its inputs)
+// and groups still start in logical order, eight at a time.
+__device__ __forceinline__ int xcd_grouped(int L, int n, int group) {
+  const int groups = n / group;
+  if (n % group != 0 || groups % 8 != 0) return L;
+  const int x = L & 7, j = L >> 3;
+  return (x + 8 * (j / group)) * group + j % group;
+}
 
 __device__ __forceinline__ void zero4(f32x4& x) { x[0] = x[1] = x[2] = x[3] = 0.f; }
 
@@ -136,14 +151,16 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   const int c16 = lane & 15;
 
   bool m_mode = false;
-  int tile = blockIdx.x;
+  const int n_tiles = a.n_tiles;
+  const int lb = xcd_grouped((int)blockIdx.x, (int)gridDim.x, n_tiles * (a.Hv / a.Hqk));
+  int tile = lb % n_tiles;
   if (kMode == kPass1) {
     m_mode = tile < p1.m_tiles;
     if (!m_mode) tile -= p1.m_tiles;
   }
   const int v0 = tile * BV;
-  const int h = blockIdx.y;
-  const int zb = blockIdx.z;
+  const int h = (lb / n_tiles) % a.Hv;
+  const int zb = lb / (n_tiles * a.Hv);
   const int seq = a.seq_order ? a.seq_order[zb] : zb;
   const int hq = h / (a.Hv / a.Hqk);
   int64_t bos, eos;
@@ -573,8 +590,13 @@ hipError_t launch_scan(const ChunkArgs& a, Pass1 p1, dim3 grid, hipStream_t stre
   const void* fn = (const void*)chunk_scan_kernel<kMode, kScanWaves>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((chunk_scan_kernel<kMode, kScanWaves>), grid, dim3(kScanWaves * 64), LDS_BYTES, stream,
-                     a, p1);
+  // 1-D launch over (tile, v-head, sequence); the kernel decodes it
+  ChunkArgs c = a;
+  c.n_tiles = (int)grid.x;
+  const int64_t n = (int64_t)grid.x * grid.y * grid.z;
+  if (n > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((chunk_scan_kernel<kMode, kScanWaves>), dim3((unsigned)n), dim3(kScanWaves * 64), LDS_BYTES,
+                     stream, c, p1);
   return hipGetLastError();
 }
 

@@ -8,7 +8,8 @@
 // 128 x 128 by 128 x 16 product M_i S on the fp32 matrix cores
 // (v_mfma_f32_16x16x4_f32, fp32 products and sums): wave w of the workgroup owns
 // row tiles 2w and 2w + 1, reads its rows of M_i straight from global memory
-// (16-byte loads, all in flight at once) and the state slice from LDS.  The k
+// (16-byte loads, all in flight at once, issued one step ahead) and the state
+// slice from LDS.  The k
 // order of the sums is free, so lane group g (lanes 16g .. 16g + 15) takes
 // k = 32 g + s at step s, which makes its M reads contiguous.  Segments follow
 // one another inside the workgroup, which needs only the M S products (a tree
@@ -45,43 +46,69 @@ __global__ void __launch_bounds__(CTHREADS) compose_kernel(const float* __restri
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;  // lane group, column within the slice
-  const int c0 = blockIdx.x * CT;
-  const int h = blockIdx.y;
-  const int ci = blockIdx.z;
+  // 1-D grid over (slice, unit = chain * Hv + head).  Workgroups go to the
+  // eight XCDs in turn by id, and every slice of a unit reads all of its M, so
+  // when the units split evenly the slices of a unit get ids eight apart (one
+  // XCD, one L2 copy of M); otherwise slices of a unit are consecutive.
+  const int n_slices = V / CT, n_units = (int)(gridDim.x / n_slices);
+  int slice, unit;
+  if (n_units % 8 == 0) {
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    unit = x + 8 * (j / n_slices);
+    slice = j % n_slices;
+  } else {
+    slice = blockIdx.x % n_slices;
+    unit = blockIdx.x / n_slices;
+  }
+  const int c0 = slice * CT;
+  const int h = unit % Hv;
+  const int ci = unit / Hv;
   const Chain ch = chains ? Chain{chains[4 * ci], chains[4 * ci + 1], chains[4 * ci + 2], chains[4 * ci + 3]}
                           : single;
 
   const int64_t head = (int64_t)h * CK * V;
   const int64_t row = (int64_t)Hv * CK * V;  // one [Hv, K, V] state
-  for (int i = tid; i < CK * CT; i += CTHREADS) {
-    const int r = i / CT, cc = i % CT;
-    sS[0][sidx(r, cc)] = (s0 && ch.n >= 0) ? s0[ch.n * row + head + (int64_t)r * V + c0 + cc] : 0.f;
-  }
-  __syncthreads();
   // accumulator element e of row tile t: row 16 (2 wave + t) + 4 g + e, column c
   int orow[2][4];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int e = 0; e < 4; ++e) orow[t][e] = 16 * (2 * wave + t) + 4 * g + e;
-  int cur = 0;
-  for (int j = 0; j < ch.count; ++j) {
+  // The loads of step j + 1 (rows of M and the b slice) are issued before the
+  // products of step j, and those of step 0 with the start state, so a chain
+  // waits on memory about once rather than once per step.  A operands: rows
+  // 16 (2 wave + t) + c of M, k = 32 g .. 32 g + 31.
+  f32x4 ma[2][8], bq[2];
+  auto load_step = [&](int j) {
     const int seg = ch.p0 + j;
-    const float* bseg = b + (int64_t)seg * row + head + c0 + c;
-    float* dst = out + (int64_t)(ch.out0 + j) * row + head + c0 + c;
-    // A operands: rows 16 (2 wave + t) + c of M, k = 32 g .. 32 g + 31
     const float* Mseg = M + ((int64_t)seg * Hv + h) * CK * CK;
-    f32x4 ma[2][8];
+    const float* bseg = b + (int64_t)seg * row + head + c0 + c;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int q = 0; q < 8; ++q)
         ma[t][q] = *reinterpret_cast<const f32x4*>(Mseg + (int64_t)(16 * (2 * wave + t) + c) * CK + 32 * g + 4 * q);
-    f32x4 acc[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int e = 0; e < 4; ++e) bq[t][e] = bseg[(int64_t)orow[t][e] * V];
+    }
+  };
+  if (ch.count > 0) load_step(0);
+  for (int i = tid; i < CK * CT; i += CTHREADS) {
+    const int r = i / CT, cc = i % CT;
+    sS[0][sidx(r, cc)] = (s0 && ch.n >= 0) ? s0[ch.n * row + head + (int64_t)r * V + c0 + cc] : 0.f;
+  }
+  __syncthreads();
+  int cur = 0;
+  for (int j = 0; j < ch.count; ++j) {
+    float* dst = out + (int64_t)(ch.out0 + j) * row + head + c0 + c;
+    f32x4 mcur[2][8], acc[2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[t][e] = bseg[(int64_t)orow[t][e] * V];
+    for (int t = 0; t < 2; ++t) {
+      acc[t] = bq[t];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) mcur[t][q] = ma[t][q];
+    }
+    if (j + 1 < ch.count) load_step(j + 1);
     if (write_before) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -93,7 +120,7 @@ __global__ void __launch_bounds__(CTHREADS) compose_kernel(const float* __restri
       const float bv = sS[cur][sidx(32 * g + s, c)];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ma[t][s >> 2][s & 3], bv, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(mcur[t][s >> 2][s & 3], bv, acc[t], 0, 0, 0);
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -122,7 +149,8 @@ hipError_t launch_compose_chains(const float* M, const float* b, const float* s0
                                  hipStream_t stream) {
   if (n_chains == 0 || Hv == 0) return hipSuccess;
   if (K != CK || V % CT != 0) return hipErrorInvalidValue;
-  dim3 grid(V / CT, Hv, n_chains);
+  if ((int64_t)(V / CT) * Hv * n_chains > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((V / CT) * Hv * n_chains));
   hipLaunchKernelGGL(compose_kernel, grid, dim3(CTHREADS), 0, stream, M, b, s0, chains, Chain{0, 0, 0, 0}, Hv, V,
                      out, write_before, final_state);
   return hipGetLastError();
@@ -134,7 +162,7 @@ hipError_t launch_compose(const float* M, const float* b, const float* s0, int P
                           int V, float* starts, float* final_state, hipStream_t stream) {
   if (P == 0 || Hv == 0) return hipSuccess;
   if (K != CK || V % CT != 0) return hipErrorInvalidValue;
-  dim3 grid(V / CT, Hv, 1);
+  const dim3 grid((unsigned)((V / CT) * Hv));
   hipLaunchKernelGGL(compose_kernel, grid, dim3(CTHREADS), 0, stream, M, b, s0, nullptr, Chain{0, 0, P, 0}, Hv, V,
                      starts, 1, final_state);
   return hipGetLastError();

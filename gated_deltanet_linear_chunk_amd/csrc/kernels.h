@@ -49,6 +49,7 @@ struct ChunkArgs {
   const int32_t* s0_ref;     // [n_seqs]: >= 0 row of s0_seg, -1 zero, <= -2 row -2-r of s0
   const float* s0_seg;       // start states [*, Hv, K, V] picked by s0_ref
   const int32_t* sf_map;     // [n_seqs]: row of sf for the final state, -1 none
+  int n_tiles;               // bf16 scan: column tiles per (sequence, v-head), set by its launcher
 };
 
 // One record: T diag(beta) hi, lo (bf16, 10 tiles x 256 each), gamma[64] and
