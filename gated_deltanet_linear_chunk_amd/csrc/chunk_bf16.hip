@@ -22,15 +22,15 @@
 // or against another pair (hi*hi + hi*lo + lo*hi): S against K and Q, T diag(beta)
 // against V - e^G K S, P against U, the decayed U against K.
 //
-// LDS (bf16 unless noted; row pitches padded by 16 B, which keeps the MFMA
-// fragment reads free of bank conflicts).  The tiles read as MFMA operands
-// (Q, K, K^T, T diag(beta), P) store each 32-wide block of their K index in
-// fragment order: index 16 h + 4 g + j sits at 8 g + 4 h + j, so the eight
-// values a lane feeds one MFMA are contiguous and come in one 16-byte read
-// (two 8-byte reads 32 bytes apart run at about half the LDS rate):
-//   sQ [64][136], sK [64][136], sKt [128][72] (K^T), sVt [128][72] (V^T of
-//   this slice), sP [2][64][72] (hi, lo), sT2 [2][64][72] (T diag(beta)
-//   hi/lo), sO fp32 [64][132], gamma[64], dec[64] fp32.
+// LDS (bf16 unless noted).  The tiles read as MFMA operands (Q, K, K^T,
+// T diag(beta), P) store each 32-wide block of their K index in fragment
+// order (index 16 h + 4 g + j at 8 g + 4 h + j), so the eight values a lane
+// feeds one MFMA are contiguous and come in one 16-byte read, and swizzle
+// the 16-byte units of a row so that those reads meet no bank conflicts
+// (tile_pos, frag16 below):
+//   sQ [64][128], sK [64][128], sKt [128][64] (K^T), sP [2][64][64] (hi, lo),
+//   sT2 [2][64][64] (T diag(beta) hi/lo); sVt [128][72] (V^T of this slice,
+//   rows padded by 16 B), sO fp32 [64][132], gamma[64], dec[64] fp32.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -42,15 +42,16 @@ constexpr int CH = 64;
 constexpr int KD = 128;
 constexpr int BV = 128;
 
-constexpr int QP = KD + 8;
-constexpr int TP = CH + 8;
+constexpr int QP = KD;      // Q, K: 128 bf16 (256 bytes) per row, no padding
+constexpr int TP = CH;      // K^T, T diag(beta), P: 64 bf16 (128 bytes) per row
+constexpr int VTP = CH + 8; // V^T (not an MFMA operand): padded rows
 constexpr int OP = BV + 4;  // fp32 O tile pitch
 
 constexpr int OFF_Q = 0;
 constexpr int OFF_K = OFF_Q + CH * QP * 2;
 constexpr int OFF_KT = OFF_K + CH * QP * 2;
 constexpr int OFF_VT = OFF_KT + KD * TP * 2;
-constexpr int OFF_P = OFF_VT + BV * TP * 2;
+constexpr int OFF_P = OFF_VT + BV * VTP * 2;
 constexpr int OFF_T2 = OFF_P + 2 * CH * TP * 2;
 constexpr int OFF_O = OFF_T2 + 2 * CH * TP * 2;
 constexpr int OFF_GAM = OFF_O + CH * OP * 4;
@@ -109,17 +110,41 @@ __device__ __forceinline__ int frag_pos(int c) {
   return (c & ~31) + 8 * ((c >> 2) & 3) + 4 * ((c >> 4) & 1) + (c & 3);
 }
 
-// A or B fragment of k-step k0 (a multiple of 32) for row `row` of a tile in
-// fragment order: one 16-byte read.
-__device__ __forceinline__ bf16x8 frag16(const uint16_t* base, int pitch, int row, int k0, int g4) {
-  return *reinterpret_cast<const bf16x8*>(base + row * pitch + k0 + 8 * g4);
+// The LDS serves 64 four-byte banks per cycle.  Operand tiles have unpadded
+// rows (16 sixteen-byte units per 256-byte row of Q and K, 8 per 128-byte
+// row of K^T, T diag(beta) and P) and store unit u of a row at u ^ swz(row).
+// A fragment read puts 16 consecutive rows at one unit: the swizzle sends
+// them to 16 different units of the 64 banks, so the read runs without
+// conflicts (unit ^ row over 16 rows; for 128-byte rows, two rows share a
+// unit index but sit in the two halves of the banks).  The extra flip by
+// row bit 4 of Q and K spreads the stash's 32 even rows over 16 units.
+__device__ __forceinline__ int swz16(int row) { return (row & 15) ^ ((row >> 4) & 1); }
+__device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
+
+// Element offset of K index c (fragment order, then swizzled) in a row of a
+// 128-wide (W16) or 64-wide tile.
+template <bool W16>
+__device__ __forceinline__ int tile_pos(int row, int c) {
+  const int p = frag_pos(c);
+  return (((p >> 3) ^ (W16 ? swz16(row) : swz8(row))) << 3) | (p & 7);
 }
 
-// Eight consecutive K indices c .. c + 7 (c a multiple of 8) as two 8-byte
-// stores in fragment order.
-__device__ __forceinline__ void store8_frag(uint16_t* row_base, int c, const u32x4& v) {
-  *reinterpret_cast<u32x2*>(row_base + frag_pos(c)) = u32x2{v[0], v[1]};
-  *reinterpret_cast<u32x2*>(row_base + frag_pos(c + 4)) = u32x2{v[2], v[3]};
+// A or B fragment of k-step k0 (a multiple of 32) for row `row` of an
+// operand tile: one 16-byte read of unit k0 / 8 + g4.
+template <bool W16>
+__device__ __forceinline__ bf16x8 frag16(const uint16_t* tile, int row, int k0, int g4) {
+  constexpr int pitch = W16 ? QP : TP;
+  const int u = ((k0 >> 3) + g4) ^ (W16 ? swz16(row) : swz8(row));
+  return *reinterpret_cast<const bf16x8*>(tile + row * pitch + 8 * u);
+}
+
+// Eight consecutive K indices c .. c + 7 (c a multiple of 8) of row `row`
+// of a tile, as two 8-byte stores.
+template <bool W16>
+__device__ __forceinline__ void store8_frag(uint16_t* tile, int row, int c, const u32x4& v) {
+  uint16_t* rb = tile + row * (W16 ? QP : TP);
+  *reinterpret_cast<u32x2*>(rb + tile_pos<W16>(row, c)) = u32x2{v[0], v[1]};
+  *reinterpret_cast<u32x2*>(rb + tile_pos<W16>(row, c + 4)) = u32x2{v[2], v[3]};
 }
 
 template <int kMode, int NW>
@@ -290,20 +315,26 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
       const bool ok0 = r0 < L, ok1 = r0 + 1 < L;
       const u32x4 k0 = ok0 ? pk[j][0] : z, k1 = ok1 ? pk[j][1] : z;
       const u32x4 v0v = (load_v && ok0) ? pv[j][0] : z, v1v = (load_v && ok1) ? pv[j][1] : z;
-      store8_frag(sK + r0 * QP, d8, k0);
-      store8_frag(sK + (r0 + 1) * QP, d8, k1);
+      store8_frag<true>(sK, r0, d8, k0);
+      store8_frag<true>(sK, r0 + 1, d8, k1);
       if (kOut) {
-        store8_frag(sQ + r0 * QP, d8, ok0 ? pq[j][0] : z);
-        store8_frag(sQ + (r0 + 1) * QP, d8, ok1 ? pq[j][1] : z);
+        store8_frag<true>(sQ, r0, d8, ok0 ? pq[j][0] : z);
+        store8_frag<true>(sQ, r0 + 1, d8, ok1 ? pq[j][1] : z);
       }
 #pragma unroll
       for (int jx = 0; jx < 4; ++jx) {
         const int d0 = d8 + 2 * jx, d1 = d0 + 1;
-        *reinterpret_cast<uint32_t*>(sKt + d0 * TP + frag_pos(r0)) = (k0[jx] & 0xFFFFu) | (k1[jx] << 16);
-        *reinterpret_cast<uint32_t*>(sKt + d1 * TP + frag_pos(r0)) = (k0[jx] >> 16) | (k1[jx] & 0xFFFF0000u);
+        // rows d0, d1 of K^T: the upper half-wave (8 rows further on, the
+        // same bank half) writes them in the other order, so each store
+        // instruction covers both halves of the banks
+        const uint32_t w0 = (k0[jx] & 0xFFFFu) | (k1[jx] << 16), w1 = (k0[jx] >> 16) | (k1[jx] & 0xFFFF0000u);
+        const bool up = (lane & 32) != 0;
+        const int da = up ? d1 : d0, db = up ? d0 : d1;
+        *reinterpret_cast<uint32_t*>(sKt + da * TP + tile_pos<false>(da, r0)) = up ? w1 : w0;
+        *reinterpret_cast<uint32_t*>(sKt + db * TP + tile_pos<false>(db, r0)) = up ? w0 : w1;
         if (load_v) {
-          *reinterpret_cast<uint32_t*>(sVt + d0 * TP + r0) = (v0v[jx] & 0xFFFFu) | (v1v[jx] << 16);
-          *reinterpret_cast<uint32_t*>(sVt + d1 * TP + r0) = (v0v[jx] >> 16) | (v1v[jx] & 0xFFFF0000u);
+          *reinterpret_cast<uint32_t*>(sVt + d0 * VTP + r0) = (v0v[jx] & 0xFFFFu) | (v1v[jx] << 16);
+          *reinterpret_cast<uint32_t*>(sVt + d1 * VTP + r0) = (v0v[jx] >> 16) | (v1v[jx] & 0xFFFF0000u);
         }
       }
     }
@@ -324,8 +355,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
           tile_ij(rem >> 5, bi, bj);
           const int r = 16 * bi + ((rem >> 1) & 15), c = 16 * bj + 8 * (rem & 1);
           unsigned char* row = smem + (f < REC_TB_UNITS ? OFF_T2 : OFF_P) + 2 * (mat * CH * TP + r * TP);
-          dst0 = row + 2 * frag_pos(c);
-          dst1 = row + 2 * frag_pos(c + 4);
+          dst0 = row + 2 * tile_pos<false>(r, c);
+          dst1 = row + 2 * tile_pos<false>(r, c + 4);
         } else {
           const int g = f - REC_TB_UNITS;  // 0..15 gamma, 16..31 dec
           dst0 = smem + OFF_GAM + 16 * g;
@@ -358,8 +389,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
       bf16x8 fk[4], fq[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        fk[rt] = frag16(sK, QP, 16 * rt + c16, 32 * m, g4);
-        if (kOut) fq[rt] = frag16(sQ, QP, 16 * rt + c16, 32 * m, g4);
+        fk[rt] = frag16<true>(sK, 16 * rt + c16, 32 * m, g4);
+        if (kOut) fq[rt] = frag16<true>(sQ, 16 * rt + c16, 32 * m, g4);
       }
 #pragma unroll
       for (int part = 0; part < 2; ++part)
@@ -393,7 +424,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
           R[rt][3] = -gam.w * KS[ct][rt][3];
           if (load_v) {
             const u32x2 vv =
-                *reinterpret_cast<const u32x2*>(sVt + (wave * CPW + 16 * ct + c16) * TP + 16 * rt + 4 * g4);
+                *reinterpret_cast<const u32x2*>(sVt + (wave * CPW + 16 * ct + c16) * VTP + 16 * rt + 4 * g4);
             R[rt][0] += __uint_as_float(vv[0] << 16);
             R[rt][1] += __uint_as_float(vv[0] & 0xFFFF0000u);
             R[rt][2] += __uint_as_float(vv[1] << 16);
@@ -410,8 +441,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
         bf16x8 th[4], tl[4];
 #pragma unroll
         for (int rt = 2 * m; rt < 4; ++rt) {
-          th[rt] = frag16(sT2, TP, 16 * rt + c16, 32 * m, g4);
-          tl[rt] = frag16(sT2 + CH * TP, TP, 16 * rt + c16, 32 * m, g4);
+          th[rt] = frag16<false>(sT2, 16 * rt + c16, 32 * m, g4);
+          tl[rt] = frag16<false>(sT2 + CH * TP, 16 * rt + c16, 32 * m, g4);
         }
 #pragma unroll
         for (int part = 0; part < 3; ++part)
@@ -450,8 +481,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
         bf16x8 ph[4], pl[4];
 #pragma unroll
         for (int rt = 2 * m; rt < 4; ++rt) {
-          ph[rt] = frag16(sP, TP, 16 * rt + c16, 32 * m, g4);
-          pl[rt] = frag16(sP + CH * TP, TP, 16 * rt + c16, 32 * m, g4);
+          ph[rt] = frag16<false>(sP, 16 * rt + c16, 32 * m, g4);
+          pl[rt] = frag16<false>(sP + CH * TP, 16 * rt + c16, 32 * m, g4);
         }
 #pragma unroll
         for (int part = 0; part < 3; ++part)
@@ -496,7 +527,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
         for (int half = 0; half < 2; ++half) {
           bf16x8 fk[4];
 #pragma unroll
-          for (int x = 0; x < 4; ++x) fk[x] = frag16(sKt, TP, 16 * (4 * half + x) + c16, 32 * m, g4);
+          for (int x = 0; x < 4; ++x) fk[x] = frag16<false>(sKt, 16 * (4 * half + x) + c16, 32 * m, g4);
 #pragma unroll
           for (int part = 0; part < 2; ++part)
 #pragma unroll
