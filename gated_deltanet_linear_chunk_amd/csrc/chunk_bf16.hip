@@ -308,30 +308,43 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
     __syncthreads();  // every wave is done with the previous chunk's tiles
 
     // ---- stash q, k, v and the prep record ---------------------------------
+    // Rows past the end of a partial chunk (and v of M columns) are zeroed in
+    // the registers first; full chunks skip this.
+    if (L < CH || !load_v) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < NPAIR; ++j) {
+        if (r0_pf >= L) pk[j][0] = pq[j][0] = z;
+        if (r0_pf + 1 >= L) pk[j][1] = pq[j][1] = z;
+        if (!load_v || r0_pf >= L) pv[j][0] = z;
+        if (!load_v || r0_pf + 1 >= L) pv[j][1] = z;
+      }
+    }
+    // K^T words: the low halves of the two rows' words (row d0) and the high
+    // halves (row d1) by byte permutes; the upper half-wave (8 rows further
+    // on, the same bank half) stores row d1 first, so that each store
+    // instruction covers both halves of the banks.
+    const bool up_ = (lane & 32) != 0;
+    const uint32_t sel_a = up_ ? 0x07060302u : 0x05040100u, sel_b = up_ ? 0x05040100u : 0x07060302u;
 #pragma unroll
     for (int j = 0; j < NPAIR; ++j) {
       const int r0 = r0_pf, d8 = d8_pf + kDJ * j;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      const bool ok0 = r0 < L, ok1 = r0 + 1 < L;
-      const u32x4 k0 = ok0 ? pk[j][0] : z, k1 = ok1 ? pk[j][1] : z;
-      const u32x4 v0v = (load_v && ok0) ? pv[j][0] : z, v1v = (load_v && ok1) ? pv[j][1] : z;
+      const u32x4 k0 = pk[j][0], k1 = pk[j][1];
+      const u32x4 v0v = pv[j][0], v1v = pv[j][1];
       store8_frag<true>(sK, r0, d8, k0);
       store8_frag<true>(sK, r0 + 1, d8, k1);
       if (kOut) {
-        store8_frag<true>(sQ, r0, d8, ok0 ? pq[j][0] : z);
-        store8_frag<true>(sQ, r0 + 1, d8, ok1 ? pq[j][1] : z);
+        store8_frag<true>(sQ, r0, d8, pq[j][0]);
+        store8_frag<true>(sQ, r0 + 1, d8, pq[j][1]);
       }
 #pragma unroll
       for (int jx = 0; jx < 4; ++jx) {
         const int d0 = d8 + 2 * jx, d1 = d0 + 1;
-        // rows d0, d1 of K^T: the upper half-wave (8 rows further on, the
-        // same bank half) writes them in the other order, so each store
-        // instruction covers both halves of the banks
-        const uint32_t w0 = (k0[jx] & 0xFFFFu) | (k1[jx] << 16), w1 = (k0[jx] >> 16) | (k1[jx] & 0xFFFF0000u);
-        const bool up = (lane & 32) != 0;
-        const int da = up ? d1 : d0, db = up ? d0 : d1;
-        *reinterpret_cast<uint32_t*>(sKt + da * TP + tile_pos<false>(da, r0)) = up ? w1 : w0;
-        *reinterpret_cast<uint32_t*>(sKt + db * TP + tile_pos<false>(db, r0)) = up ? w0 : w1;
+        const int da = up_ ? d1 : d0, db = up_ ? d0 : d1;
+        *reinterpret_cast<uint32_t*>(sKt + da * TP + tile_pos<false>(da, r0)) =
+            __builtin_amdgcn_perm(k1[jx], k0[jx], sel_a);
+        *reinterpret_cast<uint32_t*>(sKt + db * TP + tile_pos<false>(db, r0)) =
+            __builtin_amdgcn_perm(k1[jx], k0[jx], sel_b);
         if (load_v) {
           *reinterpret_cast<uint32_t*>(sVt + d0 * VTP + r0) = (v0v[jx] & 0xFFFFu) | (v1v[jx] << 16);
           *reinterpret_cast<uint32_t*>(sVt + d1 * VTP + r0) = (v0v[jx] >> 16) | (v1v[jx] & 0xFFFF0000u);
