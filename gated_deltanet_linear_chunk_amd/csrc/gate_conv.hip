@@ -224,6 +224,8 @@ __device__ __forceinline__ void conv_sub(const typename ConvRow<T>::raw_t (&buf)
                                          float (&h3)[CONV_CH_PER_THREAD],
                                          const float (&wt)[4][CONV_CH_PER_THREAD],
                                          const float (&bs)[CONV_CH_PER_THREAD],
+                                         const float (&wa)[4][CONV_CH_PER_THREAD],
+                                         const float (&ba)[CONV_CH_PER_THREAD],
                                          int n_valid,
                                          uint32_t hist_code, const ConvParams& p, bool active,
                                          T* __restrict__ yrow, uint32_t* queue, uint32_t* qcount,
@@ -254,12 +256,14 @@ __device__ __forceinline__ void conv_sub(const typename ConvRow<T>::raw_t (&buf)
       out[i] = v;
       if (kMode == 2) ss = fmaf(v, v, ss);
       if (kCheck) {
-        float A = fabsf(bs[i]);
-        A = fmaf(fabsf(wt[0][i]), fabsf(x1), A);
-        A = fmaf(fabsf(wt[1][i]), fabsf(x2), A);
-        A = fmaf(fabsf(wt[2][i]), fabsf(x3), A);
-        A = fmaf(fabsf(wt[3][i]), fabsf(cur[i]), A);
-        dbits |= (rounding_in_doubt(v, A * (9.f * 0x1p-24f)) ? 1u : 0u) << i;
+        // Ab = 9 * 2^-24 * (|bias| + sum_j |w_j| |x_j|) from taps scaled by
+        // 9 * 2^-24 beforehand (exact for bf16 taps)
+        float Ab = ba[i];
+        Ab = fmaf(wa[0][i], fabsf(x1), Ab);
+        Ab = fmaf(wa[1][i], fabsf(x2), Ab);
+        Ab = fmaf(wa[2][i], fabsf(x3), Ab);
+        Ab = fmaf(wa[3][i], fabsf(cur[i]), Ab);
+        dbits |= (rounding_in_doubt(v, Ab) ? 1u : 0u) << i;
       }
       h1[i] = h2[i];
       h2[i] = h3[i];
@@ -362,6 +366,15 @@ __device__ __forceinline__ void conv1d_run(const T* __restrict__ x, const T* __r
     for (int i = 0; i < NCH; ++i) bs[i] = bias ? Row::scalar(bias, cl + i) : 0.f;
   }
 
+  // |taps| and |bias| scaled by 9 * 2^-24 for the rounding check's bound
+  float wa[4][NCH], ba[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    ba[i] = fabsf(bs[i]) * (9.f * 0x1p-24f);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wa[j][i] = fabsf(wt[j][i]) * (9.f * 0x1p-24f);
+  }
+
   // ---- region (sample / batch row) of the first token ----------------------------
   int n = 0;
   int64_t s_start, s_end;
@@ -427,10 +440,10 @@ __device__ __forceinline__ void conv1d_run(const T* __restrict__ x, const T* __r
     const int nv_ = (int)((TS) + SUB < tw1 ? SUB : tw1 - (TS));                                        \
     T* yrow_ = y + (TS) * C + c0;                                                                      \
     if (masked_)                                                                                       \
-      conv_sub<T, kMode, true>(BUF, h1, h2, h3, wt, bs, nv_, code_, p, active, yrow_, queue,           \
+      conv_sub<T, kMode, true>(BUF, h1, h2, h3, wt, bs, wa, ba, nv_, code_, p, active, yrow_, queue,   \
                                qcount, (TS), tw0, c0, overflow);                                       \
     else                                                                                               \
-      conv_sub<T, kMode, false>(BUF, h1, h2, h3, wt, bs, nv_, code_, p, active, yrow_, queue,          \
+      conv_sub<T, kMode, false>(BUF, h1, h2, h3, wt, bs, wa, ba, nv_, code_, p, active, yrow_, queue,  \
                                 qcount, (TS), tw0, c0, overflow);                                      \
   } while (0)
   for (int64_t ts = tw0; ts < tw1; ts += 2 * SUB) {
