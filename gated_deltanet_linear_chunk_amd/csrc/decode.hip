@@ -9,6 +9,10 @@
 // bound by HBM: one pass over the state, which stays in registers between the
 // two column sums over K.
 //
+// The state is read and written once per step, so its loads and stores are
+// non-temporal (streamed past the caches: 0.222 -> 0.202 ms for 256
+// sequences at H_v = 32, K = V = 128).
+//
 // One workgroup of 256 threads owns (sequence, v-head, 32 state columns).
 // Thread t holds columns 4 (t % 8) .. + 3 of the slice in K / 32 consecutive
 // rows (row group t / 8): one 16-byte load and one store per row, eight
@@ -81,7 +85,7 @@ __global__ void __launch_bounds__(DT) decode_kernel(DecodeArgs a) {
   float* S = a.state + ((r * a.Hv + h) * K + rg * RPG) * (int64_t)a.V + j0;
   f32x4 s[RPG];
 #pragma unroll
-  for (int i = 0; i < RPG; ++i) s[i] = *reinterpret_cast<const f32x4*>(S + (int64_t)i * a.V);
+  for (int i = 0; i < RPG; ++i) s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (int64_t)i * a.V));
   const Tin* kp = reinterpret_cast<const Tin*>(a.k) + ((int64_t)n * a.Hqk + hq) * K + rg * RPG;
   const Tin* qp = reinterpret_cast<const Tin*>(a.q) + ((int64_t)n * a.Hqk + hq) * K + rg * RPG;
   const Tin* vp = reinterpret_cast<const Tin*>(a.v) + ((int64_t)n * a.Hv + h) * a.V + j0;
@@ -109,7 +113,7 @@ __global__ void __launch_bounds__(DT) decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < RPG; ++i) {
     s[i] += kv[i] * u;
-    *reinterpret_cast<f32x4*>(S + (int64_t)i * a.V) = s[i];
+    __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(S + (int64_t)i * a.V));
     pq += s[i] * qv[i];
   }
   const f32x4 sq = column_sum(pq, red_q, wave, lane, c4);
