@@ -181,6 +181,20 @@ def test_chunk_bf16_split_long_samples(gates, V):
         assert not torch.equal(o2[0], o)  # the split path really ran
 
 
+def test_chunk_bf16_gqa_ratio_three():
+    """Three v-heads per q/k head (H_qk = 8, H_v = 24): the prep builds one v-head per wave and the
+    scan places each q/k head's three v-heads on one XCD; packed samples with host offsets and
+    start states match the oracle."""
+    lengths = [3000, 1, 130, 64]
+    d = gdn_inputs.small(39, lengths, 8, 24, 128, 128, "bf16", A_log_range=(-2.0, 0.0))
+    s0 = (np.random.default_rng(9).standard_normal((len(lengths), 24, 128, 128)) * 0.05).astype(np.float32)
+    o, fin = _run_chunk(d, "bf16", s0, o_dtype=torch.float32)
+    oref, fref = _oracle_chunk(d, s0)
+    so = assert_bf16(host(o), oref, "o")
+    sf = assert_bf16(host(fin), fref, "final")
+    print("\ngqa 3: o %s final %s" % (so, sf))
+
+
 def test_chunk_bf16_store_o_bf16():
     d = gdn_inputs.small(32, [200, 57], 1, 2, 128, 128, "bf16")
     o, _ = _run_chunk(d, "bf16", o_dtype=torch.bfloat16)
