@@ -15,7 +15,8 @@
 // one before the shared tiles are overwritten, one after they are filled.
 // The next chunk's q, k, v and prep record are fetched into registers while
 // the current chunk computes; O goes through its own LDS tile so that its
-// global stores are 16-byte vectors.
+// global stores are 16-byte vectors, stored by the first half of the waves
+// after the next chunk's first barrier.
 //
 // Precision: every fp32 quantity that meets the matrix cores is a bf16 pair
 // hi + lo (~16 significant bits), multiplied against exact bf16 data (q, k)
@@ -303,9 +304,47 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
 #define GDN_PREFETCH(T0) do { GDN_PF_REC(T0); GDN_PF_KQ(T0); GDN_PF_V(T0); } while (0)
   if (bos < eos) GDN_PREFETCH(bos);
 
+  // O of a finished chunk from the fp32 LDS tile to 16-byte global stores, by
+  // the first half of the waves: the two waves that share a SIMD finish a
+  // chunk out of step, the later one (of the second half) setting the pace,
+  // so the stores go to the waves that would otherwise wait at the barrier.
+  // Rows past the end of the chunk store a second copy of its last row
+  // instead, so that every store is unconditional.  Address: uniform element
+  // offset of (chunk start, head, slice) plus a lane's 32-bit offset
+  // r * Hv * V + c (Hv * V is below 2^24: it bounds v's token stride).
+  auto flush_o = [&](int64_t tp, int Lp) {
+    constexpr int RUNS = BV / 8;  // 8-column runs per row
+    constexpr int HT = NT / 2;    // threads of the first half
+    const int64_t obase = (tp * a.Hv + h) * (int64_t)a.V + v0;
+    const uint32_t tok32 = (uint32_t)(a.Hv * a.V);
+#pragma unroll
+    for (int i = 0; i < CH * RUNS / HT; ++i) {
+      const int u = tid + HT * i;
+      const int r = min(u / RUNS, Lp - 1), c = 8 * (u % RUNS);
+      const float* src = sO + r * OP + c;
+      const float4 x0 = *reinterpret_cast<const float4*>(src);
+      const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+      const uint32_t lo = __umul24((uint32_t)r, tok32) + (uint32_t)c;
+      if (kMode == kOutBF16) {
+        uint4 w;
+        w.x = pack_bf16x2(a.scale * x0.x, a.scale * x0.y);
+        w.y = pack_bf16x2(a.scale * x0.z, a.scale * x0.w);
+        w.z = pack_bf16x2(a.scale * x1.x, a.scale * x1.y);
+        w.w = pack_bf16x2(a.scale * x1.z, a.scale * x1.w);
+        *reinterpret_cast<uint4*>((char*)((uint16_t*)a.o + obase) + 2u * lo) = w;
+      } else {
+        float* dst = (float*)((char*)((float*)a.o + obase) + 4u * lo);
+        *reinterpret_cast<float4*>(dst) = make_float4(a.scale * x0.x, a.scale * x0.y, a.scale * x0.z, a.scale * x0.w);
+        *reinterpret_cast<float4*>(dst + 4) =
+            make_float4(a.scale * x1.x, a.scale * x1.y, a.scale * x1.z, a.scale * x1.w);
+      }
+    }
+  };
+
   for (int64_t t0 = bos; t0 < eos; t0 += CH) {
     const int L = (int)((eos - t0) < CH ? (eos - t0) : CH);
     __syncthreads();  // every wave is done with the previous chunk's tiles
+    if (kOut && t0 > bos && wave < NW / 2) flush_o(t0 - CH, CH);  // a full chunk: only the last can be short
 
     // ---- stash q, k, v and the prep record ---------------------------------
     // Rows past the end of a partial chunk (and v of M columns) are zeroed in
@@ -554,8 +593,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
         }
     }
     if (kOut) {
-      // Through this wave's own columns of the O tile (no other wave touches
-      // them, and a wave's LDS accesses complete in order) to 16-byte stores.
+      // O into this wave's own columns of the fp32 O tile; the first half of
+      // the waves stores the whole tile after the next chunk's first barrier.
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -563,40 +602,12 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             sO[(16 * rt + 4 * g4 + e) * OP + wave * CPW + 16 * ct + c16] = O[ct][rt][e];
-      // Rows past the end of the chunk store a second copy of its last row
-      // instead, so that every store is unconditional and the memory counter
-      // waits further on stay exact.
-      constexpr int RUNS = CPW / 8;  // 8-column runs per row
-      // uniform element offset of (chunk start, head, slice) plus a lane's
-      // 32-bit offset r * Hv * V + c (Hv * V is below 2^24: it bounds v's stride)
-      const int64_t obase = (t0 * a.Hv + h) * (int64_t)a.V + v0;
-      const uint32_t tok32 = (uint32_t)(a.Hv * a.V);
-#pragma unroll
-      for (int i = 0; i < CH * RUNS / 64; ++i) {
-        const int u = lane + 64 * i;
-        const int r = min(u / RUNS, L - 1), c = wave * CPW + 8 * (u % RUNS);
-        const float* src = sO + r * OP + c;
-        const float4 x0 = *reinterpret_cast<const float4*>(src);
-        const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
-        {
-          const uint32_t lo = __umul24((uint32_t)r, tok32) + (uint32_t)c;
-          if (kMode == kOutBF16) {
-            uint4 w;
-            w.x = pack_bf16x2(a.scale * x0.x, a.scale * x0.y);
-            w.y = pack_bf16x2(a.scale * x0.z, a.scale * x0.w);
-            w.z = pack_bf16x2(a.scale * x1.x, a.scale * x1.y);
-            w.w = pack_bf16x2(a.scale * x1.z, a.scale * x1.w);
-            *reinterpret_cast<uint4*>((char*)((uint16_t*)a.o + obase) + 2u * lo) = w;
-          } else {
-            float* dst = (float*)((char*)((float*)a.o + obase) + 4u * lo);
-            *reinterpret_cast<float4*>(dst) =
-                make_float4(a.scale * x0.x, a.scale * x0.y, a.scale * x0.z, a.scale * x0.w);
-            *reinterpret_cast<float4*>(dst + 4) =
-                make_float4(a.scale * x1.x, a.scale * x1.y, a.scale * x1.z, a.scale * x1.w);
-          }
-        }
-      }
     }
+  }
+  if (kOut && bos < eos) {  // the last chunk's O
+    const int64_t t_last = bos + CH * ((eos - bos - 1) / CH);
+    __syncthreads();
+    if (wave < NW / 2) flush_o(t_last, (int)(eos - t_last));
   }
 
 #undef GDN_PREFETCH
