@@ -173,7 +173,7 @@ def build_pipeline(w, d, o_dtype):
     return step, chunk_timer, conv_timer, conv_step
 
 
-def build_chunk_only(w, d, o_dtype, segmented=False):
+def build_chunk_only(w, d, o_dtype, segmented=False, gated_norm=False):
     torch = _torch()
     import gated_deltanet_linear_chunk_amd as gdn
 
@@ -194,6 +194,20 @@ def build_chunk_only(w, d, o_dtype, segmented=False):
             g, beta = gdn.gdn_gate_fwd(a, b, A_log, dt_bias)
             e = timer.start() if time_kernels else None
             out = gdn.gdn_chunk_fwd_segmented(q, k, v, g, beta, off_dev, off, o_dtype=o_dtype, workspace=ws)
+            if time_kernels:
+                timer.stop(e)
+            return out
+    elif gated_norm:
+        cu = torch.from_numpy(d["cu_seqlens"]).to(dev)
+        rng = np.random.default_rng(5)
+        z = bf(rng.standard_normal((w.total_tokens, w.Hv, w.V)).astype(np.float32))[None]
+        nw = f32(rng.uniform(0.5, 1.5, w.V))
+
+        def step(time_kernels=False):
+            g, beta = gdn.gdn_gate_fwd(a, b, A_log, dt_bias)
+            e = timer.start() if time_kernels else None
+            out = gdn.gdn_chunk_fwd_gated_norm(q, k, v, g, beta, z, norm_weight=nw, cu_seqlens=cu,
+                                               cu_seqlens_host=d["cu_seqlens"], o_dtype=o_dtype)
             if time_kernels:
                 timer.stop(e)
             return out
@@ -417,6 +431,16 @@ def main():
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "alg_bytes": nbytes,
         }
         del st
+        torch.cuda.empty_cache()
+        # the chunk forward with the gated norm applied as the scan writes o (bf16 z and y), against
+        # the chunk call above plus the separate norm kernel
+        dx = gdn_inputs.draw(w, with_qkv=True)
+        st, tm = build_chunk_only(w, dx, torch.bfloat16, gated_norm=True)
+        s = timed(st, max(3, args.steps // 4), 2)
+        extras["%s[chunk + gated norm fused, bf16 z and y]" % MAIN] = {
+            "tokens_per_s": w.total_tokens / s, "ms_per_step": s * 1e3, "main_kernel_ms": tm.mean_ms(),
+        }
+        del st, dx
         torch.cuda.empty_cache()
         result["extras"] = extras
 

@@ -21,6 +21,7 @@ __all__ = [
     "gdn_gate_fwd",
     "gdn_conv1d_fwd",
     "gdn_chunk_fwd",
+    "gdn_chunk_fwd_gated_norm",
     "gdn_segment_state_scan",
     "gdn_chunk_fwd_segmented",
     "gdn_segmented_workspace_bytes",
@@ -44,6 +45,7 @@ EXPORTED_SYMBOLS = (
     "gdn_conv1d_fwd",
     "gdn_chunk_fwd_workspace_bytes",
     "gdn_chunk_fwd",
+    "gdn_chunk_fwd_gated_norm",
     "gdn_segment_state_scan_workspace_bytes",
     "gdn_segment_state_scan",
     "gdn_segmented_workspace_bytes",
@@ -87,6 +89,9 @@ def load_library():
     lib.gdn_chunk_fwd_workspace_bytes.restype = sz
     lib.gdn_chunk_fwd.argtypes = [P, P, P, ctypes.c_int, i64, i64, i64, P, P, f32, P, P, P, i32, i32, i64, i32, i32,
                                   i32, i32, P, ctypes.c_int, P, P, sz, P]
+    lib.gdn_chunk_fwd_gated_norm.argtypes = [P, P, P, ctypes.c_int, i64, i64, i64, P, P, f32, P, P, P, i32, i32, i64,
+                                             i32, i32, i32, i32, P, ctypes.c_int, P, f32, P, ctypes.c_int, P, P,
+                                             sz, P]
     lib.gdn_segment_state_scan_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
     lib.gdn_segment_state_scan_workspace_bytes.restype = sz
     lib.gdn_segment_state_scan.argtypes = [P, P, ctypes.c_int, i64, i64, P, P, P, P, i32, P, i64, i32, i32, i32, i32,
@@ -98,7 +103,7 @@ def load_library():
     lib.gdn_decode_step.argtypes = [P, P, P, ctypes.c_int, P, P, f32, P, P, i64, i32, i32, i32, i32, i32, P,
                                     ctypes.c_int, P]
     lib.gdn_gated_rmsnorm_fwd.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P, f32, i64, i32, P, ctypes.c_int, P]
-    for name in ("gdn_gate_fwd", "gdn_conv1d_fwd", "gdn_chunk_fwd", "gdn_segment_state_scan",
+    for name in ("gdn_gate_fwd", "gdn_conv1d_fwd", "gdn_chunk_fwd", "gdn_chunk_fwd_gated_norm", "gdn_segment_state_scan",
                  "gdn_chunk_fwd_segmented", "gdn_decode_step", "gdn_gated_rmsnorm_fwd"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -280,6 +285,54 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale: float = 1.0, initial_state=None, cu_s
         _ptr(o), _dtype_code(o), _ptr(fin), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev),
     )
     _check("gdn_chunk_fwd", st)
+    return o, fin
+
+
+def gdn_chunk_fwd_gated_norm(q, k, v, g, beta, z, norm_weight=None, eps: float = 1e-6, scale: float = 1.0,
+                             initial_state=None, cu_seqlens=None, cu_seqlens_host=None, o_dtype=None,
+                             output_final_state: bool = True, workspace=None):
+    """gdn_chunk_fwd whose output passes through the gated RMS norm:
+    o = n / sqrt(mean(n^2) + eps) * norm_weight * silu(z) per (token, v-head) row.
+
+    Arguments as gdn_chunk_fwd, plus z [B, T, Hv, V] (float32 or bfloat16, dense)
+    and norm_weight fp32 [V] or None.  Returns (o, final_state).
+    """
+    torch = _torch()
+    dev = q.device
+    qs, ks, vs = _token_stride(q, "q"), _token_stride(k, "k"), _token_stride(v, "v")
+    if k.dtype != q.dtype or v.dtype != q.dtype or k.device != dev or v.device != dev:
+        raise ValueError("q, k, v must share dtype and device")
+    _require(g, "g", dev, torch.float32)
+    _require(beta, "beta", dev, torch.float32)
+    _require(z, "z", dev)
+    _require(norm_weight, "norm_weight", dev, torch.float32)
+    _require(initial_state, "initial_state", dev, torch.float32)
+    _require(cu_seqlens, "cu_seqlens", dev, torch.int32)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4:
+        raise ValueError("q, k must be [B, T, Hqk, K] and v [B, T, Hv, V]")
+    B, T, Hqk, K = q.shape
+    Hv, V = v.shape[2], v.shape[3]
+    if v.shape[:2] != (B, T) or g.shape != (B, T, Hv) or beta.shape != (B, T, Hv):
+        raise ValueError("v / g / beta shapes disagree with q")
+    if z.shape != (B, T, Hv, V):
+        raise ValueError("z must be [B, T, Hv, V]")
+    if norm_weight is not None and norm_weight.shape != (V,):
+        raise ValueError("norm_weight must be [V]")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if initial_state is not None and initial_state.shape != (N, Hv, K, V):
+        raise ValueError("initial_state must be [N, Hv, K, V]")
+    o_dtype = v.dtype if o_dtype is None else o_dtype
+    o = torch.empty((B, T, Hv, V), dtype=o_dtype, device=dev)
+    fin = torch.empty((N, Hv, K, V), dtype=torch.float32, device=dev) if output_final_state else None
+    total = T if cu_seqlens is not None else B * T
+    ws = _workspace(gdn_chunk_fwd_workspace_bytes(q.dtype, total, N, Hv, K, V), dev, workspace)
+    st = load_library().gdn_chunk_fwd_gated_norm(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), qs, ks, vs, _ptr(g), _ptr(beta), float(scale), _ptr(initial_state),
+        _ptr(cu_seqlens), _host_offsets(cu_seqlens_host), 0 if cu_seqlens is None else N, B, T, Hqk, Hv, K, V,
+        _ptr(z), _dtype_code(z), _ptr(norm_weight), float(eps), _ptr(o), _dtype_code(o), _ptr(fin), _ptr(ws),
+        0 if ws is None else ws.numel(), _stream(dev),
+    )
+    _check("gdn_chunk_fwd_gated_norm", st)
     return o, fin
 
 

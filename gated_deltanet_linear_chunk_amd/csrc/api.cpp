@@ -132,14 +132,22 @@ size_t gdn_chunk_fwd_workspace_bytes(gdn_dtype in_dt, int64_t total_tokens, int3
   return std::max(plain, split_workspace_bytes(total_tokens, n_seqs + pmax, pmax, H_v, K, V));
 }
 
-gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, gdn_dtype in_dt,
+// The gated output norm that the bf16 scan applies as it writes o (null: none).
+struct FusedNorm {
+  const void* z;
+  int z_dt;
+  const float* weight;
+  float eps;
+};
+
+static gdn_status chunk_fwd_run(const void* q, const void* k, const void* v, gdn_dtype in_dt,
                          int64_t q_token_stride, int64_t k_token_stride, int64_t v_token_stride,
                          const float* g, const float* beta, float scale,
                          const float* initial_state, const int32_t* cu_seqlens,
                          const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t B, int64_t T,
                          int32_t H_qk, int32_t H_v, int32_t K, int32_t V, void* o,
                          gdn_dtype o_dt, float* final_state, void* workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
+                         size_t workspace_bytes, const FusedNorm* norm, hipStream_t stream) {
   if (!valid_dtype(in_dt) || !valid_dtype(o_dt)) return GDN_ERR_BAD_DTYPE;
   if (B < 1 || T < 0 || H_qk < 1 || H_v < 1 || K < 1 || V < 1) return GDN_ERR_BAD_SHAPE;
   if (H_v % H_qk != 0) return GDN_ERR_BAD_SHAPE;
@@ -189,6 +197,13 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, gdn_dtype 
   a.sf_seq_stride = (int64_t)H_v * K * V;
   a.sf_head_stride = (int64_t)K * V;
   a.sf_row_stride = V;
+  if (norm) {
+    if (total > 0 && !norm->z) return GDN_ERR_NULL_POINTER;
+    a.z = norm->z;
+    a.z_dt = norm->z_dt;
+    a.nw = norm->weight;
+    a.eps = norm->eps;
+  }
   if (in_dt == GDN_BF16 && cu_seqlens && cu_seqlens_host && total > 0) {
     gdn::SplitPlan plan;
     if (gdn::plan_split(cu_seqlens_host, N, H_v, V, initial_state != nullptr, device_cus(), plan) &&
@@ -233,6 +248,49 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, gdn_dtype 
   const hipError_t e = in_dt == GDN_BF16 ? gdn::launch_chunk_bf16(a, stream)
                                          : gdn::launch_chunk_f32(a, stream);
   return hip_status(e);
+}
+
+gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, gdn_dtype in_dt,
+                         int64_t q_token_stride, int64_t k_token_stride, int64_t v_token_stride,
+                         const float* g, const float* beta, float scale,
+                         const float* initial_state, const int32_t* cu_seqlens,
+                         const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t B, int64_t T,
+                         int32_t H_qk, int32_t H_v, int32_t K, int32_t V, void* o,
+                         gdn_dtype o_dt, float* final_state, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  return chunk_fwd_run(q, k, v, in_dt, q_token_stride, k_token_stride, v_token_stride, g, beta, scale,
+                       initial_state, cu_seqlens, cu_seqlens_host, n_seqs, B, T, H_qk, H_v, K, V, o, o_dt,
+                       final_state, workspace, workspace_bytes, nullptr, stream);
+}
+
+gdn_status gdn_chunk_fwd_gated_norm(const void* q, const void* k, const void* v, gdn_dtype in_dt,
+                                    int64_t q_token_stride, int64_t k_token_stride,
+                                    int64_t v_token_stride, const float* g, const float* beta,
+                                    float scale, const float* initial_state,
+                                    const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                    int32_t n_seqs, int32_t B, int64_t T, int32_t H_qk, int32_t H_v,
+                                    int32_t K, int32_t V, const void* z, gdn_dtype z_dt,
+                                    const float* norm_weight, float eps, void* o, gdn_dtype o_dt,
+                                    float* final_state, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  if (!valid_dtype(in_dt) || !valid_dtype(o_dt) || !valid_dtype(z_dt)) return GDN_ERR_BAD_DTYPE;
+  if (!(eps >= 0.f)) return GDN_ERR_BAD_SHAPE;
+  if (in_dt == GDN_BF16 && V == 128) {
+    const FusedNorm norm{z, z_dt == GDN_BF16 ? 1 : 0, norm_weight, eps};
+    return chunk_fwd_run(q, k, v, in_dt, q_token_stride, k_token_stride, v_token_stride, g, beta, scale,
+                         initial_state, cu_seqlens, cu_seqlens_host, n_seqs, B, T, H_qk, H_v, K, V, o,
+                         o_dt, final_state, workspace, workspace_bytes, &norm, stream);
+  }
+  // other shapes: the chunk forward, then the norm kernel over o in place
+  if (V != 32 && V != 64 && V != 128 && V != 256 && V != 512) return GDN_ERR_UNSUPPORTED;
+  const int64_t total = cu_seqlens ? T : (int64_t)B * T;
+  if (total > 0 && !z) return GDN_ERR_NULL_POINTER;
+  const gdn_status st = chunk_fwd_run(q, k, v, in_dt, q_token_stride, k_token_stride, v_token_stride, g,
+                                      beta, scale, initial_state, cu_seqlens, cu_seqlens_host, n_seqs, B, T,
+                                      H_qk, H_v, K, V, o, o_dt, final_state, workspace, workspace_bytes,
+                                      nullptr, stream);
+  if (st != GDN_OK || total <= 0) return st;
+  return gdn_gated_rmsnorm_fwd(o, o_dt, z, z_dt, norm_weight, eps, total * H_v, V, o, o_dt, stream);
 }
 
 size_t gdn_segment_state_scan_workspace_bytes(int64_t T, int32_t P, int32_t H_v, int32_t K,

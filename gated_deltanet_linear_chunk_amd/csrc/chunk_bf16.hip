@@ -148,7 +148,7 @@ __device__ __forceinline__ void store8_frag(uint16_t* tile, int row, int c, cons
   *reinterpret_cast<u32x2*>(rb + tile_pos<W16>(row, c + 4)) = u32x2{v[2], v[3]};
 }
 
-template <int kMode, int NW>
+template <int kMode, int NW, bool kNorm>
 __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 p1) {
   constexpr int NT = NW * 64;
   constexpr int CPW = BV / NW;     // state columns per wave
@@ -158,6 +158,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   constexpr int RUNITS = kOut ? REC_UNITS : REC_STATE_UNITS;  // record units this mode reads
   constexpr int NREC = (RUNITS + NT - 1) / NT;                 // record units per thread
   static_assert(CPW % 16 == 0 && NW * CPW == BV, "wave layout");
+  static_assert(!kNorm || kOut, "the norm applies to outputs");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + OFF_Q);
@@ -325,18 +326,57 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
       const float4 x0 = *reinterpret_cast<const float4*>(src);
       const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
       const uint32_t lo = __umul24((uint32_t)r, tok32) + (uint32_t)c;
+      float y[8] = {a.scale * x0.x, a.scale * x0.y, a.scale * x0.z, a.scale * x0.w,
+                    a.scale * x1.x, a.scale * x1.y, a.scale * x1.z, a.scale * x1.w};
+      if constexpr (kNorm) {
+        // gated RMS norm of the whole row (the 16 lanes of a row are adjacent
+        // and aligned to 16 inside the wave): y = o rsqrt(mean o^2 + eps)
+        // weight silu(z); z has o's layout, so it shares o's offsets
+        float zv[8], wv[8];
+        if (a.z_dt == 1) {
+          const uint4 zr = *reinterpret_cast<const uint4*>((const char*)((const uint16_t*)a.z + obase) + 2u * lo);
+          const uint32_t zw[4] = {zr.x, zr.y, zr.z, zr.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            zv[2 * e] = __uint_as_float(zw[e] << 16);
+            zv[2 * e + 1] = __uint_as_float(zw[e] & 0xFFFF0000u);
+          }
+        } else {
+          const float* zp = (const float*)((const char*)((const float*)a.z + obase) + 4u * lo);
+          const float4 z0 = *reinterpret_cast<const float4*>(zp);
+          const float4 z1 = *reinterpret_cast<const float4*>(zp + 4);
+          zv[0] = z0.x, zv[1] = z0.y, zv[2] = z0.z, zv[3] = z0.w;
+          zv[4] = z1.x, zv[5] = z1.y, zv[6] = z1.z, zv[7] = z1.w;
+        }
+        if (a.nw) {
+          const float4 w0 = *reinterpret_cast<const float4*>(a.nw + v0 + c);
+          const float4 w1 = *reinterpret_cast<const float4*>(a.nw + v0 + c + 4);
+          wv[0] = w0.x, wv[1] = w0.y, wv[2] = w0.z, wv[3] = w0.w;
+          wv[4] = w1.x, wv[5] = w1.y, wv[6] = w1.z, wv[7] = w1.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) wv[e] = 1.f;
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
+#pragma unroll
+        for (int off = 1; off < RUNS; off <<= 1) ss += __shfl_xor(ss, off, 64);
+        const float inv = 1.f / sqrtf(ss / (float)BV + a.eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = y[e] * inv * wv[e] * (zv[e] / (1.f + expf(-zv[e])));
+      }
       if (kMode == kOutBF16) {
         uint4 w;
-        w.x = pack_bf16x2(a.scale * x0.x, a.scale * x0.y);
-        w.y = pack_bf16x2(a.scale * x0.z, a.scale * x0.w);
-        w.z = pack_bf16x2(a.scale * x1.x, a.scale * x1.y);
-        w.w = pack_bf16x2(a.scale * x1.z, a.scale * x1.w);
+        w.x = pack_bf16x2(y[0], y[1]);
+        w.y = pack_bf16x2(y[2], y[3]);
+        w.z = pack_bf16x2(y[4], y[5]);
+        w.w = pack_bf16x2(y[6], y[7]);
         *reinterpret_cast<uint4*>((char*)((uint16_t*)a.o + obase) + 2u * lo) = w;
       } else {
         float* dst = (float*)((char*)((float*)a.o + obase) + 4u * lo);
-        *reinterpret_cast<float4*>(dst) = make_float4(a.scale * x0.x, a.scale * x0.y, a.scale * x0.z, a.scale * x0.w);
-        *reinterpret_cast<float4*>(dst + 4) =
-            make_float4(a.scale * x1.x, a.scale * x1.y, a.scale * x1.z, a.scale * x1.w);
+        *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(y[4], y[5], y[6], y[7]);
       }
     }
   };
@@ -640,9 +680,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
 
 constexpr int kScanWaves = 8;  // the prefetch code assumes 512 threads
 
-template <int kMode>
+template <int kMode, bool kNorm = false>
 hipError_t launch_scan(const ChunkArgs& a, Pass1 p1, dim3 grid, hipStream_t stream) {
-  const void* fn = (const void*)chunk_scan_kernel<kMode, kScanWaves>;
+  const void* fn = (const void*)chunk_scan_kernel<kMode, kScanWaves, kNorm>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
   if (e != hipSuccess) return e;
   // 1-D launch over (tile, v-head, sequence); the kernel decodes it
@@ -650,7 +690,7 @@ hipError_t launch_scan(const ChunkArgs& a, Pass1 p1, dim3 grid, hipStream_t stre
   c.n_tiles = (int)grid.x;
   const int64_t n = (int64_t)grid.x * grid.y * grid.z;
   if (n > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((chunk_scan_kernel<kMode, kScanWaves>), dim3((unsigned)n), dim3(kScanWaves * 64), LDS_BYTES,
+  hipLaunchKernelGGL((chunk_scan_kernel<kMode, kScanWaves, kNorm>), dim3((unsigned)n), dim3(kScanWaves * 64), LDS_BYTES,
                      stream, c, p1);
   return hipGetLastError();
 }
@@ -671,6 +711,12 @@ hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t stream, bool prep) 
   if (!with_o) {
     // state only: run the scan without outputs
     return launch_scan<kPass1>(a, Pass1{0, nullptr}, grid, stream);
+  }
+  if (a.z) {
+    // the gated norm needs a whole row of V values in one workgroup
+    if (a.V != BV) return hipErrorInvalidValue;
+    return a.o_dt == 1 ? launch_scan<kOutBF16, true>(a, Pass1{0, nullptr}, grid, stream)
+                       : launch_scan<kOutF32, true>(a, Pass1{0, nullptr}, grid, stream);
   }
   return a.o_dt == 1 ? launch_scan<kOutBF16>(a, Pass1{0, nullptr}, grid, stream)
                      : launch_scan<kOutF32>(a, Pass1{0, nullptr}, grid, stream);

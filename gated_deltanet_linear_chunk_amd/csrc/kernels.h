@@ -50,6 +50,12 @@ struct ChunkArgs {
   const float* s0_seg;       // start states [*, Hv, K, V] picked by s0_ref
   const int32_t* sf_map;     // [n_seqs]: row of sf for the final state, -1 none
   int n_tiles;               // bf16 scan: column tiles per (sequence, v-head), set by its launcher
+  // bf16 scan with V == 128: when z is set, o receives the gated RMS norm of
+  // every output row, o * rsqrt(mean(o^2) + eps) * nw * silu(z), instead of o.
+  const void* z;    // [Ttot, Hv, V] in z_dt (dense), or null
+  int z_dt;         // 0 f32, 1 bf16
+  const float* nw;  // [V] or null (ones)
+  float eps;
 };
 
 // One record: T diag(beta) hi, lo (bf16, 10 tiles x 256 each), gamma[64] and

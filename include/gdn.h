@@ -142,6 +142,32 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, gdn_dtype 
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * gdn_chunk_fwd followed by the gated output norm of gdn_gated_rmsnorm_fwd,
+ * "chunk_gated_delta_rule + norm" with the z component (LlamaFactory PR
+ * "[v1] support GDN Ulysses cp", Design; the norm's form is the per-head RMS
+ * norm gated by SiLU(z) stated at gdn_gated_rmsnorm_fwd):
+ *     o[t, h] = n / sqrt(mean(n^2) + eps) * norm_weight * z[t, h] sigmoid(z[t, h]),
+ *     n = scale * S_t^T q_t  (the output gdn_chunk_fwd would store).
+ * Arguments as in gdn_chunk_fwd, plus z [B, T, H_v, V] in z_dt (dense, o's
+ * layout), norm_weight fp32 [V] or NULL (ones), eps >= 0 (GDN_ERR_BAD_SHAPE
+ * otherwise).  With in_dt = BF16 and V = 128 the scan applies the norm to
+ * its fp32 output rows as it writes them, so n never reaches memory; other
+ * shapes run gdn_chunk_fwd into o and then the norm in place over o (V in
+ * {32, 64, 128, 256, 512}, GDN_ERR_UNSUPPORTED otherwise), with n rounded
+ * to o_dt in between.  Workspace as for gdn_chunk_fwd.
+ */
+gdn_status gdn_chunk_fwd_gated_norm(const void* q, const void* k, const void* v, gdn_dtype in_dt,
+                                    int64_t q_token_stride, int64_t k_token_stride,
+                                    int64_t v_token_stride, const float* g, const float* beta,
+                                    float scale, const float* initial_state,
+                                    const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                    int32_t n_seqs, int32_t B, int64_t T, int32_t H_qk, int32_t H_v,
+                                    int32_t K, int32_t V, const void* z, gdn_dtype z_dt,
+                                    const float* norm_weight, float eps, void* o, gdn_dtype o_dt,
+                                    float* final_state, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/*
  * Segment state scan: one long sequence cut into P contiguous segments
  * [seg_offsets[i], seg_offsets[i+1]) of the token arrays (the sglang PR's
  * per-rank segments, here on one GPU).  Pass 1 computes, for every segment

@@ -96,6 +96,29 @@ def test_chunk_validation(lib):
     assert _chunk(lib, T=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
 
 
+def _chunk_norm(lib, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, in_dt=1, qs=0, ks=0, vs=0, g=FAKE, beta=FAKE, scale=1.0, s0=None, cu=None,
+                cu_host=None, n_seqs=0, B=1, T=64, Hqk=16, Hv=32, K=128, V=128, z=FAKE, z_dt=1, nw=None, eps=1e-6,
+                o=FAKE, o_dt=0, fin=None, ws=FAKE, ws_bytes=1 << 40, stream=None)
+    args.update(kw)
+    return lib.gdn_chunk_fwd_gated_norm(*args.values())
+
+
+def test_chunk_gated_norm_validation(lib):
+    assert _chunk_norm(lib, z_dt=3) == DTYPE
+    assert _chunk_norm(lib, o_dt=3) == DTYPE
+    assert _chunk_norm(lib, eps=-1.0) == SHAPE
+    assert _chunk_norm(lib, eps=float("nan")) == SHAPE
+    assert _chunk_norm(lib, z=None) == NULLP  # fused path (bf16, V = 128)
+    assert _chunk_norm(lib, z=None, V=256) == NULLP  # chunk forward + norm kernel
+    assert _chunk_norm(lib, in_dt=0, K=32, V=96) == UNSUP  # no norm kernel for V = 96
+    assert _chunk_norm(lib, q=None) == NULLP  # the chunk forward's own checks still apply
+    assert _chunk_norm(lib, K=64) == UNSUP
+    assert _chunk_norm(lib, ws=None) == NULLP
+    assert _chunk_norm(lib, T=0, q=None, k=None, v=None, g=None, beta=None, o=None, z=None) == OK
+    assert _chunk_norm(lib, T=0, V=256, q=None, k=None, v=None, g=None, beta=None, o=None, z=None) == OK
+
+
 def test_conv_validation(lib):
     def conv(**kw):
         a = dict(x=FAKE, w=FAKE, bias=None, dt=1, cu=None, cu_host=None, n=0, B=1, T=32, C=8192, W=4, silu=1,

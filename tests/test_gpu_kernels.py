@@ -11,7 +11,7 @@ import pytest
 
 import gdn_inputs
 import oracle
-from parity_util import assert_bf16, assert_f32, dev, host, stats
+from parity_util import TOL_F32_ABS, assert_bf16, assert_f32, dev, host, stats
 
 pytestmark = pytest.mark.gpu
 
@@ -442,3 +442,72 @@ def test_gated_norm_after_the_chunk_rule():
     ref = oracle.gated_rmsnorm(oref, z, w, 1e-6)
     s = assert_bf16(host(y), ref, "y")
     print("\nnorm after chunk %s" % (s,))
+
+
+def _run_chunk_norm(d, dtype, z, w, eps, s0=None, o_dtype=None, use_cu=True):
+    q = dev(d["q"], dtype)[None]
+    k = dev(d["k"], dtype)[None]
+    v = dev(d["v"], dtype)[None]
+    g, beta = _gpu_gates(d)
+    cu = dev(d["cu_seqlens"], "i32") if use_cu else None
+    o, fin = gdn.gdn_chunk_fwd_gated_norm(
+        q, k, v, g[None], beta[None], z[None], norm_weight=w, eps=eps,
+        initial_state=None if s0 is None else dev(s0), cu_seqlens=cu,
+        cu_seqlens_host=d["cu_seqlens"] if use_cu else None, o_dtype=o_dtype,
+    )
+    torch.cuda.synchronize()
+    return o[0], fin
+
+
+@pytest.mark.parametrize("o_dt,z_dt,weighted", [("f32", "bf16", True), ("bf16", "bf16", False), ("f32", "f32", False)])
+def test_chunk_gated_norm_fused(o_dt, z_dt, weighted):
+    """bf16 inputs, V = 128: the scan applies the gated norm as it writes o (packed samples that
+    the planner splits, start states).  Matches the oracle's recurrence followed by its norm,
+    and with fp32 o the unfused pair gdn_chunk_fwd + gdn_gated_rmsnorm_fwd to fp32 rounding."""
+    lengths = [2500, 0, 700, 64, 1, 1350]
+    d = gdn_inputs.small(66, lengths, 2, 4, 128, 128, "bf16", A_log_range=(-2.0, 0.0))
+    s0 = (np.random.default_rng(67).standard_normal((len(lengths), 4, 128, 128)) * 0.05).astype(np.float32)
+    z = (np.random.default_rng(68).standard_normal((sum(lengths), 4, 128)) * 2.0).astype(np.float32)
+    if z_dt == "bf16":
+        z = oracle.round_bf16(z).astype(np.float32)
+    w = np.random.default_rng(69).uniform(0.5, 1.5, 128).astype(np.float32) if weighted else None
+    o_t = torch.float32 if o_dt == "f32" else torch.bfloat16
+    y, fin = _run_chunk_norm(d, "bf16", dev(z, z_dt), None if w is None else dev(w), 1e-6, s0, o_dtype=o_t)
+    oref, fref = _oracle_chunk(d, s0)
+    ref = oracle.gated_rmsnorm(oref, z, w, 1e-6)
+    s = assert_bf16(host(y), ref, "y", bf16_store=o_dt == "bf16")
+    assert_bf16(host(fin), fref, "final")
+    print("\nfused norm o %s z %s weight %s: %s" % (o_dt, z_dt, weighted, s))
+    if o_dt == "f32":
+        o2, _ = _run_chunk(d, "bf16", s0, o_dtype=torch.float32)
+        y2 = gdn.gdn_gated_rmsnorm_fwd(o2, dev(z, z_dt), None if w is None else dev(w), eps=1e-6)
+        torch.cuda.synchronize()
+        diff = np.abs(host(y) - host(y2))
+        assert diff.max() <= 1e-6 * max(1.0, float(np.abs(host(y2)).max())), float(diff.max())
+        print("fused vs unfused: max |diff| %.3g" % diff.max())
+
+
+def test_chunk_gated_norm_wide_v_and_fp32_paths():
+    """Shapes the scan does not fuse run the chunk forward, then the norm kernel over o in place:
+    bf16 with V = 256, and the fp32 kernel (K = V = 32)."""
+    lengths = [300, 1, 129]
+    d = gdn_inputs.small(70, lengths, 2, 4, 128, 256, "bf16")
+    z = oracle.round_bf16(np.random.default_rng(71).standard_normal((sum(lengths), 4, 256)) * 2.0)
+    z = z.astype(np.float32)
+    w = np.random.default_rng(72).uniform(0.5, 1.5, 256).astype(np.float32)
+    y, _ = _run_chunk_norm(d, "bf16", dev(z, "bf16"), dev(w), 1e-6, o_dtype=torch.float32)
+    oref, _ = _oracle_chunk(d)
+    s = assert_bf16(host(y), oracle.gated_rmsnorm(oref, z, w, 1e-6), "y V=256")
+    print("\nnorm V=256 %s" % (s,))
+
+    d = gdn_inputs.small(73, [1, 64, 65, 130], 2, 4, 32, 32, "f32")
+    z = (np.random.default_rng(74).standard_normal((260, 4, 32)) * 2.0).astype(np.float32)
+    y, _ = _run_chunk_norm(d, "f32", dev(z), None, 1e-6)
+    oref, _ = _oracle_chunk(d)
+    ref = oracle.gated_rmsnorm(oref, z, None, 1e-6)
+    # an fp32 error e in o moves the normed row by at most about 2 e / rms(row) times |silu(z)|
+    rms = np.sqrt(np.mean(oref * oref, axis=-1, keepdims=True) + 1e-6)
+    bound = 2.0 * TOL_F32_ABS / rms * np.abs(z / (1.0 + np.exp(-z.astype(np.float64)))) + 1e-6
+    err = np.abs(host(y).astype(np.float64) - ref)
+    assert np.all(err <= bound), float((err / bound).max())
+    print("norm fp32 path: worst error / bound %.3g" % float((err / bound).max()))
