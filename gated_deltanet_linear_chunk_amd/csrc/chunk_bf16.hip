@@ -315,7 +315,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   // r * Hv * V + c (Hv * V is below 2^24: it bounds v's token stride).
   auto flush_o = [&](int64_t tp, int Lp) {
     constexpr int RUNS = BV / 8;  // 8-column runs per row
-    constexpr int HT = NT / 2;    // threads of the first half
+    constexpr int HT = kNorm ? NT : NT / 2;  // threads that store (with the norm: every wave)
     const int64_t obase = (tp * a.Hv + h) * (int64_t)a.V + v0;
     const uint32_t tok32 = (uint32_t)(a.Hv * a.V);
 #pragma unroll
@@ -360,11 +360,11 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
-#pragma unroll
-        for (int off = 1; off < RUNS; off <<= 1) ss += __shfl_xor(ss, off, 64);
+        static_assert(RUNS == 16, "a row is one DPP row");
+        ss = row16_sum(ss);
         const float inv = 1.f / sqrtf(ss / (float)BV + a.eps);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = y[e] * inv * wv[e] * (zv[e] / (1.f + expf(-zv[e])));
+        for (int e = 0; e < 8; ++e) y[e] = y[e] * inv * wv[e] * silu_hw(zv[e]);
       }
       if (kMode == kOutBF16) {
         uint4 w;
@@ -384,7 +384,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   for (int64_t t0 = bos; t0 < eos; t0 += CH) {
     const int L = (int)((eos - t0) < CH ? (eos - t0) : CH);
     __syncthreads();  // every wave is done with the previous chunk's tiles
-    if (kOut && t0 > bos && wave < NW / 2) flush_o(t0 - CH, CH);  // a full chunk: only the last can be short
+    if (kOut && t0 > bos && (kNorm || wave < NW / 2)) flush_o(t0 - CH, CH);  // a full chunk: only the last can be short
 
     // ---- stash q, k, v and the prep record ---------------------------------
     // Rows past the end of a partial chunk (and v of M columns) are zeroed in
@@ -647,7 +647,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   if (kOut && bos < eos) {  // the last chunk's O
     const int64_t t_last = bos + CH * ((eos - bos - 1) / CH);
     __syncthreads();
-    if (wave < NW / 2) flush_o(t_last, (int)(eos - t_last));
+    if (kNorm || wave < NW / 2) flush_o(t_last, (int)(eos - t_last));
   }
 
 #undef GDN_PREFETCH

@@ -100,6 +100,25 @@ __device__ __forceinline__ void split_frag(const f32x4& t0, const f32x4& t1, bf1
   lo = __builtin_bit_cast(bf16x8, l);
 }
 
+// Sum over the 16 lanes of a DPP row (lanes 16j .. 16j + 15), the result in
+// every lane: partners at distance 1 and 2 (quad permutes), then the two quads
+// of each half-row (half-row mirror) and the two halves (row mirror).  Both
+// partners of a step add the same two values, so the sum has the same bits as
+// a butterfly over lane distances 1, 2, 4, 8.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));   // [2,3,0,1]
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));  // half-row mirror
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));  // row mirror
+  return x;
+}
+
+// SiLU, z * sigmoid(z) = z / (1 + 2^(-z log2 e)), with the hardware base-2
+// exponential and reciprocal (about 1 ulp each); infinities give 0 and z.
+__device__ __forceinline__ float silu_hw(float z) {
+  return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
+
 __device__ __forceinline__ int clampi(int64_t x, int64_t lo, int64_t hi) {
   return (int)(x < lo ? lo : (x > hi ? hi : x));
 }

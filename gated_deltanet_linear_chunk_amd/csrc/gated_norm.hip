@@ -78,7 +78,7 @@ __global__ void __launch_bounds__(NT) gated_norm_kernel(const To* o, const Tz* z
   const float inv = 1.f / sqrtf(ss / (float)V + eps);
   float out[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) out[i] = ov[i] * inv * w[i] * (zv[i] / (1.f + expf(-zv[i])));
+  for (int i = 0; i < 8; ++i) out[i] = ov[i] * inv * w[i] * silu_hw(zv[i]);
   if (r < rows) Vec8<Ty>::store(y + r * V + c, out);
 }
 
