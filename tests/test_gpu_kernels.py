@@ -511,3 +511,25 @@ def test_chunk_gated_norm_wide_v_and_fp32_paths():
     err = np.abs(host(y).astype(np.float64) - ref)
     assert np.all(err <= bound), float((err / bound).max())
     print("norm fp32 path: worst error / bound %.3g" % float((err / bound).max()))
+
+
+def test_chunk_gated_norm_fused_gqa_three_batched():
+    """Fused norm with three v-heads per q/k head, on batched rows (no cu_seqlens) with start
+    states: matches the oracle's recurrence per row followed by its norm."""
+    lengths = [192, 192]
+    d = gdn_inputs.small(77, lengths, 2, 6, 128, 128, "bf16", A_log_range=(-2.0, 0.0))
+    s0 = (np.random.default_rng(78).standard_normal((2, 6, 128, 128)) * 0.05).astype(np.float32)
+    z = oracle.round_bf16(np.random.default_rng(79).standard_normal((384, 6, 128)) * 2.0).astype(np.float32)
+    g, beta = _gpu_gates(d)
+    q = dev(d["q"], "bf16").reshape(2, 192, 2, 128)
+    k = dev(d["k"], "bf16").reshape(2, 192, 2, 128)
+    v = dev(d["v"], "bf16").reshape(2, 192, 6, 128)
+    y, fin = gdn.gdn_chunk_fwd_gated_norm(q, k, v, g.reshape(2, 192, 6), beta.reshape(2, 192, 6),
+                                          dev(z, "bf16").reshape(2, 192, 6, 128), eps=1e-6,
+                                          initial_state=dev(s0), o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    oref, fref = _oracle_chunk(d, s0)
+    ref = oracle.gated_rmsnorm(oref, z, None, 1e-6)
+    s = assert_bf16(host(y).reshape(384, 6, 128), ref, "y")
+    assert_bf16(host(fin), fref, "final")
+    print("\nfused norm gqa 3 batched: %s" % (s,))

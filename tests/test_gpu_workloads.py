@@ -104,6 +104,38 @@ def test_chunk_only_packed_workload():
         assert_bf16(fh[n, h], fref[0, 0], "final unit %d,%d" % (n, h))
 
 
+def test_chunk_gated_norm_packed_workload():
+    """The packed workload through gdn_chunk_fwd_gated_norm (the norm applied in the scan's
+    write-out), bf16 z and a weight: sampled (sample, head) units against the oracle's recurrence
+    and norm, and every output bit for bit against gdn_chunk_fwd followed by the norm kernel."""
+    w = gdn_inputs.WORKLOADS["packed_varlen_bf16_T8192_N8_Hv32_K128"]
+    d = gdn_inputs.draw(w)
+    rng = np.random.default_rng(76)
+    z = oracle.round_bf16(rng.standard_normal((w.total_tokens, w.Hv, w.V)) * 2.0).astype(np.float32)
+    nw = rng.uniform(0.5, 1.5, w.V).astype(np.float32)
+    g, beta = gdn.gdn_gate_fwd(dev(d["a"]), dev(d["b"]), dev(d["A_log"]), dev(d["dt_bias"]))
+    q, k, v = dev(d["q"], "bf16")[None], dev(d["k"], "bf16")[None], dev(d["v"], "bf16")[None]
+    cu_dev = dev(d["cu_seqlens"], "i32")
+    zt, wt = dev(z, "bf16")[None], dev(nw)
+    y, fin = gdn.gdn_chunk_fwd_gated_norm(q, k, v, g[None], beta[None], zt, norm_weight=wt, eps=1e-6,
+                                          cu_seqlens=cu_dev, cu_seqlens_host=d["cu_seqlens"],
+                                          o_dtype=torch.float32)
+    o2, fin2 = gdn.gdn_chunk_fwd(q, k, v, g[None], beta[None], cu_seqlens=cu_dev,
+                                 cu_seqlens_host=d["cu_seqlens"], o_dtype=torch.float32)
+    y2 = gdn.gdn_gated_rmsnorm_fwd(o2, zt, wt, eps=1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    assert torch.equal(fin, fin2)
+    go, bo = oracle.gates(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    cu = d["cu_seqlens"]
+    yh = host(y[0])
+    for n, h in _units(len(cu) - 1, w.Hv, 4, 3):
+        oref, _ = _oracle_unit(d["q"], d["k"], d["v"], go, bo, cu, n, h, w.Hqk, w.Hv)
+        a, b = int(cu[n]), int(cu[n + 1])
+        ref = oracle.gated_rmsnorm(oref[:, 0], z[a:b, h], nw, 1e-6)
+        assert_bf16(yh[a:b, h], ref, "y unit %d,%d" % (n, h))
+
+
 def test_long_segmented_workload():
     """32768 tokens in 8 segments: pass 1, fp32 chain, pass 2 == unsegmented, == oracle."""
     w = gdn_inputs.WORKLOADS["long_segmented_bf16_T32768_P8_Hv32_K128"]
