@@ -309,6 +309,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   // the first half of the waves: the two waves that share a SIMD finish a
   // chunk out of step, the later one (of the second half) setting the pace,
   // so the stores go to the waves that would otherwise wait at the barrier.
+  // With the gated norm (kNorm) every wave stores: the norm's arithmetic
+  // outweighs the slack of the first half alone.
   // Rows past the end of the chunk store a second copy of its last row
   // instead, so that every store is unconditional.  Address: uniform element
   // offset of (chunk start, head, slice) plus a lane's 32-bit offset
