@@ -218,3 +218,10 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(4, 8)
     with pytest.raises(ValueError):
         gdn.gdn_conv1d_fwd(x, torch.zeros(8, 4))
+    q = torch.zeros(1, 64, 2, 128, dtype=torch.bfloat16)
+    v = torch.zeros(1, 64, 4, 128, dtype=torch.bfloat16)
+    g = torch.zeros(1, 64, 4)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        gdn.gdn_chunk_fwd_gated_norm(q, q, v, g, g, v)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        gdn.gdn_gated_rmsnorm_fwd(v, v)
