@@ -69,6 +69,12 @@ bool plan_split(const int32_t* cu, int32_t N, int32_t H_v, int32_t V, bool has_s
     return makespan(blocks, cus);
   };
   const double base = pass2(chunks);
+  // Every chunk runs in pass 2, and no schedule beats the work spread evenly
+  // over the units: a run already within 15% of that is not split (and the
+  // search below, costly for thousands of samples, is skipped).
+  double work = 0.0;
+  for (int64_t c : chunks) work += (double)c * H_v * tiles2;
+  if (0.85 * base < work / cus) return false;
   double best = base;
   int64_t best_seg = 0;
   for (int parts = 2; parts <= 16; ++parts) {
