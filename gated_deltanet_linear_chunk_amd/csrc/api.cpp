@@ -285,6 +285,9 @@ gdn_status gdn_chunk_fwd_gated_norm(const void* q, const void* k, const void* v,
   if (V != 32 && V != 64 && V != 128 && V != 256 && V != 512) return GDN_ERR_UNSUPPORTED;
   const int64_t total = cu_seqlens ? T : (int64_t)B * T;
   if (total > 0 && !z) return GDN_ERR_NULL_POINTER;
+  // the norm kernel's own limit, checked before anything is enqueued
+  const int64_t rpb = 256 / (V / 8);
+  if (total > 0 && (total * H_v + rpb - 1) / rpb > INT32_MAX) return GDN_ERR_UNSUPPORTED;
   const gdn_status st = chunk_fwd_run(q, k, v, in_dt, q_token_stride, k_token_stride, v_token_stride, g,
                                       beta, scale, initial_state, cu_seqlens, cu_seqlens_host, n_seqs, B, T,
                                       H_qk, H_v, K, V, o, o_dt, final_state, workspace, workspace_bytes,

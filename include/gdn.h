@@ -13,8 +13,11 @@
  * and the segment-wise affine state passing S_end = M S_start + b with a chain
  * of (M, b) reduced in fp32 (sglang fork PR "Qwen3.5 cp - #1", PR body and
  * Patches; prime-rl PR "feat: hybrid CP for Qwen3.5 MoE", Approach and
- * Communication-cost table), run here as a single-GPU segment-parallel scan.
- * The state is stored K x V (prime-rl PR, Summary); the pages' V x K form
+ * Communication-cost table), run here as a single-GPU segment-parallel scan;
+ * the one-token recurrent step on cached states (sglang PR, the decode path
+ * after the prefill); and the output RMS norm gated by z that follows the rule
+ * (LlamaFactory PR, Design), on its own or applied by the chunk scan as it
+ * writes o.  The state is stored K x V (prime-rl PR, Summary); the pages' V x K form
  * S (I - beta k k^T) is its transpose.
  *
  * Conventions for every entry point:
