@@ -112,6 +112,8 @@ def test_chunk_gated_norm_validation(lib):
     assert _chunk_norm(lib, z=None) == NULLP  # fused path (bf16, V = 128)
     assert _chunk_norm(lib, z=None, V=256) == NULLP  # chunk forward + norm kernel
     assert _chunk_norm(lib, in_dt=0, K=32, V=96) == UNSUP  # no norm kernel for V = 96
+    # more norm rows than the norm kernel's grid holds: refused before the chunk forward is enqueued
+    assert _chunk_norm(lib, V=256, T=(1 << 31) - 1) == UNSUP
     assert _chunk_norm(lib, q=None) == NULLP  # the chunk forward's own checks still apply
     assert _chunk_norm(lib, K=64) == UNSUP
     assert _chunk_norm(lib, ws=None) == NULLP
