@@ -127,10 +127,7 @@ size_t gdn_chunk_fwd_workspace_bytes(gdn_dtype in_dt, int64_t total_tokens, int3
                                      int32_t H_v, int32_t K, int32_t V) {
   if (in_dt != GDN_BF16 || total_tokens < 0 || n_seqs < 0 || H_v < 1 || K < 1 || V < 1) return 0;
   const size_t plain = tbuf_bytes(total_tokens, n_seqs, H_v);
-  // pass-1 workgroups per segment are at least H_v (K + V) / 256 for any
-  // number of q/k heads, so this bounds the pass-1 segments of every plan
-  const int blocks1_min = std::max(1, (int)(((int64_t)H_v * (K + V)) / 256));
-  const int pmax = gdn::max_prefix_segments(blocks1_min, device_cus());
+  const int pmax = gdn::max_prefix_segments(H_v, V, device_cus());
   if (pmax == 0 || n_seqs < 1) return plain;
   return std::max(plain, split_workspace_bytes(total_tokens, n_seqs + pmax, pmax, H_v, K, V));
 }
@@ -209,9 +206,7 @@ static gdn_status chunk_fwd_run(const void* q, const void* k, const void* v, gdn
   }
   if (in_dt == GDN_BF16 && cu_seqlens && cu_seqlens_host && total > 0) {
     gdn::SplitPlan plan;
-    const int blocks2 = gdn::chunk_scan_blocks(H_qk, H_v, V, false);
-    const int blocks1 = gdn::chunk_scan_blocks(H_qk, H_v, V, true);
-    if (gdn::plan_split(cu_seqlens_host, N, blocks2, blocks1, initial_state != nullptr, device_cus(), plan) &&
+    if (gdn::plan_split(cu_seqlens_host, N, H_v, V, initial_state != nullptr, device_cus(), plan) &&
         workspace_bytes >= split_workspace_bytes(total, plan.n_seg, plan.n_prefix, H_v, K, V)) {
       // ---- segment-split run (see plan_split) ----------------------------------
       unsigned char* w = static_cast<unsigned char*>(workspace);
@@ -231,7 +226,7 @@ static gdn_status chunk_fwd_run(const void* q, const void* k, const void* v, gdn
       a.tbuf = rec;
       a.cu = ints;
       a.n_seqs = plan.n_seg;
-      e = gdn::launch_chunk_prep(a, stream);  // one set of records serves both passes
+      e = gdn::launch_chunk_prep(a, 1, stream);  // one set of records serves both passes
       if (e != hipSuccess) return GDN_ERR_HIP;
       gdn::ChunkArgs p1 = a;
       p1.seq_order = ints + plan.off_pre();
@@ -280,8 +275,7 @@ gdn_status gdn_chunk_fwd_gated_norm(const void* q, const void* k, const void* v,
                                     hipStream_t stream) {
   if (!valid_dtype(in_dt) || !valid_dtype(o_dt) || !valid_dtype(z_dt)) return GDN_ERR_BAD_DTYPE;
   if (!(eps >= 0.f)) return GDN_ERR_BAD_SHAPE;
-  if (in_dt == GDN_BF16 && H_qk >= 1 && H_v >= 1 && H_v % H_qk == 0 && K == 128 &&
-      gdn::chunk_scan_fuses_norm(H_qk, H_v, V)) {
+  if (in_dt == GDN_BF16 && V == 128) {
     const FusedNorm norm{z, z_dt == GDN_BF16 ? 1 : 0, norm_weight, eps};
     return chunk_fwd_run(q, k, v, in_dt, q_token_stride, k_token_stride, v_token_stride, g, beta, scale,
                          initial_state, cu_seqlens, cu_seqlens_host, n_seqs, B, T, H_qk, H_v, K, V, o,

@@ -1,45 +1,37 @@
 // chunk_bf16.hip -- serial chunk scan of the gated delta rule on gfx950 MFMA.
 //
-// One workgroup (NW waves) owns one (sequence or segment, q/k head, 32 NW
-// state columns) and walks its 64-token chunks in order.  Its columns are
-// taken from the v-heads that read that q/k head (two v-heads of 128 columns
-// for NW = 8 and V = 128), so the chunk's q and k are staged once for all of
-// them.  Wave w holds the K x 32 fp32 state of its 32 columns in registers,
-// as sixteen 16 x 16 accumulator tiles.  What about a chunk does not depend on
-// the state -- T diag(beta) (T = (I + A)^{-1}, the UT transform), the
-// in-chunk cumulative gate G and the decays -- comes precomputed from the
-// prep kernel (chunk_prep.hip).  Per chunk (local tokens r, s), each wave
-// then does, for its own columns and without any further synchronisation:
-//   R  = V - diag(e^G) K S
-//   U  = T diag(beta) R                           (= U0 - W S)
+// One workgroup (8 waves) owns one (sequence or segment, v-head, 128-column
+// slice of V) and walks its 64-token chunks in order.  The K x 128 fp32 state
+// never leaves the registers: wave w holds state columns 16 w .. 16 w + 15 as
+// eight 16 x 16 accumulator tiles.  Everything about a chunk that does not
+// depend on the state -- T diag(beta) (T = (I + A)^{-1}, the UT transform),
+// the masked Q K^T, e^G and the decays -- comes precomputed from the prep
+// kernel (chunk_prep.hip).  Per chunk (local tokens r, s), each wave then
+// does, for its own columns and without any further synchronisation:
+//   U  = T diag(beta) (V - diag(e^G) K S)      (= U0 - W S)
+//   O  = diag(e^G) Q S + P U
 //   S <- e^{G_last} S + K^T diag(e^{G_last - G}) U
-//   O^T = diag(e^G) S^T Q^T + U^T P^T,  P = lower(Q K^T . e^{G_r - G_s})
-// which is the token recurrence regrouped by chunk.  The masked Q K^T is
-// formed by each wave from the q and k in LDS (its accumulator tiles are the
-// B operand of U^T P^T as they stand).  O comes out transposed, a lane holding
-// four consecutive columns of one token, and goes to global memory from the
-// registers (16-byte stores), after the next chunk's first barrier.
-//
-// Operand order.  A pair of vertically adjacent accumulator tiles is an MFMA
-// operand whose k index runs in the slot order of device_common.h
-// (slot_row / row_slot).  The state's rows are kept permuted so that this
-// order is the natural one on the q/k side: accumulator row p of the state
-// holds key index row_slot(p), so the products against S read q and k as
-// plain 16-byte runs of a token's row.  Tokens, where they are the k index
-// (T diag(beta) R, U^T P^T, K^T U), run in the slot order on both sides: the
-// prep record stores T diag(beta)'s columns that way, and the K^T tile its
-// tokens.
+// which is the token recurrence regrouped by chunk.  Two barriers per chunk:
+// one before the shared tiles are overwritten, one after they are filled.
+// The next chunk's q, k, v and prep record are fetched into registers while
+// the current chunk computes; O goes through its own LDS tile so that its
+// global stores are 16-byte vectors, stored by the first half of the waves
+// after the next chunk's first barrier.
 //
 // Precision: every fp32 quantity that meets the matrix cores is a bf16 pair
 // hi + lo (~16 significant bits), multiplied against exact bf16 data (q, k)
 // or against another pair (hi*hi + hi*lo + lo*hi): S against K and Q, T diag(beta)
-// against R, U against P, the decayed U against K.
+// against V - e^G K S, P against U, the decayed U against K.
 //
-// LDS (bf16 unless noted): sQ, sK [64][136] (token rows), sKt [128][72] (row
-// p: key index row_slot(p), tokens in slot order), sV [64][32 NW + 8] (v of
-// the workgroup's columns), every row padded by 16 bytes, and
-// two buffers of the prep records of the workgroup's v-heads, filled by direct
-// global-to-LDS loads one chunk ahead.
+// LDS (bf16 unless noted).  The tiles read as MFMA operands (Q, K, K^T,
+// T diag(beta), P) store each 32-wide block of their K index in fragment
+// order (index 16 h + 4 g + j at 8 g + 4 h + j), so the eight values a lane
+// feeds one MFMA are contiguous and come in one 16-byte read, and swizzle
+// the 16-byte units of a row so that those reads meet no bank conflicts
+// (tile_pos, frag16 below):
+//   sQ [64][128], sK [64][128], sKt [128][64] (K^T), sP [2][64][64] (hi, lo),
+//   sT2 [2][64][64] (T diag(beta) hi/lo); sVt [128][72] (V^T of this slice,
+//   rows padded by 16 B), sO fp32 [64][132], gamma[64], dec[64] fp32.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -49,45 +41,50 @@ namespace {
 
 constexpr int CH = 64;
 constexpr int KD = 128;
-// Row pitches (bf16 elements): every row is padded by 16 bytes, so the 16
-// rows of a fragment read (one 16-byte unit each, at the same unit index)
-// start four banks apart and fall on distinct banks of the 64, and every
-// fragment of a tile is one base address plus an immediate offset.
-constexpr int QP = KD + 8;   // q, k: 128 key indices per token row
-constexpr int KTP = CH + 8;  // K^T: 64 tokens per row
-// Parts of a prep record (kernels.h): T diag(beta) hi and lo (the first
-// TB_BYTES) and the gates G, gamma, dec (the last GX_BYTES).
-constexpr int TB_BYTES = REC_G;
-constexpr int GX_BYTES = PREP_RECORD_BYTES - REC_G;
-static_assert(TB_BYTES % 1024 == 0 && GX_BYTES % 16 == 0 && REC_G == 12 * 1024, "record parts");
+constexpr int BV = 128;
 
+constexpr int QP = KD;      // Q, K: 128 bf16 (256 bytes) per row, no padding
+constexpr int TP = CH;      // K^T, T diag(beta), P: 64 bf16 (128 bytes) per row
+constexpr int VTP = CH + 8; // V^T (not an MFMA operand): padded rows
+constexpr int OP = BV + 4;  // fp32 O tile pitch
+
+constexpr int OFF_Q = 0;
+constexpr int OFF_K = OFF_Q + CH * QP * 2;
+constexpr int OFF_KT = OFF_K + CH * QP * 2;
+constexpr int OFF_VT = OFF_KT + KD * TP * 2;
+constexpr int OFF_P = OFF_VT + BV * VTP * 2;
+constexpr int OFF_T2 = OFF_P + 2 * CH * TP * 2;
+constexpr int OFF_O = OFF_T2 + 2 * CH * TP * 2;
+constexpr int OFF_GAM = OFF_O + CH * OP * 4;
+constexpr int OFF_DEC = OFF_GAM + CH * 4;
+constexpr int LDS_BYTES = OFF_DEC + CH * 4;
+static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+
+// 16-byte units of a prep record: T diag(beta) hi, lo (2 x 10 tiles x 32),
+// gamma and dec (2 x 16), then P hi, lo (2 x 10 x 32).  Forward scans read all
+// of it, state-only scans the part before P.
+constexpr int REC_TB_UNITS = 2 * 10 * 32;
+constexpr int REC_STATE_UNITS = REC_TB_UNITS + 2 * 16;
+constexpr int REC_UNITS = REC_STATE_UNITS + 2 * 10 * 32;
+static_assert(REC_UNITS * 16 == PREP_RECORD_BYTES, "record layout");
+static_assert(REC_TB_UNITS * 16 == PREP_REC_GAM && REC_STATE_UNITS * 16 == PREP_REC_P, "record layout");
+
+// Kernel modes: forward with fp32 o, forward with bf16 o, state only / pass 1.
 enum { kOutF32 = 0, kOutBF16 = 1, kPass1 = 2 };
 
-template <int NW>
-struct Lds {
-  static constexpr int NH = NW == 8 ? 2 : 1;  // v-heads a workgroup's columns can span
-  static constexpr int Q = 0;
-  static constexpr int K = Q + CH * QP * 2;
-  static constexpr int KT = K + CH * QP * 2;
-  static constexpr int VP = 32 * NW + 8;  // v: the workgroup's 32 NW columns per token row
-  static constexpr int VT = KT + KD * KTP * 2;
-  // P^T operand fragments per v-head: 6 (m, tt) blocks, hi and lo, 1 KB each
-  static constexpr int PF = VT + CH * VP * 2;
-  static constexpr int NRM = PF + NH * 12 * 1024;  // gated norm: per-wave row sums, [2][NW][64] fp32
-  static constexpr int TB = NRM + 2 * NW * 64 * 4;   // T diag(beta) of the v-heads: one buffer
-  static constexpr int GX = TB + NH * TB_BYTES;      // G, gamma, dec of the v-heads: two buffers
-  static constexpr int BYTES = GX + 2 * NH * GX_BYTES;
-  static_assert(BYTES <= 160 * 1024, "LDS budget");
-  static_assert(TB % 1024 == 0 && GX % 16 == 0, "record buffers aligned for direct loads");
+struct Pass1 {
+  int m_tiles;   // leading tiles of a (segment, head) that evolve M columns (v = 0, S0 = I)
+  float* m_out;  // [n_seqs, Hv, K, K]
 };
 
 // Workgroups go to the eight XCDs in turn by id, each XCD with its own L2.
-// The grid is 1-D over logical blocks (workgroup of a q/k head fastest, then
-// q/k head, then sequence); a group of `group` consecutive logical blocks
-// reads the same q/k.  When the groups split evenly over the XCDs, physical
-// id L runs member (L / 8) % group of group (L % 8) + 8 (L / 8 / group), so
-// every member of a group has the same L % 8 (one XCD, one L2 copy of its
-// inputs) and groups still start in logical order, eight at a time.
+// The grid is 1-D over logical blocks (tile fastest, then v-head, then
+// sequence); a group of `group` consecutive logical blocks reads the same q/k
+// (the v-heads of one q/k head with all their tiles) and, within a head, the
+// same records.  When the groups split evenly over the XCDs, physical id L
+// runs member (L / 8) % group of group (L % 8) + 8 (L / 8 / group), so every
+// member of a group has the same L % 8 (one XCD, one L2 copy of its inputs)
+// and groups still start in logical order, eight at a time.
 __device__ __forceinline__ int xcd_grouped(int L, int n, int group) {
   const int groups = n / group;
   if (n % group != 0 || groups % 8 != 0) return L;
@@ -102,92 +99,97 @@ __device__ __forceinline__ void zero4(f32x4& x) { x[0] = x[1] = x[2] = x[3] = 0.
 // the registers in flight) to one short group of products.
 #define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-// The thread index as a value the compiler cannot see through: lane-derived
-// addresses computed from it inside the chunk loop stay there (a few cheap
-// integer operations per phase) instead of being hoisted out of the loop and
-// held in registers across it.
-__device__ __forceinline__ int fresh_id(int x) {
-  asm volatile("" : "=v"(x) : "0"(x));
-  return x;
-}
-#define LANE_IDS()                                                        \
-  const int tid = fresh_id(tid0);                                         \
-  const int lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;             \
-  (void)lane, (void)g4, (void)c16
-
-// Workgroup barrier that orders LDS accesses only: waits for this wave's LDS
-// operations, not for its global loads and stores in flight.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+// tile index (0..9) -> (block row i, block column j) of the lower 4 x 4 tiles
+__device__ __forceinline__ void tile_ij(int t, int& i, int& j) {
+  i = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
+  j = t - (i * (i + 1)) / 2;
 }
 
-// 16-byte unit of a token row of q or k: key indices 8 unit .. + 7.
-__device__ __forceinline__ bf16x8 frag_row128(const uint16_t* tile, int row, int unit) {
-  return *reinterpret_cast<const bf16x8*>(tile + row * QP + 8 * unit);
-}
-// 16-byte unit of a K^T row: operand slots 8 unit .. + 7.  The units of a
-// row are swizzled by its 32-row block (u -> u ^ (row / 32)), which is uniform
-// over a fragment read and keeps the stash's transposed stores, whose 16
-// lanes write rows 32 apart in groups of four, on distinct banks.
-__device__ __forceinline__ int kt_pos(int row, int slot) {
-  return ((((slot >> 3) ^ (row >> 5)) & 7) << 3) | (slot & 7);
-}
-__device__ __forceinline__ bf16x8 frag_kt(const uint16_t* tile, int row, int unit) {
-  return *reinterpret_cast<const bf16x8*>(tile + row * KTP + 8 * (unit ^ (row >> 5)));
+// Position of K index c inside its 32-wide block in the fragment order
+// (c = 16 h + 4 g + j -> 8 g + 4 h + j); groups of four stay together.
+__device__ __forceinline__ int frag_pos(int c) {
+  return (c & ~31) + 8 * ((c >> 2) & 3) + 4 * ((c >> 4) & 1) + (c & 3);
 }
 
-// Columns of wave w of workgroup wgi of q/k head hq: its v-head, its first
-// column, and (segment pass 1) whether they are M columns (state started at
-// the identity, no values) or b columns.  In pass 1 a v-head contributes
-// K + V columns, [M | b]; otherwise V.
-struct WaveCols {
-  int head, col;
-  bool m;
-};
-template <bool kP1, int NW>
-__device__ __forceinline__ WaveCols wave_cols(int w, int wgi, int hq, int G, int V) {
-  const int gc = wgi * 32 * NW + 32 * w;
-  const int per = kP1 ? KD + V : V;
-  WaveCols r;
-  r.head = hq * G + gc / per;
-  const int within = gc % per;
-  r.m = kP1 && within < KD;
-  r.col = (kP1 && !r.m) ? within - KD : within;
-  return r;
+// The LDS serves 64 four-byte banks per cycle.  Operand tiles have unpadded
+// rows (16 sixteen-byte units per 256-byte row of Q and K, 8 per 128-byte
+// row of K^T, T diag(beta) and P) and store unit u of a row at u ^ swz(row).
+// A fragment read puts 16 consecutive rows at one unit: the swizzle sends
+// them to 16 different units of the 64 banks, so the read runs without
+// conflicts (unit ^ row over 16 rows; for 128-byte rows, two rows share a
+// unit index but sit in the two halves of the banks).  The extra flip by
+// row bit 4 of Q and K spreads the stash's 32 even rows over 16 units.
+__device__ __forceinline__ int swz16(int row) { return (row & 15) ^ ((row >> 4) & 1); }
+__device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
+
+// Element offset of K index c (fragment order, then swizzled) in a row of a
+// 128-wide (W16) or 64-wide tile.
+template <bool W16>
+__device__ __forceinline__ int tile_pos(int row, int c) {
+  const int p = frag_pos(c);
+  return (((p >> 3) ^ (W16 ? swz16(row) : swz8(row))) << 3) | (p & 7);
+}
+
+// A or B fragment of k-step k0 (a multiple of 32) for row `row` of an
+// operand tile: one 16-byte read of unit k0 / 8 + g4.
+template <bool W16>
+__device__ __forceinline__ bf16x8 frag16(const uint16_t* tile, int row, int k0, int g4) {
+  constexpr int pitch = W16 ? QP : TP;
+  const int u = ((k0 >> 3) + g4) ^ (W16 ? swz16(row) : swz8(row));
+  return *reinterpret_cast<const bf16x8*>(tile + row * pitch + 8 * u);
+}
+
+// Eight consecutive K indices c .. c + 7 (c a multiple of 8) of row `row`
+// of a tile, as two 8-byte stores.
+template <bool W16>
+__device__ __forceinline__ void store8_frag(uint16_t* tile, int row, int c, const u32x4& v) {
+  uint16_t* rb = tile + row * (W16 ? QP : TP);
+  *reinterpret_cast<u32x2*>(rb + tile_pos<W16>(row, c)) = u32x2{v[0], v[1]};
+  *reinterpret_cast<u32x2*>(rb + tile_pos<W16>(row, c + 4)) = u32x2{v[2], v[3]};
 }
 
 template <int kMode, int NW, bool kNorm>
-__global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, float* m_out) {
-  using LD = Lds<NW>;
+__global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 p1) {
   constexpr int NT = NW * 64;
-  constexpr bool kP1 = kMode == kPass1;
-  constexpr bool kOut = !kP1;
-  constexpr int NPAIR = 512 / NT;  // (row pair, 8 key indices) units of q and of k per thread
-  static_assert(NPAIR * NT == 512, "thread layout");
+  constexpr int CPW = BV / NW;     // state columns per wave
+  constexpr int NCT = CPW / 16;    // 16-column tiles per wave
+  constexpr int NPAIR = 512 / NT;  // (row pair, 8 columns) units per thread per matrix
+  constexpr bool kOut = kMode != kPass1;
+  constexpr int RUNITS = kOut ? REC_UNITS : REC_STATE_UNITS;  // record units this mode reads
+  constexpr int NREC = (RUNITS + NT - 1) / NT;                 // record units per thread
+  static_assert(CPW % 16 == 0 && NW * CPW == BV, "wave layout");
   static_assert(!kNorm || kOut, "the norm applies to outputs");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + LD::Q);
-  uint16_t* sK = reinterpret_cast<uint16_t*>(smem + LD::K);
-  uint16_t* sKt = reinterpret_cast<uint16_t*>(smem + LD::KT);
-  uint16_t* sV = reinterpret_cast<uint16_t*>(smem + LD::VT);
-  unsigned char* sPf = smem + LD::PF;
-  float* sNrm = reinterpret_cast<float*>(smem + LD::NRM);
-  unsigned char* sTb = smem + LD::TB;
-  unsigned char* sGx = smem + LD::GX;
+  uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + OFF_Q);
+  uint16_t* sK = reinterpret_cast<uint16_t*>(smem + OFF_K);
+  uint16_t* sKt = reinterpret_cast<uint16_t*>(smem + OFF_KT);
+  uint16_t* sVt = reinterpret_cast<uint16_t*>(smem + OFF_VT);
+  uint16_t* sP = reinterpret_cast<uint16_t*>(smem + OFF_P);
+  uint16_t* sT2 = reinterpret_cast<uint16_t*>(smem + OFF_T2);
+  float* sO = reinterpret_cast<float*>(smem + OFF_O);
+  float* sGam = reinterpret_cast<float*>(smem + OFF_GAM);
+  float* sDec = reinterpret_cast<float*>(smem + OFF_DEC);
 
-  const int tid0 = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);  // uniform: scalar registers
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int g4 = lane >> 4;
+  const int c16 = lane & 15;
 
-  const int G = a.Hv / a.Hqk;
-  const int wpg = a.n_tiles;  // workgroups per (sequence, q/k head)
-  const int lb = xcd_grouped((int)blockIdx.x, (int)gridDim.x, wpg);
-  const int wgi = lb % wpg;
-  const int hq = (lb / wpg) % a.Hqk;
-  const int zb = lb / (wpg * a.Hqk);
+  bool m_mode = false;
+  const int n_tiles = a.n_tiles;
+  const int lb = xcd_grouped((int)blockIdx.x, (int)gridDim.x, n_tiles * (a.Hv / a.Hqk));
+  int tile = lb % n_tiles;
+  if (kMode == kPass1) {
+    m_mode = tile < p1.m_tiles;
+    if (!m_mode) tile -= p1.m_tiles;
+  }
+  const int v0 = tile * BV;
+  const int h = (lb / n_tiles) % a.Hv;
+  const int zb = lb / (n_tiles * a.Hv);
   const int seq = a.seq_order ? a.seq_order[zb] : zb;
+  const int hq = h / (a.Hv / a.Hqk);
   int64_t bos, eos;
   if (a.cu) {
     bos = clampi(a.cu[seq], 0, a.Ttot);
@@ -196,15 +198,10 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, float*
     bos = (int64_t)seq * a.row_len;
     eos = bos + a.row_len;
   }
-  const WaveCols me = wave_cols<kP1, NW>(wave, wgi, hq, G, a.V);
-  const int head0 = wave_cols<kP1, NW>(0, wgi, hq, G, a.V).head;
-  const int nh = wave_cols<kP1, NW>(NW - 1, wgi, hq, G, a.V).head - head0 + 1;
-  const int h = me.head;
-  const int hslot = h - head0;
-
-  // start state of this wave's columns: identity (M columns), zero, or rows of V
+  const bool load_v = !m_mode;
+  // start state of this head: identity (M columns), zero, or K x V rows of V
   const float* s0p = nullptr;
-  if (!me.m) {
+  if (!m_mode) {
     if (a.s0_ref) {
       const int r = a.s0_ref[seq];
       if (r >= 0)
@@ -215,380 +212,317 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, float*
       s0p = a.s0 + ((int64_t)seq * a.Hv + h) * (int64_t)KD * a.V;
     }
   }
+  const int col_base = v0 + wave * CPW;
 
-  // ---- state: S[ct][pt][e] = S[row_slot(16 pt + 4 g4 + e)][col + 16 ct + c16]
-  f32x4 S[2][8];
-  {
-  LANE_IDS();
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-    for (int pt = 0; pt < 8; ++pt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = row_slot(16 * pt + 4 * g4 + e);
-        const int col = me.col + 16 * ct + c16;
-        float s = 0.f;
-        if (me.m)
-          s = (d == col) ? 1.f : 0.f;
-        else if (s0p)
-          s = s0p[(int64_t)d * a.V + col];
-        S[ct][pt][e] = s;
-      }
-  }
-
-  // ---- prefetch of q, k and v into registers ---------------------------------
-  // q/k unit u = tid + NT j covers token rows 2 (u >> 4) + {0, 1} and key
-  // indices 8 (u & 15) .. + 7: 16 consecutive lanes read one token's 256
-  // contiguous bytes, and a lane holds two adjacent tokens, which the K^T
-  // stash packs into 4-byte words.  v unit u = tid + NT j (j = 0..3) covers
-  // token row u / (4 NW) and the workgroup's columns 8 (u % (4 NW)) .. + 7.
-  // Every load is unconditional: rows past the end of the sequence re-read its
-  // last row (k and q are zeroed when stashed; v there meets zero columns of
-  // T diag(beta)); M columns have no values and re-read k.  A load's address is a uniform base at the
-  // chunk's first token plus a lane's 32-bit byte offset row * stride + column
-  // (strides stay below 2^24 elements, so row * stride is one 24-bit multiply).
+  // Prefetch units: unit u = tid + NT j (j < NPAIR) covers token rows
+  // 2 (u & 31) + {0, 1} and columns 8 (u >> 5) .. + 7, so all units of a
+  // thread share its two rows.  Lanes run along the tokens so that the
+  // transposed LDS stores (K^T, V^T) of a wave hit consecutive banks; the
+  // 16-byte global loads of the column groups of a row come from neighbouring
+  // waves and meet in the caches.
+  const int r0_pf = 2 * (tid & 31), d8_pf = (tid >> 5) * 8;
+  constexpr int kDJ = (NT / 32) * 8;  // column step between a thread's units
+  // Uniform base pointers at the sequence start.  Per chunk the prefetch moves
+  // them to the chunk's first token (scalar arithmetic) and adds a lane's
+  // 32-bit byte offset, row * stride + column, with row clamped to the chunk's
+  // last valid token; the host keeps strides below 2^24 elements, so the
+  // row * stride product is one 24-bit multiply.
   const char* kbase = (const char*)((const uint16_t*)a.k + bos * a.k_stride + hq * KD);
   const char* qbase = kOut ? (const char*)((const uint16_t*)a.q + bos * a.q_stride + hq * KD) : kbase;
   const int64_t q_stride = kOut ? a.q_stride : a.k_stride;
-  const uint32_t ks32 = (uint32_t)a.k_stride, qs32 = (uint32_t)q_stride;
-  const char* vbase = (const char*)((const uint16_t*)a.v + bos * a.v_stride);
-  const uint32_t vs32 = (uint32_t)a.v_stride;
-  constexpr int NVU = 4 * NW;  // 16-byte v units per token row of the workgroup
-  static_assert(NT % NVU == 0, "a thread's v units share their columns");
-  // element offset of the columns of this thread's v units inside a token row
-  // (every unit tid + NT j has the same columns), or -1 for M columns (no values)
-  const int v_col = [&]() -> int {
-    const int cg = tid0 % NVU;  // 8-column group of the workgroup
-    const WaveCols wc = wave_cols<kP1, NW>(cg >> 2, wgi, hq, G, a.V);
-    return wc.m ? -1 : wc.head * a.V + wc.col + 8 * (cg & 3);
-  }();
-
-  // The next chunk's loads are issued one at a time between the compute
-  // phases (pf_kq: index 4 j + 2 which + row, which 0 = k, 1 = q; pf_v: index
-  // 2 j + row), so that the vector memory path works through them in the
-  // background instead of in one burst that stalls the issuing waves.
-  u32x4 pk[NPAIR][2], pq[NPAIR][2], pv[4];
-  auto pf_row = [&](int64_t T0, int r0, int row) -> uint32_t {
-    const int L_ = (int)((eos - T0) < CH ? (eos - T0) : CH);
-    const int r = r0 + row;
-    return (uint32_t)(r < L_ ? r : L_ - 1);
-  };
-  // one 16-byte load at uniform base B (chunk start) + lane byte offset
-  auto ld16 = [](const char* B, uint32_t row, uint32_t s32, uint32_t col) -> u32x4 {
-    return *reinterpret_cast<const u32x4*>(B + (uint32_t)(2u * (__umul24(row, s32) + col)));
-  };
-  auto pf_kq = [&](int64_t T0, int idx) {
-    LANE_IDS();
-    const int jj = idx >> 2, which = (idx >> 1) & 1, row = idx & 1;
-    const int u = tid + NT * jj;
-    const uint32_t d = (uint32_t)((u & 15) * 8);
-    const uint32_t r = pf_row(T0, 2 * (u >> 4), row);
-    if (which == 0)
-      pk[jj][row] = ld16(kbase + 2 * (T0 - bos) * a.k_stride, r, ks32, d);
-    else if (kOut)
-      pq[jj][row] = ld16(qbase + 2 * (T0 - bos) * q_stride, r, qs32, d);
-  };
-  auto pf_v = [&](int64_t T0, int idx) {
-    LANE_IDS();
-    const int u = tid + NT * idx;
-    const uint32_t r = pf_row(T0, u / NVU, 0);
-    const int vc = v_col;
-    if (vc < 0)
-      pv[idx] = ld16(kbase + 2 * (T0 - bos) * a.k_stride, r, ks32, 0u);
-    else
-      pv[idx] = ld16(vbase + 2 * (T0 - bos) * a.v_stride, r, vs32, (uint32_t)vc);
-  };
-
-  // ---- prep records of the workgroup's v-heads: direct global-to-LDS loads ----
-  // The records of v-heads head0 .. head0 + nh - 1 of one chunk slot are
-  // adjacent in the workspace; wave w's i-th load fills 1 KB of the buffer at
-  // (i NW + w) KB, lane l its 16 bytes at l * 16.
-  // The records of v-heads head0 .. head0 + nh - 1 of one chunk slot are
-  // adjacent in the workspace.  T diag(beta) goes to its single buffer after
-  // the barrier that follows its last use in the chunk before, the gates to
-  // their double buffer one chunk ahead; wave w's i-th load of a part fills
-  // 1 KB at (i NW + w) KB, lane l its 16 bytes at l * 16.
-  const unsigned char* recg = (const unsigned char*)a.tbuf + (int64_t)head0 * PREP_RECORD_BYTES;
+  // without values (M columns) the v loads re-read k and are discarded
+  const char* vbase = load_v ? (const char*)((const uint16_t*)a.v + bos * a.v_stride + (int64_t)h * a.V + v0) : kbase;
+  const int64_t v_stride = load_v ? a.v_stride : a.k_stride;
+  const uint32_t ks32 = (uint32_t)a.k_stride, qs32 = (uint32_t)q_stride, vs32 = (uint32_t)v_stride;
+  const unsigned char* rbase = (const unsigned char*)a.tbuf + (int64_t)h * PREP_RECORD_BYTES;
   const int64_t rslot_stride = (int64_t)a.Hv * PREP_RECORD_BYTES;
-  constexpr int kTbRounds = (LD::NH * TB_BYTES / 16 + NT - 1) / NT;
-  auto load_tb = [&](int64_t slot, int i) {
-    LANE_IDS();
-    const int blk = i * NW + wave;  // 1 KB blocks: 12 per v-head
-    const int u = blk * 64 + lane;
-    if (blk < nh * (TB_BYTES / 1024))
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(recg + slot * rslot_stride + (blk / 12) * PREP_RECORD_BYTES + 16 * (u - (blk / 12) * 768)),
-          (__attribute__((address_space(3))) void*)(sTb + blk * 1024), 16, 0, 0);
-  };
-  auto load_gx = [&](int64_t slot, int buf) {
-    LANE_IDS();
-    const int u = wave * 64 + lane;  // 48 units per v-head
-    if (wave * 64 < nh * (GX_BYTES / 16) && u < nh * (GX_BYTES / 16))
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(recg + slot * rslot_stride + (u / 48) * PREP_RECORD_BYTES + REC_G + 16 * (u % 48)),
-          (__attribute__((address_space(3))) void*)(sGx + buf * (LD::NH * GX_BYTES) + wave * 1024), 16, 0, 0);
-  };
 
-  const int64_t slot0 = (bos >> 6) + seq;  // chunk j of this sequence: slot slot0 + j
-  if (bos < eos) {
+  // ---- initial state: S[ct][dt][e] = S[16 dt + 4 g4 + e][col_base + 16 ct + c16]
+  f32x4 S[NCT][8];
 #pragma unroll
-    for (int i = 0; i < 4 * NPAIR; ++i) pf_kq(bos, i);
+  for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pf_v(bos, i);
+    for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int i = 0; i < kTbRounds; ++i) load_tb(slot0, i);
-    load_gx(slot0, 0);
-  }
-
-  // O^T of a finished chunk, lane (c16, g4) of tile (ct, tt): token 16 tt + c16,
-  // columns col + 16 ct + 4 g4 .. + 3; tokens at or past Lp are not stored.
-  // Address: uniform element offset of (chunk start, head, columns) plus a
-  // lane's 32-bit offset t * Hv * V + c (Hv * V is below 2^24: it bounds v's
-  // token stride).
-  f32x4 OT[2][4];
-  // With the gated norm (kNorm) the stored value is, per output row (one
-  // token of one v-head), y = o / sqrt(mean(o^2) + eps) * nw * silu(z) with
-  // the same operations in the same order as gated_norm_kernel over a stored
-  // fp32 o: the sum of squares of each run of eight columns is one fma chain
-  // (held by lanes g4 = 2x and 2x + 1), and the runs are summed pairwise as an
-  // xor butterfly over the run index (partner runs: the other lane pair, the
-  // other column tile, then the waves of the head through sNrm).  norm_rows
-  // leaves this wave's part for chunk parity `par` in sNrm; store_o combines
-  // the parts of the head's waves.
-  auto norm_rows = [&](int par) {
-    LANE_IDS();
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      float s1[2];
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const f32x4 y = OT[ct][tt];
-        float c = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) c = fmaf(y[e], y[e], c);
-        const float first = __shfl_xor(c, 16, 64);  // the run's first four squares, for odd g4
-        float run = first;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) run = fmaf(y[e], y[e], run);
-        const float whole = __shfl_xor(run, 16, 64);
-        run = (g4 & 1) ? run : whole;  // both lanes of the pair hold the run's sum
-        s1[ct] = run + __shfl_xor(run, 32, 64);
+      for (int e = 0; e < 4; ++e) {
+        const int d = 16 * dt + 4 * g4 + e;
+        const int col = col_base + 16 * ct + c16;
+        float s = 0.f;
+        if (m_mode)
+          s = (d == col) ? 1.f : 0.f;
+        else if (s0p)
+          s = s0p[(int64_t)d * a.V + col];
+        S[ct][dt][e] = s;
       }
-      if (g4 == 0) sNrm[(par * NW + wave) * 64 + 16 * tt + c16] = s1[0] + s1[1];
-    }
-  };
-  auto store_o = [&](int64_t tp, int Lp, int par, int tt) {
-    LANE_IDS();
-    const int64_t obase = (tp * a.Hv + h) * (int64_t)a.V + me.col;
+
+  // Upper tiles of sP and sT2 that the triangular products read must be zero;
+  // the record stash only ever writes the lower tiles.
+  for (int i = tid; i < (2 + 2) * CH * TP; i += NT) sP[i] = 0;
+
+  // ---- prefetch registers --------------------------------------------------
+  // Every prefetch load is unconditional (rows past the end of the sequence
+  // re-read its last row and are zeroed when stashed; record units past the
+  // end re-read the last unit).  The next chunk's loads are issued in three
+  // groups between the compute phases of the current one, so that the
+  // vector memory pipeline works through them while the matrix cores run
+  // instead of holding up a barrier.
+  u32x4 pk[NPAIR][2], pq[NPAIR][2], pv[NPAIR][2], pr[NREC];
+#define GDN_PF_ROWS(T0)                                                                        \
+  const int64_t rel_ = (T0) - bos;                                                            \
+  const int L_ = (int)((eos - (T0)) < CH ? (eos - (T0)) : CH);                                \
+  const uint32_t row0_ = (uint32_t)(r0_pf < L_ ? r0_pf : L_ - 1);                             \
+  const uint32_t row1_ = (uint32_t)(r0_pf + 1 < L_ ? r0_pf + 1 : L_ - 1);
+// one 16-byte load at uniform base B (chunk start) + lane byte offset
+#define GDN_LD16(B, ROW, S32, COL) \
+  (*reinterpret_cast<const u32x4*>((B) + (uint32_t)(2u * (__umul24((ROW), (S32)) + (uint32_t)(COL)))))
+#define GDN_PF_REC(T0)                                                                         \
+  do {                                                                                        \
+    const unsigned char* rs_ = rbase + (((T0) >> 6) + seq) * rslot_stride;                    \
+    _Pragma("unroll") for (int u_ = 0; u_ < NREC; ++u_)                                        \
+      pr[u_] = *reinterpret_cast<const u32x4*>(rs_ + 16 * min(tid + u_ * NT, RUNITS - 1));      \
+  } while (0)
+#define GDN_PF_KQ(T0)                                                                          \
+  do {                                                                                        \
+    GDN_PF_ROWS(T0)                                                                           \
+    const char* kc_ = kbase + 2 * rel_ * a.k_stride;                                          \
+    const char* qc_ = qbase + 2 * rel_ * q_stride;                                            \
+    _Pragma("unroll") for (int j_ = 0; j_ < NPAIR; ++j_) {                                     \
+      pk[j_][0] = GDN_LD16(kc_, row0_, ks32, d8_pf + kDJ * j_);                                \
+      pk[j_][1] = GDN_LD16(kc_, row1_, ks32, d8_pf + kDJ * j_);                                \
+      pq[j_][0] = GDN_LD16(qc_, row0_, qs32, d8_pf + kDJ * j_);                                \
+      pq[j_][1] = GDN_LD16(qc_, row1_, qs32, d8_pf + kDJ * j_);                                \
+    }                                                                                         \
+  } while (0)
+#define GDN_PF_V(T0)                                                                           \
+  do {                                                                                        \
+    GDN_PF_ROWS(T0)                                                                           \
+    const char* vc_ = vbase + 2 * rel_ * v_stride;                                            \
+    _Pragma("unroll") for (int j_ = 0; j_ < NPAIR; ++j_) {                                     \
+      pv[j_][0] = GDN_LD16(vc_, row0_, vs32, d8_pf + kDJ * j_);                                \
+      pv[j_][1] = GDN_LD16(vc_, row1_, vs32, d8_pf + kDJ * j_);                                \
+    }                                                                                         \
+  } while (0)
+#define GDN_PREFETCH(T0) do { GDN_PF_REC(T0); GDN_PF_KQ(T0); GDN_PF_V(T0); } while (0)
+  if (bos < eos) GDN_PREFETCH(bos);
+
+  // O of a finished chunk from the fp32 LDS tile to 16-byte global stores, by
+  // the first half of the waves: the two waves that share a SIMD finish a
+  // chunk out of step, the later one (of the second half) setting the pace,
+  // so the stores go to the waves that would otherwise wait at the barrier.
+  // With the gated norm (kNorm) every wave stores: the norm's arithmetic
+  // outweighs the slack of the first half alone.
+  // Rows past the end of the chunk store a second copy of its last row
+  // instead, so that every store is unconditional.  Address: uniform element
+  // offset of (chunk start, head, slice) plus a lane's 32-bit offset
+  // r * Hv * V + c (Hv * V is below 2^24: it bounds v's token stride).
+  auto flush_o = [&](int64_t tp, int Lp) {
+    constexpr int RUNS = BV / 8;  // 8-column runs per row
+    constexpr int HT = kNorm ? NT : NT / 2;  // threads that store (with the norm: every wave)
+    const int64_t obase = (tp * a.Hv + h) * (int64_t)a.V + v0;
     const uint32_t tok32 = (uint32_t)(a.Hv * a.V);
-    const int w0 = wave - me.col / 32;  // first wave of this v-head
-    {
-      const int t = 16 * tt + c16;
-      float inv = 0.f;
-      if (kNorm) {
-        const float* pr = sNrm + (par * NW + w0) * 64 + t;
-        float ss = (pr[0] + pr[64]) + (pr[128] + pr[192]);
-        if (a.V == 256) ss = ss + ((pr[256] + pr[320]) + (pr[384] + pr[448]));
-        inv = 1.f / sqrtf(ss / (float)a.V + a.eps);
-      }
-      if (t < Lp) {
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const uint32_t lo = __umul24((uint32_t)t, tok32) + (uint32_t)(16 * ct + 4 * g4);
-          f32x4 y = OT[ct][tt];  // (the scale is in O already)
-          if (kNorm) {
-            f32x4 zv, wv;
-            if (a.z_dt == 1) {
-              const u32x2 zr = *reinterpret_cast<const u32x2*>((const char*)((const uint16_t*)a.z + obase) + 2u * lo);
-              zv = f32x4{__uint_as_float(zr[0] << 16), __uint_as_float(zr[0] & 0xFFFF0000u),
-                         __uint_as_float(zr[1] << 16), __uint_as_float(zr[1] & 0xFFFF0000u)};
-            } else {
-              zv = *reinterpret_cast<const f32x4*>((const char*)((const float*)a.z + obase) + 4u * lo);
-            }
-            if (a.nw)
-              wv = *reinterpret_cast<const f32x4*>(a.nw + me.col + 16 * ct + 4 * g4);
-            else
-              wv = f32x4{1.f, 1.f, 1.f, 1.f};
+    for (int i = 0; i < CH * RUNS / HT; ++i) {
+      const int u = tid + HT * i;
+      const int r = min(u / RUNS, Lp - 1), c = 8 * (u % RUNS);
+      const float* src = sO + r * OP + c;
+      const float4 x0 = *reinterpret_cast<const float4*>(src);
+      const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+      const uint32_t lo = __umul24((uint32_t)r, tok32) + (uint32_t)c;
+      float y[8] = {a.scale * x0.x, a.scale * x0.y, a.scale * x0.z, a.scale * x0.w,
+                    a.scale * x1.x, a.scale * x1.y, a.scale * x1.z, a.scale * x1.w};
+      if constexpr (kNorm) {
+        // gated RMS norm of the whole row (the 16 lanes of a row are adjacent
+        // and aligned to 16 inside the wave): y = o rsqrt(mean o^2 + eps)
+        // weight silu(z); z has o's layout, so it shares o's offsets
+        float zv[8], wv[8];
+        if (a.z_dt == 1) {
+          const uint4 zr = *reinterpret_cast<const uint4*>((const char*)((const uint16_t*)a.z + obase) + 2u * lo);
+          const uint32_t zw[4] = {zr.x, zr.y, zr.z, zr.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) y[e] = y[e] * inv * wv[e] * silu_hw(zv[e]);
+          for (int e = 0; e < 4; ++e) {
+            zv[2 * e] = __uint_as_float(zw[e] << 16);
+            zv[2 * e + 1] = __uint_as_float(zw[e] & 0xFFFF0000u);
           }
-          if (kMode == kOutBF16) {
-            *reinterpret_cast<u32x2*>((char*)((uint16_t*)a.o + obase) + 2u * lo) =
-                u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-          } else {
-            *reinterpret_cast<f32x4*>((char*)((float*)a.o + obase) + 4u * lo) = y;
-          }
+        } else {
+          const float* zp = (const float*)((const char*)((const float*)a.z + obase) + 4u * lo);
+          const float4 z0 = *reinterpret_cast<const float4*>(zp);
+          const float4 z1 = *reinterpret_cast<const float4*>(zp + 4);
+          zv[0] = z0.x, zv[1] = z0.y, zv[2] = z0.z, zv[3] = z0.w;
+          zv[4] = z1.x, zv[5] = z1.y, zv[6] = z1.z, zv[7] = z1.w;
         }
+        if (a.nw) {
+          const float4 w0 = *reinterpret_cast<const float4*>(a.nw + v0 + c);
+          const float4 w1 = *reinterpret_cast<const float4*>(a.nw + v0 + c + 4);
+          wv[0] = w0.x, wv[1] = w0.y, wv[2] = w0.z, wv[3] = w0.w;
+          wv[4] = w1.x, wv[5] = w1.y, wv[6] = w1.z, wv[7] = w1.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) wv[e] = 1.f;
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
+        static_assert(RUNS == 16, "a row is one DPP row");
+        ss = row16_sum(ss);
+        const float inv = 1.f / sqrtf(ss / (float)BV + a.eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = y[e] * inv * wv[e] * silu_hw(zv[e]);
+      }
+      if (kMode == kOutBF16) {
+        uint4 w;
+        w.x = pack_bf16x2(y[0], y[1]);
+        w.y = pack_bf16x2(y[2], y[3]);
+        w.z = pack_bf16x2(y[4], y[5]);
+        w.w = pack_bf16x2(y[6], y[7]);
+        *reinterpret_cast<uint4*>((char*)((uint16_t*)a.o + obase) + 2u * lo) = w;
+      } else {
+        float* dst = (float*)((char*)((float*)a.o + obase) + 4u * lo);
+        *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(y[4], y[5], y[6], y[7]);
       }
     }
   };
 
-  int64_t j = 0;
-  for (int64_t t0 = bos; t0 < eos; t0 += CH, ++j) {
+  for (int64_t t0 = bos; t0 < eos; t0 += CH) {
     const int L = (int)((eos - t0) < CH ? (eos - t0) : CH);
-    const int buf = (int)(j & 1);
-    __syncthreads();  // every wave is done with the previous chunk's tiles; this chunk's records are in
+    __syncthreads();  // every wave is done with the previous chunk's tiles
+    if (kOut && t0 > bos && (kNorm || wave < NW / 2)) flush_o(t0 - CH, CH);  // a full chunk: only the last can be short
 
-    // ---- stash q, k (row-major and transposed) and v -------------------------
-    {
-    LANE_IDS();
+    // ---- stash q, k, v and the prep record ---------------------------------
+    // Rows past the end of a partial chunk (and v of M columns) are zeroed in
+    // the registers first; full chunks skip this.
+    if (L < CH || !load_v) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int jj = 0; jj < NPAIR; ++jj) {
-      const int u = tid + NT * jj;
-      const int r0 = 2 * (u >> 4), d = u & 15;
-      u32x4 k0 = pk[jj][0], k1 = pk[jj][1], q0 = pq[jj][0], q1 = pq[jj][1];
-      if (L < CH) {  // rows past the end of a partial chunk
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        if (r0 >= L) k0 = q0 = z;
-        if (r0 + 1 >= L) k1 = q1 = z;
+      for (int j = 0; j < NPAIR; ++j) {
+        if (r0_pf >= L) pk[j][0] = pq[j][0] = z;
+        if (r0_pf + 1 >= L) pk[j][1] = pq[j][1] = z;
+        if (!load_v || r0_pf >= L) pv[j][0] = z;
+        if (!load_v || r0_pf + 1 >= L) pv[j][1] = z;
       }
-      *reinterpret_cast<u32x4*>(sK + r0 * QP + 8 * d) = k0;
-      *reinterpret_cast<u32x4*>(sK + (r0 + 1) * QP + 8 * d) = k1;
+    }
+    // K^T words: the low halves of the two rows' words (row d0) and the high
+    // halves (row d1) by byte permutes; the upper half-wave (8 rows further
+    // on, the same bank half) stores row d1 first, so that each store
+    // instruction covers both halves of the banks.
+    const bool up_ = (lane & 32) != 0;
+    const uint32_t sel_a = up_ ? 0x07060302u : 0x05040100u, sel_b = up_ ? 0x05040100u : 0x07060302u;
+#pragma unroll
+    for (int j = 0; j < NPAIR; ++j) {
+      const int r0 = r0_pf, d8 = d8_pf + kDJ * j;
+      const u32x4 k0 = pk[j][0], k1 = pk[j][1];
+      const u32x4 v0v = pv[j][0], v1v = pv[j][1];
+      store8_frag<true>(sK, r0, d8, k0);
+      store8_frag<true>(sK, r0 + 1, d8, k1);
       if (kOut) {
-        *reinterpret_cast<u32x4*>(sQ + r0 * QP + 8 * d) = q0;
-        *reinterpret_cast<u32x4*>(sQ + (r0 + 1) * QP + 8 * d) = q1;
+        store8_frag<true>(sQ, r0, d8, pq[j][0]);
+        store8_frag<true>(sQ, r0 + 1, d8, pq[j][1]);
       }
-      // K^T: key index kk goes to row slot_row(kk) (row slot_row(kk) + 1 for
-      // kk + 1), tokens r0, r0 + 1 to the adjacent slots row_slot(r0), + 1
-      // (one 4-byte word)
-      const int ts = row_slot(r0);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int p0 = slot_row(8 * d + 2 * x);
-        const uint32_t w0 = __builtin_amdgcn_perm(k1[x], k0[x], 0x05040100u);
-        const uint32_t w1 = __builtin_amdgcn_perm(k1[x], k0[x], 0x07060302u);
-        const int e = kt_pos(p0, ts);  // the same position in rows p0 and p0 + 1
-        *reinterpret_cast<uint32_t*>(sKt + p0 * KTP + e) = w0;
-        *reinterpret_cast<uint32_t*>(sKt + (p0 + 1) * KTP + e) = w1;
-      }
-    }
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int u = tid + NT * jj;
-      *reinterpret_cast<u32x4*>(sV + (u / NVU) * LD::VP + 8 * (u % NVU)) = pv[jj];
-    }
-    }
-    lds_barrier();  // the chunk's tiles are in LDS
-    // The previous chunk's O leaves now, after the barrier that waits for
-    // outstanding memory operations, so its stores overlap this chunk's work.
-    const bool more = t0 + CH < eos;
-    if (kOut && j > 0) {  // the previous chunk's O (only the last chunk can be short)
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) store_o(t0 - CH, CH, (int)((j - 1) & 1), tt);
-    }
-    if (more) load_gx(slot0 + j + 1, buf ^ 1);  // the next chunk's gates (other buffer)
-    const unsigned char* gx = sGx + (buf * LD::NH + hslot) * GX_BYTES;
-    const float* sG = reinterpret_cast<const float*>(gx);
-    const float* sGam = reinterpret_cast<const float*>(gx + (REC_GAM - REC_G));
-    const float* sDec = reinterpret_cast<const float*>(gx + (REC_DEC - REC_G));
-    if (kOut) {
-      LANE_IDS();
-      // P^T operand fragments, shared by the waves of a v-head: fragment
-      // f = (token block m, t-tile tt) holds the tiles (2 m, tt), (2 m + 1, tt)
-      // of scale * P^T, (P^T)[s, t] = (K Q^T)[s, t] e^{G_t - G_s} for s <= t
-      // (zero above), split into bf16 hi and lo.  Wave w < 6 forms fragment w
-      // (wave w - NW / 2 ... for four waves: fragments w and w + 4) for every
-      // v-head of the workgroup; a lane holds s = 16 st + 4 g4 + e, t = 16 tt + c16.
-      constexpr int FM[6] = {0, 0, 0, 0, 1, 1};
-      constexpr int FT[6] = {0, 1, 2, 3, 2, 3};
-      constexpr float kLog2e = 1.4426950408889634f;
-#pragma unroll
-      for (int f0 = 0; f0 < 6; f0 += NW) {
-        const int f = f0 + wave;
-        if (f < 6) {
-          const int m = f < 4 ? 0 : 1, tt = f < 4 ? f : f - 2;
-          f32x4 acc[2];
-          zero4(acc[0]);
-          zero4(acc[1]);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const bf16x8 fq = frag_row128(sQ, 16 * tt + c16, 4 * k + g4);
-            acc[0] = mfma16(frag_row128(sK, 16 * (2 * m) + c16, 4 * k + g4), fq, acc[0]);
-            if (2 * m + 1 <= tt) acc[1] = mfma16(frag_row128(sK, 16 * (2 * m + 1) + c16, 4 * k + g4), fq, acc[1]);
-          }
-          (void)FM, (void)FT;
-          for (int hh = 0; hh < nh; ++hh) {
-            const float* gh = reinterpret_cast<const float*>(sGx + (buf * LD::NH + hh) * GX_BYTES);
-            const float Gt = gh[16 * tt + c16];
-            f32x4 p[2];
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-              const int st = 2 * m + x;
-              const f32x4 Gs = *reinterpret_cast<const f32x4*>(gh + 16 * st + 4 * g4);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const bool keep = st <= tt && 16 * st + 4 * g4 + e <= 16 * tt + c16;
-                p[x][e] = keep ? acc[x][e] * (a.scale * __builtin_amdgcn_exp2f(fminf(Gt - Gs[e], 0.f) * kLog2e)) : 0.f;
-              }
-            }
-            bf16x8 ph, pl;
-            split_frag(p[0], p[1], ph, pl);
-            unsigned char* dstf = sPf + hh * (12 * 1024) + f * 2048 + lane * 16;
-            *reinterpret_cast<bf16x8*>(dstf) = ph;
-            *reinterpret_cast<bf16x8*>(dstf + 1024) = pl;
-          }
+      for (int jx = 0; jx < 4; ++jx) {
+        const int d0 = d8 + 2 * jx, d1 = d0 + 1;
+        const int da = up_ ? d1 : d0, db = up_ ? d0 : d1;
+        *reinterpret_cast<uint32_t*>(sKt + da * TP + tile_pos<false>(da, r0)) =
+            __builtin_amdgcn_perm(k1[jx], k0[jx], sel_a);
+        *reinterpret_cast<uint32_t*>(sKt + db * TP + tile_pos<false>(db, r0)) =
+            __builtin_amdgcn_perm(k1[jx], k0[jx], sel_b);
+        if (load_v) {
+          *reinterpret_cast<uint32_t*>(sVt + d0 * VTP + r0) = (v0v[jx] & 0xFFFFu) | (v1v[jx] << 16);
+          *reinterpret_cast<uint32_t*>(sVt + d1 * VTP + r0) = (v0v[jx] >> 16) | (v1v[jx] & 0xFFFF0000u);
         }
       }
     }
-
-    const unsigned char* rec = sTb + hslot * TB_BYTES;
-
-    // ---- K S and S^T Q^T over the split state -----------------------------------
-    f32x4 KS[2][4];
+    {
+      // Every unit is stored (no branch around a store): a unit past the end
+      // of what this mode reads holds a copy of its last unit and rewrites it
+      // in place.
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+      for (int u = 0; u < NREC; ++u) {
+        const int f = min(tid + u * NT, RUNITS - 1);
+        unsigned char *dst0, *dst1;  // the unit's two 8-byte halves
+        if (f < REC_TB_UNITS || f >= REC_STATE_UNITS) {
+          // T diag(beta) hi, lo -> sT2; P hi, lo -> sP (two matrices each),
+          // columns c .. c + 7 of row r, in fragment order
+          const int fm = f < REC_TB_UNITS ? f : f - REC_STATE_UNITS;
+          const int mat = fm / 320, rem = fm - 320 * mat;
+          int bi, bj;
+          tile_ij(rem >> 5, bi, bj);
+          const int r = 16 * bi + ((rem >> 1) & 15), c = 16 * bj + 8 * (rem & 1);
+          unsigned char* row = smem + (f < REC_TB_UNITS ? OFF_T2 : OFF_P) + 2 * (mat * CH * TP + r * TP);
+          dst0 = row + 2 * tile_pos<false>(r, c);
+          dst1 = row + 2 * tile_pos<false>(r, c + 4);
+        } else {
+          const int g = f - REC_TB_UNITS;  // 0..15 gamma, 16..31 dec
+          dst0 = smem + OFF_GAM + 16 * g;
+          dst1 = dst0 + 8;
+        }
+        *reinterpret_cast<u32x2*>(dst0) = u32x2{pr[u][0], pr[u][1]};
+        *reinterpret_cast<u32x2*>(dst1) = u32x2{pr[u][2], pr[u][3]};
+      }
+    }
+    // ---- fetch the next chunk while this one computes -----------------------
+    __syncthreads();  // A: chunk data in LDS
+    const bool more_ = t0 + CH < eos;
+    if (more_) GDN_PF_REC(t0 + CH);
+
+    // From here on each wave touches only its own state columns.
+    // ---- K S and Q S over the split state (hi pass, then lo pass per k-step)
+    f32x4 KS[NCT][4], O[NCT][4];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         zero4(KS[ct][rt]);
-        zero4(OT[ct][rt]);
+        zero4(O[ct][rt]);
       }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      LANE_IDS();
-      bf16x8 sh[2], sl[2];
+      bf16x8 sp[2][NCT];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) split_frag(S[ct][2 * m], S[ct][2 * m + 1], sh[ct], sl[ct]);
-      bf16x8 fk[4];
+      for (int ct = 0; ct < NCT; ++ct) split_frag(S[ct][2 * m], S[ct][2 * m + 1], sp[0][ct], sp[1][ct]);
+      bf16x8 fk[4], fq[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) fk[rt] = frag_row128(sK, 16 * rt + c16, 4 * m + g4);
+      for (int rt = 0; rt < 4; ++rt) {
+        fk[rt] = frag16<true>(sK, 16 * rt + c16, 32 * m, g4);
+        if (kOut) fq[rt] = frag16<true>(sQ, 16 * rt + c16, 32 * m, g4);
+      }
 #pragma unroll
       for (int part = 0; part < 2; ++part)
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct) KS[ct][rt] = mfma16(fk[rt], part ? sl[ct] : sh[ct], KS[ct][rt]);
-      if (kOut) {
-        bf16x8 fq[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) fq[tt] = frag_row128(sQ, 16 * tt + c16, 4 * m + g4);
-#pragma unroll
-        for (int part = 0; part < 2; ++part)
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) OT[ct][tt] = mfma16(part ? sl[ct] : sh[ct], fq[tt], OT[ct][tt]);
-      }
+          for (int ct = 0; ct < NCT; ++ct) {
+            KS[ct][rt] = mfma16(fk[rt], sp[part][ct], KS[ct][rt]);
+            if (kOut) O[ct][rt] = mfma16(fq[rt], sp[part][ct], O[ct][rt]);
+          }
       SCHED_FENCE();
     }
 
-    // ---- R = V - gamma . K S, split; U = T diag(beta) R --------------------------
-    f32x4 U[2][4];
+    if (more_) GDN_PF_KQ(t0 + CH);
+    // ---- U = T diag(beta) (V - e^G K S) ------------------------------------------
+    // R = V - gamma * (K S) is formed in the accumulator layout (V read from its
+    // transposed tile, four consecutive tokens per lane), split into bf16
+    // pairs, and multiplied by T diag(beta) as hi*hi + hi*lo + lo*hi.
+    f32x4 U[NCT][4];
     {
-      LANE_IDS();
-      bf16x8 rh[2][2], rl[2][2];
+      bf16x8 rh[NCT][2], rl[NCT][2];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
+      for (int ct = 0; ct < NCT; ++ct) {
         f32x4 R[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-          const f32x4 gam = *reinterpret_cast<const f32x4*>(sGam + 16 * rt + 4 * g4);
-          // v at tokens 16 rt + 4 g4 + e of this lane's column (M columns: none)
-          const uint16_t* vp = sV + (16 * rt + 4 * g4) * LD::VP + 32 * wave + 16 * ct + c16;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float ve = me.m ? 0.f : __uint_as_float((uint32_t)vp[e * LD::VP] << 16);
-            R[rt][e] = fmaf(-gam[e], KS[ct][rt][e], ve);
+          const float4 gam = *reinterpret_cast<const float4*>(sGam + 16 * rt + 4 * g4);
+          R[rt][0] = -gam.x * KS[ct][rt][0];
+          R[rt][1] = -gam.y * KS[ct][rt][1];
+          R[rt][2] = -gam.z * KS[ct][rt][2];
+          R[rt][3] = -gam.w * KS[ct][rt][3];
+          if (load_v) {
+            const u32x2 vv =
+                *reinterpret_cast<const u32x2*>(sVt + (wave * CPW + 16 * ct + c16) * VTP + 16 * rt + 4 * g4);
+            R[rt][0] += __uint_as_float(vv[0] << 16);
+            R[rt][1] += __uint_as_float(vv[0] & 0xFFFF0000u);
+            R[rt][2] += __uint_as_float(vv[1] << 16);
+            R[rt][3] += __uint_as_float(vv[1] & 0xFFFF0000u);
           }
         }
 #pragma unroll
@@ -596,214 +530,205 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, float*
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) zero4(U[ct][rt]);
       }
-      constexpr int FRT[6] = {0, 1, 2, 3, 2, 3};
-      constexpr int FM[6] = {0, 0, 0, 0, 1, 1};
 #pragma unroll
-      for (int f0 = 0; f0 < 6; f0 += 3) {
-        bf16x8 th[3], tl[3];
+      for (int m = 0; m < 2; ++m) {
+        bf16x8 th[4], tl[4];
 #pragma unroll
-        for (int f = 0; f < 3; ++f) {
-          th[f] = *reinterpret_cast<const bf16x8*>(rec + REC_TB_HI + (f0 + f) * 1024 + lane * 16);
-          tl[f] = *reinterpret_cast<const bf16x8*>(rec + REC_TB_LO + (f0 + f) * 1024 + lane * 16);
+        for (int rt = 2 * m; rt < 4; ++rt) {
+          th[rt] = frag16<false>(sT2, 16 * rt + c16, 32 * m, g4);
+          tl[rt] = frag16<false>(sT2 + CH * TP, 16 * rt + c16, 32 * m, g4);
         }
 #pragma unroll
         for (int part = 0; part < 3; ++part)
 #pragma unroll
-          for (int f = 0; f < 3; ++f)
+          for (int rt = 2 * m; rt < 4; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-              const int rt = FRT[f0 + f], m = FM[f0 + f];
-              U[ct][rt] = mfma16(part == 2 ? tl[f] : th[f], part == 1 ? rl[ct][m] : rh[ct][m], U[ct][rt]);
+            for (int ct = 0; ct < NCT; ++ct) {
+              const bf16x8 ta = part == 2 ? tl[rt] : th[rt];
+              const bf16x8 rb = part == 1 ? rl[ct][m] : rh[ct][m];
+              U[ct][rt] = mfma16(ta, rb, U[ct][rt]);
             }
         SCHED_FENCE();
       }
     }
-
-    // ---- U as the A operand of U^T P^T; dec . U as the B operand of K^T U -------
-    bf16x8 uh[2][2], ul[2][2], dh[2][2], dl[2][2];
-    {
-    LANE_IDS();
+    if (more_) GDN_PF_V(t0 + CH);
     if (kOut) {
+      // ---- O = diag(gamma) Q S + P U  -> fp32 O tile in LDS -------------------
+      bf16x8 Uhi[NCT][2], Ulo[NCT][2];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+      for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int m = 0; m < 2; ++m) split_frag(U[ct][2 * m], U[ct][2 * m + 1], uh[ct][m], ul[ct][m]);
+        for (int m = 0; m < 2; ++m) split_frag(U[ct][2 * m], U[ct][2 * m + 1], Uhi[ct][m], Ulo[ct][m]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const float4 gam = *reinterpret_cast<const float4*>(sGam + 16 * rt + 4 * g4);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          O[ct][rt][0] *= gam.x;
+          O[ct][rt][1] *= gam.y;
+          O[ct][rt][2] *= gam.z;
+          O[ct][rt][3] *= gam.w;
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        bf16x8 ph[4], pl[4];
+#pragma unroll
+        for (int rt = 2 * m; rt < 4; ++rt) {
+          ph[rt] = frag16<false>(sP, 16 * rt + c16, 32 * m, g4);
+          pl[rt] = frag16<false>(sP + CH * TP, 16 * rt + c16, 32 * m, g4);
+        }
+#pragma unroll
+        for (int part = 0; part < 3; ++part)
+#pragma unroll
+          for (int rt = 2 * m; rt < 4; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+              const bf16x8 pa = part == 2 ? pl[rt] : ph[rt];
+              const bf16x8 ub = part == 1 ? Ulo[ct][m] : Uhi[ct][m];
+              O[ct][rt] = mfma16(pa, ub, O[ct][rt]);
+            }
+      }
     }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const f32x4 dec = *reinterpret_cast<const f32x4*>(sDec + 16 * rt + 4 * g4);
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) U[ct][rt] *= dec;
-    }
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int m = 0; m < 2; ++m) split_frag(U[ct][2 * m], U[ct][2 * m + 1], dh[ct][m], dl[ct][m]);
-    }
-
-    // Every wave is done with this chunk's T diag(beta) and (outputs) has its
-    // P^T fragments in: the next chunk's T diag(beta) loads now.
-    lds_barrier();
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < kTbRounds; ++i) load_tb(slot0 + j + 1, i);
-    }
-
-    // ---- S <- e^{G_last} S + K^T (dec . U) ----------------------------------
+    // ---- S <- e^{G_last} S + K^T (diag(dec) U) -------------------------------
     {
-      LANE_IDS();
+      bf16x8 Uhi[NCT][2], Ulo[NCT][2];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const float4 dec = *reinterpret_cast<const float4*>(sDec + 16 * rt + 4 * g4);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          U[ct][rt][0] *= dec.x;
+          U[ct][rt][1] *= dec.y;
+          U[ct][rt][2] *= dec.z;
+          U[ct][rt][3] *= dec.w;
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) split_frag(U[ct][2 * m], U[ct][2 * m + 1], Uhi[ct][m], Ulo[ct][m]);
       const float glast = sGam[CH - 1];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+      for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int pt = 0; pt < 8; ++pt) S[ct][pt] *= glast;
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) S[ct][dt][e] *= glast;
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          bf16x8 fkt[4];
+          bf16x8 fk[4];
 #pragma unroll
-          for (int x = 0; x < 4; ++x) fkt[x] = frag_kt(sKt, 16 * (4 * half + x) + c16, 4 * m + g4);
+          for (int x = 0; x < 4; ++x) fk[x] = frag16<false>(sKt, 16 * (4 * half + x) + c16, 32 * m, g4);
 #pragma unroll
           for (int part = 0; part < 2; ++part)
 #pragma unroll
             for (int x = 0; x < 4; ++x)
 #pragma unroll
-              for (int ct = 0; ct < 2; ++ct) {
-                const int pt = 4 * half + x;
-                S[ct][pt] = mfma16(fkt[x], part ? dl[ct][m] : dh[ct][m], S[ct][pt]);
+              for (int ct = 0; ct < NCT; ++ct) {
+                const int dt = 4 * half + x;
+                S[ct][dt] = mfma16(fk[x], part ? Ulo[ct][m] : Uhi[ct][m], S[ct][dt]);
               }
-          if (more) pf_v(t0 + CH, 2 * m + half);  // the next chunk's v
           SCHED_FENCE();
         }
     }
-
-    if (more && (kP1 || NPAIR > 1)) {  // the next chunk's q, k not issued in the P^T steps
-#pragma unroll
-      for (int i = kP1 ? 0 : 4; i < 4 * NPAIR; ++i) pf_kq(t0 + CH, i);
-    }
     if (kOut) {
-      LANE_IDS();
-      // ---- O^T = scale gamma_t . (S^T Q^T) + U^T (scale P^T) -----------------
+      // O into this wave's own columns of the fp32 O tile; the first half of
+      // the waves stores the whole tile after the next chunk's first barrier.
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const float gt = a.scale * sGam[16 * tt + c16];
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) OT[ct][tt] *= gt;
-      }
-      const unsigned char* pf = sPf + hslot * (12 * 1024) + lane * 16;
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        if (more) pf_kq(t0 + CH, tt);  // the next chunk's q, k (NPAIR = 1: four loads)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          if (2 * m > tt) continue;
-          const int f = m == 0 ? tt : tt + 2;
-          const bf16x8 ph = *reinterpret_cast<const bf16x8*>(pf + f * 2048);
-          const bf16x8 pl = *reinterpret_cast<const bf16x8*>(pf + f * 2048 + 1024);
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            OT[ct][tt] = mfma16(uh[ct][m], ph, OT[ct][tt]);
-            OT[ct][tt] = mfma16(ul[ct][m], ph, OT[ct][tt]);
-            OT[ct][tt] = mfma16(uh[ct][m], pl, OT[ct][tt]);
-          }
-        }
-      }
-      if (kNorm) norm_rows(buf);  // read after the next chunk's barriers (or the one below)
+          for (int e = 0; e < 4; ++e)
+            sO[(16 * rt + 4 * g4 + e) * OP + wave * CPW + 16 * ct + c16] = O[ct][rt][e];
     }
   }
   if (kOut && bos < eos) {  // the last chunk's O
     const int64_t t_last = bos + CH * ((eos - bos - 1) / CH);
-    if (kNorm) __syncthreads();  // every wave's row sums of the last chunk
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) store_o(t_last, (int)(eos - t_last), (int)((j - 1) & 1), tt);
+    __syncthreads();
+    if (kNorm || wave < NW / 2) flush_o(t_last, (int)(eos - t_last));
   }
 
+#undef GDN_PREFETCH
+#undef GDN_PF_ROWS
+#undef GDN_PF_REC
+#undef GDN_PF_KQ
+#undef GDN_PF_V
+#undef GDN_LD16
   // ---- final state ----------------------------------------------------------
   float* dst = nullptr;
   int64_t row_stride = 0;
   const int out_row = a.sf_map ? a.sf_map[seq] : zb;
-  if (me.m) {
-    dst = m_out + ((int64_t)zb * a.Hv + h) * (int64_t)KD * KD;
+  if (m_mode) {
+    dst = p1.m_out + ((int64_t)zb * a.Hv + h) * (int64_t)KD * KD;
     row_stride = KD;
   } else if (a.sf && out_row >= 0) {
     dst = a.sf + (int64_t)out_row * a.sf_seq_stride + (int64_t)h * a.sf_head_stride;
     row_stride = a.sf_row_stride;
   }
   if (dst) {
-    LANE_IDS();
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int pt = 0; pt < 8; ++pt)
+      for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          dst[(int64_t)row_slot(16 * pt + 4 * g4 + e) * row_stride + me.col + 16 * ct + c16] = S[ct][pt][e];
+          dst[(int64_t)(16 * dt + 4 * g4 + e) * row_stride + col_base + 16 * ct + c16] = S[ct][dt][e];
   }
 }
 
-// Waves per workgroup: 8 (256 columns) when the q/k head's column space splits
-// into 256-column pieces, else 4 (128 columns).
-int scan_waves(int cols_per_group) { return cols_per_group % 256 == 0 ? 8 : 4; }
-
-template <int kMode, int NW, bool kNorm>
-hipError_t launch_scan_nw(const ChunkArgs& a, float* m_out, int nz, int cols_per_group, hipStream_t stream) {
-  const void* fn = (const void*)chunk_scan_kernel<kMode, NW, kNorm>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Lds<NW>::BYTES);
-  if (e != hipSuccess) return e;
-  ChunkArgs c = a;
-  c.n_tiles = cols_per_group / (32 * NW);
-  const int64_t n = (int64_t)nz * a.Hqk * c.n_tiles;
-  if (n > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((chunk_scan_kernel<kMode, NW, kNorm>), dim3((unsigned)n), dim3(NW * 64), Lds<NW>::BYTES, stream,
-                     c, m_out);
-  return hipGetLastError();
-}
+constexpr int kScanWaves = 8;  // the prefetch code assumes 512 threads
 
 template <int kMode, bool kNorm = false>
-hipError_t launch_scan(const ChunkArgs& a, float* m_out, int nz, hipStream_t stream) {
-  const int G = a.Hv / a.Hqk;
-  const int cols = G * (kMode == kPass1 ? KD + a.V : a.V);
-  return scan_waves(cols) == 8 ? launch_scan_nw<kMode, 8, kNorm>(a, m_out, nz, cols, stream)
-                               : launch_scan_nw<kMode, 4, kNorm>(a, m_out, nz, cols, stream);
+hipError_t launch_scan(const ChunkArgs& a, Pass1 p1, dim3 grid, hipStream_t stream) {
+  const void* fn = (const void*)chunk_scan_kernel<kMode, kScanWaves, kNorm>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  if (e != hipSuccess) return e;
+  // 1-D launch over (tile, v-head, sequence); the kernel decodes it
+  ChunkArgs c = a;
+  c.n_tiles = (int)grid.x;
+  const int64_t n = (int64_t)grid.x * grid.y * grid.z;
+  if (n > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((chunk_scan_kernel<kMode, kScanWaves, kNorm>), dim3((unsigned)n), dim3(kScanWaves * 64), LDS_BYTES,
+                     stream, c, p1);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-bool chunk_scan_fuses_norm(int Hqk, int Hv, int V) {
-  const int cols_wg = 32 * scan_waves((Hv / Hqk) * V);
-  return (V == 128 || V == 256) && V <= cols_wg;
-}
-
-int chunk_scan_blocks(int Hqk, int Hv, int V, bool pass1) {
-  const int cols = (Hv / Hqk) * (pass1 ? KD + V : V);
-  return Hqk * (cols / (32 * scan_waves(cols)));
-}
-
 hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t stream, bool prep) {
   if (a.n_seqs == 0 || a.Hv == 0) return hipSuccess;
-  if (a.K != KD || a.V % 128 != 0 || a.Hv % a.Hqk != 0 || a.tbuf == nullptr) return hipErrorInvalidValue;
-  if (a.Ttot > 0 && (a.o == nullptr || a.q == nullptr)) return hipErrorInvalidValue;
+  if (a.K != KD || a.V % BV != 0 || a.tbuf == nullptr) return hipErrorInvalidValue;
+  const bool with_o = a.o != nullptr && a.q != nullptr;
   if (prep) {
-    hipError_t e = launch_chunk_prep(a, stream);
+    hipError_t e = launch_chunk_prep(a, with_o ? 1 : 0, stream);
     if (e != hipSuccess) return e;
   }
   const int nz = a.seq_order ? a.n_blocks_z : a.n_seqs;
   if (nz == 0) return hipSuccess;
-  // (without o, as for calls with no tokens, nothing is stored but the states)
-  if (a.z) {
-    if (!chunk_scan_fuses_norm(a.Hqk, a.Hv, a.V)) return hipErrorInvalidValue;
-    return a.o_dt == 1 ? launch_scan<kOutBF16, true>(a, nullptr, nz, stream)
-                       : launch_scan<kOutF32, true>(a, nullptr, nz, stream);
+  const dim3 grid(a.V / BV, a.Hv, nz);
+  if (!with_o) {
+    // state only: run the scan without outputs
+    return launch_scan<kPass1>(a, Pass1{0, nullptr}, grid, stream);
   }
-  return a.o_dt == 1 ? launch_scan<kOutBF16>(a, nullptr, nz, stream) : launch_scan<kOutF32>(a, nullptr, nz, stream);
+  if (a.z) {
+    // the gated norm needs a whole row of V values in one workgroup
+    if (a.V != BV) return hipErrorInvalidValue;
+    return a.o_dt == 1 ? launch_scan<kOutBF16, true>(a, Pass1{0, nullptr}, grid, stream)
+                       : launch_scan<kOutF32, true>(a, Pass1{0, nullptr}, grid, stream);
+  }
+  return a.o_dt == 1 ? launch_scan<kOutBF16>(a, Pass1{0, nullptr}, grid, stream)
+                     : launch_scan<kOutF32>(a, Pass1{0, nullptr}, grid, stream);
 }
 
 hipError_t launch_segment_pass1(const ChunkArgs& a, float* M, float* b, hipStream_t stream, bool prep) {
   if (a.n_seqs == 0 || a.Hv == 0) return hipSuccess;
-  if (a.K != KD || a.V % 128 != 0 || a.Hv % a.Hqk != 0 || a.tbuf == nullptr) return hipErrorInvalidValue;
+  if (a.K != KD || a.V % BV != 0 || a.tbuf == nullptr) return hipErrorInvalidValue;
   if (prep) {
-    hipError_t e = launch_chunk_prep(a, stream);
+    hipError_t e = launch_chunk_prep(a, 0, stream);
     if (e != hipSuccess) return e;
   }
   ChunkArgs c = a;
@@ -818,7 +743,7 @@ hipError_t launch_segment_pass1(const ChunkArgs& a, float* M, float* b, hipStrea
   c.sf_map = nullptr;
   const int nz = a.seq_order ? a.n_blocks_z : a.n_seqs;
   if (nz == 0) return hipSuccess;
-  return launch_scan<kPass1>(c, M, nz, stream);
+  return launch_scan<kPass1>(c, Pass1{KD / BV, M}, dim3(KD / BV + a.V / BV, a.Hv, nz), stream);
 }
 
 }  // namespace gdn

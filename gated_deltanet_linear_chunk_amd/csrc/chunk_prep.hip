@@ -1,26 +1,29 @@
-// chunk_prep.hip -- everything of a chunk that the scan needs and cannot
-// cheaply form itself.
+// chunk_prep.hip -- everything of a chunk that does not depend on the state.
 //
 // For a 64-token chunk with local tokens r, s and in-chunk cumulative gate
 // G (fp64):
 //   A = strictly-lower(diag(beta) K K^T * e^{G_r - G_s}),  T = (I + A)^{-1},
+//   P = lower(Q K^T * e^{G_r - G_s}),
 //   gamma_r = e^{G_r},  dec_r = e^{G_last - G_r}.
 // None of these depends on the recurrent state, so they are computed here for
 // every (chunk, v-head) at once, off the serial chunk scan, which then only
-// multiplies T diag(beta) against its state.  (The masked Q K^T the outputs
-// need is rebuilt by the scan from the q and k it holds in LDS.)
+// multiplies them against its state.
 //
-// One wave owns one (chunk slot, q/k head) and builds the records of the
-// v-heads that read that q/k head (two per wave when their number is even):
-// K fragments come straight from global memory into the 16 x 16 x 32 bf16
-// MFMA (exact products, fp32 sums); masks are applied in registers; the four
-// 16 x 16 diagonal blocks of T are inverted by forward substitution (lane =
-// block, column) and the other blocks follow, one block diagonal at a time,
-// from T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj on fp32 MFMAs.
+// One wave owns one (chunk slot, v-head): K and Q fragments come straight from
+// global memory into the 16 x 16 x 32 bf16 MFMA (exact products, fp32 sums);
+// masks are applied in registers; the four 16 x 16 diagonal blocks of T are
+// inverted by forward substitution (lane = block, column) and the other
+// blocks follow, one block diagonal at a time, from
+// T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj on fp32 MFMAs.
 //
-// The record (kernels.h) holds T diag(beta) split into bf16 hi + lo, written
-// as the scan's A-operand fragments (one 16-byte load per lane and fragment,
-// straight into LDS), then G, gamma and dec in fp32.
+// Record per (chunk slot, v-head), PREP_RECORD_BYTES long:
+//   T diag(beta) hi, lo;  gamma[64], dec[64] (fp32);  P hi, lo
+//   (each matrix: 10 lower 16 x 16 bf16 tiles, i >= j, index i(i+1)/2 + j,
+//   row-major inside a tile; hi = bf16(x), lo = bf16(x - hi)), so that a
+//   state-only scan reads one contiguous prefix.
+// (The UT transform's other product, T diag(beta e^G) K S, is formed by the
+// scan as T diag(beta) (e^G * K S), so it needs no matrix of its own.)
+// Without outputs (state-only runs) the P tiles are not written.
 // Chunk slots: chunk j of sequence n (first token cu[n] + 64 j) has slot
 // floor((cu[n] + 64 j) / 64) + n, which is unique and below
 // ceil(T / 64) + n_seqs; unused slots are skipped.
@@ -56,9 +59,14 @@ __device__ __forceinline__ f32x4_t mfma_f32_4(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-__global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int heads_per_wave) {
+__device__ __forceinline__ void tile_rc(int b, int& i, int& j) {
+  i = b >= 6 ? 3 : (b >= 3 ? 2 : (b >= 1 ? 1 : 0));
+  j = b - (i * (i + 1)) / 2;
+}
+
+__global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p, int heads_per_wave) {
   __shared__ float sA[10][16][BP];
-  __shared__ float sT[10][16][BP];
+  __shared__ float sT[10][16][BP];  // P staging, then T
   __shared__ float sY[3][16][BP];
   __shared__ double sG[CH];
   __shared__ float sBeta[CH];
@@ -87,11 +95,11 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int heads_p
   if (t0 >= eos) return;  // unused slot
   const int L = (int)((eos - t0) < CH ? (eos - t0) : CH);
 
-  // ---- K fragments straight from global memory, in flight first -------------
+  // ---- K and Q fragments straight from global memory, in flight first ----------
   // row tile i, k-step m: contiguous k = 32 m + 8 g4 .. +7; rows past L read
   // the last row and are zeroed (every load unconditional)
   const int64_t head_off = (int64_t)hq * KD + 8 * g4;
-  bf16x8 kf[4][4];
+  bf16x8 kf[4][4], qf[4][4];
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -104,14 +112,27 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int heads_p
         kf[i][m] = __builtin_bit_cast(bf16x8, r < L ? v : z);
       }
     }
+    if (with_p) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * i + c16;
+        const int64_t row = t0 + (r < L ? r : L - 1);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>((const uint16_t*)a.q + row * a.q_stride + head_off + 32 * m);
+          qf[i][m] = __builtin_bit_cast(bf16x8, r < L ? v : z);
+        }
+      }
+    }
   }
 
   for (int hh = 0; hh < heads_per_wave; ++hh) {
   const int h = h0 + hh;
   unsigned char* rec = (unsigned char*)a.tbuf + ((int64_t)slot * a.Hv + h) * PREP_RECORD_BYTES;
-  float* rG = (float*)(rec + REC_G);
-  float* rgam = (float*)(rec + REC_GAM);
-  float* rdec = (float*)(rec + REC_DEC);
+  uint16_t* rtb = (uint16_t*)(rec + PREP_REC_TB);  // [2][10][256]
+  uint16_t* rp = (uint16_t*)(rec + PREP_REC_P);    // [2][10][256]
+  float* rgam = (float*)(rec + PREP_REC_GAM);
+  float* rdec = (float*)(rec + PREP_REC_DEC);
   if (hh > 0) __syncthreads();  // the previous head is done with the LDS tiles
 
   // ---- gates: G (fp64 prefix sum), gamma, dec ---------------------------------
@@ -125,14 +146,46 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int heads_p
       if (lane >= off) G += o;
     }
     const double Glast = __shfl(G, 63, 64);
+    const float gam = expf((float)G);
     sG[lane] = G;
     sBeta[lane] = b;
-    rG[lane] = (float)G;
-    rgam[lane] = expf((float)G);
+    rgam[lane] = gam;
     rdec[lane] = expf((float)(Glast - G));
   }
 
   __syncthreads();  // gates visible to all lanes
+
+  // ---- P = lower(Q K^T * decay) -> record (hi, lo) ----------------------------
+  if (with_p) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j <= i; ++j) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc = mfma16(qf[i][m], kf[j][m], acc);
+        const int s = 16 * j + c16;
+        const double Gs = sG[s];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = 4 * g4 + e, r = 16 * i + rr;
+          sT[blk(i, j)][rr][c16] = (r >= s) ? acc[e] * decay(sG[r] - Gs) : 0.f;
+        }
+      }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 10; ++u) {
+      const int f = lane + 64 * u;  // 4-element group: tile f/64, element 4 (f % 64)
+      const int b = f >> 6, e4 = (f & 63) * 4, rr = e4 >> 4, cc = e4 & 15;
+      const float* src = &sT[b][rr][cc];
+      uint32_t h0, l0, h1, l1;
+      split2(src[0], src[1], h0, l0);
+      split2(src[2], src[3], h1, l1);
+      *reinterpret_cast<u32x2*>(rp + (0 * 10 + b) * 256 + e4) = u32x2{h0, h1};
+      *reinterpret_cast<u32x2*>(rp + (1 * 10 + b) * 256 + e4) = u32x2{l0, l1};
+    }
+    __syncthreads();  // sT is reused for T
+  }
 
   // ---- A = strictly-lower(diag(beta) K K^T * decay) ---------------------------
 #pragma unroll
@@ -209,37 +262,23 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int heads_p
     }
   }
 
-  // ---- T diag(beta) as bf16 pairs -> record, as A-operand fragments ---------
-  // fragment f = (row tile rt, column block m); lane (c16, g4) holds row
-  // 16 rt + c16 at the columns 32 m + slot_row(8 g4 + j), j = 0..7, which are
-  // columns 32 m + 4 g4 + {0..3} and 32 m + 16 + 4 g4 + {0..3}
-  {
-    constexpr int FRT[6] = {0, 1, 2, 3, 2, 3};
-    constexpr int FM[6] = {0, 0, 0, 0, 1, 1};
-    uint16_t* rhi = (uint16_t*)(rec + REC_TB_HI);
-    uint16_t* rlo = (uint16_t*)(rec + REC_TB_LO);
+  // ---- T diag(beta) as bf16 pairs -> record -----------------------------------
 #pragma unroll
-    for (int f = 0; f < 6; ++f) {
-      const int rt = FRT[f], m = FM[f];
-      uint32_t hw[4], lw[4];
+  for (int u = 0; u < 10; ++u) {
+    const int f = lane + 64 * u;
+    const int b = f >> 6, e4 = (f & 63) * 4, rr = e4 >> 4, cc = e4 & 15;
+    int bi, bj;
+    tile_rc(b, bi, bj);
+    const int s = 16 * bj + cc;
+    const float* src = &sT[b][rr][cc];
+    float tb[4];
 #pragma unroll
-      for (int hh2 = 0; hh2 < 2; ++hh2) {
-        const int jb = 2 * m + hh2;  // column block of these four values
-        float tb[4];
-        if (jb <= rt) {
-          const float* src = &sT[blk(rt, jb)][c16][4 * g4];
-#pragma unroll
-          for (int x = 0; x < 4; ++x) tb[x] = src[x] * sBeta[16 * jb + 4 * g4 + x];
-        } else {
-#pragma unroll
-          for (int x = 0; x < 4; ++x) tb[x] = 0.f;
-        }
-        split2(tb[0], tb[1], hw[2 * hh2], lw[2 * hh2]);
-        split2(tb[2], tb[3], hw[2 * hh2 + 1], lw[2 * hh2 + 1]);
-      }
-      *reinterpret_cast<u32x4*>(rhi + f * 512 + lane * 8) = u32x4{hw[0], hw[1], hw[2], hw[3]};
-      *reinterpret_cast<u32x4*>(rlo + f * 512 + lane * 8) = u32x4{lw[0], lw[1], lw[2], lw[3]};
-    }
+    for (int x = 0; x < 4; ++x) tb[x] = src[x] * sBeta[s + x];
+    uint32_t uh0, ul0, uh1, ul1;
+    split2(tb[0], tb[1], uh0, ul0);
+    split2(tb[2], tb[3], uh1, ul1);
+    *reinterpret_cast<u32x2*>(rtb + (0 * 10 + b) * 256 + e4) = u32x2{uh0, uh1};
+    *reinterpret_cast<u32x2*>(rtb + (1 * 10 + b) * 256 + e4) = u32x2{ul0, ul1};
   }
   }  // v-heads of this q/k head
 }
@@ -248,13 +287,13 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int heads_p
 
 int64_t chunk_slots(int64_t Ttot, int n_seqs) { return (Ttot + 63) / 64 + n_seqs; }
 
-hipError_t launch_chunk_prep(const ChunkArgs& a, hipStream_t stream) {
+hipError_t launch_chunk_prep(const ChunkArgs& a, int with_p, hipStream_t stream) {
   const int64_t slots = chunk_slots(a.Ttot, a.n_seqs);
   if (slots == 0 || a.Hv == 0) return hipSuccess;
   // Two v-heads that read the same q/k head share one wave (one load of the
-  // k fragments and half the waves); otherwise one v-head per wave.
+  // q/k fragments and half the waves); otherwise one v-head per wave.
   const int per = (a.Hv / a.Hqk) % 2 == 0 ? 2 : 1;
-  hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)slots, a.Hv / per), dim3(64), 0, stream, a, per);
+  hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)slots, a.Hv / per), dim3(64), 0, stream, a, with_p, per);
   return hipGetLastError();
 }
 

@@ -119,19 +119,6 @@ __device__ __forceinline__ float silu_hw(float z) {
   return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
 }
 
-// Operand slot order of accumulator rows.  A pair of vertically adjacent
-// 16 x 16 accumulator tiles (rows 0..31 of a 32-row block) is, register for
-// register, an MFMA operand whose 32-long k index is in this order: operand
-// slot p = 8 g + 4 h + j (lane group g, register half h, j = 0..3) holds row
-// slot_row(p) = 16 h + 4 g + j; row_slot is the inverse.  Both act within a
-// 32-block and keep groups of four together.
-__device__ __forceinline__ int slot_row(int p) {
-  return (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3);
-}
-__device__ __forceinline__ int row_slot(int c) {
-  return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
-}
-
 __device__ __forceinline__ int clampi(int64_t x, int64_t lo, int64_t hi) {
   return (int)(x < lo ? lo : (x > hi ? hi : x));
 }

@@ -49,42 +49,29 @@ struct ChunkArgs {
   const int32_t* s0_ref;     // [n_seqs]: >= 0 row of s0_seg, -1 zero, <= -2 row -2-r of s0
   const float* s0_seg;       // start states [*, Hv, K, V] picked by s0_ref
   const int32_t* sf_map;     // [n_seqs]: row of sf for the final state, -1 none
-  int n_tiles;               // bf16 scan: workgroups per (sequence, q/k head), set by its launcher
-  // bf16 scan: when z is set, o receives the gated RMS norm of every output
-  // row, o * rsqrt(mean(o^2) + eps) * nw * silu(z), instead of o (see
-  // chunk_scan_fuses_norm).
+  int n_tiles;               // bf16 scan: column tiles per (sequence, v-head), set by its launcher
+  // bf16 scan with V == 128: when z is set, o receives the gated RMS norm of
+  // every output row, o * rsqrt(mean(o^2) + eps) * nw * silu(z), instead of o.
   const void* z;    // [Ttot, Hv, V] in z_dt (dense), or null
   int z_dt;         // 0 f32, 1 bf16
   const float* nw;  // [V] or null (ones)
   float eps;
 };
 
-// One record per (chunk slot, v-head), laid out for the scan's MFMA operand
-// reads: T diag(beta) as bf16 hi and lo, each six 1 KB fragments (row tile rt,
-// 32-wide column block m) for (rt, m) = (0,0) (1,0) (2,0) (3,0) (2,1) (3,1),
-// lane l of a fragment holding row 16 rt + l % 16 at the eight columns
-// 32 m + slot_row(8 (l / 16) + j), j = 0..7 (see device_common.h); then the
-// in-chunk cumulative gate G[64], gamma = e^G [64] and dec = e^(G_last - G) [64]
-// (fp32).  Rows and columns past the end of a partial chunk are zero (beta = 0
-// there) and G stays at its last value.
-constexpr int REC_TB_HI = 0;
-constexpr int REC_TB_LO = 6 * 1024;
-constexpr int REC_G = 12 * 1024;
-constexpr int REC_GAM = REC_G + 64 * 4;
-constexpr int REC_DEC = REC_GAM + 64 * 4;
-constexpr int PREP_RECORD_BYTES = REC_DEC + 64 * 4;  // 13 056
+// One record: T diag(beta) hi, lo (bf16, 10 tiles x 256 each), gamma[64] and
+// dec[64] (fp32), then P hi, lo; a state-only scan reads just the part before P.
+constexpr int PREP_REC_TB = 0;                        // 2 x 10 x 256 bf16
+constexpr int PREP_REC_GAM = PREP_REC_TB + 2 * 10 * 256 * 2;
+constexpr int PREP_REC_DEC = PREP_REC_GAM + 64 * 4;
+constexpr int PREP_REC_P = PREP_REC_DEC + 64 * 4;     // 2 x 10 x 256 bf16
+constexpr int PREP_RECORD_BYTES = PREP_REC_P + 2 * 10 * 256 * 2;
 
 // Number of chunk slots a launch over Ttot tokens in n_seqs sequences uses.
 int64_t chunk_slots(int64_t Ttot, int n_seqs);
-hipError_t launch_chunk_prep(const ChunkArgs& a, hipStream_t stream);
+// with_p: also form the output matrix P (needs q).
+hipError_t launch_chunk_prep(const ChunkArgs& a, int with_p, hipStream_t stream);
 
 hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t stream);
-// Workgroups the bf16 scan runs per sequence (or segment): output pass, or
-// segment pass 1 (augmented [M | b] columns).
-int chunk_scan_blocks(int Hqk, int Hv, int V, bool pass1);
-// Whether the bf16 scan can apply the gated output norm as it writes o: every
-// v-head's V columns lie in one workgroup.
-bool chunk_scan_fuses_norm(int Hqk, int Hv, int V);
 // prep + scan; with prep = false the records in a.tbuf must already be there
 hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t stream, bool prep = true);
 // Pass 1 of the segment scan: M columns (v = 0, S0 = I) and b columns (S0 = 0),

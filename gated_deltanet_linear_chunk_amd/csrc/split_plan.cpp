@@ -38,18 +38,21 @@ double makespan(const std::vector<double>& blocks, int cus) {
 
 }  // namespace
 
-// Upper bound on pass-1 segments: their blocks fit twice on the compute units.
-int max_prefix_segments(int blocks1, int cus) {
-  return std::max(0, 2 * cus / std::max(1, blocks1));
+// Upper bound on pass-1 segments: their blocks (K/128 + V/128 per head) fit
+// twice on the compute units.
+int max_prefix_segments(int32_t H_v, int32_t V, int cus) {
+  const int tiles1 = 1 + V / 128;
+  return std::max(0, 2 * cus / std::max(1, H_v * tiles1));
 }
 
 int64_t split_plan_ints_max(int n_seg, int n_prefix) {
   return 4 * (int64_t)n_seg + 1 + 5 * (int64_t)n_prefix;
 }
 
-bool plan_split(const int32_t* cu, int32_t N, int blocks2, int blocks1, bool has_s0, int cus,
+bool plan_split(const int32_t* cu, int32_t N, int32_t H_v, int32_t V, bool has_s0, int cus,
                 SplitPlan& out) {
-  const int pmax = max_prefix_segments(blocks1, cus);
+  const int tiles2 = V / 128, tiles1 = 1 + V / 128;
+  const int pmax = max_prefix_segments(H_v, V, cus);
   if (pmax == 0) return false;
   std::vector<int64_t> chunks(N);
   int64_t cmax = 0;
@@ -62,7 +65,7 @@ bool plan_split(const int32_t* cu, int32_t N, int blocks2, int blocks1, bool has
     std::sort(lens.begin(), lens.end(), std::greater<int64_t>());
     std::vector<double> blocks;
     for (int64_t c : lens)
-      for (int i = 0; i < blocks2; ++i) blocks.push_back((double)c);
+      for (int i = 0; i < H_v * tiles2; ++i) blocks.push_back((double)c);
     return makespan(blocks, cus);
   };
   const double base = pass2(chunks);
@@ -70,7 +73,7 @@ bool plan_split(const int32_t* cu, int32_t N, int blocks2, int blocks1, bool has
   // over the units: a run already within 15% of that is not split (and the
   // search below, costly for thousands of samples, is skipped).
   double work = 0.0;
-  for (int64_t c : chunks) work += (double)c * blocks2;
+  for (int64_t c : chunks) work += (double)c * H_v * tiles2;
   if (0.85 * base < work / cus) return false;
   double best = base;
   int64_t best_seg = 0;
@@ -86,9 +89,9 @@ bool plan_split(const int32_t* cu, int32_t N, int blocks2, int blocks1, bool has
       for (int64_t j = 0; j < s; ++j) lens.push_back(std::min(seg, chunks[n] - j * seg));
     }
     if (n_prefix == 0 || n_prefix > pmax) continue;
-    // a pass-1 block's chunk skips q, the output and P: about 0.65 of a
-    // pass-2 block's; a chain step costs about one chunk
-    std::vector<double> p1((size_t)n_prefix * blocks1, 0.65 * (double)seg);
+    // a pass-1 chunk skips q, the output and P: about 0.7 of a pass-2 chunk;
+    // a chain step costs about one chunk
+    std::vector<double> p1((size_t)n_prefix * H_v * tiles1, 0.7 * (double)seg);
     const double t = makespan(p1, cus) + (double)longest_chain + pass2(lens);
     if (t < best) {
       best = t;

@@ -21,16 +21,13 @@ struct SplitPlan {
   int off_chains() const { return off_pre() + n_prefix; }
 };
 
-// Most pass-1 segments a plan uses when one pass-1 segment takes blocks1
-// workgroups, on cus compute units.
-int max_prefix_segments(int blocks1, int cus);
+// Most pass-1 segments a plan uses for H_v heads of V columns on cus units.
+int max_prefix_segments(int32_t H_v, int32_t V, int cus);
 // Upper bound of SplitPlan::ints.size().
 int64_t split_plan_ints_max(int n_seg, int n_prefix);
 // Plans the split of the n samples at host offsets cu (cu[0] = 0, non-
-// decreasing), for a scan that runs a segment as blocks2 workgroups in the
-// output pass and blocks1 in pass 1; false when running them unsplit is
-// expected to be as fast.
-bool plan_split(const int32_t* cu, int32_t n, int blocks2, int blocks1, bool has_s0, int cus,
+// decreasing); false when running them unsplit is expected to be as fast.
+bool plan_split(const int32_t* cu, int32_t n, int32_t H_v, int32_t V, bool has_s0, int cus,
                 SplitPlan& out);
 
 }  // namespace gdn

@@ -1,5 +1,4 @@
-// Host driver for the split planner: reads
-// "blocks2 blocks1 has_s0 cus n len_0 .. len_{n-1}"
+// Host driver for the split planner: reads "H_v V has_s0 cus n len_0 .. len_{n-1}"
 // on stdin and prints the plan as whitespace-separated integers:
 // "split n_seg n_prefix n_chain" then the index arrays.
 #include <cstdio>
@@ -8,8 +7,8 @@
 #include "split_plan.h"
 
 int main() {
-  int blocks2, blocks1, has_s0, cus, n;
-  if (std::scanf("%d %d %d %d %d", &blocks2, &blocks1, &has_s0, &cus, &n) != 5) return 2;
+  int Hv, V, has_s0, cus, n;
+  if (std::scanf("%d %d %d %d %d", &Hv, &V, &has_s0, &cus, &n) != 5) return 2;
   std::vector<int32_t> cu(n + 1, 0);
   for (int i = 0; i < n; ++i) {
     int len;
@@ -17,9 +16,9 @@ int main() {
     cu[i + 1] = cu[i] + len;
   }
   gdn::SplitPlan p;
-  const bool split = gdn::plan_split(cu.data(), n, blocks2, blocks1, has_s0 != 0, cus, p);
+  const bool split = gdn::plan_split(cu.data(), n, Hv, V, has_s0 != 0, cus, p);
   std::printf("%d %d %d %d\n", split ? 1 : 0, p.n_seg, p.n_prefix, p.n_chain);
   for (int32_t x : p.ints) std::printf("%d ", x);
-  std::printf("\n%d\n", gdn::max_prefix_segments(blocks1, cus));
+  std::printf("\n%d\n", gdn::max_prefix_segments(Hv, V, cus));
   return 0;
 }

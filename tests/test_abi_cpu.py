@@ -87,7 +87,7 @@ def test_chunk_validation(lib):
     assert _chunk(lib, cu=FAKE, cu_host=start, n_seqs=2) == SEQ
     assert _chunk(lib, ws=None) == NULLP  # the bf16 path needs its T workspace
     need = lib.gdn_chunk_fwd_workspace_bytes(1, 64, 1, 32, 128, 128)
-    record = 2 * 6 * 1024 + 3 * 64 * 4  # per (chunk slot, v-head): T diag(beta) hi/lo, G, gamma, dec
+    record = 4 * 10 * 256 * 2 + 2 * 64 * 4  # per (chunk slot, v-head)
     plain = record * (1 + 1) * 32  # records of every chunk slot; the query adds room for splitting
     assert need >= plain
     assert _chunk(lib, ws_bytes=plain - 1) == SHAPE
@@ -110,11 +110,10 @@ def test_chunk_gated_norm_validation(lib):
     assert _chunk_norm(lib, eps=-1.0) == SHAPE
     assert _chunk_norm(lib, eps=float("nan")) == SHAPE
     assert _chunk_norm(lib, z=None) == NULLP  # fused path (bf16, V = 128)
-    assert _chunk_norm(lib, z=None, V=256) == NULLP  # fused path (two v-heads' 256 columns per workgroup)
-    assert _chunk_norm(lib, z=None, V=512) == NULLP  # chunk forward + norm kernel
+    assert _chunk_norm(lib, z=None, V=256) == NULLP  # chunk forward + norm kernel
     assert _chunk_norm(lib, in_dt=0, K=32, V=96) == UNSUP  # no norm kernel for V = 96
     # more norm rows than the norm kernel's grid holds: refused before the chunk forward is enqueued
-    assert _chunk_norm(lib, V=512, T=(1 << 31) - 1) == UNSUP
+    assert _chunk_norm(lib, V=256, T=(1 << 31) - 1) == UNSUP
     assert _chunk_norm(lib, q=None) == NULLP  # the chunk forward's own checks still apply
     assert _chunk_norm(lib, K=64) == UNSUP
     assert _chunk_norm(lib, ws=None) == NULLP
