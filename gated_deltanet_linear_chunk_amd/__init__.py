@@ -21,6 +21,7 @@ __all__ = [
     "gdn_gate_fwd",
     "gdn_conv1d_fwd",
     "gdn_chunk_fwd",
+    "gdn_chunk_fwd_noalloc",
     "gdn_chunk_fwd_gated_norm",
     "gdn_segment_state_scan",
     "gdn_chunk_fwd_segmented",
@@ -37,6 +38,8 @@ _LIB_NAME = "libgdn.so"
 _lib = None
 
 F32, BF16 = 0, 1
+# size of the fixed device array behind gdn_chunk_fwd_noalloc (GDN_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 EXPORTED_SYMBOLS = (
     "gdn_status_string",
@@ -45,6 +48,7 @@ EXPORTED_SYMBOLS = (
     "gdn_conv1d_fwd",
     "gdn_chunk_fwd_workspace_bytes",
     "gdn_chunk_fwd",
+    "gdn_chunk_fwd_noalloc",
     "gdn_chunk_fwd_gated_norm",
     "gdn_segment_state_scan_workspace_bytes",
     "gdn_segment_state_scan",
@@ -89,6 +93,8 @@ def load_library():
     lib.gdn_chunk_fwd_workspace_bytes.restype = sz
     lib.gdn_chunk_fwd.argtypes = [P, P, P, ctypes.c_int, i64, i64, i64, P, P, f32, P, P, P, i32, i32, i64, i32, i32,
                                   i32, i32, P, ctypes.c_int, P, P, sz, P]
+    lib.gdn_chunk_fwd_noalloc.argtypes = [P, P, P, ctypes.c_int, i64, i64, i64, P, P, f32, P, P, P, i32, i32, i64,
+                                          i32, i32, i32, i32, P, ctypes.c_int, P, P]
     lib.gdn_chunk_fwd_gated_norm.argtypes = [P, P, P, ctypes.c_int, i64, i64, i64, P, P, f32, P, P, P, i32, i32, i64,
                                              i32, i32, i32, i32, P, ctypes.c_int, P, f32, P, ctypes.c_int, P, P,
                                              sz, P]
@@ -103,7 +109,8 @@ def load_library():
     lib.gdn_decode_step.argtypes = [P, P, P, ctypes.c_int, P, P, f32, P, P, i64, i32, i32, i32, i32, i32, P,
                                     ctypes.c_int, P]
     lib.gdn_gated_rmsnorm_fwd.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P, f32, i64, i32, P, ctypes.c_int, P]
-    for name in ("gdn_gate_fwd", "gdn_conv1d_fwd", "gdn_chunk_fwd", "gdn_chunk_fwd_gated_norm", "gdn_segment_state_scan",
+    for name in ("gdn_gate_fwd", "gdn_conv1d_fwd", "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_gated_norm",
+                 "gdn_segment_state_scan",
                  "gdn_chunk_fwd_segmented", "gdn_decode_step", "gdn_gated_rmsnorm_fwd"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -286,6 +293,53 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale: float = 1.0, initial_state=None, cu_s
     )
     _check("gdn_chunk_fwd", st)
     return o, fin
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, g, beta, scale: float = 1.0, initial_state=None, cu_seqlens=None,
+                          cu_seqlens_host=None, o=None, final_state=None, o_dtype=None,
+                          output_final_state: bool = True):
+    """gdn_chunk_fwd with the per-chunk records in the library's fixed device array.
+
+    Arguments and results as gdn_chunk_fwd; no workspace.  Pass preallocated `o`
+    ([B, T, Hv, V]) and `final_state` ([N, Hv, K, V] fp32) to have nothing
+    allocated at all (e.g. under graph capture).  Calls that overlap on one
+    device race on the array.
+    """
+    torch = _torch()
+    dev = q.device
+    qs, ks, vs = _token_stride(q, "q"), _token_stride(k, "k"), _token_stride(v, "v")
+    if k.dtype != q.dtype or v.dtype != q.dtype or k.device != dev or v.device != dev:
+        raise ValueError("q, k, v must share dtype and device")
+    _require(g, "g", dev, torch.float32)
+    _require(beta, "beta", dev, torch.float32)
+    _require(initial_state, "initial_state", dev, torch.float32)
+    _require(cu_seqlens, "cu_seqlens", dev, torch.int32)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4:
+        raise ValueError("q, k must be [B, T, Hqk, K] and v [B, T, Hv, V]")
+    B, T, Hqk, K = q.shape
+    Hv, V = v.shape[2], v.shape[3]
+    if v.shape[:2] != (B, T) or g.shape != (B, T, Hv) or beta.shape != (B, T, Hv):
+        raise ValueError("v / g / beta shapes disagree with q")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if initial_state is not None and initial_state.shape != (N, Hv, K, V):
+        raise ValueError("initial_state must be [N, Hv, K, V]")
+    if o is None:
+        o = torch.empty((B, T, Hv, V), dtype=v.dtype if o_dtype is None else o_dtype, device=dev)
+    _require(o, "o", dev)
+    if o.shape != (B, T, Hv, V):
+        raise ValueError("o must be [B, T, Hv, V]")
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, Hv, K, V), dtype=torch.float32, device=dev)
+    _require(final_state, "final_state", dev, torch.float32)
+    if final_state is not None and final_state.shape != (N, Hv, K, V):
+        raise ValueError("final_state must be [N, Hv, K, V]")
+    st = load_library().gdn_chunk_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), qs, ks, vs, _ptr(g), _ptr(beta), float(scale), _ptr(initial_state),
+        _ptr(cu_seqlens), _host_offsets(cu_seqlens_host), 0 if cu_seqlens is None else N, B, T, Hqk, Hv, K, V,
+        _ptr(o), _dtype_code(o), _ptr(final_state), _stream(dev),
+    )
+    _check("gdn_chunk_fwd_noalloc", st)
+    return o, final_state
 
 
 def gdn_chunk_fwd_gated_norm(q, k, v, g, beta, z, norm_weight=None, eps: float = 1e-6, scale: float = 1.0,

@@ -1,13 +1,15 @@
 // api.cpp -- the extern "C" entry points declared in include/gdn.h.
 //
 // Host side only: argument validation (before anything is enqueued), choice of
-// kernel, and the launches.  Nothing here allocates device memory, keeps
-// global mutable state, or synchronises the host with the stream.
+// kernel, and the launches.  Nothing here allocates device memory or
+// synchronises the host with the stream; the only global state is the fixed
+// device array of gdn_chunk_fwd_noalloc and its per-device addresses.
 #include "gdn.h"
 
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "kernels.h"
@@ -15,7 +17,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int kMaxGrid = 65535;
 
 gdn_status hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
@@ -84,6 +86,8 @@ const char* gdn_status_string(int status) {
     case GDN_ERR_UNSUPPORTED: return "no kernel for this combination of sizes and dtype";
     case GDN_ERR_BAD_SEQLENS: return "malformed cu_seqlens / segment offsets, or offsets with B > 1";
     case GDN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case GDN_ERR_SCRATCH_TOO_SMALL:
+      return "the request needs more than the fixed scratch array of gdn_chunk_fwd_noalloc holds";
     default: return "unknown status";
   }
 }
@@ -140,6 +144,12 @@ struct FusedNorm {
   float eps;
 };
 
+// Source of the records' memory for callers without a workspace: called once
+// the arguments are validated, with the sizes of the bf16 run; sets the
+// workspace, or returns why it cannot.  Runs that use it are never split.
+typedef gdn_status (*FixedWorkspace)(hipStream_t stream, int64_t total, int32_t n_seqs, int32_t H_v,
+                                     void** workspace, size_t* workspace_bytes);
+
 static gdn_status chunk_fwd_run(const void* q, const void* k, const void* v, gdn_dtype in_dt,
                          int64_t q_token_stride, int64_t k_token_stride, int64_t v_token_stride,
                          const float* g, const float* beta, float scale,
@@ -147,7 +157,8 @@ static gdn_status chunk_fwd_run(const void* q, const void* k, const void* v, gdn
                          const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t B, int64_t T,
                          int32_t H_qk, int32_t H_v, int32_t K, int32_t V, void* o,
                          gdn_dtype o_dt, float* final_state, void* workspace,
-                         size_t workspace_bytes, const FusedNorm* norm, hipStream_t stream) {
+                         size_t workspace_bytes, const FusedNorm* norm, hipStream_t stream,
+                         FixedWorkspace fixed_ws = nullptr) {
   if (!valid_dtype(in_dt) || !valid_dtype(o_dt)) return GDN_ERR_BAD_DTYPE;
   if (B < 1 || T < 0 || H_qk < 1 || H_v < 1 || K < 1 || V < 1) return GDN_ERR_BAD_SHAPE;
   if (H_v % H_qk != 0) return GDN_ERR_BAD_SHAPE;
@@ -166,6 +177,10 @@ static gdn_status chunk_fwd_run(const void* q, const void* k, const void* v, gdn
   if (total == 0 && !final_state) return GDN_OK;
   if (total > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL_POINTER;
   if (in_dt == GDN_BF16) {
+    if (fixed_ws) {
+      const gdn_status st = fixed_ws(stream, total, N, H_v, &workspace, &workspace_bytes);
+      if (st != GDN_OK) return st;
+    }
     if (!workspace) return GDN_ERR_NULL_POINTER;
     if (workspace_bytes < tbuf_bytes(total, N, H_v)) return GDN_ERR_BAD_SHAPE;
   }
@@ -204,7 +219,7 @@ static gdn_status chunk_fwd_run(const void* q, const void* k, const void* v, gdn
     a.nw = norm->weight;
     a.eps = norm->eps;
   }
-  if (in_dt == GDN_BF16 && cu_seqlens && cu_seqlens_host && total > 0) {
+  if (!fixed_ws && in_dt == GDN_BF16 && cu_seqlens && cu_seqlens_host && total > 0) {
     gdn::SplitPlan plan;
     if (gdn::plan_split(cu_seqlens_host, N, H_v, V, initial_state != nullptr, device_cus(), plan) &&
         workspace_bytes >= split_workspace_bytes(total, plan.n_seg, plan.n_prefix, H_v, K, V)) {
@@ -261,6 +276,70 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, gdn_dtype 
   return chunk_fwd_run(q, k, v, in_dt, q_token_stride, k_token_stride, v_token_stride, g, beta, scale,
                        initial_state, cu_seqlens, cu_seqlens_host, n_seqs, B, T, H_qk, H_v, K, V, o, o_dt,
                        final_state, workspace, workspace_bytes, nullptr, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The records of gdn_chunk_fwd_noalloc.  Every GPU the library runs on holds
+// its own copy of this array until the process ends; host code uses the
+// per-device address that hipGetSymbolAddress returns, never the name.
+constexpr size_t kScratchBytes = GDN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// Address of `scratch` on the device of `stream` (which must be current),
+// looked up once per device.
+gdn_status scratch_address(hipStream_t stream, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GDN_ERR_HIP;
+  if (stream) {
+    hipDevice_t sdev = 0;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return GDN_ERR_HIP;
+    if (sdev != dev) return GDN_ERR_UNSUPPORTED;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return GDN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GDN_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDN_OK;
+}
+
+// FixedWorkspace over `scratch`: the size limit first, then the address.  The
+// records are written in full before they are read, so nothing is cleared.
+gdn_status scratch_workspace(hipStream_t stream, int64_t total, int32_t n_seqs, int32_t H_v,
+                             void** workspace, size_t* workspace_bytes) {
+  if (gdn::chunk_slots(total, n_seqs) > (int64_t)(kScratchBytes / ((size_t)gdn::PREP_RECORD_BYTES * (size_t)H_v)))
+    return GDN_ERR_SCRATCH_TOO_SMALL;
+  const gdn_status st = scratch_address(stream, workspace);
+  if (st != GDN_OK) return st;
+  *workspace_bytes = kScratchBytes;
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, gdn_dtype in_dt,
+                                 int64_t q_token_stride, int64_t k_token_stride,
+                                 int64_t v_token_stride, const float* g, const float* beta,
+                                 float scale, const float* initial_state,
+                                 const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                 int32_t n_seqs, int32_t B, int64_t T, int32_t H_qk, int32_t H_v,
+                                 int32_t K, int32_t V, void* o, gdn_dtype o_dt,
+                                 float* final_state, hipStream_t stream) {
+  return chunk_fwd_run(q, k, v, in_dt, q_token_stride, k_token_stride, v_token_stride, g, beta, scale,
+                       initial_state, cu_seqlens, cu_seqlens_host, n_seqs, B, T, H_qk, H_v, K, V, o, o_dt,
+                       final_state, nullptr, 0, nullptr, stream, scratch_workspace);
 }
 
 gdn_status gdn_chunk_fwd_gated_norm(const void* q, const void* k, const void* v, gdn_dtype in_dt,

@@ -22,8 +22,10 @@
  *
  * Conventions for every entry point:
  *  - Tensor arguments are DEVICE pointers to caller-owned, contiguous,
- *    row-major memory, 16-byte aligned.  The library allocates nothing, keeps
- *    no global mutable state, and never frees or retains caller memory.
+ *    row-major memory, 16-byte aligned.  The library allocates nothing and
+ *    never frees or retains caller memory.  Its only global state is the
+ *    fixed device array of gdn_chunk_fwd_noalloc (present on every device the
+ *    library's code is loaded on) and that array's per-device address.
  *  - Host pointers are named *_host and are read before the call returns.
  *  - Work is enqueued on `stream` (0 = the null stream) and the call returns
  *    without waiting for it.  Results are valid once the stream reaches them.
@@ -57,7 +59,8 @@ typedef enum gdn_status {
   GDN_ERR_BAD_DTYPE = 3,    /* dtype code not accepted by this entry point */
   GDN_ERR_UNSUPPORTED = 4,  /* valid request this build has no kernel for */
   GDN_ERR_BAD_SEQLENS = 5,  /* cu_seqlens / offsets malformed or with B > 1 */
-  GDN_ERR_HIP = 6           /* a HIP runtime call or kernel launch failed */
+  GDN_ERR_HIP = 6,          /* a HIP runtime call or kernel launch failed */
+  GDN_ERR_SCRATCH_TOO_SMALL = 7 /* gdn_chunk_fwd_noalloc: input beyond its fixed array */
 } gdn_status;
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -94,7 +97,7 @@ gdn_status gdn_gate_fwd(const float* a, const float* b, const float* A_log,
  *  w         [channels, width] in dt;  bias [channels] in dt or NULL
  *  cu_seqlens device int32 [n_seqs + 1] or NULL (then B rows of T tokens)
  *  width in [1, 4]; channels % 8 == 0; l2norm_channels % head_dim == 0;
- *  head_dim in {16, 32, 64, 128, 256} when l2norm_channels > 0.
+ *  head_dim a power of two in [8, 512] when l2norm_channels > 0.
  */
 gdn_status gdn_conv1d_fwd(const void* x, const void* w, const void* bias, gdn_dtype dt,
                           const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
@@ -143,6 +146,33 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, gdn_dtype 
                          int32_t H_qk, int32_t H_v, int32_t K, int32_t V, void* o,
                          gdn_dtype o_dt, float* final_state, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gdn_chunk_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as gdn_chunk_fwd without the workspace:
+ * the per-chunk records of the BF16 path live in a fixed device array of
+ * GDN_NOALLOC_SCRATCH_BYTES bytes built into the library (one per device,
+ * held until the process ends).  They take 20992 * H_v * (ceil(total/64) + N)
+ * bytes (total tokens, N sequences), which must fit
+ * (GDN_ERR_SCRATCH_TOO_SMALL otherwise; e.g. 8192 tokens in up to 71
+ * sequences at H_v = 32).  Packed runs are never segment-split here, so the
+ * call makes no host-to-device copy; it enqueues kernels only, and allocates
+ * and frees nothing.  Every call on one device shares that device's array:
+ * calls that overlap in time on one device (different streams, or threads)
+ * race and give wrong results; calls in one stream are ordered and safe.
+ * `stream` must belong to the current device (GDN_ERR_UNSUPPORTED otherwise).
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+gdn_status gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, gdn_dtype in_dt,
+                                 int64_t q_token_stride, int64_t k_token_stride,
+                                 int64_t v_token_stride, const float* g, const float* beta,
+                                 float scale, const float* initial_state,
+                                 const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                 int32_t n_seqs, int32_t B, int64_t T, int32_t H_qk, int32_t H_v,
+                                 int32_t K, int32_t V, void* o, gdn_dtype o_dt,
+                                 float* final_state, hipStream_t stream);
 
 /*
  * gdn_chunk_fwd followed by the gated output norm of gdn_gated_rmsnorm_fwd,

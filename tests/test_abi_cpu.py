@@ -13,7 +13,7 @@ import gated_deltanet_linear_chunk_amd as gdn
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdn.h")
 
-OK, NULLP, SHAPE, DTYPE, UNSUP, SEQ = 0, 1, 2, 3, 4, 5
+OK, NULLP, SHAPE, DTYPE, UNSUP, SEQ, HIP, SCRATCH = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 def _declared():
@@ -39,10 +39,10 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    for s in range(7):
+    for s in range(8):
         assert lib.gdn_status_string(s)
     assert b"unknown" in lib.gdn_status_string(99)
-    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_abi_version() == 2
 
 
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation first
@@ -94,6 +94,36 @@ def test_chunk_validation(lib):
     assert lib.gdn_chunk_fwd_workspace_bytes(0, 64, 1, 2, 32, 32) == 0  # fp32 path needs none
     # nothing to do: no tokens and no state requested
     assert _chunk(lib, T=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
+
+
+def _chunk_noalloc(lib, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, in_dt=1, qs=0, ks=0, vs=0, g=FAKE, beta=FAKE, scale=1.0, s0=None, cu=None,
+                cu_host=None, n_seqs=0, B=1, T=64, Hqk=16, Hv=32, K=128, V=128, o=FAKE, o_dt=0, fin=None, stream=None)
+    args.update(kw)
+    return lib.gdn_chunk_fwd_noalloc(*args.values())
+
+
+def test_chunk_noalloc_validation(lib):
+    # every argument check runs before the fixed array is looked up (no HIP call here)
+    assert _chunk_noalloc(lib, q=None) == NULLP
+    assert _chunk_noalloc(lib, in_dt=7) == DTYPE
+    assert _chunk_noalloc(lib, B=0) == SHAPE
+    assert _chunk_noalloc(lib, qs=100) == SHAPE
+    assert _chunk_noalloc(lib, K=64) == UNSUP
+    assert _chunk_noalloc(lib, cu=FAKE, n_seqs=2, B=2) == SEQ
+    # the records of 20992 bytes per (chunk slot, v-head) must fit GDN_NOALLOC_SCRATCH_BYTES
+    record = 4 * 10 * 256 * 2 + 2 * 64 * 4
+    assert record == 20992
+    slots_max = gdn.NOALLOC_SCRATCH_BYTES // (record * 32)
+    assert slots_max == 199
+    T = 64 * (slots_max - 1)  # 198 chunks + 1 sequence = 199 slots, the most that fit
+    assert _chunk_noalloc(lib, T=T + 64) == SCRATCH
+    assert _chunk_noalloc(lib, B=2, T=T) == SCRATCH  # 2 rows: two more slots than one row
+    cu_host = (ctypes.c_int32 * 3)(0, 64, 128)
+    assert _chunk_noalloc(lib, T=64 * 198, cu=FAKE, cu_host=None, n_seqs=2) == SCRATCH
+    assert _chunk_noalloc(lib, T=128, cu=FAKE, cu_host=cu_host, n_seqs=2, Hv=32 * 100) == SCRATCH
+    # fp32 inputs use no records: the size limit does not apply
+    assert _chunk_noalloc(lib, in_dt=0, K=32, V=32, Hqk=2, Hv=4, T=1 << 20, q=None) == NULLP
 
 
 def _chunk_norm(lib, **kw):
