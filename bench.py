@@ -1,26 +1,36 @@
 """Benchmark of the gated delta rule forward on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--extras/--no-extras] [--no-cpu]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R] [--no-extras] [--no-cpu]
 
 One step is one forward of a GatedDeltaNet layer's core over the packed
 workload (8192 tokens in 8 samples of seeded random lengths, H_qk = 16,
 H_v = 32, K = V = 128, bf16): gates, causal conv1d + SiLU + q/k L2 norm over
 the 8192 q|k|v channels, and the chunked delta rule reading q, k, v straight
-out of the conv output.  Inputs are resident in HBM before the timed region.
-The line printed is one JSON object (see the fields below); `value` is tokens
-per second of the whole step.  The duration of the gdn_chunk_fwd call (its
-kernels: chunk prep, segment pass 1, map chains, scan) is measured with HIP
-events recorded on the stream it runs on, and set against the HBM
-roofline (its algorithmic bytes) and the bf16 MFMA peak (its algorithmic
-flops).  The fp64 CPU oracle is timed on the same workload on the host.
-Extras time the other workloads (segment-parallel long sequence, batched
-prefill, wide state, the recurrent decode step on 256 sequences, and the
-gated output norm on the packed workload's output) with the same method.
+out of the conv output.  Inputs are resident in HBM before the timed region;
+the K timed steps cycle through four copies of the conv input, so no step
+finds its input in the caches the previous step filled.  `value` is tokens
+per second of the whole step (wall clock over the K steps, the device
+synchronised on both sides).
+
+Kernel lines time one library call at a time with HIP events recorded on the
+stream it runs on, R times, each after a 1 GiB read-modify-write of an
+unrelated buffer outside the events (so neither L2 nor the 256 MB MALL holds
+the inputs), and report mean, median, p10 and p90.  Each chunk-call line
+carries a roofline block: its algorithmic bytes and flops per call over the
+mean duration, against 8 TB/s HBM and against the bf16 matrix-core peak, both
+the published 2.5 PFLOP/s and the rate a probe kernel measures in the same
+run.  Lines: the packed workload's chunk call with fp32 and bf16 o and its
+conv; the long sequence in 8 segments through the segmented entry point and
+through the packed call's own split; the batched prefill (whole step, chunk
+call, conv); the wide-state workload; the recurrent decode step on 256
+sequences; the gated output norm; the chunk call with the norm fused.  The
+fp64 CPU oracle is timed on the packed workload on the host.
 """
 
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -39,6 +49,10 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "GDN fwd tokens/s at H_v=32,K=V=128 bf16; % bf16 MFMA peak"
 MAIN = "packed_varlen_bf16_T8192_N8_Hv32_K128"
+LONG = "long_segmented_bf16_T32768_P8_Hv32_K128"
+BATCHED = "batched_prefill_bf16_B8_T4096_Hv32_K128"
+WIDE = "wide_state_bf16_T32768_N4_H64_K128_V256"
+FLUSH_BYTES = 1 << 30
 
 
 def chunk_alg_flops(T, Hqk, Hv, K, V, C=64):
@@ -72,8 +86,8 @@ def sources_digest(names):
 
 def profiled_traffic(workload):
     """HBM bytes per gdn_chunk_fwd call (FETCH_SIZE + WRITE_SIZE of its kernels, scaled by a copy
-    calibration) from the committed rocprofv3 summary; None when the kernel sources have changed since
-    the counters were taken, or when there is no summary."""
+    calibration) from the committed rocprofv3 summary of that workload; None when the kernel sources
+    have changed since the counters were taken, or when there is no summary."""
     path = os.path.join(ROOT, "profiles", "chunk_fwd_%s.md" % workload)
     if not os.path.exists(path):
         return None
@@ -97,33 +111,93 @@ def _torch():
     return torch
 
 
-class Timer:
-    """HIP events on the current stream around one region; durations in ms."""
+class Flush:
+    """A 1 GiB buffer rewritten between timed reps (outside the events)."""
 
     def __init__(self):
-        self.pairs = []
-
-    def start(self):
         torch = _torch()
-        e = torch.cuda.Event(enable_timing=True)
-        e.record()
-        return e
+        self.buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
 
-    def stop(self, e0):
-        torch = _torch()
+    def __call__(self):
+        self.buf.add_(1.0)
+
+
+def time_call(call, reps, flush):
+    """Durations (ms) of `call` over reps, each after a flush, from HIP events on the current stream."""
+    torch = _torch()
+    pairs = []
+    for _ in range(reps):
+        flush()
+        e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
         e1.record()
-        self.pairs.append((e0, e1))
-
-    def mean_ms(self):
-        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else float("nan")
-
-    def reset(self):
-        self.pairs = []
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in pairs]
 
 
-def build_pipeline(w, d, o_dtype):
-    """Device inputs and a step function for a conv + gates + chunk workload."""
+def summary(ms):
+    ms = np.asarray(ms, dtype=np.float64)
+    return {"mean_ms": float(ms.mean()), "median_ms": float(np.median(ms)), "p10_ms": float(np.percentile(ms, 10)),
+            "p90_ms": float(np.percentile(ms, 90)), "reps": int(ms.size)}
+
+
+def roofline(alg_bytes, alg_flops, st, kernel, mfma_peak_tflops, traffic=None):
+    """Roofline block of one call: algorithmic bytes and flops over its mean duration."""
+    sec = st["mean_ms"] * 1e-3
+    achieved = alg_bytes / sec / 1e9
+    tflops = alg_flops / sec / 1e12
+    out = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+           "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, "kernel": kernel,
+           "alg_bytes_per_launch": int(alg_bytes), "alg_flops_per_launch": float(alg_flops),
+           "avg_launch_ms": st["mean_ms"], "median_ms": st["median_ms"], "p10_ms": st["p10_ms"],
+           "p90_ms": st["p90_ms"], "reps": st["reps"], "mfma_tflops": tflops,
+           "mfma_frac_published_peak": tflops / PEAK_BF16_TFLOPS}
+    if mfma_peak_tflops:
+        out["mfma_frac_measured_peak"] = tflops / mfma_peak_tflops
+    if traffic:
+        out["traffic_over_alg"] = traffic / alg_bytes
+    return out
+
+
+def measure_mfma_peak():
+    """Dense bf16 matrix-core rate (TFLOP/s) of this device from the probe kernel; None without it."""
+    torch = _torch()
+    path = os.path.join(ROOT, "gated_deltanet_linear_chunk_amd", "libgdn_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.gdn_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.gdn_probe_mfma_bf16.restype = ctypes.c_int
+    lib.gdn_probe_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.gdn_probe_mfma_bf16_flops.restype = ctypes.c_double
+    props = torch.cuda.get_device_properties(0)
+    blocks = 8 * props.multi_processor_count  # 32 waves per compute unit
+    iters = 4096
+    out = torch.empty(blocks, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def call():
+        rc = lib.gdn_probe_mfma_bf16(blocks, iters, out.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError("probe launch failed (%d)" % rc)
+
+    call()
+    torch.cuda.synchronize()
+    ms = time_call(call, 10, lambda: None)
+    flops = lib.gdn_probe_mfma_bf16_flops(blocks, iters)
+    return flops / (float(np.median(ms)) * 1e-3) / 1e12
+
+
+def rotated_inputs(x, copies):
+    """`copies` separate buffers holding x (the first is x itself)."""
+    return [x] + [x.clone() for _ in range(copies - 1)]
+
+
+def build_pipeline(w, d, o_dtype, rotate=4):
+    """Device inputs and the calls of a conv + gates + chunk workload."""
     torch = _torch()
     import gated_deltanet_linear_chunk_amd as gdn
 
@@ -135,45 +209,48 @@ def build_pipeline(w, d, o_dtype):
     f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)  # noqa: E731
     B = w.batch_rows
     L = T // B
-    x = bf(d["x"]).reshape(B, L, C) if B > 1 else bf(d["x"])
+    x0 = bf(d["x"]).reshape(B, L, C) if B > 1 else bf(d["x"])
+    xs = rotated_inputs(x0, rotate)
     cw, cb = bf(d["conv_w"]), bf(d["conv_bias"])
     a, b = f32(d["a"]).reshape(B, L, Hv), f32(d["b"]).reshape(B, L, Hv)
     A_log, dt_bias = f32(d["A_log"]), f32(d["dt_bias"])
     cu = None if B > 1 else torch.from_numpy(d["cu_seqlens"]).to(dev)
     cu_host = None if B > 1 else d["cu_seqlens"]
     s0 = f32(d["s0"]) if "s0" in d else None
-    chunk_timer = Timer()
-    conv_timer = Timer()
+    state = {"i": 0}
 
-    # Only the gdn_chunk_fwd call is bracketed by timing events inside a step:
-    # each recorded timing event leaves the GPU idle for a few microseconds, so
-    # the conv is timed in a loop of its own (conv_step) after the timed region.
-    def conv():
+    def conv(x=x0):
         return gdn.gdn_conv1d_fwd(x, cw, cb, cu_seqlens=cu, cu_seqlens_host=cu_host, l2norm_channels=2 * Hqk * K,
                                   head_dim=K)
 
-    def conv_step():
-        e = conv_timer.start()
-        conv()
-        conv_timer.stop(e)
-
-    def step(time_kernels=False):
-        y = conv().reshape(B, L, C)
+    def qkv(y):
+        y = y.reshape(B, L, C)
         q = y[..., : Hqk * K].unflatten(-1, (Hqk, K))
         k = y[..., Hqk * K : 2 * Hqk * K].unflatten(-1, (Hqk, K))
         v = y[..., 2 * Hqk * K :].unflatten(-1, (Hv, V))
+        return q, k, v
+
+    def chunk(q, k, v, g, beta, od=o_dtype):
+        return gdn.gdn_chunk_fwd(q, k, v, g, beta, initial_state=s0, cu_seqlens=cu, cu_seqlens_host=cu_host,
+                                 o_dtype=od)
+
+    def step():
+        x = xs[state["i"] % len(xs)]
+        state["i"] += 1
+        q, k, v = qkv(conv(x))
         g, beta = gdn.gdn_gate_fwd(a, b, A_log, dt_bias)
-        e = chunk_timer.start() if time_kernels else None
-        o, fin = gdn.gdn_chunk_fwd(q, k, v, g, beta, initial_state=s0, cu_seqlens=cu, cu_seqlens_host=cu_host,
-                                   o_dtype=o_dtype)
-        if time_kernels:
-            chunk_timer.stop(e)
-        return o, fin
+        return chunk(q, k, v, g, beta)
 
-    return step, chunk_timer, conv_timer, conv_step
+    def chunk_inputs():
+        q, k, v = qkv(conv())
+        g, beta = gdn.gdn_gate_fwd(a, b, A_log, dt_bias)
+        return q, k, v, g, beta
+
+    return {"step": step, "conv": conv, "chunk": chunk, "chunk_inputs": chunk_inputs, "C": C}
 
 
-def build_chunk_only(w, d, o_dtype, segmented=False, gated_norm=False):
+def build_chunk_only(w, d, o_dtype, mode="plain"):
+    """The chunk call of a workload with q, k, v given (mode plain, segmented or gated_norm)."""
     torch = _torch()
     import gated_deltanet_linear_chunk_amd as gdn
 
@@ -181,49 +258,22 @@ def build_chunk_only(w, d, o_dtype, segmented=False, gated_norm=False):
     bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)  # noqa: E731
     f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)  # noqa: E731
     q, k, v = bf(d["q"])[None], bf(d["k"])[None], bf(d["v"])[None]
-    a, b = f32(d["a"])[None], f32(d["b"])[None]
-    A_log, dt_bias = f32(d["A_log"]), f32(d["dt_bias"])
-    timer = Timer()
-    if segmented:
+    g, beta = gdn.gdn_gate_fwd(f32(d["a"])[None], f32(d["b"])[None], f32(d["A_log"]), f32(d["dt_bias"]))
+    if mode == "segmented":
         off = d["seg_offsets"]
         off_dev = torch.from_numpy(off).to(dev)
         ws = torch.empty(gdn.gdn_segmented_workspace_bytes(w.total_tokens, len(off) - 1, w.Hv, w.K, w.V),
                          dtype=torch.uint8, device=dev)
-
-        def step(time_kernels=False):
-            g, beta = gdn.gdn_gate_fwd(a, b, A_log, dt_bias)
-            e = timer.start() if time_kernels else None
-            out = gdn.gdn_chunk_fwd_segmented(q, k, v, g, beta, off_dev, off, o_dtype=o_dtype, workspace=ws)
-            if time_kernels:
-                timer.stop(e)
-            return out
-    elif gated_norm:
-        cu = torch.from_numpy(d["cu_seqlens"]).to(dev)
+        return lambda: gdn.gdn_chunk_fwd_segmented(q, k, v, g, beta, off_dev, off, o_dtype=o_dtype, workspace=ws)
+    cu = torch.from_numpy(d["cu_seqlens"]).to(dev)
+    if mode == "gated_norm":
         rng = np.random.default_rng(5)
         z = bf(rng.standard_normal((w.total_tokens, w.Hv, w.V)).astype(np.float32))[None]
         nw = f32(rng.uniform(0.5, 1.5, w.V))
-
-        def step(time_kernels=False):
-            g, beta = gdn.gdn_gate_fwd(a, b, A_log, dt_bias)
-            e = timer.start() if time_kernels else None
-            out = gdn.gdn_chunk_fwd_gated_norm(q, k, v, g, beta, z, norm_weight=nw, cu_seqlens=cu,
-                                               cu_seqlens_host=d["cu_seqlens"], o_dtype=o_dtype)
-            if time_kernels:
-                timer.stop(e)
-            return out
-    else:
-        cu = torch.from_numpy(d["cu_seqlens"]).to(dev)
-
-        def step(time_kernels=False):
-            g, beta = gdn.gdn_gate_fwd(a, b, A_log, dt_bias)
-            e = timer.start() if time_kernels else None
-            out = gdn.gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens=cu, cu_seqlens_host=d["cu_seqlens"],
-                                    o_dtype=o_dtype)
-            if time_kernels:
-                timer.stop(e)
-            return out
-
-    return step, timer
+        return lambda: gdn.gdn_chunk_fwd_gated_norm(q, k, v, g, beta, z, norm_weight=nw, cu_seqlens=cu,
+                                                    cu_seqlens_host=d["cu_seqlens"], o_dtype=o_dtype)
+    return lambda: gdn.gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens=cu, cu_seqlens_host=d["cu_seqlens"],
+                                     o_dtype=o_dtype)
 
 
 DECODE_N = 256  # sequences per decode step
@@ -246,16 +296,7 @@ def build_decode(N, Hqk, Hv, K, V):
     q, k, v = bf(d["q"]), bf(d["k"]), bf(d["v"])
     g, beta = gdn.gdn_gate_fwd(f32(d["a"]), f32(d["b"]), f32(d["A_log"]), f32(d["dt_bias"]))
     state = f32(d["s0"])
-    timer = Timer()
-
-    def step(time_kernels=False):
-        e = timer.start() if time_kernels else None
-        o = gdn.gdn_decode_step(q, k, v, g, beta, state, o_dtype=torch.float32)
-        if time_kernels:
-            timer.stop(e)
-        return o
-
-    return step, timer
+    return lambda: gdn.gdn_decode_step(q, k, v, g, beta, state, o_dtype=torch.float32)
 
 
 def build_gated_norm(rows, V):
@@ -269,26 +310,18 @@ def build_gated_norm(rows, V):
     z = torch.randn((rows, V), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
     w = torch.rand((V,), generator=gen, device=dev, dtype=torch.float32) + 0.5
     y = torch.empty((rows, V), dtype=torch.bfloat16, device=dev)
-    timer = Timer()
-
-    def step(time_kernels=False):
-        e = timer.start() if time_kernels else None
-        out = gdn.gdn_gated_rmsnorm_fwd(o, z, w, eps=1e-6, out=y)
-        if time_kernels:
-            timer.stop(e)
-        return out
-
-    return step, timer
+    return lambda: gdn.gdn_gated_rmsnorm_fwd(o, z, w, eps=1e-6, out=y)
 
 
-def timed(step, steps, warmup):
+def timed_steps(step, steps, warmup):
+    """Wall-clock seconds per step over exactly `steps` steps after `warmup` untimed ones."""
     torch = _torch()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        step(time_kernels=True)
+        step()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) / steps
 
@@ -314,14 +347,58 @@ def cpu_baseline(w, d):
     }
 
 
+SPLIT_KERNELS = ("plan_store_kernel + chunk_prep_kernel + chunk_scan_kernel<2,8> + compose_kernel + "
+                 "chunk_scan_kernel<%d,8>")
+
+
+def pipeline_lines(name, w, d, o_dtype, o_bytes, reps, flush, peak, steps, warmup, main=False):
+    """Whole-step rate, chunk-call roofline and conv line of a conv + gates + chunk workload."""
+    torch = _torch()
+    p = build_pipeline(w, d, o_dtype)
+    T, N = w.total_tokens, (w.batch_rows if w.batch_rows > 1 else w.n_samples)
+    s0 = "s0" in d
+    sec = timed_steps(p["step"], steps, warmup)
+    q, k, v, g, beta = p["chunk_inputs"]()
+    packed = w.batch_rows == 1
+    kernels = (SPLIT_KERNELS % (0 if o_bytes == 4 else 1)) if packed else \
+        "chunk_prep_kernel + chunk_scan_kernel<%d,8>" % (0 if o_bytes == 4 else 1)
+    st = summary(time_call(lambda: p["chunk"](q, k, v, g, beta), reps, flush))
+    lines = {
+        "step": {"tokens_per_s": T / sec, "ms_per_step": sec * 1e3, "steps": steps, "warmup": warmup},
+        "chunk": roofline(chunk_alg_bytes(T, N, w.Hqk, w.Hv, w.K, w.V, o_bytes, s0=s0),
+                          chunk_alg_flops(T, w.Hqk, w.Hv, w.K, w.V),
+                          st, "gdn_chunk_fwd (%s) = %s" % ("segment-split path" if packed else "batched rows", kernels),
+                          peak, profiled_traffic(name) if o_bytes == 4 else None),
+    }
+    if main:
+        other = torch.bfloat16 if o_bytes == 4 else torch.float32
+        ob = 2 if o_bytes == 4 else 4
+        st2 = summary(time_call(lambda: p["chunk"](q, k, v, g, beta, other), reps, flush))
+        lines["chunk_%so" % ("bf16" if ob == 2 else "f32")] = roofline(
+            chunk_alg_bytes(T, N, w.Hqk, w.Hv, w.K, w.V, ob, s0=s0), chunk_alg_flops(T, w.Hqk, w.Hv, w.K, w.V), st2,
+            "gdn_chunk_fwd with %s o" % ("bf16" if ob == 2 else "fp32"), peak)
+    cst = summary(time_call(p["conv"], reps, flush))
+    cb = conv_alg_bytes(T, p["C"])
+    lines["conv1d"] = dict(cst, hbm_frac=cb / (cst["mean_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                           achieved_gbs=cb / (cst["mean_ms"] * 1e-3) / 1e9, alg_bytes=cb,
+                           kernel="conv1d_kernel (bf16, fast rounding)")
+    del p, q, k, v, g, beta
+    torch.cuda.empty_cache()
+    return lines
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--reps", type=int, default=30, help="flushed reps per kernel line")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--o-dtype", choices=["f32", "bf16"], default="f32")
+    ap.add_argument("--only", default="",
+                    help="comma-separated extras to run (segmented, split, batched, wide, decode, norm, fused); "
+                         "default all")
     ap.add_argument("--copy-only", type=int, default=0,
                     help="only run N plain 256 MiB device copies (counter calibration for profiles)")
     args = ap.parse_args()
@@ -347,28 +424,23 @@ def main():
 
     o_dtype = torch.float32 if args.o_dtype == "f32" else torch.bfloat16
     o_bytes = 4 if args.o_dtype == "f32" else 2
+    reps = max(30, args.reps)
+    flush = Flush()
+    peak = measure_mfma_peak()
     w = gdn_inputs.WORKLOADS[MAIN]
     d = gdn_inputs.draw(w, with_qkv=False)
-    step, chunk_t, conv_t, conv_step = build_pipeline(w, d, o_dtype)
-    sec = timed(step, args.steps, args.warmup)
-    for _ in range(args.steps):
-        conv_step()
-    torch.cuda.synchronize()
+    main_lines = pipeline_lines(MAIN, w, d, o_dtype, o_bytes, reps, flush, peak, args.steps, args.warmup, main=True)
     T, N = w.total_tokens, w.n_samples
-    chunk_ms = chunk_t.mean_ms()
-    conv_ms = conv_t.mean_ms()
-    bytes_chunk = chunk_alg_bytes(T, N, w.Hqk, w.Hv, w.K, w.V, o_bytes)
-    flops_chunk = chunk_alg_flops(T, w.Hqk, w.Hv, w.K, w.V)
-    achieved = bytes_chunk / (chunk_ms * 1e-3) / 1e9
-    C = 2 * w.Hqk * w.K + w.Hv * w.V
+    step = main_lines["step"]
+    chunk = main_lines["chunk"]
     result = {
         "metric": METRIC,
-        "value": T / sec,
+        "value": step["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": sec * 1e3,
+        "ms_per_step": step["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -377,72 +449,77 @@ def main():
         "config": {"workload": MAIN, "global_batch": N, "seq_len": T, "parallelism": "none (1 GPU)",
                    "H_qk": w.Hqk, "H_v": w.Hv, "K": w.K, "V": w.V, "chunk": 64, "conv_width": 4,
                    "o_dtype": args.o_dtype, "step": "gates + conv1d/SiLU/L2 + chunked rule"},
-        "mfma_frac_chunk": flops_chunk / (chunk_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": profiled_traffic(MAIN),
-                     "kernel": "gdn_chunk_fwd (segment-split path) = plan copy + chunk_prep_kernel + "
-                               "chunk_scan_kernel<2,8> + compose_kernel + chunk_scan_kernel<0,8>",
-                     "alg_bytes_per_launch": bytes_chunk, "alg_flops_per_launch": flops_chunk,
-                     "avg_launch_ms": chunk_ms},
-        "kernels_ms": {"chunk": chunk_ms, "conv1d": conv_ms},
-        "conv1d_hbm_frac": conv_alg_bytes(T, C) / (conv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "mfma_frac_chunk": chunk["mfma_frac_published_peak"],
+        "mfma_peak_measured_tflops": peak,
+        "roofline": chunk,
+        "kernels_ms": {"chunk": chunk["avg_launch_ms"], "conv1d": main_lines["conv1d"]["mean_ms"]},
+        "conv1d_hbm_frac": main_lines["conv1d"]["hbm_frac"],
+        "lines": {"%s[%s]" % (MAIN, k): v for k, v in main_lines.items() if k != "step"},
     }
+    print("main lines done", file=sys.stderr, flush=True)
 
     if not args.no_extras:
-        extras = {}
-        del step
-        torch.cuda.empty_cache()
-        for name, kind in (("long_segmented_bf16_T32768_P8_Hv32_K128", "segmented"),
-                           ("long_segmented_bf16_T32768_P8_Hv32_K128", "unsegmented"),
-                           ("batched_prefill_bf16_B8_T4096_Hv32_K128", "pipeline"),
-                           ("wide_state_bf16_T32768_N4_H64_K128_V256", "chunk")):
-            wx = gdn_inputs.WORKLOADS[name]
-            dx = gdn_inputs.draw(wx, with_qkv=(kind != "pipeline"))
-            if kind == "pipeline":
-                st, tm, _, _ = build_pipeline(wx, dx, o_dtype)
-            else:
-                st, tm = build_chunk_only(wx, dx, o_dtype, segmented=(kind == "segmented"))
-            s = timed(st, max(3, args.steps // 4), 2)
-            ms = tm.mean_ms()
-            fl = chunk_alg_flops(wx.total_tokens, wx.Hqk, wx.Hv, wx.K, wx.V)
-            extras["%s[%s]" % (name, kind)] = {
-                "tokens_per_s": wx.total_tokens / s, "ms_per_step": s * 1e3, "main_kernel_ms": ms,
-                "mfma_frac_useful": fl / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
-            }
-            del st, dx
+        only = set(x for x in args.only.split(",") if x)
+        want = lambda key: not only or key in only  # noqa: E731
+        lines = result["lines"]
+        wl = gdn_inputs.WORKLOADS[LONG]
+        if want("segmented") or want("split"):
+            dl = gdn_inputs.draw(wl, with_qkv=True)
+            fl = chunk_alg_flops(wl.total_tokens, wl.Hqk, wl.Hv, wl.K, wl.V)
+            by = chunk_alg_bytes(wl.total_tokens, 1, wl.Hqk, wl.Hv, wl.K, wl.V, o_bytes)
+            if want("segmented"):
+                st = summary(time_call(build_chunk_only(wl, dl, o_dtype, "segmented"), reps, flush))
+                lines["%s[segmented entry point]" % LONG] = roofline(
+                    by, fl, st, "gdn_chunk_fwd_segmented = plan_store_kernel + chunk_prep_kernel + "
+                    "chunk_scan_kernel<2,8> + compose_kernel + chunk_scan_kernel<0,8>", peak)
+            if want("split"):
+                st = summary(time_call(build_chunk_only(wl, dl, o_dtype), reps, flush))
+                lines["%s[planner-split packed call]" % LONG] = roofline(
+                    by, fl, st, "gdn_chunk_fwd with host offsets (one sample; the planner splits it)", peak)
+            del dl
             torch.cuda.empty_cache()
-        st, tm = build_decode(DECODE_N, 16, 32, 128, 128)
-        s = timed(st, max(3, args.steps // 4), 2)
-        ms = tm.mean_ms()
-        nbytes = decode_alg_bytes(DECODE_N, 16, 32, 128, 128)
-        extras["decode_bf16_N%d_Hv32_K128[decode step]" % DECODE_N] = {
-            "tokens_per_s": DECODE_N / s, "ms_per_step": s * 1e3, "main_kernel_ms": ms,
-            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "alg_bytes": nbytes,
-        }
-        del st
-        torch.cuda.empty_cache()
-        rows = w.total_tokens * w.Hv
-        st, tm = build_gated_norm(rows, w.V)
-        s = timed(st, max(3, args.steps // 4), 2)
-        ms = tm.mean_ms()
-        nbytes = rows * w.V * (4 + 2 + 2)
-        extras["gated_norm_f32o_bf16z_T8192_Hv32_V128[norm]"] = {
-            "tokens_per_s": w.total_tokens / s, "ms_per_step": s * 1e3, "main_kernel_ms": ms,
-            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "alg_bytes": nbytes,
-        }
-        del st
-        torch.cuda.empty_cache()
-        # the chunk forward with the gated norm applied as the scan writes o (bf16 z and y), against
-        # the chunk call above plus the separate norm kernel
-        dx = gdn_inputs.draw(w, with_qkv=True)
-        st, tm = build_chunk_only(w, dx, torch.bfloat16, gated_norm=True)
-        s = timed(st, max(3, args.steps // 4), 2)
-        extras["%s[chunk + gated norm fused, bf16 z and y]" % MAIN] = {
-            "tokens_per_s": w.total_tokens / s, "ms_per_step": s * 1e3, "main_kernel_ms": tm.mean_ms(),
-        }
-        del st, dx
-        torch.cuda.empty_cache()
-        result["extras"] = extras
+            print("long-sequence lines done", file=sys.stderr, flush=True)
+        if want("batched"):
+            wb = gdn_inputs.WORKLOADS[BATCHED]
+            db = gdn_inputs.draw(wb, with_qkv=False)
+            for k, v in pipeline_lines(BATCHED, wb, db, o_dtype, o_bytes, reps, flush, peak,
+                                       max(3, args.steps // 2), 2).items():
+                lines["%s[%s]" % (BATCHED, k)] = v
+            del db
+            print("batched lines done", file=sys.stderr, flush=True)
+        if want("wide"):
+            ww = gdn_inputs.WORKLOADS[WIDE]
+            dw = gdn_inputs.draw(ww, with_qkv=True)
+            st = summary(time_call(build_chunk_only(ww, dw, o_dtype), reps, flush))
+            lines["%s[chunk]" % WIDE] = roofline(
+                chunk_alg_bytes(ww.total_tokens, ww.n_samples, ww.Hqk, ww.Hv, ww.K, ww.V, o_bytes),
+                chunk_alg_flops(ww.total_tokens, ww.Hqk, ww.Hv, ww.K, ww.V), st,
+                "gdn_chunk_fwd (V = 256: two column tiles per head)", peak, profiled_traffic(WIDE))
+            del dw
+            torch.cuda.empty_cache()
+            print("wide line done", file=sys.stderr, flush=True)
+        if want("decode"):
+            st = summary(time_call(build_decode(DECODE_N, 16, 32, 128, 128), reps, flush))
+            nbytes = decode_alg_bytes(DECODE_N, 16, 32, 128, 128)
+            lines["decode_bf16_N%d_Hv32_K128[decode step]" % DECODE_N] = dict(
+                st, tokens_per_s=DECODE_N / (st["mean_ms"] * 1e-3),
+                hbm_frac=nbytes / (st["mean_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, alg_bytes=nbytes)
+            torch.cuda.empty_cache()
+        if want("norm"):
+            rows = w.total_tokens * w.Hv
+            st = summary(time_call(build_gated_norm(rows, w.V), reps, flush))
+            nbytes = rows * w.V * (4 + 2 + 2)
+            lines["gated_norm_f32o_bf16z_T8192_Hv32_V128[norm]"] = dict(
+                st, hbm_frac=nbytes / (st["mean_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, alg_bytes=nbytes)
+            torch.cuda.empty_cache()
+        if want("fused"):
+            # the chunk forward with the gated norm applied as the scan writes o (bf16 z and y)
+            dx = gdn_inputs.draw(w, with_qkv=True)
+            st = summary(time_call(build_chunk_only(w, dx, torch.bfloat16, "gated_norm"), reps, flush))
+            lines["%s[chunk + gated norm fused, bf16 z and y]" % MAIN] = dict(
+                st, tokens_per_s=w.total_tokens / (st["mean_ms"] * 1e-3))
+            del dx
+            torch.cuda.empty_cache()
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, d)

@@ -88,7 +88,8 @@ def load_library():
     lib.gdn_abi_version.argtypes = []
     lib.gdn_abi_version.restype = ctypes.c_int
     lib.gdn_gate_fwd.argtypes = [P, P, P, P, i64, i32, P, P, P]
-    lib.gdn_conv1d_fwd.argtypes = [P, P, P, ctypes.c_int, P, P, i32, i32, i64, i32, i32, i32, i32, i32, f32, P, P]
+    lib.gdn_conv1d_fwd.argtypes = [P, P, P, ctypes.c_int, P, P, i32, i32, i64, i32, i32, i32, i32, i32, f32,
+                                   ctypes.c_int, P, P]
     lib.gdn_chunk_fwd_workspace_bytes.argtypes = [ctypes.c_int, i64, i32, i32, i32, i32]
     lib.gdn_chunk_fwd_workspace_bytes.restype = sz
     lib.gdn_chunk_fwd.argtypes = [P, P, P, ctypes.c_int, i64, i64, i64, P, P, f32, P, P, P, i32, i32, i64, i32, i32,
@@ -209,10 +210,13 @@ def gdn_gate_fwd(a, b, A_log, dt_bias):
 
 
 def gdn_conv1d_fwd(x, w, bias=None, cu_seqlens=None, cu_seqlens_host=None, apply_silu: bool = True,
-                   l2norm_channels: int = 0, head_dim: int = 128, l2_eps: float = 1e-6):
+                   l2norm_channels: int = 0, head_dim: int = 128, l2_eps: float = 1e-6, exact_rounding: bool = False):
     """Causal depthwise conv1d (+ SiLU, + per-head L2 norm of the first l2norm_channels).
 
     x [B, T, C] or [T, C] (packed, with cu_seqlens); w [C, W]; bias [C] or None.
+    exact_rounding: bf16 outputs of the unnormalised channels are the bf16
+    nearest to the exact value (GDN_ROUND_EXACT) instead of the rounded fp32
+    evaluation.
     """
     torch = _torch()
     dev = x.device
@@ -231,7 +235,8 @@ def gdn_conv1d_fwd(x, w, bias=None, cu_seqlens=None, cu_seqlens_host=None, apply
     host = _host_offsets(cu_seqlens_host)
     st = load_library().gdn_conv1d_fwd(
         _ptr(x), _ptr(w), _ptr(bias), _dtype_code(x), _ptr(cu_seqlens), host, n_seqs, B, T, C, w.shape[1],
-        int(bool(apply_silu)), int(l2norm_channels), int(head_dim), float(l2_eps), _ptr(y), _stream(dev),
+        int(bool(apply_silu)), int(l2norm_channels), int(head_dim), float(l2_eps), int(bool(exact_rounding)), _ptr(y),
+        _stream(dev),
     )
     _check("gdn_conv1d_fwd", st)
     return y

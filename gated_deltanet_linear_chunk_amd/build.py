@@ -3,7 +3,9 @@
 python -m gated_deltanet_linear_chunk_amd.build [--jobs N]
 
 Objects go to _build/ at the repository root; the shared library lands next
-to this file, where the Python binding loads it from.
+to this file, where the Python binding loads it from.  The same call builds
+libgdn_probe.so (csrc/probe/: the matrix-core rate probe the benchmark
+reports against), which the library does not use.
 """
 
 from __future__ import annotations
@@ -20,6 +22,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
+PROBE_LIB = os.path.join(PKG, "libgdn_probe.so")
+PROBE_SOURCES = ["probe/mfma_peak.hip"]
 
 SOURCES = ["api.cpp", "split_plan.cpp", "gate_conv.hip", "chunk_f32.hip", "chunk_prep.hip", "chunk_bf16.hip",
            "compose.hip", "decode.hip", "gated_norm.hip"]
@@ -40,7 +44,7 @@ FLAGS = [
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    obj = os.path.join(BUILD, os.path.splitext(src.replace("/", "_"))[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
     cmd = [HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,16 +57,21 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 4) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 4) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(objs[: len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     return LIB
 
 

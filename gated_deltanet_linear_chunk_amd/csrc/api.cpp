@@ -106,8 +106,10 @@ gdn_status gdn_conv1d_fwd(const void* x, const void* w, const void* bias, gdn_dt
                           const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
                           int32_t n_seqs, int32_t B, int64_t T, int32_t channels,
                           int32_t width, int32_t apply_silu, int32_t l2norm_channels,
-                          int32_t head_dim, float l2_eps, void* y, hipStream_t stream) {
+                          int32_t head_dim, float l2_eps, gdn_rounding rounding, void* y,
+                          hipStream_t stream) {
   if (!valid_dtype(dt)) return GDN_ERR_BAD_DTYPE;
+  if (rounding != GDN_ROUND_FAST && rounding != GDN_ROUND_EXACT) return GDN_ERR_BAD_SHAPE;
   if (B < 1 || T < 0 || channels <= 0 || channels % 8 != 0) return GDN_ERR_BAD_SHAPE;
   if (width < 1 || width > 4) return GDN_ERR_UNSUPPORTED;
   if (l2norm_channels < 0 || l2norm_channels > channels) return GDN_ERR_BAD_SHAPE;
@@ -124,7 +126,8 @@ gdn_status gdn_conv1d_fwd(const void* x, const void* w, const void* bias, gdn_dt
   if (!x || !w || !y) return GDN_ERR_NULL_POINTER;
   if ((total + 31) / 32 > kMaxGrid) return GDN_ERR_UNSUPPORTED;
   return hip_status(gdn::launch_conv1d(x, w, bias, dt, cu_seqlens, n_seqs, B, T, channels, width,
-                                       apply_silu, l2norm_channels, head_dim, l2_eps, y, stream));
+                                       apply_silu, l2norm_channels, head_dim, l2_eps,
+                                       rounding == GDN_ROUND_EXACT ? 1 : 0, y, stream));
 }
 
 size_t gdn_chunk_fwd_workspace_bytes(gdn_dtype in_dt, int64_t total_tokens, int32_t n_seqs,
@@ -235,8 +238,7 @@ static gdn_status chunk_fwd_run(const void* q, const void* k, const void* v, gdn
       float* starts = reinterpret_cast<float*>(w);
       w += align256((size_t)plan.n_prefix * st * sizeof(float));
       int32_t* ints = reinterpret_cast<int32_t*>(w);
-      hipError_t e = hipMemcpyAsync(ints, plan.ints.data(), plan.ints.size() * sizeof(int32_t),
-                                    hipMemcpyHostToDevice, stream);
+      hipError_t e = gdn::launch_plan_store(plan.ints.data(), (int64_t)plan.ints.size(), ints, stream);
       if (e != hipSuccess) return GDN_ERR_HIP;
       a.tbuf = rec;
       a.cu = ints;
@@ -426,16 +428,45 @@ gdn_status gdn_segment_state_scan(const void* k, const void* v, gdn_dtype in_dt,
   a.o_dt = GDN_F32;
   hipError_t e = gdn::launch_segment_pass1(a, M, b, stream);
   if (e != hipSuccess) return GDN_ERR_HIP;
-  e = gdn::launch_compose(M, b, initial_state, P, H_v, K, V, seg_initial_states, final_state, stream);
+  e = gdn::launch_compose(M, b, initial_state, P, H_v, K, V, seg_initial_states, 1, final_state, stream);
   return hip_status(e);
 }
 
-size_t gdn_segmented_workspace_bytes(int64_t T, int32_t P, int32_t H_v, int32_t K, int32_t V) {
-  if (T < 0 || P < 1 || H_v < 1 || K < 1 || V < 1) return 0;
-  const size_t per = (size_t)H_v * K;
-  return sizeof(float) * (size_t)P * per * ((size_t)K + 2 * (size_t)V) + tbuf_bytes(T, P, H_v);
+}  // extern "C"
+
+namespace {
+
+// Workspace of gdn_chunk_fwd_segmented: records of the P segments, M, b and
+// start states of the P - 1 segments that precede another, and the start /
+// final-state maps of pass 2.
+struct SegmentedLayout {
+  size_t rec, M, b, starts, ints, total;
+};
+
+SegmentedLayout segmented_layout(int64_t T, int32_t P, int32_t H_v, int32_t K, int32_t V) {
+  SegmentedLayout l;
+  const size_t pre = (size_t)(P - 1) * H_v * K;
+  l.rec = 0;
+  l.M = l.rec + align256(tbuf_bytes(T, P, H_v));
+  l.b = l.M + align256(pre * K * sizeof(float));
+  l.starts = l.b + align256(pre * V * sizeof(float));
+  l.ints = l.starts + align256(pre * V * sizeof(float));
+  l.total = l.ints + align256(2 * (size_t)P * sizeof(int32_t));
+  return l;
 }
 
+}  // namespace
+
+extern "C" {
+
+size_t gdn_segmented_workspace_bytes(int64_t T, int32_t P, int32_t H_v, int32_t K, int32_t V) {
+  if (T < 0 || P < 1 || H_v < 1 || K < 1 || V < 1) return 0;
+  return segmented_layout(T, P, H_v, K, V).total;
+}
+
+// Prep once for all P segments (the records with P serve both passes), pass 1
+// over segments 0 .. P-2 only, one fp32 chain of their maps, then pass 2 over
+// all P segments from the chained starts; pass 2 writes the final state.
 gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
                                    gdn_dtype in_dt, int64_t q_token_stride,
                                    int64_t k_token_stride, int64_t v_token_stride,
@@ -445,27 +476,84 @@ gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
                                    int32_t P, int64_t T, int32_t H_qk, int32_t H_v, int32_t K,
                                    int32_t V, void* o, gdn_dtype o_dt, float* final_state,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  // every check before anything is enqueued
   if (!valid_dtype(in_dt) || !valid_dtype(o_dt)) return GDN_ERR_BAD_DTYPE;
   if (in_dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
   if (P < 1 || T < 0 || H_qk < 1 || H_v < 1 || H_v % H_qk != 0) return GDN_ERR_BAD_SHAPE;
   if (K != 128 || V < 1 || V % 128 != 0) return GDN_ERR_UNSUPPORTED;
+  if (P > kMaxGrid || H_v > kMaxGrid) return GDN_ERR_UNSUPPORTED;
+  if (!stride_ok(&q_token_stride, (int64_t)H_qk * K) || !stride_ok(&k_token_stride, (int64_t)H_qk * K) ||
+      !stride_ok(&v_token_stride, (int64_t)H_v * V))
+    return GDN_ERR_BAD_SHAPE;
   if (seg_offsets_host && !offsets_ok(seg_offsets_host, P, 0, T, true)) return GDN_ERR_BAD_SEQLENS;
-  if (!q || !k || !v || !g || !beta || !o || !seg_offsets || !workspace) return GDN_ERR_NULL_POINTER;
-  const size_t need = gdn_segmented_workspace_bytes(T, P, H_v, K, V);
-  if (workspace_bytes < need) return GDN_ERR_BAD_SHAPE;
-  float* M = static_cast<float*>(workspace);
-  float* b = M + (size_t)P * H_v * K * K;
-  float* starts = b + (size_t)P * H_v * K * V;
-  float* tb = starts + (size_t)P * H_v * K * V;
-  const size_t tb_bytes = tbuf_bytes(T, P, H_v);
-  gdn_status s = gdn_segment_state_scan(k, v, in_dt, k_token_stride, v_token_stride, g, beta,
-                                        seg_offsets, nullptr, P,
-                                        initial_state, T, H_qk, H_v, K, V, M, b, starts,
-                                        final_state, tb, tb_bytes, stream);
-  if (s != GDN_OK) return s;
-  return gdn_chunk_fwd(q, k, v, in_dt, q_token_stride, k_token_stride, v_token_stride, g, beta,
-                       scale, starts, seg_offsets, nullptr, P, 1, T, H_qk,
-                       H_v, K, V, o, o_dt, nullptr, tb, tb_bytes, stream);
+  if (!seg_offsets || !workspace) return GDN_ERR_NULL_POINTER;
+  if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL_POINTER;
+  const SegmentedLayout l = segmented_layout(T, P, H_v, K, V);
+  if (workspace_bytes < l.total) return GDN_ERR_BAD_SHAPE;
+  if (T == 0 && !final_state) return GDN_OK;
+
+  unsigned char* w = static_cast<unsigned char*>(workspace);
+  float* M = reinterpret_cast<float*>(w + l.M);
+  float* bmap = reinterpret_cast<float*>(w + l.b);
+  float* starts = reinterpret_cast<float*>(w + l.starts);
+  int32_t* ints = reinterpret_cast<int32_t*>(w + l.ints);
+  // s0_ref: segment 0 starts from row 0 of initial_state (zero when NULL),
+  // segment i > 0 from chained start i - 1; sf_map: the last segment's state
+  // is the final state
+  std::vector<int32_t> maps(2 * (size_t)P, -1);
+  maps[0] = -2;
+  for (int32_t i = 1; i < P; ++i) maps[i] = i - 1;
+  maps[(size_t)P + P - 1] = 0;
+  hipError_t e = gdn::launch_plan_store(maps.data(), (int64_t)maps.size(), ints, stream);
+  if (e != hipSuccess) return GDN_ERR_HIP;
+
+  gdn::ChunkArgs a{};
+  a.tbuf = reinterpret_cast<float*>(w + l.rec);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.cu = seg_offsets;
+  a.n_seqs = P;
+  a.row_len = T;
+  a.Ttot = T;
+  a.Hqk = H_qk;
+  a.Hv = H_v;
+  a.K = K;
+  a.V = V;
+  a.q_stride = q_token_stride;
+  a.k_stride = k_token_stride;
+  a.v_stride = v_token_stride;
+  a.scale = scale;
+  a.in_dt = in_dt;
+  a.s0_mode = 0;
+  a.s0 = initial_state;
+  a.o = o;
+  a.o_dt = o_dt;
+  a.sf = final_state;
+  a.sf_seq_stride = (int64_t)H_v * K * V;
+  a.sf_head_stride = (int64_t)K * V;
+  a.sf_row_stride = V;
+  e = gdn::launch_chunk_prep(a, T > 0 ? 1 : 0, stream);
+  if (e != hipSuccess) return GDN_ERR_HIP;
+  if (P > 1) {
+    gdn::ChunkArgs p1 = a;
+    p1.n_seqs = P - 1;  // segments 0 .. P-2: the same chunk slots as in the P-segment records
+    e = gdn::launch_segment_pass1(p1, M, bmap, stream, false);
+    if (e != hipSuccess) return GDN_ERR_HIP;
+    e = gdn::launch_compose(M, bmap, initial_state, P - 1, H_v, K, V, starts, 0, nullptr, stream);
+    if (e != hipSuccess) return GDN_ERR_HIP;
+  }
+  gdn::ChunkArgs p2 = a;
+  p2.s0_ref = ints;
+  p2.s0_seg = starts;
+  p2.sf_map = ints + P;
+  if (T == 0) {
+    p2.q = nullptr;  // no tokens: the state-only scan copies initial_state to final_state
+    p2.o = nullptr;
+  }
+  return hip_status(gdn::launch_chunk_bf16(p2, stream, false));
 }
 
 

@@ -156,16 +156,34 @@ hipError_t launch_compose_chains(const float* M, const float* b, const float* s0
   return hipGetLastError();
 }
 
-// One chain over P segments of one sequence: starts of every segment, then
-// the final state.
+// One chain over P maps of one sequence from row 0 of s0.
 hipError_t launch_compose(const float* M, const float* b, const float* s0, int P, int Hv, int K,
-                          int V, float* starts, float* final_state, hipStream_t stream) {
+                          int V, float* out, int write_before, float* final_state, hipStream_t stream) {
   if (P == 0 || Hv == 0) return hipSuccess;
   if (K != CK || V % CT != 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((V / CT) * Hv));
   hipLaunchKernelGGL(compose_kernel, grid, dim3(CTHREADS), 0, stream, M, b, s0, nullptr, Chain{0, 0, P, 0}, Hv, V,
-                     starts, 1, final_state);
+                     out, write_before, final_state);
   return hipGetLastError();
+}
+
+// Index arrays travel to the device inside kernel arguments, which the launch
+// itself copies: no host-to-device copy (and no pageable host read) on the
+// stream.  One workgroup stores up to kPlanArgInts values.
+__global__ void __launch_bounds__(256) plan_store_kernel(PlanArg p, int32_t* __restrict__ dst) {
+  for (int i = threadIdx.x; i < p.n; i += 256) dst[i] = p.v[i];
+}
+
+hipError_t launch_plan_store(const int32_t* ints, int64_t n, int32_t* dst, hipStream_t stream) {
+  for (int64_t i0 = 0; i0 < n; i0 += kPlanArgInts) {
+    PlanArg p;
+    p.n = (int)(n - i0 < kPlanArgInts ? n - i0 : kPlanArgInts);
+    for (int i = 0; i < p.n; ++i) p.v[i] = ints[i0 + i];
+    hipLaunchKernelGGL(plan_store_kernel, dim3(1), dim3(256), 0, stream, p, dst + i0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace gdn

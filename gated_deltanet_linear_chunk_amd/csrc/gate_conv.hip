@@ -56,9 +56,11 @@ hipError_t launch_gate(const float* a, const float* b, const float* A_log, const
 // head_dim / 8 adjacent lanes with DPP exchanges (xor 1, xor 2, then the
 // half-row and row mirrors), which stay inside one head because heads are
 // 8-channel aligned.
-// Unnormalised bf16 outputs are the bf16 nearest to the exact result: each
-// value carries an error bound, and the few whose bound straddles a bf16
-// rounding midpoint are queued and recomputed in fp64 at the end of the run.
+// Outputs are the fp32 evaluation rounded once to the output type.  On
+// request (exact rounding), unnormalised bf16 outputs are instead the bf16
+// nearest to the exact result: each value carries an error bound, and the few
+// whose bound straddles a bf16 rounding midpoint are queued and recomputed in
+// fp64 at the end of the run.
 // ----------------------------------------------------------------------------
 constexpr int CONV_THREADS = 256;
 constexpr int CONV_CH_PER_THREAD = 8;
@@ -517,20 +519,20 @@ __device__ __forceinline__ void conv1d_run(const T* __restrict__ x, const T* __r
 }
 
 // Blocks below l2_end run the normalised channels, the others the plain ones
-// (with the rounding check for bf16); every block lies on one side.
-template <typename T>
+// (with the rounding check for bf16 when kExact); every block lies on one side.
+template <typename T, bool kExact>
 __global__ void __launch_bounds__(CONV_THREADS) conv1d_kernel(const T* __restrict__ x, const T* __restrict__ w,
                                                               const T* __restrict__ bias, T* __restrict__ y,
                                                               ConvParams p) {
   if (p.c_begin + (int)blockIdx.x * CONV_THREADS * CONV_CH_PER_THREAD < p.l2_end)
     conv1d_run<T, 2>(x, w, bias, y, p);
   else
-    conv1d_run<T, sizeof(T) == 2 ? 1 : 0>(x, w, bias, y, p);
+    conv1d_run<T, (kExact && sizeof(T) == 2) ? 1 : 0>(x, w, bias, y, p);
 }
 
 hipError_t launch_conv1d(const void* x, const void* w, const void* bias, int dt,
                          const int32_t* cu, int n_seqs, int B, int64_t T, int C, int width,
-                         int apply_silu, int l2_channels, int head_dim, float l2_eps, void* y,
+                         int apply_silu, int l2_channels, int head_dim, float l2_eps, int exact, void* y,
                          hipStream_t stream) {
   const int64_t Ttot = cu ? T : (int64_t)B * T;
   if (Ttot == 0 || C == 0) return hipSuccess;
@@ -571,11 +573,14 @@ hipError_t launch_conv1d(const void* x, const void* w, const void* bias, int dt,
     // their channel within the launch in 22
     if (dt == 1 && (p.tile_tokens > 256 || p.c_end - p.c_begin > (1 << 22))) return hipErrorInvalidValue;
     const dim3 grid((unsigned)cblocks, (unsigned)((Ttot + p.tile_tokens - 1) / p.tile_tokens));
-    if (dt == 1)
-      hipLaunchKernelGGL(conv1d_kernel<uint16_t>, grid, dim3(CONV_THREADS), 0, stream, (const uint16_t*)x,
+    if (dt == 1 && exact)
+      hipLaunchKernelGGL((conv1d_kernel<uint16_t, true>), grid, dim3(CONV_THREADS), 0, stream, (const uint16_t*)x,
+                         (const uint16_t*)w, (const uint16_t*)bias, (uint16_t*)y, p);
+    else if (dt == 1)
+      hipLaunchKernelGGL((conv1d_kernel<uint16_t, false>), grid, dim3(CONV_THREADS), 0, stream, (const uint16_t*)x,
                          (const uint16_t*)w, (const uint16_t*)bias, (uint16_t*)y, p);
     else
-      hipLaunchKernelGGL(conv1d_kernel<float>, grid, dim3(CONV_THREADS), 0, stream, (const float*)x,
+      hipLaunchKernelGGL((conv1d_kernel<float, false>), grid, dim3(CONV_THREADS), 0, stream, (const float*)x,
                          (const float*)w, (const float*)bias, (float*)y, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -11,7 +11,7 @@ hipError_t launch_gate(const float* a, const float* b, const float* A_log, const
 
 hipError_t launch_conv1d(const void* x, const void* w, const void* bias, int dt,
                          const int32_t* cu, int n_seqs, int B, int64_t T, int C, int width,
-                         int apply_silu, int l2_channels, int head_dim, float l2_eps, void* y,
+                         int apply_silu, int l2_channels, int head_dim, float l2_eps, int exact, void* y,
                          hipStream_t stream);
 
 // Where the sequences of a chunk-rule launch come from and what they produce.
@@ -83,9 +83,19 @@ hipError_t launch_segment_pass1(const ChunkArgs& a, float* M, float* b, hipStrea
 // maps p0 .. p0 + count - 1 of (M, b) in order; with write_before, out row
 // out0 + j receives the state before map j, else the state after it; final
 // (when not null) row c receives the state after the last map.
-// One chain of P maps (s0 row 0): starts of all P segments and the final state.
+// One chain of P maps from row 0 of s0, outputs as launch_compose_chains.
 hipError_t launch_compose(const float* M, const float* b, const float* s0, int P, int Hv, int K,
-                          int V, float* starts, float* final_state, hipStream_t stream);
+                          int V, float* out, int write_before, float* final_state, hipStream_t stream);
+
+// Stores n host values at dst (device) in stream order, carried inside kernel
+// arguments kPlanArgInts at a time: the host buffer may be reused as soon as
+// the call returns, and nothing waits for the stream.
+constexpr int kPlanArgInts = 480;
+struct PlanArg {
+  int n;
+  int32_t v[kPlanArgInts];
+};
+hipError_t launch_plan_store(const int32_t* ints, int64_t n, int32_t* dst, hipStream_t stream);
 hipError_t launch_compose_chains(const float* M, const float* b, const float* s0,
                                  const int32_t* chains, int n_chains, int Hv, int K, int V,
                                  float* out, int write_before, float* final_state,

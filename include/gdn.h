@@ -65,6 +65,9 @@ typedef enum gdn_status {
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
+/* How gdn_conv1d_fwd rounds its outputs (see there). */
+typedef enum gdn_rounding { GDN_ROUND_FAST = 0, GDN_ROUND_EXACT = 1 } gdn_rounding;
+
 /* Static text for a status code; never NULL. */
 const char* gdn_status_string(int status);
 
@@ -93,6 +96,13 @@ gdn_status gdn_gate_fwd(const float* a, const float* b, const float* A_log,
  * then, when l2norm_channels > 0, every group of head_dim consecutive
  * channels in [0, l2norm_channels) (the q and k heads) is divided by
  * sqrt(sum y^2 + l2_eps).  Accumulation is fp32; y is stored in `dt`.
+ * rounding: GDN_ROUND_FAST stores the fp32 evaluation rounded once to `dt`
+ * (round to nearest even; for bf16 within 2^-8 |y| + 1e-5 of the exact
+ * value).  GDN_ROUND_EXACT (bf16 only; no effect on fp32 outputs or on the
+ * L2-normalised channels) stores, for the other channels, the bf16 nearest to
+ * the exact conv (+ SiLU) value: the few fp32 results whose error bound
+ * straddles a rounding midpoint are recomputed in fp64 (slower).
+ * Other values: GDN_ERR_BAD_SHAPE.
  *  x, y      [B, T, channels] in dt (f32 or bf16)
  *  w         [channels, width] in dt;  bias [channels] in dt or NULL
  *  cu_seqlens device int32 [n_seqs + 1] or NULL (then B rows of T tokens)
@@ -103,7 +113,8 @@ gdn_status gdn_conv1d_fwd(const void* x, const void* w, const void* bias, gdn_dt
                           const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
                           int32_t n_seqs, int32_t B, int64_t T, int32_t channels,
                           int32_t width, int32_t apply_silu, int32_t l2norm_channels,
-                          int32_t head_dim, float l2_eps, void* y, hipStream_t stream);
+                          int32_t head_dim, float l2_eps, gdn_rounding rounding, void* y,
+                          hipStream_t stream);
 
 /*
  * Chunked gated delta rule forward (chunk size 64).  For every sequence n

@@ -154,7 +154,7 @@ def test_chunk_gated_norm_validation(lib):
 def test_conv_validation(lib):
     def conv(**kw):
         a = dict(x=FAKE, w=FAKE, bias=None, dt=1, cu=None, cu_host=None, n=0, B=1, T=32, C=8192, W=4, silu=1,
-                 l2=4096, hd=128, eps=1e-6, y=FAKE, stream=None)
+                 l2=4096, hd=128, eps=1e-6, rounding=0, y=FAKE, stream=None)
         a.update(kw)
         return lib.gdn_conv1d_fwd(*a.values())
 
@@ -168,6 +168,8 @@ def test_conv_validation(lib):
     assert conv(cu=FAKE, n=2, B=2) == SEQ
     assert conv(cu=FAKE, n=2, cu_host=(ctypes.c_int32 * 3)(0, 10, 31)) == SEQ
     assert conv(T=0, x=None, w=None, y=None) == OK
+    assert conv(rounding=2) == SHAPE  # GDN_ROUND_FAST (0) or GDN_ROUND_EXACT (1)
+    assert conv(rounding=1, x=None) == NULLP
 
 
 def test_gate_and_segment_validation(lib):
@@ -194,19 +196,39 @@ def test_gate_and_segment_validation(lib):
     assert scan(V=200) == UNSUP
     off = (ctypes.c_int32 * 3)(0, 5000, 4096)
     assert scan(P=2, off_host=off) == SEQ
-    assert lib.gdn_segmented_workspace_bytes(4096, 8, 32, 128, 128) == 4 * 8 * 32 * 128 * (128 + 256) + \
-        lib.gdn_segment_state_scan_workspace_bytes(4096, 8, 32, 128, 128)
+    # segmented forward: records of all P segments, then M, b and starts of the
+    # P - 1 segments that precede another, then 2 P ints of start/final maps
+    def a256(x):
+        return (x + 255) // 256 * 256
+    rec = lib.gdn_segment_state_scan_workspace_bytes(4096, 8, 32, 128, 128)
+    assert lib.gdn_segmented_workspace_bytes(4096, 8, 32, 128, 128) == \
+        a256(rec) + a256(4 * 7 * 32 * 128 * 128) + 2 * a256(4 * 7 * 32 * 128 * 128) + a256(4 * 16)
     assert lib.gdn_segmented_workspace_bytes(4096, 0, 32, 128, 128) == 0
-    seg = lib.gdn_chunk_fwd_segmented
+
+    def seg(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, dt=1, qs=0, ks=0, vs=0, g=FAKE, beta=FAKE, scale=1.0, s0=None, off=FAKE,
+                 off_host=(ctypes.c_int32 * 3)(0, 2048, 4096), P=2, T=4096, Hqk=16, Hv=32, K=128, V=128, o=FAKE,
+                 o_dt=0, fin=None, ws=FAKE, ws_bytes=lib.gdn_segmented_workspace_bytes(4096, 2, 32, 128, 128),
+                 stream=None)
+        a.update(kw)
+        return lib.gdn_chunk_fwd_segmented(*a.values())
+
     ws = lib.gdn_segmented_workspace_bytes(4096, 2, 32, 128, 128)
-    good = (ctypes.c_int32 * 3)(0, 2048, 4096)
-    assert seg(FAKE, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE, 1.0, None, FAKE, good, 2, 4096, 16, 32, 128, 128, FAKE, 0, None,
-               FAKE, ws - 1, None) == SHAPE
-    assert seg(FAKE, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE, 1.0, None, FAKE, good, 2, 4096, 16, 32, 128, 128, FAKE, 0, None,
-               None, ws, None) == NULLP
-    notfull = (ctypes.c_int32 * 3)(0, 2048, 4000)
-    assert seg(FAKE, FAKE, FAKE, 1, 0, 0, 0, FAKE, FAKE, 1.0, None, FAKE, notfull, 2, 4096, 16, 32, 128, 128, FAKE, 0, None,
-               FAKE, ws, None) == SEQ
+    assert seg(ws_bytes=ws - 1) == SHAPE
+    assert seg(ws=None) == NULLP
+    assert seg(off_host=(ctypes.c_int32 * 3)(0, 2048, 4000)) == SEQ
+    # every argument is checked before pass 1 writes anything, the q stride included
+    assert seg(qs=100) == SHAPE
+    assert seg(qs=1 << 24) == SHAPE
+    assert seg(o=None) == NULLP
+    assert seg(q=None) == NULLP
+    assert seg(o_dt=4) == DTYPE
+    assert seg(dt=0) == UNSUP
+    assert seg(K=64) == UNSUP
+    assert seg(Hqk=3) == SHAPE
+    assert seg(P=0) == SHAPE
+    # no tokens and no final state requested: nothing to do
+    assert seg(T=0, off_host=(ctypes.c_int32 * 3)(0, 0, 0), q=None, k=None, v=None, g=None, beta=None, o=None) == OK
 
 
 def test_decode_validation(lib):

@@ -70,24 +70,27 @@ def test_conv1d_packed(dtype, l2):
     d = gdn_inputs.draw(w)
     C = d["x"].shape[1]
     l2ch = 2 * 2 * 128 if l2 else 0
-    y = gdn.gdn_conv1d_fwd(dev(d["x"], dtype), dev(d["conv_w"], dtype), dev(d["conv_bias"], dtype),
-                           cu_seqlens=dev(d["cu_seqlens"], "i32"), cu_seqlens_host=d["cu_seqlens"],
-                           l2norm_channels=l2ch, head_dim=128)
     ref = oracle.conv1d(d["x"], d["conv_w"], d["conv_bias"], d["cu_seqlens"])
     if l2:
         q, k, _ = oracle.split_channels(ref, 2, 4, 128, 64)
         ref = ref.copy()
         ref[:, :l2ch] = np.concatenate([oracle.l2norm(q).reshape(300, -1), oracle.l2norm(k).reshape(300, -1)], 1)
-    got = host(y)
-    assert got.shape == (300, C)
-    if dtype == "f32":
-        np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-5)
-    else:
+    for exact in (False, True):
+        y = gdn.gdn_conv1d_fwd(dev(d["x"], dtype), dev(d["conv_w"], dtype), dev(d["conv_bias"], dtype),
+                               cu_seqlens=dev(d["cu_seqlens"], "i32"), cu_seqlens_host=d["cu_seqlens"],
+                               l2norm_channels=l2ch, head_dim=128, exact_rounding=exact)
+        got = host(y)
+        assert got.shape == (300, C)
+        if dtype == "f32":
+            np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-5)
+            continue
+        # the fp32 evaluation rounded once to bf16: within half a bf16 unit plus the fp32 error
         err = np.abs(got - ref)
         assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-5), float((err - 2.0 ** -8 * np.abs(ref)).max())
-        # channels stored without normalisation are the bf16 nearest to the exact value
-        plain = slice(l2ch, None)
-        np.testing.assert_array_equal(got[:, plain], oracle.round_bf16(ref[:, plain]))
+        if exact:
+            # channels stored without normalisation are the bf16 nearest to the exact value
+            plain = slice(l2ch, None)
+            np.testing.assert_array_equal(got[:, plain], oracle.round_bf16(ref[:, plain]))
 
 
 def test_conv1d_bf16_rounding_is_exact_at_scale():
@@ -96,7 +99,8 @@ def test_conv1d_bf16_rounding_is_exact_at_scale():
     w = gdn_inputs.Workload("conv_big", 13, 2048, 3, 1, 8, 64, 128, "bf16", conv_width=4, lengths=[700, 1000, 348])
     d = gdn_inputs.draw(w)
     y = gdn.gdn_conv1d_fwd(dev(d["x"], "bf16"), dev(d["conv_w"], "bf16"), dev(d["conv_bias"], "bf16"),
-                           cu_seqlens=dev(d["cu_seqlens"], "i32"), cu_seqlens_host=d["cu_seqlens"])
+                           cu_seqlens=dev(d["cu_seqlens"], "i32"), cu_seqlens_host=d["cu_seqlens"],
+                           exact_rounding=True)
     ref = oracle.conv1d(d["x"], d["conv_w"], d["conv_bias"], d["cu_seqlens"])
     np.testing.assert_array_equal(host(y), oracle.round_bf16(ref))
 
@@ -107,10 +111,13 @@ def test_conv1d_batched_rows_and_width():
     x = gdn_inputs.bf16_round(rng.standard_normal((B, T, C)).astype(np.float32))
     for W in (1, 2, 3, 4):
         wt = gdn_inputs.bf16_round(rng.standard_normal((C, W)).astype(np.float32))
-        y = gdn.gdn_conv1d_fwd(dev(x, "bf16"), dev(wt, "bf16"), None, apply_silu=False)
         cu = np.arange(B + 1) * T
         ref = oracle.conv1d(x.reshape(B * T, C), wt, None, cu, silu=False).reshape(B, T, C)
+        y = gdn.gdn_conv1d_fwd(dev(x, "bf16"), dev(wt, "bf16"), None, apply_silu=False, exact_rounding=True)
         np.testing.assert_array_equal(host(y), oracle.round_bf16(ref))
+        y = gdn.gdn_conv1d_fwd(dev(x, "bf16"), dev(wt, "bf16"), None, apply_silu=False)
+        err = np.abs(host(y) - ref)
+        assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-5), W
 
 
 # --------------------------------------------------------------------------- #

@@ -35,21 +35,27 @@ def _oracle_unit(q, k, v, g, beta, cu, n, h, Hqk, Hv, s0=None):
 
 
 def _pipeline(d, w):
-    """conv1d (+ q/k L2 norm) -> strided q, k, v views -> gates -> chunk rule."""
+    """conv1d (+ q/k L2 norm) -> strided q, k, v views -> gates -> chunk rule.
+
+    The conv rounds exactly here, so its bf16 v activations are the oracle's
+    bit for bit and the chunk tolerance applies to the rule alone (a one-unit
+    flip of a bf16 v of size 1 moves o at that token by several percent of
+    RMS(o)); the fast rounding the benchmark uses is checked on every conv
+    output of the packed workload below."""
     T = w.total_tokens
     Hqk, Hv, K, V = w.Hqk, w.Hv, w.K, w.V
     C = d["x"].shape[1]
     if w.batch_rows > 1:
         x = dev(d["x"], "bf16").reshape(w.batch_rows, T // w.batch_rows, C)
         y = gdn.gdn_conv1d_fwd(x, dev(d["conv_w"], "bf16"), dev(d["conv_bias"], "bf16"),
-                               l2norm_channels=2 * Hqk * K, head_dim=K)
+                               l2norm_channels=2 * Hqk * K, head_dim=K, exact_rounding=True)
         B, L = w.batch_rows, T // w.batch_rows
         cu = None
     else:
         cu = dev(d["cu_seqlens"], "i32")
         y = gdn.gdn_conv1d_fwd(dev(d["x"], "bf16"), dev(d["conv_w"], "bf16"), dev(d["conv_bias"], "bf16"),
                                cu_seqlens=cu, cu_seqlens_host=d["cu_seqlens"], l2norm_channels=2 * Hqk * K,
-                               head_dim=K)
+                               head_dim=K, exact_rounding=True)
         B, L = 1, T
     y = y.reshape(B, L, C)
     q = y[..., : Hqk * K].unflatten(-1, (Hqk, K))
@@ -192,24 +198,24 @@ def test_tiny_fp32_workload_full():
     assert_f32(host(fin), fref, "final")
 
 
-def test_conv1d_packed_workload_rounding_is_exact():
-    """The conv of the packed workload (8192 tokens x 8192 channels, q/k L2-normalised) in the launch
-    configuration the benchmark times: every v channel equals the oracle's fp64 conv + SiLU rounded
-    once to bf16, over all 33.5 M values; sampled q/k tokens match the normalised oracle."""
+def test_conv1d_packed_workload_all_outputs():
+    """The conv of the packed workload (8192 tokens x 8192 channels, q/k L2-normalised), every one of
+    its 67 M outputs against the oracle: in the launch configuration the benchmark times (fp32
+    evaluation rounded once) within half a bf16 unit plus the fp32 error, and with exact rounding
+    every v channel equals the oracle's fp64 conv + SiLU rounded once to bf16."""
     w = gdn_inputs.WORKLOADS["packed_varlen_bf16_T8192_N8_Hv32_K128"]
     d = gdn_inputs.draw(w, with_qkv=False)
     l2ch = 2 * w.Hqk * w.K
-    y = gdn.gdn_conv1d_fwd(dev(d["x"], "bf16"), dev(d["conv_w"], "bf16"), dev(d["conv_bias"], "bf16"),
-                           cu_seqlens=dev(d["cu_seqlens"], "i32"), cu_seqlens_host=d["cu_seqlens"],
-                           l2norm_channels=l2ch, head_dim=w.K)
-    torch.cuda.synchronize()
-    got = host(y)
     cu = d["cu_seqlens"]
-    ref_v = oracle.conv1d(d["x"][:, l2ch:], d["conv_w"][l2ch:], d["conv_bias"][l2ch:], cu)
-    mism = int(np.count_nonzero(got[:, l2ch:] != oracle.round_bf16(ref_v)))
-    assert mism == 0, "%d of %d v values differ from the correctly rounded result" % (mism, ref_v.size)
-    rows = np.random.default_rng(71).choice(w.total_tokens, 256, replace=False)
-    qk = oracle.conv1d(d["x"][:, :l2ch], d["conv_w"][:l2ch], d["conv_bias"][:l2ch], cu)[rows]
-    qk = oracle.l2norm(qk.reshape(len(rows), -1, w.K)).reshape(len(rows), -1)
-    err = np.abs(got[rows, :l2ch] - qk)
-    assert np.all(err <= 2.0 ** -8 * np.abs(qk) + 1e-5), float(err.max())
+    ref = oracle.conv1d(d["x"], d["conv_w"], d["conv_bias"], cu, threads=oracle.max_threads())
+    ref[:, :l2ch] = oracle.l2norm(ref[:, :l2ch].reshape(w.total_tokens, -1, w.K)).reshape(w.total_tokens, -1)
+    args = (dev(d["x"], "bf16"), dev(d["conv_w"], "bf16"), dev(d["conv_bias"], "bf16"))
+    kw = dict(cu_seqlens=dev(cu, "i32"), cu_seqlens_host=cu, l2norm_channels=l2ch, head_dim=w.K)
+    got = host(gdn.gdn_conv1d_fwd(*args, **kw))
+    excess = np.abs(got - ref) - (2.0 ** -8 * np.abs(ref) + 1e-5)
+    assert excess.max() <= 0, float(excess.max())
+    got = host(gdn.gdn_conv1d_fwd(*args, exact_rounding=True, **kw))
+    mism = int(np.count_nonzero(got[:, l2ch:] != oracle.round_bf16(ref[:, l2ch:])))
+    assert mism == 0, "%d of %d v values differ from the correctly rounded result" % (mism, ref[:, l2ch:].size)
+    excess = np.abs(got[:, :l2ch] - ref[:, :l2ch]) - (2.0 ** -8 * np.abs(ref[:, :l2ch]) + 1e-5)
+    assert excess.max() <= 0, float(excess.max())
