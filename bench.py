@@ -13,9 +13,10 @@ per second of the whole step (wall clock over the K steps, the device
 synchronised on both sides).
 
 Kernel lines time one library call at a time with HIP events recorded on the
-stream it runs on, R times, each after a 1 GiB read-modify-write of an
-unrelated buffer outside the events (so neither L2 nor the 256 MB MALL holds
-the inputs), and report mean, median, p10 and p90.  Each chunk-call line
+stream it runs on, R times, each after a 1 GiB read of an unrelated buffer
+outside the events (so neither L2 nor the 256 MB MALL holds the inputs, and no
+foreign dirty lines are left to write back), and report mean, median, p10 and
+p90.  Each chunk-call line
 carries a roofline block: its algorithmic bytes and flops per call over the
 mean duration, against 8 TB/s HBM and against the bf16 matrix-core peak, both
 the published 2.5 PFLOP/s and the rate a probe kernel measures in the same
@@ -112,14 +113,18 @@ def _torch():
 
 
 class Flush:
-    """A 1 GiB buffer rewritten between timed reps (outside the events)."""
+    """A 1 GiB buffer read between timed reps (outside the events): it evicts L2 and the MALL and,
+    being a read, leaves no dirty lines whose write-back the next timed call would pay for (the
+    previous call's own outputs are written back during the flush)."""
 
     def __init__(self):
         torch = _torch()
-        self.buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        self.out = torch.zeros(1, dtype=torch.float32, device="cuda:0")
 
     def __call__(self):
-        self.buf.add_(1.0)
+        torch = _torch()
+        torch.sum(self.buf, dim=0, keepdim=True, out=self.out)
 
 
 def time_call(call, reps, flush):

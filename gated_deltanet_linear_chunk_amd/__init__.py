@@ -214,9 +214,8 @@ def gdn_conv1d_fwd(x, w, bias=None, cu_seqlens=None, cu_seqlens_host=None, apply
     """Causal depthwise conv1d (+ SiLU, + per-head L2 norm of the first l2norm_channels).
 
     x [B, T, C] or [T, C] (packed, with cu_seqlens); w [C, W]; bias [C] or None.
-    exact_rounding: bf16 outputs of the unnormalised channels are the bf16
-    nearest to the exact value (GDN_ROUND_EXACT) instead of the rounded fp32
-    evaluation.
+    exact_rounding: every bf16 output is the bf16 nearest to the exact value
+    (GDN_ROUND_EXACT) instead of the rounded fp32 evaluation.
     """
     torch = _torch()
     dev = x.device

@@ -57,10 +57,11 @@ hipError_t launch_gate(const float* a, const float* b, const float* A_log, const
 // half-row and row mirrors), which stay inside one head because heads are
 // 8-channel aligned.
 // Outputs are the fp32 evaluation rounded once to the output type.  On
-// request (exact rounding), unnormalised bf16 outputs are instead the bf16
-// nearest to the exact result: each value carries an error bound, and the few
-// whose bound straddles a bf16 rounding midpoint are queued and recomputed in
-// fp64 at the end of the run.
+// request (exact rounding), bf16 outputs are instead the bf16 nearest to the
+// exact result: each value carries an error bound (for a normalised value,
+// also from its head's sum of squares and the reciprocal square root), and the
+// few whose bound straddles a bf16 rounding midpoint are queued and recomputed
+// in fp64 at the end of the run (a normalised one with its whole head).
 // ----------------------------------------------------------------------------
 constexpr int CONV_THREADS = 256;
 constexpr int CONV_CH_PER_THREAD = 8;
@@ -202,6 +203,30 @@ __device__ __noinline__ void settle_value(const uint16_t* __restrict__ x, const 
   y[t * C + c] = f32_to_bf16_bits(bf16_nearest_f64(v));
 }
 
+// One L2-normalised output in fp64: the conv (+ SiLU) of every channel of
+// c's head, their sum of squares S, and y_c / sqrt(S + eps) stored as its
+// nearest bf16.  hist as for settle_value.
+__device__ __noinline__ void settle_l2_value(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                                             const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int64_t C,
+                                             int width, int apply_silu, int head_dim, double eps, int64_t t,
+                                             int64_t c, int hist) {
+  const int64_t h0 = c - c % head_dim;
+  double S = 0.0, yc = 0.0;
+  for (int jc = 0; jc < head_dim; ++jc) {
+    const int64_t cj = h0 + jc;
+    double z = bias ? (double)bf16_bits_to_f32(bias[cj]) : 0.0;
+    for (int j = 0; j < width; ++j) {
+      const int back = width - 1 - j;
+      if (back <= hist)
+        z += (double)bf16_bits_to_f32(w[cj * width + j]) * (double)bf16_bits_to_f32(x[(t - back) * C + cj]);
+    }
+    const double v = apply_silu ? z / (1.0 + exp(-z)) : z;
+    S += v * v;
+    if (cj == c) yc = v;
+  }
+  y[t * C + c] = f32_to_bf16_bits(bf16_nearest_f64(yc / sqrt(S + eps)));
+}
+
 struct ConvParams {
   const int32_t* cu;
   int n_seqs;
@@ -216,11 +241,12 @@ struct ConvParams {
 };
 
 // One sub-tile of SUB tokens for this thread's 8 channels.  kMode: 0 plain,
-// 1 plain with the rounding check (bf16 output), 2 L2-normalised.  kMasked:
+// 1 plain with the rounding check (bf16 output), 2 L2-normalised, 3
+// L2-normalised with the rounding check (bf16 output).  kMasked:
 // the sub-tile reaches past the run or starts a sample within its first
 // three tokens, so history rows are masked per token (hist_code: 2 bits per
 // token, the count of its history rows inside its sample).
-template <typename T, int kMode, bool kMasked>
+template <typename T, int kMode, bool kMasked, bool kSilu>
 __device__ __forceinline__ void conv_sub(const typename ConvRow<T>::raw_t (&buf)[ConvRow<T>::SUB],
                                          float (&h1)[CONV_CH_PER_THREAD], float (&h2)[CONV_CH_PER_THREAD],
                                          float (&h3)[CONV_CH_PER_THREAD],
@@ -235,14 +261,15 @@ __device__ __forceinline__ void conv_sub(const typename ConvRow<T>::raw_t (&buf)
   using Row = ConvRow<T>;
   constexpr int SUB = Row::SUB;
   constexpr int NCH = CONV_CH_PER_THREAD;
-  constexpr bool kCheck = kMode == 1 && sizeof(T) == 2;
+  constexpr bool kCheck = (kMode == 1 || kMode == 3) && sizeof(T) == 2;
+  constexpr bool kL2 = kMode >= 2;
 #pragma unroll
   for (int tt = 0; tt < SUB; ++tt) {
     if (kMasked && tt >= n_valid) break;
     const int hist = kMasked ? (int)((hist_code >> (2 * tt)) & 3u) : 3;
     float cur[NCH], out[NCH];
     Row::unpack(buf[tt], cur);
-    float ss = 0.f;
+    float ss = 0.f, es = 0.f, eb[NCH];
     uint32_t dbits = 0;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
@@ -254,9 +281,9 @@ __device__ __forceinline__ void conv_sub(const typename ConvRow<T>::raw_t (&buf)
       z = fmaf(wt[1][i], x2, z);
       z = fmaf(wt[2][i], x3, z);
       z = fmaf(wt[3][i], cur[i], z);
-      const float v = p.apply_silu ? z * __builtin_amdgcn_rcpf(1.f + __expf(-z)) : z;
+      const float v = kSilu ? z * __builtin_amdgcn_rcpf(1.f + __expf(-z)) : z;
       out[i] = v;
-      if (kMode == 2) ss = fmaf(v, v, ss);
+      if (kL2) ss = fmaf(v, v, ss);
       if (kCheck) {
         // Ab = 9 * 2^-24 * (|bias| + sum_j |w_j| |x_j|) from taps scaled by
         // 9 * 2^-24 beforehand (exact for bf16 taps)
@@ -265,17 +292,37 @@ __device__ __forceinline__ void conv_sub(const typename ConvRow<T>::raw_t (&buf)
         Ab = fmaf(wa[1][i], fabsf(x2), Ab);
         Ab = fmaf(wa[2][i], fabsf(x3), Ab);
         Ab = fmaf(wa[3][i], fabsf(cur[i]), Ab);
-        dbits |= (rounding_in_doubt(v, Ab) ? 1u : 0u) << i;
+        if (kMode == 1) {
+          dbits |= (rounding_in_doubt(v, Ab) ? 1u : 0u) << i;
+        } else {
+          // bound of |v - exact| as for unnormalised outputs; 2 |v| E bounds
+          // this value's share of the error of the head's sum of squares
+          eb[i] = fmaf(0x1p-20f, fabsf(v), Ab);
+          es = fmaf(2.f * fabsf(v), eb[i], es);
+        }
       }
       h1[i] = h2[i];
       h2[i] = h3[i];
       h3[i] = cur[i];
     }
-    if (kMode == 2) {  // every lane of the wave joins the exchanges
+    if (kL2) {  // every lane of the wave joins the exchanges
       ss = group_sum(ss, p.l2_lanes_log2);
       const float inv = __builtin_amdgcn_rsqf(ss + p.l2_eps);
 #pragma unroll
       for (int i = 0; i < NCH; ++i) out[i] *= inv;
+      if (kMode == 3) {
+        // n = y / sqrt(S + eps): its relative error is that of y, half that
+        // of S + eps (es from the values, 16 roundings of the positive sum),
+        // the reciprocal square root (1 ulp) and the product, taken twice
+        es = group_sum(es, p.l2_lanes_log2);
+        const float rel = fmaf(0.5f, (es + 16.f * 0x1p-24f * ss) * __builtin_amdgcn_rcpf(ss + p.l2_eps), 0x1p-22f);
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const float bound = 2.f * fmaf(eb[i], inv, fabsf(out[i]) * rel);
+          const float mid = __uint_as_float((__float_as_uint(out[i]) & 0xFFFF0000u) | 0x8000u);
+          dbits |= (fabsf(out[i] - mid) <= bound ? 1u : 0u) << i;
+        }
+      }
     }
     if (active) Row::store(yrow + (int64_t)tt * p.C, out);
     if constexpr (kCheck) {
@@ -301,7 +348,7 @@ __device__ __forceinline__ void conv_sub(const typename ConvRow<T>::raw_t (&buf)
   }
 }
 
-template <typename T, int kMode>
+template <typename T, int kMode, bool kSilu>
 __device__ __forceinline__ void conv1d_run(const T* __restrict__ x, const T* __restrict__ w,
                                            const T* __restrict__ bias, T* __restrict__ y, const ConvParams& p) {
   using Row = ConvRow<T>;
@@ -442,10 +489,10 @@ __device__ __forceinline__ void conv1d_run(const T* __restrict__ x, const T* __r
     const int nv_ = (int)((TS) + SUB < tw1 ? SUB : tw1 - (TS));                                        \
     T* yrow_ = y + (TS) * C + c0;                                                                      \
     if (masked_)                                                                                       \
-      conv_sub<T, kMode, true>(BUF, h1, h2, h3, wt, bs, wa, ba, nv_, code_, p, active, yrow_, queue,   \
+      conv_sub<T, kMode, true, kSilu>(BUF, h1, h2, h3, wt, bs, wa, ba, nv_, code_, p, active, yrow_, queue,   \
                                qcount, (TS), tw0, c0, overflow);                                       \
     else                                                                                               \
-      conv_sub<T, kMode, false>(BUF, h1, h2, h3, wt, bs, wa, ba, nv_, code_, p, active, yrow_, queue,  \
+      conv_sub<T, kMode, false, kSilu>(BUF, h1, h2, h3, wt, bs, wa, ba, nv_, code_, p, active, yrow_, queue,  \
                                 qcount, (TS), tw0, c0, overflow);                                      \
   } while (0)
   for (int64_t ts = tw0; ts < tw1; ts += 2 * SUB) {
@@ -458,6 +505,34 @@ __device__ __forceinline__ void conv1d_run(const T* __restrict__ x, const T* __r
 #undef GDN_CONV_SUB
 
   // ---- settle the queued roundings in fp64 -----------------------------------------
+  if constexpr (kMode == 3 && sizeof(T) == 2) {
+    // normalised outputs: each queued value is recomputed with its whole head
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    const uint32_t nq = min(*qcount, (uint32_t)CONV_QCAP);
+    const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+    const uint16_t* wb = reinterpret_cast<const uint16_t*>(w);
+    const uint16_t* bb = reinterpret_cast<const uint16_t*>(bias);
+    uint16_t* yb = reinterpret_cast<uint16_t*>(y);
+    const int head_dim = CONV_CH_PER_THREAD << p.l2_lanes_log2;
+    for (uint32_t e = lane; e < nq; e += 64) {
+      const uint32_t v = queue[e];
+      const int64_t t = tw0 + (int64_t)(v & 0xFFu);
+      const int64_t c = p.c_begin + (int64_t)(v >> 10);
+      if (t < tw1 && c < p.c_end)
+        settle_l2_value(xb, wb, bb, yb, C, p.width, kSilu ? 1 : 0, head_dim, (double)p.l2_eps, t, c,
+                        (int)((v >> 8) & 3u));
+    }
+    if (overflow && active) {  // more doubtful values than the queue holds: redo the run in fp64
+      for (int64_t t = tw0; t < tw1; ++t) {
+        const int64_t back = t - region_start(p.cu, p.n_seqs, p.row_len, p.Ttot, t);
+        for (int i = 0; i < NCH; ++i)
+          settle_l2_value(xb, wb, bb, yb, C, p.width, kSilu ? 1 : 0, head_dim, (double)p.l2_eps, t, c0 + i,
+                          back < 3 ? (int)back : 3);
+      }
+    }
+  }
   if constexpr (kMode == 1 && sizeof(T) == 2) {
     // the queue and this wave's stores above are complete before any lane
     // reads the queue or overwrites a value another lane stored
@@ -524,10 +599,20 @@ template <typename T, bool kExact>
 __global__ void __launch_bounds__(CONV_THREADS) conv1d_kernel(const T* __restrict__ x, const T* __restrict__ w,
                                                               const T* __restrict__ bias, T* __restrict__ y,
                                                               ConvParams p) {
-  if (p.c_begin + (int)blockIdx.x * CONV_THREADS * CONV_CH_PER_THREAD < p.l2_end)
-    conv1d_run<T, 2>(x, w, bias, y, p);
-  else
-    conv1d_run<T, (kExact && sizeof(T) == 2) ? 1 : 0>(x, w, bias, y, p);
+  constexpr int kPlain = (kExact && sizeof(T) == 2) ? 1 : 0;
+  constexpr int kNorm = (kExact && sizeof(T) == 2) ? 3 : 2;
+  const bool l2 = p.c_begin + (int)blockIdx.x * CONV_THREADS * CONV_CH_PER_THREAD < p.l2_end;
+  if (p.apply_silu) {
+    if (l2)
+      conv1d_run<T, kNorm, true>(x, w, bias, y, p);
+    else
+      conv1d_run<T, kPlain, true>(x, w, bias, y, p);
+  } else {
+    if (l2)
+      conv1d_run<T, kNorm, false>(x, w, bias, y, p);
+    else
+      conv1d_run<T, kPlain, false>(x, w, bias, y, p);
+  }
 }
 
 hipError_t launch_conv1d(const void* x, const void* w, const void* bias, int dt,

@@ -98,10 +98,10 @@ gdn_status gdn_gate_fwd(const float* a, const float* b, const float* A_log,
  * sqrt(sum y^2 + l2_eps).  Accumulation is fp32; y is stored in `dt`.
  * rounding: GDN_ROUND_FAST stores the fp32 evaluation rounded once to `dt`
  * (round to nearest even; for bf16 within 2^-8 |y| + 1e-5 of the exact
- * value).  GDN_ROUND_EXACT (bf16 only; no effect on fp32 outputs or on the
- * L2-normalised channels) stores, for the other channels, the bf16 nearest to
- * the exact conv (+ SiLU) value: the few fp32 results whose error bound
- * straddles a rounding midpoint are recomputed in fp64 (slower).
+ * value).  GDN_ROUND_EXACT (bf16 only; no effect on fp32 outputs) stores the
+ * bf16 nearest to the exact value of every output, normalised or not: the
+ * few fp32 results whose error bound straddles a rounding midpoint are
+ * recomputed in fp64 (a normalised one with its whole head), which is slower.
  * Other values: GDN_ERR_BAD_SHAPE.
  *  x, y      [B, T, channels] in dt (f32 or bf16)
  *  w         [channels, width] in dt;  bias [channels] in dt or NULL

@@ -75,3 +75,35 @@ def assert_bf16(got, ref, what="", bf16_store=False):
     else:
         assert s["max_abs"] <= bound, (what, s)
     return s
+
+
+def assert_units_bf16(o, ref, cu, what="", bf16_store=False, fin=None, fref=None):
+    """Every (sequence, head) unit of a packed or batched run against the oracle, each to the bf16
+    bound of its own RMS: o, ref [T, H, V]; cu [N + 1] offsets; fin, fref [N, H, K, V] optional."""
+    o = np.asarray(o)
+    ref = np.asarray(ref)
+    assert o.shape == ref.shape, (o.shape, ref.shape)
+    assert np.all(np.isfinite(o)), what
+    worst = 0.0
+    for n in range(len(cu) - 1):
+        a, b = int(cu[n]), int(cu[n + 1])
+        if b > a:
+            err = np.abs(o[a:b] - ref[a:b])  # [L, H, V]
+            rms = np.sqrt(np.mean(ref[a:b] * ref[a:b], axis=(0, 2)))  # per head
+            bound = TOL_BF16_REL_RMS * rms[None, :, None]
+            if bf16_store:
+                bound = bound + 2.0 ** -8 * np.abs(ref[a:b])
+            excess = (err - bound).max(axis=(0, 2))
+            h = int(np.argmax(excess))
+            assert excess[h] <= 0, "%s: o unit (%d, %d) exceeds its bound by %.3e (max err %.3e, rms %.3e)" % (
+                what, n, h, excess[h], err[:, h].max(), rms[h])
+            worst = max(worst, float((err.max(axis=(0, 2)) / np.maximum(rms, 1e-300)).max()))
+        if fin is not None:
+            f, fr = np.asarray(fin[n]), np.asarray(fref[n])
+            assert np.all(np.isfinite(f)), what
+            err = np.abs(f - fr).max(axis=(1, 2))
+            rms = np.sqrt(np.mean(fr * fr, axis=(1, 2)))
+            h = int(np.argmax(err - TOL_BF16_REL_RMS * rms))
+            assert err[h] <= TOL_BF16_REL_RMS * rms[h], "%s: final state (%d, %d): max err %.3e, rms %.3e" % (
+                what, n, h, err[h], rms[h])
+    return worst

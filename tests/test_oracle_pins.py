@@ -502,6 +502,27 @@ def test_pipeline_activations_split_and_norm():
     np.testing.assert_array_equal(v.reshape(40, 8), oracle.round_bf16(y[:, 16:]))
 
 
+def test_split_channels_order_q_k_v():
+    """The conv channels run q | k | v, each head-major (head h of q at h*K .. h*K + K-1): channels hold
+    a code of (part, head, dim), so a q/k swap, a wrong offset or a transposed reshape shows."""
+    T, Hqk, Hv, K, V = 3, 2, 4, 8, 16
+    parts = [(0, Hqk, K), (1, Hqk, K), (2, Hv, V)]
+    cols = []
+    for part, H, D in parts:
+        for h in range(H):
+            for j in range(D):
+                cols.append(10000 * part + 100 * h + j)
+    y = np.tile(np.array(cols, dtype=np.float64), (T, 1)) + 1e6 * np.arange(T)[:, None]
+    assert y.shape[1] == 2 * Hqk * K + Hv * V
+    q, k, v = oracle.split_channels(y, Hqk, Hv, K, V)
+    assert q.shape == (T, Hqk, K) and k.shape == (T, Hqk, K) and v.shape == (T, Hv, V)
+    for part, out in ((0, q), (1, k), (2, v)):
+        H, D = out.shape[1:]
+        want = 1e6 * np.arange(T)[:, None, None] + 10000 * part + 100 * np.arange(H)[None, :, None] + \
+            np.arange(D)[None, None, :]
+        np.testing.assert_array_equal(out, want)
+
+
 # --------------------------------------------------------------------------- #
 def test_generator_is_deterministic_and_shaped():
     w = gdn_inputs.WORKLOADS["tiny_fp32_T256_H2_K32"]
