@@ -64,29 +64,41 @@ __device__ __forceinline__ void tile_rc(int b, int& i, int& j) {
   j = b - (i * (i + 1)) / 2;
 }
 
-__global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p, int heads_per_wave) {
-  __shared__ float sA[10][16][BP];
-  __shared__ float sT[10][16][BP];  // P staging, then T
-  __shared__ float sY[3][16][BP];
+// Three waves per SIMD (at most 168 registers; the LDS tiles take 9.5 KB):
+// the kernel is a chain of dependent steps, hidden by running many waves.
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3)))
+chunk_prep_kernel(ChunkArgs a, int with_p) {
+  __shared__ float sAd[4][16][BP];  // diagonal blocks of A, read by the forward substitution
+  __shared__ float sTd[4][16][BP];  // diagonal blocks of T, written column by column
   __shared__ double sG[CH];
   __shared__ float sBeta[CH];
 
   const int lane = threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int slot = blockIdx.x;
-  const int h0 = blockIdx.y * heads_per_wave;  // v-heads h0 .. h0 + heads_per_wave - 1 share q/k head hq
-  const int hq = h0 / (a.Hv / a.Hqk);
+  const int h = blockIdx.y;
+  const int hq = h / (a.Hv / a.Hqk);
 
   // sequence n owning this slot: the largest n with floor(cu[n]/64) + n <= slot
-  int lo = 0, hi = a.n_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if ((seq_begin(a, mid) >> 6) + mid <= slot)
-      lo = mid;
-    else
-      hi = mid - 1;
+  // (the keys grow with n).  Up to 64 sequences: every lane tests one key,
+  // one load round trip; more: binary search.
+  int n;
+  if (a.n_seqs <= 64) {
+    const int li = lane < a.n_seqs ? lane : 0;
+    const bool below = lane < a.n_seqs && (seq_begin(a, li) >> 6) + li <= slot;
+    const uint64_t m = __ballot(below);
+    n = m ? 63 - __builtin_clzll(m) : 0;
+  } else {
+    int lo = 0, hi = a.n_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((seq_begin(a, mid) >> 6) + mid <= slot)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    n = lo;
   }
-  const int n = lo;
   const int64_t bos = seq_begin(a, n);
   const int64_t eos = a.cu ? (int64_t)clampi(a.cu[n + 1], bos, a.Ttot) : bos + a.row_len;
   const int64_t j0 = (int64_t)slot - ((bos >> 6) + n);
@@ -95,11 +107,12 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p,
   if (t0 >= eos) return;  // unused slot
   const int L = (int)((eos - t0) < CH ? (eos - t0) : CH);
 
-  // ---- K and Q fragments straight from global memory, in flight first ----------
+  // ---- K and Q fragments straight from global memory, and the gates -----------
   // row tile i, k-step m: contiguous k = 32 m + 8 g4 .. +7; rows past L read
   // the last row and are zeroed (every load unconditional)
   const int64_t head_off = (int64_t)hq * KD + 8 * g4;
   bf16x8 kf[4][4], qf[4][4];
+  float graw, braw;
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -124,163 +137,136 @@ __global__ void __launch_bounds__(64) chunk_prep_kernel(ChunkArgs a, int with_p,
         }
       }
     }
+    const bool ok = lane < L;
+    const int64_t row = t0 + (ok ? lane : 0);
+    graw = ok ? a.g[row * a.Hv + h] : 0.f;
+    braw = ok ? a.beta[row * a.Hv + h] : 0.f;
   }
 
-  for (int hh = 0; hh < heads_per_wave; ++hh) {
-  const int h = h0 + hh;
   unsigned char* rec = (unsigned char*)a.tbuf + ((int64_t)slot * a.Hv + h) * PREP_RECORD_BYTES;
   uint16_t* rtb = (uint16_t*)(rec + PREP_REC_TB);  // [2][10][256]
   uint16_t* rp = (uint16_t*)(rec + PREP_REC_P);    // [2][10][256]
-  float* rgam = (float*)(rec + PREP_REC_GAM);
-  float* rdec = (float*)(rec + PREP_REC_DEC);
-  if (hh > 0) __syncthreads();  // the previous head is done with the LDS tiles
 
   // ---- gates: G (fp64 prefix sum), gamma, dec ---------------------------------
   {
-    const bool ok = lane < L;
-    double G = ok ? (double)a.g[(t0 + lane) * a.Hv + h] : 0.0;
-    const float b = ok ? a.beta[(t0 + lane) * a.Hv + h] : 0.f;
+    double G = (double)graw;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const double o = __shfl_up(G, off, 64);
       if (lane >= off) G += o;
     }
     const double Glast = __shfl(G, 63, 64);
-    const float gam = expf((float)G);
     sG[lane] = G;
-    sBeta[lane] = b;
-    rgam[lane] = gam;
-    rdec[lane] = expf((float)(Glast - G));
+    sBeta[lane] = braw;
+    reinterpret_cast<float*>(rec + PREP_REC_GAM)[lane] = expf((float)G);
+    reinterpret_cast<float*>(rec + PREP_REC_DEC)[lane] = expf((float)(Glast - G));
   }
-
   __syncthreads();  // gates visible to all lanes
 
-  // ---- P = lower(Q K^T * decay) -> record (hi, lo) ----------------------------
-  if (with_p) {
+  // ---- A and P tiles, transposed: lane (g4, c16) holds (row c16 of tile i,
+  // columns 4 g4 .. 4 g4 + 3 of tile j) of
+  //   A = strictly-lower(diag(beta) K K^T * decay)  (kept for T), and
+  //   P = lower(Q K^T * decay)                      (4 consecutive values of a
+  //                                                  row: one 8-byte store each)
+  // one decay per element serves both.
+  f32x4 AT[10];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j <= i; ++j) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acc = mfma16(qf[i][m], kf[j][m], acc);
-        const int s = 16 * j + c16;
-        const double Gs = sG[s];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int rr = 4 * g4 + e, r = 16 * i + rr;
-          sT[blk(i, j)][rr][c16] = (r >= s) ? acc[e] * decay(sG[r] - Gs) : 0.f;
-        }
-      }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < 10; ++u) {
-      const int f = lane + 64 * u;  // 4-element group: tile f/64, element 4 (f % 64)
-      const int b = f >> 6, e4 = (f & 63) * 4, rr = e4 >> 4, cc = e4 & 15;
-      const float* src = &sT[b][rr][cc];
-      uint32_t h0, l0, h1, l1;
-      split2(src[0], src[1], h0, l0);
-      split2(src[2], src[3], h1, l1);
-      *reinterpret_cast<u32x2*>(rp + (0 * 10 + b) * 256 + e4) = u32x2{h0, h1};
-      *reinterpret_cast<u32x2*>(rp + (1 * 10 + b) * 256 + e4) = u32x2{l0, l1};
-    }
-    __syncthreads();  // sT is reused for T
-  }
-
-  // ---- A = strictly-lower(diag(beta) K K^T * decay) ---------------------------
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int R = 16 * i + c16;
+    const double GR = sG[R];
+    const float bR = sBeta[R];
 #pragma unroll
     for (int j = 0; j <= i; ++j) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 0; m < 4; ++m) acc = mfma16(kf[i][m], kf[j][m], acc);
-      const int s = 16 * j + c16;
-      const double Gs = sG[s];
+      for (int m = 0; m < 4; ++m) accA = mfma16(kf[j][m], kf[i][m], accA);
+      if (with_p) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) accP = mfma16(kf[j][m], qf[i][m], accP);
+      }
+      f32x4 av, pv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int rr = 4 * g4 + e, r = 16 * i + rr;
-        sA[blk(i, j)][rr][c16] = (r > s) ? sBeta[r] * acc[e] * decay(sG[r] - Gs) : 0.f;
+        const int S = 16 * j + 4 * g4 + e;
+        const float d = (R >= S) ? decay(GR - sG[S]) : 0.f;
+        av[e] = (R > S) ? bR * accA[e] * d : 0.f;
+        pv[e] = accP[e] * d;
+      }
+      const int b = blk(i, j);
+      AT[b] = av;
+      if (i == j) *reinterpret_cast<f32x4*>(&sAd[i][c16][4 * g4]) = av;
+      if (with_p) {
+        uint32_t h0, l0, h1, l1;
+        split2(pv[0], pv[1], h0, l0);
+        split2(pv[2], pv[3], h1, l1);
+        *reinterpret_cast<u32x2*>(rp + (0 * 10 + b) * 256 + c16 * 16 + 4 * g4) = u32x2{h0, h1};
+        *reinterpret_cast<u32x2*>(rp + (1 * 10 + b) * 256 + c16 * 16 + 4 * g4) = u32x2{l0, l1};
       }
     }
-  __syncthreads();
+  }
+  __syncthreads();  // diagonal blocks of A visible
 
   // ---- T: diagonal blocks, lane = (block b, column c) -------------------------
   {
     const int b = g4, c = c16;
-    const float(*Ab)[BP] = sA[blk(b, b)];
+    const float(*Ab)[BP] = sAd[b];
+    // column c of the block's inverse: x[r] = e_c[r] - sum_{s<r} A[r][s] x[s],
+    // the sums taken in order of s; once x[s] is final it updates every later
+    // row, so the rows' chains run side by side
     float x[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float val = (r == c) ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
 #pragma unroll
-      for (int s = 0; s < r; ++s) val = fmaf(-Ab[r][s], x[s], val);
-      x[r] = val;
-    }
+    for (int s = 0; s < 15; ++s)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sT[blk(b, b)][r][c] = x[r];
+      for (int r = s + 1; r < 16; ++r) x[r] = fmaf(-Ab[r][s], x[s], x[r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sTd[b][r][c] = x[r];
   }
   __syncthreads();
 
-  // ---- T: off-diagonal blocks, T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj -------------
-  // Blocks one diagonal at a time (the blocks of a diagonal are independent);
-  // each 16 x 16 x 16 product is four fp32 MFMAs with operands read from LDS.
-  {
-    const int ar = c16, ak = g4;  // A operand: row, k within a 4-step
+  // ---- T: off-diagonal blocks in registers, T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
+  // fp32 16 x 16 x 4 MFMAs with the k index of step st at 4 g4 + st: the A
+  // operand is then a transposed tile (A_ik as held above, T_ii read so), the
+  // B operand a tile in the MFMA output layout (T_kj, the partial sums Y).
+  f32x4 T[10], TTd[4];
 #pragma unroll
-    for (int dist = 1; dist < 4; ++dist) {
-      // Y_ij = sum_k A_ik T_kj for every block of this diagonal, kept in sY
-      f32x4_t y[3];
+  for (int b = 0; b < 4; ++b) {
 #pragma unroll
-      for (int bb = 0; bb < 4 - dist; ++bb) {
-        const int i = bb + dist, j = bb;
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        for (int kb = j; kb < i; ++kb) {
-          const float(*Aik)[BP] = sA[blk(i, kb)];
-          const float(*Tkj)[BP] = sT[blk(kb, j)];
+    for (int e = 0; e < 4; ++e) T[blk(b, b)][e] = sTd[b][4 * g4 + e][c16];
+    TTd[b] = *reinterpret_cast<const f32x4*>(&sTd[b][c16][4 * g4]);
+  }
 #pragma unroll
-          for (int st = 0; st < 4; ++st) acc = mfma_f32_4(Aik[ar][4 * st + ak], Tkj[4 * st + ak][c16], acc);
-        }
-        y[bb] = acc;
-      }
+  for (int dist = 1; dist < 4; ++dist) {
 #pragma unroll
-      for (int bb = 0; bb < 4 - dist; ++bb)
+    for (int j = 0; j + dist < 4; ++j) {
+      const int i = j + dist;
+      f32x4_t y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sY[bb][4 * g4 + e][c16] = y[bb][e];
-      __syncthreads();
+      for (int k = j; k < i; ++k)
 #pragma unroll
-      for (int bb = 0; bb < 4 - dist; ++bb) {
-        const int i = bb + dist, j = bb;
-        const float(*Tii)[BP] = sT[blk(i, i)];
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int st = 0; st < 4; ++st) y = mfma_f32_4(AT[blk(i, k)][st], T[blk(k, j)][st], y);
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int st = 0; st < 4; ++st) acc = mfma_f32_4(Tii[ar][4 * st + ak], sY[bb][4 * st + ak][c16], acc);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sT[blk(i, j)][4 * g4 + e][c16] = -acc[e];
-      }
-      __syncthreads();
+      for (int st = 0; st < 4; ++st) acc = mfma_f32_4(TTd[i][st], y[st], acc);
+      T[blk(i, j)] = f32x4{-acc[0], -acc[1], -acc[2], -acc[3]};
     }
   }
 
-  // ---- T diag(beta) as bf16 pairs -> record -----------------------------------
+  // ---- T diag(beta) as bf16 pairs -> record (row 4 g4 + e, column c16 of each tile)
 #pragma unroll
-  for (int u = 0; u < 10; ++u) {
-    const int f = lane + 64 * u;
-    const int b = f >> 6, e4 = (f & 63) * 4, rr = e4 >> 4, cc = e4 & 15;
+  for (int b = 0; b < 10; ++b) {
     int bi, bj;
     tile_rc(b, bi, bj);
-    const int s = 16 * bj + cc;
-    const float* src = &sT[b][rr][cc];
-    float tb[4];
+    const float bs = sBeta[16 * bj + c16];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) tb[x] = src[x] * sBeta[s + x];
-    uint32_t uh0, ul0, uh1, ul1;
-    split2(tb[0], tb[1], uh0, ul0);
-    split2(tb[2], tb[3], uh1, ul1);
-    *reinterpret_cast<u32x2*>(rtb + (0 * 10 + b) * 256 + e4) = u32x2{uh0, uh1};
-    *reinterpret_cast<u32x2*>(rtb + (1 * 10 + b) * 256 + e4) = u32x2{ul0, ul1};
+    for (int e = 0; e < 4; ++e) {
+      uint16_t hi, lo;
+      split_bf16(T[b][e] * bs, hi, lo);
+      rtb[(0 * 10 + b) * 256 + (4 * g4 + e) * 16 + c16] = hi;
+      rtb[(1 * 10 + b) * 256 + (4 * g4 + e) * 16 + c16] = lo;
+    }
   }
-  }  // v-heads of this q/k head
 }
 
 }  // namespace
@@ -290,10 +276,8 @@ int64_t chunk_slots(int64_t Ttot, int n_seqs) { return (Ttot + 63) / 64 + n_seqs
 hipError_t launch_chunk_prep(const ChunkArgs& a, int with_p, hipStream_t stream) {
   const int64_t slots = chunk_slots(a.Ttot, a.n_seqs);
   if (slots == 0 || a.Hv == 0) return hipSuccess;
-  // Two v-heads that read the same q/k head share one wave (one load of the
-  // q/k fragments and half the waves); otherwise one v-head per wave.
-  const int per = (a.Hv / a.Hqk) % 2 == 0 ? 2 : 1;
-  hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)slots, a.Hv / per), dim3(64), 0, stream, a, with_p, per);
+  // one wave per (chunk slot, v-head)
+  hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)slots, a.Hv), dim3(64), 0, stream, a, with_p);
   return hipGetLastError();
 }
 
