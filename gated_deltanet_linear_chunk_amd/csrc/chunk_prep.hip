@@ -75,8 +75,22 @@ chunk_prep_kernel(ChunkArgs a, int with_p) {
 
   const int lane = threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
-  const int slot = blockIdx.x;
-  const int h = blockIdx.y;
+  // 1-D grid.  Workgroup ids go to the eight XCDs in turn, so ids x and x + 8
+  // share an XCD (and its L2): with an even GQA ratio they are the two v-heads
+  // of one q/k head in one chunk slot, and the second reads K and Q from L2.
+  int slot, h;
+  {
+    const int x = blockIdx.x;
+    if ((a.Hv / a.Hqk) % 2 == 0) {
+      const int pair = (x >> 4) * 8 + (x & 7), member = (x >> 3) & 1;
+      const int pairs_per_slot = a.Hv / 2;
+      slot = pair / pairs_per_slot;
+      h = 2 * (pair % pairs_per_slot) + member;
+    } else {
+      slot = x / a.Hv;
+      h = x % a.Hv;
+    }
+  }
   const int hq = h / (a.Hv / a.Hqk);
 
   // sequence n owning this slot: the largest n with floor(cu[n]/64) + n <= slot
@@ -277,7 +291,11 @@ hipError_t launch_chunk_prep(const ChunkArgs& a, int with_p, hipStream_t stream)
   const int64_t slots = chunk_slots(a.Ttot, a.n_seqs);
   if (slots == 0 || a.Hv == 0) return hipSuccess;
   // one wave per (chunk slot, v-head)
-  hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)slots, a.Hv), dim3(64), 0, stream, a, with_p);
+  // pairs of v-heads fill groups of 16 ids: pad the grid to whole groups
+  int64_t n = slots * a.Hv;
+  if ((a.Hv / a.Hqk) % 2 == 0) n = (n + 15) / 16 * 16;
+  if (n > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)n), dim3(64), 0, stream, a, with_p);
   return hipGetLastError();
 }
 
