@@ -64,11 +64,12 @@ int device_cus() {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace of a split run: records of n_seg segments, M and b of the pass-1
-// segments, start states of the later segments, the plan's index arrays.
-size_t split_workspace_bytes(int64_t total, int n_seg, int n_prefix, int32_t H_v, int32_t K, int32_t V) {
+// Workspace of a split run: records of the N samples (laid out as for the
+// unsplit run), M and b of the pass-1 segments, start states of the later
+// segments, the plan's index arrays.
+size_t split_workspace_bytes(int64_t total, int N, int n_seg, int n_prefix, int32_t H_v, int32_t K, int32_t V) {
   const size_t st = (size_t)H_v * K * V * sizeof(float);
-  return align256(tbuf_bytes(total, n_seg, H_v)) + align256((size_t)n_prefix * H_v * K * K * sizeof(float)) +
+  return align256(tbuf_bytes(total, N, H_v)) + align256((size_t)n_prefix * H_v * K * K * sizeof(float)) +
          2 * align256((size_t)n_prefix * st) +
          align256(sizeof(int32_t) * (size_t)gdn::split_plan_ints_max(n_seg, n_prefix));
 }
@@ -136,7 +137,7 @@ size_t gdn_chunk_fwd_workspace_bytes(gdn_dtype in_dt, int64_t total_tokens, int3
   const size_t plain = tbuf_bytes(total_tokens, n_seqs, H_v);
   const int pmax = gdn::max_prefix_segments(H_v, V, device_cus());
   if (pmax == 0 || n_seqs < 1) return plain;
-  return std::max(plain, split_workspace_bytes(total_tokens, n_seqs + pmax, pmax, H_v, K, V));
+  return std::max(plain, split_workspace_bytes(total_tokens, n_seqs, n_seqs + pmax, pmax, H_v, K, V));
 }
 
 // The gated output norm that the bf16 scan applies as it writes o (null: none).
@@ -222,15 +223,19 @@ static gdn_status chunk_fwd_run(const void* q, const void* k, const void* v, gdn
     a.nw = norm->weight;
     a.eps = norm->eps;
   }
-  if (!fixed_ws && in_dt == GDN_BF16 && cu_seqlens && cu_seqlens_host && total > 0) {
+  if (in_dt != GDN_BF16) return hip_status(gdn::launch_chunk_f32(a, stream));
+  // The per-chunk records of the samples go first: the host plans a split
+  // while they run, and a split run reads the same records.
+  hipError_t e = gdn::launch_chunk_prep(a, (o && q) ? 1 : 0, stream);
+  if (e != hipSuccess) return GDN_ERR_HIP;
+  if (!fixed_ws && cu_seqlens && cu_seqlens_host && total > 0) {
     gdn::SplitPlan plan;
     if (gdn::plan_split(cu_seqlens_host, N, H_v, V, initial_state != nullptr, device_cus(), plan) &&
-        workspace_bytes >= split_workspace_bytes(total, plan.n_seg, plan.n_prefix, H_v, K, V)) {
+        workspace_bytes >= split_workspace_bytes(total, N, plan.n_seg, plan.n_prefix, H_v, K, V)) {
       // ---- segment-split run (see plan_split) ----------------------------------
       unsigned char* w = static_cast<unsigned char*>(workspace);
       const size_t st = (size_t)H_v * K * V;
-      float* rec = reinterpret_cast<float*>(w);
-      w += align256(tbuf_bytes(total, plan.n_seg, H_v));
+      w += align256(tbuf_bytes(total, N, H_v));
       float* M = reinterpret_cast<float*>(w);
       w += align256((size_t)plan.n_prefix * H_v * K * K * sizeof(float));
       float* bmap = reinterpret_cast<float*>(w);
@@ -238,13 +243,11 @@ static gdn_status chunk_fwd_run(const void* q, const void* k, const void* v, gdn
       float* starts = reinterpret_cast<float*>(w);
       w += align256((size_t)plan.n_prefix * st * sizeof(float));
       int32_t* ints = reinterpret_cast<int32_t*>(w);
-      hipError_t e = gdn::launch_plan_store(plan.ints.data(), (int64_t)plan.ints.size(), ints, stream);
+      e = gdn::launch_plan_store(plan.ints.data(), (int64_t)plan.ints.size(), ints, stream);
       if (e != hipSuccess) return GDN_ERR_HIP;
-      a.tbuf = rec;
       a.cu = ints;
       a.n_seqs = plan.n_seg;
-      e = gdn::launch_chunk_prep(a, 1, stream);  // one set of records serves both passes
-      if (e != hipSuccess) return GDN_ERR_HIP;
+      a.rec_seq = ints + plan.off_sample();
       gdn::ChunkArgs p1 = a;
       p1.seq_order = ints + plan.off_pre();
       p1.n_blocks_z = plan.n_prefix;
@@ -262,9 +265,7 @@ static gdn_status chunk_fwd_run(const void* q, const void* k, const void* v, gdn
       return hip_status(gdn::launch_chunk_bf16(p2, stream, false));
     }
   }
-  const hipError_t e = in_dt == GDN_BF16 ? gdn::launch_chunk_bf16(a, stream)
-                                         : gdn::launch_chunk_f32(a, stream);
-  return hip_status(e);
+  return hip_status(gdn::launch_chunk_bf16(a, stream, false));
 }
 
 gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, gdn_dtype in_dt,

@@ -32,6 +32,8 @@
 //   sQ [64][128], sK [64][128], sKt [128][64] (K^T), sP [2][64][64] (hi, lo),
 //   sT2 [2][64][64] (T diag(beta) hi/lo); sVt [128][72] (V^T of this slice,
 //   rows padded by 16 B), sO fp32 [64][132], gamma[64], dec[64] fp32.
+#include <atomic>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -236,6 +238,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   const uint32_t ks32 = (uint32_t)a.k_stride, qs32 = (uint32_t)q_stride, vs32 = (uint32_t)v_stride;
   const unsigned char* rbase = (const unsigned char*)a.tbuf + (int64_t)h * PREP_RECORD_BYTES;
   const int64_t rslot_stride = (int64_t)a.Hv * PREP_RECORD_BYTES;
+  const int rec_seq = a.rec_seq ? a.rec_seq[seq] : seq;
 
   // ---- initial state: S[ct][dt][e] = S[16 dt + 4 g4 + e][col_base + 16 ct + c16]
   f32x4 S[NCT][8];
@@ -277,7 +280,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   (*reinterpret_cast<const u32x4*>((B) + (uint32_t)(2u * (__umul24((ROW), (S32)) + (uint32_t)(COL)))))
 #define GDN_PF_REC(T0)                                                                         \
   do {                                                                                        \
-    const unsigned char* rs_ = rbase + (((T0) >> 6) + seq) * rslot_stride;                    \
+    const unsigned char* rs_ = rbase + (((T0) >> 6) + rec_seq) * rslot_stride;                \
     _Pragma("unroll") for (int u_ = 0; u_ < NREC; ++u_)                                        \
       pr[u_] = *reinterpret_cast<const u32x4*>(rs_ + 16 * min(tid + u_ * NT, RUNITS - 1));      \
   } while (0)
@@ -684,9 +687,18 @@ constexpr int kScanWaves = 8;  // the prefetch code assumes 512 threads
 
 template <int kMode, bool kNorm = false>
 hipError_t launch_scan(const ChunkArgs& a, Pass1 p1, dim3 grid, hipStream_t stream) {
-  const void* fn = (const void*)chunk_scan_kernel<kMode, kScanWaves, kNorm>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  // the LDS limit is raised once per device (a host call on every launch otherwise)
+  static std::atomic<uint64_t> attr_set{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (!bit || !(attr_set.load(std::memory_order_acquire) & bit)) {
+    const void* fn = (const void*)chunk_scan_kernel<kMode, kScanWaves, kNorm>;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set.fetch_or(bit, std::memory_order_acq_rel);
+  }
   // 1-D launch over (tile, v-head, sequence); the kernel decodes it
   ChunkArgs c = a;
   c.n_tiles = (int)grid.x;

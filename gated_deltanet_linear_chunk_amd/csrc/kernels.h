@@ -49,6 +49,9 @@ struct ChunkArgs {
   const int32_t* s0_ref;     // [n_seqs]: >= 0 row of s0_seg, -1 zero, <= -2 row -2-r of s0
   const float* s0_seg;       // start states [*, Hv, K, V] picked by s0_ref
   const int32_t* sf_map;     // [n_seqs]: row of sf for the final state, -1 none
+  // [n_seqs]: row of the records a sequence reads (the sample a segment cuts;
+  // records are laid out by the offsets prep ran on), or null (its own index)
+  const int32_t* rec_seq;
   int n_tiles;               // bf16 scan: column tiles per (sequence, v-head), set by its launcher
   // bf16 scan with V == 128: when z is set, o receives the gated RMS norm of
   // every output row, o * rsqrt(mean(o^2) + eps) * nw * silu(z), instead of o.

@@ -15,26 +15,63 @@
 
 #include <algorithm>
 #include <functional>
-#include <queue>
+#include <map>
+#include <mutex>
 
 namespace gdn {
 
 namespace {
 
-// Finish time of blocks of the given durations dispatched in order, each to
-// the first free compute unit (one block per unit at a time).
-double makespan(const std::vector<double>& blocks, int cus) {
-  std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
-  for (int i = 0; i < cus; ++i) free_at.push(0.0);
+// A run of `count` blocks of one duration, dispatched back to back.
+struct Group {
+  double d;
+  int64_t count;
+};
+
+// Finish time of the groups' blocks dispatched in order, each block to the
+// first free compute unit (one block per unit at a time).  The units are kept
+// as (free-at time, number of units) classes, so a group costs one step per
+// class it touches rather than one per block.
+double makespan(const std::vector<Group>& groups, int cus) {
+  std::map<double, int64_t> free_at{{0.0, (int64_t)cus}};
   double end = 0.0;
-  for (double d : blocks) {
-    const double t = free_at.top() + d;
-    free_at.pop();
-    free_at.push(t);
-    end = std::max(end, t);
+  for (const Group& g : groups) {
+    int64_t left = g.count;
+    while (left > 0) {
+      auto it = free_at.begin();
+      const double t = it->first;
+      const int64_t take = std::min(left, it->second);
+      if (take == it->second)
+        free_at.erase(it);
+      else
+        it->second -= take;
+      free_at[t + g.d] += take;
+      end = std::max(end, t + g.d);
+      left -= take;
+    }
   }
   return end;
 }
+
+// The last plans, keyed by everything they depend on: repeated calls with the
+// same offsets (a serving loop, a benchmark) skip the search.
+struct PlanKey {
+  std::vector<int32_t> cu;
+  int32_t H_v, V;
+  bool has_s0;
+  int cus;
+  bool operator==(const PlanKey& o) const {
+    return H_v == o.H_v && V == o.V && has_s0 == o.has_s0 && cus == o.cus && cu == o.cu;
+  }
+};
+struct CachedPlan {
+  PlanKey key;
+  bool split;
+  SplitPlan plan;
+};
+constexpr size_t kCacheSize = 8;
+std::mutex g_cache_mutex;
+std::vector<CachedPlan> g_cache;  // most recent last
 
 }  // namespace
 
@@ -46,11 +83,39 @@ int max_prefix_segments(int32_t H_v, int32_t V, int cus) {
 }
 
 int64_t split_plan_ints_max(int n_seg, int n_prefix) {
-  return 4 * (int64_t)n_seg + 1 + 5 * (int64_t)n_prefix;
+  return 5 * (int64_t)n_seg + 1 + 5 * (int64_t)n_prefix;
 }
+
+static bool plan_split_uncached(const int32_t* cu, int32_t N, int32_t H_v, int32_t V, bool has_s0, int cus,
+                                SplitPlan& out);
 
 bool plan_split(const int32_t* cu, int32_t N, int32_t H_v, int32_t V, bool has_s0, int cus,
                 SplitPlan& out) {
+  PlanKey key{std::vector<int32_t>(cu, cu + N + 1), H_v, V, has_s0, cus};
+  {
+    std::lock_guard<std::mutex> lock(g_cache_mutex);
+    for (size_t i = 0; i < g_cache.size(); ++i)
+      if (g_cache[i].key == key) {
+        CachedPlan hit = g_cache[i];
+        g_cache.erase(g_cache.begin() + (int64_t)i);
+        g_cache.push_back(hit);
+        out = hit.plan;
+        return hit.split;
+      }
+  }
+  SplitPlan plan;
+  const bool split = plan_split_uncached(cu, N, H_v, V, has_s0, cus, plan);
+  {
+    std::lock_guard<std::mutex> lock(g_cache_mutex);
+    if (g_cache.size() >= kCacheSize) g_cache.erase(g_cache.begin());
+    g_cache.push_back(CachedPlan{std::move(key), split, plan});
+  }
+  out = std::move(plan);
+  return split;
+}
+
+static bool plan_split_uncached(const int32_t* cu, int32_t N, int32_t H_v, int32_t V, bool has_s0, int cus,
+                                SplitPlan& out) {
   const int tiles2 = V / 128, tiles1 = 1 + V / 128;
   const int pmax = max_prefix_segments(H_v, V, cus);
   if (pmax == 0) return false;
@@ -63,10 +128,9 @@ bool plan_split(const int32_t* cu, int32_t N, int32_t H_v, int32_t V, bool has_s
   // pass 2 (or the unsplit scan): longest first
   auto pass2 = [&](std::vector<int64_t> lens) {
     std::sort(lens.begin(), lens.end(), std::greater<int64_t>());
-    std::vector<double> blocks;
-    for (int64_t c : lens)
-      for (int i = 0; i < H_v * tiles2; ++i) blocks.push_back((double)c);
-    return makespan(blocks, cus);
+    std::vector<Group> groups;
+    for (int64_t c : lens) groups.push_back(Group{(double)c, (int64_t)H_v * tiles2});
+    return makespan(groups, cus);
   };
   const double base = pass2(chunks);
   // Every chunk runs in pass 2, and no schedule beats the work spread evenly
@@ -91,7 +155,7 @@ bool plan_split(const int32_t* cu, int32_t N, int32_t H_v, int32_t V, bool has_s
     if (n_prefix == 0 || n_prefix > pmax) continue;
     // a pass-1 chunk skips q, the output and P: about 0.7 of a pass-2 chunk;
     // a chain step costs about one chunk
-    std::vector<double> p1((size_t)n_prefix * H_v * tiles1, 0.7 * (double)seg);
+    const std::vector<Group> p1{Group{0.7 * (double)seg, n_prefix * H_v * tiles1}};
     const double t = makespan(p1, cus) + (double)longest_chain + pass2(lens);
     if (t < best) {
       best = t;
@@ -120,7 +184,7 @@ bool plan_split(const int32_t* cu, int32_t N, int32_t H_v, int32_t V, bool has_s
     if (g.j + 1 < g.s) ++out.n_prefix;
     if (g.j == 0 && g.s > 1) ++out.n_chain;
   }
-  out.ints.assign((size_t)out.off_chains() + 4 * out.n_chain, 0);
+  out.ints.assign((size_t)out.off_sample() + out.n_seg, 0);
   int32_t* I = out.ints.data();
   for (int i = 0; i < out.n_seg; ++i) I[i] = segs[i].begin;
   I[out.n_seg] = segs.back().end;
@@ -142,6 +206,7 @@ bool plan_split(const int32_t* cu, int32_t N, int32_t H_v, int32_t V, bool has_s
     }
     I[out.off_s0ref() + i] = g.j == 0 ? (has_s0 ? -2 - g.n : -1) : later++;
     I[out.off_sfmap() + i] = g.j + 1 == g.s ? g.n : -1;
+    I[out.off_sample() + i] = g.n;
     if (g.j + 1 < g.s) I[out.off_pre() + pre++] = i;
   }
   return true;

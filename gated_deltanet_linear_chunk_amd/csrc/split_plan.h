@@ -10,7 +10,8 @@ namespace gdn {
 
 // A packed run cut into segments (see split_plan.cpp).  Index arrays, laid
 // out as the device copy: seg_cu [n_seg + 1] | order [n_seg] | s0_ref [n_seg] |
-// sf_map [n_seg] | pre_order [n_prefix] | chains [4 n_chain].
+// sf_map [n_seg] | pre_order [n_prefix] | chains [4 n_chain] | sample [n_seg]
+// (the sample each segment cuts, whose chunk records it reads).
 struct SplitPlan {
   int n_seg = 0, n_prefix = 0, n_chain = 0;
   std::vector<int32_t> ints;
@@ -19,6 +20,7 @@ struct SplitPlan {
   int off_sfmap() const { return off_s0ref() + n_seg; }
   int off_pre() const { return off_sfmap() + n_seg; }
   int off_chains() const { return off_pre() + n_prefix; }
+  int off_sample() const { return off_chains() + 4 * n_chain; }
 };
 
 // Most pass-1 segments a plan uses for H_v heads of V columns on cus units.

@@ -37,13 +37,15 @@ def planner(tmp_path_factory):
 
 def check_plan(p, lengths, has_s0):
     n_seg, n_prefix, n_chain, I = p["n_seg"], p["n_prefix"], p["n_chain"], p["ints"]
-    assert len(I) == (n_seg + 1) + 3 * n_seg + n_prefix + 4 * n_chain
+    assert len(I) == (n_seg + 1) + 3 * n_seg + n_prefix + 4 * n_chain + n_seg
     cu = np.concatenate([[0], np.cumsum(lengths)])
     seg_cu = I[: n_seg + 1]
     o = n_seg + 1
     order, s0_ref, sf_map = I[o: o + n_seg], I[o + n_seg: o + 2 * n_seg], I[o + 2 * n_seg: o + 3 * n_seg]
     pre = I[o + 3 * n_seg: o + 3 * n_seg + n_prefix]
-    chains = I[o + 3 * n_seg + n_prefix:].reshape(n_chain, 4)
+    o2 = o + 3 * n_seg + n_prefix
+    chains = I[o2: o2 + 4 * n_chain].reshape(n_chain, 4)
+    seg_sample = I[o2 + 4 * n_chain:]
     assert seg_cu[0] == 0 and seg_cu[-1] == cu[-1] and np.all(np.diff(seg_cu) >= 0)
     # segments tile the samples: every sample boundary is a segment boundary
     assert set(cu.tolist()) <= set(seg_cu.tolist())
@@ -55,11 +57,16 @@ def check_plan(p, lengths, has_s0):
         if b > a:
             n = int(sample[i])
             assert cu[n] <= a and b <= cu[n + 1]
+            assert seg_sample[i] == n  # the segment reads the chunk records of its sample
             assert (a - cu[n]) % 64 == 0  # chunk-aligned from the sample start
             owners.setdefault(n, []).append(i)
     assert sorted(order.tolist()) == list(range(n_seg))
     seg_len = np.diff(seg_cu)
     assert np.all(np.diff(seg_len[order]) <= 0)  # longest first
+    # an empty segment is the one segment of a zero-length sample (its final-state row)
+    for i in range(n_seg):
+        if seg_cu[i + 1] == seg_cu[i]:
+            assert sf_map[i] == seg_sample[i]
     # final states: one per sample, from its last segment
     assert sorted(x for x in sf_map.tolist() if x >= 0) == list(range(len(lengths)))
     later = []
