@@ -44,10 +44,15 @@ bool stride_ok(int64_t* stride, int64_t dense) {
   return *stride >= dense && *stride % 8 == 0 && *stride < (int64_t(1) << 24);
 }
 
+// The bf16 MFMA kernels (with their per-chunk records) take K = 128 and V a
+// multiple of 128; every other supported shape (K in {32, 64, 128}, V a
+// multiple of 32, either input dtype) runs the fp32 vector-ALU kernel.
+bool mfma_path(int in_dt, int32_t K, int32_t V) { return in_dt == GDN_BF16 && K == 128 && V > 0 && V % 128 == 0; }
+
 // Which chunk kernel serves (in_dt, K, V); GDN_OK when one does.
 gdn_status chunk_supported(int in_dt, int32_t K, int32_t V) {
-  if (in_dt == GDN_BF16) return (K == 128 && V > 0 && V % 128 == 0) ? GDN_OK : GDN_ERR_UNSUPPORTED;
-  if (K == 32 || K == 64) return (V > 0 && V % 32 == 0) ? GDN_OK : GDN_ERR_UNSUPPORTED;
+  if (mfma_path(in_dt, K, V)) return GDN_OK;
+  if (K == 32 || K == 64 || K == 128) return (V > 0 && V % 32 == 0) ? GDN_OK : GDN_ERR_UNSUPPORTED;
   return GDN_ERR_UNSUPPORTED;
 }
 
@@ -133,7 +138,7 @@ gdn_status gdn_conv1d_fwd(const void* x, const void* w, const void* bias, gdn_dt
 
 size_t gdn_chunk_fwd_workspace_bytes(gdn_dtype in_dt, int64_t total_tokens, int32_t n_seqs,
                                      int32_t H_v, int32_t K, int32_t V) {
-  if (in_dt != GDN_BF16 || total_tokens < 0 || n_seqs < 0 || H_v < 1 || K < 1 || V < 1) return 0;
+  if (!mfma_path(in_dt, K, V) || total_tokens < 0 || n_seqs < 0 || H_v < 1) return 0;
   const size_t plain = tbuf_bytes(total_tokens, n_seqs, H_v);
   const int pmax = gdn::max_prefix_segments(H_v, V, device_cus());
   if (pmax == 0 || n_seqs < 1) return plain;
@@ -180,7 +185,8 @@ static gdn_status chunk_fwd_run(const void* q, const void* k, const void* v, gdn
   const int64_t total = cu_seqlens ? T : (int64_t)B * T;
   if (total == 0 && !final_state) return GDN_OK;
   if (total > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL_POINTER;
-  if (in_dt == GDN_BF16) {
+  const bool mfma = mfma_path(in_dt, K, V);
+  if (mfma) {
     if (fixed_ws) {
       const gdn_status st = fixed_ws(stream, total, N, H_v, &workspace, &workspace_bytes);
       if (st != GDN_OK) return st;
@@ -223,7 +229,7 @@ static gdn_status chunk_fwd_run(const void* q, const void* k, const void* v, gdn
     a.nw = norm->weight;
     a.eps = norm->eps;
   }
-  if (in_dt != GDN_BF16) return hip_status(gdn::launch_chunk_f32(a, stream));
+  if (!mfma) return hip_status(gdn::launch_chunk_f32(a, stream));
   // The per-chunk records of the samples go first: the host plans a split
   // while they run, and a split run reads the same records.
   hipError_t e = gdn::launch_chunk_prep(a, (o && q) ? 1 : 0, stream);
@@ -357,7 +363,7 @@ gdn_status gdn_chunk_fwd_gated_norm(const void* q, const void* k, const void* v,
                                     hipStream_t stream) {
   if (!valid_dtype(in_dt) || !valid_dtype(o_dt) || !valid_dtype(z_dt)) return GDN_ERR_BAD_DTYPE;
   if (!(eps >= 0.f)) return GDN_ERR_BAD_SHAPE;
-  if (in_dt == GDN_BF16 && V == 128) {
+  if (mfma_path(in_dt, K, V) && V == 128) {
     const FusedNorm norm{z, z_dt == GDN_BF16 ? 1 : 0, norm_weight, eps};
     return chunk_fwd_run(q, k, v, in_dt, q_token_stride, k_token_stride, v_token_stride, g, beta, scale,
                          initial_state, cu_seqlens, cu_seqlens_host, n_seqs, B, T, H_qk, H_v, K, V, o,

@@ -1,8 +1,10 @@
 // chunk_f32.hip -- chunked gated delta rule, fp32 vector-ALU kernel.
 //
-// The fp32 path (fp32 inputs, small head dims): every product runs on the fp32
-// vector units, so results stay within ~1e-6 relative of exact arithmetic.
-// One workgroup owns (sequence, v-head, 32-column slice of V) and walks the
+// The fp32 path (fp32 inputs, and bf16 inputs of the head sizes the MFMA
+// kernel does not take): every product runs on the fp32 vector units, so
+// results stay within ~1e-6 relative of exact arithmetic on the given inputs.
+// One workgroup owns (sequence, v-head, 32-column slice of V; 16 columns for
+// K = 128) and walks the
 // sequence's 64-token chunks in order.  Per chunk, with local tokens r, s and
 // G the in-chunk cumulative gate (kept in fp64 so that G_r - G_s does not
 // cancel), it forms
@@ -21,7 +23,10 @@ namespace gdn {
 namespace {
 
 constexpr int CH = 64;      // chunk length
-constexpr int F32_BV = 32;  // V columns per workgroup
+constexpr int F32_BV = 32;  // V columns per workgroup (16 for K = 128, which needs the LDS for Q, K, W)
+
+template <int K>
+constexpr int f32_bv() { return K >= 128 ? 16 : F32_BV; }
 constexpr int F32_THREADS = 256;
 
 template <typename TI>
@@ -35,7 +40,7 @@ __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, int64_t i) {
 
 template <int K, typename TI>
 __global__ void __launch_bounds__(F32_THREADS) chunk_f32_kernel(ChunkArgs a) {
-  constexpr int BV = F32_BV;
+  constexpr int BV = f32_bv<K>();
   __shared__ float sQ[CH][K + 1];
   __shared__ float sK[CH][K + 1];
   __shared__ float sW[CH][K + 1];
@@ -211,7 +216,7 @@ __global__ void __launch_bounds__(F32_THREADS) chunk_f32_kernel(ChunkArgs a) {
 
 template <int K>
 hipError_t launch_k(const ChunkArgs& a, hipStream_t stream) {
-  dim3 grid(a.V / F32_BV, a.Hv, a.n_seqs);
+  dim3 grid(a.V / f32_bv<K>(), a.Hv, a.n_seqs);
   if (a.in_dt == 1)
     hipLaunchKernelGGL((chunk_f32_kernel<K, uint16_t>), grid, dim3(F32_THREADS), 0, stream, a);
   else
@@ -226,6 +231,7 @@ hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t stream) {
   switch (a.K) {
     case 32: return launch_k<32>(a, stream);
     case 64: return launch_k<64>(a, stream);
+    case 128: return launch_k<128>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

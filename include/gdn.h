@@ -134,13 +134,14 @@ gdn_status gdn_conv1d_fwd(const void* x, const void* w, const void* bias, gdn_dt
  *  strides must be multiples of 8, at least the dense size and below 2^24
  *  elements (GDN_ERR_BAD_SHAPE otherwise).  The B
  *  batch rows are then B*T tokens at that stride.
- * Kernels: in_dt = BF16 runs bf16 MFMA tiles with fp32 accumulation, an fp32
- * state, and split-bf16 operands where fp32 intermediates meet the matrix
- * cores (needs K = 128, V % 128 == 0); in_dt = F32 runs an fp32 vector-ALU
- * kernel (K in {32, 64}, V % 32 == 0).
+ * Kernels: in_dt = BF16 with K = 128 and V % 128 == 0 runs bf16 MFMA tiles
+ * with fp32 accumulation, an fp32 state, and split-bf16 operands where fp32
+ * intermediates meet the matrix cores; every other supported shape (K in
+ * {32, 64, 128}, V % 32 == 0, in_dt F32 or BF16) runs an fp32 vector-ALU
+ * kernel on the inputs as given (GDN_ERR_UNSUPPORTED otherwise).
  * o_dt is F32 or BF16 (round to nearest even).
  * workspace: device memory of at least gdn_chunk_fwd_workspace_bytes(...)
- * bytes (0 for F32 inputs; NULL allowed then).  The BF16 path stores there,
+ * bytes (0 for the vector-ALU shapes; NULL allowed then).  The MFMA path stores there,
  * per 64-token chunk and v-head, the state-independent matrices of the UT
  * transform (products of T = (I + A)^{-1}, the masked Q K^T, the decays),
  * which a parallel pass computes before the serial chunk scan; contents on
@@ -194,7 +195,7 @@ gdn_status gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, gd
  *     n = scale * S_t^T q_t  (the output gdn_chunk_fwd would store).
  * Arguments as in gdn_chunk_fwd, plus z [B, T, H_v, V] in z_dt (dense, o's
  * layout), norm_weight fp32 [V] or NULL (ones), eps >= 0 (GDN_ERR_BAD_SHAPE
- * otherwise).  With in_dt = BF16 and V = 128 the scan applies the norm to
+ * otherwise).  On the MFMA path with V = 128 the scan applies the norm to
  * its fp32 output rows as it writes them, so n never reaches memory; other
  * shapes run gdn_chunk_fwd into o and then the norm in place over o (V in
  * {32, 64, 128, 256, 512}, GDN_ERR_UNSUPPORTED otherwise), with n rounded

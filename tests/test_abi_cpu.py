@@ -73,10 +73,14 @@ def test_chunk_validation(lib):
     assert _chunk(lib, qs=1 << 24) == SHAPE
     assert _chunk(lib, vs=1 << 24) == SHAPE
     assert _chunk(lib, Hqk=3) == SHAPE  # 32 % 3 != 0
-    assert _chunk(lib, K=64) == UNSUP  # bf16 kernel needs K = 128
-    assert _chunk(lib, V=96) == UNSUP
-    assert _chunk(lib, in_dt=0, K=128) == UNSUP  # fp32 kernel: K in {32, 64}
+    assert _chunk(lib, K=96) == UNSUP  # K in {32, 64, 128}
+    assert _chunk(lib, V=100) == UNSUP  # V a multiple of 32
+    assert _chunk(lib, in_dt=0, K=96) == UNSUP
     assert _chunk(lib, in_dt=0, K=32, V=48) == UNSUP
+    # bf16 K = 32 / 64, V = 32 and fp32 K = 128 run the vector-ALU kernel: supported, no workspace
+    assert _chunk(lib, K=64, V=32, ws=None, q=None) == NULLP
+    assert _chunk(lib, in_dt=0, K=128, ws=None, q=None) == NULLP
+    assert lib.gdn_chunk_fwd_workspace_bytes(1, 64, 1, 32, 64, 128) == 0
     assert _chunk(lib, cu=FAKE, n_seqs=2, B=2) == SEQ  # cu_seqlens needs B == 1
     assert _chunk(lib, cu=FAKE, n_seqs=0) == SEQ
     bad = (ctypes.c_int32 * 3)(0, 40, 30)  # decreasing
@@ -109,7 +113,7 @@ def test_chunk_noalloc_validation(lib):
     assert _chunk_noalloc(lib, in_dt=7) == DTYPE
     assert _chunk_noalloc(lib, B=0) == SHAPE
     assert _chunk_noalloc(lib, qs=100) == SHAPE
-    assert _chunk_noalloc(lib, K=64) == UNSUP
+    assert _chunk_noalloc(lib, K=96) == UNSUP
     assert _chunk_noalloc(lib, cu=FAKE, n_seqs=2, B=2) == SEQ
     # the records of 20992 bytes per (chunk slot, v-head) must fit GDN_NOALLOC_SCRATCH_BYTES
     record = 4 * 10 * 256 * 2 + 2 * 64 * 4
@@ -145,7 +149,7 @@ def test_chunk_gated_norm_validation(lib):
     # more norm rows than the norm kernel's grid holds: refused before the chunk forward is enqueued
     assert _chunk_norm(lib, V=256, T=(1 << 31) - 1) == UNSUP
     assert _chunk_norm(lib, q=None) == NULLP  # the chunk forward's own checks still apply
-    assert _chunk_norm(lib, K=64) == UNSUP
+    assert _chunk_norm(lib, K=96) == UNSUP
     assert _chunk_norm(lib, ws=None) == NULLP
     assert _chunk_norm(lib, T=0, q=None, k=None, v=None, g=None, beta=None, o=None, z=None) == OK
     assert _chunk_norm(lib, T=0, V=256, q=None, k=None, v=None, g=None, beta=None, o=None, z=None) == OK

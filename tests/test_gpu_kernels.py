@@ -128,7 +128,7 @@ def test_chunk_fp32_tiny_workload():
     assert_f32(host(fin), fref, "final")
 
 
-@pytest.mark.parametrize("K,V", [(32, 32), (64, 64), (32, 96)])
+@pytest.mark.parametrize("K,V", [(32, 32), (64, 64), (32, 96), (128, 32), (128, 128)])
 def test_chunk_fp32_packed_with_state(K, V):
     d = gdn_inputs.small(21, [1, 64, 65, 130, 7], 2, 4, K, V, "f32")
     N = 5
@@ -137,6 +137,26 @@ def test_chunk_fp32_packed_with_state(K, V):
     oref, fref = _oracle_chunk(d, s0)
     assert_f32(host(o), oref, "o")
     assert_f32(host(fin), fref, "final")
+
+
+@pytest.mark.parametrize("K,V", [(32, 32), (64, 128), (128, 32)])
+@pytest.mark.parametrize("o_dtype", ["f32", "bf16"])
+def test_chunk_bf16_small_heads_vector_kernel(K, V, o_dtype):
+    """bf16 inputs of head sizes outside the MFMA kernel's (K = 128, V % 128 == 0) run the fp32
+    vector-ALU kernel on the given bf16 values: fp32 arithmetic, so the fp32 bound holds (bf16 o
+    adds its own rounding)."""
+    d = gdn_inputs.small(22, [1, 64, 65, 130, 0, 7], 2, 4, K, V, "bf16")
+    N = 6
+    s0 = (np.random.default_rng(4).standard_normal((N, 4, K, V)) * 0.5).astype(np.float32)
+    od = torch.float32 if o_dtype == "f32" else torch.bfloat16
+    o, fin = _run_chunk(d, "bf16", s0, o_dtype=od)
+    oref, fref = _oracle_chunk(d, s0)
+    assert_f32(host(fin), fref, "final")
+    if o_dtype == "f32":
+        assert_f32(host(o), oref, "o")
+    else:
+        excess = np.abs(host(o) - oref) - (TOL_F32_ABS + 2.0 ** -8 * np.abs(oref))
+        assert excess.max() <= 0, float(excess.max())
 
 
 GATES = {
