@@ -68,8 +68,11 @@ __device__ __forceinline__ void tile_rc(int b, int& i, int& j) {
 // the kernel is a chain of dependent steps, hidden by running many waves.
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3)))
 chunk_prep_kernel(ChunkArgs a, int with_p) {
-  __shared__ float sAd[4][16][BP];  // diagonal blocks of A, read by the forward substitution
-  __shared__ float sTd[4][16][BP];  // diagonal blocks of T, written column by column
+  // diagonal blocks of A (read by the forward substitution) and of T (written
+  // column by column); at the end the same 8 tiles stage T diag(beta)
+  __shared__ float sStage[8][16][BP];
+  float(*sAd)[16][BP] = sStage;
+  float(*sTd)[16][BP] = sStage + 4;
   __shared__ double sG[CH];
   __shared__ float sBeta[CH];
 
@@ -267,19 +270,35 @@ chunk_prep_kernel(ChunkArgs a, int with_p) {
     }
   }
 
-  // ---- T diag(beta) as bf16 pairs -> record (row 4 g4 + e, column c16 of each tile)
+  // ---- T diag(beta) as bf16 pairs -> record, staged through LDS (eight tiles
+  // at a time) so that a lane stores four consecutive values of a row
 #pragma unroll
-  for (int b = 0; b < 10; ++b) {
-    int bi, bj;
-    tile_rc(b, bi, bj);
-    const float bs = sBeta[16 * bj + c16];
+  for (int round = 0; round < 2; ++round) {
+    constexpr int kStage = 8;
+    const int b0 = kStage * round, nb = round == 0 ? kStage : 10 - kStage;
+    __syncthreads();  // the stage's previous contents are read
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      uint16_t hi, lo;
-      split_bf16(T[b][e] * bs, hi, lo);
-      rtb[(0 * 10 + b) * 256 + (4 * g4 + e) * 16 + c16] = hi;
-      rtb[(1 * 10 + b) * 256 + (4 * g4 + e) * 16 + c16] = lo;
-    }
+    for (int bb = 0; bb < kStage; ++bb)
+      if (bb < nb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sStage[bb][4 * g4 + e][c16] = T[b0 + bb][e];
+      }
+    __syncthreads();
+#pragma unroll
+    for (int bb = 0; bb < kStage; ++bb)
+      if (bb < nb) {
+        const int b = b0 + bb;
+        int bi, bj;
+        tile_rc(b, bi, bj);
+        float tb[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) tb[x] = sStage[bb][c16][4 * g4 + x] * sBeta[16 * bj + 4 * g4 + x];
+        uint32_t h0, l0, h1, l1;
+        split2(tb[0], tb[1], h0, l0);
+        split2(tb[2], tb[3], h1, l1);
+        *reinterpret_cast<u32x2*>(rtb + (0 * 10 + b) * 256 + c16 * 16 + 4 * g4) = u32x2{h0, h1};
+        *reinterpret_cast<u32x2*>(rtb + (1 * 10 + b) * 256 + c16 * 16 + 4 * g4) = u32x2{l0, l1};
+      }
   }
 }
 
