@@ -48,6 +48,7 @@ import gdn_inputs  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_F32_VALU_TFLOPS = 157.3  # MI355X fp32 vector ALU
 METRIC = "GDN fwd tokens/s at H_v=32,K=V=128 bf16; % bf16 MFMA peak"
 MAIN = "packed_varlen_bf16_T8192_N8_Hv32_K128"
 LONG = "long_segmented_bf16_T32768_P8_Hv32_K128"
@@ -71,6 +72,16 @@ def chunk_alg_bytes(T, N, Hqk, Hv, K, V, o_bytes, in_bytes=2, s0=False):
 
 def conv_alg_bytes(T, C, in_bytes=2):
     return 2 * in_bytes * T * C
+
+
+def conv_alg_flops(T, C, width):
+    """conv taps, SiLU (exp, add, divide) and the L2 norm (square, sum, scale) per channel and token."""
+    return (2 * width + 6) * T * C
+
+
+def conv_chunk_alg_bytes(T, N, Hqk, Hv, K, V, o_bytes, in_bytes=2, s0=False):
+    """The fused conv + chunk call: raw q | k | v channels in, gates in, o out, states (weights negligible)."""
+    return chunk_alg_bytes(T, N, Hqk, Hv, K, V, o_bytes, in_bytes, s0)
 
 
 CHUNK_SOURCES = ("chunk_prep.hip", "chunk_bf16.hip", "compose.hip", "split_plan.cpp", "api.cpp", "device_common.h",
@@ -254,6 +265,42 @@ def build_pipeline(w, d, o_dtype, rotate=4):
     return {"step": step, "conv": conv, "chunk": chunk, "chunk_inputs": chunk_inputs, "C": C}
 
 
+def build_conv_chunk(w, d):
+    """Gates + the fused conv + chunk call of a workload, on its raw conv input."""
+    torch = _torch()
+    import gated_deltanet_linear_chunk_amd as gdn
+
+    dev = torch.device("cuda:0")
+    T = w.total_tokens
+    Hv = w.Hv
+    C = 2 * w.Hqk * w.K + Hv * w.V
+    B = w.batch_rows
+    L = T // B
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)  # noqa: E731
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)  # noqa: E731
+    xs = rotated_inputs(bf(d["x"]).reshape(B, L, C), 4)
+    cw, cb = bf(d["conv_w"]), bf(d["conv_bias"])
+    a, b = f32(d["a"]).reshape(B, L, Hv), f32(d["b"]).reshape(B, L, Hv)
+    A_log, dt_bias = f32(d["A_log"]), f32(d["dt_bias"])
+    cu = None if B > 1 else torch.from_numpy(d["cu_seqlens"]).to(dev)
+    cu_host = None if B > 1 else d["cu_seqlens"]
+    s0 = f32(d["s0"]) if "s0" in d else None
+    g0, beta0 = gdn.gdn_gate_fwd(a, b, A_log, dt_bias)
+    state = {"i": 0}
+
+    def fused(x, g, beta):
+        return gdn.gdn_conv_chunk_fwd(x, cw, g, beta, Hqk=w.Hqk, K=w.K, bias=cb, initial_state=s0, cu_seqlens=cu,
+                                      cu_seqlens_host=cu_host, o_dtype=torch.float32)
+
+    def step():
+        x = xs[state["i"] % len(xs)]
+        state["i"] += 1
+        g, beta = gdn.gdn_gate_fwd(a, b, A_log, dt_bias)
+        return fused(x, g, beta)
+
+    return {"step": step, "call": lambda: fused(xs[0], g0, beta0), "C": C}
+
+
 def build_chunk_only(w, d, o_dtype, mode="plain"):
     """The chunk call of a workload with q, k, v given (mode plain, segmented or gated_norm)."""
     torch = _torch()
@@ -402,7 +449,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--o-dtype", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--only", default="",
-                    help="comma-separated extras to run (segmented, split, batched, wide, decode, norm, fused); "
+                    help="comma-separated extras to run (segmented, split, batched, wide, decode, norm, fused, "
+                         "conv_chunk); "
                          "default all")
     ap.add_argument("--copy-only", type=int, default=0,
                     help="only run N plain 256 MiB device copies (counter calibration for profiles)")
@@ -525,6 +573,25 @@ def main():
                 st, tokens_per_s=w.total_tokens / (st["mean_ms"] * 1e-3))
             del dx
             torch.cuda.empty_cache()
+
+        if want("conv_chunk"):
+            # conv1d + SiLU + q/k L2 norm inside the fp32 vector-ALU chunk kernel (activations never stored)
+            fc = build_conv_chunk(w, d)
+            sec = timed_steps(fc["step"], max(3, args.steps // 4), 1)
+            st = summary(time_call(fc["call"], max(3, reps // 6), flush))
+            C = fc["C"]
+            fused_b = conv_chunk_alg_bytes(T, N, w.Hqk, w.Hv, w.K, w.V, o_bytes, s0="s0" in d)
+            unfused_b = conv_alg_bytes(T, C) + 16 * w.Hv * T + chunk_alg_bytes(T, N, w.Hqk, w.Hv, w.K, w.V, o_bytes,
+                                                                               s0="s0" in d)
+            flops = chunk_alg_flops(T, w.Hqk, w.Hv, w.K, w.V) + conv_alg_flops(T, C, w.conv_width)
+            lines["%s[conv + chunk fused, vector-ALU kernel]" % MAIN] = dict(
+                st, step_tokens_per_s=T / sec, kernel="chunk_f32_kernel<128, bf16, conv>",
+                bytes_per_token_fused=fused_b / T, bytes_per_token_unfused=unfused_b / T,
+                achieved_tflops=flops / (st["median_ms"] * 1e-3) / 1e12, peak_tflops=PEAK_F32_VALU_TFLOPS,
+                alu_frac=flops / (st["median_ms"] * 1e-3) / 1e12 / PEAK_F32_VALU_TFLOPS)
+            del fc
+            torch.cuda.empty_cache()
+            print("conv_chunk line done", file=sys.stderr, flush=True)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, d)

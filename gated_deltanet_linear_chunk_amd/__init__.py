@@ -23,6 +23,7 @@ __all__ = [
     "gdn_chunk_fwd",
     "gdn_chunk_fwd_noalloc",
     "gdn_chunk_fwd_gated_norm",
+    "gdn_conv_chunk_fwd",
     "gdn_segment_state_scan",
     "gdn_chunk_fwd_segmented",
     "gdn_segmented_workspace_bytes",
@@ -50,6 +51,7 @@ EXPORTED_SYMBOLS = (
     "gdn_chunk_fwd",
     "gdn_chunk_fwd_noalloc",
     "gdn_chunk_fwd_gated_norm",
+    "gdn_conv_chunk_fwd",
     "gdn_segment_state_scan_workspace_bytes",
     "gdn_segment_state_scan",
     "gdn_segmented_workspace_bytes",
@@ -99,6 +101,8 @@ def load_library():
     lib.gdn_chunk_fwd_gated_norm.argtypes = [P, P, P, ctypes.c_int, i64, i64, i64, P, P, f32, P, P, P, i32, i32, i64,
                                              i32, i32, i32, i32, P, ctypes.c_int, P, f32, P, ctypes.c_int, P, P,
                                              sz, P]
+    lib.gdn_conv_chunk_fwd.argtypes = [P, P, P, ctypes.c_int, i32, f32, P, P, f32, P, P, P, i32, i32, i64, i32, i32,
+                                       i32, i32, P, ctypes.c_int, P, P]
     lib.gdn_segment_state_scan_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
     lib.gdn_segment_state_scan_workspace_bytes.restype = sz
     lib.gdn_segment_state_scan.argtypes = [P, P, ctypes.c_int, i64, i64, P, P, P, P, i32, P, i64, i32, i32, i32, i32,
@@ -111,7 +115,7 @@ def load_library():
                                     ctypes.c_int, P]
     lib.gdn_gated_rmsnorm_fwd.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P, f32, i64, i32, P, ctypes.c_int, P]
     for name in ("gdn_gate_fwd", "gdn_conv1d_fwd", "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_gated_norm",
-                 "gdn_segment_state_scan",
+                 "gdn_conv_chunk_fwd", "gdn_segment_state_scan",
                  "gdn_chunk_fwd_segmented", "gdn_decode_step", "gdn_gated_rmsnorm_fwd"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -391,6 +395,50 @@ def gdn_chunk_fwd_gated_norm(q, k, v, g, beta, z, norm_weight=None, eps: float =
         0 if ws is None else ws.numel(), _stream(dev),
     )
     _check("gdn_chunk_fwd_gated_norm", st)
+    return o, fin
+
+
+def gdn_conv_chunk_fwd(x, w, g, beta, Hqk: int, K: int, bias=None, scale: float = 1.0, initial_state=None,
+                       cu_seqlens=None, cu_seqlens_host=None, l2_eps: float = 1e-6, o_dtype=None,
+                       output_final_state: bool = True):
+    """conv1d + SiLU + q/k L2 norm formed inside the chunk kernel, then the chunk rule.
+
+    x [B, T, C] raw channels q heads | k heads | v heads, C = 2 Hqk K + Hv V;
+    w [C, W] and bias [C] or None in x's dtype; g, beta fp32 [B, T, Hv] (Hv
+    from g).  The activations stay in fp32 inside the kernel.  Other arguments
+    and the results as gdn_chunk_fwd.
+    """
+    torch = _torch()
+    dev = x.device
+    _require(x, "x", dev)
+    _require(w, "w", dev, x.dtype)
+    _require(bias, "bias", dev, x.dtype)
+    _require(g, "g", dev, torch.float32)
+    _require(beta, "beta", dev, torch.float32)
+    _require(initial_state, "initial_state", dev, torch.float32)
+    _require(cu_seqlens, "cu_seqlens", dev, torch.int32)
+    if x.dim() != 3 or g.dim() != 3:
+        raise ValueError("x must be [B, T, C] and g, beta [B, T, Hv]")
+    B, T, C = x.shape
+    Hv = g.shape[2]
+    if g.shape[:2] != (B, T) or beta.shape != g.shape:
+        raise ValueError("g / beta shapes disagree with x")
+    if Hv < 1 or (C - 2 * Hqk * K) <= 0 or (C - 2 * Hqk * K) % Hv != 0:
+        raise ValueError("x channels must be 2 Hqk K + Hv V")
+    V = (C - 2 * Hqk * K) // Hv
+    if w.dim() != 2 or w.shape[0] != C or (bias is not None and tuple(bias.shape) != (C,)):
+        raise ValueError("w must be [C, W] and bias [C]")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if initial_state is not None and initial_state.shape != (N, Hv, K, V):
+        raise ValueError("initial_state must be [N, Hv, K, V]")
+    o = torch.empty((B, T, Hv, V), dtype=x.dtype if o_dtype is None else o_dtype, device=dev)
+    fin = torch.empty((N, Hv, K, V), dtype=torch.float32, device=dev) if output_final_state else None
+    st = load_library().gdn_conv_chunk_fwd(
+        _ptr(x), _ptr(w), _ptr(bias), _dtype_code(x), w.shape[1], float(l2_eps), _ptr(g), _ptr(beta), float(scale),
+        _ptr(initial_state), _ptr(cu_seqlens), _host_offsets(cu_seqlens_host), 0 if cu_seqlens is None else N, B, T,
+        Hqk, Hv, K, V, _ptr(o), _dtype_code(o), _ptr(fin), _stream(dev),
+    )
+    _check("gdn_conv_chunk_fwd", st)
     return o, fin
 
 

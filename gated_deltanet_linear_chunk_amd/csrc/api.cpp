@@ -384,6 +384,65 @@ gdn_status gdn_chunk_fwd_gated_norm(const void* q, const void* k, const void* v,
   return gdn_gated_rmsnorm_fwd(o, o_dt, z, z_dt, norm_weight, eps, total * H_v, V, o, o_dt, stream);
 }
 
+gdn_status gdn_conv_chunk_fwd(const void* x, const void* w, const void* bias, gdn_dtype in_dt,
+                              int32_t width, float l2_eps, const float* g, const float* beta,
+                              float scale, const float* initial_state, const int32_t* cu_seqlens,
+                              const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t B, int64_t T,
+                              int32_t H_qk, int32_t H_v, int32_t K, int32_t V, void* o,
+                              gdn_dtype o_dt, float* final_state, hipStream_t stream) {
+  if (!valid_dtype(in_dt) || !valid_dtype(o_dt)) return GDN_ERR_BAD_DTYPE;
+  if (B < 1 || T < 0 || H_qk < 1 || H_v < 1 || K < 1 || V < 1) return GDN_ERR_BAD_SHAPE;
+  if (H_v % H_qk != 0 || !(l2_eps > 0.f)) return GDN_ERR_BAD_SHAPE;
+  if (width < 1 || width > 4) return GDN_ERR_UNSUPPORTED;
+  if ((K != 32 && K != 64 && K != 128) || V % 32 != 0) return GDN_ERR_UNSUPPORTED;
+  const int64_t C = 2 * (int64_t)H_qk * K + (int64_t)H_v * V;
+  int64_t stride = C;
+  if (!stride_ok(&stride, C)) return GDN_ERR_BAD_SHAPE;
+  if (cu_seqlens) {
+    if (B != 1 || n_seqs < 1) return GDN_ERR_BAD_SEQLENS;
+    if (cu_seqlens_host && !offsets_ok(cu_seqlens_host, n_seqs, 0, T, true)) return GDN_ERR_BAD_SEQLENS;
+  }
+  const int32_t N = cu_seqlens ? n_seqs : B;
+  if (N > kMaxGrid || H_v > kMaxGrid) return GDN_ERR_UNSUPPORTED;
+  const int64_t total = cu_seqlens ? T : (int64_t)B * T;
+  if (total == 0 && !final_state) return GDN_OK;
+  if (total > 0 && (!x || !w || !g || !beta || !o)) return GDN_ERR_NULL_POINTER;
+  const size_t es = in_dt == GDN_BF16 ? 2 : 4;
+  const unsigned char* xb = static_cast<const unsigned char*>(x);
+  gdn::ChunkArgs a{};
+  a.q = xb;
+  a.k = xb ? xb + es * (size_t)H_qk * K : nullptr;
+  a.v = xb ? xb + es * 2 * (size_t)H_qk * K : nullptr;
+  a.g = g;
+  a.beta = beta;
+  a.cu = cu_seqlens;
+  a.n_seqs = N;
+  a.row_len = T;
+  a.Ttot = total;
+  a.Hqk = H_qk;
+  a.Hv = H_v;
+  a.K = K;
+  a.V = V;
+  a.q_stride = a.k_stride = a.v_stride = stride;
+  a.scale = scale;
+  a.in_dt = in_dt;
+  a.s0_mode = initial_state ? 1 : 0;
+  a.s0 = initial_state;
+  a.o = o;
+  a.o_dt = o_dt;
+  a.sf = final_state;
+  a.sf_seq_stride = (int64_t)H_v * K * V;
+  a.sf_head_stride = (int64_t)K * V;
+  a.sf_row_stride = V;
+  a.cw = w;
+  a.cb = bias;
+  a.conv_width = width;
+  a.l2_eps = l2_eps;
+  // A zero-token call only copies the start states; the plain kernel does that.
+  if (total == 0) a.cw = nullptr;
+  return hip_status(gdn::launch_chunk_f32(a, stream));
+}
+
 size_t gdn_segment_state_scan_workspace_bytes(int64_t T, int32_t P, int32_t H_v, int32_t K,
                                               int32_t V) {
   (void)K;

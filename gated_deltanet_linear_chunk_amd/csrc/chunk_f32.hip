@@ -3,18 +3,27 @@
 // The fp32 path (fp32 inputs, and bf16 inputs of the head sizes the MFMA
 // kernel does not take): every product runs on the fp32 vector units, so
 // results stay within ~1e-6 relative of exact arithmetic on the given inputs.
-// One workgroup owns (sequence, v-head, 32-column slice of V; 16 columns for
-// K = 128) and walks the
-// sequence's 64-token chunks in order.  Per chunk, with local tokens r, s and
-// G the in-chunk cumulative gate (kept in fp64 so that G_r - G_s does not
-// cancel), it forms
+// One workgroup of 1024 threads owns (sequence, v-head, 32-column slice of V)
+// and walks the sequence's 64-token chunks in order.  Per chunk, with local
+// tokens r, s and G the in-chunk cumulative gate (kept in fp64 so that
+// G_r - G_s does not cancel), it forms
 //   A = strictly-lower(diag(beta) K K^T * e^{G_r - G_s}),  T = (I + A)^{-1},
-//   W = T diag(beta e^G) K,  U0 = T diag(beta) V,
-//   U = U0 - W S,  O = diag(e^G) Q S + lower(Q K^T * e^{G_r - G_s}) U,
+//   R = V - diag(e^G) K S,  U = T diag(beta) R,
+//   O = diag(e^G) Q S + lower(Q K^T * e^{G_r - G_s}) U,
 //   S <- e^{G_last} S + (diag(e^{G_last - G}) K)^T U,
-// which is the token recurrence regrouped by chunk (each column of S evolves
-// independently, hence the V slices).  Rows past the end of a sequence are
-// zero with g = beta = 0, which leaves S and every valid output unchanged.
+// which is the token recurrence regrouped by chunk (the UT transform's
+// U = T diag(beta) V - T diag(beta e^G) K S, grouped so that no K-wide
+// product of T is formed; each column of S evolves independently, hence the
+// V slices).  Rows past the end of a sequence are zero with g = beta = 0,
+// which leaves S and every valid output unchanged.
+//
+// Fused variant (ChunkArgs::cw set): the layer's short convolution feeds the
+// rule on the same token-major layout (LlamaFactory PR "[v1] support GDN
+// Ulysses cp", Design), so the load stage takes the raw q | k | v channels
+// instead and forms each chunk row itself: depthwise causal conv over the
+// row's own sequence (x is zero before its first token), SiLU, and the L2
+// norm of every q and k row over its head.  The activations stay in fp32
+// registers and LDS; nothing of them is stored or rounded to in_dt.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -23,11 +32,9 @@ namespace gdn {
 namespace {
 
 constexpr int CH = 64;      // chunk length
-constexpr int F32_BV = 32;  // V columns per workgroup (16 for K = 128, which needs the LDS for Q, K, W)
-
-template <int K>
-constexpr int f32_bv() { return K >= 128 ? 16 : F32_BV; }
-constexpr int F32_THREADS = 256;
+constexpr int TB = 16;      // block size of the triangular inverse
+constexpr int BV = 32;  // V columns per workgroup
+constexpr int F32_THREADS = 1024;  // 4 waves per SIMD: one workgroup fills a CU's LDS
 
 template <typename TI>
 __device__ __forceinline__ float ld(const TI* p, int64_t i);
@@ -38,12 +45,24 @@ __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, int64_t i) {
   return bf16_bits_to_f32(p[i]);
 }
 
-template <int K, typename TI>
+// SiLU(bias + sum_j w[j] x[t - W + 1 + j]) for one channel: x at column col
+// of a token-major buffer with `stride` elements per token, rows before bos
+// counted as zero.
+template <typename TI>
+__device__ __forceinline__ float conv_silu(const TI* x, int64_t stride, int64_t col, const TI* w, const TI* b,
+                                           int W, int64_t t, int64_t bos) {
+  float z = b ? ld<TI>(b, 0) : 0.f;
+  for (int j = 0; j < W; ++j) {
+    const int64_t tt = t - (W - 1) + j;
+    if (tt >= bos) z = fmaf(ld<TI>(w, j), ld<TI>(x, tt * stride + col), z);
+  }
+  return z / (1.f + expf(-z));
+}
+
+template <int K, typename TI, bool kConv>
 __global__ void __launch_bounds__(F32_THREADS) chunk_f32_kernel(ChunkArgs a) {
-  constexpr int BV = f32_bv<K>();
   __shared__ float sQ[CH][K + 1];
   __shared__ float sK[CH][K + 1];
-  __shared__ float sW[CH][K + 1];
   __shared__ float sU[CH][BV + 1];
   __shared__ float sV[CH][BV + 1];
   __shared__ float sS[K][BV + 1];
@@ -51,6 +70,7 @@ __global__ void __launch_bounds__(F32_THREADS) chunk_f32_kernel(ChunkArgs a) {
   __shared__ float sT[CH][CH + 1];
   __shared__ double sG[CH];
   __shared__ float sBeta[CH], sGam[CH], sDec[CH];
+  __shared__ float sInv[2 * CH];  // fused conv: 1 / L2 norm of the q rows, then the k rows
 
   const int tid = threadIdx.x;
   const int v0 = blockIdx.x * BV;
@@ -83,32 +103,77 @@ __global__ void __launch_bounds__(F32_THREADS) chunk_f32_kernel(ChunkArgs a) {
   for (int64_t t0 = bos; t0 < eos; t0 += CH) {
     const int L = (int)((eos - t0) < CH ? (eos - t0) : CH);
     __syncthreads();  // previous chunk fully consumed
-    for (int i = tid; i < CH * K; i += F32_THREADS) {
-      const int r = i / K, d = i % K;
-      float qv = 0.f, kv = 0.f;
-      if (r < L) {
-        kv = ld<TI>(k, (t0 + r) * a.k_stride + (int64_t)hq * K + d);
-        if (a.q) qv = ld<TI>(q, (t0 + r) * a.q_stride + (int64_t)hq * K + d);
+    if constexpr (kConv) {
+      const TI* cw = (const TI*)a.cw;
+      const TI* cb = (const TI*)a.cb;
+      const int W = a.conv_width;
+      const int64_t kc0 = (int64_t)a.Hqk * K;  // first k channel; v's follow k's
+#pragma unroll 2
+      for (int i = tid; i < CH * K; i += F32_THREADS) {
+        const int r = i / K, d = i % K;
+        const int64_t c = (int64_t)hq * K + d;
+        float qv = 0.f, kv = 0.f;
+        if (r < L) {
+          kv = conv_silu<TI>(k, a.k_stride, c, cw + (kc0 + c) * W, cb ? cb + kc0 + c : nullptr, W, t0 + r, bos);
+          if (a.q) qv = conv_silu<TI>(q, a.q_stride, c, cw + c * W, cb ? cb + c : nullptr, W, t0 + r, bos);
+        }
+        sQ[r][d] = qv;
+        sK[r][d] = kv;
       }
-      sQ[r][d] = qv;
-      sK[r][d] = kv;
+      for (int i = tid; i < CH * BV; i += F32_THREADS) {
+        const int r = i / BV, c = i % BV;
+        const int64_t col = (int64_t)h * a.V + v0 + c;
+        float vv = 0.f;
+        if (r < L)
+          vv = conv_silu<TI>(v, a.v_stride, col, cw + (2 * kc0 + col) * W, cb ? cb + 2 * kc0 + col : nullptr, W,
+                             t0 + r, bos);
+        sV[r][c] = vv;
+      }
+      __syncthreads();
+      if (tid < 2 * CH) {
+        const int r = tid % CH;
+        const float* row = tid < CH ? &sQ[r][0] : &sK[r][0];
+        float ss = 0.f;
+        for (int d = 0; d < K; ++d) ss = fmaf(row[d], row[d], ss);
+        sInv[tid] = 1.f / sqrtf(ss + a.l2_eps);
+      }
+      __syncthreads();
+      for (int i = tid; i < CH * K; i += F32_THREADS) {
+        const int r = i / K, d = i % K;
+        if (r < L) {  // rows past the end stay zero
+          sQ[r][d] *= sInv[r];
+          sK[r][d] *= sInv[CH + r];
+        }
+      }
+    } else {
+#pragma unroll 8
+      for (int i = tid; i < CH * K; i += F32_THREADS) {
+        const int r = i / K, d = i % K;
+        float qv = 0.f, kv = 0.f;
+        if (r < L) {
+          kv = ld<TI>(k, (t0 + r) * a.k_stride + (int64_t)hq * K + d);
+          if (a.q) qv = ld<TI>(q, (t0 + r) * a.q_stride + (int64_t)hq * K + d);
+        }
+        sQ[r][d] = qv;
+        sK[r][d] = kv;
+      }
+      for (int i = tid; i < CH * BV; i += F32_THREADS) {
+        const int r = i / BV, c = i % BV;
+        float vv = 0.f;
+        if (r < L && a.v) vv = ld<TI>(v, (t0 + r) * a.v_stride + (int64_t)h * a.V + v0 + c);
+        sV[r][c] = vv;
+      }
     }
-    for (int i = tid; i < CH * BV; i += F32_THREADS) {
-      const int r = i / BV, c = i % BV;
-      float vv = 0.f;
-      if (r < L && a.v) vv = ld<TI>(v, (t0 + r) * a.v_stride + (int64_t)h * a.V + v0 + c);
-      sV[r][c] = vv;
-    }
-    if (tid < CH) {
+    if (tid < CH) {  // wave 0: beta, and G as an inclusive fp64 scan across the wave's lanes
       const bool ok = tid < L;
       sBeta[tid] = ok ? a.beta[(t0 + tid) * a.Hv + h] : 0.f;
-    }
-    if (tid == 0) {
-      double G = 0.0;
-      for (int r = 0; r < CH; ++r) {
-        if (r < L) G += (double)a.g[(t0 + r) * a.Hv + h];
-        sG[r] = G;
+      double G = ok ? (double)a.g[(t0 + tid) * a.Hv + h] : 0.0;
+#pragma unroll
+      for (int off = 1; off < CH; off <<= 1) {
+        const double y = __shfl_up(G, off, CH);
+        if (tid >= off) G += y;
       }
+      sG[tid] = G;
     }
     __syncthreads();
     if (tid < CH) {
@@ -128,21 +193,51 @@ __global__ void __launch_bounds__(F32_THREADS) chunk_f32_kernel(ChunkArgs a) {
       sA[r][s] = val;
     }
     __syncthreads();
-    // T = (I + A)^{-1}, one column per thread, forward substitution
+    // T = (I + A)^{-1} by 16x16 blocks (A is strictly lower, so I + A is unit
+    // lower triangular).  The diagonal blocks T_ii = (I + A_ii)^{-1} come from
+    // forward substitution, one column per lane in registers; below them
+    // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, which follows from (I + A) T = I
+    // and needs only blocks of earlier block diagonals, so the block
+    // diagonals i - j = 1, 2, 3 follow one another, each as two small
+    // products over all threads (the sum into sU, free until U is formed,
+    // then the product with T_ii).  Blocks above the diagonal are never read.
     if (tid < CH) {
-      const int j = tid;
-      for (int r = 0; r < CH; ++r) {
-        float val = 0.f;
-        if (r == j) {
-          val = 1.f;
-        } else if (r > j) {
-          for (int s = j; s < r; ++s) val = fmaf(-sA[r][s], sT[s][j], val);
-        }
-        sT[r][j] = val;
+      const int b0 = (tid / TB) * TB, j = tid % TB;
+      float x[TB];
+#pragma unroll
+      for (int r = 0; r < TB; ++r) {
+        float acc = 0.f;
+#pragma unroll
+        for (int u = 0; u < r; ++u) acc = fmaf(-sA[b0 + r][b0 + u], x[u], acc);
+        x[r] = r == j ? 1.f : (r < j ? 0.f : acc);
+        sT[b0 + r][b0 + j] = x[r];
       }
     }
     __syncthreads();
-    // P (into sA), W, U0
+    for (int dd = 1; dd < CH / TB; ++dd) {
+      const int nb = CH / TB - dd;  // blocks on this block diagonal
+      for (int t = tid; t < nb * TB * TB; t += F32_THREADS) {
+        const int jb = t / (TB * TB), r = (t / TB) % TB, c = t % TB;
+        const int ib = jb + dd;
+        float acc = 0.f;
+        for (int kb = jb; kb < ib; ++kb) {
+#pragma unroll
+          for (int u = 0; u < TB; ++u) acc = fmaf(sA[ib * TB + r][kb * TB + u], sT[kb * TB + u][jb * TB + c], acc);
+        }
+        sU[jb * TB + r][c] = acc;
+      }
+      __syncthreads();
+      for (int t = tid; t < nb * TB * TB; t += F32_THREADS) {
+        const int jb = t / (TB * TB), r = (t / TB) % TB, c = t % TB;
+        const int ib = jb + dd;
+        float acc = 0.f;
+#pragma unroll
+        for (int u = 0; u < TB; ++u) acc = fmaf(sT[ib * TB + r][ib * TB + u], sU[jb * TB + u][c], acc);
+        sT[ib * TB + r][jb * TB + c] = -acc;
+      }
+      __syncthreads();
+    }
+    // P = lower(Q K^T * D) into sA, and R = V - diag(gamma) K S in place of V
     for (int i = tid; i < CH * CH; i += F32_THREADS) {
       const int r = i / CH, s = i % CH;
       float val = 0.f;
@@ -154,25 +249,20 @@ __global__ void __launch_bounds__(F32_THREADS) chunk_f32_kernel(ChunkArgs a) {
       }
       sA[r][s] = val;
     }
-    for (int i = tid; i < CH * K; i += F32_THREADS) {
-      const int r = i / K, d = i % K;
-      float acc = 0.f;
-      for (int s = 0; s <= r; ++s) acc = fmaf(sT[r][s] * sBeta[s] * sGam[s], sK[s][d], acc);
-      sW[r][d] = acc;
-    }
     for (int i = tid; i < CH * BV; i += F32_THREADS) {
       const int r = i / BV, c = i % BV;
-      float acc = 0.f;
-      for (int s = 0; s <= r; ++s) acc = fmaf(sT[r][s] * sBeta[s], sV[s][c], acc);
-      sU[r][c] = acc;
+      float ks = 0.f;
+#pragma unroll 8
+      for (int d = 0; d < K; ++d) ks = fmaf(sK[r][d], sS[d][c], ks);
+      sV[r][c] = fmaf(-sGam[r], ks, sV[r][c]);
     }
     __syncthreads();
-    // U = U0 - W S
+    // U = T diag(beta) R
     for (int i = tid; i < CH * BV; i += F32_THREADS) {
       const int r = i / BV, c = i % BV;
-      float acc = sU[r][c];
+      float acc = 0.f;
 #pragma unroll 8
-      for (int d = 0; d < K; ++d) acc = fmaf(-sW[r][d], sS[d][c], acc);
+      for (int s = 0; s <= r; ++s) acc = fmaf(sT[r][s] * sBeta[s], sV[s][c], acc);
       sU[r][c] = acc;
     }
     __syncthreads();
@@ -185,7 +275,8 @@ __global__ void __launch_bounds__(F32_THREADS) chunk_f32_kernel(ChunkArgs a) {
 #pragma unroll 8
         for (int d = 0; d < K; ++d) qs = fmaf(sQ[r][d], sS[d][c], qs);
         float pu = 0.f;
-        for (int s = 0; s <= r; ++s) pu = fmaf(sA[r][s], sU[s][c], pu);
+  #pragma unroll 8
+      for (int s = 0; s <= r; ++s) pu = fmaf(sA[r][s], sU[s][c], pu);
         const float out = a.scale * fmaf(sGam[r], qs, pu);
         const int64_t off = ((t0 + r) * a.Hv + h) * (int64_t)a.V + v0 + c;
         if (a.o_dt == 1)
@@ -200,6 +291,7 @@ __global__ void __launch_bounds__(F32_THREADS) chunk_f32_kernel(ChunkArgs a) {
     for (int i = tid; i < K * BV; i += F32_THREADS) {
       const int d = i / BV, c = i % BV;
       float acc = 0.f;
+#pragma unroll 8
       for (int s = 0; s < CH; ++s) acc = fmaf(sK[s][d] * sDec[s], sU[s][c], acc);
       sS[d][c] = fmaf(gl, sS[d][c], acc);
     }
@@ -216,11 +308,16 @@ __global__ void __launch_bounds__(F32_THREADS) chunk_f32_kernel(ChunkArgs a) {
 
 template <int K>
 hipError_t launch_k(const ChunkArgs& a, hipStream_t stream) {
-  dim3 grid(a.V / f32_bv<K>(), a.Hv, a.n_seqs);
-  if (a.in_dt == 1)
-    hipLaunchKernelGGL((chunk_f32_kernel<K, uint16_t>), grid, dim3(F32_THREADS), 0, stream, a);
+  dim3 grid(a.V / BV, a.Hv, a.n_seqs);
+  const bool conv = a.cw != nullptr;
+  if (a.in_dt == 1 && conv)
+    hipLaunchKernelGGL((chunk_f32_kernel<K, uint16_t, true>), grid, dim3(F32_THREADS), 0, stream, a);
+  else if (a.in_dt == 1)
+    hipLaunchKernelGGL((chunk_f32_kernel<K, uint16_t, false>), grid, dim3(F32_THREADS), 0, stream, a);
+  else if (conv)
+    hipLaunchKernelGGL((chunk_f32_kernel<K, float, true>), grid, dim3(F32_THREADS), 0, stream, a);
   else
-    hipLaunchKernelGGL((chunk_f32_kernel<K, float>), grid, dim3(F32_THREADS), 0, stream, a);
+    hipLaunchKernelGGL((chunk_f32_kernel<K, float, false>), grid, dim3(F32_THREADS), 0, stream, a);
   return hipGetLastError();
 }
 

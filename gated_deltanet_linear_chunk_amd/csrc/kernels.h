@@ -59,6 +59,17 @@ struct ChunkArgs {
   int z_dt;         // 0 f32, 1 bf16
   const float* nw;  // [V] or null (ones)
   float eps;
+  // fp32 kernel only: when cw is set, q, k and v point at the q | k | v
+  // channel groups of one token-major buffer of raw conv inputs (k's group
+  // starts Hqk*K channels after q's, v's 2*Hqk*K after), cw [channels,
+  // conv_width] and cb [channels] (or null) are the depthwise conv's weights
+  // and bias in in_dt, and the kernel forms q, k, v itself: conv over the
+  // sequence's previous conv_width - 1 tokens (zero before its start), SiLU,
+  // and q, k rows divided by sqrt(sum of squares + l2_eps) per head.
+  const void* cw;
+  const void* cb;
+  int conv_width;
+  float l2_eps;
 };
 
 // One record: T diag(beta) hi, lo (bf16, 10 tiles x 256 each), gamma[64] and

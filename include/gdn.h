@@ -213,6 +213,38 @@ gdn_status gdn_chunk_fwd_gated_norm(const void* q, const void* k, const void* v,
                                     hipStream_t stream);
 
 /*
+ * The short convolution, SiLU and q/k L2 norm of gdn_conv1d_fwd fused into
+ * the chunk rule's load stage.  The pages run the depthwise conv over the
+ * concatenated q | k | v channels and hand its output to the chunk rule on
+ * the same token-major layout (LlamaFactory PR "[v1] support GDN Ulysses
+ * cp", Design: Q/K/V concatenated for conv1d, then the chunk rule); here
+ * the chunk kernel forms each 64-token chunk's q, k, v rows from the raw
+ * channels itself:
+ *     a[t, c] = silu(bias[c] + sum_{j<width} w[c, j] x[t - width + 1 + j, c])
+ * with x zero before the first token of t's sequence, and every q and k
+ * head row divided by sqrt(sum of squares + l2_eps) -- the activations of
+ * gdn_conv1d_fwd with l2norm_channels = 2 H_qk K, head_dim = K -- then runs
+ * the rule of gdn_chunk_fwd on them.  The activations are kept in fp32 and
+ * never written to memory (nor rounded to in_dt).
+ *  x     [B, T, C] in in_dt, dense, C = 2 H_qk K + H_v V channels in the order
+ *        q heads | k heads | v heads
+ *  w     [C, width] in in_dt, width in [1, 4];  bias [C] in in_dt or NULL
+ *  l2_eps > 0 (GDN_ERR_BAD_SHAPE otherwise)
+ *  g, beta, scale, initial_state, cu_seqlens, cu_seqlens_host, n_seqs, B,
+ *  T, H_qk, H_v, K, V, o, o_dt, final_state: as gdn_chunk_fwd.
+ * Runs the fp32 vector-ALU chunk kernel for every shape (K in {32, 64, 128},
+ * V % 32 == 0; GDN_ERR_UNSUPPORTED otherwise), with no workspace: each
+ * workgroup forms the q, k rows of its head and the v columns of its slice,
+ * so q and k are convolved once per column slice and v-head sharing them.
+ */
+gdn_status gdn_conv_chunk_fwd(const void* x, const void* w, const void* bias, gdn_dtype in_dt,
+                              int32_t width, float l2_eps, const float* g, const float* beta,
+                              float scale, const float* initial_state, const int32_t* cu_seqlens,
+                              const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t B, int64_t T,
+                              int32_t H_qk, int32_t H_v, int32_t K, int32_t V, void* o,
+                              gdn_dtype o_dt, float* final_state, hipStream_t stream);
+
+/*
  * Segment state scan: one long sequence cut into P contiguous segments
  * [seg_offsets[i], seg_offsets[i+1]) of the token arrays (the sglang PR's
  * per-rank segments, here on one GPU).  Pass 1 computes, for every segment

@@ -176,6 +176,34 @@ def test_conv_validation(lib):
     assert conv(rounding=1, x=None) == NULLP
 
 
+def test_conv_chunk_validation(lib):
+    def cc(**kw):
+        a = dict(x=FAKE, w=FAKE, bias=None, in_dt=1, W=4, eps=1e-6, g=FAKE, beta=FAKE, scale=1.0, s0=None, cu=None,
+                 cu_host=None, n_seqs=0, B=1, T=64, Hqk=16, Hv=32, K=128, V=128, o=FAKE, o_dt=0, fin=None,
+                 stream=None)
+        a.update(kw)
+        return lib.gdn_conv_chunk_fwd(*a.values())
+
+    assert cc(x=None) == NULLP
+    assert cc(w=None) == NULLP
+    assert cc(g=None) == NULLP
+    assert cc(o=None) == NULLP
+    assert cc(in_dt=3) == DTYPE
+    assert cc(o_dt=3) == DTYPE
+    assert cc(B=0) == SHAPE
+    assert cc(Hv=24) == SHAPE  # H_v % H_qk
+    assert cc(eps=0.0) == SHAPE
+    assert cc(eps=float("nan")) == SHAPE
+    assert cc(W=5) == UNSUP
+    assert cc(W=0) == UNSUP
+    assert cc(K=96) == UNSUP
+    assert cc(V=100) == UNSUP
+    assert cc(cu=FAKE, n_seqs=2, B=2) == SEQ
+    assert cc(cu=FAKE, n_seqs=2, cu_host=(ctypes.c_int32 * 3)(0, 10, 63)) == SEQ  # must end at T
+    assert cc(cu=FAKE, n_seqs=0) == SEQ
+    assert cc(T=0, x=None, w=None, g=None, beta=None, o=None) == OK  # nothing to do without a final state
+
+
 def test_gate_and_segment_validation(lib):
     assert lib.gdn_gate_fwd(FAKE, FAKE, FAKE, FAKE, 10, 0, FAKE, FAKE, None) == SHAPE
     assert lib.gdn_gate_fwd(None, FAKE, FAKE, FAKE, 10, 4, FAKE, FAKE, None) == NULLP
@@ -283,3 +311,5 @@ def test_binding_refuses_cpu_tensors():
         gdn.gdn_chunk_fwd_gated_norm(q, q, v, g, g, v)
     with pytest.raises(ValueError, match="GPU tensor"):
         gdn.gdn_gated_rmsnorm_fwd(v, v)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        gdn.gdn_conv_chunk_fwd(torch.zeros(1, 64, 1024), torch.zeros(1024, 4), g, g, Hqk=2, K=128)

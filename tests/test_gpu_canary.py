@@ -162,6 +162,37 @@ def test_conv_writes_nothing_outside(exact):
     assert bool(torch.isfinite(y.payload().view(torch.bfloat16)).all())
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_conv_chunk_writes_nothing_outside(dtype):
+    """The fused conv + chunk call, with device-only offsets that leave the last
+    sample's tokens in no sample: their o rows stay untouched as well."""
+    lib = gdn.load_library()
+    Hqk, Hv, K, V = 2, 4, 64, 64
+    lengths = [1, 63, 0, 130, 40]
+    d = gdn_inputs.small(23, lengths, Hqk, Hv, K, V, dtype, conv_width=4, s0_std=0.05)
+    T, C = d["x"].shape
+    N = len(lengths) - 1
+    es = 2 if dtype == "bf16" else 4
+    x, cw, cb = dev(d["x"], dtype), dev(d["conv_w"], dtype), dev(d["conv_bias"], dtype)
+    g, beta = gdn.gdn_gate_fwd(dev(d["a"]), dev(d["b"]), dev(d["A_log"]), dev(d["dt_bias"]))
+    cu = dev(d["cu_seqlens"][:-1], "i32")
+    s0 = dev(d["s0"][:N])
+    o = Guarded(T * Hv * V * es)
+    fin = Guarded(N * Hv * K * V * 4)
+    in_dt = gdn.BF16 if dtype == "bf16" else gdn.F32
+    st = lib.gdn_conv_chunk_fwd(x.data_ptr(), cw.data_ptr(), cb.data_ptr(), in_dt, 4, 1e-6, g.data_ptr(),
+                                beta.data_ptr(), 0.125, s0.data_ptr(), cu.data_ptr(), None, N, 1, T, Hqk, Hv, K, V,
+                                o.ptr, in_dt, fin.ptr, _stream())
+    assert st == 0
+    o.check("o")
+    fin.check("final_state")
+    rows = o.payload((T, Hv * V * es))
+    last = int(d["cu_seqlens"][-2])
+    assert bool((rows[last:] == PATTERN).all()), "o rows of tokens in no sample were written"
+    vals = rows[:last].view(torch.bfloat16 if dtype == "bf16" else torch.float32)
+    assert bool(torch.isfinite(vals).all())
+
+
 def test_segment_scan_and_segmented_forward_write_nothing_outside():
     lib = gdn.load_library()
     Hqk, Hv, K, V = 2, 4, 128, 128
