@@ -230,48 +230,50 @@ static gdn_status chunk_fwd_run(const void* q, const void* k, const void* v, gdn
     a.eps = norm->eps;
   }
   if (!mfma) return hip_status(gdn::launch_chunk_f32(a, stream));
-  // The per-chunk records of the samples go first: the host plans a split
-  // while they run, and a split run reads the same records.
-  hipError_t e = gdn::launch_chunk_prep(a, (o && q) ? 1 : 0, stream);
-  if (e != hipSuccess) return GDN_ERR_HIP;
-  if (!fixed_ws && cu_seqlens && cu_seqlens_host && total > 0) {
-    gdn::SplitPlan plan;
-    if (gdn::plan_split(cu_seqlens_host, N, H_v, V, initial_state != nullptr, device_cus(), plan) &&
-        workspace_bytes >= split_workspace_bytes(total, N, plan.n_seg, plan.n_prefix, H_v, K, V)) {
-      // ---- segment-split run (see plan_split) ----------------------------------
-      unsigned char* w = static_cast<unsigned char*>(workspace);
-      const size_t st = (size_t)H_v * K * V;
-      w += align256(tbuf_bytes(total, N, H_v));
-      float* M = reinterpret_cast<float*>(w);
-      w += align256((size_t)plan.n_prefix * H_v * K * K * sizeof(float));
-      float* bmap = reinterpret_cast<float*>(w);
-      w += align256((size_t)plan.n_prefix * st * sizeof(float));
-      float* starts = reinterpret_cast<float*>(w);
-      w += align256((size_t)plan.n_prefix * st * sizeof(float));
-      int32_t* ints = reinterpret_cast<int32_t*>(w);
-      e = gdn::launch_plan_store(plan.ints.data(), (int64_t)plan.ints.size(), ints, stream);
-      if (e != hipSuccess) return GDN_ERR_HIP;
-      a.cu = ints;
-      a.n_seqs = plan.n_seg;
-      a.rec_seq = ints + plan.off_sample();
-      gdn::ChunkArgs p1 = a;
-      p1.seq_order = ints + plan.off_pre();
-      p1.n_blocks_z = plan.n_prefix;
-      e = gdn::launch_segment_pass1(p1, M, bmap, stream, false);
-      if (e != hipSuccess) return GDN_ERR_HIP;
-      e = gdn::launch_compose_chains(M, bmap, initial_state, ints + plan.off_chains(), plan.n_chain, H_v, K, V,
-                                     starts, 0, nullptr, stream);
-      if (e != hipSuccess) return GDN_ERR_HIP;
-      gdn::ChunkArgs p2 = a;
-      p2.seq_order = ints + plan.off_order();
-      p2.n_blocks_z = plan.n_seg;
-      p2.s0_ref = ints + plan.off_s0ref();
-      p2.s0_seg = starts;
-      p2.sf_map = ints + plan.off_sfmap();
-      return hip_status(gdn::launch_chunk_bf16(p2, stream, false));
-    }
+  // A split plan (cached for repeated offsets) comes first, so that the prep
+  // launch on the samples also stores its index arrays.
+  gdn::SplitPlan plan;
+  bool split = false;
+  if (!fixed_ws && cu_seqlens && cu_seqlens_host && total > 0)
+    split = gdn::plan_split(cu_seqlens_host, N, H_v, V, initial_state != nullptr, device_cus(), plan) &&
+            workspace_bytes >= split_workspace_bytes(total, N, plan.n_seg, plan.n_prefix, H_v, K, V);
+  if (!split) {
+    const hipError_t e = gdn::launch_chunk_prep(a, (o && q) ? 1 : 0, stream);
+    if (e != hipSuccess) return GDN_ERR_HIP;
+    return hip_status(gdn::launch_chunk_bf16(a, stream, false));
   }
-  return hip_status(gdn::launch_chunk_bf16(a, stream, false));
+  // ---- segment-split run (see plan_split) ----------------------------------------
+  unsigned char* w = static_cast<unsigned char*>(workspace);
+  const size_t st = (size_t)H_v * K * V;
+  w += align256(tbuf_bytes(total, N, H_v));
+  float* M = reinterpret_cast<float*>(w);
+  w += align256((size_t)plan.n_prefix * H_v * K * K * sizeof(float));
+  float* bmap = reinterpret_cast<float*>(w);
+  w += align256((size_t)plan.n_prefix * st * sizeof(float));
+  float* starts = reinterpret_cast<float*>(w);
+  w += align256((size_t)plan.n_prefix * st * sizeof(float));
+  int32_t* ints = reinterpret_cast<int32_t*>(w);
+  hipError_t e = gdn::launch_chunk_prep(a, (o && q) ? 1 : 0, stream, plan.ints.data(), (int64_t)plan.ints.size(),
+                                        ints);
+  if (e != hipSuccess) return GDN_ERR_HIP;
+  a.cu = ints;
+  a.n_seqs = plan.n_seg;
+  a.rec_seq = ints + plan.off_sample();
+  gdn::ChunkArgs p1 = a;
+  p1.seq_order = ints + plan.off_pre();
+  p1.n_blocks_z = plan.n_prefix;
+  e = gdn::launch_segment_pass1(p1, M, bmap, stream, false);
+  if (e != hipSuccess) return GDN_ERR_HIP;
+  e = gdn::launch_compose_chains(M, bmap, initial_state, ints + plan.off_chains(), plan.n_chain, H_v, K, V,
+                                 starts, 0, nullptr, stream);
+  if (e != hipSuccess) return GDN_ERR_HIP;
+  gdn::ChunkArgs p2 = a;
+  p2.seq_order = ints + plan.off_order();
+  p2.n_blocks_z = plan.n_seg;
+  p2.s0_ref = ints + plan.off_s0ref();
+  p2.s0_seg = starts;
+  p2.sf_map = ints + plan.off_sfmap();
+  return hip_status(gdn::launch_chunk_bf16(p2, stream, false));
 }
 
 gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, gdn_dtype in_dt,
@@ -570,9 +572,6 @@ gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
   maps[0] = -2;
   for (int32_t i = 1; i < P; ++i) maps[i] = i - 1;
   maps[(size_t)P + P - 1] = 0;
-  hipError_t e = gdn::launch_plan_store(maps.data(), (int64_t)maps.size(), ints, stream);
-  if (e != hipSuccess) return GDN_ERR_HIP;
-
   gdn::ChunkArgs a{};
   a.tbuf = reinterpret_cast<float*>(w + l.rec);
   a.q = q;
@@ -601,7 +600,8 @@ gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
   a.sf_seq_stride = (int64_t)H_v * K * V;
   a.sf_head_stride = (int64_t)K * V;
   a.sf_row_stride = V;
-  e = gdn::launch_chunk_prep(a, T > 0 ? 1 : 0, stream);
+  // the maps go to the device with the prep launch
+  hipError_t e = gdn::launch_chunk_prep(a, T > 0 ? 1 : 0, stream, maps.data(), (int64_t)maps.size(), ints);
   if (e != hipSuccess) return GDN_ERR_HIP;
   if (P > 1) {
     gdn::ChunkArgs p1 = a;

@@ -67,7 +67,7 @@ __device__ __forceinline__ void tile_rc(int b, int& i, int& j) {
 // Three waves per SIMD (at most 168 registers; the LDS tiles take 9.5 KB):
 // the kernel is a chain of dependent steps, hidden by running many waves.
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3)))
-chunk_prep_kernel(ChunkArgs a, int with_p) {
+chunk_prep_kernel(ChunkArgs a, int with_p, PlanArg plan, int32_t* __restrict__ plan_dst) {
   // diagonal blocks of A (read by the forward substitution) and of T (written
   // column by column); at the end the same 8 tiles stage T diag(beta)
   __shared__ float sStage[8][16][BP];
@@ -78,6 +78,11 @@ chunk_prep_kernel(ChunkArgs a, int with_p) {
 
   const int lane = threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
+  // Index arrays of the scans that follow, carried in the launch's arguments
+  // (see launch_plan_store): stored by workgroup 0, so they need no launch of
+  // their own.
+  if (blockIdx.x == 0)
+    for (int i = lane; i < plan.n; i += 64) plan_dst[i] = plan.v[i];
   // 1-D grid.  Workgroup ids go to the eight XCDs in turn, so ids x and x + 8
   // share an XCD (and its L2): with an even GQA ratio they are the two v-heads
   // of one q/k head in one chunk slot, and the second reads K and Q from L2.
@@ -306,15 +311,24 @@ chunk_prep_kernel(ChunkArgs a, int with_p) {
 
 int64_t chunk_slots(int64_t Ttot, int n_seqs) { return (Ttot + 63) / 64 + n_seqs; }
 
-hipError_t launch_chunk_prep(const ChunkArgs& a, int with_p, hipStream_t stream) {
+hipError_t launch_chunk_prep(const ChunkArgs& a, int with_p, hipStream_t stream, const int32_t* ints,
+                             int64_t n_ints, int32_t* ints_dst) {
   const int64_t slots = chunk_slots(a.Ttot, a.n_seqs);
-  if (slots == 0 || a.Hv == 0) return hipSuccess;
+  if (slots == 0 || a.Hv == 0) return n_ints > 0 ? launch_plan_store(ints, n_ints, ints_dst, stream) : hipSuccess;
+  PlanArg plan;
+  plan.n = (int)(n_ints < kPlanArgInts ? n_ints : kPlanArgInts);
+  for (int i = 0; i < plan.n; ++i) plan.v[i] = ints[i];
+  if (n_ints > kPlanArgInts) {  // the rest by plan_store_kernel
+    const hipError_t e = launch_plan_store(ints + kPlanArgInts, n_ints - kPlanArgInts, ints_dst + kPlanArgInts,
+                                           stream);
+    if (e != hipSuccess) return e;
+  }
   // one wave per (chunk slot, v-head)
   // pairs of v-heads fill groups of 16 ids: pad the grid to whole groups
   int64_t n = slots * a.Hv;
   if ((a.Hv / a.Hqk) % 2 == 0) n = (n + 15) / 16 * 16;
   if (n > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)n), dim3(64), 0, stream, a, with_p);
+  hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)n), dim3(64), 0, stream, a, with_p, plan, ints_dst);
   return hipGetLastError();
 }
 

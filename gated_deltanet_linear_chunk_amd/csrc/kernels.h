@@ -82,8 +82,6 @@ constexpr int PREP_RECORD_BYTES = PREP_REC_P + 2 * 10 * 256 * 2;
 
 // Number of chunk slots a launch over Ttot tokens in n_seqs sequences uses.
 int64_t chunk_slots(int64_t Ttot, int n_seqs);
-// with_p: also form the output matrix P (needs q).
-hipError_t launch_chunk_prep(const ChunkArgs& a, int with_p, hipStream_t stream);
 
 hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t stream);
 // prep + scan; with prep = false the records in a.tbuf must already be there
@@ -110,6 +108,11 @@ struct PlanArg {
   int32_t v[kPlanArgInts];
 };
 hipError_t launch_plan_store(const int32_t* ints, int64_t n, int32_t* dst, hipStream_t stream);
+// The per-chunk records of a (with_p: also the output matrix P, which needs
+// q).  When n_ints > 0 the same launch also stores ints[0, n_ints) at
+// ints_dst, as launch_plan_store does.
+hipError_t launch_chunk_prep(const ChunkArgs& a, int with_p, hipStream_t stream, const int32_t* ints = nullptr,
+                             int64_t n_ints = 0, int32_t* ints_dst = nullptr);
 hipError_t launch_compose_chains(const float* M, const float* b, const float* s0,
                                  const int32_t* chains, int n_chains, int Hv, int K, int V,
                                  float* out, int write_before, float* final_state,
