@@ -78,21 +78,28 @@ __global__ void __launch_bounds__(CTHREADS) compose_kernel(const float* __restri
   // products of step j, and those of step 0 with the start state, so a chain
   // waits on memory about once rather than once per step.  A operands: rows
   // 16 (2 wave + t) + c of M, k = 32 g .. 32 g + 31.
+  // A chain from a zero state (no s0 row) has b_0 as its first result exactly
+  // (M_0 0 adds only zeros), so its first step neither loads M_0 nor
+  // multiplies, and M_1 is on its way at once.
+  const bool zero_start = !(s0 && ch.n >= 0);
   f32x4 ma[2][8], bq[2];
-  auto load_step = [&](int j) {
+  auto load_step = [&](int j, bool with_m) {
     const int seg = ch.p0 + j;
     const float* Mseg = M + ((int64_t)seg * Hv + h) * CK * CK;
     const float* bseg = b + (int64_t)seg * row + head + c0 + c;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      if (with_m) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        ma[t][q] = *reinterpret_cast<const f32x4*>(Mseg + (int64_t)(16 * (2 * wave + t) + c) * CK + 32 * g + 4 * q);
+        for (int q = 0; q < 8; ++q)
+          ma[t][q] =
+              *reinterpret_cast<const f32x4*>(Mseg + (int64_t)(16 * (2 * wave + t) + c) * CK + 32 * g + 4 * q);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) bq[t][e] = bseg[(int64_t)orow[t][e] * V];
     }
   };
-  if (ch.count > 0) load_step(0);
+  if (ch.count > 0) load_step(0, !zero_start);
   for (int i = tid; i < CK * CT; i += CTHREADS) {
     const int r = i / CT, cc = i % CT;
     sS[0][sidx(r, cc)] = (s0 && ch.n >= 0) ? s0[ch.n * row + head + (int64_t)r * V + c0 + cc] : 0.f;
@@ -101,26 +108,31 @@ __global__ void __launch_bounds__(CTHREADS) compose_kernel(const float* __restri
   int cur = 0;
   for (int j = 0; j < ch.count; ++j) {
     float* dst = out + (int64_t)(ch.out0 + j) * row + head + c0 + c;
+    const bool product = j > 0 || !zero_start;
     f32x4 mcur[2][8], acc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       acc[t] = bq[t];
+      if (product) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) mcur[t][q] = ma[t][q];
+        for (int q = 0; q < 8; ++q) mcur[t][q] = ma[t][q];
+      }
     }
-    if (j + 1 < ch.count) load_step(j + 1);
+    if (j + 1 < ch.count) load_step(j + 1, true);
     if (write_before) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) dst[(int64_t)orow[t][e] * V] = sS[cur][sidx(orow[t][e], c)];
     }
+    if (product) {
 #pragma unroll
-    for (int s = 0; s < 32; ++s) {
-      const float bv = sS[cur][sidx(32 * g + s, c)];
+      for (int s = 0; s < 32; ++s) {
+        const float bv = sS[cur][sidx(32 * g + s, c)];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(mcur[t][s >> 2][s & 3], bv, acc[t], 0, 0, 0);
+        for (int t = 0; t < 2; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(mcur[t][s >> 2][s & 3], bv, acc[t], 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
