@@ -458,7 +458,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the path shards by head, "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the path shards by head, "
               "sequence or segment; see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

@@ -57,7 +57,7 @@ typedef enum gdn_status {
   GDN_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
   GDN_ERR_BAD_SHAPE = 2,    /* negative / inconsistent sizes */
   GDN_ERR_BAD_DTYPE = 3,    /* dtype code not accepted by this entry point */
-  GDN_ERR_UNSUPPORTED = 4,  /* valid request this build has no kernel for */
+  GDN_ERR_UNSUPPORTED = 4,  /* valid request for which the library has no kernel */
   GDN_ERR_BAD_SEQLENS = 5,  /* cu_seqlens / offsets malformed or with B > 1 */
   GDN_ERR_HIP = 6,          /* a HIP runtime call or kernel launch failed */
   GDN_ERR_SCRATCH_TOO_SMALL = 7 /* gdn_chunk_fwd_noalloc: input beyond its fixed array */
