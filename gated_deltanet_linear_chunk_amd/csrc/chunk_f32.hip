@@ -15,7 +15,10 @@
 // U = T diag(beta) V - T diag(beta e^G) K S, grouped so that no K-wide
 // product of T is formed; each column of S evolves independently, hence the
 // V slices).  Rows past the end of a sequence are zero with g = beta = 0,
-// which leaves S and every valid output unchanged.
+// which leaves S and every valid output unchanged.  The kernel is bound by
+// LDS reads, so every product gives each thread a small register tile (2 x 2
+// of A and P, two rows of R, U and O, K / 32 rows of S) whose operands are
+// each read once and used two or more times.
 //
 // Fused variant (ChunkArgs::cw set): the layer's short convolution feeds the
 // rule on the same token-major layout (LlamaFactory PR "[v1] support GDN
@@ -35,6 +38,7 @@ constexpr int CH = 64;      // chunk length
 constexpr int TB = 16;      // block size of the triangular inverse
 constexpr int BV = 32;  // V columns per workgroup
 constexpr int F32_THREADS = 1024;  // 4 waves per SIMD: one workgroup fills a CU's LDS
+static_assert(F32_THREADS == 1024 && CH == 64 && BV == 32, "the register tiles give one tile to every thread");
 
 template <typename TI>
 __device__ __forceinline__ float ld(const TI* p, int64_t i);
@@ -45,18 +49,41 @@ __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, int64_t i) {
   return bf16_bits_to_f32(p[i]);
 }
 
-// SiLU(bias + sum_j w[j] x[t - W + 1 + j]) for one channel: x at column col
-// of a token-major buffer with `stride` elements per token, rows before bos
-// counted as zero.
-template <typename TI>
-__device__ __forceinline__ float conv_silu(const TI* x, int64_t stride, int64_t col, const TI* w, const TI* b,
-                                           int W, int64_t t, int64_t bos) {
-  float z = b ? ld<TI>(b, 0) : 0.f;
-  for (int j = 0; j < W; ++j) {
-    const int64_t tt = t - (W - 1) + j;
-    if (tt >= bos) z = fmaf(ld<TI>(w, j), ld<TI>(x, tt * stride + col), z);
+// The thread index as a value the compiler cannot see through.  Taken anew
+// in every chunk step, it keeps the LDS addresses of the phases (all indexed
+// by it) from being hoisted out of the chunk loop, where they would all stay
+// live across it and spill.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// SiLU(bias + sum_{j<W} w[j] x[t - W + 1 + j]) for one channel at the R
+// consecutive tokens t = t_first .. t_first + R - 1: x at column col of a
+// token-major buffer with `stride` elements per token, counted as zero outside
+// [bos, eos); tokens from eos on give 0.  The W <= 4 taps sit in the last of
+// four slots (the others hold 0, adding exact zeros first), and the R + 3
+// tokens the window spans are loaded once.
+template <typename TI, int R>
+__device__ __forceinline__ void conv_silu_rows(const TI* x, int64_t stride, int64_t col, const TI* w, const TI* b,
+                                               int W, int64_t t_first, int64_t bos, int64_t eos, float (&out)[R]) {
+  float w4[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w4[j] = j >= 4 - W ? ld<TI>(w, j - (4 - W)) : 0.f;
+  const float bias = b ? ld<TI>(b, 0) : 0.f;
+  float xw[R + 3];
+#pragma unroll
+  for (int u = 0; u < R + 3; ++u) {
+    const int64_t tt = t_first - 3 + u;
+    xw[u] = (tt >= bos && tt < eos) ? ld<TI>(x, tt * stride + col) : 0.f;
   }
-  return z / (1.f + expf(-z));
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float z = bias;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) z = fmaf(w4[j], xw[r + j], z);
+    out[r] = t_first + r < eos ? z / (1.f + expf(-z)) : 0.f;
+  }
 }
 
 template <int K, typename TI, bool kConv>
@@ -72,7 +99,7 @@ __global__ void __launch_bounds__(F32_THREADS) chunk_f32_kernel(ChunkArgs a) {
   __shared__ float sBeta[CH], sGam[CH], sDec[CH];
   __shared__ float sInv[2 * CH];  // fused conv: 1 / L2 norm of the q rows, then the k rows
 
-  const int tid = threadIdx.x;
+  const int tid0 = threadIdx.x;
   const int v0 = blockIdx.x * BV;
   const int h = blockIdx.y;
   const int seq = blockIdx.z;
@@ -90,7 +117,7 @@ __global__ void __launch_bounds__(F32_THREADS) chunk_f32_kernel(ChunkArgs a) {
   const TI* v = (const TI*)a.v;
 
   // initial state
-  for (int i = tid; i < K * BV; i += F32_THREADS) {
+  for (int i = tid0; i < K * BV; i += F32_THREADS) {
     const int d = i / BV, c = i % BV;
     float s = 0.f;
     if (a.s0_mode == 1)
@@ -101,6 +128,7 @@ __global__ void __launch_bounds__(F32_THREADS) chunk_f32_kernel(ChunkArgs a) {
   }
 
   for (int64_t t0 = bos; t0 < eos; t0 += CH) {
+    const int tid = opaque(tid0);
     const int L = (int)((eos - t0) < CH ? (eos - t0) : CH);
     __syncthreads();  // previous chunk fully consumed
     if constexpr (kConv) {
@@ -108,26 +136,34 @@ __global__ void __launch_bounds__(F32_THREADS) chunk_f32_kernel(ChunkArgs a) {
       const TI* cb = (const TI*)a.cb;
       const int W = a.conv_width;
       const int64_t kc0 = (int64_t)a.Hqk * K;  // first k channel; v's follow k's
-#pragma unroll 2
-      for (int i = tid; i < CH * K; i += F32_THREADS) {
-        const int r = i / K, d = i % K;
+      {  // q and k: channel d, rows rb .. rb + RQ - 1
+        constexpr int RQ = CH * K / F32_THREADS;
+        const int d = tid % K, rb = (tid / K) * RQ;
         const int64_t c = (int64_t)hq * K + d;
-        float qv = 0.f, kv = 0.f;
-        if (r < L) {
-          kv = conv_silu<TI>(k, a.k_stride, c, cw + (kc0 + c) * W, cb ? cb + kc0 + c : nullptr, W, t0 + r, bos);
-          if (a.q) qv = conv_silu<TI>(q, a.q_stride, c, cw + c * W, cb ? cb + c : nullptr, W, t0 + r, bos);
+        float qv[RQ], kv[RQ];
+        conv_silu_rows<TI, RQ>(k, a.k_stride, c, cw + (kc0 + c) * W, cb ? cb + kc0 + c : nullptr, W, t0 + rb, bos,
+                               eos, kv);
+        if (a.q) {
+          conv_silu_rows<TI, RQ>(q, a.q_stride, c, cw + c * W, cb ? cb + c : nullptr, W, t0 + rb, bos, eos, qv);
+        } else {
+#pragma unroll
+          for (int r = 0; r < RQ; ++r) qv[r] = 0.f;
         }
-        sQ[r][d] = qv;
-        sK[r][d] = kv;
+#pragma unroll
+        for (int r = 0; r < RQ; ++r) {
+          sQ[rb + r][d] = qv[r];
+          sK[rb + r][d] = kv[r];
+        }
       }
-      for (int i = tid; i < CH * BV; i += F32_THREADS) {
-        const int r = i / BV, c = i % BV;
-        const int64_t col = (int64_t)h * a.V + v0 + c;
-        float vv = 0.f;
-        if (r < L)
-          vv = conv_silu<TI>(v, a.v_stride, col, cw + (2 * kc0 + col) * W, cb ? cb + 2 * kc0 + col : nullptr, W,
-                             t0 + r, bos);
-        sV[r][c] = vv;
+      {  // v: column cc of the slice, rows rb .. rb + RV - 1
+        constexpr int RV = CH * BV / F32_THREADS;
+        const int cc = tid % BV, rb = (tid / BV) * RV;
+        const int64_t col = (int64_t)h * a.V + v0 + cc;
+        float vv[RV];
+        conv_silu_rows<TI, RV>(v, a.v_stride, col, cw + (2 * kc0 + col) * W, cb ? cb + 2 * kc0 + col : nullptr, W,
+                               t0 + rb, bos, eos, vv);
+#pragma unroll
+        for (int r = 0; r < RV; ++r) sV[rb + r][cc] = vv[r];
       }
       __syncthreads();
       if (tid < 2 * CH) {
@@ -180,17 +216,25 @@ __global__ void __launch_bounds__(F32_THREADS) chunk_f32_kernel(ChunkArgs a) {
       sGam[tid] = expf((float)sG[tid]);
       sDec[tid] = expf((float)(sG[CH - 1] - sG[tid]));
     }
-    // A (strictly lower)
-    for (int i = tid; i < CH * CH; i += F32_THREADS) {
-      const int r = i / CH, s = i % CH;
-      float val = 0.f;
-      if (s < r) {
-        float acc = 0.f;
-#pragma unroll 8
-        for (int d = 0; d < K; ++d) acc = fmaf(sK[r][d], sK[s][d], acc);
-        val = sBeta[r] * acc * expf((float)(sG[r] - sG[s]));
+    // A (strictly lower).  Register tiles: thread (r0, c0) = (tid / 32,
+    // tid % 32) forms rows r0, r0 + 32 against columns c0, c0 + 32 (the
+    // block (r0, c0 + 32) is above the diagonal), so that each value read
+    // from LDS feeds more than one product.
+    {
+      const int r0 = tid >> 5, c0 = tid & 31;
+      float a00 = 0.f, a10 = 0.f, a11 = 0.f;
+#pragma unroll 4
+      for (int d = 0; d < K; ++d) {
+        const float x0 = sK[r0][d], x1 = sK[r0 + 32][d], y0 = sK[c0][d], y1 = sK[c0 + 32][d];
+        a00 = fmaf(x0, y0, a00);
+        a10 = fmaf(x1, y0, a10);
+        a11 = fmaf(x1, y1, a11);
       }
-      sA[r][s] = val;
+      const bool lo = c0 < r0;
+      sA[r0][c0] = lo ? sBeta[r0] * a00 * expf((float)(sG[r0] - sG[c0])) : 0.f;
+      sA[r0 + 32][c0] = sBeta[r0 + 32] * a10 * expf((float)(sG[r0 + 32] - sG[c0]));
+      sA[r0 + 32][c0 + 32] = lo ? sBeta[r0 + 32] * a11 * expf((float)(sG[r0 + 32] - sG[c0 + 32])) : 0.f;
+      sA[r0][c0 + 32] = 0.f;
     }
     __syncthreads();
     // T = (I + A)^{-1} by 16x16 blocks (A is strictly lower, so I + A is unit
@@ -237,48 +281,72 @@ __global__ void __launch_bounds__(F32_THREADS) chunk_f32_kernel(ChunkArgs a) {
       }
       __syncthreads();
     }
-    // P = lower(Q K^T * D) into sA, and R = V - diag(gamma) K S in place of V
-    for (int i = tid; i < CH * CH; i += F32_THREADS) {
-      const int r = i / CH, s = i % CH;
-      float val = 0.f;
-      if (s <= r) {
-        float acc = 0.f;
-#pragma unroll 8
-        for (int d = 0; d < K; ++d) acc = fmaf(sQ[r][d], sK[s][d], acc);
-        val = acc * expf((float)(sG[r] - sG[s]));
+    // P = lower(Q K^T * D) into sA (tiles as for A), R = V - diag(gamma) K S
+    // in place of V (rows r0, r0 + 32 of column c0), and T <- T diag(beta)
+    {
+      const int r0 = tid >> 5, c0 = tid & 31;
+      float p00 = 0.f, p10 = 0.f, p11 = 0.f, k0 = 0.f, k1 = 0.f;
+#pragma unroll 4
+      for (int d = 0; d < K; ++d) {
+        const float x0 = sQ[r0][d], x1 = sQ[r0 + 32][d], y0 = sK[c0][d], y1 = sK[c0 + 32][d];
+        p00 = fmaf(x0, y0, p00);
+        p10 = fmaf(x1, y0, p10);
+        p11 = fmaf(x1, y1, p11);
       }
-      sA[r][s] = val;
-    }
-    for (int i = tid; i < CH * BV; i += F32_THREADS) {
-      const int r = i / BV, c = i % BV;
-      float ks = 0.f;
-#pragma unroll 8
-      for (int d = 0; d < K; ++d) ks = fmaf(sK[r][d], sS[d][c], ks);
-      sV[r][c] = fmaf(-sGam[r], ks, sV[r][c]);
+#pragma unroll 4
+      for (int d = 0; d < K; ++d) {
+        const float sv = sS[d][c0];
+        k0 = fmaf(sK[r0][d], sv, k0);
+        k1 = fmaf(sK[r0 + 32][d], sv, k1);
+      }
+      const bool lo = c0 <= r0;
+      sA[r0][c0] = lo ? p00 * expf((float)(sG[r0] - sG[c0])) : 0.f;
+      sA[r0 + 32][c0] = p10 * expf((float)(sG[r0 + 32] - sG[c0]));
+      sA[r0 + 32][c0 + 32] = lo ? p11 * expf((float)(sG[r0 + 32] - sG[c0 + 32])) : 0.f;
+      sA[r0][c0 + 32] = 0.f;
+      sV[r0][c0] = fmaf(-sGam[r0], k0, sV[r0][c0]);
+      sV[r0 + 32][c0] = fmaf(-sGam[r0 + 32], k1, sV[r0 + 32][c0]);
+      sT[r0][c0] *= sBeta[c0];
+      sT[r0 + 32][c0] *= sBeta[c0];
+      sT[r0 + 32][c0 + 32] *= sBeta[c0 + 32];
     }
     __syncthreads();
-    // U = T diag(beta) R
-    for (int i = tid; i < CH * BV; i += F32_THREADS) {
-      const int r = i / BV, c = i % BV;
-      float acc = 0.f;
-#pragma unroll 8
-      for (int s = 0; s <= r; ++s) acc = fmaf(sT[r][s] * sBeta[s], sV[s][c], acc);
-      sU[r][c] = acc;
+    // U = (T diag(beta)) R, rows r0 and r0 + 32 of column c0
+    {
+      const int r0 = tid >> 5, c0 = tid & 31;
+      float u0 = 0.f, u1 = 0.f;
+      for (int s = 0; s <= r0; ++s) {
+        const float rv = sV[s][c0];
+        u0 = fmaf(sT[r0][s], rv, u0);
+        u1 = fmaf(sT[r0 + 32][s], rv, u1);
+      }
+      for (int s = r0 + 1; s <= r0 + 32; ++s) u1 = fmaf(sT[r0 + 32][s], sV[s][c0], u1);
+      sU[r0][c0] = u0;
+      sU[r0 + 32][c0] = u1;
     }
     __syncthreads();
     // O = diag(gamma) Q S + P U
-    if (a.o) {
-      for (int i = tid; i < CH * BV; i += F32_THREADS) {
-        const int r = i / BV, c = i % BV;
+    if (a.o) {  // rows r0 and r0 + 32 of column c0
+      const int r0 = tid >> 5, c0 = tid & 31;
+      float q0 = 0.f, q1 = 0.f, w0 = 0.f, w1 = 0.f;
+#pragma unroll 4
+      for (int d = 0; d < K; ++d) {
+        const float sv = sS[d][c0];
+        q0 = fmaf(sQ[r0][d], sv, q0);
+        q1 = fmaf(sQ[r0 + 32][d], sv, q1);
+      }
+      for (int s = 0; s <= r0; ++s) {
+        const float uv = sU[s][c0];
+        w0 = fmaf(sA[r0][s], uv, w0);
+        w1 = fmaf(sA[r0 + 32][s], uv, w1);
+      }
+      for (int s = r0 + 1; s <= r0 + 32; ++s) w1 = fmaf(sA[r0 + 32][s], sU[s][c0], w1);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = r0 + 32 * j;
         if (r >= L) continue;
-        float qs = 0.f;
-#pragma unroll 8
-        for (int d = 0; d < K; ++d) qs = fmaf(sQ[r][d], sS[d][c], qs);
-        float pu = 0.f;
-  #pragma unroll 8
-      for (int s = 0; s <= r; ++s) pu = fmaf(sA[r][s], sU[s][c], pu);
-        const float out = a.scale * fmaf(sGam[r], qs, pu);
-        const int64_t off = ((t0 + r) * a.Hv + h) * (int64_t)a.V + v0 + c;
+        const float out = a.scale * fmaf(sGam[r], j ? q1 : q0, j ? w1 : w0);
+        const int64_t off = ((t0 + r) * a.Hv + h) * (int64_t)a.V + v0 + c0;
         if (a.o_dt == 1)
           ((uint16_t*)a.o)[off] = f32_to_bf16_bits(out);
         else
@@ -286,20 +354,29 @@ __global__ void __launch_bounds__(F32_THREADS) chunk_f32_kernel(ChunkArgs a) {
       }
       __syncthreads();
     }
-    // S <- gamma_last S + (diag(dec) K)^T U
-    const float gl = sGam[CH - 1];
-    for (int i = tid; i < K * BV; i += F32_THREADS) {
-      const int d = i / BV, c = i % BV;
-      float acc = 0.f;
-#pragma unroll 8
-      for (int s = 0; s < CH; ++s) acc = fmaf(sK[s][d] * sDec[s], sU[s][c], acc);
-      sS[d][c] = fmaf(gl, sS[d][c], acc);
+    // S <- gamma_last S + (diag(dec) K)^T U: rows d0 + 32 j (j < K / 32) of
+    // column c0
+    {
+      constexpr int NR = K / 32;
+      const int d0 = tid >> 5, c0 = tid & 31;
+      const float gl = sGam[CH - 1];
+      float acc[NR];
+#pragma unroll
+      for (int j = 0; j < NR; ++j) acc[j] = 0.f;
+#pragma unroll 4
+      for (int s = 0; s < CH; ++s) {
+        const float du = sDec[s] * sU[s][c0];
+#pragma unroll
+        for (int j = 0; j < NR; ++j) acc[j] = fmaf(sK[s][d0 + 32 * j], du, acc[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < NR; ++j) sS[d0 + 32 * j][c0] = fmaf(gl, sS[d0 + 32 * j][c0], acc[j]);
     }
   }
   __syncthreads();
   if (a.sf) {
     float* dst = a.sf + (int64_t)seq * a.sf_seq_stride + (int64_t)h * a.sf_head_stride;
-    for (int i = tid; i < K * BV; i += F32_THREADS) {
+    for (int i = tid0; i < K * BV; i += F32_THREADS) {
       const int d = i / BV, c = i % BV;
       dst[(int64_t)d * a.sf_row_stride + v0 + c] = sS[d][c];
     }
