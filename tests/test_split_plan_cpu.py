@@ -123,3 +123,35 @@ def test_plans_are_consistent(planner, lengths, Hv, V):
 ])
 def test_balanced_or_crowded_runs_are_not_split(planner, lengths, Hv, V):
     assert not planner(lengths, Hv, V)["split"]
+
+
+def test_planner_under_address_and_undefined_behaviour_sanitizers(tmp_path):
+    """The planner is host C++ that runs on every split call: build it (host only, g++) with
+    AddressSanitizer and UBSan and plan length mixes with empty samples, one long sample, many
+    short ones and the workloads' shapes; any out-of-bounds access, leak or undefined operation
+    aborts the driver or prints a report."""
+    if shutil.which("g++") is None:
+        pytest.skip("needs g++")
+    exe = str(tmp_path / "split_plan_san")
+    build = subprocess.run(["g++", "-O1", "-g", "-std=c++17", "-fsanitize=address,undefined", "-fno-omit-frame-pointer",
+                            "-fno-sanitize-recover=undefined", "-I", CSRC, os.path.join(ROOT, "tests", "split_plan_main.cpp"),
+                            os.path.join(CSRC, "split_plan.cpp"), "-o", exe], capture_output=True, text=True)
+    if build.returncode != 0:
+        pytest.skip("sanitizer runtimes not available: " + build.stderr[-200:])
+    rng = np.random.default_rng(3)
+    cases = [
+        (32, 128, [8192]),
+        (32, 128, [0, 0, 8192, 0]),
+        (32, 128, [1] * 300 + [20000]),
+        (32, 256, [3000, 200, 64, 1, 700, 2500, 1000, 727]),
+        (64, 256, [int(x) for x in rng.integers(0, 20000, 4)]),
+        (32, 128, [int(x) for x in rng.integers(0, 3000, 90)]),
+        (16, 128, [32768]),
+    ]
+    for Hv, V, lengths in cases:
+        for has_s0 in (0, 1):
+            inp = "%d %d %d %d %d %s" % (Hv, V, has_s0, 256, len(lengths), " ".join(map(str, lengths)))
+            r = subprocess.run([exe], input=inp, capture_output=True, text=True,
+                               env=dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1"))
+            assert r.returncode == 0, (Hv, V, lengths[:8], r.stderr[-2000:])
+            assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr[-2000:]
