@@ -139,8 +139,11 @@ class Flush:
 
 
 def time_call(call, reps, flush):
-    """Durations (ms) of `call` over reps, each after a flush, from HIP events on the current stream."""
+    """Durations (ms) of `call` over reps, each after a flush, from HIP events on the current stream.
+    One untimed call first: a kernel's first launch in a process also loads its code."""
     torch = _torch()
+    call()
+    torch.cuda.synchronize()
     pairs = []
     for _ in range(reps):
         flush()
