@@ -79,6 +79,47 @@ size_t split_workspace_bytes(int64_t total, int N, int n_seg, int n_prefix, int3
          align256(sizeof(int32_t) * (size_t)gdn::split_plan_ints_max(n_seg, n_prefix));
 }
 
+// Segment shapes: bf16 with K = 128 and V % 128 == 0 on the MFMA kernels;
+// K = 128 with V % 32 == 0 otherwise (either dtype) on the fp32 vector-ALU
+// kernel, whose maps the same fp32 composition chains.
+gdn_status segment_supported(int in_dt, int32_t K, int32_t V) {
+  if (mfma_path(in_dt, K, V)) return GDN_OK;
+  return (K == 128 && V > 0 && V % 32 == 0) ? GDN_OK : GDN_ERR_UNSUPPORTED;
+}
+
+// Pass 1 on the vector-ALU kernel: the augmented state [M | b] of each of the
+// a.n_seqs segments as two runs of the rule, M's K columns from the identity
+// with zero values, b's V columns from zero with the values.
+hipError_t segment_pass1_f32(const gdn::ChunkArgs& a, float* M, float* b, hipStream_t stream) {
+  gdn::ChunkArgs m = a;
+  m.q = nullptr;
+  m.v = nullptr;
+  m.o = nullptr;
+  m.V = a.K;
+  m.s0_mode = 2;
+  m.s0 = nullptr;
+  m.s0_ref = nullptr;
+  m.sf_map = nullptr;
+  m.sf = M;
+  m.sf_seq_stride = (int64_t)a.Hv * a.K * a.K;
+  m.sf_head_stride = (int64_t)a.K * a.K;
+  m.sf_row_stride = a.K;
+  hipError_t e = gdn::launch_chunk_f32(m, stream);
+  if (e != hipSuccess) return e;
+  gdn::ChunkArgs c = a;
+  c.q = nullptr;
+  c.o = nullptr;
+  c.s0_mode = 0;
+  c.s0 = nullptr;
+  c.s0_ref = nullptr;
+  c.sf_map = nullptr;
+  c.sf = b;
+  c.sf_seq_stride = (int64_t)a.Hv * a.K * a.V;
+  c.sf_head_stride = (int64_t)a.K * a.V;
+  c.sf_row_stride = a.V;
+  return gdn::launch_chunk_f32(c, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -462,16 +503,18 @@ gdn_status gdn_segment_state_scan(const void* k, const void* v, gdn_dtype in_dt,
                                   float* b, float* seg_initial_states, float* final_state,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!valid_dtype(in_dt)) return GDN_ERR_BAD_DTYPE;
-  if (in_dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
   if (P < 1 || T < 0 || H_qk < 1 || H_v < 1 || H_v % H_qk != 0) return GDN_ERR_BAD_SHAPE;
-  if (K != 128 || V < 1 || V % 128 != 0) return GDN_ERR_UNSUPPORTED;
+  const gdn_status sup = segment_supported(in_dt, K, V);
+  if (sup != GDN_OK) return sup;
+  const bool mfma = mfma_path(in_dt, K, V);
   if (P > kMaxGrid || H_v > kMaxGrid) return GDN_ERR_UNSUPPORTED;
   if (!stride_ok(&k_token_stride, (int64_t)H_qk * K) || !stride_ok(&v_token_stride, (int64_t)H_v * V))
     return GDN_ERR_BAD_SHAPE;
   if (!seg_offsets) return GDN_ERR_NULL_POINTER;
   if (seg_offsets_host && !offsets_ok(seg_offsets_host, P, T, T, false)) return GDN_ERR_BAD_SEQLENS;
-  if (!k || !v || !g || !beta || !M || !b || !seg_initial_states || !workspace) return GDN_ERR_NULL_POINTER;
-  if (workspace_bytes < tbuf_bytes(T, P, H_v)) return GDN_ERR_BAD_SHAPE;
+  if (!k || !v || !g || !beta || !M || !b || !seg_initial_states) return GDN_ERR_NULL_POINTER;
+  if (mfma && !workspace) return GDN_ERR_NULL_POINTER;
+  if (mfma && workspace_bytes < tbuf_bytes(T, P, H_v)) return GDN_ERR_BAD_SHAPE;
   gdn::ChunkArgs a{};
   a.tbuf = static_cast<float*>(workspace);
   a.q = nullptr;
@@ -494,7 +537,7 @@ gdn_status gdn_segment_state_scan(const void* k, const void* v, gdn_dtype in_dt,
   a.in_dt = in_dt;
   a.s0_mode = 0;
   a.o_dt = GDN_F32;
-  hipError_t e = gdn::launch_segment_pass1(a, M, b, stream);
+  hipError_t e = mfma ? gdn::launch_segment_pass1(a, M, b, stream) : segment_pass1_f32(a, M, b, stream);
   if (e != hipSuccess) return GDN_ERR_HIP;
   e = gdn::launch_compose(M, b, initial_state, P, H_v, K, V, seg_initial_states, 1, final_state, stream);
   return hip_status(e);
@@ -546,9 +589,10 @@ gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
   // every check before anything is enqueued
   if (!valid_dtype(in_dt) || !valid_dtype(o_dt)) return GDN_ERR_BAD_DTYPE;
-  if (in_dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
   if (P < 1 || T < 0 || H_qk < 1 || H_v < 1 || H_v % H_qk != 0) return GDN_ERR_BAD_SHAPE;
-  if (K != 128 || V < 1 || V % 128 != 0) return GDN_ERR_UNSUPPORTED;
+  const gdn_status sup = segment_supported(in_dt, K, V);
+  if (sup != GDN_OK) return sup;
+  const bool mfma = mfma_path(in_dt, K, V);
   if (P > kMaxGrid || H_v > kMaxGrid) return GDN_ERR_UNSUPPORTED;
   if (!stride_ok(&q_token_stride, (int64_t)H_qk * K) || !stride_ok(&k_token_stride, (int64_t)H_qk * K) ||
       !stride_ok(&v_token_stride, (int64_t)H_v * V))
@@ -600,13 +644,14 @@ gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
   a.sf_seq_stride = (int64_t)H_v * K * V;
   a.sf_head_stride = (int64_t)K * V;
   a.sf_row_stride = V;
-  // the maps go to the device with the prep launch
-  hipError_t e = gdn::launch_chunk_prep(a, T > 0 ? 1 : 0, stream, maps.data(), (int64_t)maps.size(), ints);
+  // the maps go to the device with the prep launch (or a store of their own)
+  hipError_t e = mfma ? gdn::launch_chunk_prep(a, T > 0 ? 1 : 0, stream, maps.data(), (int64_t)maps.size(), ints)
+                      : gdn::launch_plan_store(maps.data(), (int64_t)maps.size(), ints, stream);
   if (e != hipSuccess) return GDN_ERR_HIP;
   if (P > 1) {
     gdn::ChunkArgs p1 = a;
     p1.n_seqs = P - 1;  // segments 0 .. P-2: the same chunk slots as in the P-segment records
-    e = gdn::launch_segment_pass1(p1, M, bmap, stream, false);
+    e = mfma ? gdn::launch_segment_pass1(p1, M, bmap, stream, false) : segment_pass1_f32(p1, M, bmap, stream);
     if (e != hipSuccess) return GDN_ERR_HIP;
     e = gdn::launch_compose(M, bmap, initial_state, P - 1, H_v, K, V, starts, 0, nullptr, stream);
     if (e != hipSuccess) return GDN_ERR_HIP;
@@ -619,7 +664,7 @@ gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
     p2.q = nullptr;  // no tokens: the state-only scan copies initial_state to final_state
     p2.o = nullptr;
   }
-  return hip_status(gdn::launch_chunk_bf16(p2, stream, false));
+  return hip_status(mfma ? gdn::launch_chunk_bf16(p2, stream, false) : gdn::launch_chunk_f32(p2, stream));
 }
 
 

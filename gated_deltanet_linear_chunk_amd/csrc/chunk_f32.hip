@@ -116,12 +116,23 @@ __global__ void __launch_bounds__(F32_THREADS) chunk_f32_kernel(ChunkArgs a) {
   const TI* k = (const TI*)a.k;
   const TI* v = (const TI*)a.v;
 
-  // initial state
+  // initial state: a row of s0 or of s0_seg (picked by s0_ref when set),
+  // the identity (augmented M columns), or zero
+  const float* s0p = nullptr;
+  if (a.s0_ref) {
+    const int r = a.s0_ref[seq];
+    if (r >= 0)
+      s0p = a.s0_seg + ((int64_t)r * a.Hv + h) * K * a.V;
+    else if (r <= -2 && a.s0)
+      s0p = a.s0 + ((int64_t)(-2 - r) * a.Hv + h) * K * a.V;
+  } else if (a.s0_mode == 1) {
+    s0p = a.s0 + ((int64_t)seq * a.Hv + h) * K * a.V;
+  }
   for (int i = tid0; i < K * BV; i += F32_THREADS) {
     const int d = i / BV, c = i % BV;
     float s = 0.f;
-    if (a.s0_mode == 1)
-      s = a.s0[((int64_t)seq * a.Hv + h) * K * a.V + (int64_t)d * a.V + v0 + c];
+    if (s0p)
+      s = s0p[(int64_t)d * a.V + v0 + c];
     else if (a.s0_mode == 2)
       s = (d == v0 + c) ? 1.f : 0.f;
     sS[d][c] = s;
@@ -374,8 +385,9 @@ __global__ void __launch_bounds__(F32_THREADS) chunk_f32_kernel(ChunkArgs a) {
     }
   }
   __syncthreads();
-  if (a.sf) {
-    float* dst = a.sf + (int64_t)seq * a.sf_seq_stride + (int64_t)h * a.sf_head_stride;
+  const int out_row = a.sf_map ? a.sf_map[seq] : seq;  // -1: no final state for this sequence
+  if (a.sf && out_row >= 0) {
+    float* dst = a.sf + (int64_t)out_row * a.sf_seq_stride + (int64_t)h * a.sf_head_stride;
     for (int i = tid0; i < K * BV; i += F32_THREADS) {
       const int d = i / BV, c = i % BV;
       dst[(int64_t)d * a.sf_row_stride + v0 + c] = sS[d][c];

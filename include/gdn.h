@@ -253,7 +253,11 @@ gdn_status gdn_conv_chunk_fwd(const void* x, const void* w, const void* bias, gd
  * reached from a zero start), by running the chunked rule on the augmented
  * state [M | b] started at [I | 0].  The maps are then composed in fp32,
  * S_start,0 = initial_state (zero when NULL), S_start,i+1 = M_i S_start,i + b_i.
- *  k [T, H_qk, K], v [T, H_v, V] in in_dt (BF16, K = 128, V % 128 == 0),
+ *  k [T, H_qk, K], v [T, H_v, V] in in_dt with K = 128 and V % 32 == 0
+ *  (GDN_ERR_UNSUPPORTED otherwise): bf16 with V % 128 == 0 runs the MFMA
+ *  kernels, fp32 inputs and other V the fp32 vector-ALU kernel (pass 1 as
+ *  two runs of the rule, M's columns from the identity with zero values and
+ *  b's from zero); the composition is fp32 MFMA for both;
  *  token strides as in gdn_chunk_fwd (0 = dense);
  *  g, beta fp32 [T, H_v]; seg_offsets device int32 [P + 1] (host mirror
  *  seg_offsets_host optional, validated when given);
@@ -265,7 +269,8 @@ gdn_status gdn_conv_chunk_fwd(const void* x, const void* w, const void* bias, gd
  * seg_offsets[P] = T) and initial_state = seg_initial_states is pass 2: it
  * yields every output of the unsegmented run.
  * workspace: at least gdn_segment_state_scan_workspace_bytes(...) bytes
- * (the per-chunk UT-transform matrices of pass 1).
+ * (the per-chunk UT-transform matrices of pass 1) on the MFMA shapes; not
+ * used, and NULL allowed, on the vector-ALU shapes.
  */
 size_t gdn_segment_state_scan_workspace_bytes(int64_t T, int32_t P, int32_t H_v, int32_t K,
                                               int32_t V);
@@ -284,10 +289,12 @@ gdn_status gdn_segment_state_scan(const void* k, const void* v, gdn_dtype in_dt,
  * (pass 1 + fp32 composition) followed by gdn_chunk_fwd over the segments
  * started from the composed states (pass 2).  Same q/k/v/g/beta/o layouts as
  * gdn_chunk_fwd with B = 1; seg_offsets as above with seg_offsets[0] = 0 and
- * seg_offsets[P] = T.  final_state fp32 [H_v, K, V] or NULL.
+ * seg_offsets[P] = T.  final_state fp32 [H_v, K, V] or NULL.  Shapes and
+ * kernels as gdn_segment_state_scan.
  * workspace: device memory of at least gdn_segmented_workspace_bytes(...)
- * bytes, used for M, b, the composed starts and the per-chunk matrices;
- * its contents on entry do not matter.
+ * bytes, used for M, b, the composed starts, the start and final-state maps
+ * and (MFMA shapes) the per-chunk matrices; its contents on entry do not
+ * matter.
  */
 size_t gdn_segmented_workspace_bytes(int64_t T, int32_t P, int32_t H_v, int32_t K, int32_t V);
 

@@ -223,7 +223,13 @@ def test_gate_and_segment_validation(lib):
     assert scan(M=None) == NULLP
     assert scan(ws=None) == NULLP
     assert scan(ws_bytes=lib.gdn_segment_state_scan_workspace_bytes(4096, 8, 32, 128, 128) - 4) == SHAPE
-    assert scan(dt=0) == UNSUP
+    # K = 128 only; bf16 with V % 128 == 0 on the MFMA kernels, otherwise fp32 or
+    # V % 32 == 0 on the vector-ALU kernel (which needs no workspace)
+    assert scan(dt=0, K=64) == UNSUP
+    assert scan(dt=1, K=32, V=32) == UNSUP
+    assert scan(dt=0, V=200) == UNSUP
+    assert scan(dt=0, M=None, ws=None) == NULLP  # fp32 accepted; the outputs are still required
+    assert scan(V=96, starts=None, ws=None) == NULLP  # bf16 with V = 96 accepted
     assert scan(P=0) == SHAPE
     assert scan(V=200) == UNSUP
     off = (ctypes.c_int32 * 3)(0, 5000, 4096)
@@ -255,7 +261,9 @@ def test_gate_and_segment_validation(lib):
     assert seg(o=None) == NULLP
     assert seg(q=None) == NULLP
     assert seg(o_dt=4) == DTYPE
-    assert seg(dt=0) == UNSUP
+    assert seg(dt=0, K=64) == UNSUP
+    assert seg(dt=0, q=None) == NULLP  # fp32 accepted
+    assert seg(V=96, o=None) == NULLP  # bf16 with V = 96 accepted
     assert seg(K=64) == UNSUP
     assert seg(Hqk=3) == SHAPE
     assert seg(P=0) == SHAPE

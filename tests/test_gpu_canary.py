@@ -193,11 +193,13 @@ def test_conv_chunk_writes_nothing_outside(dtype):
     assert bool(torch.isfinite(vals).all())
 
 
-def test_segment_scan_and_segmented_forward_write_nothing_outside():
+@pytest.mark.parametrize("dtype,V", [("bf16", 128), ("f32", 96)])  # MFMA and vector-ALU shapes
+def test_segment_scan_and_segmented_forward_write_nothing_outside(dtype, V):
     lib = gdn.load_library()
-    Hqk, Hv, K, V = 2, 4, 128, 128
+    Hqk, Hv, K = 2, 4, 128
     T = 600
-    d, t = _inputs([T], Hqk, Hv, K, V, s0=True)
+    in_dt = gdn.BF16 if dtype == "bf16" else gdn.F32
+    d, t = _inputs([T], Hqk, Hv, K, V, dtype=dtype, s0=True)
     off = np.array([0, 64, 64, 333, 600], dtype=np.int32)  # an empty and a ragged segment
     P = len(off) - 1
     off_dev = dev(off, "i32")
@@ -207,7 +209,7 @@ def test_segment_scan_and_segmented_forward_write_nothing_outside():
     fin = Guarded(Hv * K * V * 4)
     ws_bytes = lib.gdn_segment_state_scan_workspace_bytes(T, P, Hv, K, V)
     ws = Guarded(ws_bytes)
-    st = lib.gdn_segment_state_scan(t["k"].data_ptr(), t["v"].data_ptr(), gdn.BF16, 0, 0, t["g"].data_ptr(),
+    st = lib.gdn_segment_state_scan(t["k"].data_ptr(), t["v"].data_ptr(), in_dt, 0, 0, t["g"].data_ptr(),
                                     t["beta"].data_ptr(), off_dev.data_ptr(), _host_cu(off), P,
                                     t["s0"].data_ptr(), T, Hqk, Hv, K, V, M.ptr, b.ptr, starts.ptr, fin.ptr,
                                     ws.ptr, ws_bytes, _stream())
@@ -218,7 +220,7 @@ def test_segment_scan_and_segmented_forward_write_nothing_outside():
     fin2 = Guarded(Hv * K * V * 4)
     ws_bytes = lib.gdn_segmented_workspace_bytes(T, P, Hv, K, V)
     ws2 = Guarded(ws_bytes)
-    st = lib.gdn_chunk_fwd_segmented(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), gdn.BF16, 0, 0, 0,
+    st = lib.gdn_chunk_fwd_segmented(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), in_dt, 0, 0, 0,
                                      t["g"].data_ptr(), t["beta"].data_ptr(), 0.1, t["s0"].data_ptr(),
                                      off_dev.data_ptr(), _host_cu(off), P, T, Hqk, Hv, K, V, o.ptr, gdn.F32,
                                      fin2.ptr, ws2.ptr, ws_bytes, _stream())

@@ -344,6 +344,55 @@ def test_segmented_forward_matches_oracle(gates):
     assert torch.equal(o1, o2)
 
 
+@pytest.mark.parametrize("dtype,V,gates", [("f32", 128, "slow"), ("f32", 32, "zero_decay"), ("bf16", 96, "slow"),
+                                            ("f32", 64, "fast")])
+def test_segment_state_scan_vector_alu(dtype, V, gates):
+    """K = 128 segment scans outside the MFMA shapes (fp32 inputs, or bf16 with V % 128 != 0): pass 1
+    on the vector-ALU kernel, M, b, the chained starts and the final state against the oracle."""
+    T = 512
+    d = gdn_inputs.small(43, [T], 2, 4, 128, V, dtype, **GATES[gates])
+    off = np.array([0, 64, 100, 256, 257, 512], dtype=np.int32)
+    s0 = (np.random.default_rng(8).standard_normal((4, 128, V)) * 0.1).astype(np.float32)
+    g, beta = _gpu_gates(d)
+    M, b, starts, fin = gdn.gdn_segment_state_scan(dev(d["k"], dtype), dev(d["v"], dtype), g, beta,
+                                                   dev(off, "i32"), off, initial_state=dev(s0))
+    torch.cuda.synchronize()
+    go, bo = _oracle_gates(d)
+    Mref, bref = oracle.segment_affine(d["k"], d["v"], go, bo, off, Hqk=2)
+    sref, fref = oracle.chain(Mref, bref, s0)
+    check = assert_f32 if dtype == "f32" else assert_bf16
+    for i in range(len(off) - 1):
+        check(host(M[i]), Mref[i], "M[%d]" % i)
+        check(host(b[i]), bref[i], "b[%d]" % i)
+        check(host(starts[i]), sref[i], "start[%d]" % i)
+    check(host(fin), fref, "final")
+
+
+@pytest.mark.parametrize("dtype,V", [("f32", 128), ("bf16", 32), ("f32", 96)])
+def test_segmented_forward_vector_alu(dtype, V):
+    """The segmented forward on the vector-ALU kernel (pass 1, fp32 chain, pass 2 from the chained
+    starts through the start/final-state maps) against the oracle; one segment equals the plain call."""
+    T = 640
+    d = gdn_inputs.small(44, [T], 2, 4, 128, V, dtype, **GATES["slow"])
+    off = np.array([0, 128, 320, 321, 640], dtype=np.int32)
+    s0 = (np.random.default_rng(9).standard_normal((1, 4, 128, V)) * 0.05).astype(np.float32)
+    g, beta = _gpu_gates(d)
+    q, k, v = dev(d["q"], dtype)[None], dev(d["k"], dtype)[None], dev(d["v"], dtype)[None]
+    o, fin = gdn.gdn_chunk_fwd_segmented(q, k, v, g[None], beta[None], dev(off, "i32"), off,
+                                         initial_state=dev(s0[0]), o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    oref, fref = _oracle_chunk(d, s0)
+    check = assert_f32 if dtype == "f32" else assert_bf16
+    check(host(o[0]), oref, "o")
+    check(host(fin), fref[0], "final")
+    one = np.array([0, T], dtype=np.int32)
+    o1, f1 = gdn.gdn_chunk_fwd_segmented(q, k, v, g[None], beta[None], dev(one, "i32"), one,
+                                         initial_state=dev(s0[0]), o_dtype=torch.float32)
+    o2, f2 = gdn.gdn_chunk_fwd(q, k, v, g[None], beta[None], initial_state=dev(s0), o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2[0])
+
+
 # --------------------------------------------------------------------------- #
 # Recurrent decode step (one new token per sequence, state updated in place)
 # --------------------------------------------------------------------------- #
