@@ -23,9 +23,13 @@
  * Conventions for every entry point:
  *  - Tensor arguments are DEVICE pointers to caller-owned, contiguous,
  *    row-major memory, 16-byte aligned.  The library allocates nothing and
- *    never frees or retains caller memory.  Its only global state is the
- *    fixed device array of gdn_chunk_fwd_noalloc (present on every device the
- *    library's code is loaded on) and that array's per-device address.
+ *    never frees or retains caller memory.  Its global state: the fixed
+ *    device array of gdn_chunk_fwd_noalloc (present on every device the
+ *    library's code is loaded on) and that array's per-device address; on the
+ *    host, a cache of the last eight split plans (keyed by the offsets and
+ *    sizes, behind a mutex) and a per-device flag that the scan kernels' LDS
+ *    limit is raised.  Calls from several host threads are safe (calls of
+ *    gdn_chunk_fwd_noalloc that overlap on one device race on its array).
  *  - Host pointers are named *_host and are read before the call returns.
  *  - Work is enqueued on `stream` (0 = the null stream) and the call returns
  *    without waiting for it.  Results are valid once the stream reaches them.
