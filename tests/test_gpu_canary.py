@@ -193,14 +193,18 @@ def test_conv_chunk_writes_nothing_outside(dtype):
     assert bool(torch.isfinite(vals).all())
 
 
-@pytest.mark.parametrize("dtype,V", [("bf16", 128), ("f32", 96)])  # MFMA and vector-ALU shapes
-def test_segment_scan_and_segmented_forward_write_nothing_outside(dtype, V):
+@pytest.mark.parametrize("dtype,V,many", [("bf16", 128, False), ("f32", 96, False), ("bf16", 128, True)])
+def test_segment_scan_and_segmented_forward_write_nothing_outside(dtype, V, many):
+    """MFMA and vector-ALU shapes, and a chain of 39 maps."""
     lib = gdn.load_library()
     Hqk, Hv, K = 2, 4, 128
     T = 600
     in_dt = gdn.BF16 if dtype == "bf16" else gdn.F32
     d, t = _inputs([T], Hqk, Hv, K, V, dtype=dtype, s0=True)
     off = np.array([0, 64, 64, 333, 600], dtype=np.int32)  # an empty and a ragged segment
+    if many:
+        off = np.concatenate([[0], np.arange(1, 40) * 15, [600]]).astype(np.int32)
+        off[20] = off[19]
     P = len(off) - 1
     off_dev = dev(off, "i32")
     M = Guarded(P * Hv * K * K * 4)

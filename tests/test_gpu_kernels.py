@@ -393,6 +393,53 @@ def test_segmented_forward_vector_alu(dtype, V):
     assert torch.equal(o1, o2) and torch.equal(f1, f2[0])
 
 
+def _many_offsets(T, P, seed):
+    """P chunk-unaligned segments of T tokens, a few of them empty."""
+    rng = np.random.default_rng(seed)
+    cuts = np.sort(rng.integers(0, T + 1, P - 1))
+    off = np.concatenate([[0], cuts, [T]]).astype(np.int32)
+    off[P // 2] = off[P // 2 - 1]  # at least one empty segment
+    return np.maximum.accumulate(off).astype(np.int32)
+
+
+@pytest.mark.parametrize("dtype,V,P", [("bf16", 128, 17), ("bf16", 128, 18), ("bf16", 128, 64), ("f32", 64, 40)])
+def test_segment_state_scan_long_chains(dtype, V, P):
+    """Long serial chains of maps (up to 64, with empty and ragged segments): every start and the
+    final state against the oracle's chain."""
+    T = 1536
+    d = gdn_inputs.small(45 + P, [T], 2, 4, 128, V, dtype, **GATES["slow"])
+    off = _many_offsets(T, P, P)
+    s0 = (np.random.default_rng(10).standard_normal((4, 128, V)) * 0.1).astype(np.float32)
+    g, beta = _gpu_gates(d)
+    M, b, starts, fin = gdn.gdn_segment_state_scan(dev(d["k"], dtype), dev(d["v"], dtype), g, beta,
+                                                   dev(off, "i32"), off, initial_state=dev(s0))
+    torch.cuda.synchronize()
+    go, bo = _oracle_gates(d)
+    Mref, bref = oracle.segment_affine(d["k"], d["v"], go, bo, off, Hqk=2)
+    sref, fref = oracle.chain(Mref, bref, s0)
+    check = assert_f32 if dtype == "f32" else assert_bf16
+    for i in range(P):
+        check(host(starts[i]), sref[i], "start[%d]" % i)
+    check(host(fin), fref, "final")
+
+
+@pytest.mark.parametrize("dtype,V,P", [("bf16", 128, 40), ("f32", 32, 33)])
+def test_segmented_forward_long_chains(dtype, V, P):
+    T = 1600
+    d = gdn_inputs.small(46 + P, [T], 2, 4, 128, V, dtype, **GATES["slow"])
+    off = _many_offsets(T, P, 100 + P)
+    s0 = (np.random.default_rng(11).standard_normal((1, 4, 128, V)) * 0.05).astype(np.float32)
+    g, beta = _gpu_gates(d)
+    o, fin = gdn.gdn_chunk_fwd_segmented(dev(d["q"], dtype)[None], dev(d["k"], dtype)[None], dev(d["v"], dtype)[None],
+                                         g[None], beta[None], dev(off, "i32"), off, initial_state=dev(s0[0]),
+                                         o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    oref, fref = _oracle_chunk(d, s0)
+    check = assert_f32 if dtype == "f32" else assert_bf16
+    check(host(o[0]), oref, "o")
+    check(host(fin), fref[0], "final")
+
+
 # --------------------------------------------------------------------------- #
 # Recurrent decode step (one new token per sequence, state updated in place)
 # --------------------------------------------------------------------------- #
