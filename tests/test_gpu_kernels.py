@@ -655,3 +655,50 @@ def test_chunk_gated_norm_fused_gqa_three_batched():
     s = assert_bf16(host(y).reshape(384, 6, 128), ref, "y")
     assert_bf16(host(fin), fref, "final")
     print("\nfused norm gqa 3 batched: %s" % (s,))
+
+
+def test_chunk_calls_from_two_host_threads():
+    """Split packed calls from two host threads on two streams at once (the planner's cache and the
+    LDS-limit flag are the library's shared host state) give what the same calls give one at a time,
+    bit for bit."""
+    import threading
+
+    Hqk, Hv, K, V = 2, 4, 128, 128
+    sets = []
+    for seed, lengths in ((61, [2000, 64, 130, 7]), (62, [50, 1900, 300])):
+        d = gdn_inputs.small(seed, lengths, Hqk, Hv, K, V, "bf16", s0_std=0.05)
+        g, beta = _gpu_gates(d)
+        sets.append(dict(q=dev(d["q"], "bf16")[None], k=dev(d["k"], "bf16")[None], v=dev(d["v"], "bf16")[None],
+                         g=g[None], beta=beta[None], s0=dev(d["s0"]), cu=dev(d["cu_seqlens"], "i32"),
+                         cu_host=d["cu_seqlens"]))
+    torch.cuda.synchronize()
+
+    def call(t):
+        return gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], initial_state=t["s0"],
+                                 cu_seqlens=t["cu"], cu_seqlens_host=t["cu_host"], o_dtype=torch.float32)
+
+    ref = [call(t) for t in sets]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    results = [[None] * 8, [None] * 8]
+    errors = []
+
+    def worker(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                for r in range(8):
+                    results[i][r] = call(sets[i])
+            streams[i].synchronize()
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        for o, fin in results[i]:
+            assert torch.equal(o, ref[i][0]) and torch.equal(fin, ref[i][1])
