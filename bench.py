@@ -260,12 +260,18 @@ def build_pipeline(w, d, o_dtype, rotate=4):
         g, beta = gdn.gdn_gate_fwd(a, b, A_log, dt_bias)
         return chunk(q, k, v, g, beta)
 
+    def step_on(x):
+        q, k, v = qkv(conv(x))
+        g, beta = gdn.gdn_gate_fwd(a, b, A_log, dt_bias)
+        return chunk(q, k, v, g, beta)
+
     def chunk_inputs():
         q, k, v = qkv(conv())
         g, beta = gdn.gdn_gate_fwd(a, b, A_log, dt_bias)
         return q, k, v, g, beta
 
-    return {"step": step, "conv": conv, "chunk": chunk, "chunk_inputs": chunk_inputs, "C": C}
+    step_fns = [lambda x=x: step_on(x) for x in xs]
+    return {"step": step, "step_fns": step_fns, "conv": conv, "chunk": chunk, "chunk_inputs": chunk_inputs, "C": C}
 
 
 def build_conv_chunk(w, d):
@@ -381,6 +387,39 @@ def timed_steps(step, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
+def graph_steps(fns, steps, warmup):
+    """Seconds per step over `steps` replays of HIP graphs of the step, one graph per step function
+    (one per input copy, replayed in turn), after `warmup` untimed replays.  Each function runs
+    eagerly first (the library's one-time set-up and the planner's cache), then is captured."""
+    torch = _torch()
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for f in fns:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            f()
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    del graphs
+    return sec
+
+
 def cpu_baseline(w, d):
     """The fp64 oracle on the same packed workload, on this host's cores."""
     import oracle
@@ -413,13 +452,15 @@ def pipeline_lines(name, w, d, o_dtype, o_bytes, reps, flush, peak, steps, warmu
     T, N = w.total_tokens, (w.batch_rows if w.batch_rows > 1 else w.n_samples)
     s0 = "s0" in d
     sec = timed_steps(p["step"], steps, warmup)
+    sec_graph = graph_steps(p["step_fns"], steps, warmup)
     q, k, v, g, beta = p["chunk_inputs"]()
     packed = w.batch_rows == 1
     kernels = (SPLIT_KERNELS % (0 if o_bytes == 4 else 1)) if packed else \
         "chunk_prep_kernel + chunk_scan_kernel<%d,8>" % (0 if o_bytes == 4 else 1)
     st = summary(time_call(lambda: p["chunk"](q, k, v, g, beta), reps, flush))
     lines = {
-        "step": {"tokens_per_s": T / sec, "ms_per_step": sec * 1e3, "steps": steps, "warmup": warmup},
+        "step": {"tokens_per_s": T / sec, "ms_per_step": sec * 1e3, "steps": steps, "warmup": warmup,
+                 "graph_tokens_per_s": T / sec_graph, "graph_ms_per_step": sec_graph * 1e3},
         "chunk": roofline(chunk_alg_bytes(T, N, w.Hqk, w.Hv, w.K, w.V, o_bytes, s0=s0),
                           chunk_alg_flops(T, w.Hqk, w.Hv, w.K, w.V),
                           st, "gdn_chunk_fwd (%s) = %s" % ("segment-split path" if packed else "batched rows", kernels),
@@ -497,6 +538,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": step["ms_per_step"],
+        "ms_per_step_graph_replay": step["graph_ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -504,7 +546,8 @@ def main():
         "data": "synthetic (seeded; packed lengths by a flat Dirichlet draw)",
         "config": {"workload": MAIN, "global_batch": N, "seq_len": T, "parallelism": "none (1 GPU)",
                    "H_qk": w.Hqk, "H_v": w.Hv, "K": w.K, "V": w.V, "chunk": 64, "conv_width": 4,
-                   "o_dtype": args.o_dtype, "step": "gates + conv1d/SiLU/L2 + chunked rule"},
+                   "o_dtype": args.o_dtype, "step": "gates + conv1d/SiLU/L2 + chunked rule",
+                   "launch": "eager (HIP graph replay of the same step also reported)"},
         "mfma_frac_chunk": chunk["mfma_frac_published_peak"],
         "mfma_peak_measured_tflops": peak,
         "roofline": chunk,
