@@ -441,8 +441,8 @@ def cpu_baseline(w, d):
     }
 
 
-SPLIT_KERNELS = ("plan_store_kernel + chunk_prep_kernel + chunk_scan_kernel<2,8> + compose_kernel + "
-                 "chunk_scan_kernel<%d,8>")
+SPLIT_KERNELS = ("chunk_prep_kernel (stores the plan) + chunk_scan_kernel<{0},8,mixed> (pass 1) + compose_kernel + "
+                 "chunk_scan_kernel<{0},8> (pass 2)")
 
 
 def pipeline_lines(name, w, d, o_dtype, o_bytes, reps, flush, peak, steps, warmup, main=False):
@@ -455,7 +455,7 @@ def pipeline_lines(name, w, d, o_dtype, o_bytes, reps, flush, peak, steps, warmu
     sec_graph = graph_steps(p["step_fns"], steps, warmup)
     q, k, v, g, beta = p["chunk_inputs"]()
     packed = w.batch_rows == 1
-    kernels = (SPLIT_KERNELS % (0 if o_bytes == 4 else 1)) if packed else \
+    kernels = SPLIT_KERNELS.format(0 if o_bytes == 4 else 1) if packed else \
         "chunk_prep_kernel + chunk_scan_kernel<%d,8>" % (0 if o_bytes == 4 else 1)
     st = summary(time_call(lambda: p["chunk"](q, k, v, g, beta), reps, flush))
     lines = {

@@ -300,17 +300,24 @@ static gdn_status chunk_fwd_run(const void* q, const void* k, const void* v, gdn
   a.cu = ints;
   a.n_seqs = plan.n_seg;
   a.rec_seq = ints + plan.off_sample();
+  // pass 1: the first segment of every split sample forward, its end state to
+  // the start row of the sample's second segment; the middle segments' maps
   gdn::ChunkArgs p1 = a;
   p1.seq_order = ints + plan.off_pre();
   p1.n_blocks_z = plan.n_prefix;
-  e = gdn::launch_segment_pass1(p1, M, bmap, stream, false);
+  p1.s0_ref = ints + plan.off_s0ref();
+  p1.s0_seg = starts;
+  p1.sf = starts;
+  p1.sf_map = ints + plan.off_s0ref() + 1;  // segment i ends where segment i + 1 starts
+  e = gdn::launch_split_pass1(p1, plan.n_fwd, M, bmap, stream);
   if (e != hipSuccess) return GDN_ERR_HIP;
-  e = gdn::launch_compose_chains(M, bmap, initial_state, ints + plan.off_chains(), plan.n_chain, H_v, K, V,
-                                 starts, 0, nullptr, stream);
+  // chains from each second segment's start through the maps
+  e = gdn::launch_compose_chains(M, bmap, starts, ints + plan.off_chains(), plan.n_chain, H_v, K, V, starts, 0,
+                                 nullptr, stream);
   if (e != hipSuccess) return GDN_ERR_HIP;
   gdn::ChunkArgs p2 = a;
   p2.seq_order = ints + plan.off_order();
-  p2.n_blocks_z = plan.n_seg;
+  p2.n_blocks_z = plan.n_seg - plan.n_fwd;
   p2.s0_ref = ints + plan.off_s0ref();
   p2.s0_seg = starts;
   p2.sf_map = ints + plan.off_sfmap();

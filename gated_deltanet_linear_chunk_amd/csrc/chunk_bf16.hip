@@ -33,6 +33,7 @@
 //   sT2 [2][64][64] (T diag(beta) hi/lo); sVt [128][72] (V^T of this slice,
 //   rows padded by 16 B), sO fp32 [64][132], gamma[64], dec[64] fp32.
 #include <atomic>
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -77,6 +78,15 @@ enum { kOutF32 = 0, kOutBF16 = 1, kPass1 = 2 };
 struct Pass1 {
   int m_tiles;   // leading tiles of a (segment, head) that evolve M columns (v = 0, S0 = I)
   float* m_out;  // [n_seqs, Hv, K, K]
+  // Mixed launches (forward kernels with kMixed): the first n_fwd segments of
+  // the launch run forward (V / 128 blocks per head), the rest form maps
+  // (m_tiles + V / 128 blocks per head), M into m_out and b into b_out
+  // [n_seqs - n_fwd, Hv, K, V].  The grid holds the forward blocks, then the
+  // map blocks, with no idle ones: blocks are dealt to the shader engines in
+  // turn, and idle blocks at fixed positions of that order would leave the
+  // real ones of some engines more than their compute units.
+  int n_fwd;
+  float* b_out;
 };
 
 // Workgroups go to the eight XCDs in turn by id, each XCD with its own L2.
@@ -150,7 +160,7 @@ __device__ __forceinline__ void store8_frag(uint16_t* tile, int row, int c, cons
   *reinterpret_cast<u32x2*>(rb + tile_pos<W16>(row, c + 4)) = u32x2{v[2], v[3]};
 }
 
-template <int kMode, int NW, bool kNorm>
+template <int kMode, int NW, bool kNorm, bool kMixed>
 __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 p1) {
   constexpr int NT = NW * 64;
   constexpr int CPW = BV / NW;     // state columns per wave
@@ -161,6 +171,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   constexpr int NREC = (RUNITS + NT - 1) / NT;                 // record units per thread
   static_assert(CPW % 16 == 0 && NW * CPW == BV, "wave layout");
   static_assert(!kNorm || kOut, "the norm applies to outputs");
+  static_assert(!kMixed || kOut, "mixed launches run forward kernels");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + OFF_Q);
@@ -180,16 +191,37 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   const int c16 = lane & 15;
 
   bool m_mode = false;
-  const int n_tiles = a.n_tiles;
-  const int lb = xcd_grouped((int)blockIdx.x, (int)gridDim.x, n_tiles * (a.Hv / a.Hqk));
+  int n_tiles = a.n_tiles, zb0 = 0, L = (int)blockIdx.x, n_blocks = (int)gridDim.x;
+  if (kMixed) {
+    const int nf = p1.n_fwd * a.Hv * (a.V / BV);  // forward blocks first
+    if (L < nf) {
+      n_tiles = a.V / BV;
+      n_blocks = nf;
+    } else {
+      L -= nf;
+      n_blocks -= nf;
+      zb0 = p1.n_fwd;
+    }
+  }
+  const int lb = xcd_grouped(L, n_blocks, n_tiles * (a.Hv / a.Hqk));
   int tile = lb % n_tiles;
+  const int h = (lb / n_tiles) % a.Hv;
+  const int zb = zb0 + lb / (n_tiles * a.Hv);
+  // state only: a map block of a mixed launch (from the identity for M
+  // columns, zero for b columns), which skips q and O like pass 1
+  bool so = false;
   if (kMode == kPass1) {
     m_mode = tile < p1.m_tiles;
     if (!m_mode) tile -= p1.m_tiles;
   }
+  if (kMixed && zb >= p1.n_fwd) {
+    so = true;
+    m_mode = tile < p1.m_tiles;
+    if (!m_mode) tile -= p1.m_tiles;
+  }
+  // q, O and its stores: forward kernels, except on the map blocks of a mixed launch
+  const bool outb = kOut && !so;
   const int v0 = tile * BV;
-  const int h = (lb / n_tiles) % a.Hv;
-  const int zb = lb / (n_tiles * a.Hv);
   const int seq = a.seq_order ? a.seq_order[zb] : zb;
   const int hq = h / (a.Hv / a.Hqk);
   int64_t bos, eos;
@@ -203,7 +235,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   const bool load_v = !m_mode;
   // start state of this head: identity (M columns), zero, or K x V rows of V
   const float* s0p = nullptr;
-  if (!m_mode) {
+  if (!m_mode && !so) {
     if (a.s0_ref) {
       const int r = a.s0_ref[seq];
       if (r >= 0)
@@ -230,8 +262,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   // last valid token; the host keeps strides below 2^24 elements, so the
   // row * stride product is one 24-bit multiply.
   const char* kbase = (const char*)((const uint16_t*)a.k + bos * a.k_stride + hq * KD);
-  const char* qbase = kOut ? (const char*)((const uint16_t*)a.q + bos * a.q_stride + hq * KD) : kbase;
-  const int64_t q_stride = kOut ? a.q_stride : a.k_stride;
+  const char* qbase = outb ? (const char*)((const uint16_t*)a.q + bos * a.q_stride + hq * KD) : kbase;
+  const int64_t q_stride = outb ? a.q_stride : a.k_stride;
   // without values (M columns) the v loads re-read k and are discarded
   const char* vbase = load_v ? (const char*)((const uint16_t*)a.v + bos * a.v_stride + (int64_t)h * a.V + v0) : kbase;
   const int64_t v_stride = load_v ? a.v_stride : a.k_stride;
@@ -389,7 +421,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   for (int64_t t0 = bos; t0 < eos; t0 += CH) {
     const int L = (int)((eos - t0) < CH ? (eos - t0) : CH);
     __syncthreads();  // every wave is done with the previous chunk's tiles
-    if (kOut && t0 > bos && (kNorm || wave < NW / 2)) flush_o(t0 - CH, CH);  // a full chunk: only the last can be short
+    if (outb && t0 > bos && (kNorm || wave < NW / 2)) flush_o(t0 - CH, CH);  // a full chunk: only the last can be short
 
     // ---- stash q, k, v and the prep record ---------------------------------
     // Rows past the end of a partial chunk (and v of M columns) are zeroed in
@@ -417,7 +449,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
       const u32x4 v0v = pv[j][0], v1v = pv[j][1];
       store8_frag<true>(sK, r0, d8, k0);
       store8_frag<true>(sK, r0 + 1, d8, k1);
-      if (kOut) {
+      if (outb) {
         store8_frag<true>(sQ, r0, d8, pq[j][0]);
         store8_frag<true>(sQ, r0 + 1, d8, pq[j][1]);
       }
@@ -429,10 +461,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
             __builtin_amdgcn_perm(k1[jx], k0[jx], sel_a);
         *reinterpret_cast<uint32_t*>(sKt + db * TP + tile_pos<false>(db, r0)) =
             __builtin_amdgcn_perm(k1[jx], k0[jx], sel_b);
-        if (load_v) {
-          *reinterpret_cast<uint32_t*>(sVt + d0 * VTP + r0) = (v0v[jx] & 0xFFFFu) | (v1v[jx] << 16);
-          *reinterpret_cast<uint32_t*>(sVt + d1 * VTP + r0) = (v0v[jx] >> 16) | (v1v[jx] & 0xFFFF0000u);
-        }
+        // (zeros for M columns: their values were cleared above)
+        *reinterpret_cast<uint32_t*>(sVt + d0 * VTP + r0) = (v0v[jx] & 0xFFFFu) | (v1v[jx] << 16);
+        *reinterpret_cast<uint32_t*>(sVt + d1 * VTP + r0) = (v0v[jx] >> 16) | (v1v[jx] & 0xFFFF0000u);
       }
     }
     {
@@ -478,28 +509,35 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
         zero4(KS[ct][rt]);
         zero4(O[ct][rt]);
       }
+    auto state_products = [&](auto with_q) {
+      constexpr bool WQ = decltype(with_q)::value;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      bf16x8 sp[2][NCT];
+      for (int m = 0; m < 4; ++m) {
+        bf16x8 sp[2][NCT];
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) split_frag(S[ct][2 * m], S[ct][2 * m + 1], sp[0][ct], sp[1][ct]);
-      bf16x8 fk[4], fq[4];
+        for (int ct = 0; ct < NCT; ++ct) split_frag(S[ct][2 * m], S[ct][2 * m + 1], sp[0][ct], sp[1][ct]);
+        bf16x8 fk[4], fq[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        fk[rt] = frag16<true>(sK, 16 * rt + c16, 32 * m, g4);
-        if (kOut) fq[rt] = frag16<true>(sQ, 16 * rt + c16, 32 * m, g4);
+        for (int rt = 0; rt < 4; ++rt) {
+          fk[rt] = frag16<true>(sK, 16 * rt + c16, 32 * m, g4);
+          if (WQ) fq[rt] = frag16<true>(sQ, 16 * rt + c16, 32 * m, g4);
+        }
+#pragma unroll
+        for (int part = 0; part < 2; ++part)
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+              KS[ct][rt] = mfma16(fk[rt], sp[part][ct], KS[ct][rt]);
+              if (WQ) O[ct][rt] = mfma16(fq[rt], sp[part][ct], O[ct][rt]);
+            }
+        SCHED_FENCE();
       }
-#pragma unroll
-      for (int part = 0; part < 2; ++part)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) {
-            KS[ct][rt] = mfma16(fk[rt], sp[part][ct], KS[ct][rt]);
-            if (kOut) O[ct][rt] = mfma16(fq[rt], sp[part][ct], O[ct][rt]);
-          }
-      SCHED_FENCE();
-    }
+    };
+    if (outb)
+      state_products(std::integral_constant<bool, kOut>{});
+    else
+      state_products(std::false_type{});
 
     if (more_) GDN_PF_KQ(t0 + CH);
     // ---- U = T diag(beta) (V - e^G K S) ------------------------------------------
@@ -519,14 +557,12 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
           R[rt][1] = -gam.y * KS[ct][rt][1];
           R[rt][2] = -gam.z * KS[ct][rt][2];
           R[rt][3] = -gam.w * KS[ct][rt][3];
-          if (load_v) {
-            const u32x2 vv =
-                *reinterpret_cast<const u32x2*>(sVt + (wave * CPW + 16 * ct + c16) * VTP + 16 * rt + 4 * g4);
-            R[rt][0] += __uint_as_float(vv[0] << 16);
-            R[rt][1] += __uint_as_float(vv[0] & 0xFFFF0000u);
-            R[rt][2] += __uint_as_float(vv[1] << 16);
-            R[rt][3] += __uint_as_float(vv[1] & 0xFFFF0000u);
-          }
+          const u32x2 vv =
+              *reinterpret_cast<const u32x2*>(sVt + (wave * CPW + 16 * ct + c16) * VTP + 16 * rt + 4 * g4);
+          R[rt][0] += __uint_as_float(vv[0] << 16);
+          R[rt][1] += __uint_as_float(vv[0] & 0xFFFF0000u);
+          R[rt][2] += __uint_as_float(vv[1] << 16);
+          R[rt][3] += __uint_as_float(vv[1] & 0xFFFF0000u);
         }
 #pragma unroll
         for (int m = 0; m < 2; ++m) split_frag(R[2 * m], R[2 * m + 1], rh[ct][m], rl[ct][m]);
@@ -555,7 +591,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
       }
     }
     if (more_) GDN_PF_V(t0 + CH);
-    if (kOut) {
+    if (outb) {
       // ---- O = diag(gamma) Q S + P U  -> fp32 O tile in LDS -------------------
       bf16x8 Uhi[NCT][2], Ulo[NCT][2];
 #pragma unroll
@@ -637,7 +673,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
           SCHED_FENCE();
         }
     }
-    if (kOut) {
+    if (outb) {
       // O into this wave's own columns of the fp32 O tile; the first half of
       // the waves stores the whole tile after the next chunk's first barrier.
 #pragma unroll
@@ -649,7 +685,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
             sO[(16 * rt + 4 * g4 + e) * OP + wave * CPW + 16 * ct + c16] = O[ct][rt][e];
     }
   }
-  if (kOut && bos < eos) {  // the last chunk's O
+  if (outb && bos < eos) {  // the last chunk's O
     const int64_t t_last = bos + CH * ((eos - bos - 1) / CH);
     __syncthreads();
     if (kNorm || wave < NW / 2) flush_o(t_last, (int)(eos - t_last));
@@ -666,8 +702,11 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
   int64_t row_stride = 0;
   const int out_row = a.sf_map ? a.sf_map[seq] : zb;
   if (m_mode) {
-    dst = p1.m_out + ((int64_t)zb * a.Hv + h) * (int64_t)KD * KD;
+    dst = p1.m_out + ((int64_t)(zb - (kMixed ? p1.n_fwd : 0)) * a.Hv + h) * (int64_t)KD * KD;
     row_stride = KD;
+  } else if (kMixed && so) {
+    dst = p1.b_out + ((int64_t)(zb - p1.n_fwd) * a.Hv + h) * (int64_t)KD * a.V;
+    row_stride = a.V;
   } else if (a.sf && out_row >= 0) {
     dst = a.sf + (int64_t)out_row * a.sf_seq_stride + (int64_t)h * a.sf_head_stride;
     row_stride = a.sf_row_stride;
@@ -685,8 +724,10 @@ __global__ void __launch_bounds__(NW * 64) chunk_scan_kernel(ChunkArgs a, Pass1 
 
 constexpr int kScanWaves = 8;  // the prefetch code assumes 512 threads
 
-template <int kMode, bool kNorm = false>
-hipError_t launch_scan(const ChunkArgs& a, Pass1 p1, dim3 grid, hipStream_t stream) {
+// n workgroups over blocks of n_tiles column tiles (the tile count of
+// the map blocks in a mixed launch)
+template <int kMode, bool kNorm = false, bool kMixed = false>
+hipError_t launch_scan(const ChunkArgs& a, Pass1 p1, int n_tiles, int64_t n, hipStream_t stream) {
   // the LDS limit is raised once per device (a host call on every launch otherwise)
   static std::atomic<uint64_t> attr_set{0};
   int dev = 0;
@@ -694,18 +735,17 @@ hipError_t launch_scan(const ChunkArgs& a, Pass1 p1, dim3 grid, hipStream_t stre
   if (e != hipSuccess) return e;
   const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
   if (!bit || !(attr_set.load(std::memory_order_acquire) & bit)) {
-    const void* fn = (const void*)chunk_scan_kernel<kMode, kScanWaves, kNorm>;
+    const void* fn = (const void*)chunk_scan_kernel<kMode, kScanWaves, kNorm, kMixed>;
     e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit, std::memory_order_acq_rel);
   }
   // 1-D launch over (tile, v-head, sequence); the kernel decodes it
   ChunkArgs c = a;
-  c.n_tiles = (int)grid.x;
-  const int64_t n = (int64_t)grid.x * grid.y * grid.z;
+  c.n_tiles = n_tiles;
   if (n > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((chunk_scan_kernel<kMode, kScanWaves, kNorm>), dim3((unsigned)n), dim3(kScanWaves * 64), LDS_BYTES,
-                     stream, c, p1);
+  hipLaunchKernelGGL((chunk_scan_kernel<kMode, kScanWaves, kNorm, kMixed>), dim3((unsigned)n), dim3(kScanWaves * 64),
+                     LDS_BYTES, stream, c, p1);
   return hipGetLastError();
 }
 
@@ -721,19 +761,21 @@ hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t stream, bool prep) 
   }
   const int nz = a.seq_order ? a.n_blocks_z : a.n_seqs;
   if (nz == 0) return hipSuccess;
-  const dim3 grid(a.V / BV, a.Hv, nz);
+  const int tiles = a.V / BV;
+  const int64_t n = (int64_t)tiles * a.Hv * nz;
+  const Pass1 none{0, nullptr, 0, nullptr};
   if (!with_o) {
     // state only: run the scan without outputs
-    return launch_scan<kPass1>(a, Pass1{0, nullptr}, grid, stream);
+    return launch_scan<kPass1>(a, none, tiles, n, stream);
   }
   if (a.z) {
     // the gated norm needs a whole row of V values in one workgroup
     if (a.V != BV) return hipErrorInvalidValue;
-    return a.o_dt == 1 ? launch_scan<kOutBF16, true>(a, Pass1{0, nullptr}, grid, stream)
-                       : launch_scan<kOutF32, true>(a, Pass1{0, nullptr}, grid, stream);
+    return a.o_dt == 1 ? launch_scan<kOutBF16, true>(a, none, tiles, n, stream)
+                       : launch_scan<kOutF32, true>(a, none, tiles, n, stream);
   }
-  return a.o_dt == 1 ? launch_scan<kOutBF16>(a, Pass1{0, nullptr}, grid, stream)
-                     : launch_scan<kOutF32>(a, Pass1{0, nullptr}, grid, stream);
+  return a.o_dt == 1 ? launch_scan<kOutBF16>(a, none, tiles, n, stream)
+                     : launch_scan<kOutF32>(a, none, tiles, n, stream);
 }
 
 hipError_t launch_segment_pass1(const ChunkArgs& a, float* M, float* b, hipStream_t stream, bool prep) {
@@ -755,7 +797,24 @@ hipError_t launch_segment_pass1(const ChunkArgs& a, float* M, float* b, hipStrea
   c.sf_map = nullptr;
   const int nz = a.seq_order ? a.n_blocks_z : a.n_seqs;
   if (nz == 0) return hipSuccess;
-  return launch_scan<kPass1>(c, Pass1{KD / BV, M}, dim3(KD / BV + a.V / BV, a.Hv, nz), stream);
+  const int tiles = KD / BV + a.V / BV;
+  return launch_scan<kPass1>(c, Pass1{KD / BV, M, 0, nullptr}, tiles, (int64_t)tiles * a.Hv * nz, stream);
+}
+
+hipError_t launch_split_pass1(const ChunkArgs& a, int n_fwd, float* M, float* b, hipStream_t stream) {
+  if (a.n_seqs == 0 || a.Hv == 0 || a.n_blocks_z == 0) return hipSuccess;
+  if (a.K != KD || a.V % BV != 0 || a.tbuf == nullptr || a.seq_order == nullptr) return hipErrorInvalidValue;
+  if (a.o == nullptr || a.q == nullptr || n_fwd < 0 || n_fwd > a.n_blocks_z) return hipErrorInvalidValue;
+  const Pass1 p1{KD / BV, M, n_fwd, b};
+  const int tiles = KD / BV + a.V / BV;  // of a map block
+  const int64_t n = (int64_t)n_fwd * a.Hv * (a.V / BV) + (int64_t)(a.n_blocks_z - n_fwd) * a.Hv * tiles;
+  if (a.z) {
+    if (a.V != BV) return hipErrorInvalidValue;
+    return a.o_dt == 1 ? launch_scan<kOutBF16, true, true>(a, p1, tiles, n, stream)
+                       : launch_scan<kOutF32, true, true>(a, p1, tiles, n, stream);
+  }
+  return a.o_dt == 1 ? launch_scan<kOutBF16, false, true>(a, p1, tiles, n, stream)
+                     : launch_scan<kOutF32, false, true>(a, p1, tiles, n, stream);
 }
 
 }  // namespace gdn

@@ -35,13 +35,13 @@ struct Chain {
   int n, p0, count, out0;
 };
 
+// s0 and out may be one buffer (a chain that starts from a row another launch
+// wrote, and writes later rows of it): neither is restrict-qualified.
 __global__ void __launch_bounds__(CTHREADS) compose_kernel(const float* __restrict__ M,
-                                                           const float* __restrict__ b,
-                                                           const float* __restrict__ s0,
+                                                           const float* __restrict__ b, const float* s0,
                                                            const int32_t* __restrict__ chains,
-                                                           Chain single, int Hv, int V,
-                                                           float* __restrict__ out, int write_before,
-                                                           float* __restrict__ final_state) {
+                                                           Chain single, int Hv, int V, float* out,
+                                                           int write_before, float* __restrict__ final_state) {
   __shared__ float sS[2][SROWS];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;

@@ -90,6 +90,12 @@ hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t stream, bool prep =
 // row z of M and b for block z.
 hipError_t launch_segment_pass1(const ChunkArgs& a, float* M, float* b, hipStream_t stream,
                                 bool prep = true);
+// Pass 1 of a split packed run, one launch over the a.n_blocks_z segments of
+// a.seq_order (records already in a.tbuf): the first n_fwd run forward with
+// outputs (start states by a.s0_ref, end states to rows a.sf_map of a.sf),
+// the others form their maps as launch_segment_pass1 does, into row
+// z - n_fwd of M and b.
+hipError_t launch_split_pass1(const ChunkArgs& a, int n_fwd, float* M, float* b, hipStream_t stream);
 // fp32 chains of affine maps.  chains[4 c .. 4 c + 3] = {n, p0, count, out0}:
 // chain c starts from row n of s0 (zero when s0 is null or n < 0) and applies
 // maps p0 .. p0 + count - 1 of (M, b) in order; with write_before, out row

@@ -2,15 +2,19 @@
 //
 // The chunk scan is serial along a sequence, so a packed batch whose samples
 // differ a lot in length is bounded by its longest sample.  When the offsets
-// are known on the host, long samples are cut into chunk-aligned segments:
-// pass 1 runs the state-only scan of every segment but the last of each
-// sample on the augmented state [M | b] (the segment's affine map), an fp32
-// chain turns the maps into the true start state of every later segment, and
-// pass 2 runs all segments of all samples at once from those starts (the same
-// segment-wise state passing as the segmented entry point, applied per sample).
-// The cut length is chosen with a small list-scheduling model of the two
-// passes on the device's compute units; nothing is split unless the model
-// expects the run to be at least 15% shorter.
+// are known on the host, long samples are cut into chunk-aligned segments
+// s_0 .. s_{n-1}.  Pass 1 runs s_0 forward from the sample's start state (its
+// outputs, and its end state, which is the true start of s_1) and, beside it,
+// the state-only scan of s_1 .. s_{n-2} on the augmented state [M | b] (each
+// segment's affine map); an fp32 chain from s_1's start through those maps
+// gives the true start of s_2 .. s_{n-1}; pass 2 runs every segment but the
+// s_0 of split samples (the unsplit samples whole) from those starts.  This is
+// the segment-wise state passing of the segmented entry point applied per
+// sample, with the first segment of each chain run in pass 1, where the map
+// blocks leave compute units free.  The cut length is chosen with a small
+// list-scheduling model of the two passes on the device's compute units;
+// nothing is split unless the model expects the run to be at least 15%
+// shorter.
 #include "split_plan.h"
 
 #include <algorithm>
@@ -75,8 +79,9 @@ std::vector<CachedPlan> g_cache;  // most recent last
 
 }  // namespace
 
-// Upper bound on pass-1 segments: their blocks (K/128 + V/128 per head) fit
-// twice on the compute units.
+// Upper bound on pass-1 segments: their blocks (K/128 + V/128 per head, the
+// launch size of a forward and a map segment alike) fit twice on the
+// compute units.
 int max_prefix_segments(int32_t H_v, int32_t V, int cus) {
   const int tiles1 = 1 + V / 128;
   return std::max(0, 2 * cus / std::max(1, H_v * tiles1));
@@ -125,17 +130,17 @@ static bool plan_split_uncached(const int32_t* cu, int32_t N, int32_t H_v, int32
     chunks[n] = ((int64_t)cu[n + 1] - cu[n] + 63) / 64;
     cmax = std::max(cmax, chunks[n]);
   }
-  // pass 2 (or the unsplit scan): longest first
-  auto pass2 = [&](std::vector<int64_t> lens) {
+  // a forward pass over segments of these lengths, longest first
+  auto forward = [&](std::vector<int64_t> lens) {
     std::sort(lens.begin(), lens.end(), std::greater<int64_t>());
     std::vector<Group> groups;
     for (int64_t c : lens) groups.push_back(Group{(double)c, (int64_t)H_v * tiles2});
     return makespan(groups, cus);
   };
-  const double base = pass2(chunks);
-  // Every chunk runs in pass 2, and no schedule beats the work spread evenly
-  // over the units: a run already within 15% of that is not split (and the
-  // search below, costly for thousands of samples, is skipped).
+  const double base = forward(chunks);
+  // Every chunk runs forward once, and no schedule beats that work spread
+  // evenly over the units: a run already within 15% of it is not split (and
+  // the search below, costly for thousands of samples, is skipped).
   double work = 0.0;
   for (int64_t c : chunks) work += (double)c * H_v * tiles2;
   if (0.85 * base < work / cus) return false;
@@ -144,19 +149,28 @@ static bool plan_split_uncached(const int32_t* cu, int32_t N, int32_t H_v, int32
   for (int parts = 2; parts <= 16; ++parts) {
     const int64_t seg = (cmax + parts - 1) / parts;  // chunks per segment
     if (seg < 4) break;
-    std::vector<int64_t> lens;
-    int64_t n_prefix = 0, longest_chain = 0;
+    std::vector<int64_t> lens2, fwd1;
+    int64_t n_maps = 0, longest_chain = 0;
     for (int32_t n = 0; n < N; ++n) {
       const int64_t s = chunks[n] > seg ? (chunks[n] + seg - 1) / seg : 1;
-      n_prefix += s - 1;
-      longest_chain = std::max(longest_chain, s - 1);
-      for (int64_t j = 0; j < s; ++j) lens.push_back(std::min(seg, chunks[n] - j * seg));
+      if (s == 1) {
+        lens2.push_back(chunks[n]);
+        continue;
+      }
+      fwd1.push_back(seg);
+      n_maps += s - 2;
+      longest_chain = std::max(longest_chain, s - 2);
+      for (int64_t j = 1; j < s; ++j) lens2.push_back(std::min(seg, chunks[n] - j * seg));
     }
-    if (n_prefix == 0 || n_prefix > pmax) continue;
-    // a pass-1 chunk skips q, the output and P: about 0.7 of a pass-2 chunk;
-    // a chain step costs about one chunk
-    const std::vector<Group> p1{Group{0.7 * (double)seg, n_prefix * H_v * tiles1}};
-    const double t = makespan(p1, cus) + (double)longest_chain + pass2(lens);
+    const int64_t n_pass1 = (int64_t)fwd1.size() + n_maps;
+    if (n_pass1 == 0 || n_pass1 > pmax) continue;
+    // pass 1: the forward segments first, then the maps; a map chunk skips
+    // q, the output and P: about 0.7 of a forward chunk; a chain step costs
+    // about one chunk
+    std::vector<Group> p1;
+    for (int64_t c : fwd1) p1.push_back(Group{(double)c, (int64_t)H_v * tiles2});
+    p1.push_back(Group{0.7 * (double)seg, n_maps * H_v * tiles1});
+    const double t = makespan(p1, cus) + (double)longest_chain + forward(lens2);
     if (t < best) {
       best = t;
       best_seg = seg;
@@ -179,35 +193,41 @@ static bool plan_split_uncached(const int32_t* cu, int32_t N, int32_t H_v, int32
   }
   out.n_seg = (int)segs.size();
   out.n_prefix = 0;
+  out.n_fwd = 0;
   out.n_chain = 0;
   for (const Seg& g : segs) {
-    if (g.j + 1 < g.s) ++out.n_prefix;
-    if (g.j == 0 && g.s > 1) ++out.n_chain;
+    if (g.s > 1 && g.j + 1 < g.s) ++out.n_prefix;
+    if (g.s > 1 && g.j == 0) ++out.n_fwd;
+    if (g.s > 2 && g.j == 0) ++out.n_chain;
   }
   out.ints.assign((size_t)out.off_sample() + out.n_seg, 0);
   int32_t* I = out.ints.data();
   for (int i = 0; i < out.n_seg; ++i) I[i] = segs[i].begin;
   I[out.n_seg] = segs.back().end;
+  // pass 2 longest first, then the segments pass 1 runs forward
+  auto in_pass1 = [&](int32_t x) { return segs[x].s > 1 && segs[x].j == 0; };
   std::vector<int32_t> order(out.n_seg);
   for (int i = 0; i < out.n_seg; ++i) order[i] = i;
   std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+    if (in_pass1(x) != in_pass1(y)) return in_pass1(y);
     return segs[x].end - segs[x].begin > segs[y].end - segs[y].begin;
   });
   std::copy(order.begin(), order.end(), I + out.off_order());
-  int pre = 0, later = 0, chain = 0;
+  int fwd = 0, map = 0, later = 0, chain = 0;
   for (int i = 0; i < out.n_seg; ++i) {
     const Seg& g = segs[i];
-    if (g.j == 0 && g.s > 1) {  // the chain of this sample: maps of its pass-1 segments
+    if (g.j == 0 && g.s > 2) {  // the chain of this sample: from s_1's start through its maps
       int32_t* c = I + out.off_chains() + 4 * chain++;
-      c[0] = has_s0 ? g.n : -1;
-      c[1] = pre;
-      c[2] = g.s - 1;
-      c[3] = later;
+      c[0] = later;
+      c[1] = map;
+      c[2] = g.s - 2;
+      c[3] = later + 1;
     }
     I[out.off_s0ref() + i] = g.j == 0 ? (has_s0 ? -2 - g.n : -1) : later++;
     I[out.off_sfmap() + i] = g.j + 1 == g.s ? g.n : -1;
     I[out.off_sample() + i] = g.n;
-    if (g.j + 1 < g.s) I[out.off_pre() + pre++] = i;
+    if (g.s > 1 && g.j == 0) I[out.off_pre() + fwd++] = i;
+    if (g.j > 0 && g.j + 1 < g.s) I[out.off_pre() + out.n_fwd + map++] = i;
   }
   return true;
 }

@@ -1,6 +1,6 @@
 // Host driver for the split planner: reads "H_v V has_s0 cus n len_0 .. len_{n-1}"
 // on stdin and prints the plan as whitespace-separated integers:
-// "split n_seg n_prefix n_chain" then the index arrays.
+// "split n_seg n_prefix n_chain n_fwd" then the index arrays.
 #include <cstdio>
 #include <vector>
 
@@ -17,7 +17,7 @@ int main() {
   }
   gdn::SplitPlan p;
   const bool split = gdn::plan_split(cu.data(), n, Hv, V, has_s0 != 0, cus, p);
-  std::printf("%d %d %d %d\n", split ? 1 : 0, p.n_seg, p.n_prefix, p.n_chain);
+  std::printf("%d %d %d %d %d\n", split ? 1 : 0, p.n_seg, p.n_prefix, p.n_chain, p.n_fwd);
   for (int32_t x : p.ints) std::printf("%d ", x);
   std::printf("\n%d\n", gdn::max_prefix_segments(Hv, V, cus));
   return 0;

@@ -2,9 +2,12 @@
 
 The planner is compiled with g++ together with a small driver (split_plan_main.cpp) and run on
 sample lengths shaped like the workloads; every plan is checked for what pass 1, the fp32 chains
-and pass 2 rely on: the segments tile every sample in order and are chunk-aligned from its start,
-each later segment gets exactly one composed start state from the chain of its sample, every
-sample's final state comes from its last segment, and the pass-1 list is the non-last segments.
+and pass 2 rely on: the segments tile every sample in order and are chunk-aligned from its start;
+pass 1 runs the first segment of every split sample forward (from the sample's start state, its
+end state going to the start row of the second segment) and forms the maps of the segments
+between the first and the last; each segment after the second gets its start from its sample's
+chain, which begins at the second segment's start row and runs through the maps in order; pass 2
+runs every other segment; every sample's final state comes from its last segment.
 """
 import os
 import shutil
@@ -28,9 +31,9 @@ def planner(tmp_path_factory):
     def run(lengths, Hv, V, has_s0=True, cus=256):
         inp = "%d %d %d %d %d %s" % (Hv, V, int(has_s0), cus, len(lengths), " ".join(map(str, lengths)))
         out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True).stdout.split("\n")
-        split, n_seg, n_prefix, n_chain = map(int, out[0].split())
+        split, n_seg, n_prefix, n_chain, n_fwd = map(int, out[0].split())
         ints = np.array(out[1].split(), dtype=np.int64)
-        return dict(split=bool(split), n_seg=n_seg, n_prefix=n_prefix, n_chain=n_chain, ints=ints,
+        return dict(split=bool(split), n_seg=n_seg, n_prefix=n_prefix, n_chain=n_chain, n_fwd=n_fwd, ints=ints,
                     pmax=int(out[2]))
     return run
 
@@ -62,7 +65,9 @@ def check_plan(p, lengths, has_s0):
             owners.setdefault(n, []).append(i)
     assert sorted(order.tolist()) == list(range(n_seg))
     seg_len = np.diff(seg_cu)
-    assert np.all(np.diff(seg_len[order]) <= 0)  # longest first
+    n_fwd = p["n_fwd"]
+    pass2, fwd1 = order[: n_seg - n_fwd], order[n_seg - n_fwd:]
+    assert np.all(np.diff(seg_len[pass2]) <= 0)  # longest first
     # an empty segment is the one segment of a zero-length sample (its final-state row)
     for i in range(n_seg):
         if seg_cu[i + 1] == seg_cu[i]:
@@ -70,6 +75,7 @@ def check_plan(p, lengths, has_s0):
     # final states: one per sample, from its last segment
     assert sorted(x for x in sf_map.tolist() if x >= 0) == list(range(len(lengths)))
     later = []
+    split = {n: segs for n, segs in owners.items() if len(segs) > 1}
     for n, segs in owners.items():
         assert segs == list(range(segs[0], segs[-1] + 1))
         assert sf_map[segs[-1]] == n and all(sf_map[i] == -1 for i in segs[:-1])
@@ -78,17 +84,26 @@ def check_plan(p, lengths, has_s0):
         for i in segs[:-1]:
             assert seg_len[i] % 64 == 0
     assert sorted(later) == list(range(n_prefix))
-    assert sorted(pre.tolist()) == pre.tolist() and len(pre) == n_prefix
+    # pass 1: the first segment of every split sample forward, then the middle segments' maps
+    assert n_fwd == len(split) and len(pre) == n_prefix
+    assert sorted(fwd1.tolist()) == sorted(segs[0] for segs in split.values())
+    assert pre[:n_fwd].tolist() == sorted(segs[0] for segs in split.values())
+    maps = pre[n_fwd:].tolist()
+    assert maps == sorted(i for segs in split.values() for i in segs[1:-1])
     assert all(sf_map[i] == -1 for i in pre)
-    # chains: sample n's maps are consecutive pass-1 rows, outputs are its later segments' starts
-    assert len(chains) == sum(1 for segs in owners.values() if len(segs) > 1)
-    for n0, p0, count, out0 in chains:
-        n = int(sample[pre[p0]])
-        assert n0 == (n if has_s0 else -1)
-        segs = owners[n]
-        assert count == len(segs) - 1
-        assert pre[p0: p0 + count].tolist() == segs[:-1]
-        assert [int(s0_ref[i]) for i in segs[1:]] == list(range(out0, out0 + count))
+    # a forward pass-1 segment ends where the next segment's start row is read (s0_ref of i + 1)
+    for i in pre[:n_fwd]:
+        assert seg_sample[i + 1] == seg_sample[i] and s0_ref[i + 1] >= 0
+    # chains: from the second segment's start row through the sample's maps, in order, to the
+    # start rows of its later segments
+    assert len(chains) == sum(1 for segs in split.values() if len(segs) > 2)
+    for start, p0, count, out0 in chains:
+        n = int(sample[maps[p0]])
+        segs = split[n]
+        assert count == len(segs) - 2
+        assert start == s0_ref[segs[1]]
+        assert maps[p0: p0 + count] == segs[1:-1]
+        assert [int(s0_ref[i]) for i in segs[2:]] == list(range(out0, out0 + count))
     assert n_prefix <= p["pmax"]
 
 
