@@ -569,7 +569,7 @@ SegmentedLayout segmented_layout(int64_t T, int32_t P, int32_t H_v, int32_t K, i
   l.b = l.M + align256(pre * K * sizeof(float));
   l.starts = l.b + align256(pre * V * sizeof(float));
   l.ints = l.starts + align256(pre * V * sizeof(float));
-  l.total = l.ints + align256(2 * (size_t)P * sizeof(int32_t));
+  l.total = l.ints + align256((3 * (size_t)P + 3) * sizeof(int32_t));
   return l;
 }
 
@@ -582,9 +582,13 @@ size_t gdn_segmented_workspace_bytes(int64_t T, int32_t P, int32_t H_v, int32_t 
   return segmented_layout(T, P, H_v, K, V).total;
 }
 
-// Prep once for all P segments (the records with P serve both passes), pass 1
-// over segments 0 .. P-2 only, one fp32 chain of their maps, then pass 2 over
-// all P segments from the chained starts; pass 2 writes the final state.
+// Prep once for all P segments (the records with P serve both passes).  On
+// the MFMA kernels pass 1 runs segment 0 forward (its end state is the start
+// of segment 1) beside the maps of segments 1 .. P-2, one fp32 chain carries
+// segment 1's start through those maps, and pass 2 runs segments 1 .. P-1
+// from the chained starts; on the vector-ALU kernel pass 1 forms the maps of
+// segments 0 .. P-2, the chain starts from initial_state, and pass 2 runs all
+// P segments.  Pass 2 writes the final state.
 gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
                                    gdn_dtype in_dt, int64_t q_token_stride,
                                    int64_t k_token_stride, int64_t v_token_stride,
@@ -616,13 +620,21 @@ gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
   float* bmap = reinterpret_cast<float*>(w + l.b);
   float* starts = reinterpret_cast<float*>(w + l.starts);
   int32_t* ints = reinterpret_cast<int32_t*>(w + l.ints);
-  // s0_ref: segment 0 starts from row 0 of initial_state (zero when NULL),
-  // segment i > 0 from chained start i - 1; sf_map: the last segment's state
-  // is the final state
+  // s0_ref [P]: segment 0 starts from row 0 of initial_state (zero when
+  // NULL), segment i > 0 from start row i - 1; sf_map [P]: the last segment's
+  // state is the final state; then the MFMA path's chain (from start row 0
+  // through maps 0 .. P-3 to start rows 1 .. P-2) and its pass-2 order
+  // (segments 1 .. P-1)
+  const bool mixed = mfma && P > 1 && T > 0;
   std::vector<int32_t> maps(2 * (size_t)P, -1);
   maps[0] = -2;
   for (int32_t i = 1; i < P; ++i) maps[i] = i - 1;
   maps[(size_t)P + P - 1] = 0;
+  if (mixed) {
+    const int32_t chain[4] = {0, 0, P - 2, 1};
+    maps.insert(maps.end(), chain, chain + 4);
+    for (int32_t i = 1; i < P; ++i) maps.push_back(i);
+  }
   gdn::ChunkArgs a{};
   a.tbuf = reinterpret_cast<float*>(w + l.rec);
   a.q = q;
@@ -655,7 +667,19 @@ gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
   hipError_t e = mfma ? gdn::launch_chunk_prep(a, T > 0 ? 1 : 0, stream, maps.data(), (int64_t)maps.size(), ints)
                       : gdn::launch_plan_store(maps.data(), (int64_t)maps.size(), ints, stream);
   if (e != hipSuccess) return GDN_ERR_HIP;
-  if (P > 1) {
+  if (mixed) {
+    gdn::ChunkArgs p1 = a;
+    p1.n_blocks_z = P - 1;  // segment 0 forward, segments 1 .. P-2 maps
+    p1.s0_ref = ints;
+    p1.s0_seg = starts;
+    p1.sf = starts;
+    p1.sf_map = ints + 1;  // segment 0 ends where segment 1 starts
+    e = gdn::launch_split_pass1(p1, 1, M, bmap, stream);
+    if (e != hipSuccess) return GDN_ERR_HIP;
+    e = gdn::launch_compose_chains(M, bmap, starts, ints + 2 * P, P > 2 ? 1 : 0, H_v, K, V, starts, 0, nullptr,
+                                   stream);
+    if (e != hipSuccess) return GDN_ERR_HIP;
+  } else if (P > 1) {
     gdn::ChunkArgs p1 = a;
     p1.n_seqs = P - 1;  // segments 0 .. P-2: the same chunk slots as in the P-segment records
     e = mfma ? gdn::launch_segment_pass1(p1, M, bmap, stream, false) : segment_pass1_f32(p1, M, bmap, stream);
@@ -667,6 +691,10 @@ gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
   p2.s0_ref = ints;
   p2.s0_seg = starts;
   p2.sf_map = ints + P;
+  if (mixed) {
+    p2.seq_order = ints + 2 * P + 4;
+    p2.n_blocks_z = P - 1;
+  }
   if (T == 0) {
     p2.q = nullptr;  // no tokens: the state-only scan copies initial_state to final_state
     p2.o = nullptr;

@@ -803,7 +803,7 @@ hipError_t launch_segment_pass1(const ChunkArgs& a, float* M, float* b, hipStrea
 
 hipError_t launch_split_pass1(const ChunkArgs& a, int n_fwd, float* M, float* b, hipStream_t stream) {
   if (a.n_seqs == 0 || a.Hv == 0 || a.n_blocks_z == 0) return hipSuccess;
-  if (a.K != KD || a.V % BV != 0 || a.tbuf == nullptr || a.seq_order == nullptr) return hipErrorInvalidValue;
+  if (a.K != KD || a.V % BV != 0 || a.tbuf == nullptr) return hipErrorInvalidValue;
   if (a.o == nullptr || a.q == nullptr || n_fwd < 0 || n_fwd > a.n_blocks_z) return hipErrorInvalidValue;
   const Pass1 p1{KD / BV, M, n_fwd, b};
   const int tiles = KD / BV + a.V / BV;  // of a map block

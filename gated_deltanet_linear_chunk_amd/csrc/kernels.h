@@ -90,8 +90,8 @@ hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t stream, bool prep =
 // row z of M and b for block z.
 hipError_t launch_segment_pass1(const ChunkArgs& a, float* M, float* b, hipStream_t stream,
                                 bool prep = true);
-// Pass 1 of a split packed run, one launch over the a.n_blocks_z segments of
-// a.seq_order (records already in a.tbuf): the first n_fwd run forward with
+// Pass 1 of a split run, one launch over a.n_blocks_z segments (those of
+// a.seq_order, or the first ones; records already in a.tbuf): the first n_fwd run forward with
 // outputs (start states by a.s0_ref, end states to rows a.sf_map of a.sf),
 // the others form their maps as launch_segment_pass1 does, into row
 // z - n_fwd of M and b.

@@ -289,9 +289,13 @@ gdn_status gdn_segment_state_scan(const void* k, const void* v, gdn_dtype in_dt,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Segment-parallel forward of one long sequence: gdn_segment_state_scan
- * (pass 1 + fp32 composition) followed by gdn_chunk_fwd over the segments
- * started from the composed states (pass 2).  Same q/k/v/g/beta/o layouts as
+ * Segment-parallel forward of one long sequence: the segments' affine maps
+ * (pass 1), their fp32 composition into start states, then the forward over
+ * the segments from those starts (pass 2).  On the MFMA kernels pass 1 runs
+ * segment 0 forward beside the maps of segments 1 .. P-2 and the chain
+ * starts from segment 0's end state, so P = 2 gives the unsegmented result
+ * bit for bit; on the vector-ALU kernel pass 1 forms the maps of segments
+ * 0 .. P-2 as gdn_segment_state_scan does.  Same q/k/v/g/beta/o layouts as
  * gdn_chunk_fwd with B = 1; seg_offsets as above with seg_offsets[0] = 0 and
  * seg_offsets[P] = T.  final_state fp32 [H_v, K, V] or NULL.  Shapes and
  * kernels as gdn_segment_state_scan.
