@@ -293,9 +293,10 @@ gdn_status gdn_segment_state_scan(const void* k, const void* v, gdn_dtype in_dt,
  * (pass 1), their fp32 composition into start states, then the forward over
  * the segments from those starts (pass 2).  On the MFMA kernels pass 1 runs
  * segment 0 forward beside the maps of segments 1 .. P-2 and the chain
- * starts from segment 0's end state, so P = 2 gives the unsegmented result
- * bit for bit; on the vector-ALU kernel pass 1 forms the maps of segments
- * 0 .. P-2 as gdn_segment_state_scan does.  Same q/k/v/g/beta/o layouts as
+ * starts from segment 0's end state, so P = 2 with the cut at a multiple of
+ * 64 tokens gives the unsegmented result bit for bit; on the vector-ALU
+ * kernel pass 1 forms the maps of segments 0 .. P-2 as
+ * gdn_segment_state_scan does.  Same q/k/v/g/beta/o layouts as
  * gdn_chunk_fwd with B = 1; seg_offsets as above with seg_offsets[0] = 0 and
  * seg_offsets[P] = T.  final_state fp32 [H_v, K, V] or NULL.  Shapes and
  * kernels as gdn_segment_state_scan.

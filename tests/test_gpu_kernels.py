@@ -342,10 +342,18 @@ def test_segmented_forward_matches_oracle(gates):
     o1, _ = gdn.gdn_chunk_fwd_segmented(dev(d["q"], "bf16")[None], dev(d["k"], "bf16")[None],
                                         dev(d["v"], "bf16")[None], g[None], beta[None], dev(one, "i32"), one,
                                         initial_state=dev(s0[0]), o_dtype=torch.float32)
-    o2, _ = gdn.gdn_chunk_fwd(dev(d["q"], "bf16")[None], dev(d["k"], "bf16")[None], dev(d["v"], "bf16")[None],
-                              g[None], beta[None], initial_state=dev(s0), o_dtype=torch.float32)
+    o2, f2 = gdn.gdn_chunk_fwd(dev(d["q"], "bf16")[None], dev(d["k"], "bf16")[None], dev(d["v"], "bf16")[None],
+                               g[None], beta[None], initial_state=dev(s0), o_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+    # two segments cut at a chunk boundary: pass 1 runs segment 0 forward and segment 1 starts from
+    # its end state, with no map and no chain, so the result is the plain path's bit for bit
+    two = np.array([0, 256, T], dtype=np.int32)
+    o3, f3 = gdn.gdn_chunk_fwd_segmented(dev(d["q"], "bf16")[None], dev(d["k"], "bf16")[None],
+                                         dev(d["v"], "bf16")[None], g[None], beta[None], dev(two, "i32"), two,
+                                         initial_state=dev(s0[0]), o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o2) and torch.equal(f3, f2[0])
 
 
 @pytest.mark.parametrize("dtype,V,gates", [("f32", 128, "slow"), ("f32", 32, "zero_decay"), ("bf16", 96, "slow"),
