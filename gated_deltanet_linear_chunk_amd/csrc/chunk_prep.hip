@@ -66,8 +66,11 @@ __device__ __forceinline__ void tile_rc(int b, int& i, int& j) {
 
 // Three waves per SIMD (at most 168 registers; the LDS tiles take 9.5 KB):
 // the kernel is a chain of dependent steps, hidden by running many waves.
+// kP: also P (forward runs); a template parameter so that the loads of the
+// two kinds of run need no merged wait counts.
+template <bool kP>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3)))
-chunk_prep_kernel(ChunkArgs a, int with_p, PlanArg plan, int32_t* __restrict__ plan_dst) {
+chunk_prep_kernel(ChunkArgs a, PlanArg plan, int32_t* __restrict__ plan_dst) {
   // diagonal blocks of A (read by the forward substitution) and of T (written
   // column by column); at the end the same 8 tiles stage T diag(beta)
   __shared__ float sStage[8][16][BP];
@@ -129,40 +132,42 @@ chunk_prep_kernel(ChunkArgs a, int with_p, PlanArg plan, int32_t* __restrict__ p
   if (t0 >= eos) return;  // unused slot
   const int L = (int)((eos - t0) < CH ? (eos - t0) : CH);
 
-  // ---- K and Q fragments straight from global memory, and the gates -----------
-  // row tile i, k-step m: contiguous k = 32 m + 8 g4 .. +7; rows past L read
-  // the last row and are zeroed (every load unconditional)
+  // ---- the gates, then K and Q fragments straight from global memory ----------
+  // The gates go first: loads complete in order, so the gate scan below waits
+  // only for them while the fragments are still on their way.  Row tile i,
+  // k-step m: contiguous k = 32 m + 8 g4 .. +7.  Rows past L re-read the
+  // chunk's last row (every load unconditional) and are left as they are:
+  // their beta is zero, so their rows of A vanish, and no row inside the
+  // chunk reaches them through the lower triangles of A and P, so T and P
+  // rows before L never see them (the rows past L of T and P are never used
+  // for a stored output).
   const int64_t head_off = (int64_t)hq * KD + 8 * g4;
   bf16x8 kf[4][4], qf[4][4];
   float graw, braw;
   {
-    const u32x4 z = {0u, 0u, 0u, 0u};
+    const bool ok = lane < L;
+    const int64_t grow = t0 + (ok ? lane : 0);
+    graw = a.g[grow * a.Hv + h];
+    braw = a.beta[grow * a.Hv + h];
+    if (!ok) graw = braw = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * i + c16;
       const int64_t row = t0 + (r < L ? r : L - 1);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>((const uint16_t*)a.k + row * a.k_stride + head_off + 32 * m);
-        kf[i][m] = __builtin_bit_cast(bf16x8, r < L ? v : z);
-      }
+      for (int m = 0; m < 4; ++m)
+        kf[i][m] = *reinterpret_cast<const bf16x8*>((const uint16_t*)a.k + row * a.k_stride + head_off + 32 * m);
     }
-    if (with_p) {
+    if (kP) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * i + c16;
         const int64_t row = t0 + (r < L ? r : L - 1);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>((const uint16_t*)a.q + row * a.q_stride + head_off + 32 * m);
-          qf[i][m] = __builtin_bit_cast(bf16x8, r < L ? v : z);
-        }
+        for (int m = 0; m < 4; ++m)
+          qf[i][m] = *reinterpret_cast<const bf16x8*>((const uint16_t*)a.q + row * a.q_stride + head_off + 32 * m);
       }
     }
-    const bool ok = lane < L;
-    const int64_t row = t0 + (ok ? lane : 0);
-    graw = ok ? a.g[row * a.Hv + h] : 0.f;
-    braw = ok ? a.beta[row * a.Hv + h] : 0.f;
   }
 
   unsigned char* rec = (unsigned char*)a.tbuf + ((int64_t)slot * a.Hv + h) * PREP_RECORD_BYTES;
@@ -202,7 +207,7 @@ chunk_prep_kernel(ChunkArgs a, int with_p, PlanArg plan, int32_t* __restrict__ p
       f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < 4; ++m) accA = mfma16(kf[j][m], kf[i][m], accA);
-      if (with_p) {
+      if (kP) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) accP = mfma16(kf[j][m], qf[i][m], accP);
       }
@@ -217,7 +222,7 @@ chunk_prep_kernel(ChunkArgs a, int with_p, PlanArg plan, int32_t* __restrict__ p
       const int b = blk(i, j);
       AT[b] = av;
       if (i == j) *reinterpret_cast<f32x4*>(&sAd[i][c16][4 * g4]) = av;
-      if (with_p) {
+      if (kP) {
         uint32_t h0, l0, h1, l1;
         split2(pv[0], pv[1], h0, l0);
         split2(pv[2], pv[3], h1, l1);
@@ -328,7 +333,10 @@ hipError_t launch_chunk_prep(const ChunkArgs& a, int with_p, hipStream_t stream,
   int64_t n = slots * a.Hv;
   if ((a.Hv / a.Hqk) % 2 == 0) n = (n + 15) / 16 * 16;
   if (n > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)n), dim3(64), 0, stream, a, with_p, plan, ints_dst);
+  if (with_p)
+    hipLaunchKernelGGL(chunk_prep_kernel<true>, dim3((unsigned)n), dim3(64), 0, stream, a, plan, ints_dst);
+  else
+    hipLaunchKernelGGL(chunk_prep_kernel<false>, dim3((unsigned)n), dim3(64), 0, stream, a, plan, ints_dst);
   return hipGetLastError();
 }
 
