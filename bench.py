@@ -48,7 +48,6 @@ import gdn_inputs  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
-PEAK_F32_VALU_TFLOPS = 157.3  # MI355X fp32 vector ALU
 METRIC = "GDN fwd tokens/s at H_v=32,K=V=128 bf16; % bf16 MFMA peak"
 MAIN = "packed_varlen_bf16_T8192_N8_Hv32_K128"
 LONG = "long_segmented_bf16_T32768_P8_Hv32_K128"
@@ -621,7 +620,7 @@ def main():
             torch.cuda.empty_cache()
 
         if want("conv_chunk"):
-            # conv1d + SiLU + q/k L2 norm inside the fp32 vector-ALU chunk kernel (activations never stored)
+            # conv1d + SiLU + q/k L2 norm in the chunk prep of the MFMA path (gdn_conv_chunk_fwd)
             fc = build_conv_chunk(w, d)
             sec = timed_steps(fc["step"], max(3, args.steps // 4), 1)
             st = summary(time_call(fc["call"], max(3, reps // 6), flush))
@@ -630,11 +629,14 @@ def main():
             unfused_b = conv_alg_bytes(T, C) + 16 * w.Hv * T + chunk_alg_bytes(T, N, w.Hqk, w.Hv, w.K, w.V, o_bytes,
                                                                                s0="s0" in d)
             flops = chunk_alg_flops(T, w.Hqk, w.Hv, w.K, w.V) + conv_alg_flops(T, C, w.conv_width)
-            lines["%s[conv + chunk fused, vector-ALU kernel]" % MAIN] = dict(
-                st, step_tokens_per_s=T / sec, kernel="chunk_f32_kernel<128, bf16, conv>",
+            kern = ("chunk_prep_conv_kernel (stores the plan and the activations) + chunk_scan_kernel<0,8,mixed> + "
+                    "compose_kernel + chunk_scan_kernel<0,8>")
+            lines["%s[conv + chunk fused, conv in the chunk prep]" % MAIN] = dict(
+                st, step_tokens_per_s=T / sec, kernel=kern,
                 bytes_per_token_fused=fused_b / T, bytes_per_token_unfused=unfused_b / T,
-                achieved_tflops=flops / (st["median_ms"] * 1e-3) / 1e12, peak_tflops=PEAK_F32_VALU_TFLOPS,
-                alu_frac=flops / (st["median_ms"] * 1e-3) / 1e12 / PEAK_F32_VALU_TFLOPS)
+                achieved_gbs=fused_b / (st["median_ms"] * 1e-3) / 1e9,
+                hbm_frac=fused_b / (st["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                mfma_tflops=flops / (st["median_ms"] * 1e-3) / 1e12)
             del fc
             torch.cuda.empty_cache()
             print("conv_chunk line done", file=sys.stderr, flush=True)

@@ -28,6 +28,7 @@ __all__ = [
     "gdn_chunk_fwd_segmented",
     "gdn_segmented_workspace_bytes",
     "gdn_chunk_fwd_workspace_bytes",
+    "gdn_conv_chunk_fwd_workspace_bytes",
     "gdn_segment_state_scan_workspace_bytes",
     "gdn_decode_step",
     "gdn_gated_rmsnorm_fwd",
@@ -51,6 +52,7 @@ EXPORTED_SYMBOLS = (
     "gdn_chunk_fwd",
     "gdn_chunk_fwd_noalloc",
     "gdn_chunk_fwd_gated_norm",
+    "gdn_conv_chunk_fwd_workspace_bytes",
     "gdn_conv_chunk_fwd",
     "gdn_segment_state_scan_workspace_bytes",
     "gdn_segment_state_scan",
@@ -101,8 +103,10 @@ def load_library():
     lib.gdn_chunk_fwd_gated_norm.argtypes = [P, P, P, ctypes.c_int, i64, i64, i64, P, P, f32, P, P, P, i32, i32, i64,
                                              i32, i32, i32, i32, P, ctypes.c_int, P, f32, P, ctypes.c_int, P, P,
                                              sz, P]
+    lib.gdn_conv_chunk_fwd_workspace_bytes.argtypes = [ctypes.c_int, i64, i32, i32, i32, i32, i32]
+    lib.gdn_conv_chunk_fwd_workspace_bytes.restype = sz
     lib.gdn_conv_chunk_fwd.argtypes = [P, P, P, ctypes.c_int, i32, f32, P, P, f32, P, P, P, i32, i32, i64, i32, i32,
-                                       i32, i32, P, ctypes.c_int, P, P]
+                                       i32, i32, P, ctypes.c_int, P, P, sz, P]
     lib.gdn_segment_state_scan_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
     lib.gdn_segment_state_scan_workspace_bytes.restype = sz
     lib.gdn_segment_state_scan.argtypes = [P, P, ctypes.c_int, i64, i64, P, P, P, P, i32, P, i64, i32, i32, i32, i32,
@@ -398,15 +402,24 @@ def gdn_chunk_fwd_gated_norm(q, k, v, g, beta, z, norm_weight=None, eps: float =
     return o, fin
 
 
+def gdn_conv_chunk_fwd_workspace_bytes(in_dtype, total_tokens: int, n_seqs: int, Hqk: int, Hv: int, K: int,
+                                       V: int) -> int:
+    torch = _torch()
+    code = BF16 if in_dtype == torch.bfloat16 else F32
+    return int(load_library().gdn_conv_chunk_fwd_workspace_bytes(code, total_tokens, n_seqs, Hqk, Hv, K, V))
+
+
 def gdn_conv_chunk_fwd(x, w, g, beta, Hqk: int, K: int, bias=None, scale: float = 1.0, initial_state=None,
                        cu_seqlens=None, cu_seqlens_host=None, l2_eps: float = 1e-6, o_dtype=None,
-                       output_final_state: bool = True):
-    """conv1d + SiLU + q/k L2 norm formed inside the chunk kernel, then the chunk rule.
+                       output_final_state: bool = True, workspace=None):
+    """conv1d + SiLU + q/k L2 norm formed inside the chunk kernels, then the chunk rule.
 
     x [B, T, C] raw channels q heads | k heads | v heads, C = 2 Hqk K + Hv V;
     w [C, W] and bias [C] or None in x's dtype; g, beta fp32 [B, T, Hv] (Hv
-    from g).  The activations stay in fp32 inside the kernel.  Other arguments
-    and the results as gdn_chunk_fwd.
+    from g).  bf16 with the MFMA head sizes forms the activations in the chunk
+    prep (bf16, as the separate conv stores them); other shapes keep them in
+    fp32 inside the vector-ALU kernel.  Other arguments and the results as
+    gdn_chunk_fwd.
     """
     torch = _torch()
     dev = x.device
@@ -433,10 +446,12 @@ def gdn_conv_chunk_fwd(x, w, g, beta, Hqk: int, K: int, bias=None, scale: float 
         raise ValueError("initial_state must be [N, Hv, K, V]")
     o = torch.empty((B, T, Hv, V), dtype=x.dtype if o_dtype is None else o_dtype, device=dev)
     fin = torch.empty((N, Hv, K, V), dtype=torch.float32, device=dev) if output_final_state else None
+    total = T if cu_seqlens is not None else B * T
+    ws = _workspace(gdn_conv_chunk_fwd_workspace_bytes(x.dtype, total, N, Hqk, Hv, K, V), dev, workspace)
     st = load_library().gdn_conv_chunk_fwd(
         _ptr(x), _ptr(w), _ptr(bias), _dtype_code(x), w.shape[1], float(l2_eps), _ptr(g), _ptr(beta), float(scale),
         _ptr(initial_state), _ptr(cu_seqlens), _host_offsets(cu_seqlens_host), 0 if cu_seqlens is None else N, B, T,
-        Hqk, Hv, K, V, _ptr(o), _dtype_code(o), _ptr(fin), _stream(dev),
+        Hqk, Hv, K, V, _ptr(o), _dtype_code(o), _ptr(fin), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev),
     )
     _check("gdn_conv_chunk_fwd", st)
     return o, fin

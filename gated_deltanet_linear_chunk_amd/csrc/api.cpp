@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 constexpr int kMaxGrid = 65535;
 
 gdn_status hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
@@ -194,6 +194,18 @@ struct FusedNorm {
   float eps;
 };
 
+// The short convolution in front of the MFMA path (gdn_conv_chunk_fwd): raw
+// channels x, taps, bias, width and eps, and y, the buffer the prep stores the
+// activations to (q, k, v of the run point into it).
+struct ConvIn {
+  const void* x;
+  const void* w;
+  const void* bias;
+  int width;
+  float eps;
+  void* y;
+};
+
 // Source of the records' memory for callers without a workspace: called once
 // the arguments are validated, with the sizes of the bf16 run; sets the
 // workspace, or returns why it cannot.  Runs that use it are never split.
@@ -208,7 +220,7 @@ static gdn_status chunk_fwd_run(const void* q, const void* k, const void* v, gdn
                          int32_t H_qk, int32_t H_v, int32_t K, int32_t V, void* o,
                          gdn_dtype o_dt, float* final_state, void* workspace,
                          size_t workspace_bytes, const FusedNorm* norm, hipStream_t stream,
-                         FixedWorkspace fixed_ws = nullptr) {
+                         FixedWorkspace fixed_ws = nullptr, const ConvIn* conv = nullptr) {
   if (!valid_dtype(in_dt) || !valid_dtype(o_dt)) return GDN_ERR_BAD_DTYPE;
   if (B < 1 || T < 0 || H_qk < 1 || H_v < 1 || K < 1 || V < 1) return GDN_ERR_BAD_SHAPE;
   if (H_v % H_qk != 0) return GDN_ERR_BAD_SHAPE;
@@ -271,6 +283,14 @@ static gdn_status chunk_fwd_run(const void* q, const void* k, const void* v, gdn
     a.eps = norm->eps;
   }
   if (!mfma) return hip_status(gdn::launch_chunk_f32(a, stream));
+  if (conv) {
+    a.cx = conv->x;
+    a.cy = conv->y;
+    a.cw = conv->w;
+    a.cb = conv->bias;
+    a.conv_width = conv->width;
+    a.l2_eps = conv->eps;
+  }
   // A split plan (cached for repeated offsets) comes first, so that the prep
   // launch on the samples also stores its index arrays.
   gdn::SplitPlan plan;
@@ -434,12 +454,27 @@ gdn_status gdn_chunk_fwd_gated_norm(const void* q, const void* k, const void* v,
   return gdn_gated_rmsnorm_fwd(o, o_dt, z, z_dt, norm_weight, eps, total * H_v, V, o, o_dt, stream);
 }
 
+// The MFMA path with the conv in its prep: bf16, the MFMA head sizes, and at
+// most four v-heads per q/k head (one workgroup of the prep holds them all).
+static bool conv_chunk_mfma(gdn_dtype in_dt, int32_t H_qk, int32_t H_v, int32_t K, int32_t V) {
+  return in_dt == GDN_BF16 && mfma_path(in_dt, K, V) && H_qk > 0 && H_v % H_qk == 0 && H_v / H_qk <= 4;
+}
+
+size_t gdn_conv_chunk_fwd_workspace_bytes(gdn_dtype in_dt, int64_t total_tokens, int32_t n_seqs,
+                                          int32_t H_qk, int32_t H_v, int32_t K, int32_t V) {
+  if (!conv_chunk_mfma(in_dt, H_qk, H_v, K, V) || total_tokens < 0 || n_seqs < 0) return 0;
+  const int64_t C = 2 * (int64_t)H_qk * K + (int64_t)H_v * V;
+  return align256((size_t)total_tokens * (size_t)C * 2) +
+         gdn_chunk_fwd_workspace_bytes(in_dt, total_tokens, n_seqs, H_v, K, V);
+}
+
 gdn_status gdn_conv_chunk_fwd(const void* x, const void* w, const void* bias, gdn_dtype in_dt,
                               int32_t width, float l2_eps, const float* g, const float* beta,
                               float scale, const float* initial_state, const int32_t* cu_seqlens,
                               const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t B, int64_t T,
                               int32_t H_qk, int32_t H_v, int32_t K, int32_t V, void* o,
-                              gdn_dtype o_dt, float* final_state, hipStream_t stream) {
+                              gdn_dtype o_dt, float* final_state, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
   if (!valid_dtype(in_dt) || !valid_dtype(o_dt)) return GDN_ERR_BAD_DTYPE;
   if (B < 1 || T < 0 || H_qk < 1 || H_v < 1 || K < 1 || V < 1) return GDN_ERR_BAD_SHAPE;
   if (H_v % H_qk != 0 || !(l2_eps > 0.f)) return GDN_ERR_BAD_SHAPE;
@@ -458,6 +493,18 @@ gdn_status gdn_conv_chunk_fwd(const void* x, const void* w, const void* bias, gd
   if (total == 0 && !final_state) return GDN_OK;
   if (total > 0 && (!x || !w || !g || !beta || !o)) return GDN_ERR_NULL_POINTER;
   const size_t es = in_dt == GDN_BF16 ? 2 : 4;
+  if (conv_chunk_mfma(in_dt, H_qk, H_v, K, V)) {
+    // the activations take the front of the workspace, the chunk rule the rest
+    if (!workspace) return GDN_ERR_NULL_POINTER;
+    if (workspace_bytes < gdn_conv_chunk_fwd_workspace_bytes(in_dt, total, N, H_qk, H_v, K, V))
+      return GDN_ERR_BAD_SHAPE;
+    const size_t ybytes = align256((size_t)total * (size_t)C * es);
+    unsigned char* y = static_cast<unsigned char*>(workspace);
+    const ConvIn conv{x, w, bias, width, l2_eps, y};
+    return chunk_fwd_run(y, y + es * (size_t)H_qk * K, y + es * 2 * (size_t)H_qk * K, in_dt, C, C, C, g, beta,
+                         scale, initial_state, cu_seqlens, cu_seqlens_host, n_seqs, B, T, H_qk, H_v, K, V, o,
+                         o_dt, final_state, y + ybytes, workspace_bytes - ybytes, nullptr, stream, nullptr, &conv);
+  }
   const unsigned char* xb = static_cast<const unsigned char*>(x);
   gdn::ChunkArgs a{};
   a.q = xb;

@@ -119,6 +119,28 @@ __device__ __forceinline__ float silu_hw(float z) {
   return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
 }
 
+// The short convolution's SiLU, z / (1 + e^-z) with the hardware reciprocal;
+// the separate conv and the conv fused into the chunk prep share it, so that
+// both store the same activations.
+__device__ __forceinline__ float silu_conv(float z) { return z * __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false);
+  return v + __int_as_float(o);
+}
+
+// Sum over aligned groups of 2^lanes_log2 lanes (uniform lanes_log2 <= 6).
+__device__ __forceinline__ float group_sum(float v, int lanes_log2) {
+  if (lanes_log2 >= 1) v = dpp_add<0xB1>(v);   // quad_perm [1, 0, 3, 2]: xor 1
+  if (lanes_log2 >= 2) v = dpp_add<0x4E>(v);   // quad_perm [2, 3, 0, 1]: xor 2
+  if (lanes_log2 >= 3) v = dpp_add<0x141>(v);  // half-row mirror: the other quad of 8
+  if (lanes_log2 >= 4) v = dpp_add<0x140>(v);  // row mirror: the other half of 16
+  if (lanes_log2 >= 5) v += __shfl_xor(v, 16, 64);
+  if (lanes_log2 >= 6) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
 __device__ __forceinline__ int clampi(int64_t x, int64_t lo, int64_t hi) {
   return (int)(x < lo ? lo : (x > hi ? hi : x));
 }

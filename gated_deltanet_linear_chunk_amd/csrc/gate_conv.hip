@@ -156,22 +156,6 @@ __device__ __forceinline__ float bf16_nearest_f64(double d) {
   return __uint_as_float(b);
 }
 
-template <int kCtrl>
-__device__ __forceinline__ float dpp_add(float v) {
-  const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false);
-  return v + __int_as_float(o);
-}
-
-// Sum over aligned groups of 2^lanes_log2 lanes (uniform lanes_log2 <= 6).
-__device__ __forceinline__ float group_sum(float v, int lanes_log2) {
-  if (lanes_log2 >= 1) v = dpp_add<0xB1>(v);   // quad_perm [1, 0, 3, 2]: xor 1
-  if (lanes_log2 >= 2) v = dpp_add<0x4E>(v);   // quad_perm [2, 3, 0, 1]: xor 2
-  if (lanes_log2 >= 3) v = dpp_add<0x141>(v);  // half-row mirror: the other quad of 8
-  if (lanes_log2 >= 4) v = dpp_add<0x140>(v);  // row mirror: the other half of 16
-  if (lanes_log2 >= 5) v += __shfl_xor(v, 16, 64);
-  if (lanes_log2 >= 6) v += __shfl_xor(v, 32, 64);
-  return v;
-}
 
 // Whether y (fp32, from bf16 inputs) might round to another bf16 value than
 // the exact conv (+ SiLU) result.  The tap products are exact and each of the
@@ -281,7 +265,7 @@ __device__ __forceinline__ void conv_sub(const typename ConvRow<T>::raw_t (&buf)
       z = fmaf(wt[1][i], x2, z);
       z = fmaf(wt[2][i], x3, z);
       z = fmaf(wt[3][i], cur[i], z);
-      const float v = kSilu ? z * __builtin_amdgcn_rcpf(1.f + __expf(-z)) : z;
+      const float v = kSilu ? silu_conv(z) : z;
       out[i] = v;
       if (kL2) ss = fmaf(v, v, ss);
       if (kCheck) {

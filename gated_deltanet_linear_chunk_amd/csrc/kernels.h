@@ -70,6 +70,13 @@ struct ChunkArgs {
   const void* cb;
   int conv_width;
   float l2_eps;
+  // bf16 MFMA path with the conv fused into the prep (chunk_prep_conv_kernel):
+  // cx is the raw q | k | v channel input [tokens, 2*Hqk*K + Hv*V] (token
+  // stride q_stride), cy the activations the prep stores in the same layout
+  // (conv, SiLU, L2 norm of q and k rows; q, k, v point into it for the
+  // scans), cw, cb, conv_width and l2_eps as above.
+  const void* cx;
+  void* cy;
 };
 
 // One record: T diag(beta) hi, lo (bf16, 10 tiles x 256 each), gamma[64] and

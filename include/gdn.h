@@ -222,31 +222,44 @@ gdn_status gdn_chunk_fwd_gated_norm(const void* q, const void* k, const void* v,
  * concatenated q | k | v channels and hand its output to the chunk rule on
  * the same token-major layout (LlamaFactory PR "[v1] support GDN Ulysses
  * cp", Design: Q/K/V concatenated for conv1d, then the chunk rule); here
- * the chunk kernel forms each 64-token chunk's q, k, v rows from the raw
- * channels itself:
+ * the chunk kernels form each 64-token chunk's q, k, v rows from the raw
+ * channels themselves:
  *     a[t, c] = silu(bias[c] + sum_{j<width} w[c, j] x[t - width + 1 + j, c])
  * with x zero before the first token of t's sequence, and every q and k
  * head row divided by sqrt(sum of squares + l2_eps) -- the activations of
- * gdn_conv1d_fwd with l2norm_channels = 2 H_qk K, head_dim = K -- then runs
- * the rule of gdn_chunk_fwd on them.  The activations are kept in fp32 and
- * never written to memory (nor rounded to in_dt).
+ * gdn_conv1d_fwd with l2norm_channels = 2 H_qk K, head_dim = K -- then run
+ * the rule of gdn_chunk_fwd on them.
  *  x     [B, T, C] in in_dt, dense, C = 2 H_qk K + H_v V channels in the order
  *        q heads | k heads | v heads
  *  w     [C, width] in in_dt, width in [1, 4];  bias [C] in in_dt or NULL
  *  l2_eps > 0 (GDN_ERR_BAD_SHAPE otherwise)
  *  g, beta, scale, initial_state, cu_seqlens, cu_seqlens_host, n_seqs, B,
  *  T, H_qk, H_v, K, V, o, o_dt, final_state: as gdn_chunk_fwd.
- * Runs the fp32 vector-ALU chunk kernel for every shape (K in {32, 64, 128},
- * V % 32 == 0; GDN_ERR_UNSUPPORTED otherwise), with no workspace: each
- * workgroup forms the q, k rows of its head and the v columns of its slice,
- * so q and k are convolved once per column slice and v-head sharing them.
+ * Kernels: bf16 inputs with K = 128, V % 128 == 0 and H_v / H_qk <= 4 run
+ * the MFMA path with the conv in its chunk prep: the prep stores the
+ * activations as bf16 into the workspace, computed exactly as
+ * gdn_conv1d_fwd with GDN_ROUND_FAST computes them, so o and final_state
+ * equal the unfused pair (gdn_conv1d_fwd, then gdn_chunk_fwd on its output)
+ * bit for bit; packed calls with host offsets are split as gdn_chunk_fwd
+ * splits them.  Every other shape (K in {32, 64, 128}, V % 32 == 0;
+ * GDN_ERR_UNSUPPORTED otherwise) runs the fp32 vector-ALU kernel, which keeps
+ * the activations in fp32, never writes them and needs no workspace: each of
+ * its workgroups forms the q, k rows of its head and the v columns of its
+ * slice.
+ *  workspace: device memory of at least gdn_conv_chunk_fwd_workspace_bytes
+ *  bytes (0 for shapes of the vector-ALU kernel, where it may be NULL); its
+ *  contents on entry do not matter.  GDN_ERR_NULL_POINTER when a workspace is
+ *  needed and missing, GDN_ERR_BAD_SHAPE when it is too small.
  */
+size_t gdn_conv_chunk_fwd_workspace_bytes(gdn_dtype in_dt, int64_t total_tokens, int32_t n_seqs,
+                                          int32_t H_qk, int32_t H_v, int32_t K, int32_t V);
 gdn_status gdn_conv_chunk_fwd(const void* x, const void* w, const void* bias, gdn_dtype in_dt,
                               int32_t width, float l2_eps, const float* g, const float* beta,
                               float scale, const float* initial_state, const int32_t* cu_seqlens,
                               const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t B, int64_t T,
                               int32_t H_qk, int32_t H_v, int32_t K, int32_t V, void* o,
-                              gdn_dtype o_dt, float* final_state, hipStream_t stream);
+                              gdn_dtype o_dt, float* final_state, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Segment state scan: one long sequence cut into P contiguous segments

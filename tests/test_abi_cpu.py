@@ -42,7 +42,7 @@ def test_status_strings_and_version(lib):
     for s in range(8):
         assert lib.gdn_status_string(s)
     assert b"unknown" in lib.gdn_status_string(99)
-    assert lib.gdn_abi_version() == 2
+    assert lib.gdn_abi_version() == 3
 
 
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation first
@@ -180,7 +180,7 @@ def test_conv_chunk_validation(lib):
     def cc(**kw):
         a = dict(x=FAKE, w=FAKE, bias=None, in_dt=1, W=4, eps=1e-6, g=FAKE, beta=FAKE, scale=1.0, s0=None, cu=None,
                  cu_host=None, n_seqs=0, B=1, T=64, Hqk=16, Hv=32, K=128, V=128, o=FAKE, o_dt=0, fin=None,
-                 stream=None)
+                 ws=FAKE, ws_bytes=1 << 40, stream=None)
         a.update(kw)
         return lib.gdn_conv_chunk_fwd(*a.values())
 
@@ -202,6 +202,15 @@ def test_conv_chunk_validation(lib):
     assert cc(cu=FAKE, n_seqs=2, cu_host=(ctypes.c_int32 * 3)(0, 10, 63)) == SEQ  # must end at T
     assert cc(cu=FAKE, n_seqs=0) == SEQ
     assert cc(T=0, x=None, w=None, g=None, beta=None, o=None) == OK  # nothing to do without a final state
+    # bf16 with the MFMA head sizes needs the workspace its query names
+    need = lib.gdn_conv_chunk_fwd_workspace_bytes(1, 64, 1, 16, 32, 128, 128)
+    assert need > 64 * (2 * 16 * 128 + 32 * 128) * 2
+    assert cc(ws=None) == NULLP
+    assert cc(ws_bytes=need - 1) == SHAPE
+    # the vector-ALU shapes need none
+    assert lib.gdn_conv_chunk_fwd_workspace_bytes(0, 64, 1, 16, 32, 128, 128) == 0  # fp32
+    assert lib.gdn_conv_chunk_fwd_workspace_bytes(1, 64, 1, 16, 32, 64, 64) == 0  # K = 64
+    assert lib.gdn_conv_chunk_fwd_workspace_bytes(1, 64, 1, 4, 32, 128, 128) == 0  # 8 v-heads per q/k head
 
 
 def test_gate_and_segment_validation(lib):

@@ -162,12 +162,14 @@ def test_conv_writes_nothing_outside(exact):
     assert bool(torch.isfinite(y.payload().view(torch.bfloat16)).all())
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_conv_chunk_writes_nothing_outside(dtype):
+@pytest.mark.parametrize("dtype,K", [("bf16", 64), ("f32", 64), ("bf16", 128)])
+def test_conv_chunk_writes_nothing_outside(dtype, K):
     """The fused conv + chunk call, with device-only offsets that leave the last
-    sample's tokens in no sample: their o rows stay untouched as well."""
+    sample's tokens in no sample: their o rows stay untouched as well.  K = 128
+    in bf16 runs the MFMA path, whose workspace (activations and records) is
+    guarded too."""
     lib = gdn.load_library()
-    Hqk, Hv, K, V = 2, 4, 64, 64
+    Hqk, Hv, V = 2, 4, K
     lengths = [1, 63, 0, 130, 40]
     d = gdn_inputs.small(23, lengths, Hqk, Hv, K, V, dtype, conv_width=4, s0_std=0.05)
     T, C = d["x"].shape
@@ -180,12 +182,17 @@ def test_conv_chunk_writes_nothing_outside(dtype):
     o = Guarded(T * Hv * V * es)
     fin = Guarded(N * Hv * K * V * 4)
     in_dt = gdn.BF16 if dtype == "bf16" else gdn.F32
+    nws = lib.gdn_conv_chunk_fwd_workspace_bytes(in_dt, T, N, Hqk, Hv, K, V)
+    assert (nws > 0) == (dtype == "bf16" and K == 128)
+    ws = Guarded(nws) if nws else None
     st = lib.gdn_conv_chunk_fwd(x.data_ptr(), cw.data_ptr(), cb.data_ptr(), in_dt, 4, 1e-6, g.data_ptr(),
                                 beta.data_ptr(), 0.125, s0.data_ptr(), cu.data_ptr(), None, N, 1, T, Hqk, Hv, K, V,
-                                o.ptr, in_dt, fin.ptr, _stream())
+                                o.ptr, in_dt, fin.ptr, ws.ptr if ws else None, nws, _stream())
     assert st == 0
     o.check("o")
     fin.check("final_state")
+    if ws:
+        ws.check("workspace")
     rows = o.payload((T, Hv * V * es))
     last = int(d["cu_seqlens"][-2])
     assert bool((rows[last:] == PATTERN).all()), "o rows of tokens in no sample were written"
