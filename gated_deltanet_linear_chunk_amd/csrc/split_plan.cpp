@@ -144,36 +144,49 @@ static bool plan_split_uncached(const int32_t* cu, int32_t N, int32_t H_v, int32
   double work = 0.0;
   for (int64_t c : chunks) work += (double)c * H_v * tiles2;
   if (0.85 * base < work / cus) return false;
+  // A sample of more than seg chunks is cut into a first segment of `first`
+  // chunks (run forward in pass 1) and segments of seg chunks after it.
+  auto n_segs = [](int64_t c, int64_t seg, int64_t first) -> int64_t {
+    return c > seg ? 1 + (c - first + seg - 1) / seg : 1;
+  };
   double best = base;
-  int64_t best_seg = 0;
+  int64_t best_seg = 0, best_first = 0;
   for (int parts = 2; parts <= 16; ++parts) {
-    const int64_t seg = (cmax + parts - 1) / parts;  // chunks per segment
-    if (seg < 4) break;
-    std::vector<int64_t> lens2, fwd1;
-    int64_t n_maps = 0, longest_chain = 0;
-    for (int32_t n = 0; n < N; ++n) {
-      const int64_t s = chunks[n] > seg ? (chunks[n] + seg - 1) / seg : 1;
-      if (s == 1) {
-        lens2.push_back(chunks[n]);
-        continue;
+    const int64_t even = (cmax + parts - 1) / parts;  // chunks per segment, all equal
+    if (even < 4) break;
+    // The first segment runs forward in pass 1 beside the maps, which cost
+    // about 0.7 of a forward chunk each: a shorter first segment (the others
+    // longer, so that the longest sample keeps `parts` segments) can end
+    // pass 1 with the maps.
+    for (const int64_t first : {even, (4 * even + 4) / 5, (3 * even + 3) / 4, (2 * even + 2) / 3}) {
+      const int64_t seg = first == even ? even : (cmax - first + parts - 2) / (parts - 1);
+      std::vector<int64_t> lens2, fwd1;
+      int64_t n_maps = 0, longest_chain = 0;
+      for (int32_t n = 0; n < N; ++n) {
+        const int64_t s = n_segs(chunks[n], seg, first);
+        if (s == 1) {
+          lens2.push_back(chunks[n]);
+          continue;
+        }
+        fwd1.push_back(first);
+        n_maps += s - 2;
+        longest_chain = std::max(longest_chain, s - 2);
+        for (int64_t j = 1; j < s; ++j) lens2.push_back(std::min(seg, chunks[n] - first - (j - 1) * seg));
       }
-      fwd1.push_back(seg);
-      n_maps += s - 2;
-      longest_chain = std::max(longest_chain, s - 2);
-      for (int64_t j = 1; j < s; ++j) lens2.push_back(std::min(seg, chunks[n] - j * seg));
-    }
-    const int64_t n_pass1 = (int64_t)fwd1.size() + n_maps;
-    if (n_pass1 == 0 || n_pass1 > pmax) continue;
-    // pass 1: the forward segments first, then the maps; a map chunk skips
-    // q, the output and P: about 0.7 of a forward chunk; a chain step costs
-    // about one chunk
-    std::vector<Group> p1;
-    for (int64_t c : fwd1) p1.push_back(Group{(double)c, (int64_t)H_v * tiles2});
-    p1.push_back(Group{0.7 * (double)seg, n_maps * H_v * tiles1});
-    const double t = makespan(p1, cus) + (double)longest_chain + forward(lens2);
-    if (t < best) {
-      best = t;
-      best_seg = seg;
+      const int64_t n_pass1 = (int64_t)fwd1.size() + n_maps;
+      if (n_pass1 == 0 || n_pass1 > pmax) continue;
+      // pass 1: the forward segments first, then the maps; a map chunk skips
+      // q, the output and P: about 0.7 of a forward chunk; a chain step costs
+      // about one chunk
+      std::vector<Group> p1;
+      for (int64_t c : fwd1) p1.push_back(Group{(double)c, (int64_t)H_v * tiles2});
+      p1.push_back(Group{0.7 * (double)seg, n_maps * H_v * tiles1});
+      const double t = makespan(p1, cus) + (double)longest_chain + forward(lens2);
+      if (t < best) {
+        best = t;
+        best_seg = seg;
+        best_first = first;
+      }
     }
   }
   if (best_seg == 0 || best > 0.85 * base) return false;
@@ -184,10 +197,12 @@ static bool plan_split_uncached(const int32_t* cu, int32_t N, int32_t H_v, int32
   };
   std::vector<Seg> segs;
   for (int32_t n = 0; n < N; ++n) {
-    const int64_t s = chunks[n] > best_seg ? (chunks[n] + best_seg - 1) / best_seg : 1;
+    const int64_t s = n_segs(chunks[n], best_seg, best_first);
+    // chunk where segment j starts: 0, first, first + seg, ...
+    auto start = [&](int64_t j) { return j == 0 ? 0 : best_first + (j - 1) * best_seg; };
     for (int64_t j = 0; j < s; ++j) {
-      const int32_t b = (int32_t)(cu[n] + 64 * best_seg * j);
-      const int32_t e = j + 1 < s ? (int32_t)(cu[n] + 64 * best_seg * (j + 1)) : cu[n + 1];
+      const int32_t b = (int32_t)(cu[n] + 64 * start(j));
+      const int32_t e = j + 1 < s ? (int32_t)(cu[n] + 64 * start(j + 1)) : cu[n + 1];
       segs.push_back({b, e, n, (int32_t)j, (int32_t)s});
     }
   }
