@@ -191,7 +191,7 @@ static bool plan_split_uncached(const int32_t* cu, int32_t N, int32_t H_v, int32
   }
   if (best_seg == 0 || best > 0.85 * base) return false;
 
-  // ---- the plan for segments of best_seg chunks --------------------------------
+  // ---- the plan: a first segment of best_first chunks, then segments of best_seg --
   struct Seg {
     int32_t begin, end, n, j, s;
   };
