@@ -204,6 +204,7 @@ def _unfused(d, Hqk, K, B=1, packed=True, bias=True, s0=None, o_dtype=torch.floa
     ([2500, 0, 700, 64, 1, 1350], 4, True, 4),  # long samples: the planner splits them
     (LENGTHS, 3, False, 4),
     ([300, 5, 1000], 1, True, 6),
+    ([700, 64, 1, 190], 4, True, 8),  # four v-heads per q/k head: the widest prep workgroup
 ])
 def test_conv_chunk_mfma_equals_unfused_bitwise(lengths, W, bias, Hv):
     """The conv in the chunk prep computes every activation as the separate conv does, so the fused
