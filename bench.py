@@ -274,7 +274,7 @@ def build_pipeline(w, d, o_dtype, rotate=4):
 
 
 def build_conv_chunk(w, d):
-    """Gates + the fused conv + chunk call of a workload, on its raw conv input."""
+    """The fused call of a workload (gates, conv and chunk rule in one call), on its raw inputs."""
     torch = _torch()
     import gated_deltanet_linear_chunk_amd as gdn
 
@@ -293,20 +293,18 @@ def build_conv_chunk(w, d):
     cu = None if B > 1 else torch.from_numpy(d["cu_seqlens"]).to(dev)
     cu_host = None if B > 1 else d["cu_seqlens"]
     s0 = f32(d["s0"]) if "s0" in d else None
-    g0, beta0 = gdn.gdn_gate_fwd(a, b, A_log, dt_bias)
     state = {"i": 0}
 
-    def fused(x, g, beta):
-        return gdn.gdn_conv_chunk_fwd(x, cw, g, beta, Hqk=w.Hqk, K=w.K, bias=cb, initial_state=s0, cu_seqlens=cu,
-                                      cu_seqlens_host=cu_host, o_dtype=torch.float32)
+    def fused(x):
+        return gdn.gdn_conv_chunk_fwd(x, cw, a, b, A_log, dt_bias, Hqk=w.Hqk, K=w.K, bias=cb, initial_state=s0,
+                                      cu_seqlens=cu, cu_seqlens_host=cu_host, o_dtype=torch.float32)
 
     def step():
         x = xs[state["i"] % len(xs)]
         state["i"] += 1
-        g, beta = gdn.gdn_gate_fwd(a, b, A_log, dt_bias)
-        return fused(x, g, beta)
+        return fused(x)
 
-    return {"step": step, "call": lambda: fused(xs[0], g0, beta0), "C": C}
+    return {"step": step, "call": lambda: fused(xs[0]), "C": C}
 
 
 def build_chunk_only(w, d, o_dtype, mode="plain"):

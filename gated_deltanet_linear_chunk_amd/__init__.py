@@ -105,8 +105,8 @@ def load_library():
                                              sz, P]
     lib.gdn_conv_chunk_fwd_workspace_bytes.argtypes = [ctypes.c_int, i64, i32, i32, i32, i32, i32]
     lib.gdn_conv_chunk_fwd_workspace_bytes.restype = sz
-    lib.gdn_conv_chunk_fwd.argtypes = [P, P, P, ctypes.c_int, i32, f32, P, P, f32, P, P, P, i32, i32, i64, i32, i32,
-                                       i32, i32, P, ctypes.c_int, P, P, sz, P]
+    lib.gdn_conv_chunk_fwd.argtypes = [P, P, P, ctypes.c_int, i32, f32, P, P, P, P, f32, P, P, P, i32, i32, i64, i32,
+                                       i32, i32, i32, P, ctypes.c_int, P, P, sz, P]
     lib.gdn_segment_state_scan_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
     lib.gdn_segment_state_scan_workspace_bytes.restype = sz
     lib.gdn_segment_state_scan.argtypes = [P, P, ctypes.c_int, i64, i64, P, P, P, P, i32, P, i64, i32, i32, i32, i32,
@@ -409,14 +409,15 @@ def gdn_conv_chunk_fwd_workspace_bytes(in_dtype, total_tokens: int, n_seqs: int,
     return int(load_library().gdn_conv_chunk_fwd_workspace_bytes(code, total_tokens, n_seqs, Hqk, Hv, K, V))
 
 
-def gdn_conv_chunk_fwd(x, w, g, beta, Hqk: int, K: int, bias=None, scale: float = 1.0, initial_state=None,
-                       cu_seqlens=None, cu_seqlens_host=None, l2_eps: float = 1e-6, o_dtype=None,
-                       output_final_state: bool = True, workspace=None):
-    """conv1d + SiLU + q/k L2 norm formed inside the chunk kernels, then the chunk rule.
+def gdn_conv_chunk_fwd(x, w, a, b, A_log, dt_bias, Hqk: int, K: int, bias=None, scale: float = 1.0,
+                       initial_state=None, cu_seqlens=None, cu_seqlens_host=None, l2_eps: float = 1e-6,
+                       o_dtype=None, output_final_state: bool = True, workspace=None):
+    """conv1d + SiLU + q/k L2 norm and the gates formed inside the chunk kernels, then the chunk rule.
 
     x [B, T, C] raw channels q heads | k heads | v heads, C = 2 Hqk K + Hv V;
-    w [C, W] and bias [C] or None in x's dtype; g, beta fp32 [B, T, Hv] (Hv
-    from g).  bf16 with the MFMA head sizes forms the activations in the chunk
+    w [C, W] and bias [C] or None in x's dtype; a, b fp32 [B, T, Hv] gate
+    inputs and A_log, dt_bias fp32 [Hv] (g and beta as gdn_gate_fwd forms
+    them).  bf16 with the MFMA head sizes forms the activations in the chunk
     prep (bf16, as the separate conv stores them); other shapes keep them in
     fp32 inside the vector-ALU kernel.  Other arguments and the results as
     gdn_chunk_fwd.
@@ -426,16 +427,18 @@ def gdn_conv_chunk_fwd(x, w, g, beta, Hqk: int, K: int, bias=None, scale: float 
     _require(x, "x", dev)
     _require(w, "w", dev, x.dtype)
     _require(bias, "bias", dev, x.dtype)
-    _require(g, "g", dev, torch.float32)
-    _require(beta, "beta", dev, torch.float32)
+    if a is None or b is None or A_log is None or dt_bias is None:
+        raise ValueError("a, b, A_log and dt_bias are required")
+    for t, name in ((a, "a"), (b, "b"), (A_log, "A_log"), (dt_bias, "dt_bias")):
+        _require(t, name, dev, torch.float32)
     _require(initial_state, "initial_state", dev, torch.float32)
     _require(cu_seqlens, "cu_seqlens", dev, torch.int32)
-    if x.dim() != 3 or g.dim() != 3:
-        raise ValueError("x must be [B, T, C] and g, beta [B, T, Hv]")
+    if x.dim() != 3 or a.dim() != 3:
+        raise ValueError("x must be [B, T, C] and a, b [B, T, Hv]")
     B, T, C = x.shape
-    Hv = g.shape[2]
-    if g.shape[:2] != (B, T) or beta.shape != g.shape:
-        raise ValueError("g / beta shapes disagree with x")
+    Hv = a.shape[2]
+    if a.shape[:2] != (B, T) or b.shape != a.shape or A_log.shape != (Hv,) or dt_bias.shape != (Hv,):
+        raise ValueError("a / b must be [B, T, Hv] and A_log / dt_bias [Hv]")
     if Hv < 1 or (C - 2 * Hqk * K) <= 0 or (C - 2 * Hqk * K) % Hv != 0:
         raise ValueError("x channels must be 2 Hqk K + Hv V")
     V = (C - 2 * Hqk * K) // Hv
@@ -449,9 +452,10 @@ def gdn_conv_chunk_fwd(x, w, g, beta, Hqk: int, K: int, bias=None, scale: float 
     total = T if cu_seqlens is not None else B * T
     ws = _workspace(gdn_conv_chunk_fwd_workspace_bytes(x.dtype, total, N, Hqk, Hv, K, V), dev, workspace)
     st = load_library().gdn_conv_chunk_fwd(
-        _ptr(x), _ptr(w), _ptr(bias), _dtype_code(x), w.shape[1], float(l2_eps), _ptr(g), _ptr(beta), float(scale),
-        _ptr(initial_state), _ptr(cu_seqlens), _host_offsets(cu_seqlens_host), 0 if cu_seqlens is None else N, B, T,
-        Hqk, Hv, K, V, _ptr(o), _dtype_code(o), _ptr(fin), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev),
+        _ptr(x), _ptr(w), _ptr(bias), _dtype_code(x), w.shape[1], float(l2_eps), _ptr(a), _ptr(b), _ptr(A_log),
+        _ptr(dt_bias), float(scale), _ptr(initial_state), _ptr(cu_seqlens), _host_offsets(cu_seqlens_host),
+        0 if cu_seqlens is None else N, B, T, Hqk, Hv, K, V, _ptr(o), _dtype_code(o), _ptr(fin), _ptr(ws),
+        0 if ws is None else ws.numel(), _stream(dev),
     )
     _check("gdn_conv_chunk_fwd", st)
     return o, fin

@@ -195,8 +195,9 @@ struct FusedNorm {
 };
 
 // The short convolution in front of the MFMA path (gdn_conv_chunk_fwd): raw
-// channels x, taps, bias, width and eps, and y, the buffer the prep stores the
-// activations to (q, k, v of the run point into it).
+// channels x, taps, bias, width and eps, y, the buffer the prep stores the
+// activations to (q, k, v of the run point into it), and the raw gate inputs
+// the prep forms g and beta from.
 struct ConvIn {
   const void* x;
   const void* w;
@@ -204,6 +205,7 @@ struct ConvIn {
   int width;
   float eps;
   void* y;
+  const float *ga, *gb, *gA_log, *gdt_bias;
 };
 
 // Source of the records' memory for callers without a workspace: called once
@@ -237,7 +239,8 @@ static gdn_status chunk_fwd_run(const void* q, const void* k, const void* v, gdn
   if (N > kMaxGrid || H_v > kMaxGrid) return GDN_ERR_UNSUPPORTED;
   const int64_t total = cu_seqlens ? T : (int64_t)B * T;
   if (total == 0 && !final_state) return GDN_OK;
-  if (total > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL_POINTER;
+  const bool raw_gates = conv && conv->ga;
+  if (total > 0 && (!q || !k || !v || (!raw_gates && (!g || !beta)) || !o)) return GDN_ERR_NULL_POINTER;
   const bool mfma = mfma_path(in_dt, K, V);
   if (mfma) {
     if (fixed_ws) {
@@ -290,6 +293,10 @@ static gdn_status chunk_fwd_run(const void* q, const void* k, const void* v, gdn
     a.cb = conv->bias;
     a.conv_width = conv->width;
     a.l2_eps = conv->eps;
+    a.ga = conv->ga;
+    a.gb = conv->gb;
+    a.gA_log = conv->gA_log;
+    a.gdt_bias = conv->gdt_bias;
   }
   // A split plan (cached for repeated offsets) comes first, so that the prep
   // launch on the samples also stores its index arrays.
@@ -469,8 +476,8 @@ size_t gdn_conv_chunk_fwd_workspace_bytes(gdn_dtype in_dt, int64_t total_tokens,
 }
 
 gdn_status gdn_conv_chunk_fwd(const void* x, const void* w, const void* bias, gdn_dtype in_dt,
-                              int32_t width, float l2_eps, const float* g, const float* beta,
-                              float scale, const float* initial_state, const int32_t* cu_seqlens,
+                              int32_t width, float l2_eps, const float* ga, const float* gb,
+                              const float* A_log, const float* dt_bias, float scale, const float* initial_state, const int32_t* cu_seqlens,
                               const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t B, int64_t T,
                               int32_t H_qk, int32_t H_v, int32_t K, int32_t V, void* o,
                               gdn_dtype o_dt, float* final_state, void* workspace,
@@ -491,7 +498,7 @@ gdn_status gdn_conv_chunk_fwd(const void* x, const void* w, const void* bias, gd
   if (N > kMaxGrid || H_v > kMaxGrid) return GDN_ERR_UNSUPPORTED;
   const int64_t total = cu_seqlens ? T : (int64_t)B * T;
   if (total == 0 && !final_state) return GDN_OK;
-  if (total > 0 && (!x || !w || !g || !beta || !o)) return GDN_ERR_NULL_POINTER;
+  if (total > 0 && (!x || !w || !ga || !gb || !A_log || !dt_bias || !o)) return GDN_ERR_NULL_POINTER;
   const size_t es = in_dt == GDN_BF16 ? 2 : 4;
   if (conv_chunk_mfma(in_dt, H_qk, H_v, K, V)) {
     // the activations take the front of the workspace, the chunk rule the rest
@@ -500,8 +507,8 @@ gdn_status gdn_conv_chunk_fwd(const void* x, const void* w, const void* bias, gd
       return GDN_ERR_BAD_SHAPE;
     const size_t ybytes = align256((size_t)total * (size_t)C * es);
     unsigned char* y = static_cast<unsigned char*>(workspace);
-    const ConvIn conv{x, w, bias, width, l2_eps, y};
-    return chunk_fwd_run(y, y + es * (size_t)H_qk * K, y + es * 2 * (size_t)H_qk * K, in_dt, C, C, C, g, beta,
+    const ConvIn conv{x, w, bias, width, l2_eps, y, ga, gb, A_log, dt_bias};
+    return chunk_fwd_run(y, y + es * (size_t)H_qk * K, y + es * 2 * (size_t)H_qk * K, in_dt, C, C, C, nullptr, nullptr,
                          scale, initial_state, cu_seqlens, cu_seqlens_host, n_seqs, B, T, H_qk, H_v, K, V, o,
                          o_dt, final_state, y + ybytes, workspace_bytes - ybytes, nullptr, stream, nullptr, &conv);
   }
@@ -510,8 +517,10 @@ gdn_status gdn_conv_chunk_fwd(const void* x, const void* w, const void* bias, gd
   a.q = xb;
   a.k = xb ? xb + es * (size_t)H_qk * K : nullptr;
   a.v = xb ? xb + es * 2 * (size_t)H_qk * K : nullptr;
-  a.g = g;
-  a.beta = beta;
+  a.ga = ga;
+  a.gb = gb;
+  a.gA_log = A_log;
+  a.gdt_bias = dt_bias;
   a.cu = cu_seqlens;
   a.n_seqs = N;
   a.row_len = T;

@@ -213,8 +213,18 @@ __global__ void __launch_bounds__(F32_THREADS) chunk_f32_kernel(ChunkArgs a) {
     }
     if (tid < CH) {  // wave 0: beta, and G as an inclusive fp64 scan across the wave's lanes
       const bool ok = tid < L;
-      sBeta[tid] = ok ? a.beta[(t0 + tid) * a.Hv + h] : 0.f;
-      double G = ok ? (double)a.g[(t0 + tid) * a.Hv + h] : 0.0;
+      float gv = 0.f, bv = 0.f;
+      if (ok) {
+        const int64_t i = (t0 + tid) * a.Hv + h;
+        if (a.ga)
+          gate_values(a.ga[i], a.gb[i], a.gA_log[h], a.gdt_bias[h], gv, bv);
+        else {
+          gv = a.g[i];
+          bv = a.beta[i];
+        }
+      }
+      sBeta[tid] = bv;
+      double G = (double)gv;
 #pragma unroll
       for (int off = 1; off < CH; off <<= 1) {
         const double y = __shfl_up(G, off, CH);

@@ -63,6 +63,17 @@ __device__ __forceinline__ int slot_sequence(const ChunkArgs& a, int slot, int l
   return lo;
 }
 
+// g and beta of element i (token * Hv + h): read, or formed from the raw gate
+// inputs.
+__device__ __forceinline__ void load_gates(const ChunkArgs& a, int64_t i, int h, float& g, float& beta) {
+  if (a.ga)
+    gate_values(a.ga[i], a.gb[i], a.gA_log[h], a.gdt_bias[h], g, beta);
+  else {
+    g = a.g[i];
+    beta = a.beta[i];
+  }
+}
+
 __device__ __forceinline__ int blk(int i, int j) { return (i * (i + 1)) / 2 + j; }
 
 // e^x for x = G_r - G_s <= 0 (an fp64 difference, so no cancellation), on the
@@ -302,8 +313,7 @@ chunk_prep_kernel(ChunkArgs a, PlanArg plan, int32_t* __restrict__ plan_dst) {
   {
     const bool ok = lane < L;
     const int64_t grow = t0 + (ok ? lane : 0);
-    graw = a.g[grow * a.Hv + h];
-    braw = a.beta[grow * a.Hv + h];
+    load_gates(a, grow * a.Hv + h, h, graw, braw);
     if (!ok) graw = braw = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -498,8 +508,7 @@ chunk_prep_conv_kernel(ChunkArgs a, PlanArg plan, int32_t* __restrict__ plan_dst
   {
     const bool ok = lane < L;
     const int64_t grow = t0 + (ok ? lane : 0);
-    graw = a.g[grow * a.Hv + h];
-    braw = a.beta[grow * a.Hv + h];
+    load_gates(a, grow * a.Hv + h, h, graw, braw);
     if (!ok) graw = braw = 0.f;
   }
 

@@ -124,6 +124,16 @@ __device__ __forceinline__ float silu_hw(float z) {
 // both store the same activations.
 __device__ __forceinline__ float silu_conv(float z) { return z * __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
 
+// The gates of one (token, v-head): g = -e^{A_log} softplus(a + dt_bias),
+// beta = sigmoid(b); the gate kernel and the kernels that form the gates
+// from the raw inputs themselves share it, so both give the same values.
+__device__ __forceinline__ void gate_values(float a, float b, float A_log, float dt_bias, float& g, float& beta) {
+  const float x = a + dt_bias;
+  const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+  g = -expf(A_log) * sp;
+  beta = 1.f / (1.f + expf(-b));
+}
+
 template <int kCtrl>
 __device__ __forceinline__ float dpp_add(float v) {
   const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false);

@@ -19,10 +19,7 @@ __global__ void __launch_bounds__(256) gate_kernel(const float* __restrict__ a,
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
     const int h = (int)(i % H);
-    const float x = a[i] + dt_bias[h];
-    const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
-    g[i] = -expf(A_log[h]) * sp;
-    beta[i] = 1.f / (1.f + expf(-b[i]));
+    gate_values(a[i], b[i], A_log[h], dt_bias[h], g[i], beta[i]);
   }
 }
 

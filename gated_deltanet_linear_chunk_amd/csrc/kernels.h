@@ -77,6 +77,13 @@ struct ChunkArgs {
   // scans), cw, cb, conv_width and l2_eps as above.
   const void* cx;
   void* cy;
+  // Raw gate inputs (gdn_conv_chunk_fwd): when ga is set, the kernels form g
+  // and beta themselves from ga, gb [Ttot, Hv] and gA_log, gdt_bias [Hv]
+  // (gate_values) instead of reading g and beta.
+  const float* ga;
+  const float* gb;
+  const float* gA_log;
+  const float* gdt_bias;
 };
 
 // One record: T diag(beta) hi, lo (bf16, 10 tiles x 256 each), gamma[64] and

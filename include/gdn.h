@@ -233,14 +233,17 @@ gdn_status gdn_chunk_fwd_gated_norm(const void* q, const void* k, const void* v,
  *        q heads | k heads | v heads
  *  w     [C, width] in in_dt, width in [1, 4];  bias [C] in in_dt or NULL
  *  l2_eps > 0 (GDN_ERR_BAD_SHAPE otherwise)
- *  g, beta, scale, initial_state, cu_seqlens, cu_seqlens_host, n_seqs, B,
- *  T, H_qk, H_v, K, V, o, o_dt, final_state: as gdn_chunk_fwd.
+ *  a, b  fp32 [B, T, H_v] gate inputs, A_log, dt_bias fp32 [H_v]: the call
+ *        forms g = -exp(A_log) softplus(a + dt_bias) and beta = sigmoid(b)
+ *        itself, with the arithmetic of gdn_gate_fwd
+ *  scale, initial_state, cu_seqlens, cu_seqlens_host, n_seqs, B, T, H_qk,
+ *  H_v, K, V, o, o_dt, final_state: as gdn_chunk_fwd.
  * Kernels: bf16 inputs with K = 128, V % 128 == 0 and H_v / H_qk <= 4 run
  * the MFMA path with the conv in its chunk prep: the prep stores the
  * activations as bf16 into the workspace, computed exactly as
  * gdn_conv1d_fwd with GDN_ROUND_FAST computes them, so o and final_state
- * equal the unfused pair (gdn_conv1d_fwd, then gdn_chunk_fwd on its output)
- * bit for bit; packed calls with host offsets are split as gdn_chunk_fwd
+ * equal the unfused steps (gdn_gate_fwd and gdn_conv1d_fwd, then
+ * gdn_chunk_fwd on their outputs) bit for bit; packed calls with host offsets are split as gdn_chunk_fwd
  * splits them.  Every other shape (K in {32, 64, 128}, V % 32 == 0;
  * GDN_ERR_UNSUPPORTED otherwise) runs the fp32 vector-ALU kernel, which keeps
  * the activations in fp32, never writes them and needs no workspace: each of
@@ -254,8 +257,8 @@ gdn_status gdn_chunk_fwd_gated_norm(const void* q, const void* k, const void* v,
 size_t gdn_conv_chunk_fwd_workspace_bytes(gdn_dtype in_dt, int64_t total_tokens, int32_t n_seqs,
                                           int32_t H_qk, int32_t H_v, int32_t K, int32_t V);
 gdn_status gdn_conv_chunk_fwd(const void* x, const void* w, const void* bias, gdn_dtype in_dt,
-                              int32_t width, float l2_eps, const float* g, const float* beta,
-                              float scale, const float* initial_state, const int32_t* cu_seqlens,
+                              int32_t width, float l2_eps, const float* a, const float* b,
+                              const float* A_log, const float* dt_bias, float scale, const float* initial_state, const int32_t* cu_seqlens,
                               const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t B, int64_t T,
                               int32_t H_qk, int32_t H_v, int32_t K, int32_t V, void* o,
                               gdn_dtype o_dt, float* final_state, void* workspace,

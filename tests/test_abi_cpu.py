@@ -178,7 +178,8 @@ def test_conv_validation(lib):
 
 def test_conv_chunk_validation(lib):
     def cc(**kw):
-        a = dict(x=FAKE, w=FAKE, bias=None, in_dt=1, W=4, eps=1e-6, g=FAKE, beta=FAKE, scale=1.0, s0=None, cu=None,
+        a = dict(x=FAKE, w=FAKE, bias=None, in_dt=1, W=4, eps=1e-6, ga=FAKE, gb=FAKE, A_log=FAKE, dt_bias=FAKE,
+                 scale=1.0, s0=None, cu=None,
                  cu_host=None, n_seqs=0, B=1, T=64, Hqk=16, Hv=32, K=128, V=128, o=FAKE, o_dt=0, fin=None,
                  ws=FAKE, ws_bytes=1 << 40, stream=None)
         a.update(kw)
@@ -186,7 +187,10 @@ def test_conv_chunk_validation(lib):
 
     assert cc(x=None) == NULLP
     assert cc(w=None) == NULLP
-    assert cc(g=None) == NULLP
+    assert cc(ga=None) == NULLP
+    assert cc(gb=None) == NULLP
+    assert cc(A_log=None) == NULLP
+    assert cc(dt_bias=None) == NULLP
     assert cc(o=None) == NULLP
     assert cc(in_dt=3) == DTYPE
     assert cc(o_dt=3) == DTYPE
@@ -201,7 +205,7 @@ def test_conv_chunk_validation(lib):
     assert cc(cu=FAKE, n_seqs=2, B=2) == SEQ
     assert cc(cu=FAKE, n_seqs=2, cu_host=(ctypes.c_int32 * 3)(0, 10, 63)) == SEQ  # must end at T
     assert cc(cu=FAKE, n_seqs=0) == SEQ
-    assert cc(T=0, x=None, w=None, g=None, beta=None, o=None) == OK  # nothing to do without a final state
+    assert cc(T=0, x=None, w=None, ga=None, gb=None, A_log=None, dt_bias=None, o=None) == OK  # nothing to do
     # bf16 with the MFMA head sizes needs the workspace its query names
     need = lib.gdn_conv_chunk_fwd_workspace_bytes(1, 64, 1, 16, 32, 128, 128)
     assert need > 64 * (2 * 16 * 128 + 32 * 128) * 2
@@ -329,4 +333,5 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError, match="GPU tensor"):
         gdn.gdn_gated_rmsnorm_fwd(v, v)
     with pytest.raises(ValueError, match="GPU tensor"):
-        gdn.gdn_conv_chunk_fwd(torch.zeros(1, 64, 1024), torch.zeros(1024, 4), g, g, Hqk=2, K=128)
+        gdn.gdn_conv_chunk_fwd(torch.zeros(1, 64, 1024), torch.zeros(1024, 4), g, g, torch.zeros(4), torch.zeros(4),
+                               Hqk=2, K=128)

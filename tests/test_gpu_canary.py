@@ -176,7 +176,6 @@ def test_conv_chunk_writes_nothing_outside(dtype, K):
     N = len(lengths) - 1
     es = 2 if dtype == "bf16" else 4
     x, cw, cb = dev(d["x"], dtype), dev(d["conv_w"], dtype), dev(d["conv_bias"], dtype)
-    g, beta = gdn.gdn_gate_fwd(dev(d["a"]), dev(d["b"]), dev(d["A_log"]), dev(d["dt_bias"]))
     cu = dev(d["cu_seqlens"][:-1], "i32")
     s0 = dev(d["s0"][:N])
     o = Guarded(T * Hv * V * es)
@@ -185,8 +184,10 @@ def test_conv_chunk_writes_nothing_outside(dtype, K):
     nws = lib.gdn_conv_chunk_fwd_workspace_bytes(in_dt, T, N, Hqk, Hv, K, V)
     assert (nws > 0) == (dtype == "bf16" and K == 128)
     ws = Guarded(nws) if nws else None
-    st = lib.gdn_conv_chunk_fwd(x.data_ptr(), cw.data_ptr(), cb.data_ptr(), in_dt, 4, 1e-6, g.data_ptr(),
-                                beta.data_ptr(), 0.125, s0.data_ptr(), cu.data_ptr(), None, N, 1, T, Hqk, Hv, K, V,
+    ga, gb, gA, gdt = dev(d["a"]), dev(d["b"]), dev(d["A_log"]), dev(d["dt_bias"])
+    st = lib.gdn_conv_chunk_fwd(x.data_ptr(), cw.data_ptr(), cb.data_ptr(), in_dt, 4, 1e-6, ga.data_ptr(),
+                                gb.data_ptr(), gA.data_ptr(), gdt.data_ptr(), 0.125, s0.data_ptr(), cu.data_ptr(),
+                                None, N, 1, T, Hqk, Hv, K, V,
                                 o.ptr, in_dt, fin.ptr, ws.ptr if ws else None, nws, _stream())
     assert st == 0
     o.check("o")

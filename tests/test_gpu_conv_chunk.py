@@ -52,12 +52,13 @@ def _oracle(d, Hqk, Hv, K, V, scale=1.0, s0=None, threads=0, act_round="none"):
 
 
 def _fused(d, dtype, Hqk, K, B=1, packed=True, bias=True, scale=1.0, s0=None, o_dtype=None):
+    """The fused call on the raw conv input and the raw gate inputs."""
     T, C = d["x"].shape
-    g, beta = gdn.gdn_gate_fwd(dev(d["a"]), dev(d["b"]), dev(d["A_log"]), dev(d["dt_bias"]))
-    Hv = g.shape[-1]
+    Hv = d["a"].shape[-1]
     x = dev(d["x"], dtype).reshape(B, T // B, C)
     o, fin = gdn.gdn_conv_chunk_fwd(
-        x, dev(d["conv_w"], dtype), g.reshape(B, T // B, Hv), beta.reshape(B, T // B, Hv), Hqk=Hqk, K=K,
+        x, dev(d["conv_w"], dtype), dev(d["a"]).reshape(B, T // B, Hv), dev(d["b"]).reshape(B, T // B, Hv),
+        dev(d["A_log"]), dev(d["dt_bias"]), Hqk=Hqk, K=K,
         bias=dev(d["conv_bias"], dtype) if bias else None, scale=scale, initial_state=None if s0 is None else dev(s0),
         cu_seqlens=dev(d["cu_seqlens"], "i32") if packed else None,
         cu_seqlens_host=d["cu_seqlens"] if packed else None, o_dtype=o_dtype)
