@@ -179,7 +179,8 @@ def _token_stride(t, name: str) -> int:
     if st[-1] != 1 or (H > 1 and st[-2] != D):
         raise ValueError("%s: the head and feature dims must be dense" % name)
     ts = st[-3] if t.shape[-3] > 1 else H * D
-    if t.dim() == 4 and t.shape[0] > 1 and st[0] != t.shape[1] * ts:
+    # (rows of no tokens have no stride to check: torch reports one anyway)
+    if t.dim() == 4 and t.shape[0] > 1 and t.shape[1] > 0 and st[0] != t.shape[1] * ts:
         raise ValueError("%s: batch rows must be evenly strided" % name)
     if ts % 8 != 0 or ts < H * D or t.data_ptr() % 16 != 0:
         raise ValueError("%s: token stride must be a multiple of 8 elements and 16-byte aligned" % name)
