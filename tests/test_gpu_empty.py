@@ -1,4 +1,4 @@
-"""Calls with no tokens at all: every sample (or batch row) is empty.
+"""Calls with no tokens at all: every sample, batch row or segment is empty.
 
 The recurrence over an empty sample applies no state update, so the final
 state must equal the initial state bit for bit (zero without one), and o has
@@ -103,3 +103,23 @@ def test_chunk_fwd_c_abi_null_data_without_tokens(shape):
                            torch.cuda.current_stream().cuda_stream)
     assert st == 0, lib.gdn_status_string(st)
     _expect_state(fin, s0)
+
+
+@pytest.mark.parametrize("with_s0", [True, False], ids=["s0", "no_s0"])
+@pytest.mark.parametrize("shape", [SHAPES[0], (torch.float32, 2, 4, 128, 64)],  # the segment maps need K = 128
+                         ids=lambda s: "%s_K%d" % (str(s[0])[6:], s[3]))
+def test_segmented_forward_without_tokens(shape, with_s0):
+    """Three empty segments: each segment's map is the identity, so the chain
+    hands the initial state through unchanged."""
+    dt, Hqk, Hv, K, V = shape
+    q = torch.empty((1, 0, Hqk, K), dtype=dt, device=DEV)
+    k = torch.empty_like(q)
+    v = torch.empty((1, 0, Hv, V), dtype=dt, device=DEV)
+    g = torch.empty((1, 0, Hv), dtype=torch.float32, device=DEV)
+    beta = torch.empty_like(g)
+    s0 = _state(1, Hv, K, V, with_s0, 10)
+    off = np.zeros(4, dtype=np.int32)
+    o, fin = gdn.gdn_chunk_fwd_segmented(q, k, v, g, beta, torch.from_numpy(off).to(DEV), off,
+                                         initial_state=None if s0 is None else s0[0], o_dtype=torch.float32)
+    assert o.shape == (1, 0, Hv, V)
+    _expect_state(fin[None], s0)
