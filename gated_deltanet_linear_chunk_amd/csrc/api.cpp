@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <cstdlib>
 #include <mutex>
 #include <vector>
 
@@ -36,6 +38,28 @@ bool offsets_ok(const int32_t* cu, int32_t n, int64_t first_max, int64_t last, b
   return true;
 }
 
+// GDN_VALIDATE=1 in the environment (read at every call): offsets passed on
+// the device alone are copied back and checked like a host mirror, and the
+// call waits for `stream` up to that copy.  A debugging aid: it blocks the
+// host and cannot be captured into a graph.
+bool validate_device_offsets() {
+  const char* e = std::getenv("GDN_VALIDATE");
+  return e && e[0] == '1' && e[1] == 0;
+}
+
+// Offsets check of an entry point: the host mirror when given, else (with
+// GDN_VALIDATE=1) a host copy of the device array; n >= 1.
+gdn_status check_offsets(const int32_t* dev, const int32_t* host, int32_t n, int64_t first_max, int64_t last,
+                         bool exact_ends, hipStream_t stream) {
+  if (host) return offsets_ok(host, n, first_max, last, exact_ends) ? GDN_OK : GDN_ERR_BAD_SEQLENS;
+  if (!dev || !validate_device_offsets()) return GDN_OK;
+  std::vector<int32_t> copy((size_t)n + 1);
+  if (hipMemcpyAsync(copy.data(), dev, sizeof(int32_t) * copy.size(), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return GDN_ERR_HIP;
+  return offsets_ok(copy.data(), n, first_max, last, exact_ends) ? GDN_OK : GDN_ERR_BAD_SEQLENS;
+}
+
 // Token stride: 0 selects the dense value; otherwise a multiple of 8, >= dense.
 // Below 2^24 elements, so that the kernels form a lane's offset inside a
 // 64-token chunk with one 24-bit multiply.
@@ -60,10 +84,14 @@ size_t tbuf_bytes(int64_t Ttot, int32_t n_seqs, int32_t H_v) {
   return (size_t)gdn::PREP_RECORD_BYTES * (size_t)gdn::chunk_slots(Ttot, n_seqs) * (size_t)H_v;
 }
 
+// Compute units of the current device, queried once per device.
 int device_cus() {
+  static std::atomic<int> known[64];
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64 && (n = known[dev].load(std::memory_order_relaxed)) > 0) return n;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 256;
+  if (dev >= 0 && dev < 64) known[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
@@ -166,7 +194,8 @@ gdn_status gdn_conv1d_fwd(const void* x, const void* w, const void* bias, gdn_dt
   }
   if (cu_seqlens) {
     if (B != 1 || n_seqs < 1) return GDN_ERR_BAD_SEQLENS;
-    if (cu_seqlens_host && !offsets_ok(cu_seqlens_host, n_seqs, 0, T, true)) return GDN_ERR_BAD_SEQLENS;
+    const gdn_status cs = check_offsets(cu_seqlens, cu_seqlens_host, n_seqs, 0, T, true, stream);
+    if (cs != GDN_OK) return cs;
   }
   const int64_t total = (int64_t)B * T;
   if (total == 0) return GDN_OK;
@@ -231,7 +260,8 @@ static gdn_status chunk_fwd_run(const void* q, const void* k, const void* v, gdn
     return GDN_ERR_BAD_SHAPE;
   if (cu_seqlens) {
     if (B != 1 || n_seqs < 1) return GDN_ERR_BAD_SEQLENS;
-    if (cu_seqlens_host && !offsets_ok(cu_seqlens_host, n_seqs, 0, T, true)) return GDN_ERR_BAD_SEQLENS;
+    const gdn_status cs = check_offsets(cu_seqlens, cu_seqlens_host, n_seqs, 0, T, true, stream);
+    if (cs != GDN_OK) return cs;
   }
   const gdn_status sup = chunk_supported(in_dt, K, V);
   if (sup != GDN_OK) return sup;
@@ -492,7 +522,8 @@ gdn_status gdn_conv_chunk_fwd(const void* x, const void* w, const void* bias, gd
   if (!stride_ok(&stride, C)) return GDN_ERR_BAD_SHAPE;
   if (cu_seqlens) {
     if (B != 1 || n_seqs < 1) return GDN_ERR_BAD_SEQLENS;
-    if (cu_seqlens_host && !offsets_ok(cu_seqlens_host, n_seqs, 0, T, true)) return GDN_ERR_BAD_SEQLENS;
+    const gdn_status cs = check_offsets(cu_seqlens, cu_seqlens_host, n_seqs, 0, T, true, stream);
+    if (cs != GDN_OK) return cs;
   }
   const int32_t N = cu_seqlens ? n_seqs : B;
   if (N > kMaxGrid || H_v > kMaxGrid) return GDN_ERR_UNSUPPORTED;
@@ -574,7 +605,8 @@ gdn_status gdn_segment_state_scan(const void* k, const void* v, gdn_dtype in_dt,
   if (!stride_ok(&k_token_stride, (int64_t)H_qk * K) || !stride_ok(&v_token_stride, (int64_t)H_v * V))
     return GDN_ERR_BAD_SHAPE;
   if (!seg_offsets) return GDN_ERR_NULL_POINTER;
-  if (seg_offsets_host && !offsets_ok(seg_offsets_host, P, T, T, false)) return GDN_ERR_BAD_SEQLENS;
+  const gdn_status cs = check_offsets(seg_offsets, seg_offsets_host, P, T, T, false, stream);
+  if (cs != GDN_OK) return cs;
   if (!k || !v || !g || !beta || !M || !b || !seg_initial_states) return GDN_ERR_NULL_POINTER;
   if (mfma && !workspace) return GDN_ERR_NULL_POINTER;
   if (mfma && workspace_bytes < tbuf_bytes(T, P, H_v)) return GDN_ERR_BAD_SHAPE;
@@ -664,7 +696,8 @@ gdn_status gdn_chunk_fwd_segmented(const void* q, const void* k, const void* v,
   if (!stride_ok(&q_token_stride, (int64_t)H_qk * K) || !stride_ok(&k_token_stride, (int64_t)H_qk * K) ||
       !stride_ok(&v_token_stride, (int64_t)H_v * V))
     return GDN_ERR_BAD_SHAPE;
-  if (seg_offsets_host && !offsets_ok(seg_offsets_host, P, 0, T, true)) return GDN_ERR_BAD_SEQLENS;
+  const gdn_status cs = check_offsets(seg_offsets, seg_offsets_host, P, 0, T, true, stream);
+  if (cs != GDN_OK) return cs;
   if (!seg_offsets || !workspace) return GDN_ERR_NULL_POINTER;
   if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL_POINTER;
   const SegmentedLayout l = segmented_layout(T, P, H_v, K, V);

@@ -27,8 +27,8 @@
  *    device array of gdn_chunk_fwd_noalloc (present on every device the
  *    library's code is loaded on) and that array's per-device address; on the
  *    host, a cache of the last eight split plans (keyed by the offsets and
- *    sizes, behind a mutex) and a per-device flag that the scan kernels' LDS
- *    limit is raised.  Calls from several host threads are safe (calls of
+ *    sizes, behind a mutex), a per-device flag that the scan kernels' LDS
+ *    limit is raised, and each device's compute-unit count.  Calls from several host threads are safe (calls of
  *    gdn_chunk_fwd_noalloc that overlap on one device race on its array).
  *  - Host pointers are named *_host and are read before the call returns.
  *  - Work is enqueued on `stream` (0 = the null stream) and the call returns
@@ -41,7 +41,12 @@
  *    only accepted with B == 1 (LlamaFactory PR, Design, decision 6).  Kernels
  *    clamp every offset into [0, T] so a malformed array cannot make them
  *    access memory out of bounds; pass the same array as cu_seqlens_host to
- *    have it validated (GDN_ERR_BAD_SEQLENS) before launch.
+ *    have it validated (GDN_ERR_BAD_SEQLENS) before launch.  With
+ *    GDN_VALIDATE=1 in the environment (read at every call), offsets given on
+ *    the device alone are copied back and validated the same way; the call
+ *    then waits for its stream, so this is for debugging, not for graph
+ *    capture.  The same holds for the segment offsets of the segment entry
+ *    points.
  *  - GQA: v-head h reads q/k head h / (H_v / H_qk) (contiguous groups).
  */
 #ifndef GDN_H_
