@@ -117,6 +117,16 @@ def test_packed_workload_is_split(planner):
         assert seg_len.max() < 3540 * 0.6  # the longest sample no longer bounds the scan
 
 
+def test_one_long_sample_among_many_short_ones_is_split(planner):
+    """The lengths the GPU test of packed calls with more than 64 samples runs through the split
+    path (tests/test_gpu_many_samples.py): the long sample is cut, the short ones run whole."""
+    lengths = [1] * 150 + [0] * 5 + [4000] + [37] * 10
+    for has_s0 in (False, True):
+        p = planner(lengths, 4, 128, has_s0)
+        assert p["split"] and p["n_fwd"] == 1 and p["n_seg"] > len(lengths)
+        check_plan(p, lengths, has_s0)
+
+
 @pytest.mark.parametrize("lengths,Hv,V", [
     ([2500, 0, 700, 64, 1, 1350], 4, 128),
     ([2500, 0, 700, 64, 1, 1350], 4, 256),
