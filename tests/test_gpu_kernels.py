@@ -11,7 +11,7 @@ import pytest
 
 import gdn_inputs
 import oracle
-from parity_util import TOL_F32_ABS, assert_bf16, assert_f32, dev, host, stats
+from parity_util import assert_units_bf16, TOL_F32_ABS, assert_bf16, assert_f32, dev, host, stats
 
 pytestmark = pytest.mark.gpu
 
@@ -209,6 +209,37 @@ def test_chunk_bf16_split_long_samples(gates, V):
     # exactly; without decay the composed starts differ in the last bits.
     if gates == "zero_decay":
         assert not torch.equal(o2[0], o)  # the split path really ran
+
+
+@pytest.mark.parametrize("V", [384, 512])
+def test_chunk_bf16_three_and_four_column_tiles(V):
+    """V = 384 and 512: three and four 128-column workgroups per head, in the split packed run
+    (forward and map blocks of pass 1 over 4 and 5 tiles), the unsplit run and batched rows; every
+    unit against the oracle."""
+    lengths = [2500, 0, 700, 64, 1, 1350]
+    d = gdn_inputs.small(40 + V, lengths, 2, 4, 128, V, "bf16", **GATES["slow"])
+    s0 = (np.random.default_rng(12).standard_normal((len(lengths), 4, 128, V)) * 0.05).astype(np.float32)
+    oref, fref = _oracle_chunk(d, s0)
+    cu = d["cu_seqlens"]
+    o, fin = _run_chunk(d, "bf16", s0, o_dtype=torch.float32)
+    assert_units_bf16(host(o), oref, cu, "split V=%d" % V, fin=host(fin), fref=fref)
+    q, k, v = (dev(d[n], "bf16")[None] for n in ("q", "k", "v"))
+    g, beta = _gpu_gates(d)
+    o2, f2 = gdn.gdn_chunk_fwd(q, k, v, g[None], beta[None], initial_state=dev(s0), cu_seqlens=dev(cu, "i32"),
+                               o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_units_bf16(host(o2[0]), oref, cu, "unsplit V=%d" % V, fin=host(f2), fref=fref)
+    # batched rows: two rows of 300 tokens
+    db = gdn_inputs.small(41 + V, [300, 300], 2, 4, 128, V, "bf16", **GATES["slow"])
+    s0b = s0[:2]
+    q, k, v = (dev(db[n], "bf16").reshape(2, 300, *db[n].shape[1:]) for n in ("q", "k", "v"))
+    g, beta = _gpu_gates(db)
+    o3, f3 = gdn.gdn_chunk_fwd(q, k, v, g.reshape(2, 300, 4), beta.reshape(2, 300, 4), initial_state=dev(s0b),
+                               o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    orefb, frefb = _oracle_chunk(db, s0b)
+    assert_units_bf16(host(o3).reshape(600, 4, V), orefb, db["cu_seqlens"], "batched V=%d" % V, fin=host(f3),
+                      fref=frefb)
 
 
 def test_chunk_bf16_gqa_ratio_three():
