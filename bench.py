@@ -95,10 +95,11 @@ def sources_digest(names):
     return h.hexdigest()[:16]
 
 
-def profiled_traffic(workload):
-    """HBM bytes per gdn_chunk_fwd call (FETCH_SIZE + WRITE_SIZE of its kernels, scaled by a copy
-    calibration) from the committed rocprofv3 summary of that workload; None when the kernel sources
-    have changed since the counters were taken, or when there is no summary."""
+def profiled_traffic(workload, key="traffic_bytes_per_launch"):
+    """HBM bytes per chunk call (FETCH_SIZE + WRITE_SIZE of its kernels, scaled by a copy
+    calibration) from the committed rocprofv3 summary of that workload (`key` names the call when
+    the summary covers several); None when the kernel sources have changed since the counters were
+    taken, or when there is no summary."""
     path = os.path.join(ROOT, "profiles", "chunk_fwd_%s.md" % workload)
     if not os.path.exists(path):
         return None
@@ -111,7 +112,7 @@ def profiled_traffic(workload):
     if fields.get("chunk_sources_sha256_16") != sources_digest(CHUNK_SOURCES):
         return None
     try:
-        return int(fields["traffic_bytes_per_launch"])
+        return int(fields[key])
     except (KeyError, ValueError):
         return None
 
@@ -334,6 +335,16 @@ def build_chunk_only(w, d, o_dtype, mode="plain"):
                                      o_dtype=o_dtype)
 
 
+# Lines whose chunk call --counters runs alone: workload, build_chunk_only mode, o dtype.  The
+# committed summaries divide each counter's sum over the library's chunk kernels by the calls.
+COUNTER_LINES = {
+    "bf16o": (MAIN, "plain", "bfloat16"),
+    "segmented": (LONG, "segmented", "float32"),
+    "split": (LONG, "plain", "float32"),
+    "wide": (WIDE, "plain", "float32"),
+}
+COUNTER_CALLS = 11
+
 DECODE_N = 256  # sequences per decode step
 
 
@@ -469,7 +480,8 @@ def pipeline_lines(name, w, d, o_dtype, o_bytes, reps, flush, peak, steps, warmu
         st2 = summary(time_call(lambda: p["chunk"](q, k, v, g, beta, other), reps, flush))
         lines["chunk_%so" % ("bf16" if ob == 2 else "f32")] = roofline(
             chunk_alg_bytes(T, N, w.Hqk, w.Hv, w.K, w.V, ob, s0=s0), chunk_alg_flops(T, w.Hqk, w.Hv, w.K, w.V), st2,
-            "gdn_chunk_fwd with %s o" % ("bf16" if ob == 2 else "fp32"), peak)
+            "gdn_chunk_fwd with %s o" % ("bf16" if ob == 2 else "fp32"), peak,
+            profiled_traffic(name + "_bf16o") if ob == 2 else None)
     cst = summary(time_call(p["conv"], reps, flush))
     cb = conv_alg_bytes(T, p["C"])
     lines["conv1d"] = dict(cst, hbm_frac=cb / (cst["mean_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
@@ -493,6 +505,9 @@ def main():
                     help="comma-separated extras to run (segmented, split, batched, wide, decode, norm, fused, "
                          "conv_chunk); "
                          "default all")
+    ap.add_argument("--counters", choices=list(COUNTER_LINES), default="",
+                    help="only make %d chunk calls of that line (nothing else of the library runs), for "
+                         "rocprofv3 counter passes" % COUNTER_CALLS)
     ap.add_argument("--copy-only", type=int, default=0,
                     help="only run N plain 256 MiB device copies (counter calibration for profiles)")
     args = ap.parse_args()
@@ -518,6 +533,15 @@ def main():
 
     o_dtype = torch.float32 if args.o_dtype == "f32" else torch.bfloat16
     o_bytes = 4 if args.o_dtype == "f32" else 2
+    if args.counters:
+        name, mode, od = COUNTER_LINES[args.counters]
+        wc = gdn_inputs.WORKLOADS[name]
+        fn = build_chunk_only(wc, gdn_inputs.draw(wc, with_qkv=True), getattr(torch, od), mode)
+        for _ in range(COUNTER_CALLS):
+            fn()
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_line": args.counters, "workload": name, "calls": COUNTER_CALLS}))
+        return
     reps = max(30, args.reps)
     flush = Flush()
     peak = measure_mfma_peak()
@@ -566,12 +590,13 @@ def main():
             if want("segmented"):
                 st = summary(time_call(build_chunk_only(wl, dl, o_dtype, "segmented"), reps, flush))
                 lines["%s[segmented entry point]" % LONG] = roofline(
-                    by, fl, st, "gdn_chunk_fwd_segmented = plan_store_kernel + chunk_prep_kernel + "
-                    "chunk_scan_kernel<2,8> + compose_kernel + chunk_scan_kernel<0,8>", peak)
+                    by, fl, st, "gdn_chunk_fwd_segmented (8 segments) = " + SPLIT_KERNELS.format(0 if o_bytes == 4 else 1), peak,
+                    profiled_traffic(LONG, "traffic_bytes_per_launch_segmented") if o_bytes == 4 else None)
             if want("split"):
                 st = summary(time_call(build_chunk_only(wl, dl, o_dtype), reps, flush))
                 lines["%s[planner-split packed call]" % LONG] = roofline(
-                    by, fl, st, "gdn_chunk_fwd with host offsets (one sample; the planner splits it)", peak)
+                    by, fl, st, "gdn_chunk_fwd with host offsets (one sample; the planner splits it)", peak,
+                    profiled_traffic(LONG, "traffic_bytes_per_launch_split") if o_bytes == 4 else None)
             del dl
             torch.cuda.empty_cache()
             print("long-sequence lines done", file=sys.stderr, flush=True)
@@ -590,7 +615,8 @@ def main():
             lines["%s[chunk]" % WIDE] = roofline(
                 chunk_alg_bytes(ww.total_tokens, ww.n_samples, ww.Hqk, ww.Hv, ww.K, ww.V, o_bytes),
                 chunk_alg_flops(ww.total_tokens, ww.Hqk, ww.Hv, ww.K, ww.V), st,
-                "gdn_chunk_fwd (V = 256: two column tiles per head)", peak, profiled_traffic(WIDE))
+                "gdn_chunk_fwd (V = 256: two column tiles per head)", peak,
+                profiled_traffic(WIDE) if o_bytes == 4 else None)
             del dw
             torch.cuda.empty_cache()
             print("wide line done", file=sys.stderr, flush=True)
