@@ -107,8 +107,8 @@ def profiled_traffic(workload, key="traffic_bytes_per_launch"):
     with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith(("#", "|", "`")):
-                key, _, val = line.partition(":")
-                fields[key.strip()] = val.strip()
+                name, _, val = line.partition(":")
+                fields[name.strip()] = val.strip()
     if fields.get("chunk_sources_sha256_16") != sources_digest(CHUNK_SOURCES):
         return None
     try:
