@@ -226,7 +226,7 @@ gdn_status gdn_chunk_fwd_gated_norm(const void* q, const void* k, const void* v,
  * the chunk rule's load stage.  The pages run the depthwise conv over the
  * concatenated q | k | v channels and hand its output to the chunk rule on
  * the same token-major layout (LlamaFactory PR "[v1] support GDN Ulysses
- * cp", Design: Q/K/V concatenated for conv1d, then the chunk rule); here
+ * cp", Design: one conv over the joined q, k, v channels feeds the chunk rule); here
  * the chunk kernels form each 64-token chunk's q, k, v rows from the raw
  * channels themselves:
  *     a[t, c] = silu(bias[c] + sum_{j<width} w[c, j] x[t - width + 1 + j, c])
